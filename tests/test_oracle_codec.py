@@ -1,0 +1,250 @@
+"""Pins for the oracle's MXFP4 codec (CPU only).
+
+Each test checks the oracle against something other than itself: a closed
+form written from the bit fields, a library routine, a different
+formulation of the rounding rule, hand-worked blocks (tests/golden/), or an
+invariant of the format.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import mxfp4 as q
+from bit_quantized_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+# ---------------------------------------------------------------- decoders
+def test_e2m1_decode_matches_bitfield_formula():
+    # E2M1: 1 sign, 2 exponent bits (bias 1), 1 mantissa bit; exponent 0 is
+    # subnormal with value m * 0.5.  Closed form written from the fields.
+    for code in range(16):
+        s, e, m = code >> 3, (code >> 1) & 3, code & 1
+        val = (0.5 * m) if e == 0 else (2.0 ** (e - 1)) * (1 + 0.5 * m)
+        val = -val if s else val
+        got = q.e2m1_decode(np.array([code], dtype=np.uint8))[0]
+        assert got == val and np.signbit(got) == bool(s) or (val == 0 and got == 0)
+    grid = sorted(set(np.abs(q.e2m1_decode(np.arange(16, dtype=np.uint8)))))
+    assert grid == [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0]
+
+
+def test_e8m0_decode_matches_torch_float8_e8m0():
+    codes = np.arange(255, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e8m0fnu).to(torch.float64).numpy()
+    np.testing.assert_array_equal(q.e8m0_decode(codes), ref)
+    with pytest.raises(ValueError):
+        q.e8m0_decode(np.array([255]))
+
+
+# ---------------------------------------------------------------- encoder
+def _threshold_encode(t):
+    """The same rounding written as decision thresholds at the midpoints.
+
+    Ties (midpoints) go to the even code: <= at midpoints whose lower
+    neighbour has an even code, < where it is odd.
+    """
+    a = np.abs(t)
+    code = np.where(a <= 0.25, 0,
+           np.where(a < 0.75, 1,
+           np.where(a <= 1.25, 2,
+           np.where(a < 1.75, 3,
+           np.where(a <= 2.5, 4,
+           np.where(a < 3.5, 5,
+           np.where(a <= 5.0, 6, 7)))))))
+    return (code | (np.signbit(t) << 3)).astype(np.uint8)
+
+
+def test_encode_equals_threshold_rule_on_fine_grid_and_ties():
+    fine = np.arange(0, 12 * 256 + 1) / 256.0           # 0 .. 12 in 1/256 steps
+    mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
+    near = np.concatenate([mids, np.nextafter(mids, 0), np.nextafter(mids, 10)])
+    vals = np.concatenate([fine, near, [1e-30, 6.0, 7.999, 1e6]])
+    vals = np.concatenate([vals, -vals])
+    np.testing.assert_array_equal(q.e2m1_encode(vals), _threshold_encode(vals))
+
+
+def test_encode_random_against_threshold_rule():
+    rng = np.random.default_rng(7)
+    t = rng.uniform(-9, 9, 200000)
+    np.testing.assert_array_equal(q.e2m1_encode(t), _threshold_encode(t))
+
+
+def test_encode_negative_zero_and_tiny_negatives_keep_sign():
+    got = q.e2m1_encode(np.array([-0.0, 0.0, -1e-9, -0.25, -0.2500001]))
+    np.testing.assert_array_equal(got, [8, 0, 8, 8, 9])
+
+
+# ---------------------------------------------------------------- scale
+def test_scale_equals_biased_exponent_rule():
+    # floor(log2 amax) - 2 + 127 equals the fp32 biased exponent field minus 2
+    # for normal fp32 amax; clamp below at 0.
+    rng = np.random.default_rng(3)
+    bits = synth.to_bf16_bits(np.abs(rng.standard_normal(20000)) * np.exp2(rng.uniform(-140, 125, 20000)))
+    amax = q.bf16_bits_to_f64(bits)
+    field = ((bits.astype(np.int64) >> 7) & 0xFF)
+    ref = np.clip(field - 2, 0, 254)
+    np.testing.assert_array_equal(q.e8m0_from_amax(amax).astype(np.int64), ref)
+    assert q.e8m0_from_amax(np.array([0.0]))[0] == 0
+
+
+# ---------------------------------------------------------------- bf16 rounding
+def test_bf16_rounding_matches_torch_cast_on_fp32_values():
+    rng = np.random.default_rng(11)
+    x = (rng.standard_normal(100000) * np.exp2(rng.uniform(-130, 120, 100000))).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    np.testing.assert_array_equal(q.f64_to_bf16_bits(x.astype(np.float64)), ref)
+
+
+def test_bf16_rounding_ties_even_by_hand():
+    # 1 + 2^-8 lies halfway between 1 and 1 + 2^-7: ties to even -> 1.0 (0x3f80);
+    # 1 + 3*2^-8 is halfway between 1+2^-7 (odd) and 1+2^-6 (even) -> 0x3f82.
+    got = q.f64_to_bf16_bits(np.array([1 + 2 ** -8, 1 + 3 * 2 ** -8, 1 + 2 ** -8 + 2 ** -30]))
+    np.testing.assert_array_equal(got, [0x3F80, 0x3F82, 0x3F81])
+
+
+def test_bf16_widening_exact():
+    bits = np.arange(0, 0x7F80, dtype=np.uint16)
+    np.testing.assert_array_equal(q.f64_to_bf16_bits(q.bf16_bits_to_f64(bits)), bits)
+
+
+# ---------------------------------------------------------------- golden blocks
+def _golden_blocks():
+    with open(os.path.join(GOLDEN, "hand_blocks.json")) as f:
+        return json.load(f)["blocks"]
+
+
+@pytest.mark.parametrize("blk", _golden_blocks(), ids=lambda b: b["name"])
+def test_hand_worked_blocks(blk):
+    bits = np.zeros(32, dtype=np.uint16)
+    vals = [int(h, 16) for h in blk["in"]]
+    bits[:len(vals)] = vals
+    codes, scales = q.quantize_row32(bits[None, :])
+    unpacked = q.unpack_nibbles(codes)[0]
+    exp = np.zeros(32, dtype=np.uint8)
+    exp[:len(blk["codes"])] = blk["codes"]
+    assert scales[0, 0] == int(blk["scale"], 16)
+    np.testing.assert_array_equal(unpacked, exp)
+
+
+def test_packing_order_low_nibble_first():
+    bits = np.zeros((1, 32), dtype=np.uint16)
+    bits[0, 0] = 0x3F80   # 1.0 -> code 2 at element 0
+    bits[0, 1] = 0x40C0   # 6.0 -> code 7 at element 1
+    codes, _ = q.quantize_row32(bits)
+    assert codes[0, 0] == (2 | (7 << 4))
+
+
+# ---------------------------------------------------------------- invariants
+def _random_blocks(seed, n):
+    rng = np.random.default_rng(seed)
+    v = rng.standard_t(2, size=(n, 32)) * np.exp2(rng.integers(-40, 40, size=(n, 1)))
+    return synth.to_bf16_bits(v)
+
+
+def test_idempotence():
+    bits = _random_blocks(1, 20000)
+    c1, s1 = q.quantize_row32(bits)
+    deq = q.dequantize_row32(c1, s1)
+    c2, s2 = q.quantize_row32(q.f64_to_bf16_bits(deq))
+    np.testing.assert_array_equal(c1, c2)
+    np.testing.assert_array_equal(s1, s2)
+
+
+def test_sign_symmetry():
+    bits = _random_blocks(2, 5000)
+    c1, s1 = q.quantize_row32(bits)
+    c2, s2 = q.quantize_row32(bits ^ np.uint16(0x8000))
+    np.testing.assert_array_equal(c2, c1 ^ np.uint8(0x88))
+    np.testing.assert_array_equal(s1, s2)
+
+
+def test_scale_equivariance():
+    bits = _random_blocks(3, 5000)
+    x = q.bf16_bits_to_f64(bits)
+    c1, s1 = q.quantize_row32(bits)
+    for k in (-5, 3, 17):
+        c2, s2 = q.quantize_row32(q.f64_to_bf16_bits(x * 2.0 ** k))
+        np.testing.assert_array_equal(c1, c2)
+        np.testing.assert_array_equal(s2.astype(int), s1.astype(int) + k)
+
+
+def test_error_bound_within_half_step_or_saturation():
+    # |x - deq| <= half the local grid spacing times the scale, except values
+    # above 6 * scale which clip to 6 * scale.
+    bits = _random_blocks(4, 4000)
+    x = q.bf16_bits_to_f64(bits)
+    c, s = q.quantize_row32(bits)
+    d = q.dequantize_row32(c, s)
+    sc = np.repeat(q.e8m0_decode(s), 32, axis=1)
+    t = np.abs(x) / sc
+    spacing = np.where(t < 2, 0.5, np.where(t < 4, 1.0, 2.0))
+    err = np.abs(x - d) / sc
+    ok = (err <= spacing / 2 + 1e-12) | ((t > 6) & (np.abs(d) / sc == 6))
+    assert ok.all()
+    assert np.all(t < 8)      # floor(log2 amax) - 2 keeps scaled values below 8
+
+
+def test_lossless_blocks_round_trip_exactly():
+    rng = np.random.default_rng(5)
+    n = 3000
+    grid = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    v = rng.choice(grid, size=(n, 32)) * rng.choice([-1, 1], size=(n, 32))
+    v[:, 0] = rng.choice([4.0, 6.0], size=n)
+    v = v * np.exp2(rng.integers(-100, 100, size=(n, 1)))
+    bits = synth.to_bf16_bits(v)
+    assert np.array_equal(q.bf16_bits_to_f64(bits), v)
+    c, s = q.quantize_row32(bits)
+    np.testing.assert_array_equal(q.dequantize_row32(c, s), v)
+
+
+def test_row32_t_is_row32_of_transpose_by_hand():
+    rng = np.random.default_rng(6)
+    x = synth.to_bf16_bits(rng.standard_normal((64, 96)))
+    ct, st = q.quantize_row32_t(x)
+    assert ct.shape == (96, 32) and st.shape == (96, 2)
+    # element (i, j) of x is element (j, i) of the transposed layout:
+    # its block along the original rows is rows 32*(i//32) .. +32 of column j.
+    xf = q.bf16_bits_to_f64(x)
+    for (i, j) in [(0, 0), (5, 7), (40, 95), (63, 33)]:
+        blk = xf[32 * (i // 32): 32 * (i // 32) + 32, j]
+        codes, sc = q.quantize_blocks(blk[None, :])
+        assert st[j, i // 32] == sc[0]
+        assert q.unpack_nibbles(ct)[j, i] == codes[0, i % 32]
+
+
+def test_tile32_transpose_invariant():
+    rng = np.random.default_rng(8)
+    w = synth.to_bf16_bits(rng.standard_normal((96, 160)) * np.exp2(rng.integers(-8, 8, (96, 1))))
+    c, s = q.quantize_tile32(w)
+    ct, st = q.quantize_tile32(np.ascontiguousarray(w.T))
+    np.testing.assert_array_equal(q.unpack_nibbles(ct), q.unpack_nibbles(c).T)
+    np.testing.assert_array_equal(st, s.T)
+
+
+def test_tile32_scale_is_tile_amax_rule():
+    rng = np.random.default_rng(9)
+    w = synth.to_bf16_bits(rng.standard_normal((64, 64)) * 0.02)
+    wf = q.bf16_bits_to_f64(w)
+    _, s = q.quantize_tile32(w)
+    for ti in range(2):
+        for tj in range(2):
+            amax = np.abs(wf[32 * ti:32 * ti + 32, 32 * tj:32 * tj + 32]).max()
+            e = int(np.floor(np.log2(amax)))
+            assert s[ti, tj] == e - 2 + 127
+
+
+def test_adversarial_blocks_obey_threshold_rule():
+    bits = synth.adversarial_blocks(0, 600)
+    c, s = q.quantize_row32(bits)
+    x = q.bf16_bits_to_f64(bits)
+    t = x / np.repeat(q.e8m0_decode(s), 32, axis=1)
+    np.testing.assert_array_equal(q.unpack_nibbles(c), _threshold_encode(t))
+
+
+def test_nonfinite_rejected():
+    with pytest.raises(ValueError):
+        q.quantize_row32(np.full((1, 32), 0x7F80, dtype=np.uint16))
