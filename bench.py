@@ -1,0 +1,318 @@
+#!/usr/bin/env python3
+"""Benchmark of FourTune's W4A4G4 triple-branch linear on one MI355X.
+
+One step = forward + backward of the FLUX fused-QKV linear (4608 tokens,
+3072 -> 9216, stabilizer rank 32, LoRA rank 16) through the C ABI:
+  fwd: quantize X + down-projection U  |  MXFP4 GEMM + U V epilogue -> Y
+  bwd: quantize dY + down-projection P |  MXFP4 dgrad GEMM + P D^T -> dX
+       | dA = X^T P_lora | dB = U_lora^T dY
+Four independent input sets (X, dY, W_res, ...) are rotated across steps so
+that no step finds the previous step's operands in the 256 MB last-level
+cache.  The weight quantization (32x32 tiles) happens once per layer
+before training and is not part of a step; it is timed separately on the
+quantizer stress shapes together with the dual-layout activation quantizer.
+
+Prints ONE JSON line.  `value` = algorithmic FLOP of the step / measured
+step time.  The roofline entry is for the kernel with the largest share of
+the step, timed with HIP events on the stream it runs on.
+
+    python bench.py [--steps 50] [--warmup 10] [--gpus 1]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+PEAK_FP4_TFLOPS = 10100.0     # MI355X dense MXFP4 MFMA
+PEAK_BF16_TFLOPS = 2500.0
+PEAK_HBM_GBS = 8000.0
+METRIC = "W4A4G4 linear fwd+bwd TFLOP/s at FLUX shapes; % MXFP4 MFMA peak; quantizer GB/s"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--sets", type=int, default=4)
+    ap.add_argument("--cpu-rows", type=int, default=1024,
+                    help="tokens of the QKV layer the CPU oracle baseline runs")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-stress", action="store_true")
+    ap.add_argument("--only", choices=["step", "stress"], default=None,
+                    help="run only one part (for profiler runs)")
+    return ap.parse_args()
+
+
+def layer_work(M, K, N, rs, rl):
+    """Algorithmic FLOP and HBM bytes of each kernel of one fwd+bwd step."""
+    R = rs + rl
+    w = {
+        "fwd_quant_down": {"flop": 2 * M * K * R,
+                           "bytes": 2 * M * K + M * K // 2 + M * K // 32 + 2 * M * R + 2 * K * R,
+                           "bound": "hbm"},
+        "fwd_gemm": {"flop": 2 * M * N * K + 2 * M * R * N,
+                     "mfma_flop": 2 * M * N * K,
+                     "bytes": M * K // 2 + M * K // 32 + N * K // 2 + N * K // 1024 + 2 * M * R
+                     + 2 * R * N + 2 * M * N,
+                     "bound": "mfma"},
+        "bwd_quant_down": {"flop": 2 * M * N * R,
+                           "bytes": 2 * M * N + M * N // 2 + M * N // 32 + 2 * M * R + 2 * N * R,
+                           "bound": "hbm"},
+        "bwd_gemm_dgrad": {"flop": 2 * M * N * K + 2 * M * R * K,
+                           "mfma_flop": 2 * M * N * K,
+                           "bytes": M * N // 2 + M * N // 32 + N * K // 2 + N * K // 1024
+                           + 2 * M * R + 2 * R * K + 2 * M * K,
+                           "bound": "mfma"},
+        "bwd_lora_dA": {"flop": 2 * M * K * rl, "bytes": 2 * M * K + 2 * M * R + 2 * K * rl,
+                        "bound": "hbm"},
+        "bwd_lora_dB": {"flop": 2 * M * N * rl, "bytes": 2 * M * N + 2 * M * R + 2 * N * rl,
+                        "bound": "hbm"},
+    }
+    return w
+
+
+def source_sha():
+    h = hashlib.sha256()
+    d = os.path.join(HERE, "bit_quantized_amd", "csrc")
+    for f in sorted(os.listdir(d)):
+        with open(os.path.join(d, f), "rb") as fh:
+            h.update(f.encode() + fh.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, sha):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel sources."""
+    p = os.path.join(HERE, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    with open(p) as f:
+        d = json.load(f)
+    e = d.get(kernel)
+    if not e or e.get("source_sha") != sha:
+        return None
+    return e.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(rows):
+    """The oracle as it stands, on the first `rows` tokens of the same layer."""
+    import numpy as np
+    from threadpoolctl import threadpool_info
+    from bit_quantized_amd import synth
+    from oracle import linear as OL
+    from oracle import mxfp4 as OQ
+    c = synth.qkv_case()
+    rows = min(rows, c.M)
+    wc, ws = OQ.quantize_tile32(c.W_res)   # offline weight prep, not timed
+    X, dY = c.X[:rows], c.dY[:rows]
+    t0 = time.perf_counter()
+    f = OL.linear_fwd(X, wc, ws, c.L1, c.L2, c.A, c.B)
+    OL.linear_bwd(dY, X, f["U"], wc, ws, c.L1, c.L2, c.A, c.B)
+    dt = time.perf_counter() - t0
+    flop = sum(v["flop"] for v in layer_work(rows, c.K, c.N, c.r_s, c.r_l).values())
+    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
+                  or [1])
+    return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "seconds": round(dt, 3),
+            "sample": f"float64 numpy oracle, forward+backward of the same QKV linear on its first "
+                      f"{rows} of {c.M} tokens (X and dY quantization, both 4-bit products, "
+                      f"low-rank branches, adapter gradients); the oracle's 32x32 weight "
+                      f"quantization runs before the timer as offline preparation",
+            "host_cpus": len(os.sched_getaffinity(0))}
+
+
+def main():
+    a = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if a.gpus != 1 or world != 1:
+        print(json.dumps({"error": "this benchmark runs on one GPU only; the layer's data-parallel "
+                                   "sharding across GPUs is described in DESIGN.md, not run",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from bit_quantized_amd import ops, synth
+    from bit_quantized_amd.layer import QuantizedLinear, bf16_tensor
+
+    dev = torch.device("cuda:0")
+    ops.lib()
+    out = {"metric": METRIC}
+    stream = torch.cuda.current_stream()
+
+    def log(*x):
+        print(*x, file=sys.stderr, flush=True)
+
+    # ------------------------------------------------------------ layer step
+    c = synth.qkv_case()
+    M, K, N, rs, rl = c.M, c.K, c.N, c.r_s, c.r_l
+    work = layer_work(M, K, N, rs, rl)
+    step_flop = sum(v["flop"] for v in work.values())
+    if a.only in (None, "step"):
+        log(f"bench: QKV linear M={M} K={K} N={N} r_s={rs} r_l={rl}, {a.sets} input sets")
+        X0, dY0, W0 = (bf16_tensor(x, dev) for x in (c.X, c.dY, c.W_res))
+        L1, L2, A, B = (bf16_tensor(x, dev) for x in (c.L1, c.L2, c.A, c.B))
+        sets = []
+        for s in range(a.sets):
+            # distinct memory per set with the same values, rolled along tokens / rows
+            X = torch.roll(X0, 97 * s, 0).contiguous()
+            dY = torch.roll(dY0, 97 * s, 0).contiguous()
+            W = torch.roll(W0, 32 * s, 0).contiguous()
+            lay = QuantizedLinear(W, L1.clone(), L2.clone(), A.clone(), B.clone())
+            del W
+            U = torch.empty((M, rs + rl), dtype=torch.bfloat16, device=dev)
+            Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
+            dA = torch.empty((K, rl), dtype=torch.bfloat16, device=dev)
+            dB = torch.empty((rl, N), dtype=torch.bfloat16, device=dev)
+            wsf = lay.workspace(M, False)
+            wsb = lay.workspace(M, True)
+            sets.append((lay, X, dY, U, Y, dX, dA, dB, wsf, wsb))
+        del X0, dY0, W0
+        torch.cuda.synchronize()
+
+        def step(i):
+            lay, X, dY, U, Y, dX, dA, dB, wsf, wsb = sets[i % len(sets)]
+            d = lay.desc(M)
+            ops.fourtune_linear_fwd(d, X, Y, U, None, None, wsf, wsf.numel(), stream)
+            ops.fourtune_linear_bwd(d, dY, X, U, dX, dA, dB, ops.FT_BF16, None, None, None, wsb,
+                                    wsb.numel(), stream)
+
+        for i in range(a.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(a.steps):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / a.steps
+        log(f"bench: {ms * 1e3:.1f} us/step, {step_flop / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
+
+        # same steps again with every launch bracketed by HIP events
+        ops.fourtune_timing_reset()
+        ops.fourtune_timing_enable(True)
+        e0.record(stream)
+        for i in range(a.steps):
+            step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ops.fourtune_timing_enable(False)
+        ms_instr = e0.elapsed_time(e1) / a.steps
+        tm = ops.fourtune_timing_read()
+        sha = source_sha()
+        kernels = {}
+        for name, (tot, cnt) in tm.items():
+            if name not in work or cnt == 0:
+                continue
+            us = tot / cnt * 1e3
+            wk = work[name]
+            if wk["bound"] == "mfma":
+                ach = wk["mfma_flop"] / (us * 1e-6) / 1e12
+                kernels[name] = {"avg_us": round(us, 2), "launches": cnt, "bound": "mfma",
+                                 "achieved": round(ach, 1), "peak": PEAK_FP4_TFLOPS,
+                                 "unit": "TFLOP/s", "frac": round(ach / PEAK_FP4_TFLOPS, 4)}
+            else:
+                ach = wk["bytes"] / (us * 1e-6) / 1e9
+                kernels[name] = {"avg_us": round(us, 2), "launches": cnt, "bound": "hbm",
+                                 "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                 "frac": round(ach / PEAK_HBM_GBS, 4)}
+        dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
+        dk = kernels[dom]
+        traffic = load_traffic(dom, sha)
+        out.update({
+            "value": round(step_flop / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
+            "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "mxfp4",
+            "data": "synthetic",
+            "config": {"workload": "flux_qkv_linear_fwd_bwd", "M": M, "K": K, "N": N,
+                       "r_stab": rs, "r_lora": rl, "input_sets": a.sets,
+                       "step_flop": step_flop},
+            "roofline": {"kernel": dom, "bound": dk["bound"], "achieved": dk["achieved"],
+                         "peak": dk["peak"], "unit": dk["unit"], "frac": dk["frac"],
+                         "traffic": traffic},
+            "kernels": kernels,
+            "ms_per_step_with_kernel_events": round(ms_instr, 5),
+            "sum_kernel_us": round(sum(v["avg_us"] for v in kernels.values()), 2),
+            "source_sha": sha,
+        })
+        del sets
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ quantizer stress
+    if not a.no_stress and a.only in (None, "stress"):
+        rows, cols, wn = 16384, 12288, 12288
+        g = torch.Generator(device=dev)
+        g.manual_seed(4)
+        log("bench: quantizer stress shapes")
+        T = torch.randn((rows, cols), generator=g, device=dev)
+        chi = sum(torch.randn((rows, cols), generator=g, device=dev) ** 2 for _ in range(3)) / 3.0
+        T = T / chi.sqrt() * 1e-3
+        del chi
+        T = torch.where(torch.rand((rows, cols), generator=g, device=dev) < 1e-3, T * 1e3, T)
+        zt = (torch.rand((rows // 32, 1, cols // 32, 1), generator=g, device=dev) < 0.01)
+        T = T.view(rows // 32, 32, cols // 32, 32).masked_fill(zt, 0.0).view(rows, cols)
+        T = T.to(torch.bfloat16).contiguous()
+        W = (torch.randn((wn, wn), generator=g, device=dev) * 0.02).to(torch.bfloat16)
+        u8 = torch.uint8
+        c1 = torch.empty((rows, cols // 2), dtype=u8, device=dev)
+        s1 = torch.empty((rows, cols // 32), dtype=u8, device=dev)
+        c2 = torch.empty((cols, rows // 2), dtype=u8, device=dev)
+        s2 = torch.empty((cols, rows // 32), dtype=u8, device=dev)
+        cw = torch.empty((wn, wn // 2), dtype=u8, device=dev)
+        sw = torch.empty((wn // 32, wn // 32), dtype=u8, device=dev)
+        flush = torch.empty(1 << 28, dtype=torch.int32, device=dev)   # 1 GiB
+
+        def timed(fn, iters=10):
+            ts = []
+            for _ in range(iters):
+                flush.fill_(1)
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record(stream)
+                fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1) * 1e3)
+            return float(np.median(ts)), float(np.min(ts))
+
+        q_t = lambda: ops.fourtune_quantize(ops.FT_Q_ROW32_T, T, rows, cols, cols, c1, s1, c2, s2,
+                                            stream)
+        q_w = lambda: ops.fourtune_quantize(ops.FT_Q_TILE32, W, wn, wn, wn, cw, sw, None, None,
+                                            stream)
+        q_r = lambda: ops.fourtune_quantize(ops.FT_Q_ROW32, T, rows, cols, cols, c1, s1, None,
+                                            None, stream)
+        q_t(); q_w(); q_r()
+        torch.cuda.synchronize()
+        res = {}
+        for name, fn, nbytes in (
+                ("quant_row32_t", q_t, rows * cols * (2 + 2 * (0.5 + 1 / 32))),
+                ("quant_tile32", q_w, wn * wn * (2 + 0.5 + 1 / 1024)),
+                ("quant_row32", q_r, rows * cols * (2 + 0.5 + 1 / 32))):
+            med, mn = timed(fn)
+            res[name] = {"median_us": round(med, 2), "min_us": round(mn, 2),
+                         "GB/s": round(nbytes / (med * 1e-6) / 1e9, 1),
+                         "frac_hbm": round(nbytes / (med * 1e-6) / 1e9 / PEAK_HBM_GBS, 4),
+                         "algorithmic_bytes": int(nbytes)}
+        res["shapes"] = {"activation": [rows, cols], "weight": [wn, wn]}
+        out["quantizer_stress"] = res
+        log("bench: stress", json.dumps(res))
+        del T, W, flush
+
+    # ------------------------------------------------------------ CPU oracle
+    if not a.no_cpu_baseline and a.only is None:
+        log(f"bench: CPU oracle baseline on {a.cpu_rows} tokens")
+        out["cpu_baseline"] = cpu_baseline(a.cpu_rows)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

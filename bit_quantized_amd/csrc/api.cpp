@@ -1,0 +1,362 @@
+// libfourtune C ABI (include/fourtune.h): argument checks, workspace layout
+// and kernel dispatch.  Every check runs before the first launch, so a call
+// that fails has enqueued nothing.
+#include "../../include/fourtune.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "ft_kernels.h"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+constexpr int64_t kMaxDim = int64_t(1) << 30;
+
+// 1 = current device is gfx950, 0 = not, -1 = unknown yet.  Cached per device.
+int g_arch_ok[64];
+std::once_flag g_arch_once;
+
+ft_status device_check() {
+  std::call_once(g_arch_once, [] {
+    for (int& v : g_arch_ok) v = -1;
+  });
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return FT_EUNSUPPORTED;
+  if (dev < 0 || dev >= 64) return FT_EUNSUPPORTED;
+  if (g_arch_ok[dev] < 0) {
+    hipDeviceProp_t prop;
+    if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FT_EUNSUPPORTED;
+    g_arch_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+  }
+  return g_arch_ok[dev] == 1 ? FT_OK : FT_EUNSUPPORTED;
+}
+
+ft_status launched(hipError_t e) { return e == hipSuccess ? FT_OK : FT_EDEVICE; }
+
+// ---- optional per-kernel timing (benchmarks): hipEvents around each launch
+struct TimingState {
+  std::mutex mu;
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  struct Pending { int slot; hipEvent_t a, b; };
+  std::vector<Pending> pending;
+  std::vector<std::string> names;
+  std::vector<double> total_ms;
+  std::vector<int64_t> counts;
+  int slot(const char* n) {
+    for (size_t i = 0; i < names.size(); ++i)
+      if (names[i] == n) return static_cast<int>(i);
+    names.emplace_back(n);
+    total_ms.push_back(0.0);
+    counts.push_back(0);
+    return static_cast<int>(names.size() - 1);
+  }
+  hipEvent_t take() {
+    if (pool.empty()) {
+      hipEvent_t e = nullptr;
+      if (hipEventCreate(&e) != hipSuccess) return nullptr;
+      return e;
+    }
+    hipEvent_t e = pool.back();
+    pool.pop_back();
+    return e;
+  }
+  void drain() {  // caller holds mu
+    for (auto& p : pending) {
+      float ms = 0.f;
+      if (hipEventSynchronize(p.b) == hipSuccess && hipEventElapsedTime(&ms, p.a, p.b) == hipSuccess) {
+        total_ms[p.slot] += ms;
+        counts[p.slot] += 1;
+      }
+      pool.push_back(p.a);
+      pool.push_back(p.b);
+    }
+    pending.clear();
+  }
+};
+TimingState g_tm;
+
+// Brackets one launch with events when timing is on.
+struct Timed {
+  hipEvent_t a = nullptr, b = nullptr;
+  int slot = -1;
+  hipStream_t st;
+  Timed(const char* name, hipStream_t s) : st(s) {
+    if (!g_tm.on) return;
+    std::lock_guard<std::mutex> lk(g_tm.mu);
+    slot = g_tm.slot(name);
+    a = g_tm.take();
+    b = g_tm.take();
+    if (a && b) hipEventRecord(a, st);
+  }
+  hipError_t done(hipError_t e) {
+    if (a && b) {
+      hipEventRecord(b, st);
+      std::lock_guard<std::mutex> lk(g_tm.mu);
+      g_tm.pending.push_back({slot, a, b});
+    }
+    return e;
+  }
+};
+
+// Checks shared by forward and backward.
+ft_status check_linear(const ft_linear* L) {
+  if (!L) return FT_EINVAL;
+  if (L->M < 1 || L->K < 32 || L->N < 32) return FT_ESHAPE;
+  if (L->M > kMaxDim || L->K > kMaxDim || L->N > kMaxDim) return FT_ESHAPE;
+  if ((L->K & 31) || (L->N & 31)) return FT_ESHAPE;
+  if (L->r_stab < 0 || L->r_lora < 0 || L->r_stab + L->r_lora > FT_MAX_RANK) return FT_ESHAPE;
+  if (!L->w_codes || !L->w_scales) return FT_EINVAL;
+  if (L->r_stab > 0 && (!L->L1 || !L->L2)) return FT_EINVAL;
+  if (L->r_lora > 0 && (!L->A || !L->B)) return FT_EINVAL;
+  const void* ptrs[] = {L->w_codes, L->w_scales, L->L1, L->L2, L->A, L->B};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FT_EALIGN;
+  return FT_OK;
+}
+
+struct FwdLayout {
+  size_t xq_codes, xq_scales, part, cnt, total;
+};
+FwdLayout fwd_layout(const ft_linear* L) {
+  const int R = L->r_stab + L->r_lora;
+  FwdLayout o;
+  size_t off = 0;
+  o.xq_codes = off; off += align_up(static_cast<size_t>(L->M) * (L->K / 2));
+  o.xq_scales = off; off += align_up(static_cast<size_t>(L->M) * (L->K / 32));
+  o.part = off; off += align_up(R ? ft::quant_down_part_bytes(L->M, L->K, R) : 0);
+  o.cnt = off; off += align_up(ft::quant_down_cnt_bytes(L->M));
+  o.total = off;
+  return o;
+}
+
+struct BwdLayout {
+  size_t gq_codes, gq_scales, P, part, cnt, dA_part, dA_cnt, dB_part, dB_cnt, total;
+};
+BwdLayout bwd_layout(const ft_linear* L) {
+  const int R = L->r_stab + L->r_lora;
+  const int rl = L->r_lora;
+  BwdLayout o;
+  size_t off = 0;
+  o.gq_codes = off; off += align_up(static_cast<size_t>(L->M) * (L->N / 2));
+  o.gq_scales = off; off += align_up(static_cast<size_t>(L->M) * (L->N / 32));
+  o.P = off; off += align_up(static_cast<size_t>(L->M) * R * 2);
+  o.part = off; off += align_up(R ? ft::quant_down_part_bytes(L->M, L->N, R) : 0);
+  o.cnt = off; off += align_up(ft::quant_down_cnt_bytes(L->M));
+  o.dA_part = off; off += align_up(rl ? ft::lora_grad_part_bytes(L->M, L->K, rl) : 0);
+  o.dA_cnt = off; off += align_up(rl ? ft::lora_grad_cnt_bytes(L->K) : 0);
+  o.dB_part = off; off += align_up(rl ? ft::lora_grad_part_bytes(L->M, L->N, rl) : 0);
+  o.dB_cnt = off; off += align_up(rl ? ft::lora_grad_cnt_bytes(L->N) : 0);
+  o.total = off;
+  return o;
+}
+
+// Rank operand indexed by k: D = [L1 | A], D[k][r].
+ft::LowRankPieces pieces_D(const ft_linear* L) {
+  return ft::LowRankPieces{L->L1, L->r_stab, 1, L->r_stab, L->A, L->r_lora, 1, L->r_lora};
+}
+// Rank operand indexed by n: V^T, V = [L2 ; B], V[r][n].
+ft::LowRankPieces pieces_Vt(const ft_linear* L) {
+  return ft::LowRankPieces{L->L2, 1, L->N, L->r_stab, L->B, 1, L->N, L->r_lora};
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* fourtune_status_string(ft_status s) {
+  switch (s) {
+    case FT_OK: return "ok";
+    case FT_EINVAL: return "invalid argument (null pointer or bad enum value)";
+    case FT_ESHAPE: return "unsupported shape";
+    case FT_EALIGN: return "misaligned pointer or row stride";
+    case FT_EWORKSPACE: return "workspace too small";
+    case FT_EDEVICE: return "HIP launch failed";
+    case FT_EUNSUPPORTED: return "no supported GPU (gfx950) is current";
+  }
+  return "unknown status";
+}
+
+ft_status fourtune_quantize(int mode, const uint16_t* in, int64_t rows, int64_t cols,
+                            int64_t ld_in, uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
+                            uint8_t* scales_t, void* stream) {
+  if (mode != FT_Q_ROW32 && mode != FT_Q_ROW32_T && mode != FT_Q_TILE32) return FT_EINVAL;
+  if (!in || !codes || !scales) return FT_EINVAL;
+  if (mode == FT_Q_ROW32_T) {
+    if (!codes_t || !scales_t) return FT_EINVAL;
+  } else if (codes_t || scales_t) {
+    return FT_EINVAL;
+  }
+  if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return FT_ESHAPE;
+  if (cols & 31) return FT_ESHAPE;
+  if (mode != FT_Q_ROW32 && (rows & 31)) return FT_ESHAPE;
+  if (ld_in < cols || (ld_in & 7)) return FT_EALIGN;
+  if (!aligned16(in) || !aligned16(codes) || !aligned16(scales)) return FT_EALIGN;
+  if (codes_t && !aligned16(codes_t)) return FT_EALIGN;
+  if (scales_t && !aligned16(scales_t)) return FT_EALIGN;
+  if (rows == 0 || cols == 0) return FT_OK;
+  if (ft_status s = device_check(); s != FT_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  switch (mode) {
+    case FT_Q_ROW32:
+      { Timed tm("quant_row32", st); return launched(tm.done(ft::launch_quant_row32(in, rows, cols, ld_in, codes, scales, st))); }
+    case FT_Q_TILE32:
+      { Timed tm("quant_tile32", st); return launched(tm.done(ft::launch_quant_tile32(in, rows, cols, ld_in, codes, scales, st))); }
+    default:
+    {
+      Timed tm("quant_row32_t", st);
+      return launched(tm.done(
+          ft::launch_quant_row32_t(in, rows, cols, ld_in, codes, scales, codes_t, scales_t, st)));
+    }
+  }
+}
+
+size_t fourtune_workspace_bytes(const ft_linear* L, int is_bwd) {
+  if (!L || L->M < 1 || L->K < 32 || L->N < 32 || (L->K & 31) || (L->N & 31)) return 0;
+  if (L->M > kMaxDim || L->K > kMaxDim || L->N > kMaxDim) return 0;
+  if (L->r_stab < 0 || L->r_lora < 0 || L->r_stab + L->r_lora > FT_MAX_RANK) return 0;
+  return is_bwd ? bwd_layout(L).total : fwd_layout(L).total;
+}
+
+ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y,
+                              uint16_t* U_save, uint8_t* xq_codes, uint8_t* xq_scales,
+                              void* workspace, size_t ws_bytes, void* stream) {
+  if (ft_status s = check_linear(L); s != FT_OK) return s;
+  const int R = L->r_stab + L->r_lora;
+  if (!X || !Y) return FT_EINVAL;
+  if (R > 0 && !U_save) return FT_EINVAL;
+  if ((xq_codes == nullptr) != (xq_scales == nullptr)) return FT_EINVAL;
+  const void* ptrs[] = {X, Y, U_save, xq_codes, xq_scales, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FT_EALIGN;
+  const FwdLayout lay = fwd_layout(L);
+  if (ws_bytes < lay.total) return FT_EWORKSPACE;
+  if (!workspace) return FT_EINVAL;
+  if (ft_status s = device_check(); s != FT_OK) return s;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* qc = xq_codes ? xq_codes : ws + lay.xq_codes;
+  uint8_t* qs = xq_scales ? xq_scales : ws + lay.xq_scales;
+  hipError_t e;
+  {
+    Timed tm("fwd_quant_down", st);
+    if (R > 0)
+      e = ft::launch_quant_down(X, L->M, L->K, L->K, qc, qs, pieces_D(L), U_save,
+                                reinterpret_cast<float*>(ws + lay.part),
+                                reinterpret_cast<uint32_t*>(ws + lay.cnt), st);
+    else
+      e = ft::launch_quant_row32(X, L->M, L->K, L->K, qc, qs, st);
+    tm.done(e);
+  }
+  if (e != hipSuccess) return FT_EDEVICE;
+  ft::GemmArgs g{};
+  g.M = L->M; g.RED = L->K; g.NOUT = L->N;
+  g.a_codes = qc; g.a_scales = qs;
+  g.w_codes = L->w_codes; g.w_scales = L->w_scales; g.w_cols = L->K;
+  g.lm = U_save; g.lo = pieces_Vt(L); g.R = R; g.out = Y;
+  Timed tm("fwd_gemm", st);
+  return launched(tm.done(ft::launch_gemm_fwd(g, st)));
+}
+
+ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint16_t* X,
+                              const uint16_t* U_save, uint16_t* dX, void* dA, void* dB,
+                              ft_dtype grad_dtype, uint16_t* P_save, uint8_t* gq_codes,
+                              uint8_t* gq_scales, void* workspace, size_t ws_bytes,
+                              void* stream) {
+  if (ft_status s = check_linear(L); s != FT_OK) return s;
+  const int R = L->r_stab + L->r_lora;
+  const int rl = L->r_lora;
+  if (!dY) return FT_EINVAL;
+  if (grad_dtype != FT_BF16 && grad_dtype != FT_F32) return FT_EINVAL;
+  if (rl > 0 && (!X || !U_save || !dA || !dB)) return FT_EINVAL;
+  if ((gq_codes == nullptr) != (gq_scales == nullptr)) return FT_EINVAL;
+  const void* ptrs[] = {dY, X, U_save, dX, dA, dB, P_save, gq_codes, gq_scales, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FT_EALIGN;
+  const BwdLayout lay = bwd_layout(L);
+  if (ws_bytes < lay.total) return FT_EWORKSPACE;
+  if (!workspace) return FT_EINVAL;
+  if (ft_status s = device_check(); s != FT_OK) return s;
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  uint8_t* qc = gq_codes ? gq_codes : ws + lay.gq_codes;
+  uint8_t* qs = gq_scales ? gq_scales : ws + lay.gq_scales;
+  uint16_t* P = P_save ? P_save : reinterpret_cast<uint16_t*>(ws + lay.P);
+  hipError_t e;
+  {
+    Timed tm("bwd_quant_down", st);
+    if (R > 0)
+      e = ft::launch_quant_down(dY, L->M, L->N, L->N, qc, qs, pieces_Vt(L), P,
+                                reinterpret_cast<float*>(ws + lay.part),
+                                reinterpret_cast<uint32_t*>(ws + lay.cnt), st);
+    else
+      e = ft::launch_quant_row32(dY, L->M, L->N, L->N, qc, qs, st);
+    tm.done(e);
+  }
+  if (e != hipSuccess) return FT_EDEVICE;
+  if (dX) {
+    ft::GemmArgs g{};
+    g.M = L->M; g.RED = L->N; g.NOUT = L->K;
+    g.a_codes = qc; g.a_scales = qs;
+    g.w_codes = L->w_codes; g.w_scales = L->w_scales; g.w_cols = L->K;
+    g.lm = P; g.lo = pieces_D(L); g.R = R; g.out = dX;
+    Timed tm("bwd_gemm_dgrad", st);
+    if (tm.done(ft::launch_gemm_dgrad(g, st)) != hipSuccess) return FT_EDEVICE;
+  }
+  if (rl > 0) {
+    const int f32 = grad_dtype == FT_F32 ? 1 : 0;
+    ft::LoraGradArgs a{};
+    a.M = L->M; a.I = L->K; a.big = X; a.small = P; a.ld_small = R; a.r0 = L->r_stab; a.rl = rl;
+    a.out = dA; a.out_f32 = f32; a.transpose_out = 0;
+    a.part = reinterpret_cast<float*>(ws + lay.dA_part);
+    a.cnt = reinterpret_cast<uint32_t*>(ws + lay.dA_cnt);
+    {
+      Timed tm("bwd_lora_dA", st);
+      if (tm.done(ft::launch_lora_grad(a, st)) != hipSuccess) return FT_EDEVICE;
+    }
+    ft::LoraGradArgs b{};
+    b.M = L->M; b.I = L->N; b.big = dY; b.small = U_save; b.ld_small = R; b.r0 = L->r_stab; b.rl = rl;
+    b.out = dB; b.out_f32 = f32; b.transpose_out = 1;
+    b.part = reinterpret_cast<float*>(ws + lay.dB_part);
+    b.cnt = reinterpret_cast<uint32_t*>(ws + lay.dB_cnt);
+    Timed tm("bwd_lora_dB", st);
+    if (tm.done(ft::launch_lora_grad(b, st)) != hipSuccess) return FT_EDEVICE;
+  }
+  return FT_OK;
+}
+
+void fourtune_timing_enable(int on) {
+  std::lock_guard<std::mutex> lk(g_tm.mu);
+  g_tm.on = on != 0;
+}
+
+void fourtune_timing_reset(void) {
+  std::lock_guard<std::mutex> lk(g_tm.mu);
+  g_tm.drain();
+  for (auto& v : g_tm.total_ms) v = 0.0;
+  for (auto& c : g_tm.counts) c = 0;
+}
+
+int fourtune_timing_read(const char** names, double* total_ms, int64_t* counts, int max_entries) {
+  std::lock_guard<std::mutex> lk(g_tm.mu);
+  g_tm.drain();
+  const int n = static_cast<int>(g_tm.names.size());
+  for (int i = 0; i < n && i < max_entries; ++i) {
+    if (names) names[i] = g_tm.names[i].c_str();
+    if (total_ms) total_ms[i] = g_tm.total_ms[i];
+    if (counts) counts[i] = g_tm.counts[i];
+  }
+  return n;
+}
+
+}  // extern "C"

@@ -1,0 +1,131 @@
+// Device-side building blocks shared by the HIP kernels of libfourtune:
+// vector types, bf16 rounding, the MXFP4 block-scale rule and wrappers of
+// the gfx950 matrix-core and conversion instructions.
+//
+// MXFP4 (OCP Microscaling v1.0, the format FourTune's "2.3 Model
+// Quantization" cites): a block of 32 (or a 32x32 tile) shares one E8M0
+// scale 2^(s-127) with s = floor(log2(amax)) - 2 + 127, clamped to >= 0;
+// elements are E2M1, rounded to nearest with ties to even and saturated at
+// 6.  On gfx950, v_cvt_scalef32_pk_fp4_bf16 divides two bf16 values by a
+// power-of-two fp32 scale and encodes them that way (round to nearest even,
+// saturating, sign of zero kept), including the fp32-denormal scale 2^-127.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ft {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef int i32x8 __attribute__((ext_vector_type(8)));
+typedef int i32x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef uint16_t u16x2 __attribute__((ext_vector_type(2)));
+
+#define FT_LDS __attribute__((address_space(3)))
+
+// ---------------------------------------------------------------- bf16
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+__device__ __forceinline__ float bf16lo_to_f32(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16hi_to_f32(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+
+// Round a finite fp32 to bf16, nearest with ties to even.
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2_rne(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16_rne(lo)) |
+         (static_cast<uint32_t>(f32_to_bf16_rne(hi)) << 16);
+}
+
+// ---------------------------------------------------------------- MXFP4 scale
+// Magnitude bits of two packed bf16 (sign bits cleared).
+__device__ __forceinline__ uint32_t abs_bf16x2(uint32_t w) { return w & 0x7FFF7FFFu; }
+
+// Lane-wise max of two packed u16 pairs (v_pk_max_u16).
+__device__ __forceinline__ uint32_t max_u16x2(uint32_t a, uint32_t b) {
+  u16x2 x = __builtin_bit_cast(u16x2, a);
+  u16x2 y = __builtin_bit_cast(u16x2, b);
+  return __builtin_bit_cast(uint32_t, __builtin_elementwise_max(x, y));
+}
+
+// Largest magnitude (as bf16 magnitude bits) in a packed-max accumulator.
+__device__ __forceinline__ uint32_t hmax_u16x2(uint32_t m) {
+  uint32_t lo = m & 0xFFFFu, hi = m >> 16;
+  return lo > hi ? lo : hi;
+}
+
+// E8M0 scale byte from the bf16 magnitude bits of the block amax:
+// floor(log2(amax)) is the unbiased exponent for normals; bf16 subnormals
+// and zero have exponent field 0 and give 0 after the clamp.
+__device__ __forceinline__ uint32_t e8m0_from_amax_bits(uint32_t amax_bits) {
+  int e = static_cast<int>(amax_bits >> 7) - 2;
+  e = e < 0 ? 0 : e;
+  return static_cast<uint32_t>(e > 254 ? 254 : e);
+}
+
+// The scale 2^(s-127) as an fp32 value; s == 0 is the denormal 2^-127.
+__device__ __forceinline__ float e8m0_to_f32(uint32_t s) {
+  return __uint_as_float(s ? (s << 23) : 0x00400000u);
+}
+
+// Encode 8 bf16 (4 packed words) to 8 E2M1 codes (one u32, element i in
+// nibble i) with scale `sc`.
+__device__ __forceinline__ uint32_t encode8(uint32_t w0, uint32_t w1, uint32_t w2, uint32_t w3,
+                                            float sc) {
+  uint32_t r = 0;
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w0), sc, 0);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w1), sc, 1);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w2), sc, 2);
+  r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, __builtin_bit_cast(bf16x2, w3), sc, 3);
+  return r;
+}
+
+// ---------------------------------------------------------------- matrix cores
+// 32x32x64 MXFP4 x MXFP4 -> fp32.  Lane l supplies 32 E2M1 codes (16 bytes)
+// of row/column l%32 for reduction block l/32, and the E8M0 scale of that
+// block in byte OPSEL of its scale word.
+template <int OPA, int OPB>
+__device__ __forceinline__ f32x16 mfma_fp4_32x32x64(u32x4 a, u32x4 b, f32x16 c, uint32_t sa,
+                                                    uint32_t sb) {
+  i32x8 av = {(int)a[0], (int)a[1], (int)a[2], (int)a[3], 0, 0, 0, 0};
+  i32x8 bv = {(int)b[0], (int)b[1], (int)b[2], (int)b[3], 0, 0, 0, 0};
+  return __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(av, bv, c, 4, 4, OPA, (int)sa, OPB,
+                                                         (int)sb);
+}
+
+// 32x32x16 bf16 -> fp32 (same accumulator layout as the fp4 instruction).
+__device__ __forceinline__ f32x16 mfma_bf16_32x32x16(u32x4 a, u32x4 b, f32x16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 16x16x32 bf16 -> fp32.
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                 __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+}
+
+// 64-bit LDS read with a 16x16 transpose of 4-bit elements across each
+// group of 16 lanes: lane q of a group receives nibble q of the 8 bytes
+// addressed by each of the 16 lanes, in lane order.  `p` must point into
+// __shared__ memory.
+__device__ __forceinline__ u32x2 lds_read_tr4(const void* p) {
+  i32x2 r = __builtin_amdgcn_ds_read_tr4_b64_v2i32((FT_LDS i32x2*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
+// 128-bit read from __shared__ memory.
+__device__ __forceinline__ u32x4 lds_read_b128(const void* p) {
+  return *(const FT_LDS u32x4*)(p);
+}
+
+}  // namespace ft

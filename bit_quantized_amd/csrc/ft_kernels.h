@@ -1,0 +1,71 @@
+// Internal launchers of libfourtune (host side).  Not part of the public ABI.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace ft {
+
+// A rank-R operand given as two bf16 pieces along the rank axis: element
+// (c, r) = r < r0 ? p0[c*s0c + r*s0r] : p1[c*s1c + (r-r0)*s1r], where c runs
+// over the long axis (K or N) of the layer.
+struct LowRankPieces {
+  const uint16_t* p0;
+  int64_t s0c, s0r;
+  int r0;
+  const uint16_t* p1;
+  int64_t s1c, s1r;
+  int r1;
+};
+
+// quantize.hip
+hipError_t launch_quant_row32(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
+                              uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_quant_tile32(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
+                               uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_quant_row32_t(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
+                                uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
+                                uint8_t* scales_t, hipStream_t st);
+hipError_t launch_quant_down(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
+                             uint8_t* codes, uint8_t* scales, const LowRankPieces& pr,
+                             uint16_t* out_lr, float* part, uint32_t* cnt, hipStream_t st);
+size_t quant_down_part_bytes(int64_t rows, int64_t cols, int R);
+size_t quant_down_cnt_bytes(int64_t rows);
+
+// gemm.hip: C[m][j] = sum_red deq(a)[m][red] deq(b)(red, j) + sum_r lm[m][r] lo(j, r)
+// FWD : a = Qrow(X) [M, K], b = Qtile(W) read as W[j][red] (j = n), lo = V^T
+// DGRAD: a = Qrow(dY) [M, N], b = Qtile(W) read as W[red][j] (j = k), lo = D
+struct GemmArgs {
+  int64_t M, RED, NOUT;           // rows, reduction length, output columns
+  const uint8_t* a_codes;         // [M, RED/2]
+  const uint8_t* a_scales;        // [M, RED/32]
+  const uint8_t* w_codes;         // W codes [N, K/2]
+  const uint8_t* w_scales;        // [N/32, K/32]
+  int64_t w_cols;                 // K (codes row length is K/2, scales row length K/32)
+  const uint16_t* lm;             // bf16 [M, R] (U or P), may be null when R == 0
+  LowRankPieces lo;               // rank operand indexed by output column
+  int R;
+  uint16_t* out;                  // bf16 [M, NOUT]
+};
+hipError_t launch_gemm_fwd(const GemmArgs& g, hipStream_t st);
+hipError_t launch_gemm_dgrad(const GemmArgs& g, hipStream_t st);
+
+// lora.hip: out(i, r) = sum_m big[m][i] * small[m][r0 + r], r < rl.
+// transpose_out: write out[r][i] (dB) instead of out[i][r] (dA).
+struct LoraGradArgs {
+  int64_t M, I;                   // rows, columns of big
+  const uint16_t* big;            // bf16 [M, I]
+  const uint16_t* small;          // bf16 [M, ld_small], columns r0 .. r0+rl used
+  int ld_small, r0, rl;
+  void* out;                      // [I, rl] or [rl, I]
+  int out_f32;                    // 0 bf16, 1 fp32
+  int transpose_out;
+  float* part;                    // workspace partials
+  uint32_t* cnt;                  // workspace counters (zeroed by the launcher)
+};
+hipError_t launch_lora_grad(const LoraGradArgs& a, hipStream_t st);
+size_t lora_grad_part_bytes(int64_t M, int64_t I, int rl);
+size_t lora_grad_cnt_bytes(int64_t I);
+
+}  // namespace ft

@@ -1,0 +1,118 @@
+"""Device-side plumbing around the C ABI: a layer object that owns its
+quantized frozen weight, stabilizer and adapter tensors, allocates outputs
+and workspace with PyTorch, and calls fourtune_linear_fwd / _bwd.  Also a
+torch.autograd.Function for use inside a training graph.
+
+Nothing here computes any part of the layer; it only moves memory and
+calls the library.
+"""
+from __future__ import annotations
+
+import numpy as np
+import torch
+
+from . import ops
+
+
+def bf16_tensor(bits: np.ndarray, device) -> torch.Tensor:
+    """Upload bf16 bit patterns (uint16 numpy) as a torch.bfloat16 tensor."""
+    t = torch.from_numpy(np.ascontiguousarray(bits).view(np.int16))
+    return t.to(device).view(torch.bfloat16)
+
+
+def bits_of(t: torch.Tensor) -> np.ndarray:
+    """Download a bf16 tensor as uint16 bit patterns."""
+    return t.detach().contiguous().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def _empty(shape, dtype, device):
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+class QuantizedLinear:
+    """One triple-branch linear on the GPU.
+
+    W_res (bf16 [N, K]) is quantized once on the device to 32x32 MXFP4 tiles
+    by fourtune_quantize; L1, L2 (frozen) and A, B (trainable) stay bf16.
+    """
+
+    def __init__(self, W_res: torch.Tensor, L1: torch.Tensor | None, L2: torch.Tensor | None,
+                 A: torch.Tensor | None, B: torch.Tensor | None, stream=None):
+        N, K = W_res.shape
+        dev = W_res.device
+        self.N, self.K = int(N), int(K)
+        self.r_s = 0 if L1 is None else int(L1.shape[1])
+        self.r_l = 0 if A is None else int(A.shape[1])
+        self.L1, self.L2, self.A, self.B = L1, L2, A, B
+        self.w_codes = _empty((N, K // 2), torch.uint8, dev)
+        self.w_scales = _empty((N // 32, K // 32), torch.uint8, dev)
+        ops.fourtune_quantize(ops.FT_Q_TILE32, W_res, N, K, K, self.w_codes, self.w_scales,
+                              stream=stream)
+        self.device = dev
+        self._ws = {}
+
+    @property
+    def R(self):
+        return self.r_s + self.r_l
+
+    def desc(self, M: int) -> ops.FtLinear:
+        return ops.make_linear(M, self.K, self.N, self.r_s, self.r_l, self.w_codes,
+                               self.w_scales, self.L1, self.L2, self.A, self.B)
+
+    def workspace(self, M: int, is_bwd: bool):
+        key = (M, bool(is_bwd))
+        if key not in self._ws:
+            n = ops.fourtune_workspace_bytes(self.desc(M), is_bwd)
+            self._ws[key] = _empty((max(n, 256),), torch.uint8, self.device)
+        return self._ws[key]
+
+    def forward(self, X: torch.Tensor, stream=None, want_codes: bool = False):
+        """Returns (Y, U) or (Y, U, xq_codes, xq_scales)."""
+        M = int(X.shape[0])
+        dev = self.device
+        Y = _empty((M, self.N), torch.bfloat16, dev)
+        U = _empty((M, max(self.R, 1)), torch.bfloat16, dev)
+        qc = _empty((M, self.K // 2), torch.uint8, dev) if want_codes else None
+        qs = _empty((M, self.K // 32), torch.uint8, dev) if want_codes else None
+        ws = self.workspace(M, False)
+        ops.fourtune_linear_fwd(self.desc(M), X, Y, U if self.R else None, qc, qs, ws,
+                                ws.numel(), stream)
+        return (Y, U, qc, qs) if want_codes else (Y, U)
+
+    def backward(self, dY: torch.Tensor, X: torch.Tensor, U: torch.Tensor, need_dx: bool = True,
+                 grad_f32: bool = False, stream=None, want_codes: bool = False):
+        """Returns (dX, dA, dB, P) or (dX, dA, dB, P, gq_codes, gq_scales)."""
+        M = int(dY.shape[0])
+        dev = self.device
+        dX = _empty((M, self.K), torch.bfloat16, dev) if need_dx else None
+        gdt = torch.float32 if grad_f32 else torch.bfloat16
+        dA = _empty((self.K, self.r_l), gdt, dev) if self.r_l else None
+        dB = _empty((self.r_l, self.N), gdt, dev) if self.r_l else None
+        P = _empty((M, max(self.R, 1)), torch.bfloat16, dev)
+        qc = _empty((M, self.N // 2), torch.uint8, dev) if want_codes else None
+        qs = _empty((M, self.N // 32), torch.uint8, dev) if want_codes else None
+        ws = self.workspace(M, True)
+        ops.fourtune_linear_bwd(self.desc(M), dY, X, U if self.R else None, dX, dA, dB,
+                                ops.FT_F32 if grad_f32 else ops.FT_BF16,
+                                P if self.R else None, qc, qs, ws, ws.numel(), stream)
+        out = (dX, dA, dB, P)
+        return out + (qc, qs) if want_codes else out
+
+
+class FourTuneLinearFunction(torch.autograd.Function):
+    """Y = layer(X) with gradients for X, A and B (W_res, L1, L2 frozen)."""
+
+    @staticmethod
+    def forward(ctx, X, A, B, layer: QuantizedLinear):
+        Y, U = layer.forward(X.contiguous())
+        ctx.save_for_backward(X, U)
+        ctx.layer = layer
+        return Y
+
+    @staticmethod
+    def backward(ctx, dY):
+        X, U = ctx.saved_tensors
+        layer = ctx.layer
+        dX, dA, dB, _ = layer.backward(dY.contiguous().to(torch.bfloat16), X, U,
+                                       need_dx=ctx.needs_input_grad[0])
+        return dX, dA, dB, None

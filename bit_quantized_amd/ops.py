@@ -1,0 +1,158 @@
+"""Thin ctypes binding of libfourtune.so (include/fourtune.h).
+
+Argument marshalling only: every step of the layer runs in the HIP kernels
+behind the C ABI.  PyTorch provides device memory and the stream.  The
+functions keep the C names; they take torch tensors (device memory) and
+raise FourTuneError on any status other than FT_OK.  bf16 tensors may be
+passed as torch.bfloat16 or as int16/uint16 bit patterns.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libfourtune.so")
+
+FT_OK, FT_EINVAL, FT_ESHAPE, FT_EALIGN, FT_EWORKSPACE, FT_EDEVICE, FT_EUNSUPPORTED = range(7)
+FT_BF16, FT_F32 = 0, 1
+FT_Q_ROW32, FT_Q_ROW32_T, FT_Q_TILE32 = 1, 2, 4
+FT_MAX_RANK = 64
+
+EXPORTS = ("fourtune_quantize", "fourtune_workspace_bytes", "fourtune_linear_fwd",
+           "fourtune_linear_bwd", "fourtune_status_string", "fourtune_timing_enable",
+           "fourtune_timing_reset", "fourtune_timing_read")
+
+
+class FourTuneError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        super().__init__(f"{where}: status {status} ({status_string(status)})")
+        self.status = status
+
+
+class FtLinear(ctypes.Structure):
+    _fields_ = [("M", ctypes.c_int64), ("K", ctypes.c_int64), ("N", ctypes.c_int64),
+                ("r_stab", ctypes.c_int32), ("r_lora", ctypes.c_int32),
+                ("w_codes", ctypes.c_void_p), ("w_scales", ctypes.c_void_p),
+                ("L1", ctypes.c_void_p), ("L2", ctypes.c_void_p),
+                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """Load libfourtune.so once; fail loudly if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m bit_quantized_amd.build`")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        L.fourtune_quantize.argtypes = [st, vp, i64, i64, i64, vp, vp, vp, vp, vp]
+        L.fourtune_quantize.restype = st
+        L.fourtune_workspace_bytes.argtypes = [ctypes.POINTER(FtLinear), st]
+        L.fourtune_workspace_bytes.restype = ctypes.c_size_t
+        L.fourtune_linear_fwd.argtypes = [ctypes.POINTER(FtLinear), vp, vp, vp, vp, vp, vp,
+                                          ctypes.c_size_t, vp]
+        L.fourtune_linear_fwd.restype = st
+        L.fourtune_linear_bwd.argtypes = [ctypes.POINTER(FtLinear), vp, vp, vp, vp, vp, vp, st,
+                                          vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.fourtune_linear_bwd.restype = st
+        L.fourtune_status_string.argtypes = [st]
+        L.fourtune_status_string.restype = ctypes.c_char_p
+        L.fourtune_timing_enable.argtypes = [st]
+        L.fourtune_timing_enable.restype = None
+        L.fourtune_timing_reset.argtypes = []
+        L.fourtune_timing_reset.restype = None
+        L.fourtune_timing_read.argtypes = [ctypes.POINTER(ctypes.c_char_p),
+                                           ctypes.POINTER(ctypes.c_double),
+                                           ctypes.POINTER(ctypes.c_int64), st]
+        L.fourtune_timing_read.restype = st
+        _lib = L
+    return _lib
+
+
+def status_string(s: int) -> str:
+    return lib().fourtune_status_string(int(s)).decode()
+
+
+fourtune_status_string = status_string
+
+
+def _ptr(t) -> int | None:
+    """Device address of a tensor, an int address, or None."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> int | None:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _check(status: int, where: str):
+    if status != FT_OK:
+        raise FourTuneError(status, where)
+
+
+def make_linear(M, K, N, r_stab, r_lora, w_codes, w_scales, L1=None, L2=None, A=None,
+                B=None) -> FtLinear:
+    """Fill the ft_linear descriptor from tensors (device) or raw addresses."""
+    return FtLinear(int(M), int(K), int(N), int(r_stab), int(r_lora), _ptr(w_codes),
+                    _ptr(w_scales), _ptr(L1), _ptr(L2), _ptr(A), _ptr(B))
+
+
+def fourtune_quantize(mode, x, rows, cols, ld, codes, scales, codes_t=None, scales_t=None,
+                      stream=None):
+    s = lib().fourtune_quantize(int(mode), _ptr(x), int(rows), int(cols), int(ld), _ptr(codes),
+                                _ptr(scales), _ptr(codes_t), _ptr(scales_t), _stream(stream))
+    _check(s, "fourtune_quantize")
+
+
+def fourtune_workspace_bytes(layer: FtLinear, is_bwd: bool) -> int:
+    return int(lib().fourtune_workspace_bytes(ctypes.byref(layer), int(bool(is_bwd))))
+
+
+def fourtune_linear_fwd(layer: FtLinear, X, Y, U_save, xq_codes, xq_scales, workspace,
+                        ws_bytes, stream=None):
+    s = lib().fourtune_linear_fwd(ctypes.byref(layer), _ptr(X), _ptr(Y), _ptr(U_save),
+                                  _ptr(xq_codes), _ptr(xq_scales), _ptr(workspace),
+                                  int(ws_bytes), _stream(stream))
+    _check(s, "fourtune_linear_fwd")
+
+
+def fourtune_linear_bwd(layer: FtLinear, dY, X, U_save, dX, dA, dB, grad_dtype, P_save,
+                        gq_codes, gq_scales, workspace, ws_bytes, stream=None):
+    s = lib().fourtune_linear_bwd(ctypes.byref(layer), _ptr(dY), _ptr(X), _ptr(U_save),
+                                  _ptr(dX), _ptr(dA), _ptr(dB), int(grad_dtype), _ptr(P_save),
+                                  _ptr(gq_codes), _ptr(gq_scales), _ptr(workspace),
+                                  int(ws_bytes), _stream(stream))
+    _check(s, "fourtune_linear_bwd")
+
+
+def fourtune_timing_enable(on: bool):
+    lib().fourtune_timing_enable(int(bool(on)))
+
+
+def fourtune_timing_reset():
+    lib().fourtune_timing_reset()
+
+
+def fourtune_timing_read() -> dict:
+    """{kernel name: (total ms, launches)} accumulated since the last reset."""
+    L = lib()
+    n = L.fourtune_timing_read(None, None, None, 0)
+    names = (ctypes.c_char_p * max(n, 1))()
+    tot = (ctypes.c_double * max(n, 1))()
+    cnt = (ctypes.c_int64 * max(n, 1))()
+    n = L.fourtune_timing_read(names, tot, cnt, n)
+    return {names[i].decode(): (tot[i], cnt[i]) for i in range(n)}

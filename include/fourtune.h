@@ -1,0 +1,178 @@
+/*
+ * fourtune.h - C ABI of libfourtune.so: FourTune's W4A4G4 triple-branch
+ * linear layer on AMD Instinct MI355X (gfx950).
+ *
+ * Method: FourTune (arXiv 2607.05711).  "3.1 Triple-Branch Hybrid-Precision
+ * Pipeline", Eq. (2): the forward adds a 4-bit product of the quantized
+ * input and the quantized frozen residual weight, a frozen high-precision
+ * low-rank stabilizer L1 L2 and a trainable LoRA adapter A B, all reading
+ * the same input.  "3.2 4-Bit Backward Pass via Block-Quantization", Eq. (3):
+ * the input gradient runs through the same three branches, the 4-bit
+ * backbone with the *same* block-quantized weight read transposed, and only
+ * the adapter receives weight gradients.  "3.3 Kernel Fusion": quantization
+ * and the low-rank down-projections share one read of the input, and the
+ * up-projections are accumulated inside the 4-bit GEMM.
+ *
+ * Number format: MXFP4 (OCP Microscaling v1.0, cited by the paper in "2.3
+ * Model Quantization"): E2M1 elements, one E8M0 power-of-two scale per
+ * block, scale exponent floor(log2(amax)) - 2, round to nearest with ties
+ * to even, saturating at 6.  Blocks are 1x32 along the reduction dimension
+ * for activations and gradients, and 32x32 square tiles (one scale per
+ * tile) for the frozen residual weight.
+ *
+ * Shapes and orientation (weights stored like torch.nn.Linear.weight):
+ *   X   [M, K] bf16      input             dY  [M, N] bf16  incoming gradient
+ *   W_res [N, K]         frozen residual, given as MXFP4 32x32 tiles
+ *   L1  [K, r_stab], L2 [r_stab, N]        frozen stabilizer, bf16
+ *   A   [K, r_lora], B  [r_lora, N]        trainable adapter, bf16
+ *   D = [L1 | A]  [K, R],  V = [L2 ; B]  [R, N],  R = r_stab + r_lora <= 64
+ *
+ *   forward : Y  = deq(Qrow(X)) deq(Qtile(W_res))^T + U V,   U = bf16(X D)
+ *   backward: dX = deq(Qrow(dY)) deq(Qtile(W_res)) + P D^T,  P = bf16(dY V^T)
+ *             dA = X^T P[:, r_stab:]          dB = U[:, r_stab:]^T dY
+ *
+ * Every product accumulates in fp32 and is rounded once to the output type.
+ *
+ * Memory layouts (all row-major, no padding between rows):
+ *   bf16 tensors are arrays of uint16_t bit patterns.
+ *   MXFP4 codes: byte i of a row holds element 2i in its low nibble and
+ *   element 2i+1 in its high nibble; bit 3 of a nibble is the sign.
+ *   Row-block scales [rows, cols/32]; tile scales [rows/32, cols/32]; one
+ *   E8M0 byte each (value 2^(byte-127)).
+ *
+ * Conventions for every entry point:
+ *   - Pointers are device pointers owned by the caller, except the ft_linear
+ *     descriptor itself, which is host memory read during the call only.
+ *   - Work is enqueued on `stream` (a hipStream_t, NULL = default stream);
+ *     the call returns without synchronizing.  The library allocates and
+ *     frees nothing and keeps no pointer after it returns.
+ *   - All checks run on the host before anything is enqueued: a call that
+ *     returns an error has enqueued no work and written no device memory.
+ *   - Device pointers must be 16-byte aligned.  Inputs must be finite; NaN
+ *     or Inf inputs give unspecified (but in-bounds) results.
+ *   - Calls on different streams must use distinct workspaces and outputs.
+ */
+#ifndef FOURTUNE_H
+#define FOURTUNE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  FT_OK = 0,
+  FT_EINVAL = 1,       /* null pointer where one is required, bad enum value   */
+  FT_ESHAPE = 2,       /* size not allowed (K or N not multiple of 32, R > 64)  */
+  FT_EALIGN = 3,       /* device pointer not 16-byte aligned, or bad row stride */
+  FT_EWORKSPACE = 4,   /* workspace smaller than fourtune_workspace_bytes       */
+  FT_EDEVICE = 5,      /* a HIP launch failed                                   */
+  FT_EUNSUPPORTED = 6  /* no GPU of the supported architecture (gfx950)         */
+} ft_status;
+
+typedef enum { FT_BF16 = 0, FT_F32 = 1 } ft_dtype;
+
+typedef enum {
+  FT_Q_ROW32 = 1,    /* 1x32 blocks along each row                                   */
+  FT_Q_ROW32_T = 2,  /* ROW32 of the input and, from the same read, ROW32 of its
+                        transpose                                                     */
+  FT_Q_TILE32 = 4    /* 32x32 square tiles, one scale per tile (weights)             */
+} ft_qmode;
+
+#define FT_MAX_RANK 64
+
+/* One triple-branch linear layer.  Host struct; the pointers in it are device
+ * pointers.  Either rank may be 0 (then its two pointers may be NULL). */
+typedef struct {
+  int64_t M, K, N;            /* tokens, input features, output features            */
+  int32_t r_stab, r_lora;     /* stabilizer and adapter ranks, r_stab + r_lora <= 64 */
+  const uint8_t* w_codes;     /* Qtile(W_res) codes  [N, K/2]                         */
+  const uint8_t* w_scales;    /* Qtile(W_res) scales [N/32, K/32]                     */
+  const uint16_t* L1;         /* bf16 [K, r_stab]  (frozen)                           */
+  const uint16_t* L2;         /* bf16 [r_stab, N]  (frozen)                           */
+  const uint16_t* A;          /* bf16 [K, r_lora]  (trainable)                        */
+  const uint16_t* B;          /* bf16 [r_lora, N]  (trainable)                        */
+} ft_linear;
+
+/* Quantize a bf16 matrix `in` [rows, cols] with row stride ld_in elements.
+ *
+ * Paper: "2.3 Model Quantization" (Round(W/s) with a block scale, MXFP4);
+ * "3.2 4-Bit Backward Pass via Block-Quantization" (square blocks whose
+ * scales stay local, so the weight serves the transposed product as is).
+ *
+ * mode FT_Q_ROW32:   codes [rows, cols/2], scales [rows, cols/32];
+ *                    codes_t and scales_t must be NULL.
+ * mode FT_Q_ROW32_T: as ROW32, plus codes_t [cols, rows/2] and
+ *                    scales_t [cols, rows/32] = ROW32 of in^T; rows % 32 == 0.
+ * mode FT_Q_TILE32:  codes [rows, cols/2], scales [rows/32, cols/32];
+ *                    rows % 32 == 0; codes_t and scales_t must be NULL.
+ * Requirements: cols % 32 == 0, rows >= 0, ld_in >= cols, ld_in % 8 == 0.
+ * rows == 0 is a no-op.
+ * Errors: FT_EINVAL (mode, NULLs), FT_ESHAPE, FT_EALIGN. */
+ft_status fourtune_quantize(int mode, const uint16_t* in, int64_t rows, int64_t cols,
+                            int64_t ld_in, uint8_t* codes, uint8_t* scales,
+                            uint8_t* codes_t, uint8_t* scales_t, void* stream);
+
+/* Bytes of device workspace fwd (is_bwd = 0) or bwd (is_bwd = 1) needs for
+ * layer L (shapes and ranks only are read).  Returns 0 for invalid shapes. */
+size_t fourtune_workspace_bytes(const ft_linear* L, int is_bwd);
+
+/* Forward, Eq. (2), with the fusions of "3.3 Kernel Fusion":
+ *   kernel 1 reads X once and writes Qrow(X) and U = bf16(X D);
+ *   kernel 2 computes deq(Qrow(X)) deq(Qtile(W_res))^T + U V in fp32 and
+ *   writes Y (bf16 [M, N]) once.
+ * U_save  : bf16 [M, R], written; the backward needs it.  May be NULL if R == 0.
+ * xq_codes, xq_scales: optional outputs [M, K/2], [M, K/32]; NULL = keep
+ *   them in the workspace.
+ * workspace: device memory of at least fourtune_workspace_bytes(L, 0) bytes;
+ *   contents on entry are ignored and on return unspecified.
+ * Requirements: M >= 1, K % 32 == 0, N % 32 == 0, R <= 64.
+ * Errors: FT_EINVAL, FT_ESHAPE, FT_EALIGN, FT_EWORKSPACE, FT_EDEVICE. */
+ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y,
+                              uint16_t* U_save, uint8_t* xq_codes, uint8_t* xq_scales,
+                              void* workspace, size_t ws_bytes, void* stream);
+
+/* Backward, Eq. (3) and the adapter gradients of section 3.2:
+ *   kernel 1 reads dY once and writes Qrow(dY) (1x32 blocks along N, the
+ *   reduction dimension of the input gradient) and P = bf16(dY V^T);
+ *   kernel 2 computes deq(Qrow(dY)) deq(Qtile(W_res)) + P D^T, reading the
+ *   same 32x32-tile codes as the forward, transposed on chip, and writes dX
+ *   (bf16 [M, K]) once;
+ *   the adapter gradients dA = X^T P[:, r_stab:] ([K, r_lora]) and
+ *   dB = U[:, r_stab:]^T dY ([r_lora, N]) are written in grad_dtype
+ *   (FT_BF16 or FT_F32).
+ * X and U_save are the forward's input and saved U.  dX may be NULL (no
+ * input gradient).  dA, dB may be NULL only when r_lora == 0.
+ * P_save : optional bf16 [M, R] output of P; NULL = workspace only.
+ * gq_codes, gq_scales: optional outputs [M, N/2], [M, N/32].
+ * workspace: at least fourtune_workspace_bytes(L, 1) bytes.
+ * No gradient is produced for W_res, L1 or L2 (frozen).
+ * Errors: FT_EINVAL, FT_ESHAPE, FT_EALIGN, FT_EWORKSPACE, FT_EDEVICE. */
+ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint16_t* X,
+                              const uint16_t* U_save, uint16_t* dX, void* dA, void* dB,
+                              ft_dtype grad_dtype, uint16_t* P_save, uint8_t* gq_codes,
+                              uint8_t* gq_scales, void* workspace, size_t ws_bytes,
+                              void* stream);
+
+/* Static, human-readable text for a status code. */
+const char* fourtune_status_string(ft_status s);
+
+/* Per-kernel timing for benchmarks (process-wide, off by default).  While
+ * enabled, every kernel the entry points above enqueue is bracketed by two
+ * hipEvents recorded on the call's stream; the events come from a pool the
+ * library creates on first use and keeps.  fourtune_timing_read waits for the
+ * recorded events, adds their elapsed times per kernel name and returns the
+ * number of distinct kernels; it fills up to max_entries entries of names
+ * (static strings owned by the library), total_ms and counts (any of the
+ * three may be NULL).  fourtune_timing_reset clears the totals. */
+void fourtune_timing_enable(int on);
+void fourtune_timing_reset(void);
+int fourtune_timing_read(const char** names, double* total_ms, int64_t* counts, int max_entries);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FOURTUNE_H */

@@ -96,7 +96,9 @@ def e2m1_encode(t: np.ndarray) -> np.ndarray:
     of t (so -0.0 gives 0x8).
     """
     t = np.asarray(t, dtype=np.float64)
-    a = np.abs(t).reshape(-1)
+    # Every |t| >= 7 has 6 as its nearest point; clipping at 8 keeps that
+    # while keeping the distances below exact in float64 for huge inputs.
+    a = np.minimum(np.abs(t), 8.0).reshape(-1)
     dist = np.abs(a[:, None] - E2M1_MAGNITUDES[None, :])       # [n, 8]
     best = np.argmin(dist, axis=1)                              # lowest index on ties
     dmin = dist[np.arange(a.size), best]

@@ -1,0 +1,156 @@
+"""Helpers for the GPU parity tests: upload a synthetic case, run the layer
+through the C ABI, and compare with the CPU oracle."""
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from bit_quantized_amd import ops
+from bit_quantized_amd.layer import QuantizedLinear, bf16_tensor, bits_of
+from oracle import linear as OL
+from oracle import mxfp4 as OQ
+
+DEV = torch.device("cuda:0")
+REL_TOL = 1e-3          # relative Frobenius bar for Y, dX, dA, dB
+BIT_AGREE = 0.999       # fraction of identical bf16 bits required of U and P
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def require_gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    ops.lib()  # fail loudly when the library is missing
+
+
+def up(bits):
+    return bf16_tensor(bits, DEV)
+
+
+def u8(t):
+    return t.detach().cpu().numpy()
+
+
+class GpuCase:
+    """A LinearCase resident on the device with its quantized weight."""
+
+    def __init__(self, case):
+        self.c = case
+        self.X = up(case.X)
+        self.dY = up(case.dY)
+        W = up(case.W_res)
+        opt = lambda a: up(a) if a.size else None
+        self.layer = QuantizedLinear(W, opt(case.L1) if case.r_s else None,
+                                     opt(case.L2) if case.r_s else None,
+                                     opt(case.A) if case.r_l else None,
+                                     opt(case.B) if case.r_l else None)
+        del W
+
+    def run(self, grad_f32=False):
+        Y, U, xc, xs = self.layer.forward(self.X, want_codes=True)
+        dX, dA, dB, P, gc, gs = self.layer.backward(self.dY, self.X, U, grad_f32=grad_f32,
+                                                    want_codes=True)
+        torch.cuda.synchronize()
+        out = dict(Y=bits_of(Y), U=bits_of(U)[:, :self.c.R] if self.c.R else None,
+                   xq_codes=u8(xc), xq_scales=u8(xs), dX=bits_of(dX),
+                   P=bits_of(P)[:, :self.c.R] if self.c.R else None, gq_codes=u8(gc),
+                   gq_scales=u8(gs), w_codes=u8(self.layer.w_codes),
+                   w_scales=u8(self.layer.w_scales))
+        if self.c.r_l:
+            if grad_f32:
+                out["dA"] = dA.cpu().numpy()
+                out["dB"] = dB.cpu().numpy()
+            else:
+                out["dA"] = bits_of(dA)
+                out["dB"] = bits_of(dB)
+        return out
+
+
+def bit_agreement(a, b):
+    if a is None or a.size == 0:
+        return 1.0
+    return float(np.mean(a == b))
+
+
+def check_full(case, got, grad_f32=False):
+    """Full-size oracle comparison for cases the oracle finishes in seconds."""
+    c = case
+    wc, ws = OQ.quantize_tile32(c.W_res)
+    np.testing.assert_array_equal(got["w_codes"], wc)
+    np.testing.assert_array_equal(got["w_scales"], ws)
+    f = OL.linear_fwd(c.X, wc, ws, c.L1, c.L2, c.A, c.B)
+    b = OL.linear_bwd(c.dY, c.X, f["U"], wc, ws, c.L1, c.L2, c.A, c.B,
+                      grad_dtype="f32" if grad_f32 else "bf16")
+    np.testing.assert_array_equal(got["xq_codes"], f["xq_codes"])
+    np.testing.assert_array_equal(got["xq_scales"], f["xq_scales"])
+    np.testing.assert_array_equal(got["gq_codes"], b["gq_codes"])
+    np.testing.assert_array_equal(got["gq_scales"], b["gq_scales"])
+    res = {}
+    if c.R:
+        res["U_bits"] = bit_agreement(got["U"], f["U"])
+        res["P_bits"] = bit_agreement(got["P"], b["P"])
+        res["U"] = OL.rel_frobenius(got["U"], f["U"])
+        res["P"] = OL.rel_frobenius(got["P"], b["P"])
+    res["Y"] = OL.rel_frobenius(got["Y"], f["Y"])
+    res["dX"] = OL.rel_frobenius(got["dX"], b["dX"])
+    if c.r_l:
+        res["dA"] = OL.rel_frobenius(got["dA"], b["dA"])
+        res["dB"] = OL.rel_frobenius(got["dB"], b["dB"])
+    say(c.name, {k: (round(v, 7) if isinstance(v, float) else v) for k, v in res.items()})
+    for k in ("Y", "dX", "dA", "dB"):
+        if k in res:
+            assert res[k] <= REL_TOL, (k, res[k])
+    for k in ("U_bits", "P_bits"):
+        if k in res:
+            assert res[k] >= BIT_AGREE, (k, res[k])
+    for k in ("U", "P"):
+        if k in res:
+            assert res[k] <= REL_TOL, (k, res[k])
+    return res
+
+
+def check_sampled(case, got, rows):
+    """Large cases: outputs of sampled rows, and the adapter gradients in full."""
+    c = case
+    wc, ws = OQ.quantize_tile32(c.W_res)
+    np.testing.assert_array_equal(got["w_codes"], wc)
+    np.testing.assert_array_equal(got["w_scales"], ws)
+    xc, xs = OQ.quantize_row32(c.X[rows])
+    np.testing.assert_array_equal(got["xq_codes"][rows], xc)
+    np.testing.assert_array_equal(got["xq_scales"][rows], xs)
+    gc, gs = OQ.quantize_row32(c.dY[rows])
+    np.testing.assert_array_equal(got["gq_codes"][rows], gc)
+    np.testing.assert_array_equal(got["gq_scales"][rows], gs)
+    Y, U = OL.linear_fwd_rows(rows, c.X, wc, ws, c.L1, c.L2, c.A, c.B)
+    dX, P = OL.linear_bwd_rows(rows, c.dY, wc, ws, c.L1, c.L2, c.A, c.B)
+    res = {"Y": OL.rel_frobenius(got["Y"][rows], OQ.f64_to_bf16_bits(Y)),
+           "dX": OL.rel_frobenius(got["dX"][rows], OQ.f64_to_bf16_bits(dX))}
+    if c.R:
+        # the rank-R down-projections are cheap: check them over all tokens
+        D = OL.stack_down(c.L1, c.A)
+        V = OL.stack_up(c.L2, c.B)
+        Uf = OL.down_proj(c.X, D)
+        Pf = OL.down_proj(c.dY, V.T)
+        np.testing.assert_array_equal(Uf[rows], U)
+        np.testing.assert_array_equal(Pf[rows], P)
+        res["U_bits"] = bit_agreement(got["U"], Uf)
+        res["P_bits"] = bit_agreement(got["P"], Pf)
+        res["U"] = OL.rel_frobenius(got["U"], Uf)
+        res["P"] = OL.rel_frobenius(got["P"], Pf)
+    if c.r_l:
+        dA = OQ.bf16_bits_to_f64(c.X).T @ OQ.bf16_bits_to_f64(Pf)[:, c.r_s:]
+        dB = OQ.bf16_bits_to_f64(Uf)[:, c.r_s:].T @ OQ.bf16_bits_to_f64(c.dY)
+        res["dA"] = OL.rel_frobenius(got["dA"], OQ.f64_to_bf16_bits(dA))
+        res["dB"] = OL.rel_frobenius(got["dB"], OQ.f64_to_bf16_bits(dB))
+    say(c.name, {k: round(v, 7) for k, v in res.items()})
+    for k in ("Y", "dX", "dA", "dB", "U", "P"):
+        if k in res:
+            assert res[k] <= REL_TOL, (k, res[k])
+    for k in ("U_bits", "P_bits"):
+        if k in res:
+            assert res[k] >= BIT_AGREE, (k, res[k])
+    return res

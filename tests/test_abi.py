@@ -1,0 +1,119 @@
+"""C-ABI checks that need no GPU: the library loads, exports every function
+include/fourtune.h declares, and rejects bad arguments on the host before
+touching any device memory (fake addresses are never dereferenced)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from bit_quantized_amd import ops
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "fourtune.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(ops.LIB_PATH),
+                                reason="libfourtune.so not built")
+
+A16 = 0x10000000  # a fake 16-byte-aligned device address
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(fourtune_\w+)\s*\(", text)))
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert set(names) == set(ops.EXPORTS)
+    L = ops.lib()
+    for n in names:
+        assert getattr(L, n) is not None
+
+
+def test_status_strings():
+    for s in range(7):
+        assert ops.status_string(s)
+    assert ops.status_string(99) == "unknown status"
+
+
+def _q(mode, x=A16, rows=64, cols=64, ld=64, c=A16, s=A16, ct=None, st=None):
+    return ops.lib().fourtune_quantize(mode, x, rows, cols, ld, c, s, ct, st, None)
+
+
+def test_quantize_argument_errors():
+    assert _q(3) == ops.FT_EINVAL
+    assert _q(ops.FT_Q_ROW32, x=None) == ops.FT_EINVAL
+    assert _q(ops.FT_Q_ROW32, ct=A16, st=A16) == ops.FT_EINVAL
+    assert _q(ops.FT_Q_ROW32_T) == ops.FT_EINVAL          # transposed outputs missing
+    assert _q(ops.FT_Q_ROW32, cols=48, ld=48) == ops.FT_ESHAPE
+    assert _q(ops.FT_Q_TILE32, rows=40) == ops.FT_ESHAPE
+    assert _q(ops.FT_Q_ROW32_T, rows=40, ct=A16, st=A16) == ops.FT_ESHAPE
+    assert _q(ops.FT_Q_ROW32, rows=-1) == ops.FT_ESHAPE
+    assert _q(ops.FT_Q_ROW32, ld=32) == ops.FT_EALIGN     # ld < cols
+    assert _q(ops.FT_Q_ROW32, ld=68) == ops.FT_EALIGN     # ld not a multiple of 8
+    assert _q(ops.FT_Q_ROW32, x=A16 + 2) == ops.FT_EALIGN
+    assert _q(ops.FT_Q_ROW32, rows=0) == ops.FT_OK        # empty is a no-op
+
+
+def _layer(M=64, K=64, N=64, rs=8, rl=8, **kw):
+    d = dict(w_codes=A16, w_scales=A16, L1=A16, L2=A16, A=A16, B=A16)
+    d.update(kw)
+    return ops.make_linear(M, K, N, rs, rl, **d)
+
+
+def _fwd(L, X=A16, Y=A16, U=A16, qc=None, qs=None, ws=A16, wsb=1 << 40):
+    return ops.lib().fourtune_linear_fwd(ctypes.byref(L), X, Y, U, qc, qs, ws, wsb, None)
+
+
+def _bwd(L, dY=A16, X=A16, U=A16, dX=A16, dA=A16, dB=A16, gdt=0, P=None, qc=None, qs=None,
+         ws=A16, wsb=1 << 40):
+    return ops.lib().fourtune_linear_bwd(ctypes.byref(L), dY, X, U, dX, dA, dB, gdt, P, qc, qs,
+                                         ws, wsb, None)
+
+
+def test_linear_shape_errors():
+    for L in (_layer(M=0), _layer(K=48), _layer(N=40), _layer(K=0), _layer(rs=40, rl=30),
+              _layer(rs=-1)):
+        assert _fwd(L) == ops.FT_ESHAPE
+        assert _bwd(L) == ops.FT_ESHAPE
+    assert ops.lib().fourtune_linear_fwd(None, A16, A16, A16, None, None, A16, 1, None) == ops.FT_EINVAL
+
+
+def test_linear_pointer_errors():
+    assert _fwd(_layer(w_codes=None)) == ops.FT_EINVAL
+    assert _fwd(_layer(L1=None)) == ops.FT_EINVAL
+    assert _fwd(_layer(B=None)) == ops.FT_EINVAL
+    assert _fwd(_layer(), X=None) == ops.FT_EINVAL
+    assert _fwd(_layer(), U=None) == ops.FT_EINVAL
+    assert _fwd(_layer(), qc=A16) == ops.FT_EINVAL              # codes without scales
+    assert _fwd(_layer(), X=A16 + 8) == ops.FT_EALIGN
+    assert _fwd(_layer(A=A16 + 4)) == ops.FT_EALIGN
+    assert _bwd(_layer(), dY=None) == ops.FT_EINVAL
+    assert _bwd(_layer(), dA=None) == ops.FT_EINVAL
+    assert _bwd(_layer(), gdt=7) == ops.FT_EINVAL
+    assert _bwd(_layer(), dX=A16 + 2) == ops.FT_EALIGN
+    # ranks zero: no low-rank pointers are needed
+    L0 = _layer(rs=0, rl=0, L1=None, L2=None, A=None, B=None)
+    assert _fwd(L0, U=None, wsb=0) == ops.FT_EWORKSPACE
+
+
+def test_workspace_size_checked_before_launch():
+    L = _layer(M=300, K=288, N=544)
+    need_f = ops.fourtune_workspace_bytes(L, False)
+    need_b = ops.fourtune_workspace_bytes(L, True)
+    assert need_f >= 300 * 288 // 2 + 300 * 288 // 32
+    assert need_b >= 300 * 544 // 2 + 300 * 544 // 32 + 300 * 16 * 2
+    assert _fwd(L, wsb=need_f - 1) == ops.FT_EWORKSPACE
+    assert _bwd(L, wsb=need_b - 1) == ops.FT_EWORKSPACE
+    assert _fwd(L, ws=None, wsb=need_f) == ops.FT_EINVAL
+    assert ops.fourtune_workspace_bytes(_layer(K=40), False) == 0
+
+
+def test_valid_call_without_gpu_reports_unsupported():
+    # With no GPU present the first HIP query fails; the call must say so
+    # instead of launching anything.
+    import torch
+    if torch.cuda.is_available():
+        pytest.skip("a GPU is present")
+    assert _fwd(_layer()) == ops.FT_EUNSUPPORTED

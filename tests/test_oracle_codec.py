@@ -62,7 +62,7 @@ def test_encode_equals_threshold_rule_on_fine_grid_and_ties():
     fine = np.arange(0, 12 * 256 + 1) / 256.0           # 0 .. 12 in 1/256 steps
     mids = np.array([0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0])
     near = np.concatenate([mids, np.nextafter(mids, 0), np.nextafter(mids, 10)])
-    vals = np.concatenate([fine, near, [1e-30, 6.0, 7.999, 1e6]])
+    vals = np.concatenate([fine, near, [1e-30, 6.0, 7.999, 1e6, 7.26e16, 3e300]])
     vals = np.concatenate([vals, -vals])
     np.testing.assert_array_equal(q.e2m1_encode(vals), _threshold_encode(vals))
 
