@@ -71,10 +71,9 @@ def layer_work(M, K, N, rs, rl):
                            "bytes": M * N // 2 + M * N // 32 + N * K // 2 + N * K // 1024
                            + 2 * M * R + 2 * R * K + 2 * M * K,
                            "bound": "mfma"},
-        "bwd_lora_dA": {"flop": 2 * M * K * rl, "bytes": 2 * M * K + 2 * M * R + 2 * K * rl,
-                        "bound": "hbm"},
-        "bwd_lora_dB": {"flop": 2 * M * N * rl, "bytes": 2 * M * N + 2 * M * R + 2 * N * rl,
-                        "bound": "hbm"},
+        "bwd_lora_grads": {"flop": 2 * M * (K + N) * rl,
+                           "bytes": 2 * M * K + 2 * M * N + 4 * M * R + 2 * (K + N) * rl,
+                           "bound": "hbm"},
     }
     return w
 

@@ -5,8 +5,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
+#include <chrono>
 #include <cstring>
-#include <map>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -19,6 +20,19 @@ constexpr size_t kAlign = 256;
 inline size_t align_up(size_t x) { return (x + kAlign - 1) & ~(kAlign - 1); }
 inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 constexpr int64_t kMaxDim = int64_t(1) << 30;
+// Kernels address tensors with 32-bit buffer offsets.
+constexpr int64_t kMaxBytes = (int64_t(1) << 31) - 1;
+
+// Per-call tag for the workspace arrival counters of split reductions.  A
+// process-wide counter started at a time-derived value, so counters left in
+// a reused workspace by an earlier call or process never match.
+std::atomic<uint32_t> g_epoch{static_cast<uint32_t>(
+    std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761ull)};
+uint32_t next_epoch() {
+  uint32_t e;
+  do { e = g_epoch.fetch_add(1) + 1; } while (e == 0);
+  return e;
+}
 
 // 1 = current device is gfx950, 0 = not, -1 = unknown yet.  Cached per device.
 int g_arch_ok[64];
@@ -113,6 +127,8 @@ ft_status check_linear(const ft_linear* L) {
   if (L->M < 1 || L->K < 32 || L->N < 32) return FT_ESHAPE;
   if (L->M > kMaxDim || L->K > kMaxDim || L->N > kMaxDim) return FT_ESHAPE;
   if ((L->K & 31) || (L->N & 31)) return FT_ESHAPE;
+  if (L->M * L->K * 2 > kMaxBytes || L->M * L->N * 2 > kMaxBytes || L->N * L->K / 2 > kMaxBytes)
+    return FT_ESHAPE;
   if (L->r_stab < 0 || L->r_lora < 0 || L->r_stab + L->r_lora > FT_MAX_RANK) return FT_ESHAPE;
   if (!L->w_codes || !L->w_scales) return FT_EINVAL;
   if (L->r_stab > 0 && (!L->L1 || !L->L2)) return FT_EINVAL;
@@ -196,6 +212,7 @@ ft_status fourtune_quantize(int mode, const uint16_t* in, int64_t rows, int64_t 
     return FT_EINVAL;
   }
   if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return FT_ESHAPE;
+  if (rows * ld_in * 2 > kMaxBytes) return FT_ESHAPE;
   if (cols & 31) return FT_ESHAPE;
   if (mode != FT_Q_ROW32 && (rows & 31)) return FT_ESHAPE;
   if (ld_in < cols || (ld_in & 7)) return FT_EALIGN;
@@ -252,7 +269,7 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
     if (R > 0)
       e = ft::launch_quant_down(X, L->M, L->K, L->K, qc, qs, pieces_D(L), U_save,
                                 reinterpret_cast<float*>(ws + lay.part),
-                                reinterpret_cast<uint32_t*>(ws + lay.cnt), st);
+                                reinterpret_cast<unsigned long long*>(ws + lay.cnt), next_epoch(), st);
     else
       e = ft::launch_quant_row32(X, L->M, L->K, L->K, qc, qs, st);
     tm.done(e);
@@ -298,7 +315,7 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
     if (R > 0)
       e = ft::launch_quant_down(dY, L->M, L->N, L->N, qc, qs, pieces_Vt(L), P,
                                 reinterpret_cast<float*>(ws + lay.part),
-                                reinterpret_cast<uint32_t*>(ws + lay.cnt), st);
+                                reinterpret_cast<unsigned long long*>(ws + lay.cnt), next_epoch(), st);
     else
       e = ft::launch_quant_row32(dY, L->M, L->N, L->N, qc, qs, st);
     tm.done(e);
@@ -315,22 +332,20 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
   }
   if (rl > 0) {
     const int f32 = grad_dtype == FT_F32 ? 1 : 0;
+    const uint32_t epoch = next_epoch();
     ft::LoraGradArgs a{};
     a.M = L->M; a.I = L->K; a.big = X; a.small = P; a.ld_small = R; a.r0 = L->r_stab; a.rl = rl;
     a.out = dA; a.out_f32 = f32; a.transpose_out = 0;
     a.part = reinterpret_cast<float*>(ws + lay.dA_part);
-    a.cnt = reinterpret_cast<uint32_t*>(ws + lay.dA_cnt);
-    {
-      Timed tm("bwd_lora_dA", st);
-      if (tm.done(ft::launch_lora_grad(a, st)) != hipSuccess) return FT_EDEVICE;
-    }
-    ft::LoraGradArgs b{};
-    b.M = L->M; b.I = L->N; b.big = dY; b.small = U_save; b.ld_small = R; b.r0 = L->r_stab; b.rl = rl;
-    b.out = dB; b.out_f32 = f32; b.transpose_out = 1;
+    a.cnt = reinterpret_cast<unsigned long long*>(ws + lay.dA_cnt);
+    a.epoch = epoch;
+    ft::LoraGradArgs b = a;
+    b.I = L->N; b.big = dY; b.small = U_save;
+    b.out = dB; b.transpose_out = 1;
     b.part = reinterpret_cast<float*>(ws + lay.dB_part);
-    b.cnt = reinterpret_cast<uint32_t*>(ws + lay.dB_cnt);
-    Timed tm("bwd_lora_dB", st);
-    if (tm.done(ft::launch_lora_grad(b, st)) != hipSuccess) return FT_EDEVICE;
+    b.cnt = reinterpret_cast<unsigned long long*>(ws + lay.dB_cnt);
+    Timed tm("bwd_lora_grads", st);
+    if (tm.done(ft::launch_lora_grads(a, b, st)) != hipSuccess) return FT_EDEVICE;
   }
   return FT_OK;
 }

@@ -27,9 +27,12 @@ hipError_t launch_quant_tile32(const uint16_t* in, int64_t rows, int64_t cols, i
 hipError_t launch_quant_row32_t(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
                                 uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
                                 uint8_t* scales_t, hipStream_t st);
+// Row quantization fused with the down-projection; `cnt` is a workspace array
+// of 64-bit arrival slots (any contents), `epoch` a value unique to this call.
 hipError_t launch_quant_down(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
                              uint8_t* codes, uint8_t* scales, const LowRankPieces& pr,
-                             uint16_t* out_lr, float* part, uint32_t* cnt, hipStream_t st);
+                             uint16_t* out_lr, float* part, unsigned long long* cnt,
+                             uint32_t epoch, hipStream_t st);
 size_t quant_down_part_bytes(int64_t rows, int64_t cols, int R);
 size_t quant_down_cnt_bytes(int64_t rows);
 
@@ -62,9 +65,11 @@ struct LoraGradArgs {
   int out_f32;                    // 0 bf16, 1 fp32
   int transpose_out;
   float* part;                    // workspace partials
-  uint32_t* cnt;                  // workspace counters (zeroed by the launcher)
+  unsigned long long* cnt;        // workspace arrival slots (any contents)
+  uint32_t epoch;                 // unique to this call
 };
-hipError_t launch_lora_grad(const LoraGradArgs& a, hipStream_t st);
+// dA and dB of one backward in a single launch (both problems in one grid).
+hipError_t launch_lora_grads(const LoraGradArgs& dA, const LoraGradArgs& dB, hipStream_t st);
 size_t lora_grad_part_bytes(int64_t M, int64_t I, int rl);
 size_t lora_grad_cnt_bytes(int64_t I);
 

@@ -180,69 +180,146 @@ __global__ __launch_bounds__(256) void k_quant_row32_t(const uint16_t* __restric
 // out_lr[row][r] = bf16( sum_c in[row][c] * proj(c, r) ),  r < R,
 // proj(c, r) = r < r0 ? p0[c*s0c + r*s0r] : p1[c*s1c + (r-r0)*s1r].
 //
-// Workgroup: 4 waves x 16 rows = 64 rows; blockIdx.y selects a column range
-// of `kc` columns (multiple of 128).  Per 128-column step a lane owns one
-// 1x32 block of its row (row = l%16, block = l/16): it quantizes the block
-// and feeds the same 32 values to four 16x16x32 bf16 MFMAs, in the
-// reduction order (block, 8-element group, element); the projection slice
-// is staged in LDS transposed and read with the same order.
-template <int NRG>
-__global__ __launch_bounds__(256) void k_quant_down(
-    const uint16_t* __restrict__ in, uint32_t rows, uint32_t cols, int64_t ld,
-    uint8_t* __restrict__ codes, uint8_t* __restrict__ scales, const uint16_t* __restrict__ p0,
-    int64_t s0c, int64_t s0r, int r0, const uint16_t* __restrict__ p1, int64_t s1c, int64_t s1r,
-    int R, uint16_t* __restrict__ out_lr, float* __restrict__ part, uint32_t* __restrict__ cnt,
-    uint32_t kc) {
-  constexpr int RP = NRG * 16;      // padded rank
-  constexpr int PT = 128 + 8;       // LDS pitch (bf16) of the staged projection
+// Workgroup: 4 waves x 16 rows = 64 rows and KC = 128*NS columns.  Every
+// global load of the workgroup is issued up front: the lane's NS blocks of
+// 32 input values (one block per 128-column step: row = l%16, block l/16)
+// and the projection slice, which goes to LDS transposed (rank-major, the
+// column index contiguous).  Per step the lane quantizes its block and
+// feeds the same 32 values to four 16x16x32 bf16 MFMAs in the reduction
+// order (block, 8-element group, element), reading the projection in the
+// same order.  With more than one column range per row block, each
+// workgroup stores fp32 partials and the last one to arrive sums them in
+// range order (deterministic) and rounds once.
+struct QDArgs {
+  const uint16_t* in;
+  uint32_t rows, cols;
+  int64_t ld;
+  uint8_t* codes;
+  uint8_t* scales;
+  LowRankPieces pr;
+  int R;
+  uint16_t* out_lr;
+  float* part;
+  unsigned long long* cnt;
+  uint32_t epoch;
+};
+
+template <int NRG, int NS>
+__global__ __launch_bounds__(256) void k_quant_down(const QDArgs a) {
+  constexpr int RP = NRG * 16;          // padded rank
+  constexpr int KC = 128 * NS;          // columns of this workgroup
+  constexpr int PT = KC + 8;            // LDS pitch (bf16) of the staged projection
   __shared__ __attribute__((aligned(16))) uint16_t pt[RP * PT];
   __shared__ int s_last;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int g = lane >> 4, lr = lane & 15;
+  const uint32_t rows = a.rows, cols = a.cols;
   const uint32_t m0 = blockIdx.x * 64;
   const uint32_t row = m0 + wave * 16 + lr;
-  const uint32_t cbeg = blockIdx.y * kc;
-  const uint32_t cend = min(cols, cbeg + kc);
+  const uint32_t cbeg = blockIdx.y * KC;
+  const int R = a.R;
+  const LowRankPieces& p = a.pr;
+
+  // ---- issue the input loads of all steps
+  const auto rin = make_rsrc(a.in, static_cast<uint64_t>(rows) * a.ld * 2);
+  u32x4 v[NS][4];
+#pragma unroll
+  for (int s = 0; s < NS; ++s) {
+    const uint32_t cb = cbeg + 128 * s + 32 * g;
+    const uint32_t off = cb < cols ? static_cast<uint32_t>((row * a.ld + cb) * 2) : BUF_OOB;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[s][i] = buf_load128(rin, off == BUF_OOB ? off : off + 16 * i);
+  }
+
+  // ---- stage the projection slice: pt[r][c - cbeg] = proj(c, r)
+  // column-contiguous rank rows (V^T) give 8 columns per 16-byte load;
+  // rank-contiguous rows (D) give 8 ranks when both ranks are multiples of 8
+  const bool col_fast = p.s0c == 1 && p.s1c == 1 && (p.r0 == 0 || (p.s0r & 7) == 0) &&
+                        (p.r1 == 0 || (p.s1r & 7) == 0);
+  if (col_fast || ((p.r0 & 7) == 0 && (p.r1 & 7) == 0)) {
+    const auto r0s = make_rsrc(p.p0, piece_bytes(p.s0c, p.s0r, p.r0, cols));
+    const auto r1s = make_rsrc(p.p1, piece_bytes(p.s1c, p.s1r, p.r1, cols));
+    constexpr int CH = RP * KC / 8;      // 16-byte chunks of the padded slice
+    constexpr int PER = (CH + 255) / 256;
+    u32x4 w[PER];
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int c = t + 256 * e;
+      uint32_t off0 = BUF_OOB, off1 = BUF_OOB;
+      if (c < CH) {
+        if (col_fast) {                   // 8 consecutive columns of rank row r
+          const int r = c / (KC / 8), cc = (c % (KC / 8)) * 8;
+          const uint32_t col = cbeg + cc;
+          if (col < cols && r < R) {
+            if (r < p.r0) off0 = static_cast<uint32_t>((r * p.s0r + col) * 2);
+            else off1 = static_cast<uint32_t>(((r - p.r0) * p.s1r + col) * 2);
+          }
+        } else {                          // 8 consecutive ranks of column cc
+          const int rc = c / KC, cc = c % KC;
+          const uint32_t col = cbeg + cc;
+          if (col < cols && 8 * rc < R) {
+            if (8 * rc < p.r0) off0 = static_cast<uint32_t>((col * p.s0c + 8 * rc) * 2);
+            else off1 = static_cast<uint32_t>((col * p.s1c + 8 * rc - p.r0) * 2);
+          }
+        }
+      }
+      w[e] = off0 != BUF_OOB ? buf_load128(r0s, off0) : buf_load128(r1s, off1);
+    }
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int c = t + 256 * e;
+      if (c >= CH) continue;
+      if (col_fast) {
+        const int r = c / (KC / 8), cc = (c % (KC / 8)) * 8;
+        *reinterpret_cast<u32x4*>(&pt[r * PT + cc]) = w[e];
+      } else {
+        const int rc = c / KC, cc = c % KC;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          pt[(8 * rc + 2 * k) * PT + cc] = static_cast<uint16_t>(w[e][k]);
+          pt[(8 * rc + 2 * k + 1) * PT + cc] = static_cast<uint16_t>(w[e][k] >> 16);
+        }
+      }
+    }
+  } else {
+    for (int idx = t; idx < RP * KC; idx += 256) {
+      const int r = idx / KC, cc = idx % KC;
+      const uint32_t c = cbeg + cc;
+      uint16_t val = 0;
+      if (c < cols && r < R)
+        val = r < p.r0 ? p.p0[c * p.s0c + r * p.s0r] : p.p1[c * p.s1c + (r - p.r0) * p.s1r];
+      pt[r * PT + cc] = val;
+    }
+  }
+  __syncthreads();
+
+  // ---- quantize + down-project, one 128-column step at a time
   f32x4 acc[NRG];
 #pragma unroll
   for (int c = 0; c < NRG; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  for (uint32_t c0 = cbeg; c0 < cend; c0 += 128) {
-    __syncthreads();
-    for (int idx = t; idx < RP * 128; idx += 256) {
-      const int r = idx >> 7, cc = idx & 127;
-      const uint32_t c = c0 + cc;
-      uint16_t v = 0;
-      if (c < cend && r < R)
-        v = r < r0 ? p0[c * s0c + r * s0r] : p1[c * s1c + (r - r0) * s1r];
-      pt[r * PT + cc] = v;
-    }
-    __syncthreads();
-    const uint32_t cb = c0 + 32 * g;
-    u32x4 v[4] = {{0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}, {0, 0, 0, 0}};
-    if (row < rows && cb < cend) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(in + row * ld + cb);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v[i] = __builtin_nontemporal_load(src + i);
+  for (int s = 0; s < NS; ++s) {
+    const uint32_t cb = cbeg + 128 * s + 32 * g;
+    if (row < rows && cb < cols) {
       uint32_t m = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j) m = max_u16x2(m, abs_bf16x2(v[i][j]));
-      const uint32_t s = e8m0_from_amax_bits(hmax_u16x2(m));
-      const float sc = e8m0_to_f32(s);
+        for (int j = 0; j < 4; ++j) m = max_u16x2(m, abs_bf16x2(v[s][i][j]));
+      const uint32_t sc8 = e8m0_from_amax_bits(hmax_u16x2(m));
+      const float sc = e8m0_to_f32(sc8);
       u32x4 o;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = encode8(v[i][0], v[i][1], v[i][2], v[i][3], sc);
-      *reinterpret_cast<u32x4*>(codes + static_cast<uint64_t>(row) * (cols >> 1) + (cb >> 1)) = o;
-      scales[static_cast<uint64_t>(row) * (cols >> 5) + (cb >> 5)] = static_cast<uint8_t>(s);
+      for (int i = 0; i < 4; ++i) o[i] = encode8(v[s][i][0], v[s][i][1], v[s][i][2], v[s][i][3], sc);
+      *reinterpret_cast<u32x4*>(a.codes + static_cast<uint64_t>(row) * (cols >> 1) + (cb >> 1)) = o;
+      a.scales[static_cast<uint64_t>(row) * (cols >> 5) + (cb >> 5)] = static_cast<uint8_t>(sc8);
     }
 #pragma unroll
     for (int c = 0; c < NRG; ++c)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const u32x4 b = lds_read_b128(&pt[(16 * c + lr) * PT + 32 * g + 8 * i]);
-        acc[c] = mfma_bf16_16x16x32(v[i], b, acc[c]);
+        const u32x4 b = lds_read_b128(&pt[(16 * c + lr) * PT + 128 * s + 32 * g + 8 * i]);
+        acc[c] = mfma_bf16_16x16x32(v[s][i], b, acc[c]);
       }
   }
 
@@ -254,45 +331,35 @@ __global__ __launch_bounds__(256) void k_quant_down(
       for (int j = 0; j < 4; ++j) {
         const uint32_t rr = m0 + wave * 16 + 4 * g + j;
         const int r = 16 * c + lr;
-        if (rr < rows && r < R) out_lr[static_cast<uint64_t>(rr) * R + r] = f32_to_bf16_rne(acc[c][j]);
+        if (rr < rows && r < R) a.out_lr[static_cast<uint64_t>(rr) * R + r] = f32_to_bf16_rne(acc[c][j]);
       }
     return;
   }
-  float* mypart = part + (static_cast<uint64_t>(blockIdx.y) * rows) * RP;
+  float* mypart = a.part + (static_cast<uint64_t>(blockIdx.y) * rows) * RP;
 #pragma unroll
   for (int c = 0; c < NRG; ++c)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const uint32_t rr = m0 + wave * 16 + 4 * g + j;
-      if (rr < rows) mypart[static_cast<uint64_t>(rr) * RP + 16 * c + lr] = acc[c][j];
+      if (rr < rows) store_partial(&mypart[static_cast<uint64_t>(rr) * RP + 16 * c + lr], acc[c][j]);
     }
-  __threadfence();
+  wait_stores();
   __syncthreads();
-  if (t == 0) {
-    const uint32_t old = atomicAdd(&cnt[blockIdx.x], 1u);
-    s_last = (old == gridDim.y - 1);
-  }
+  if (t == 0) s_last = arrive_last(a.cnt + blockIdx.x, a.epoch, gridDim.y);
   __syncthreads();
   if (!s_last) return;
-  __threadfence();
   // Last workgroup of this row block: sum the column-range partials in
   // range order (independent of arrival order) and round once.
-  for (int idx = t; idx < 64 * RP; idx += 256) {
-    const uint32_t rr = m0 + idx / RP;
-    const int r = idx % RP;
+  for (int idx = t; idx < 64 * (RP / 4); idx += 256) {
+    const uint32_t rr = m0 + idx / (RP / 4);
+    const int r = (idx % (RP / 4)) * 4;
     if (rr >= rows || r >= R) continue;
-    float s = 0.f;
-    for (uint32_t y = 0; y < gridDim.y; ++y)
-      s += __hip_atomic_load(part + (static_cast<uint64_t>(y) * rows + rr) * RP + r,
-                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    out_lr[static_cast<uint64_t>(rr) * R + r] = f32_to_bf16_rne(s);
+    const f32x4 sum = sum_partials(a.part + static_cast<uint64_t>(rr) * RP + r,
+                                   static_cast<uint64_t>(rows) * RP, gridDim.y);
+#pragma unroll
+    for (int k = 0; k < 4; ++k)
+      if (r + k < R) a.out_lr[static_cast<uint64_t>(rr) * R + r + k] = f32_to_bf16_rne(sum[k]);
   }
-  if (t == 0) cnt[blockIdx.x] = 0;
-}
-
-__global__ void k_fill_u32(uint32_t* p, uint32_t n, uint32_t v) {
-  for (uint32_t i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x)
-    p[i] = v;
 }
 
 // ---------------------------------------------------------------------------
@@ -325,51 +392,46 @@ hipError_t launch_quant_row32_t(const uint16_t* in, int64_t rows, int64_t cols, 
   return hipGetLastError();
 }
 
-int quant_down_splits(int64_t rows, int64_t cols) {
+// Columns per workgroup for the fused kernel: the largest of 512, 256, 128
+// that still gives at least one workgroup per CU.
+static int quant_down_kc(int64_t rows, int64_t cols) {
   const int64_t rb = (rows + 63) / 64;
-  const int64_t steps = (cols + 127) / 128;
-  int64_t s = 1;
-  while (rb * s < 512 && s * 2 <= steps && s < 16) s *= 2;
-  return static_cast<int>(s);
+  for (int kc = 512; kc > 128; kc /= 2)
+    if (rb * ((cols + kc - 1) / kc) >= 256) return kc;
+  return 128;
 }
 
 hipError_t launch_quant_down(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
                              uint8_t* codes, uint8_t* scales, const LowRankPieces& pr,
-                             uint16_t* out_lr, float* part, uint32_t* cnt, hipStream_t st) {
-  const int splits = quant_down_splits(rows, cols);
-  const int64_t steps = (cols + 127) / 128;
-  const uint32_t kc = static_cast<uint32_t>(((steps + splits - 1) / splits) * 128);
-  const uint32_t rb = static_cast<uint32_t>((rows + 63) / 64);
-  const uint32_t ny = static_cast<uint32_t>((cols + kc - 1) / kc);
-  if (ny > 1) {
-    hipLaunchKernelGGL(k_fill_u32, dim3((rb + 255) / 256), dim3(256), 0, st, cnt, rb, 0u);
+                             uint16_t* out_lr, float* part, unsigned long long* cnt,
+                             uint32_t epoch, hipStream_t st) {
+  const int kc = quant_down_kc(rows, cols);
+  dim3 grid(static_cast<uint32_t>((rows + 63) / 64), static_cast<uint32_t>((cols + kc - 1) / kc));
+  QDArgs a{in, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols), ld, codes, scales, pr,
+           pr.r0 + pr.r1, out_lr, part, cnt, epoch};
+  const int nrg = (a.R + 15) / 16;
+#define FT_QD(NRG, NS) hipLaunchKernelGGL((k_quant_down<NRG, NS>), grid, dim3(256), 0, st, a)
+#define FT_QD_NS(NRG) \
+  do { if (kc == 512) FT_QD(NRG, 4); else if (kc == 256) FT_QD(NRG, 2); else FT_QD(NRG, 1); } while (0)
+  switch (nrg) {
+    case 1: FT_QD_NS(1); break;
+    case 2: FT_QD_NS(2); break;
+    case 3: FT_QD_NS(3); break;
+    default: FT_QD_NS(4); break;
   }
-  dim3 grid(rb, ny);
-  const int R = pr.r0 + pr.r1;
-#define FT_QD(NRG)                                                                              \
-  hipLaunchKernelGGL(k_quant_down<NRG>, grid, dim3(256), 0, st, in, static_cast<uint32_t>(rows), \
-                     static_cast<uint32_t>(cols), ld, codes, scales, pr.p0, pr.s0c, pr.s0r,     \
-                     pr.r0, pr.p1, pr.s1c, pr.s1r, R, out_lr, part, cnt, kc)
-  switch ((R + 15) / 16) {
-    case 1: FT_QD(1); break;
-    case 2: FT_QD(2); break;
-    case 3: FT_QD(3); break;
-    default: FT_QD(4); break;
-  }
+#undef FT_QD_NS
 #undef FT_QD
   return hipGetLastError();
 }
 
 size_t quant_down_part_bytes(int64_t rows, int64_t cols, int R) {
-  const int splits = quant_down_splits(rows, cols);
-  if (splits <= 1 || R == 0) return 0;
-  const int64_t steps = (cols + 127) / 128;
-  const int64_t kc = ((steps + splits - 1) / splits) * 128;
+  const int kc = quant_down_kc(rows, cols);
   const int64_t ny = (cols + kc - 1) / kc;
+  if (ny <= 1 || R == 0) return 0;
   const int RP = ((R + 15) / 16) * 16;
   return static_cast<size_t>(ny) * rows * RP * sizeof(float);
 }
 
-size_t quant_down_cnt_bytes(int64_t rows) { return static_cast<size_t>((rows + 63) / 64) * 4; }
+size_t quant_down_cnt_bytes(int64_t rows) { return static_cast<size_t>((rows + 63) / 64) * 8; }
 
 }  // namespace ft

@@ -13,7 +13,6 @@ from oracle import mxfp4 as OQ
 
 DEV = torch.device("cuda:0")
 REL_TOL = 1e-3          # relative Frobenius bar for Y, dX, dA, dB
-BIT_AGREE = 0.999       # fraction of identical bf16 bits required of U and P
 
 
 def say(*a):
@@ -76,6 +75,30 @@ def bit_agreement(a, b):
     return float(np.mean(a == b))
 
 
+def check_rounding_flips(got, ref, name, absdot, n_terms):
+    """U and P are bf16 roundings of long fp32 (GPU) vs fp64 (oracle) sums.
+    They may differ only where the exact sum lies within fp32 accumulation
+    error of a bf16 rounding boundary: in at most 0.1% of the elements (two
+    are always allowed), and each by at most one bf16 ulp plus the
+    recursive-summation bound n * 2^-24 * sum_k |x_k d_k| (absdot)."""
+    if got is None or got.size == 0:
+        return
+    diff = got != ref
+    n = int(diff.sum())
+    assert n <= max(2, 0.001 * got.size), (name, n, got.size)
+    g = OQ.bf16_bits_to_f64(got[diff])
+    r = OQ.bf16_bits_to_f64(ref[diff])
+    ulp = np.ldexp(1.0, np.frexp(np.maximum(np.abs(r), 1e-38))[1] - 8)
+    bound = ulp + n_terms * 2.0 ** -24 * absdot[diff]
+    assert np.all(np.abs(g - r) <= bound), (name, np.abs(g - r).max())
+
+
+def _absdots(c):
+    D = np.abs(OL.stack_down(c.L1, c.A))
+    V = np.abs(OL.stack_up(c.L2, c.B))
+    return (np.abs(OQ.bf16_bits_to_f64(c.X)) @ D, np.abs(OQ.bf16_bits_to_f64(c.dY)) @ V.T)
+
+
 def check_full(case, got, grad_f32=False):
     """Full-size oracle comparison for cases the oracle finishes in seconds."""
     c = case
@@ -104,9 +127,10 @@ def check_full(case, got, grad_f32=False):
     for k in ("Y", "dX", "dA", "dB"):
         if k in res:
             assert res[k] <= REL_TOL, (k, res[k])
-    for k in ("U_bits", "P_bits"):
-        if k in res:
-            assert res[k] >= BIT_AGREE, (k, res[k])
+    if c.R:
+        ua, pa = _absdots(c)
+        check_rounding_flips(got["U"], f["U"], "U", ua, c.K)
+        check_rounding_flips(got["P"], b["P"], "P", pa, c.N)
     for k in ("U", "P"):
         if k in res:
             assert res[k] <= REL_TOL, (k, res[k])
@@ -150,7 +174,8 @@ def check_sampled(case, got, rows):
     for k in ("Y", "dX", "dA", "dB", "U", "P"):
         if k in res:
             assert res[k] <= REL_TOL, (k, res[k])
-    for k in ("U_bits", "P_bits"):
-        if k in res:
-            assert res[k] >= BIT_AGREE, (k, res[k])
+    if c.R:
+        ua, pa = _absdots(c)
+        check_rounding_flips(got["U"], Uf, "U", ua, c.K)
+        check_rounding_flips(got["P"], Pf, "P", pa, c.N)
     return res

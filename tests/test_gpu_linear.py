@@ -33,6 +33,8 @@ def test_tiny_case_full():
     (1, 128, 64, 8, 8),          # a single token
     (2, 3072, 1024, 32, 16),     # modulation-like: two tokens, long reduction
     (520, 1024, 768, 32, 16),    # several k steps, aligned scales
+    (4200, 1120, 800, 32, 16),   # several column splits of 256 with a ragged last one
+    (96, 256, 320, 5, 3),        # ranks that are not multiples of 8
 ])
 def test_ragged_shapes_full(shape):
     M, K, N, rs, rl = shape
