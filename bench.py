@@ -132,8 +132,8 @@ def main():
     a = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
-        print(json.dumps({"error": "this benchmark runs on one GPU only; the layer's data-parallel "
-                                   "sharding across GPUs is described in DESIGN.md, not run",
+        print(json.dumps({"error": "this benchmark runs on one GPU only: a step is one GPU's "
+                                   "share of the layer, and no multi-GPU run is made",
                           "n_gpus": a.gpus}))
         sys.exit(2)
 
@@ -165,13 +165,13 @@ def main():
             X = torch.roll(X0, 97 * s, 0).contiguous()
             dY = torch.roll(dY0, 97 * s, 0).contiguous()
             W = torch.roll(W0, 32 * s, 0).contiguous()
-            lay = QuantizedLinear(W, L1.clone(), L2.clone(), A.clone(), B.clone())
+            lay = QuantizedLinear.from_factors(W, L1.clone(), L2.clone(), A.clone(), B.clone())
             del W
             U = torch.empty((M, rs + rl), dtype=torch.bfloat16, device=dev)
             Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
             dA = torch.empty((K, rl), dtype=torch.bfloat16, device=dev)
-            dB = torch.empty((rl, N), dtype=torch.bfloat16, device=dev)
+            dB = torch.empty((N, rl), dtype=torch.bfloat16, device=dev)   # dB^T, like B^T
             wsf = lay.workspace(M, False)
             wsb = lay.workspace(M, True)
             sets.append((lay, X, dY, U, Y, dX, dA, dB, wsf, wsb))

@@ -130,10 +130,12 @@ ft_status check_linear(const ft_linear* L) {
   if (L->M * L->K * 2 > kMaxBytes || L->M * L->N * 2 > kMaxBytes || L->N * L->K / 2 > kMaxBytes)
     return FT_ESHAPE;
   if (L->r_stab < 0 || L->r_lora < 0 || L->r_stab + L->r_lora > FT_MAX_RANK) return FT_ESHAPE;
+  if (L->M * (L->r_stab + L->r_lora) * 2 > kMaxBytes) return FT_ESHAPE;
   if (!L->w_codes || !L->w_scales) return FT_EINVAL;
-  if (L->r_stab > 0 && (!L->L1 || !L->L2)) return FT_EINVAL;
-  if (L->r_lora > 0 && (!L->A || !L->B)) return FT_EINVAL;
-  const void* ptrs[] = {L->w_codes, L->w_scales, L->L1, L->L2, L->A, L->B};
+  if ((L->wt_codes == nullptr) != (L->wt_scales == nullptr)) return FT_EINVAL;
+  if (L->r_stab > 0 && (!L->L1 || !L->L2t)) return FT_EINVAL;
+  if (L->r_lora > 0 && (!L->A || !L->Bt)) return FT_EINVAL;
+  const void* ptrs[] = {L->w_codes, L->w_scales, L->wt_codes, L->wt_scales, L->L1, L->L2t, L->A, L->Bt};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return FT_EALIGN;
   return FT_OK;
@@ -179,9 +181,9 @@ BwdLayout bwd_layout(const ft_linear* L) {
 ft::LowRankPieces pieces_D(const ft_linear* L) {
   return ft::LowRankPieces{L->L1, L->r_stab, 1, L->r_stab, L->A, L->r_lora, 1, L->r_lora};
 }
-// Rank operand indexed by n: V^T, V = [L2 ; B], V[r][n].
+// Rank operand indexed by n: V^T = [L2^T | B^T], V^T[n][r].
 ft::LowRankPieces pieces_Vt(const ft_linear* L) {
-  return ft::LowRankPieces{L->L2, 1, L->N, L->r_stab, L->B, 1, L->N, L->r_lora};
+  return ft::LowRankPieces{L->L2t, L->r_stab, 1, L->r_stab, L->Bt, L->r_lora, 1, L->r_lora};
 }
 
 }  // namespace
@@ -208,6 +210,8 @@ ft_status fourtune_quantize(int mode, const uint16_t* in, int64_t rows, int64_t 
   if (!in || !codes || !scales) return FT_EINVAL;
   if (mode == FT_Q_ROW32_T) {
     if (!codes_t || !scales_t) return FT_EINVAL;
+  } else if (mode == FT_Q_TILE32) {
+    if ((codes_t == nullptr) != (scales_t == nullptr)) return FT_EINVAL;
   } else if (codes_t || scales_t) {
     return FT_EINVAL;
   }
@@ -226,7 +230,7 @@ ft_status fourtune_quantize(int mode, const uint16_t* in, int64_t rows, int64_t 
     case FT_Q_ROW32:
       { Timed tm("quant_row32", st); return launched(tm.done(ft::launch_quant_row32(in, rows, cols, ld_in, codes, scales, st))); }
     case FT_Q_TILE32:
-      { Timed tm("quant_tile32", st); return launched(tm.done(ft::launch_quant_tile32(in, rows, cols, ld_in, codes, scales, st))); }
+      { Timed tm("quant_tile32", st); return launched(tm.done(ft::launch_quant_tile32(in, rows, cols, ld_in, codes, scales, codes_t, scales_t, st))); }
     default:
     {
       Timed tm("quant_row32_t", st);
@@ -278,10 +282,10 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
   ft::GemmArgs g{};
   g.M = L->M; g.RED = L->K; g.NOUT = L->N;
   g.a_codes = qc; g.a_scales = qs;
-  g.w_codes = L->w_codes; g.w_scales = L->w_scales; g.w_cols = L->K;
-  g.lm = U_save; g.lo = pieces_Vt(L); g.R = R; g.out = Y;
+  g.b_codes = L->w_codes; g.b_scales = L->w_scales;
+  g.lm = U_save; g.lo0 = L->L2t; g.lo1 = L->Bt; g.R = R; g.r0 = L->r_stab; g.out = Y;
   Timed tm("fwd_gemm", st);
-  return launched(tm.done(ft::launch_gemm_fwd(g, st)));
+  return launched(tm.done(ft::launch_gemm(g, st)));
 }
 
 ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint16_t* X,
@@ -293,6 +297,7 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
   const int R = L->r_stab + L->r_lora;
   const int rl = L->r_lora;
   if (!dY) return FT_EINVAL;
+  if (dX && !L->wt_codes) return FT_EINVAL;
   if (grad_dtype != FT_BF16 && grad_dtype != FT_F32) return FT_EINVAL;
   if (rl > 0 && (!X || !U_save || !dA || !dB)) return FT_EINVAL;
   if ((gq_codes == nullptr) != (gq_scales == nullptr)) return FT_EINVAL;
@@ -325,23 +330,23 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
     ft::GemmArgs g{};
     g.M = L->M; g.RED = L->N; g.NOUT = L->K;
     g.a_codes = qc; g.a_scales = qs;
-    g.w_codes = L->w_codes; g.w_scales = L->w_scales; g.w_cols = L->K;
-    g.lm = P; g.lo = pieces_D(L); g.R = R; g.out = dX;
+    g.b_codes = L->wt_codes; g.b_scales = L->wt_scales;
+    g.lm = P; g.lo0 = L->L1; g.lo1 = L->A; g.R = R; g.r0 = L->r_stab; g.out = dX;
     Timed tm("bwd_gemm_dgrad", st);
-    if (tm.done(ft::launch_gemm_dgrad(g, st)) != hipSuccess) return FT_EDEVICE;
+    if (tm.done(ft::launch_gemm(g, st)) != hipSuccess) return FT_EDEVICE;
   }
   if (rl > 0) {
     const int f32 = grad_dtype == FT_F32 ? 1 : 0;
     const uint32_t epoch = next_epoch();
     ft::LoraGradArgs a{};
     a.M = L->M; a.I = L->K; a.big = X; a.small = P; a.ld_small = R; a.r0 = L->r_stab; a.rl = rl;
-    a.out = dA; a.out_f32 = f32; a.transpose_out = 0;
+    a.out = dA; a.out_f32 = f32;
     a.part = reinterpret_cast<float*>(ws + lay.dA_part);
     a.cnt = reinterpret_cast<unsigned long long*>(ws + lay.dA_cnt);
     a.epoch = epoch;
     ft::LoraGradArgs b = a;
     b.I = L->N; b.big = dY; b.small = U_save;
-    b.out = dB; b.transpose_out = 1;
+    b.out = dB;
     b.part = reinterpret_cast<float*>(ws + lay.dB_part);
     b.cnt = reinterpret_cast<unsigned long long*>(ws + lay.dB_cnt);
     Timed tm("bwd_lora_grads", st);

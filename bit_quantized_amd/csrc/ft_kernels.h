@@ -22,8 +22,10 @@ struct LowRankPieces {
 // quantize.hip
 hipError_t launch_quant_row32(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
                               uint8_t* codes, uint8_t* scales, hipStream_t st);
+// codes_t / scales_t: optional transposed copy (both null or both set).
 hipError_t launch_quant_tile32(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
-                               uint8_t* codes, uint8_t* scales, hipStream_t st);
+                               uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
+                               uint8_t* scales_t, hipStream_t st);
 hipError_t launch_quant_row32_t(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
                                 uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
                                 uint8_t* scales_t, hipStream_t st);
@@ -36,34 +38,31 @@ hipError_t launch_quant_down(const uint16_t* in, int64_t rows, int64_t cols, int
 size_t quant_down_part_bytes(int64_t rows, int64_t cols, int R);
 size_t quant_down_cnt_bytes(int64_t rows);
 
-// gemm.hip: C[m][j] = sum_red deq(a)[m][red] deq(b)(red, j) + sum_r lm[m][r] lo(j, r)
-// FWD : a = Qrow(X) [M, K], b = Qtile(W) read as W[j][red] (j = n), lo = V^T
-// DGRAD: a = Qrow(dY) [M, N], b = Qtile(W) read as W[red][j] (j = k), lo = D
+// gemm.hip: out[m][j] = sum_red deq(a)[m][red] deq(b)[j][red] + sum_r lm[m][r] lo[j][r]
+// forward: a = Qrow(X) [M, K], b = Qtile(W) [N, K], lm = U, lo = [L2^T | B^T]
+// dgrad  : a = Qrow(dY) [M, N], b = Qtile(W)^T [K, N], lm = P, lo = [L1 | A]
 struct GemmArgs {
   int64_t M, RED, NOUT;           // rows, reduction length, output columns
   const uint8_t* a_codes;         // [M, RED/2]
   const uint8_t* a_scales;        // [M, RED/32]
-  const uint8_t* w_codes;         // W codes [N, K/2]
-  const uint8_t* w_scales;        // [N/32, K/32]
-  int64_t w_cols;                 // K (codes row length is K/2, scales row length K/32)
-  const uint16_t* lm;             // bf16 [M, R] (U or P), may be null when R == 0
-  LowRankPieces lo;               // rank operand indexed by output column
-  int R;
+  const uint8_t* b_codes;         // [NOUT, RED/2]
+  const uint8_t* b_scales;        // [NOUT/32, RED/32] (one scale per 32x32 tile)
+  const uint16_t* lm;             // bf16 [M, R], may be null when R == 0
+  const uint16_t* lo0;            // bf16 [NOUT, r0]: ranks 0 .. r0-1 of lo
+  const uint16_t* lo1;            // bf16 [NOUT, R - r0]: ranks r0 .. R-1
+  int R, r0;
   uint16_t* out;                  // bf16 [M, NOUT]
 };
-hipError_t launch_gemm_fwd(const GemmArgs& g, hipStream_t st);
-hipError_t launch_gemm_dgrad(const GemmArgs& g, hipStream_t st);
+hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 
-// lora.hip: out(i, r) = sum_m big[m][i] * small[m][r0 + r], r < rl.
-// transpose_out: write out[r][i] (dB) instead of out[i][r] (dA).
+// lora.hip: out[i][r] = sum_m big[m][i] * small[m][r0 + r], r < rl.
 struct LoraGradArgs {
   int64_t M, I;                   // rows, columns of big
   const uint16_t* big;            // bf16 [M, I]
   const uint16_t* small;          // bf16 [M, ld_small], columns r0 .. r0+rl used
   int ld_small, r0, rl;
-  void* out;                      // [I, rl] or [rl, I]
+  void* out;                      // [I, rl]
   int out_f32;                    // 0 bf16, 1 fp32
-  int transpose_out;
   float* part;                    // workspace partials
   unsigned long long* cnt;        // workspace arrival slots (any contents)
   uint32_t epoch;                 // unique to this call

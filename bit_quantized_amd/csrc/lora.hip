@@ -5,9 +5,10 @@
 //   dL/dB = (X A)^T G,    dL/dA = X^T (G B^T),
 // with X and G unquantized.  Here (X A) is the adapter part of the saved
 // down-projection U = bf16(X [L1|A]) and (G B^T) the adapter part of
-// P = bf16(G [L2;B]^T), so both gradients have the form
-//   out(i, r) = sum_m big[m][i] * small[m][r0 + r]
-// with big = X (dA) or dY (dB) and small = P or U.  One launch computes
+// P = bf16(G [L2;B]^T).  dA is kept [K, r] like A and dB is kept [N, r]
+// like the stored B^T, so both gradients have the form
+//   out[i][r] = sum_m big[m][i] * small[m][r0 + r]
+// with big = X (dA) or dY (dB^T) and small = P or U.  One launch computes
 // both: the first workgroup columns cover dA, the rest dB.
 //
 // The reduction runs over tokens m, which is the row index of both
@@ -143,7 +144,7 @@ __global__ __launch_bounds__(256) void k_lora_grads(const LoraGradArgs pa, const
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       if (r + k >= rl) break;
-      const int64_t o = a.transpose_out ? static_cast<int64_t>(r + k) * I + i : i * rl + r + k;
+      const int64_t o = i * rl + r + k;
       if (a.out_f32) static_cast<float*>(a.out)[o] = sum[k];
       else static_cast<uint16_t*>(a.out)[o] = f32_to_bf16_rne(sum[k]);
     }

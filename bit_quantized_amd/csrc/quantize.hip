@@ -55,11 +55,16 @@ __global__ __launch_bounds__(256) void k_quant_row32(const uint16_t* __restrict_
 // ---------------------------------------------------------------------------
 // 32x32 tiles.  A workgroup covers 32 rows x 128 columns (4 tiles); thread
 // t reads 16 consecutive elements of row t/8 (columns 16*(t%8) ...).
+// Optionally also writes the transposed codes [cols, rows/2] and scales
+// [cols/32, rows/32]: the same numbers, since a tile has one scale.
 __global__ __launch_bounds__(256) void k_quant_tile32(const uint16_t* __restrict__ in,
                                                       uint32_t rows, uint32_t cols, int64_t ld,
                                                       uint8_t* __restrict__ codes,
-                                                      uint8_t* __restrict__ scales) {
+                                                      uint8_t* __restrict__ scales,
+                                                      uint8_t* __restrict__ codes_t,
+                                                      uint8_t* __restrict__ scales_t) {
   __shared__ uint32_t red[4][4];
+  __shared__ __attribute__((aligned(16))) uint8_t ct[32 * 64];   // this block's codes, row-major
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const uint32_t row = blockIdx.y * 32 + (t >> 3);
   const uint32_t col = blockIdx.x * 128 + (t & 7) * 16;
@@ -86,15 +91,34 @@ __global__ __launch_bounds__(256) void k_quant_tile32(const uint16_t* __restrict
   a = max(max(red[0][tile], red[1][tile]), max(red[2][tile], red[3][tile]));
   const uint32_t s = e8m0_from_amax_bits(a);
   const float sc = e8m0_to_f32(s);
+  u32x2 o;
+  o[0] = encode8(v0[0], v0[1], v0[2], v0[3], sc);
+  o[1] = encode8(v1[0], v1[1], v1[2], v1[3], sc);
   if (ok) {
-    u32x2 o;
-    o[0] = encode8(v0[0], v0[1], v0[2], v0[3], sc);
-    o[1] = encode8(v1[0], v1[1], v1[2], v1[3], sc);
     *reinterpret_cast<u32x2*>(codes + static_cast<uint64_t>(row) * (cols >> 1) + (col >> 1)) = o;
-    if ((t >> 3) == 0 && (t & 1) == 0)
-      scales[static_cast<uint64_t>(blockIdx.y) * (cols >> 5) + (col >> 5)] =
-          static_cast<uint8_t>(s);
+    if ((t >> 3) == 0 && (t & 1) == 0) {
+      scales[static_cast<uint64_t>(blockIdx.y) * (cols >> 5) + (col >> 5)] = static_cast<uint8_t>(s);
+      if (scales_t)
+        scales_t[static_cast<uint64_t>(col >> 5) * (rows >> 5) + blockIdx.y] = static_cast<uint8_t>(s);
+    }
   }
+  if (!codes_t) return;
+  *reinterpret_cast<u32x2*>(&ct[(t >> 3) * 64 + (t & 7) * 8]) = o;
+  __syncthreads();
+  // transposed row c (an input column) gets 16 input rows, 2 per byte
+  const int c = t >> 1, h = t & 1;
+  const uint32_t gc = blockIdx.x * 128 + c;
+  if (gc >= cols) return;
+  uint32_t w[2] = {0, 0};
+#pragma unroll
+  for (int b = 0; b < 8; ++b) {
+    const int r = 16 * h + 2 * b;
+    const uint32_t lo = (ct[r * 64 + (c >> 1)] >> (4 * (c & 1))) & 0xFu;
+    const uint32_t hi = (ct[(r + 1) * 64 + (c >> 1)] >> (4 * (c & 1))) & 0xFu;
+    w[b >> 2] |= (lo | (hi << 4)) << (8 * (b & 3));
+  }
+  *reinterpret_cast<u32x2*>(codes_t + static_cast<uint64_t>(gc) * (rows >> 1) + blockIdx.y * 16 + 8 * h) =
+      u32x2{w[0], w[1]};
 }
 
 // ---------------------------------------------------------------------------
@@ -376,10 +400,11 @@ hipError_t launch_quant_row32(const uint16_t* in, int64_t rows, int64_t cols, in
 }
 
 hipError_t launch_quant_tile32(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
-                               uint8_t* codes, uint8_t* scales, hipStream_t st) {
+                               uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
+                               uint8_t* scales_t, hipStream_t st) {
   dim3 grid(static_cast<uint32_t>((cols + 127) / 128), static_cast<uint32_t>(rows / 32));
   hipLaunchKernelGGL(k_quant_tile32, grid, dim3(256), 0, st, in, static_cast<uint32_t>(rows),
-                     static_cast<uint32_t>(cols), ld, codes, scales);
+                     static_cast<uint32_t>(cols), ld, codes, scales, codes_t, scales_t);
   return hipGetLastError();
 }
 

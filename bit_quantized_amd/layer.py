@@ -33,23 +33,34 @@ class QuantizedLinear:
     """One triple-branch linear on the GPU.
 
     W_res (bf16 [N, K]) is quantized once on the device to 32x32 MXFP4 tiles
-    by fourtune_quantize; L1, L2 (frozen) and A, B (trainable) stay bf16.
+    by fourtune_quantize, which also writes the transposed codes the backward
+    reads.  The rank factors are kept in the library's storage: L1 [K, r_s],
+    L2t = L2^T [N, r_s] (frozen), A [K, r_l], Bt = B^T [N, r_l] (trainable).
     """
 
-    def __init__(self, W_res: torch.Tensor, L1: torch.Tensor | None, L2: torch.Tensor | None,
-                 A: torch.Tensor | None, B: torch.Tensor | None, stream=None):
+    def __init__(self, W_res: torch.Tensor, L1: torch.Tensor | None, L2t: torch.Tensor | None,
+                 A: torch.Tensor | None, Bt: torch.Tensor | None, stream=None):
         N, K = W_res.shape
         dev = W_res.device
         self.N, self.K = int(N), int(K)
         self.r_s = 0 if L1 is None else int(L1.shape[1])
         self.r_l = 0 if A is None else int(A.shape[1])
-        self.L1, self.L2, self.A, self.B = L1, L2, A, B
+        self.L1, self.L2t, self.A, self.Bt = L1, L2t, A, Bt
         self.w_codes = _empty((N, K // 2), torch.uint8, dev)
         self.w_scales = _empty((N // 32, K // 32), torch.uint8, dev)
+        self.wt_codes = _empty((K, N // 2), torch.uint8, dev)
+        self.wt_scales = _empty((K // 32, N // 32), torch.uint8, dev)
         ops.fourtune_quantize(ops.FT_Q_TILE32, W_res, N, K, K, self.w_codes, self.w_scales,
-                              stream=stream)
+                              self.wt_codes, self.wt_scales, stream=stream)
         self.device = dev
         self._ws = {}
+
+    @classmethod
+    def from_factors(cls, W_res, L1, L2, A, B, stream=None) -> "QuantizedLinear":
+        """From factors in the method's orientation (L2 [r_s, N], B [r_l, N]):
+        the up-projections are copied once into the [N, r] storage."""
+        t = lambda x: None if x is None else x.t().contiguous()
+        return cls(W_res, L1, t(L2), A, t(B), stream=stream)
 
     @property
     def R(self):
@@ -57,7 +68,8 @@ class QuantizedLinear:
 
     def desc(self, M: int) -> ops.FtLinear:
         return ops.make_linear(M, self.K, self.N, self.r_s, self.r_l, self.w_codes,
-                               self.w_scales, self.L1, self.L2, self.A, self.B)
+                               self.w_scales, self.wt_codes, self.wt_scales, self.L1, self.L2t,
+                               self.A, self.Bt)
 
     def workspace(self, M: int, is_bwd: bool):
         key = (M, bool(is_bwd))
@@ -81,13 +93,14 @@ class QuantizedLinear:
 
     def backward(self, dY: torch.Tensor, X: torch.Tensor, U: torch.Tensor, need_dx: bool = True,
                  grad_f32: bool = False, stream=None, want_codes: bool = False):
-        """Returns (dX, dA, dB, P) or (dX, dA, dB, P, gq_codes, gq_scales)."""
+        """Returns (dX, dA, dBt, P) or (dX, dA, dBt, P, gq_codes, gq_scales);
+        dBt = dB^T [N, r_l], the layout of Bt."""
         M = int(dY.shape[0])
         dev = self.device
         dX = _empty((M, self.K), torch.bfloat16, dev) if need_dx else None
         gdt = torch.float32 if grad_f32 else torch.bfloat16
         dA = _empty((self.K, self.r_l), gdt, dev) if self.r_l else None
-        dB = _empty((self.r_l, self.N), gdt, dev) if self.r_l else None
+        dB = _empty((self.N, self.r_l), gdt, dev) if self.r_l else None
         P = _empty((M, max(self.R, 1)), torch.bfloat16, dev)
         qc = _empty((M, self.N // 2), torch.uint8, dev) if want_codes else None
         qs = _empty((M, self.N // 32), torch.uint8, dev) if want_codes else None
@@ -100,10 +113,11 @@ class QuantizedLinear:
 
 
 class FourTuneLinearFunction(torch.autograd.Function):
-    """Y = layer(X) with gradients for X, A and B (W_res, L1, L2 frozen)."""
+    """Y = layer(X) with gradients for X, A and Bt (W_res, L1, L2 frozen).
+    A and Bt must be the tensors the layer holds."""
 
     @staticmethod
-    def forward(ctx, X, A, B, layer: QuantizedLinear):
+    def forward(ctx, X, A, Bt, layer: QuantizedLinear):
         Y, U = layer.forward(X.contiguous())
         ctx.save_for_backward(X, U)
         ctx.layer = layer

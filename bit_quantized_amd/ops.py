@@ -34,8 +34,9 @@ class FtLinear(ctypes.Structure):
     _fields_ = [("M", ctypes.c_int64), ("K", ctypes.c_int64), ("N", ctypes.c_int64),
                 ("r_stab", ctypes.c_int32), ("r_lora", ctypes.c_int32),
                 ("w_codes", ctypes.c_void_p), ("w_scales", ctypes.c_void_p),
-                ("L1", ctypes.c_void_p), ("L2", ctypes.c_void_p),
-                ("A", ctypes.c_void_p), ("B", ctypes.c_void_p)]
+                ("wt_codes", ctypes.c_void_p), ("wt_scales", ctypes.c_void_p),
+                ("L1", ctypes.c_void_p), ("L2t", ctypes.c_void_p),
+                ("A", ctypes.c_void_p), ("Bt", ctypes.c_void_p)]
 
 
 _lib = None
@@ -104,11 +105,14 @@ def _check(status: int, where: str):
         raise FourTuneError(status, where)
 
 
-def make_linear(M, K, N, r_stab, r_lora, w_codes, w_scales, L1=None, L2=None, A=None,
-                B=None) -> FtLinear:
-    """Fill the ft_linear descriptor from tensors (device) or raw addresses."""
+def make_linear(M, K, N, r_stab, r_lora, w_codes, w_scales, wt_codes=None, wt_scales=None,
+                L1=None, L2t=None, A=None, Bt=None) -> FtLinear:
+    """Fill the ft_linear descriptor from tensors (device) or raw addresses.
+
+    L2t and Bt are the up-projection factors stored [N, r] (L2^T, B^T)."""
     return FtLinear(int(M), int(K), int(N), int(r_stab), int(r_lora), _ptr(w_codes),
-                    _ptr(w_scales), _ptr(L1), _ptr(L2), _ptr(A), _ptr(B))
+                    _ptr(w_scales), _ptr(wt_codes), _ptr(wt_scales), _ptr(L1), _ptr(L2t),
+                    _ptr(A), _ptr(Bt))
 
 
 def fourtune_quantize(mode, x, rows, cols, ld, codes, scales, codes_t=None, scales_t=None,

@@ -20,9 +20,10 @@
  * for activations and gradients, and 32x32 square tiles (one scale per
  * tile) for the frozen residual weight.
  *
- * Shapes and orientation (weights stored like torch.nn.Linear.weight):
+ * Shapes (the method's notation):
  *   X   [M, K] bf16      input             dY  [M, N] bf16  incoming gradient
- *   W_res [N, K]         frozen residual, given as MXFP4 32x32 tiles
+ *   W_res [N, K]         frozen residual (like torch.nn.Linear.weight),
+ *                        given as MXFP4 32x32 tiles
  *   L1  [K, r_stab], L2 [r_stab, N]        frozen stabilizer, bf16
  *   A   [K, r_lora], B  [r_lora, N]        trainable adapter, bf16
  *   D = [L1 | A]  [K, R],  V = [L2 ; B]  [R, N],  R = r_stab + r_lora <= 64
@@ -32,6 +33,15 @@
  *             dA = X^T P[:, r_stab:]          dB = U[:, r_stab:]^T dY
  *
  * Every product accumulates in fp32 and is rounded once to the output type.
+ *
+ * Storage of the factors: every low-rank factor is kept rank-contiguous
+ * (row-major with the rank index innermost), so L1 and A are passed as is
+ * ([K, r]) and L2 and B as their transposes L2^T [N, r_stab] and B^T
+ * [N, r_lora] (the torch.nn.Linear.weight orientation of the up-projections).
+ * dB is returned in the same [N, r_lora] layout.  The backward also takes the
+ * weight's MXFP4 codes in transposed order, [K, N/2] with scales [K/32, N/32]
+ * (FT_Q_TILE32 writes them beside the plain order): with one scale per 32x32
+ * tile the transpose of the quantized weight is exactly these numbers.
  *
  * Memory layouts (all row-major, no padding between rows):
  *   bf16 tensors are arrays of uint16_t bit patterns.
@@ -90,10 +100,12 @@ typedef struct {
   int32_t r_stab, r_lora;     /* stabilizer and adapter ranks, r_stab + r_lora <= 64 */
   const uint8_t* w_codes;     /* Qtile(W_res) codes  [N, K/2]                         */
   const uint8_t* w_scales;    /* Qtile(W_res) scales [N/32, K/32]                     */
+  const uint8_t* wt_codes;    /* the same codes transposed [K, N/2]; backward only,  */
+  const uint8_t* wt_scales;   /*   scales [K/32, N/32]; may be NULL for the forward   */
   const uint16_t* L1;         /* bf16 [K, r_stab]  (frozen)                           */
-  const uint16_t* L2;         /* bf16 [r_stab, N]  (frozen)                           */
+  const uint16_t* L2t;        /* bf16 [N, r_stab] = L2^T  (frozen)                    */
   const uint16_t* A;          /* bf16 [K, r_lora]  (trainable)                        */
-  const uint16_t* B;          /* bf16 [r_lora, N]  (trainable)                        */
+  const uint16_t* Bt;         /* bf16 [N, r_lora] = B^T  (trainable)                  */
 } ft_linear;
 
 /* Quantize a bf16 matrix `in` [rows, cols] with row stride ld_in elements.
@@ -107,7 +119,9 @@ typedef struct {
  * mode FT_Q_ROW32_T: as ROW32, plus codes_t [cols, rows/2] and
  *                    scales_t [cols, rows/32] = ROW32 of in^T; rows % 32 == 0.
  * mode FT_Q_TILE32:  codes [rows, cols/2], scales [rows/32, cols/32];
- *                    rows % 32 == 0; codes_t and scales_t must be NULL.
+ *                    rows % 32 == 0; codes_t [cols, rows/2] and scales_t
+ *                    [cols/32, rows/32] are optional (both NULL or both set)
+ *                    and receive the transposed copy.
  * Requirements: cols % 32 == 0, rows >= 0, ld_in >= cols, ld_in % 8 == 0.
  * rows == 0 is a no-op.
  * Errors: FT_EINVAL (mode, NULLs), FT_ESHAPE, FT_EALIGN. */
@@ -137,14 +151,15 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
 /* Backward, Eq. (3) and the adapter gradients of section 3.2:
  *   kernel 1 reads dY once and writes Qrow(dY) (1x32 blocks along N, the
  *   reduction dimension of the input gradient) and P = bf16(dY V^T);
- *   kernel 2 computes deq(Qrow(dY)) deq(Qtile(W_res)) + P D^T, reading the
- *   same 32x32-tile codes as the forward, transposed on chip, and writes dX
+ *   kernel 2 computes deq(Qrow(dY)) deq(Qtile(W_res)) + P D^T from the
+ *   32x32-tile codes in transposed order (wt_codes, wt_scales) and writes dX
  *   (bf16 [M, K]) once;
- *   the adapter gradients dA = X^T P[:, r_stab:] ([K, r_lora]) and
- *   dB = U[:, r_stab:]^T dY ([r_lora, N]) are written in grad_dtype
- *   (FT_BF16 or FT_F32).
+ *   kernel 3 writes the adapter gradients dA = X^T P[:, r_stab:] ([K, r_lora])
+ *   and dB, stored as dB^T = dY^T U[:, r_stab:] ([N, r_lora], the layout of
+ *   Bt), in grad_dtype (FT_BF16 or FT_F32).
  * X and U_save are the forward's input and saved U.  dX may be NULL (no
- * input gradient).  dA, dB may be NULL only when r_lora == 0.
+ * input gradient; then wt_codes and wt_scales may be NULL).  dA, dB may be
+ * NULL only when r_lora == 0.
  * P_save : optional bf16 [M, R] output of P; NULL = workspace only.
  * gq_codes, gq_scales: optional outputs [M, N/2], [M, N/32].
  * workspace: at least fourtune_workspace_bytes(L, 1) bytes.

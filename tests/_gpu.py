@@ -43,10 +43,10 @@ class GpuCase:
         self.dY = up(case.dY)
         W = up(case.W_res)
         opt = lambda a: up(a) if a.size else None
-        self.layer = QuantizedLinear(W, opt(case.L1) if case.r_s else None,
-                                     opt(case.L2) if case.r_s else None,
-                                     opt(case.A) if case.r_l else None,
-                                     opt(case.B) if case.r_l else None)
+        self.layer = QuantizedLinear.from_factors(W, opt(case.L1) if case.r_s else None,
+                                                  opt(case.L2) if case.r_s else None,
+                                                  opt(case.A) if case.r_l else None,
+                                                  opt(case.B) if case.r_l else None)
         del W
 
     def run(self, grad_f32=False):
@@ -58,14 +58,16 @@ class GpuCase:
                    xq_codes=u8(xc), xq_scales=u8(xs), dX=bits_of(dX),
                    P=bits_of(P)[:, :self.c.R] if self.c.R else None, gq_codes=u8(gc),
                    gq_scales=u8(gs), w_codes=u8(self.layer.w_codes),
-                   w_scales=u8(self.layer.w_scales))
+                   w_scales=u8(self.layer.w_scales), wt_codes=u8(self.layer.wt_codes),
+                   wt_scales=u8(self.layer.wt_scales))
+        # dB comes back as dB^T [N, r_l] (the layout of the stored B^T)
         if self.c.r_l:
             if grad_f32:
                 out["dA"] = dA.cpu().numpy()
-                out["dB"] = dB.cpu().numpy()
+                out["dB"] = np.ascontiguousarray(dB.cpu().numpy().T)
             else:
                 out["dA"] = bits_of(dA)
-                out["dB"] = bits_of(dB)
+                out["dB"] = np.ascontiguousarray(bits_of(dB).T)
         return out
 
 
@@ -99,12 +101,22 @@ def _absdots(c):
     return (np.abs(OQ.bf16_bits_to_f64(c.X)) @ D, np.abs(OQ.bf16_bits_to_f64(c.dY)) @ V.T)
 
 
-def check_full(case, got, grad_f32=False):
-    """Full-size oracle comparison for cases the oracle finishes in seconds."""
-    c = case
+def check_weight_codes(c, got):
+    """Qtile(W) and the transposed copy the backward reads, which must be
+    Qtile(W^T): the same numbers, since a 32x32 tile has one scale."""
     wc, ws = OQ.quantize_tile32(c.W_res)
     np.testing.assert_array_equal(got["w_codes"], wc)
     np.testing.assert_array_equal(got["w_scales"], ws)
+    wtc, wts = OQ.quantize_tile32(np.ascontiguousarray(c.W_res.T))
+    np.testing.assert_array_equal(got["wt_codes"], wtc)
+    np.testing.assert_array_equal(got["wt_scales"], wts)
+    return wc, ws
+
+
+def check_full(case, got, grad_f32=False):
+    """Full-size oracle comparison for cases the oracle finishes in seconds."""
+    c = case
+    wc, ws = check_weight_codes(c, got)
     f = OL.linear_fwd(c.X, wc, ws, c.L1, c.L2, c.A, c.B)
     b = OL.linear_bwd(c.dY, c.X, f["U"], wc, ws, c.L1, c.L2, c.A, c.B,
                       grad_dtype="f32" if grad_f32 else "bf16")
@@ -140,9 +152,7 @@ def check_full(case, got, grad_f32=False):
 def check_sampled(case, got, rows):
     """Large cases: outputs of sampled rows, and the adapter gradients in full."""
     c = case
-    wc, ws = OQ.quantize_tile32(c.W_res)
-    np.testing.assert_array_equal(got["w_codes"], wc)
-    np.testing.assert_array_equal(got["w_scales"], ws)
+    wc, ws = check_weight_codes(c, got)
     xc, xs = OQ.quantize_row32(c.X[rows])
     np.testing.assert_array_equal(got["xq_codes"][rows], xc)
     np.testing.assert_array_equal(got["xq_scales"][rows], xs)

@@ -75,14 +75,14 @@ def test_autograd_function_matches_library():
     g = GpuCase(c)
     X = g.X.clone().requires_grad_(True)
     A = g.layer.A.clone().requires_grad_(True)
-    B = g.layer.B.clone().requires_grad_(True)
-    Y = FourTuneLinearFunction.apply(X, A, B, g.layer)
+    Bt = g.layer.Bt.clone().requires_grad_(True)
+    Y = FourTuneLinearFunction.apply(X, A, Bt, g.layer)
     Y.backward(g.dY)
     ref = g.run()
     np.testing.assert_array_equal(bits_of(Y), ref["Y"])
     np.testing.assert_array_equal(bits_of(X.grad), ref["dX"])
     np.testing.assert_array_equal(bits_of(A.grad), ref["dA"])
-    np.testing.assert_array_equal(bits_of(B.grad), ref["dB"])
+    np.testing.assert_array_equal(bits_of(Bt.grad).T, ref["dB"])
 
 
 def _rows(M, n=48, seed=0):
