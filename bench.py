@@ -170,8 +170,8 @@ def main():
             U = torch.empty((M, rs + rl), dtype=torch.bfloat16, device=dev)
             Y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
             dX = torch.empty((M, K), dtype=torch.bfloat16, device=dev)
-            dA = torch.empty((K, rl), dtype=torch.bfloat16, device=dev)
-            dB = torch.empty((N, rl), dtype=torch.bfloat16, device=dev)   # dB^T, like B^T
+            dA = torch.empty((rl, K), dtype=torch.bfloat16, device=dev)   # dA^T, like A^T
+            dB = torch.empty((rl, N), dtype=torch.bfloat16, device=dev)
             wsf = lay.workspace(M, False)
             wsb = lay.workspace(M, True)
             sets.append((lay, X, dY, U, Y, dX, dA, dB, wsf, wsb))

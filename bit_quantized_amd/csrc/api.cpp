@@ -133,42 +133,46 @@ ft_status check_linear(const ft_linear* L) {
   if (L->M * (L->r_stab + L->r_lora) * 2 > kMaxBytes) return FT_ESHAPE;
   if (!L->w_codes || !L->w_scales) return FT_EINVAL;
   if ((L->wt_codes == nullptr) != (L->wt_scales == nullptr)) return FT_EINVAL;
-  if (L->r_stab > 0 && (!L->L1 || !L->L2t)) return FT_EINVAL;
-  if (L->r_lora > 0 && (!L->A || !L->Bt)) return FT_EINVAL;
-  const void* ptrs[] = {L->w_codes, L->w_scales, L->wt_codes, L->wt_scales, L->L1, L->L2t, L->A, L->Bt};
+  if (L->r_stab > 0 && (!L->L1t || !L->L2)) return FT_EINVAL;
+  if (L->r_lora > 0 && (!L->At || !L->B)) return FT_EINVAL;
+  const void* ptrs[] = {L->w_codes, L->w_scales, L->wt_codes, L->wt_scales, L->L1t, L->L2, L->At, L->B};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return FT_EALIGN;
   return FT_OK;
 }
 
 struct FwdLayout {
-  size_t xq_codes, xq_scales, part, cnt, total;
+  size_t xq_codes, xq_scales, u_pad, v_pad, part, total;
 };
 FwdLayout fwd_layout(const ft_linear* L) {
   const int R = L->r_stab + L->r_lora;
+  const size_t rp = static_cast<size_t>(ft::rank_pad(R));
   FwdLayout o;
   size_t off = 0;
   o.xq_codes = off; off += align_up(static_cast<size_t>(L->M) * (L->K / 2));
   o.xq_scales = off; off += align_up(static_cast<size_t>(L->M) * (L->K / 32));
-  o.part = off; off += align_up(R ? ft::quant_down_part_bytes(L->M, L->K, R) : 0);
-  o.cnt = off; off += align_up(ft::quant_down_cnt_bytes(L->M));
+  o.u_pad = off; off += align_up(static_cast<size_t>(L->M) * rp * 2);     // U, zero-padded ranks
+  o.v_pad = off; off += align_up(static_cast<size_t>(L->N) * rp * 2);     // [L2^T | B^T], padded
+  o.part = off; off += align_up(ft::quant_down_part_bytes(L->M, L->K, R));
   o.total = off;
   return o;
 }
 
 struct BwdLayout {
-  size_t gq_codes, gq_scales, P, part, cnt, dA_part, dA_cnt, dB_part, dB_cnt, total;
+  size_t gq_codes, gq_scales, P, p_pad, d_pad, part, dA_part, dA_cnt, dB_part, dB_cnt, total;
 };
 BwdLayout bwd_layout(const ft_linear* L) {
   const int R = L->r_stab + L->r_lora;
   const int rl = L->r_lora;
+  const size_t rp = static_cast<size_t>(ft::rank_pad(R));
   BwdLayout o;
   size_t off = 0;
   o.gq_codes = off; off += align_up(static_cast<size_t>(L->M) * (L->N / 2));
   o.gq_scales = off; off += align_up(static_cast<size_t>(L->M) * (L->N / 32));
   o.P = off; off += align_up(static_cast<size_t>(L->M) * R * 2);
-  o.part = off; off += align_up(R ? ft::quant_down_part_bytes(L->M, L->N, R) : 0);
-  o.cnt = off; off += align_up(ft::quant_down_cnt_bytes(L->M));
+  o.p_pad = off; off += align_up(static_cast<size_t>(L->M) * rp * 2);     // P, zero-padded ranks
+  o.d_pad = off; off += align_up(static_cast<size_t>(L->K) * rp * 2);     // [L1 | A], padded
+  o.part = off; off += align_up(ft::quant_down_part_bytes(L->M, L->N, R));
   o.dA_part = off; off += align_up(rl ? ft::lora_grad_part_bytes(L->M, L->K, rl) : 0);
   o.dA_cnt = off; off += align_up(rl ? ft::lora_grad_cnt_bytes(L->K) : 0);
   o.dB_part = off; off += align_up(rl ? ft::lora_grad_part_bytes(L->M, L->N, rl) : 0);
@@ -177,13 +181,13 @@ BwdLayout bwd_layout(const ft_linear* L) {
   return o;
 }
 
-// Rank operand indexed by k: D = [L1 | A], D[k][r].
-ft::LowRankPieces pieces_D(const ft_linear* L) {
-  return ft::LowRankPieces{L->L1, L->r_stab, 1, L->r_stab, L->A, L->r_lora, 1, L->r_lora};
+// The factors rank-major: D^T = [L1^T ; A^T] (rows of K values) and
+// V = [L2 ; B] (rows of N values).
+ft::RankRows rows_Dt(const ft_linear* L) {
+  return ft::RankRows{L->L1t, L->At, L->r_stab, L->r_lora, L->K};
 }
-// Rank operand indexed by n: V^T = [L2^T | B^T], V^T[n][r].
-ft::LowRankPieces pieces_Vt(const ft_linear* L) {
-  return ft::LowRankPieces{L->L2t, L->r_stab, 1, L->r_stab, L->Bt, L->r_lora, 1, L->r_lora};
+ft::RankRows rows_V(const ft_linear* L) {
+  return ft::RankRows{L->L2, L->B, L->r_stab, L->r_lora, L->N};
 }
 
 }  // namespace
@@ -267,13 +271,14 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   uint8_t* qc = xq_codes ? xq_codes : ws + lay.xq_codes;
   uint8_t* qs = xq_scales ? xq_scales : ws + lay.xq_scales;
+  uint16_t* u_pad = reinterpret_cast<uint16_t*>(ws + lay.u_pad);
+  uint16_t* v_pad = reinterpret_cast<uint16_t*>(ws + lay.v_pad);
   hipError_t e;
   {
     Timed tm("fwd_quant_down", st);
     if (R > 0)
-      e = ft::launch_quant_down(X, L->M, L->K, L->K, qc, qs, pieces_D(L), U_save,
-                                reinterpret_cast<float*>(ws + lay.part),
-                                reinterpret_cast<unsigned long long*>(ws + lay.cnt), next_epoch(), st);
+      e = ft::launch_quant_down(X, L->M, L->K, L->K, qc, qs, rows_Dt(L), U_save, u_pad, rows_V(L),
+                                L->N, v_pad, reinterpret_cast<float*>(ws + lay.part), st);
     else
       e = ft::launch_quant_row32(X, L->M, L->K, L->K, qc, qs, st);
     tm.done(e);
@@ -283,7 +288,7 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
   g.M = L->M; g.RED = L->K; g.NOUT = L->N;
   g.a_codes = qc; g.a_scales = qs;
   g.b_codes = L->w_codes; g.b_scales = L->w_scales;
-  g.lm = U_save; g.lo0 = L->L2t; g.lo1 = L->Bt; g.R = R; g.r0 = L->r_stab; g.out = Y;
+  g.lm = u_pad; g.lo = v_pad; g.nlr = ft::rank_pad(R) / 32; g.out = Y;
   Timed tm("fwd_gemm", st);
   return launched(tm.done(ft::launch_gemm(g, st)));
 }
@@ -314,13 +319,14 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
   uint8_t* qc = gq_codes ? gq_codes : ws + lay.gq_codes;
   uint8_t* qs = gq_scales ? gq_scales : ws + lay.gq_scales;
   uint16_t* P = P_save ? P_save : reinterpret_cast<uint16_t*>(ws + lay.P);
+  uint16_t* p_pad = reinterpret_cast<uint16_t*>(ws + lay.p_pad);
+  uint16_t* d_pad = reinterpret_cast<uint16_t*>(ws + lay.d_pad);
   hipError_t e;
   {
     Timed tm("bwd_quant_down", st);
     if (R > 0)
-      e = ft::launch_quant_down(dY, L->M, L->N, L->N, qc, qs, pieces_Vt(L), P,
-                                reinterpret_cast<float*>(ws + lay.part),
-                                reinterpret_cast<unsigned long long*>(ws + lay.cnt), next_epoch(), st);
+      e = ft::launch_quant_down(dY, L->M, L->N, L->N, qc, qs, rows_V(L), P, p_pad, rows_Dt(L),
+                                dX ? L->K : 0, d_pad, reinterpret_cast<float*>(ws + lay.part), st);
     else
       e = ft::launch_quant_row32(dY, L->M, L->N, L->N, qc, qs, st);
     tm.done(e);
@@ -331,7 +337,7 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
     g.M = L->M; g.RED = L->N; g.NOUT = L->K;
     g.a_codes = qc; g.a_scales = qs;
     g.b_codes = L->wt_codes; g.b_scales = L->wt_scales;
-    g.lm = P; g.lo0 = L->L1; g.lo1 = L->A; g.R = R; g.r0 = L->r_stab; g.out = dX;
+    g.lm = p_pad; g.lo = d_pad; g.nlr = ft::rank_pad(R) / 32; g.out = dX;
     Timed tm("bwd_gemm_dgrad", st);
     if (tm.done(ft::launch_gemm(g, st)) != hipSuccess) return FT_EDEVICE;
   }

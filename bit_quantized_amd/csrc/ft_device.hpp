@@ -200,9 +200,5 @@ __device__ __forceinline__ uint32_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_
 }
 constexpr uint32_t BUF_OOB = 0x80000000u;   // a buffer offset past every tensor
 
-// Bytes spanned by a rank piece p[c*sc + r*sr], c < ncols, r < nr (bf16).
-__device__ __forceinline__ uint64_t piece_bytes(int64_t sc, int64_t sr, int nr, int64_t ncols) {
-  return nr ? static_cast<uint64_t>((ncols - 1) * sc + (nr - 1) * sr + 1) * 2 : 0;
-}
 
 }  // namespace ft

@@ -7,16 +7,14 @@
 
 namespace ft {
 
-// A rank-R operand given as two bf16 pieces along the rank axis: element
-// (c, r) = r < r0 ? p0[c*s0c + r*s0r] : p1[c*s1c + (r-r0)*s1r], where c runs
-// over the long axis (K or N) of the layer.
-struct LowRankPieces {
+// A rank-R operand stored rank-major: rank r < r0 is row r of p0, rank
+// r >= r0 row r - r0 of p1; every row holds `ld` bf16 values (ld % 8 == 0,
+// rows 16-byte aligned).
+struct RankRows {
   const uint16_t* p0;
-  int64_t s0c, s0r;
-  int r0;
   const uint16_t* p1;
-  int64_t s1c, s1r;
-  int r1;
+  int r0, r1;
+  int64_t ld;
 };
 
 // quantize.hip
@@ -29,39 +27,47 @@ hipError_t launch_quant_tile32(const uint16_t* in, int64_t rows, int64_t cols, i
 hipError_t launch_quant_row32_t(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
                                 uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
                                 uint8_t* scales_t, hipStream_t st);
-// Row quantization fused with the down-projection; `cnt` is a workspace array
-// of 64-bit arrival slots (any contents), `epoch` a value unique to this call.
+// Ranks of the zero-padded rank operands the GEMM reads: 64 (FT_MAX_RANK)
+// whenever there is a rank part, so that every tile has the same two rank
+// steps.
+inline int rank_pad(int R) { return R > 0 ? 64 : 0; }
+
+// Row quantization fused with the down-projection out_lr = bf16(in . pr^T)
+// (pr rank-major, `cols` values per rank), as two launches (partial sums per
+// column range into `part`, then their ordered sum).  Also writes out_pad
+// [rows, rank_pad(R)], the same values zero-padded, and the transposed copy
+// cp_dst [cp_rows, rank_pad(R)] of the rank-major operand cp.  `part` needs
+// quant_down_part_bytes(rows, cols, R) bytes.
 hipError_t launch_quant_down(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
-                             uint8_t* codes, uint8_t* scales, const LowRankPieces& pr,
-                             uint16_t* out_lr, float* part, unsigned long long* cnt,
-                             uint32_t epoch, hipStream_t st);
+                             uint8_t* codes, uint8_t* scales, const RankRows& pr, uint16_t* out_lr,
+                             uint16_t* out_pad, const RankRows& cp, int64_t cp_rows,
+                             uint16_t* cp_dst, float* part, hipStream_t st);
 size_t quant_down_part_bytes(int64_t rows, int64_t cols, int R);
-size_t quant_down_cnt_bytes(int64_t rows);
 
 // gemm.hip: out[m][j] = sum_red deq(a)[m][red] deq(b)[j][red] + sum_r lm[m][r] lo[j][r]
 // forward: a = Qrow(X) [M, K], b = Qtile(W) [N, K], lm = U, lo = [L2^T | B^T]
 // dgrad  : a = Qrow(dY) [M, N], b = Qtile(W)^T [K, N], lm = P, lo = [L1 | A]
+// The rank operands are the zero-padded copies, rank_pad(R) = 32 * nlr ranks.
 struct GemmArgs {
   int64_t M, RED, NOUT;           // rows, reduction length, output columns
   const uint8_t* a_codes;         // [M, RED/2]
   const uint8_t* a_scales;        // [M, RED/32]
   const uint8_t* b_codes;         // [NOUT, RED/2]
   const uint8_t* b_scales;        // [NOUT/32, RED/32] (one scale per 32x32 tile)
-  const uint16_t* lm;             // bf16 [M, R], may be null when R == 0
-  const uint16_t* lo0;            // bf16 [NOUT, r0]: ranks 0 .. r0-1 of lo
-  const uint16_t* lo1;            // bf16 [NOUT, R - r0]: ranks r0 .. R-1
-  int R, r0;
+  const uint16_t* lm;             // bf16 [M, 32 * nlr], may be null when nlr == 0
+  const uint16_t* lo;             // bf16 [NOUT, 32 * nlr]
+  int nlr;                        // 32-rank groups: 0 or 2 (rank_pad)
   uint16_t* out;                  // bf16 [M, NOUT]
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 
-// lora.hip: out[i][r] = sum_m big[m][i] * small[m][r0 + r], r < rl.
+// lora.hip: out[r][i] = sum_m big[m][i] * small[m][r0 + r], r < rl.
 struct LoraGradArgs {
   int64_t M, I;                   // rows, columns of big
   const uint16_t* big;            // bf16 [M, I]
   const uint16_t* small;          // bf16 [M, ld_small], columns r0 .. r0+rl used
   int ld_small, r0, rl;
-  void* out;                      // [I, rl]
+  void* out;                      // [rl, I]
   int out_f32;                    // 0 bf16, 1 fp32
   float* part;                    // workspace partials
   unsigned long long* cnt;        // workspace arrival slots (any contents)

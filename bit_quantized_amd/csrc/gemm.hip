@@ -14,34 +14,40 @@
 //   out[m][j] = sum_red deq(a)[m][red] deq(b)[j][red] + sum_r lm[m][r] lo[j][r]
 //   forward: a = Qrow(X) [M, K],  b = Qtile(W) [N, K],   lm = U, lo = [L2^T | B^T]
 //   dgrad  : a = Qrow(G) [M, N],  b = Qtile(W)^T [K, N], lm = P, lo = [L1 | A]
-// with lo given as two row-major pieces [NOUT, r0] and [NOUT, R - r0].
+// with lm and lo zero-padded to 32 * nlr ranks (written that way by the
+// fused quantize + down-projection kernel that runs just before).
 //
-// Tiling for gfx950: a 256-thread workgroup computes a 256x256 output tile;
+// Tiling for gfx950: a 256-thread workgroup computes 256x256 output tiles;
 // each of its 4 waves owns 128x128 = 4x4 tiles of the 32x32x64 scaled MXFP4
 // MFMA (fp32 accumulators in AGPRs, 16 per lane per tile).
-//   - The rank-R part goes first: its bf16 fragments are loaded straight
-//     from global memory (rank-contiguous rows, 16 bytes per lane) while the
-//     first operand stages are in flight, and 32x32x16 bf16 MFMAs put
-//     lm . lo^T into the accumulators.
-//   - Reduction steps of 128 elements (64 code bytes per row) go from global
-//     memory into LDS with buffer_load ... lds (no registers), 4 stages deep.
-//     Each step is split in two halves of 16 MFMAs (one 64-element chunk
-//     each); the LDS reads of the next chunk are issued before the MFMAs that
-//     need the previous one, and the 10 DMA instructions that refill a stage
-//     are spread between MFMAs so that their issue overlaps matrix work.  One
-//     barrier per step, between the halves, both publishes the next stage
-//     and frees the stage just read.
+//   - Persistent: one workgroup per CU walks its share of the output tiles.
+//     Its loads run as one pipeline across tile boundaries, so only the
+//     first tile waits for memory and each tile's output stores overlap the
+//     next tile's loads.
+//   - A tile is a sequence of 64-byte-per-row steps: first nlr rank steps
+//     (32 ranks of lm and lo in bf16, 32x32x16 bf16 MFMAs), then RED/128
+//     reduction steps (128 4-bit elements of a and b, scaled MXFP4 MFMAs).
+//     Both kinds have the same shape, so they share the load pipeline and
+//     the LDS layout.
+//   - Operands go from global memory into LDS with buffer_load ... lds (no
+//     registers), 4 stages deep.  Each step is split in two halves of 16
+//     MFMAs (one 64-element chunk each); the barrier between them publishes
+//     the next stage and frees the stage just read.  The 10 DMA instructions
+//     that refill a stage are spread between the MFMAs.
+//   - Even and odd steps use separate fragment and scale registers, so that
+//     no LDS read or VALU result ever targets a register an MFMA still in
+//     flight reads (such writes stall the wave until the MFMA is done).
 //   - Scales: one E8M0 byte per 32-block; a lane passes the word holding the
 //     bytes of its row and the step's blocks and selects the byte with
 //     op_sel.
 //   - Raw buffer loads: addresses past the end of a tensor read as zero,
 //     which covers ragged edges without branches.
-//   - Workgroups are mapped so that each XCD (own L2) works on a compact
-//     block of output tiles.
-//   - The accumulators are rounded to bf16 in registers (v_cvt_pk_bf16_f32,
-//     round to nearest even), neighbouring lanes swap halves so that each
-//     holds two adjacent columns of one row, and each store writes 4 bytes a
-//     lane.
+//   - Tiles are handed out so that the workgroups one XCD (own L2) runs at
+//     the same time work on a compact block of output tiles.
+//   - Output: the accumulators are rounded to bf16 in registers
+//     (v_cvt_pk_bf16_f32, round to nearest even), neighbouring lanes swap
+//     halves so that each holds two adjacent columns of one row, and 16-row
+//     strips go through a small per-wave LDS area to 16-byte global stores.
 #include "ft_device.hpp"
 #include "ft_kernels.h"
 
@@ -50,7 +56,7 @@ namespace ft {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 128;  // BK in 4-bit elements
-constexpr int ROWB = BK / 2;                 // 64 bytes of codes per row and step
+constexpr int ROWB = BK / 2;                 // 64 bytes per row and step
 constexpr uint32_t OOB = 0x80000000u;        // a buffer offset past every tensor
 
 // 16-byte chunk swizzle of 64-byte rows: the 16 rows one 16-lane group reads
@@ -65,27 +71,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, uint64_t b
 __device__ __forceinline__ u32x4 bload128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
 }
-__device__ __forceinline__ uint32_t bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
-}
 __device__ __forceinline__ uint32_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
 }
 
-// Workgroup i of n -> logical tile index, so that the workgroups the
-// hardware sends to one XCD (i % 8) get consecutive logical indices.
+// Workgroup i of n -> logical index, so that the workgroups the hardware
+// sends to one XCD (i % 8) get consecutive logical indices.
 __device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t n) {
   const uint32_t x = i & 7, j = i >> 3, q = n >> 3, r = n & 7;
   return x * q + (x < r ? x : r) + j;
 }
 
-// Output tile of this workgroup: XCD-contiguous logical index, then groups
-// of 4 m-tiles with the n-tiles inner, so that the workgroups one XCD runs at
-// the same time share A rows and B columns in its L2.
-__device__ __forceinline__ void tile_origin(int64_t M, int64_t NOUT, int64_t& m0, int64_t& j0) {
-  const uint32_t mt_n = static_cast<uint32_t>((M + BM - 1) / BM);
-  const uint32_t nt_n = static_cast<uint32_t>((NOUT + BN - 1) / BN);
-  const uint32_t lid = xcd_remap(blockIdx.x, mt_n * nt_n);
+// Logical tile index -> tile origin: groups of 4 m-tiles with the n-tiles
+// inner, so that consecutive indices share A rows and B columns.
+__device__ __forceinline__ void tile_coords(uint32_t lid, uint32_t mt_n, uint32_t nt_n, int64_t& m0,
+                                            int64_t& j0) {
   constexpr uint32_t GM = 4;
   const uint32_t grp_sz = GM * nt_n;
   const uint32_t gidx = lid / grp_sz, gfirst = gidx * GM;
@@ -95,147 +95,35 @@ __device__ __forceinline__ void tile_origin(int64_t M, int64_t NOUT, int64_t& m0
   j0 = static_cast<int64_t>(in_g / gm) * BN;
 }
 
-// ---------------------------------------------------------------------------
-// Rank-R part.  For the 32x32x16 bf16 MFMA a lane holds 8 consecutive ranks
-// (16q + 8*grp ...) of one row (l%32) of each operand.
-template <int NRQ>
-struct LowRankFrags {
-  u32x4 u[NRQ][4];   // lm rows  wm*128 + 32*i + l32
-  u32x4 v[NRQ][4];   // lo rows  wn*128 + 32*i + l32
-};
+// Byte selector for pair_bf16: even lanes keep the low halves (own, then
+// neighbour's), odd lanes the high halves (neighbour's, then own).
+__device__ __forceinline__ uint32_t pair_sel(int odd) { return odd ? 0x03020706u : 0x05040100u; }
 
-// Ranks are a multiple of 8 and the pieces meet at a multiple of 8: every
-// lane segment is 16 contiguous bytes of one piece.
-__device__ __forceinline__ bool lowrank_vec(const GemmArgs& g) { return (g.R & 7) == 0 && (g.r0 & 7) == 0; }
-
-// Issue the 16-byte fragment loads (no wait).  Ranks R .. 16*NRQ read as zero.
-template <int NRQ>
-__device__ __forceinline__ void load_lowrank(const GemmArgs& g, int64_t m0, int64_t j0,
-                                             LowRankFrags<NRQ>& f) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, grp = lane >> 5;
-  const int64_t M = g.M, NOUT = g.NOUT;
-  const int R = g.R, r0 = g.r0, r1 = g.R - g.r0;
-  const auto rm = rsrc(g.lm, static_cast<uint64_t>(M) * R * 2);
-  const auto rv0 = rsrc(g.lo0, static_cast<uint64_t>(NOUT) * r0 * 2);
-  const auto rv1 = rsrc(g.lo1, static_cast<uint64_t>(NOUT) * r1 * 2);
-#pragma unroll
-  for (int q = 0; q < NRQ; ++q) {
-    const int c8 = 16 * q + 8 * grp;        // first rank of this lane's segment
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int64_t m = m0 + wm * 128 + 32 * i + l32;
-      f.u[q][i] = bload128(rm, (c8 < R && m < M) ? static_cast<uint32_t>((m * R + c8) * 2) : OOB);
-      const int64_t j = j0 + wn * 128 + 32 * i + l32;
-      const bool jok = j < NOUT;
-      if (16 * q + 16 <= r0) {              // both halves in piece 0 (uniform)
-        f.v[q][i] = bload128(rv0, jok ? static_cast<uint32_t>((j * r0 + c8) * 2) : OOB);
-      } else if (16 * q >= r0) {            // both halves in piece 1 (uniform)
-        f.v[q][i] = bload128(rv1, (jok && c8 < R) ? static_cast<uint32_t>((j * r1 + c8 - r0) * 2) : OOB);
-      } else {                              // the pieces meet inside this rank group
-        const u32x4 x = bload128(rv0, (jok && c8 < r0) ? static_cast<uint32_t>((j * r0 + c8) * 2) : OOB);
-        const u32x4 y = bload128(rv1, (jok && c8 >= r0 && c8 < R)
-                                          ? static_cast<uint32_t>((j * r1 + c8 - r0) * 2) : OOB);
-        f.v[q][i] = x | y;
-      }
-    }
-  }
-}
-
-template <int NRQ>
-__device__ __forceinline__ void mma_lowrank(const LowRankFrags<NRQ>& f, f32x16 (&acc)[4][4]) {
-#pragma unroll
-  for (int q = 0; q < NRQ; ++q)
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_bf16_32x32x16(f.u[q][mt], f.v[q][nt], acc[mt][nt]);
-}
-
-// Any other ranks: both rank tiles are staged element by element in LDS
-// (rows of 16*NRQ ranks, zero-padded; `buf` holds 2 * 256 * 32 * NRQ bytes)
-// and the fragments are read from there.  The loops stay rolled, so few
-// registers are live.  Ends with a barrier; `buf` is free afterwards.
-template <int NRQ>
-__device__ __forceinline__ void lowrank_lds(const GemmArgs& g, int64_t m0, int64_t j0,
-                                            f32x16 (&acc)[4][4], uint8_t* buf) {
-  constexpr int RP = 16 * NRQ;
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, grp = lane >> 5;
-  const int64_t M = g.M, NOUT = g.NOUT;
-  const int R = g.R, r0 = g.r0, r1 = g.R - g.r0;
-  uint16_t* um = reinterpret_cast<uint16_t*>(buf);
-  uint16_t* vm = um + 256 * RP;
-#pragma unroll 1
-  for (int idx = t; idx < 256 * RP; idx += 256) {
-    const int row = idx / RP, r = idx % RP;
-    const int64_t m = m0 + row, j = j0 + row;
-    um[idx] = (m < M && r < R) ? g.lm[m * R + r] : uint16_t(0);
-    uint16_t v = 0;
-    if (j < NOUT && r < R) v = r < r0 ? g.lo0[j * r0 + r] : g.lo1[j * r1 + (r - r0)];
-    vm[idx] = v;
-  }
-  __syncthreads();
-#pragma unroll
-  for (int q = 0; q < NRQ; ++q) {
-    u32x4 u[4], v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      u[i] = lds_read_b128(um + (wm * 128 + 32 * i + l32) * RP + 16 * q + 8 * grp);
-      v[i] = lds_read_b128(vm + (wn * 128 + 32 * i + l32) * RP + 16 * q + 8 * grp);
-    }
-#pragma unroll
-    for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_bf16_32x32x16(u[mt], v[nt], acc[mt][nt]);
-  }
-  __syncthreads();
+// Round an accumulator pair to bf16 and swap halves with the neighbouring
+// lane: accumulator elements e, e+1 of tile column l32 are rows q, q+1; the
+// result is row q (even lane) or q+1 (odd lane) at columns l32&~1, +1.
+__device__ __forceinline__ uint32_t pair_bf16(float x0, float x1, uint32_t sel) {
+  const f32x2 x = {x0, x1};
+  const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+  const uint32_t o = static_cast<uint32_t>(
+      __builtin_amdgcn_update_dpp(0, static_cast<int>(w), 0xB1, 0xF, 0xF, false));
+  return __builtin_amdgcn_perm(o, w, sel);
 }
 
 // ---------------------------------------------------------------------------
-// bf16 output straight from the accumulators.  Accumulator element r of
-// tile (mt, nt) is row 8*(r/4) + 4*grp + r%4, column l32 of the 32x32 tile.
-// Rows 2p and 2p+1 of a column are rounded together into one word; lanes
-// 2c and 2c+1 then swap halves, so the even lane holds row 2p and the odd
-// lane row 2p+1, each for columns 2c and 2c+1.
-__device__ __forceinline__ void store_tile(const GemmArgs& g, const f32x16 (&acc)[4][4], int64_t m0,
-                                           int64_t j0) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int wm = wave >> 1, wn = wave & 1, l32 = lane & 31, grp = lane >> 5;
-  const int odd = lane & 1;
-  const int64_t M = g.M, NOUT = g.NOUT;
-  const auto ro = rsrc(g.out, static_cast<uint64_t>(M) * NOUT * 2);
-#pragma unroll
-  for (int mt = 0; mt < 4; ++mt)
-#pragma unroll
-    for (int nt = 0; nt < 4; ++nt) {
-      const int64_t col = j0 + wn * 128 + nt * 32 + (l32 & ~1);
-#pragma unroll
-      for (int p = 0; p < 8; ++p) {
-        const f32x2 x = {acc[mt][nt][2 * p], acc[mt][nt][2 * p + 1]};
-        const uint32_t w = __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
-        const uint32_t o = static_cast<uint32_t>(
-            __builtin_amdgcn_update_dpp(0, static_cast<int>(w), 0xB1, 0xF, 0xF, false));
-        const uint32_t val = odd ? ((o >> 16) | (w & 0xFFFF0000u)) : ((w & 0xFFFFu) | (o << 16));
-        const int64_t row = m0 + wm * 128 + mt * 32 + 8 * (p >> 1) + 4 * grp + 2 * (p & 1) + odd;
-        const uint32_t off = (row < M && col < NOUT) ? static_cast<uint32_t>((row * NOUT + col) * 2) : OOB;
-        __builtin_amdgcn_raw_buffer_store_b32(val, ro, static_cast<int>(off), 0, 0);
-      }
-    }
-}
-
-// ---------------------------------------------------------------------------
-// Pipelined kernel for reduction lengths that are a multiple of 128 (every
-// step holds whole 4-block scale words).
+// Pipelined persistent kernel, reduction lengths that are a multiple of 128.
 constexpr int NST = 4;                      // LDS stages
-constexpr int ST_A = BM * ROWB;             // 16 KB of A codes
-constexpr int ST_B = BN * ROWB;             // 16 KB of B codes
+constexpr int ST_A = BM * ROWB;             // 16 KB of A codes (or lm ranks)
+constexpr int ST_B = BN * ROWB;             // 16 KB of B codes (or lo ranks)
 constexpr int ST_SA = BM * 4;               // A scale words, one per row
 constexpr int ST_SB = 4 * 256;              // B scale words, one 256-byte region per wave
 constexpr int ST_BYTES = ST_A + ST_B + ST_SA + ST_SB;
-// Per wave and stage: 4 + 4 code DMAs and 1 + 1 scale DMAs, issued as two
+constexpr int OUT_WAVE = 16 * 256;          // per-wave output strip: 16 rows x 128 bf16
+// Per wave and stage: 4 + 4 row DMAs and 1 + 1 scale DMAs, issued as two
 // halves of 5 (A part, B part).
 constexpr int DMA_HALF = 5;
+// Global stores of one tile's output per lane (8 strips x 4).
+constexpr int STORES = 32;
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt[6:4] |
 // lgkmcnt[11:8] | vmcnt[5:4] << 14); fields not waited on are at their max.
@@ -250,72 +138,125 @@ __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uin
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FT_LDS void*)(lds), 4, (int)off, 0, 0, 0);
 }
 
-template <int NRQ>
-__global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * ST_BYTES];
+// Fragments and scales of one step: chunk 0 (a0, b0), chunk 1 (a1, b1).
+struct Frags {
+  u32x4 a0[4], b0[4], a1[4], b1[4];
+  uint32_t as[4], bs[4];
+};
 
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+template <int K> struct MfmaKind { static constexpr int v = K; };   // 0: MXFP4, 1: bf16 ranks
+
+// LR: the tiles start with two rank steps (64 padded ranks).  ODD: the
+// number of reduction steps RED/128 is odd.
+template <bool LR, bool ODD>
+__global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * ST_BYTES + 4 * OUT_WAVE];
+
+  const int t = threadIdx.x, lane = t & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, grp = lane >> 5;
+  const int l32 = lane & 31, grp = lane >> 5, odd = lane & 1;
   const int64_t M = g.M, RED = g.RED, NOUT = g.NOUT;
-  int64_t m0, j0;
-  tile_origin(M, NOUT, m0, j0);
+
+  const uint32_t mt_n = static_cast<uint32_t>((M + BM - 1) / BM);
+  const uint32_t nt_n = static_cast<uint32_t>((NOUT + BN - 1) / BN);
+  const uint32_t ntiles = mt_n * nt_n, G = gridDim.x, bid = blockIdx.x;
+  const uint32_t full = ntiles / G, nlast = ntiles % G;
+  const uint32_t my_tiles = full + (bid < nlast ? 1u : 0u);
+  constexpr int NLR = LR ? 2 : 0;
+  const int nks = static_cast<int>(RED / BK);
+  const int spt = nks + NLR;                             // steps per tile
+  const int total = static_cast<int>(my_tiles) * spt;
+  const bool tiny = spt < 3;                              // see the barrier waits
+
+  // k-th tile of this workgroup: rounds of G tiles, XCD-compact in a round
+  auto tile_of = [&](uint32_t k, int64_t& m0, int64_t& j0) {
+    const uint32_t n_round = k < full ? G : nlast;
+    tile_coords(k * G + xcd_remap(bid, n_round), mt_n, nt_n, m0, j0);
+  };
 
   const uint32_t row_bytes = static_cast<uint32_t>(RED >> 1);
   const uint32_t row_sc = static_cast<uint32_t>(RED >> 5);
-  const int nks = static_cast<int>(RED / BK);
-
+  constexpr uint32_t LR_BYTES = 64 * 2;                  // a padded rank row: 64 bf16
   const auto ra_codes = rsrc(g.a_codes, static_cast<uint64_t>(M) * row_bytes);
   const auto ra_sc = rsrc(g.a_scales, static_cast<uint64_t>(M) * row_sc);
   const auto rb_codes = rsrc(g.b_codes, static_cast<uint64_t>(NOUT) * row_bytes);
   const auto rb_sc = rsrc(g.b_scales, static_cast<uint64_t>(NOUT >> 5) * row_sc);
+  const auto r_lm = rsrc(g.lm, LR ? static_cast<uint64_t>(M) * LR_BYTES : 0);
+  const auto r_lo = rsrc(g.lo, LR ? static_cast<uint64_t>(NOUT) * LR_BYTES : 0);
 
-  // ---- rank-R fragments: loads go out before the operand stages
-  f32x16 acc[4][4];
-#pragma unroll
-  for (int a = 0; a < 4; ++a)
-#pragma unroll
-    for (int b = 0; b < 4; ++b)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-  LowRankFrags<(NRQ > 0 ? NRQ : 1)> lrf;
-  const bool lr_vec = NRQ > 0 && lowrank_vec(g);
-  if constexpr (NRQ > 0) {
-    if (lr_vec) load_lowrank<NRQ>(g, m0, j0, lrf);
-    else lowrank_lds<NRQ>(g, m0, j0, acc, lds);
-  }
-
-  // ---- per-lane DMA source offsets at step 0.  Instruction q of wave w
+  // Per-lane parts of the DMA source offsets (rows relative to the tile
+  // origin; A and B tiles have the same shape).  Instruction q of wave w
   // fills 1 KB of LDS (16 rows of 64 bytes); lane i lands at byte 16 i.
-  uint32_t a_src[4], b_src[4];
+  uint32_t code_row[4], lr_row[4];
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t row = 64 * wave + 16 * q + (lane >> 2), pch = lane & 3;
-    a_src[q] = static_cast<uint32_t>(m0 + row) * row_bytes + ((pch ^ swz16(row)) << 4);
-    b_src[q] = static_cast<uint32_t>(j0 + row) * row_bytes + ((pch ^ swz16(row)) << 4);
+    const uint32_t row = 64 * wave + 16 * q + (lane >> 2), ch = (lane & 3) ^ swz16(row);
+    code_row[q] = row * row_bytes + (ch << 4);
+    lr_row[q] = row * LR_BYTES + (ch << 4);
   }
-  const uint32_t sa_src = static_cast<uint32_t>(m0 + 64 * wave + lane) * row_sc;
-  uint32_t sb_src = OOB;
-  {
-    const uint32_t nb = static_cast<uint32_t>(j0 >> 5) + lane;
-    if (wave == 0 && lane < 8 && nb < (NOUT >> 5)) sb_src = nb * row_sc;
-  }
+  const uint32_t sa_lane = static_cast<uint32_t>(64 * wave + lane) * row_sc;
+  const uint32_t sb_lane = (wave == 0 && lane < 8) ? static_cast<uint32_t>(lane) * row_sc : OOB;
 
-  // DMA instruction `item` (0..9) of stage ks for this wave
-  auto dma = [&](int ks, int item) {
-    uint8_t* st = lds + (ks & (NST - 1)) * ST_BYTES;
-    const uint32_t k0 = static_cast<uint32_t>(ks) * BK;
-    const bool kin = k0 < RED;
-    if (item < 4)
-      dma16(ra_codes, st + (64 * wave + 16 * item) * ROWB, kin ? a_src[item] + (k0 >> 1) : OOB);
-    else if (item == 4)
-      dma4(ra_sc, st + ST_A + ST_B + 64 * wave * 4, kin ? sa_src + (k0 >> 5) : OOB);
-    else if (item < 9)
-      dma16(rb_codes, st + ST_A + (64 * wave + 16 * (item - 5)) * ROWB,
-            kin ? b_src[item - 5] + (k0 >> 1) : OOB);
-    else
-      dma4(rb_sc, st + ST_A + ST_B + ST_SA + wave * 256,
-           (kin && sb_src != OOB) ? sb_src + (k0 >> 5) : OOB);
+  // DMA cursor: the (tile, step) whose A or B half is loaded next, with the
+  // tile's base offsets.  A cursors use m0, B cursors j0.
+  struct Cursor {
+    int gs, s;
+    uint32_t k, code, sc, lr;
+  };
+  auto cursor_tile = [&](Cursor& c, bool is_b) {
+    int64_t m0 = 0, j0 = 0;
+    if (c.k < my_tiles) tile_of(c.k, m0, j0);
+    const uint32_t o = static_cast<uint32_t>(is_b ? j0 : m0);
+    c.code = o * row_bytes;
+    c.sc = is_b ? (o >> 5) * row_sc : o * row_sc;
+    c.lr = o * LR_BYTES;
+  };
+  auto cursor_next = [&](Cursor& c, bool is_b) {
+    ++c.gs;
+    if (++c.s == spt) {
+      c.s = 0;
+      ++c.k;
+      cursor_tile(c, is_b);
+    }
+  };
+  // The uniform part of one half (A or B) of cursor c's step, computed once
+  // per half: source, offsets (pushed out of range when the step lies past
+  // this workgroup's last tile) and the LDS region.  Each DMA instruction
+  // then only adds its lane's row offset.
+  struct HalfDma {
+    __amdgpu_buffer_rsrc_t rows, sc;
+    uint32_t base, sbase;
+    uint8_t* dst;        // this wave's rows of the stage's A or B part
+    uint8_t* sdst;       // this wave's scale words
+    bool lr;
+  };
+  auto half_dma = [&](const Cursor& c, bool is_b) {
+    HalfDma h;
+    const bool live = c.gs < total;
+    const bool lrs = LR && c.s < NLR;
+    const int ks = c.s - NLR;
+    h.lr = lrs;
+    h.rows = lrs ? (is_b ? r_lo : r_lm) : (is_b ? rb_codes : ra_codes);
+    h.sc = is_b ? rb_sc : ra_sc;
+    h.base = !live ? OOB : (lrs ? c.lr + static_cast<uint32_t>(c.s) * 64 : c.code + static_cast<uint32_t>(ks) * 64);
+    h.sbase = (!live || lrs) ? OOB : c.sc + static_cast<uint32_t>(ks) * 4;
+    uint8_t* st = lds + (c.gs & (NST - 1)) * ST_BYTES;
+    h.dst = st + (is_b ? ST_A : 0) + 64 * wave * ROWB;
+    h.sdst = is_b ? st + ST_A + ST_B + ST_SA + wave * 256 : st + ST_A + ST_B + 64 * wave * 4;
+    return h;
+  };
+  // DMA instruction `item` (0..4) of a half.  Offsets stay below 2^32: lane
+  // parts are below 2^31 and OOB is 2^31.
+  auto dma = [&](const HalfDma& h, int item, bool is_b) {
+    if (item < 4) {
+      const uint32_t lane_off = h.lr ? lr_row[item] : code_row[item];
+      dma16(h.rows, h.dst + item * 16 * ROWB, lane_off + h.base);
+    } else if (!is_b) {
+      dma4(h.sc, h.sdst, sa_lane + h.sbase);
+    } else {
+      dma4(h.sc, h.sdst, sb_lane == OOB ? OOB : sb_lane + h.sbase);
+    }
   };
   auto read_frags = [&](int buf, int c, u32x4 (&af)[4], u32x4 (&bf)[4]) {
     const uint8_t* st = lds + buf * ST_BYTES;
@@ -330,92 +271,218 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
       bf[i] = lds_read_b128(st + ST_A + row * ROWB + (((2 * c + grp) ^ swz16(row)) << 4));
     }
   };
+  // raw scale words (the lane's byte is selected later by a shift)
   auto read_scales = [&](int buf, uint32_t (&as)[4], uint32_t (&bs)[4]) {
     const uint8_t* st = lds + buf * ST_BYTES;
     const uint32_t* ssa = reinterpret_cast<const uint32_t*>(st + ST_A + ST_B);
     const uint32_t* ssb = reinterpret_cast<const uint32_t*>(st + ST_A + ST_B + ST_SA);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      as[i] = ssa[wm * 128 + i * 32 + l32] >> (8 * grp);
-      bs[i] = ssb[wn * 4 + i] >> (8 * grp);
+      as[i] = ssa[wm * 128 + i * 32 + l32];
+      bs[i] = ssb[wn * 4 + i];
     }
   };
 
+  f32x16 acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int b = 0; b < 4; ++b)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+
+  // Output of the finished tile (m0, j0): 8 strips of 16 rows per wave,
+  // then the accumulators are cleared for the next tile.
+  uint8_t* ostage = lds + NST * ST_BYTES + wave * OUT_WAVE;
+  const uint32_t psel = pair_sel(odd);
+  const auto r_out = rsrc(g.out, static_cast<uint64_t>(M) * NOUT * 2);
+  auto store_tile = [&](int64_t m0, int64_t j0) {
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        // accumulator elements 8h .. 8h+7 are rows 16h .. 16h+15 of tile mt
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const uint32_t v = pair_bf16(acc[mt][nt][8 * h + 2 * p], acc[mt][nt][8 * h + 2 * p + 1], psel);
+            const int row = 8 * (p >> 1) + 4 * grp + 2 * (p & 1) + odd;     // 0 .. 15
+            const int sw = (row & 1) | (((row >> 2) & 1) << 1);             // 64-byte segment swizzle
+            const int col = nt * 32 + (l32 & ~1);
+            *reinterpret_cast<uint32_t*>(ostage + row * 256 + (((col >> 5) ^ sw) << 6) + (col & 31) * 2) = v;
+          }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int idx = e * 64 + lane, row = idx >> 4, c16 = idx & 15;
+          const int sw = (row & 1) | (((row >> 2) & 1) << 1);
+          const u32x4 v = lds_read_b128(ostage + row * 256 + ((((c16 >> 2) ^ sw) << 6) | ((c16 & 3) << 4)));
+          const int64_t grow = m0 + wm * 128 + mt * 32 + 16 * h + row;
+          const int64_t gcol = j0 + wn * 128 + c16 * 8;
+          const uint32_t off = (grow < M && gcol < NOUT) ? static_cast<uint32_t>((grow * NOUT + gcol) * 2) : OOB;
+          __builtin_amdgcn_raw_buffer_store_b128(v, r_out, static_cast<int>(off), 0, 0);
+        }
+      }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  };
+
   // ---- prologue: stages 0..2 and the A half of stage 3
+  Cursor ca{0, 0, 0, 0, 0, 0}, cb{0, 0, 0, 0, 0, 0};
+  cursor_tile(ca, false);
+  cursor_tile(cb, true);
+  for (int s = 0; s < NST - 1; ++s) {
+    const HalfDma ha = half_dma(ca, false), hb = half_dma(cb, true);
 #pragma unroll
-  for (int s = 0; s < NST - 1; ++s)
+    for (int item = 0; item < DMA_HALF; ++item) dma(ha, item, false);
 #pragma unroll
-    for (int item = 0; item < 2 * DMA_HALF; ++item) dma(s, item);
+    for (int item = 0; item < DMA_HALF; ++item) dma(hb, item, true);
+    cursor_next(ca, false);
+    cursor_next(cb, true);
+  }
+  {
+    const HalfDma ha = half_dma(ca, false);
 #pragma unroll
-  for (int item = 0; item < DMA_HALF; ++item) dma(NST - 1, item);
-  if constexpr (NRQ > 0) {
-    if (lr_vec) mma_lowrank<NRQ>(lrf, acc);
+    for (int item = 0; item < DMA_HALF; ++item) dma(ha, item, false);
+    cursor_next(ca, false);
   }
   __builtin_amdgcn_sched_barrier(0);
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(5 * DMA_HALF, 0xF));   // this wave's stage 0 landed
   __builtin_amdgcn_s_barrier();                                  // ... and every wave's
   __builtin_amdgcn_sched_barrier(0);
-  u32x4 a0[4], b0[4];
-  uint32_t as[4], bs[4];
-  read_scales(0, as, bs);
-  read_frags(0, 0, a0, b0);
+  Frags E, O;
+  read_scales(0, E.as, E.bs);
+  read_frags(0, 0, E.a0, E.b0);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) { E.as[i] >>= 8 * grp; E.bs[i] >>= 8 * grp; }
   __builtin_amdgcn_sched_barrier(0);
 
-  // Step ks: stage ks is in LDS and its chunk-0 fragments and scales are in
-  // registers.  DMA order per wave: ..., B half of stage ks+3 (first half of
-  // step ks), A half of stage ks+4 (second half of step ks), ...  Past the
-  // end of the reduction they are zero-fill loads that are never read.
-  for (int ks = 0; ks < nks; ++ks) {
-    const int cur = ks & (NST - 1);
-    u32x4 a1[4], b1[4];
-    read_frags(cur, 1, a1, b1);
+  int gs = 0;   // global step of this workgroup
+
+  // One step.  Cur holds this step's chunk-0 fragments and scales; Nxt gets
+  // the next step's (Nxt may be Cur: one wait on in-flight MFMAs).  DMA
+  // order per wave: ..., B half of stage gs+3 (first half of step gs), A
+  // half of stage gs+4 (second half), [a tile's 32 output stores after its
+  // last step], ...  after_store: one of the last two steps ended a tile.
+  // Keeps a half's MFMAs ahead of what follows: without it the compiler may
+  // sink these side-effect-free instructions past the barrier and the DMA
+  // issues of the step, next to their first use, which serializes the step.
+  auto pin_acc = [&]() {
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) asm volatile("" : "+a"(acc[a][b]));
+  };
+  // Empty uses that extend live ranges: the registers an MFMA of the
+  // previous half may still read are not reused for values loaded now.
+  auto keep4 = [](const u32x4 (&x)[4]) {
+    asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
+  };
+  auto keep_s = [](const uint32_t (&x)[4]) {
+    asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
+  };
+  // SAME: Cur and Nxt are one register set (the odd step of a tile).
+  auto step = [&](Frags& Cur, Frags& Nxt, auto kind, bool after_store, auto same) {
+    constexpr bool RANK = decltype(kind)::v == 1;
+    constexpr bool SAME = decltype(same)::v == 1;
+    const int buf = gs & (NST - 1);
+    const HalfDma hb = half_dma(cb, true);
+    read_frags(buf, 1, Cur.a1, Cur.b1);
+    if constexpr (!SAME) { keep4(Nxt.a1); keep4(Nxt.b1); }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      acc[i >> 2][i & 3] =
-          mfma_fp4_32x32x64<0, 0>(a0[i >> 2], b0[i & 3], acc[i >> 2][i & 3], as[i >> 2], bs[i & 3]);
+      if constexpr (RANK)
+        acc[i >> 2][i & 3] = mfma_bf16_32x32x16(Cur.a0[i >> 2], Cur.b0[i & 3], acc[i >> 2][i & 3]);
+      else
+        acc[i >> 2][i & 3] = mfma_fp4_32x32x64<0, 0>(Cur.a0[i >> 2], Cur.b0[i & 3], acc[i >> 2][i & 3],
+                                                     Cur.as[i >> 2], Cur.bs[i & 3]);
       if (i % 3 == 1) {
         __builtin_amdgcn_sched_barrier(0);
-        dma(ks + NST - 1, DMA_HALF + i / 3);
+        dma(hb, i / 3, true);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    pin_acc();
     __builtin_amdgcn_sched_barrier(0);
-    // Own loads of stage ks+1 landed (the 4 younger halves may be in
-    // flight) and own reads of stage ks done; after the barrier the same
-    // holds for every wave: stage ks+1 is readable and stage ks reusable.
-    __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 * DMA_HALF, 0));
+    // Own loads of stage gs+1 landed (the 4 younger halves, and a tile's
+    // stores issued in the last two steps, may be in flight) and own reads
+    // of stage gs done; after the barrier the same holds for every wave:
+    // stage gs+1 is readable and stage gs reusable.  With fewer than 3
+    // steps per tile two store batches can be in that window: drain.
+    if (tiny) __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0));
+    else if (after_store) __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 * DMA_HALF + STORES, 0));
+    else __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 * DMA_HALF, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    uint32_t as2[4], bs2[4];
-    read_scales((ks + 1) & (NST - 1), as2, bs2);
-    read_frags((ks + 1) & (NST - 1), 0, a0, b0);
+    const HalfDma ha = half_dma(ca, false);
+    uint32_t ras[4], rbs[4];
+    read_scales((gs + 1) & (NST - 1), ras, rbs);
+    read_frags((gs + 1) & (NST - 1), 0, Nxt.a0, Nxt.b0);
+    if constexpr (!SAME) { keep4(Cur.a0); keep4(Cur.b0); }
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      acc[i >> 2][i & 3] =
-          mfma_fp4_32x32x64<2, 2>(a1[i >> 2], b1[i & 3], acc[i >> 2][i & 3], as[i >> 2], bs[i & 3]);
+      if constexpr (RANK)
+        acc[i >> 2][i & 3] = mfma_bf16_32x32x16(Cur.a1[i >> 2], Cur.b1[i & 3], acc[i >> 2][i & 3]);
+      else
+        acc[i >> 2][i & 3] = mfma_fp4_32x32x64<2, 2>(Cur.a1[i >> 2], Cur.b1[i & 3], acc[i >> 2][i & 3],
+                                                     Cur.as[i >> 2], Cur.bs[i & 3]);
       if (i % 3 == 1) {
         __builtin_amdgcn_sched_barrier(0);
-        dma(ks + NST, i / 3);
+        dma(ha, i / 3, false);
         __builtin_amdgcn_sched_barrier(0);
       }
     }
+    pin_acc();
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { as[i] = as2[i]; bs[i] = bs2[i]; }
+    for (int i = 0; i < 4; ++i) { Nxt.as[i] = ras[i] >> (8 * grp); Nxt.bs[i] = rbs[i] >> (8 * grp); }
+    if constexpr (!SAME) { keep_s(Cur.as); keep_s(Cur.bs); }
+    keep_s(Nxt.as);
+    keep_s(Nxt.bs);
+    cursor_next(cb, true);
+    cursor_next(ca, false);
+    ++gs;
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  const MfmaKind<0> fp4, two;
+  const MfmaKind<1> rank, one;
+  for (uint32_t k = 0; k < my_tiles; ++k) {
+    const bool after = k > 0;
+    if constexpr (LR) {
+      step(E, O, rank, after, two);
+      step(O, E, rank, after, two);
+      for (int p = 0; p < nks / 2; ++p) {
+        step(E, O, fp4, false, two);
+        step(O, E, fp4, false, two);
+      }
+    } else {
+      for (int p = 0; p < nks / 2; ++p) {
+        step(E, O, fp4, after && p == 0, two);
+        step(O, E, fp4, after && p == 0, two);
+      }
+    }
+    if constexpr (ODD) step(E, E, fp4, !LR && after && nks == 1, one);
+    int64_t m0, j0;
+    tile_of(k, m0, j0);
+    store_tile(m0, j0);
   }
   // DMAs into LDS must land before the workgroup can end
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0xF));
-  store_tile(g, acc, m0, j0);
 }
 
 // ---------------------------------------------------------------------------
 // Register-staged kernel for reduction lengths that are a multiple of 32
 // but not of 128: the last step is partial, so scale bytes are fetched one
 // by one and code chunks past the row end read as zero.  Two LDS buffers;
-// the loads of step k+1 are in flight while step k runs.
-template <int NRQ>
+// the loads of step k+1 are in flight while step k runs.  The rank part
+// comes first, from fragments loaded straight from the padded rank rows.
 __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (BM + BN) * ROWB];  // 64 KB
   uint8_t* const lds_a = lds;                      // 2 A buffers
@@ -423,11 +490,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
 
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, grp = lane >> 5;
+  const int l32 = lane & 31, grp = lane >> 5, odd = lane & 1;
   const int64_t M = g.M, RED = g.RED, NOUT = g.NOUT;
 
   int64_t m0, j0;
-  tile_origin(M, NOUT, m0, j0);
+  {
+    const uint32_t mt_n = static_cast<uint32_t>((M + BM - 1) / BM);
+    const uint32_t nt_n = static_cast<uint32_t>((NOUT + BN - 1) / BN);
+    tile_coords(xcd_remap(blockIdx.x, mt_n * nt_n), mt_n, nt_n, m0, j0);
+  }
 
   const uint32_t row_bytes = static_cast<uint32_t>(RED >> 1);
   const uint32_t row_sc = static_cast<uint32_t>(RED >> 5);
@@ -445,14 +516,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
     for (int b = 0; b < 4; ++b)
 #pragma unroll
       for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
-  if constexpr (NRQ > 0) {
-    if (lowrank_vec(g)) {
-      LowRankFrags<NRQ> lrf;
-      load_lowrank<NRQ>(g, m0, j0, lrf);
-      mma_lowrank<NRQ>(lrf, acc);
-    } else {
-      lowrank_lds<NRQ>(g, m0, j0, acc, lds);
+
+  // rank part: lane (row l32, half grp) holds ranks 16q + 8grp .. +7
+  const int lrb = g.nlr * 64;
+  const auto r_lm = rsrc(g.lm, static_cast<uint64_t>(M) * lrb);
+  const auto r_lo = rsrc(g.lo, static_cast<uint64_t>(NOUT) * lrb);
+  for (int q = 0; q < 2 * g.nlr; ++q) {
+    u32x4 u[4], v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int64_t m = m0 + wm * 128 + 32 * i + l32, j = j0 + wn * 128 + 32 * i + l32;
+      u[i] = bload128(r_lm, m < M ? static_cast<uint32_t>(m * lrb + 32 * q + 16 * grp) : OOB);
+      v[i] = bload128(r_lo, j < NOUT ? static_cast<uint32_t>(j * lrb + 32 * q + 16 * grp) : OOB);
     }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) acc[mt][nt] = mfma_bf16_32x32x16(u[mt], v[nt], acc[mt][nt]);
   }
 
   uint32_t a_off[4], b_off[4];
@@ -552,27 +632,49 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
     __syncthreads();
     take_scales();
   }
-  store_tile(g, acc, m0, j0);
+
+  // bf16 output, 4 bytes a lane (see pair_bf16)
+  const auto r_out = rsrc(g.out, static_cast<uint64_t>(M) * NOUT * 2);
+  const uint32_t psel = pair_sel(odd);
+#pragma unroll
+  for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt) {
+      const int64_t col = j0 + wn * 128 + nt * 32 + (l32 & ~1);
+#pragma unroll
+      for (int p = 0; p < 8; ++p) {
+        const uint32_t val = pair_bf16(acc[mt][nt][2 * p], acc[mt][nt][2 * p + 1], psel);
+        const int64_t row = m0 + wm * 128 + mt * 32 + 8 * (p >> 1) + 4 * grp + 2 * (p & 1) + odd;
+        const uint32_t off = (row < M && col < NOUT) ? static_cast<uint32_t>((row * NOUT + col) * 2) : OOB;
+        __builtin_amdgcn_raw_buffer_store_b32(val, r_out, static_cast<int>(off), 0, 0);
+      }
+    }
 }
+
+int g_cu_count[64];
 
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const uint32_t n = static_cast<uint32_t>(((g.NOUT + BN - 1) / BN) * ((g.M + BM - 1) / BM));
-  const bool pipe = (g.RED & 127) == 0;
-#define FT_G(NRQ)                                                                          \
-  do {                                                                                     \
-    if (pipe) hipLaunchKernelGGL((k_gemm_pipe<NRQ>), dim3(n), dim3(256), 0, st, g);         \
-    else hipLaunchKernelGGL((k_gemm<NRQ>), dim3(n), dim3(256), 0, st, g);                   \
-  } while (0)
-  switch ((g.R + 15) / 16) {
-    case 0: FT_G(0); break;
-    case 1: FT_G(1); break;
-    case 2: FT_G(2); break;
-    case 3: FT_G(3); break;
-    default: FT_G(4); break;
+  if ((g.RED & 127) == 0) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
+    if (g_cu_count[dev] <= 0) {
+      int cus = 0;
+      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
+        return hipErrorInvalidDevice;
+      g_cu_count[dev] = cus;
+    }
+    const uint32_t grid = n < static_cast<uint32_t>(g_cu_count[dev]) ? n : static_cast<uint32_t>(g_cu_count[dev]);
+    const bool odd = ((g.RED / BK) & 1) != 0;
+#define FT_GP(LR, ODD) hipLaunchKernelGGL((k_gemm_pipe<LR, ODD>), dim3(grid), dim3(256), 0, st, g)
+    if (g.nlr > 0) { if (odd) FT_GP(true, true); else FT_GP(true, false); }
+    else { if (odd) FT_GP(false, true); else FT_GP(false, false); }
+#undef FT_GP
+  } else {
+    hipLaunchKernelGGL(k_gemm, dim3(n), dim3(256), 0, st, g);
   }
-#undef FT_G
   return hipGetLastError();
 }
 

@@ -5,10 +5,10 @@
 //   dL/dB = (X A)^T G,    dL/dA = X^T (G B^T),
 // with X and G unquantized.  Here (X A) is the adapter part of the saved
 // down-projection U = bf16(X [L1|A]) and (G B^T) the adapter part of
-// P = bf16(G [L2;B]^T).  dA is kept [K, r] like A and dB is kept [N, r]
-// like the stored B^T, so both gradients have the form
-//   out[i][r] = sum_m big[m][i] * small[m][r0 + r]
-// with big = X (dA) or dY (dB^T) and small = P or U.  One launch computes
+// P = bf16(G [L2;B]^T).  Both gradients have the form
+//   g(i, r) = sum_m big[m][i] * small[m][r0 + r]
+// with big = X (dA) or dY (dB) and small = P or U, and are stored like the
+// factors, rank-major: out[r][i] (dA^T [r, K] and dB [r, N]).  One launch computes
 // both: the first workgroup columns cover dA, the rest dB.
 //
 // The reduction runs over tokens m, which is the row index of both
@@ -136,15 +136,16 @@ __global__ __launch_bounds__(256) void k_lora_grads(const LoraGradArgs pa, const
   if (t == 0) s_last = arrive_last(a.cnt + cb, a.epoch, gridDim.y);
   __syncthreads();
   if (!s_last) return;
+  // consecutive threads take consecutive columns i: coalesced out[r][i] stores
   for (int idx = t; idx < IB * (RP / 4); idx += 256) {
-    const int64_t i = i0 + idx / (RP / 4);
-    const int r = (idx % (RP / 4)) * 4;
+    const int64_t i = i0 + idx % IB;
+    const int r = (idx / IB) * 4;
     if (i >= I || r >= rl) continue;
     const f32x4 sum = sum_partials(a.part + i * RP + r, static_cast<uint64_t>(I) * RP, gridDim.y);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       if (r + k >= rl) break;
-      const int64_t o = i * rl + r + k;
+      const int64_t o = static_cast<int64_t>(r + k) * I + i;
       if (a.out_f32) static_cast<float*>(a.out)[o] = sum[k];
       else static_cast<uint16_t*>(a.out)[o] = f32_to_bf16_rne(sum[k]);
     }

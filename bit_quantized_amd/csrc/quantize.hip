@@ -199,33 +199,37 @@ __global__ __launch_bounds__(256) void k_quant_row32_t(const uint16_t* __restric
 }
 
 // ---------------------------------------------------------------------------
-// Fused 1x32 row quantization + rank-R down-projection.
+// Fused 1x32 row quantization + rank-R down-projection, in two kernels.
 //
-// out_lr[row][r] = bf16( sum_c in[row][c] * proj(c, r) ),  r < R,
-// proj(c, r) = r < r0 ? p0[c*s0c + r*s0r] : p1[c*s1c + (r-r0)*s1r].
+// out_lr[row][r] = bf16( sum_c in[row][c] * proj[r][c] ),  r < R,
+// with proj given rank-major (one row of `cols` values per rank) as two
+// pieces of r0 and r1 rows.
 //
-// Workgroup: 4 waves x 16 rows = 64 rows and KC = 128*NS columns.  Every
-// global load of the workgroup is issued up front: the lane's NS blocks of
-// 32 input values (one block per 128-column step: row = l%16, block l/16)
-// and the projection slice, which goes to LDS transposed (rank-major, the
-// column index contiguous).  Per step the lane quantizes its block and
-// feeds the same 32 values to four 16x16x32 bf16 MFMAs in the reduction
-// order (block, 8-element group, element), reading the projection in the
-// same order.  With more than one column range per row block, each
-// workgroup stores fp32 partials and the last one to arrive sums them in
-// range order (deterministic) and rounds once.
+// k_quant_down: a workgroup covers 64 rows (16 per wave) and KC = 128*NS
+// columns.  Every global load is issued up front: the lane's NS blocks of 32
+// input values (one block per 128-column step: row = l%16, block l/16) and
+// the projection slice [RP ranks x KC columns], which is copied to LDS with
+// 16-byte stores.  Per step the lane quantizes its block and feeds the same
+// 32 values to four 16x16x32 bf16 MFMAs in the reduction order (block,
+// 8-element group, element), reading the projection in the same order.  The
+// fp32 result of the column range goes to a workspace slab, laid out as the
+// accumulators are held (16 contiguous bytes per lane).
+//
+// k_rank_reduce (the next kernel on the stream, so every slab is visible):
+// sums the slabs of a 64-row block in column-range order (deterministic),
+// rounds once, and writes out_lr [rows, R] and out_pad [rows, rpad] (the
+// same values with zero ranks R .. rpad-1, for the 4-bit GEMM).  It also
+// copies the GEMM's other rank operand transposed, cp_dst[i][r] = cp[r][i],
+// zero-padded to rpad ranks.
 struct QDArgs {
   const uint16_t* in;
   uint32_t rows, cols;
   int64_t ld;
   uint8_t* codes;
   uint8_t* scales;
-  LowRankPieces pr;
+  RankRows pr;
   int R;
-  uint16_t* out_lr;
-  float* part;
-  unsigned long long* cnt;
-  uint32_t epoch;
+  float* part;          // [splits][rows/64][4 waves][NRG][64 lanes][4]
 };
 
 template <int NRG, int NS>
@@ -234,7 +238,6 @@ __global__ __launch_bounds__(256) void k_quant_down(const QDArgs a) {
   constexpr int KC = 128 * NS;          // columns of this workgroup
   constexpr int PT = KC + 8;            // LDS pitch (bf16) of the staged projection
   __shared__ __attribute__((aligned(16))) uint16_t pt[RP * PT];
-  __shared__ int s_last;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int g = lane >> 4, lr = lane & 15;
   const uint32_t rows = a.rows, cols = a.cols;
@@ -242,7 +245,7 @@ __global__ __launch_bounds__(256) void k_quant_down(const QDArgs a) {
   const uint32_t row = m0 + wave * 16 + lr;
   const uint32_t cbeg = blockIdx.y * KC;
   const int R = a.R;
-  const LowRankPieces& p = a.pr;
+  const RankRows& p = a.pr;
 
   // ---- issue the input loads of all steps
   const auto rin = make_rsrc(a.in, static_cast<uint64_t>(rows) * a.ld * 2);
@@ -250,69 +253,32 @@ __global__ __launch_bounds__(256) void k_quant_down(const QDArgs a) {
 #pragma unroll
   for (int s = 0; s < NS; ++s) {
     const uint32_t cb = cbeg + 128 * s + 32 * g;
-    const uint32_t off = cb < cols ? static_cast<uint32_t>((row * a.ld + cb) * 2) : BUF_OOB;
+    const uint32_t off = (cb < cols && row < rows) ? static_cast<uint32_t>((row * a.ld + cb) * 2) : BUF_OOB;
 #pragma unroll
     for (int i = 0; i < 4; ++i) v[s][i] = buf_load128(rin, off == BUF_OOB ? off : off + 16 * i);
   }
 
-  // ---- stage the projection slice: pt[r][c - cbeg] = proj(c, r)
-  // column-contiguous rank rows (V^T) give 8 columns per 16-byte load;
-  // rank-contiguous rows (D) give 8 ranks when both ranks are multiples of 8
-  const bool col_fast = p.s0c == 1 && p.s1c == 1 && (p.r0 == 0 || (p.s0r & 7) == 0) &&
-                        (p.r1 == 0 || (p.s1r & 7) == 0);
-  if (col_fast || ((p.r0 & 7) == 0 && (p.r1 & 7) == 0)) {
-    const auto r0s = make_rsrc(p.p0, piece_bytes(p.s0c, p.s0r, p.r0, cols));
-    const auto r1s = make_rsrc(p.p1, piece_bytes(p.s1c, p.s1r, p.r1, cols));
-    constexpr int CH = RP * KC / 8;      // 16-byte chunks of the padded slice
-    constexpr int PER = (CH + 255) / 256;
+  // ---- projection slice: pt[r][c - cbeg] = proj[r][c], 8 columns a chunk
+  {
+    const auto r0s = make_rsrc(p.p0, static_cast<uint64_t>(p.r0) * p.ld * 2);
+    const auto r1s = make_rsrc(p.p1, static_cast<uint64_t>(p.r1) * p.ld * 2);
+    constexpr int CPR = KC / 8;          // chunks per rank row
+    constexpr int PER = (RP * CPR + 255) / 256;
     u32x4 w[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const int c = t + 256 * e;
-      uint32_t off0 = BUF_OOB, off1 = BUF_OOB;
-      if (c < CH) {
-        if (col_fast) {                   // 8 consecutive columns of rank row r
-          const int r = c / (KC / 8), cc = (c % (KC / 8)) * 8;
-          const uint32_t col = cbeg + cc;
-          if (col < cols && r < R) {
-            if (r < p.r0) off0 = static_cast<uint32_t>((r * p.s0r + col) * 2);
-            else off1 = static_cast<uint32_t>(((r - p.r0) * p.s1r + col) * 2);
-          }
-        } else {                          // 8 consecutive ranks of column cc
-          const int rc = c / KC, cc = c % KC;
-          const uint32_t col = cbeg + cc;
-          if (col < cols && 8 * rc < R) {
-            if (8 * rc < p.r0) off0 = static_cast<uint32_t>((col * p.s0c + 8 * rc) * 2);
-            else off1 = static_cast<uint32_t>((col * p.s1c + 8 * rc - p.r0) * 2);
-          }
-        }
-      }
-      w[e] = off0 != BUF_OOB ? buf_load128(r0s, off0) : buf_load128(r1s, off1);
+      const int r = c / CPR, cc = (c % CPR) * 8;
+      const uint32_t col = cbeg + cc;
+      const bool ok = c < RP * CPR && col < cols;
+      const uint32_t o0 = (ok && r < p.r0) ? static_cast<uint32_t>((r * p.ld + col) * 2) : BUF_OOB;
+      const uint32_t o1 = (ok && r >= p.r0 && r < R) ? static_cast<uint32_t>(((r - p.r0) * p.ld + col) * 2) : BUF_OOB;
+      w[e] = buf_load128(r0s, o0) | buf_load128(r1s, o1);
     }
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const int c = t + 256 * e;
-      if (c >= CH) continue;
-      if (col_fast) {
-        const int r = c / (KC / 8), cc = (c % (KC / 8)) * 8;
-        *reinterpret_cast<u32x4*>(&pt[r * PT + cc]) = w[e];
-      } else {
-        const int rc = c / KC, cc = c % KC;
-#pragma unroll
-        for (int k = 0; k < 4; ++k) {
-          pt[(8 * rc + 2 * k) * PT + cc] = static_cast<uint16_t>(w[e][k]);
-          pt[(8 * rc + 2 * k + 1) * PT + cc] = static_cast<uint16_t>(w[e][k] >> 16);
-        }
-      }
-    }
-  } else {
-    for (int idx = t; idx < RP * KC; idx += 256) {
-      const int r = idx / KC, cc = idx % KC;
-      const uint32_t c = cbeg + cc;
-      uint16_t val = 0;
-      if (c < cols && r < R)
-        val = r < p.r0 ? p.p0[c * p.s0c + r * p.s0r] : p.p1[c * p.s1c + (r - p.r0) * p.s1r];
-      pt[r * PT + cc] = val;
+      if (c < RP * CPR) *reinterpret_cast<u32x4*>(&pt[(c / CPR) * PT + (c % CPR) * 8]) = w[e];
     }
   }
   __syncthreads();
@@ -347,43 +313,78 @@ __global__ __launch_bounds__(256) void k_quant_down(const QDArgs a) {
       }
   }
 
-  // acc[c][j] holds row m0 + 16*wave + 4*g + j, rank index 16*c + lr.
-  if (gridDim.y == 1) {
+  // acc[c][j] holds row m0 + 16*wave + 4*g + j, rank 16*c + lr
+  float* slab = a.part + ((static_cast<uint64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * 4 + wave) * (NRG * 256);
 #pragma unroll
-    for (int c = 0; c < NRG; ++c)
+  for (int c = 0; c < NRG; ++c) *reinterpret_cast<f32x4*>(slab + (c * 64 + lane) * 4) = acc[c];
+}
+
+struct RRArgs {
+  const float* part;
+  uint32_t rows, splits;
+  int R, rpad;
+  uint16_t* out_lr;
+  uint16_t* out_pad;
+  RankRows cp;
+  int64_t cp_rows;
+  uint16_t* cp_dst;
+};
+
+// cp_dst[i][r] = cp[r][i] (r < R) or 0 (R <= r < rpad), spread over the
+// grid: a thread makes one 16-byte chunk (8 ranks of row i) from 8 loads
+// that are coalesced across the lanes (consecutive lanes, consecutive i).
+__device__ __forceinline__ void copy_rank_operand(const RRArgs& a) {
+  const RankRows& p = a.cp;
+  const int cpr = a.rpad >> 3;                         // chunks per destination row
+  const uint64_t total = static_cast<uint64_t>(a.cp_rows) * cpr;
+  const uint64_t nthr = static_cast<uint64_t>(gridDim.x) * 256;
+  const uint64_t first = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x;
+  for (uint64_t e = first; e < total; e += nthr) {
+    const int c = static_cast<int>(e / a.cp_rows);       // chunk: ranks 8c .. 8c+7
+    const int64_t i = static_cast<int64_t>(e % a.cp_rows);
+    uint32_t w[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const uint32_t rr = m0 + wave * 16 + 4 * g + j;
-        const int r = 16 * c + lr;
-        if (rr < rows && r < R) a.out_lr[static_cast<uint64_t>(rr) * R + r] = f32_to_bf16_rne(acc[c][j]);
+    for (int k = 0; k < 4; ++k) {
+      uint32_t h[2];
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int r = 8 * c + 2 * k + q;
+        h[q] = r < p.r0 ? p.p0[r * p.ld + i] : (r < a.R ? p.p1[(r - p.r0) * p.ld + i] : uint16_t(0));
       }
-    return;
-  }
-  float* mypart = a.part + (static_cast<uint64_t>(blockIdx.y) * rows) * RP;
-#pragma unroll
-  for (int c = 0; c < NRG; ++c)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t rr = m0 + wave * 16 + 4 * g + j;
-      if (rr < rows) store_partial(&mypart[static_cast<uint64_t>(rr) * RP + 16 * c + lr], acc[c][j]);
+      w[k] = h[0] | (h[1] << 16);
     }
-  wait_stores();
-  __syncthreads();
-  if (t == 0) s_last = arrive_last(a.cnt + blockIdx.x, a.epoch, gridDim.y);
-  __syncthreads();
-  if (!s_last) return;
-  // Last workgroup of this row block: sum the column-range partials in
-  // range order (independent of arrival order) and round once.
-  for (int idx = t; idx < 64 * (RP / 4); idx += 256) {
-    const uint32_t rr = m0 + idx / (RP / 4);
-    const int r = (idx % (RP / 4)) * 4;
-    if (rr >= rows || r >= R) continue;
-    const f32x4 sum = sum_partials(a.part + static_cast<uint64_t>(rr) * RP + r,
-                                   static_cast<uint64_t>(rows) * RP, gridDim.y);
-#pragma unroll
-    for (int k = 0; k < 4; ++k)
-      if (r + k < R) a.out_lr[static_cast<uint64_t>(rr) * R + r + k] = f32_to_bf16_rne(sum[k]);
+    *reinterpret_cast<u32x4*>(a.cp_dst + i * a.rpad + 8 * c) = u32x4{w[0], w[1], w[2], w[3]};
   }
+}
+
+template <int NRG>
+__global__ __launch_bounds__(256) void k_rank_reduce(const RRArgs a) {
+  constexpr int RP = NRG * 16;
+  __shared__ float sum[64][RP + 1];
+  const int t = threadIdx.x;
+  const uint32_t m0 = blockIdx.x * 64;
+  const uint64_t slab = static_cast<uint64_t>(4) * NRG * 256;          // floats per row block
+  const uint64_t split_stride = static_cast<uint64_t>(gridDim.x) * slab;
+  const float* base = a.part + blockIdx.x * slab;
+  // item = (wave, c, lane): 4 rows (16 wave + 4 g + j) of rank 16 c + (lane & 15)
+  for (int item = t; item < 4 * NRG * 64; item += 256) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (uint32_t y = 0; y < a.splits; ++y) s += *reinterpret_cast<const f32x4*>(base + y * split_stride + item * 4);
+    const int wave = item / (NRG * 64), c = (item / 64) % NRG, lane = item % 64;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sum[16 * wave + 4 * (lane >> 4) + j][16 * c + (lane & 15)] = s[j];
+  }
+  __syncthreads();
+  const int R = a.R, rpad = a.rpad;
+  for (int idx = t; idx < 64 * rpad; idx += 256) {
+    const int rl = idx / rpad, r = idx % rpad;
+    const uint32_t rr = m0 + rl;
+    if (rr >= a.rows) continue;
+    const uint16_t v = r < R ? f32_to_bf16_rne(sum[rl][r]) : uint16_t(0);
+    if (r < R) a.out_lr[static_cast<uint64_t>(rr) * R + r] = v;
+    a.out_pad[static_cast<uint64_t>(rr) * rpad + r] = v;
+  }
+  copy_rank_operand(a);
 }
 
 // ---------------------------------------------------------------------------
@@ -417,7 +418,7 @@ hipError_t launch_quant_row32_t(const uint16_t* in, int64_t rows, int64_t cols, 
   return hipGetLastError();
 }
 
-// Columns per workgroup for the fused kernel: the largest of 512, 256, 128
+// Columns per workgroup of the fused kernel: the largest of 512, 256, 128
 // that still gives at least one workgroup per CU.
 static int quant_down_kc(int64_t rows, int64_t cols) {
   const int64_t rb = (rows + 63) / 64;
@@ -426,18 +427,27 @@ static int quant_down_kc(int64_t rows, int64_t cols) {
   return 128;
 }
 
+size_t quant_down_part_bytes(int64_t rows, int64_t cols, int R) {
+  if (R == 0) return 0;
+  const int64_t splits = (cols + quant_down_kc(rows, cols) - 1) / quant_down_kc(rows, cols);
+  const int64_t nrg = (R + 15) / 16;
+  return static_cast<size_t>(splits) * ((rows + 63) / 64) * 4 * nrg * 256 * sizeof(float);
+}
+
 hipError_t launch_quant_down(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
-                             uint8_t* codes, uint8_t* scales, const LowRankPieces& pr,
-                             uint16_t* out_lr, float* part, unsigned long long* cnt,
-                             uint32_t epoch, hipStream_t st) {
+                             uint8_t* codes, uint8_t* scales, const RankRows& pr, uint16_t* out_lr,
+                             uint16_t* out_pad, const RankRows& cp, int64_t cp_rows,
+                             uint16_t* cp_dst, float* part, hipStream_t st) {
+  const int R = pr.r0 + pr.r1;
   const int kc = quant_down_kc(rows, cols);
-  dim3 grid(static_cast<uint32_t>((rows + 63) / 64), static_cast<uint32_t>((cols + kc - 1) / kc));
-  QDArgs a{in, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols), ld, codes, scales, pr,
-           pr.r0 + pr.r1, out_lr, part, cnt, epoch};
-  const int nrg = (a.R + 15) / 16;
+  const uint32_t nrb = static_cast<uint32_t>((rows + 63) / 64);
+  const uint32_t splits = static_cast<uint32_t>((cols + kc - 1) / kc);
+  QDArgs a{in, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols), ld, codes, scales, pr, R, part};
+  dim3 grid(nrb, splits);
 #define FT_QD(NRG, NS) hipLaunchKernelGGL((k_quant_down<NRG, NS>), grid, dim3(256), 0, st, a)
 #define FT_QD_NS(NRG) \
   do { if (kc == 512) FT_QD(NRG, 4); else if (kc == 256) FT_QD(NRG, 2); else FT_QD(NRG, 1); } while (0)
+  const int nrg = (R + 15) / 16;
   switch (nrg) {
     case 1: FT_QD_NS(1); break;
     case 2: FT_QD_NS(2); break;
@@ -446,17 +456,17 @@ hipError_t launch_quant_down(const uint16_t* in, int64_t rows, int64_t cols, int
   }
 #undef FT_QD_NS
 #undef FT_QD
+  if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+  RRArgs b{part, static_cast<uint32_t>(rows), splits, R, rank_pad(R), out_lr, out_pad, cp, cp_rows, cp_dst};
+#define FT_RR(NRG) hipLaunchKernelGGL((k_rank_reduce<NRG>), dim3(nrb), dim3(256), 0, st, b)
+  switch (nrg) {
+    case 1: FT_RR(1); break;
+    case 2: FT_RR(2); break;
+    case 3: FT_RR(3); break;
+    default: FT_RR(4); break;
+  }
+#undef FT_RR
   return hipGetLastError();
 }
-
-size_t quant_down_part_bytes(int64_t rows, int64_t cols, int R) {
-  const int kc = quant_down_kc(rows, cols);
-  const int64_t ny = (cols + kc - 1) / kc;
-  if (ny <= 1 || R == 0) return 0;
-  const int RP = ((R + 15) / 16) * 16;
-  return static_cast<size_t>(ny) * rows * RP * sizeof(float);
-}
-
-size_t quant_down_cnt_bytes(int64_t rows) { return static_cast<size_t>((rows + 63) / 64) * 8; }
 
 }  // namespace ft

@@ -34,18 +34,19 @@ class QuantizedLinear:
 
     W_res (bf16 [N, K]) is quantized once on the device to 32x32 MXFP4 tiles
     by fourtune_quantize, which also writes the transposed codes the backward
-    reads.  The rank factors are kept in the library's storage: L1 [K, r_s],
-    L2t = L2^T [N, r_s] (frozen), A [K, r_l], Bt = B^T [N, r_l] (trainable).
+    reads.  The rank factors are kept in the library's rank-major storage:
+    L1t = L1^T [r_s, K], L2 [r_s, N] (frozen), At = A^T [r_l, K], B [r_l, N]
+    (trainable).
     """
 
-    def __init__(self, W_res: torch.Tensor, L1: torch.Tensor | None, L2t: torch.Tensor | None,
-                 A: torch.Tensor | None, Bt: torch.Tensor | None, stream=None):
+    def __init__(self, W_res: torch.Tensor, L1t: torch.Tensor | None, L2: torch.Tensor | None,
+                 At: torch.Tensor | None, B: torch.Tensor | None, stream=None):
         N, K = W_res.shape
         dev = W_res.device
         self.N, self.K = int(N), int(K)
-        self.r_s = 0 if L1 is None else int(L1.shape[1])
-        self.r_l = 0 if A is None else int(A.shape[1])
-        self.L1, self.L2t, self.A, self.Bt = L1, L2t, A, Bt
+        self.r_s = 0 if L1t is None else int(L1t.shape[0])
+        self.r_l = 0 if At is None else int(At.shape[0])
+        self.L1t, self.L2, self.At, self.B = L1t, L2, At, B
         self.w_codes = _empty((N, K // 2), torch.uint8, dev)
         self.w_scales = _empty((N // 32, K // 32), torch.uint8, dev)
         self.wt_codes = _empty((K, N // 2), torch.uint8, dev)
@@ -57,10 +58,10 @@ class QuantizedLinear:
 
     @classmethod
     def from_factors(cls, W_res, L1, L2, A, B, stream=None) -> "QuantizedLinear":
-        """From factors in the method's orientation (L2 [r_s, N], B [r_l, N]):
-        the up-projections are copied once into the [N, r] storage."""
+        """From factors in the method's orientation (L1 [K, r_s], A [K, r_l]):
+        the down-projections are copied once into the rank-major storage."""
         t = lambda x: None if x is None else x.t().contiguous()
-        return cls(W_res, L1, t(L2), A, t(B), stream=stream)
+        return cls(W_res, t(L1), L2, t(A), B, stream=stream)
 
     @property
     def R(self):
@@ -68,8 +69,8 @@ class QuantizedLinear:
 
     def desc(self, M: int) -> ops.FtLinear:
         return ops.make_linear(M, self.K, self.N, self.r_s, self.r_l, self.w_codes,
-                               self.w_scales, self.wt_codes, self.wt_scales, self.L1, self.L2t,
-                               self.A, self.Bt)
+                               self.w_scales, self.wt_codes, self.wt_scales, self.L1t, self.L2,
+                               self.At, self.B)
 
     def workspace(self, M: int, is_bwd: bool):
         key = (M, bool(is_bwd))
@@ -93,14 +94,14 @@ class QuantizedLinear:
 
     def backward(self, dY: torch.Tensor, X: torch.Tensor, U: torch.Tensor, need_dx: bool = True,
                  grad_f32: bool = False, stream=None, want_codes: bool = False):
-        """Returns (dX, dA, dBt, P) or (dX, dA, dBt, P, gq_codes, gq_scales);
-        dBt = dB^T [N, r_l], the layout of Bt."""
+        """Returns (dX, dAt, dB, P) or (dX, dAt, dB, P, gq_codes, gq_scales);
+        dAt = dA^T [r_l, K] and dB [r_l, N], the layouts of At and B."""
         M = int(dY.shape[0])
         dev = self.device
         dX = _empty((M, self.K), torch.bfloat16, dev) if need_dx else None
         gdt = torch.float32 if grad_f32 else torch.bfloat16
-        dA = _empty((self.K, self.r_l), gdt, dev) if self.r_l else None
-        dB = _empty((self.N, self.r_l), gdt, dev) if self.r_l else None
+        dA = _empty((self.r_l, self.K), gdt, dev) if self.r_l else None
+        dB = _empty((self.r_l, self.N), gdt, dev) if self.r_l else None
         P = _empty((M, max(self.R, 1)), torch.bfloat16, dev)
         qc = _empty((M, self.N // 2), torch.uint8, dev) if want_codes else None
         qs = _empty((M, self.N // 32), torch.uint8, dev) if want_codes else None
@@ -113,11 +114,11 @@ class QuantizedLinear:
 
 
 class FourTuneLinearFunction(torch.autograd.Function):
-    """Y = layer(X) with gradients for X, A and Bt (W_res, L1, L2 frozen).
-    A and Bt must be the tensors the layer holds."""
+    """Y = layer(X) with gradients for X, At and B (W_res, L1, L2 frozen).
+    At and B must be the tensors the layer holds."""
 
     @staticmethod
-    def forward(ctx, X, A, Bt, layer: QuantizedLinear):
+    def forward(ctx, X, At, B, layer: QuantizedLinear):
         Y, U = layer.forward(X.contiguous())
         ctx.save_for_backward(X, U)
         ctx.layer = layer

@@ -35,8 +35,8 @@ class FtLinear(ctypes.Structure):
                 ("r_stab", ctypes.c_int32), ("r_lora", ctypes.c_int32),
                 ("w_codes", ctypes.c_void_p), ("w_scales", ctypes.c_void_p),
                 ("wt_codes", ctypes.c_void_p), ("wt_scales", ctypes.c_void_p),
-                ("L1", ctypes.c_void_p), ("L2t", ctypes.c_void_p),
-                ("A", ctypes.c_void_p), ("Bt", ctypes.c_void_p)]
+                ("L1t", ctypes.c_void_p), ("L2", ctypes.c_void_p),
+                ("At", ctypes.c_void_p), ("B", ctypes.c_void_p)]
 
 
 _lib = None
@@ -106,13 +106,14 @@ def _check(status: int, where: str):
 
 
 def make_linear(M, K, N, r_stab, r_lora, w_codes, w_scales, wt_codes=None, wt_scales=None,
-                L1=None, L2t=None, A=None, Bt=None) -> FtLinear:
+                L1t=None, L2=None, At=None, B=None) -> FtLinear:
     """Fill the ft_linear descriptor from tensors (device) or raw addresses.
 
-    L2t and Bt are the up-projection factors stored [N, r] (L2^T, B^T)."""
+    The factors are rank-major: L1t = L1^T [r_stab, K], L2 [r_stab, N],
+    At = A^T [r_lora, K], B [r_lora, N]."""
     return FtLinear(int(M), int(K), int(N), int(r_stab), int(r_lora), _ptr(w_codes),
-                    _ptr(w_scales), _ptr(wt_codes), _ptr(wt_scales), _ptr(L1), _ptr(L2t),
-                    _ptr(A), _ptr(Bt))
+                    _ptr(w_scales), _ptr(wt_codes), _ptr(wt_scales), _ptr(L1t), _ptr(L2),
+                    _ptr(At), _ptr(B))
 
 
 def fourtune_quantize(mode, x, rows, cols, ld, codes, scales, codes_t=None, scales_t=None,

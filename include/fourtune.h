@@ -34,13 +34,14 @@
  *
  * Every product accumulates in fp32 and is rounded once to the output type.
  *
- * Storage of the factors: every low-rank factor is kept rank-contiguous
- * (row-major with the rank index innermost), so L1 and A are passed as is
- * ([K, r]) and L2 and B as their transposes L2^T [N, r_stab] and B^T
- * [N, r_lora] (the torch.nn.Linear.weight orientation of the up-projections).
- * dB is returned in the same [N, r_lora] layout.  The backward also takes the
- * weight's MXFP4 codes in transposed order, [K, N/2] with scales [K/32, N/32]
- * (FT_Q_TILE32 writes them beside the plain order): with one scale per 32x32
+ * Storage of the factors: every low-rank factor is stored rank-major, one
+ * row per rank: L1 and A as their transposes L1^T [r_stab, K] and A^T
+ * [r_lora, K] (the torch.nn.Linear.weight orientation of the
+ * down-projections), L2 [r_stab, N] and B [r_lora, N] as they are.  The
+ * adapter gradients come back the same way: dA^T [r_lora, K] and dB
+ * [r_lora, N].  The backward also takes the weight's MXFP4 codes in
+ * transposed order, [K, N/2] with scales [K/32, N/32] (FT_Q_TILE32 writes
+ * them beside the plain order): with one scale per 32x32
  * tile the transpose of the quantized weight is exactly these numbers.
  *
  * Memory layouts (all row-major, no padding between rows):
@@ -102,10 +103,10 @@ typedef struct {
   const uint8_t* w_scales;    /* Qtile(W_res) scales [N/32, K/32]                     */
   const uint8_t* wt_codes;    /* the same codes transposed [K, N/2]; backward only,  */
   const uint8_t* wt_scales;   /*   scales [K/32, N/32]; may be NULL for the forward   */
-  const uint16_t* L1;         /* bf16 [K, r_stab]  (frozen)                           */
-  const uint16_t* L2t;        /* bf16 [N, r_stab] = L2^T  (frozen)                    */
-  const uint16_t* A;          /* bf16 [K, r_lora]  (trainable)                        */
-  const uint16_t* Bt;         /* bf16 [N, r_lora] = B^T  (trainable)                  */
+  const uint16_t* L1t;        /* bf16 [r_stab, K] = L1^T  (frozen)                    */
+  const uint16_t* L2;         /* bf16 [r_stab, N]  (frozen)                           */
+  const uint16_t* At;         /* bf16 [r_lora, K] = A^T  (trainable)                  */
+  const uint16_t* B;          /* bf16 [r_lora, N]  (trainable)                        */
 } ft_linear;
 
 /* Quantize a bf16 matrix `in` [rows, cols] with row stride ld_in elements.
@@ -154,9 +155,9 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
  *   kernel 2 computes deq(Qrow(dY)) deq(Qtile(W_res)) + P D^T from the
  *   32x32-tile codes in transposed order (wt_codes, wt_scales) and writes dX
  *   (bf16 [M, K]) once;
- *   kernel 3 writes the adapter gradients dA = X^T P[:, r_stab:] ([K, r_lora])
- *   and dB, stored as dB^T = dY^T U[:, r_stab:] ([N, r_lora], the layout of
- *   Bt), in grad_dtype (FT_BF16 or FT_F32).
+ *   kernel 3 writes the adapter gradients, rank-major like At and B:
+ *   dA^T = P[:, r_stab:]^T X ([r_lora, K]) and dB = U[:, r_stab:]^T dY
+ *   ([r_lora, N]), in grad_dtype (FT_BF16 or FT_F32).
  * X and U_save are the forward's input and saved U.  dX may be NULL (no
  * input gradient; then wt_codes and wt_scales may be NULL).  dA, dB may be
  * NULL only when r_lora == 0.

@@ -60,14 +60,14 @@ class GpuCase:
                    gq_scales=u8(gs), w_codes=u8(self.layer.w_codes),
                    w_scales=u8(self.layer.w_scales), wt_codes=u8(self.layer.wt_codes),
                    wt_scales=u8(self.layer.wt_scales))
-        # dB comes back as dB^T [N, r_l] (the layout of the stored B^T)
+        # dA comes back as dA^T [r_l, K] (the layout of the stored A^T)
         if self.c.r_l:
             if grad_f32:
-                out["dA"] = dA.cpu().numpy()
-                out["dB"] = np.ascontiguousarray(dB.cpu().numpy().T)
+                out["dA"] = np.ascontiguousarray(dA.cpu().numpy().T)
+                out["dB"] = dB.cpu().numpy()
             else:
-                out["dA"] = bits_of(dA)
-                out["dB"] = np.ascontiguousarray(bits_of(dB).T)
+                out["dA"] = np.ascontiguousarray(bits_of(dA).T)
+                out["dB"] = bits_of(dB)
         return out
 
 

@@ -59,8 +59,8 @@ def test_quantize_argument_errors():
 
 
 def _layer(M=64, K=64, N=64, rs=8, rl=8, **kw):
-    d = dict(w_codes=A16, w_scales=A16, wt_codes=A16, wt_scales=A16, L1=A16, L2t=A16, A=A16,
-             Bt=A16)
+    d = dict(w_codes=A16, w_scales=A16, wt_codes=A16, wt_scales=A16, L1t=A16, L2=A16, At=A16,
+             B=A16)
     d.update(kw)
     return ops.make_linear(M, K, N, rs, rl, **d)
 
@@ -85,9 +85,9 @@ def test_linear_shape_errors():
 
 def test_linear_pointer_errors():
     assert _fwd(_layer(w_codes=None)) == ops.FT_EINVAL
-    assert _fwd(_layer(L1=None)) == ops.FT_EINVAL
-    assert _fwd(_layer(Bt=None)) == ops.FT_EINVAL
-    assert _fwd(_layer(L2t=None)) == ops.FT_EINVAL
+    assert _fwd(_layer(L1t=None)) == ops.FT_EINVAL
+    assert _fwd(_layer(B=None)) == ops.FT_EINVAL
+    assert _fwd(_layer(L2=None)) == ops.FT_EINVAL
     assert _fwd(_layer(wt_scales=None)) == ops.FT_EINVAL        # transposed codes without scales
     assert _bwd(_layer(wt_codes=None, wt_scales=None)) == ops.FT_EINVAL   # dX needs them
     assert _fwd(_layer(wt_codes=A16 + 4)) == ops.FT_EALIGN
@@ -95,13 +95,13 @@ def test_linear_pointer_errors():
     assert _fwd(_layer(), U=None) == ops.FT_EINVAL
     assert _fwd(_layer(), qc=A16) == ops.FT_EINVAL              # codes without scales
     assert _fwd(_layer(), X=A16 + 8) == ops.FT_EALIGN
-    assert _fwd(_layer(A=A16 + 4)) == ops.FT_EALIGN
+    assert _fwd(_layer(At=A16 + 4)) == ops.FT_EALIGN
     assert _bwd(_layer(), dY=None) == ops.FT_EINVAL
     assert _bwd(_layer(), dA=None) == ops.FT_EINVAL
     assert _bwd(_layer(), gdt=7) == ops.FT_EINVAL
     assert _bwd(_layer(), dX=A16 + 2) == ops.FT_EALIGN
     # ranks zero: no low-rank pointers are needed
-    L0 = _layer(rs=0, rl=0, L1=None, L2t=None, A=None, Bt=None)
+    L0 = _layer(rs=0, rl=0, L1t=None, L2=None, At=None, B=None)
     assert _fwd(L0, U=None, wsb=0) == ops.FT_EWORKSPACE
 
 

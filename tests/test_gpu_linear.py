@@ -74,15 +74,15 @@ def test_autograd_function_matches_library():
     say("case autograd")
     g = GpuCase(c)
     X = g.X.clone().requires_grad_(True)
-    A = g.layer.A.clone().requires_grad_(True)
-    Bt = g.layer.Bt.clone().requires_grad_(True)
-    Y = FourTuneLinearFunction.apply(X, A, Bt, g.layer)
+    At = g.layer.At.clone().requires_grad_(True)
+    B = g.layer.B.clone().requires_grad_(True)
+    Y = FourTuneLinearFunction.apply(X, At, B, g.layer)
     Y.backward(g.dY)
     ref = g.run()
     np.testing.assert_array_equal(bits_of(Y), ref["Y"])
     np.testing.assert_array_equal(bits_of(X.grad), ref["dX"])
-    np.testing.assert_array_equal(bits_of(A.grad), ref["dA"])
-    np.testing.assert_array_equal(bits_of(Bt.grad).T, ref["dB"])
+    np.testing.assert_array_equal(bits_of(At.grad).T, ref["dA"])
+    np.testing.assert_array_equal(bits_of(B.grad), ref["dB"])
 
 
 def _rows(M, n=48, seed=0):
