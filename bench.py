@@ -42,12 +42,22 @@ def parse():
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--sets", type=int, default=4)
-    ap.add_argument("--cpu-rows", type=int, default=1024,
+    ap.add_argument("--cpu-rows", type=int, default=4608,
                     help="tokens of the QKV layer the CPU oracle baseline runs")
+    ap.add_argument("--cpu-reps", type=int, default=3,
+                    help="timed repetitions of the CPU oracle step (the rate is their mean)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stress", action="store_true")
     ap.add_argument("--only", choices=["step", "stress"], default=None,
                     help="run only one part (for profiler runs)")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain bf16 elementwise copy of known size (the reference "
+                         "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE to bytes)")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print a markdown summary of a rocprofv3 --kernel-trace --stats run and exit")
+    ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print per-launch HBM traffic (JSON) from two rocprofv3 --pmc runs of "
+                         "this script with --copy-probe (FETCH_SIZE, then WRITE_SIZE) and exit")
     return ap.parse_args()
 
 
@@ -101,8 +111,9 @@ def load_traffic(kernel, sha):
     return e.get("hbm_bytes_per_launch")
 
 
-def cpu_baseline(rows):
-    """The oracle as it stands, on the first `rows` tokens of the same layer."""
+def cpu_baseline(rows, reps=1):
+    """The oracle as it stands, on the first `rows` tokens of the same layer,
+    run `reps` times back to back."""
     import numpy as np
     from threadpoolctl import threadpool_info
     from bit_quantized_amd import synth
@@ -113,23 +124,150 @@ def cpu_baseline(rows):
     wc, ws = OQ.quantize_tile32(c.W_res)   # offline weight prep, not timed
     X, dY = c.X[:rows], c.dY[:rows]
     t0 = time.perf_counter()
-    f = OL.linear_fwd(X, wc, ws, c.L1, c.L2, c.A, c.B)
-    OL.linear_bwd(dY, X, f["U"], wc, ws, c.L1, c.L2, c.A, c.B)
-    dt = time.perf_counter() - t0
+    for _ in range(reps):
+        f = OL.linear_fwd(X, wc, ws, c.L1, c.L2, c.A, c.B)
+        OL.linear_bwd(dY, X, f["U"], wc, ws, c.L1, c.L2, c.A, c.B)
+    dt = (time.perf_counter() - t0) / reps
     flop = sum(v["flop"] for v in layer_work(rows, c.K, c.N, c.r_s, c.r_l).values())
     threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
                   or [1])
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
-            "seconds": round(dt, 3),
-            "sample": f"float64 numpy oracle, forward+backward of the same QKV linear on its first "
-                      f"{rows} of {c.M} tokens (X and dY quantization, both 4-bit products, "
+            "seconds_per_step": round(dt, 3), "reps": reps,
+            "sample": f"float64 numpy oracle, {reps} x forward+backward of the same QKV linear on "
+                      f"its first {rows} of {c.M} tokens (X and dY quantization, both 4-bit products, "
                       f"low-rank branches, adapter gradients); the oracle's 32x32 weight "
                       f"quantization runs before the timer as offline preparation",
             "host_cpus": len(os.sched_getaffinity(0))}
 
 
+# ------------------------------------------------------------ rocprofv3 summaries
+def _csv_rows(d, suffix):
+    import csv
+    import glob
+    rows = []
+    for f in sorted(glob.glob(os.path.join(d, "**", "*" + suffix), recursive=True)):
+        with open(f) as fh:
+            rows.extend(csv.DictReader(fh))
+    return rows
+
+
+def _short(name):
+    """Kernel name without its argument list."""
+    return name.replace("(anonymous namespace)::", "").split("(")[0].replace("void ", "")
+
+
+def summarize_trace(d):
+    """Markdown table of a `rocprofv3 --kernel-trace --stats` run."""
+    rows = _csv_rows(d, "kernel_stats.csv")
+    out = ["| kernel | calls | avg us | min us | max us | share |", "|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.2f} | "
+                   f"{float(r['MinNs']) / 1e3:.2f} | {float(r['MaxNs']) / 1e3:.2f} | "
+                   f"{float(r['Percentage']):.1f}% |")
+    return "\n".join(out)
+
+
+COPY_PROBE_ELEMS = 1 << 27      # bf16 elements of the reference copy (256 MiB each way)
+
+
+def _step_kernel(kname, state):
+    """Name of the step kernel a dispatch belongs to (None if it is not one).
+
+    Dispatches are taken in order: each quantize + down-projection opens a
+    new phase (forward, then backward), and the reduction kernel after it
+    belongs to the same launch.  Returns (name, opens_launch)."""
+    if "k_quant_down" in kname:
+        state["fwd"] = not state.get("fwd", False)
+        return ("fwd_quant_down" if state["fwd"] else "bwd_quant_down"), True
+    if "k_rank_reduce" in kname:
+        return ("fwd_quant_down" if state.get("fwd") else "bwd_quant_down"), False
+    if "k_gemm" in kname:
+        return ("fwd_gemm" if state.get("fwd") else "bwd_gemm_dgrad"), True
+    if "k_lora" in kname:
+        return "bwd_lora_grads", True
+    return None, False
+
+
+def summarize_trace_by_step_kernel(d):
+    """Mean duration per launch of each step kernel from a kernel trace
+    (the quantize + down-projection launch is its two kernels together)."""
+    rows = sorted(_csv_rows(d, "kernel_trace.csv"), key=lambda r: int(r["Dispatch_Id"]))
+    tot, n, state = {}, {}, {}
+    for r in rows:
+        name, opens = _step_kernel(r["Kernel_Name"], state)
+        if name is None:
+            continue
+        tot[name] = tot.get(name, 0.0) + (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+        n[name] = n.get(name, 0) + int(opens)
+    return {k: (round(tot[k] / n[k], 2), n[k]) for k in tot if n.get(k)}
+
+
+def _pmc_per_step_kernel(d, counter):
+    """Mean counter value per launch of each step kernel, and of the reference copy."""
+    rows = sorted(_csv_rows(d, "counter_collection.csv"), key=lambda r: int(r["Dispatch_Id"]))
+    acc, n_launch, state = {}, {}, {}
+    copy = []
+    for r in rows:
+        if r["Counter_Name"] != counter:
+            continue
+        k, v = r["Kernel_Name"], float(r["Counter_Value"])
+        if "neg_kernel" in k:
+            copy.append(v)
+            continue
+        name, opens = _step_kernel(k, state)
+        if name is None:
+            continue
+        acc[name] = acc.get(name, 0.0) + v
+        n_launch[name] = n_launch.get(name, 0) + int(opens)
+    per = {k: acc[k] / n_launch[k] for k in acc if n_launch.get(k)}
+    return per, (sum(copy) / len(copy) if copy else None)
+
+
+def summarize_pmc(fetch_dir, write_dir):
+    """HBM bytes per launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of each
+    kernel, each divided by the same counter's reading per byte of a plain
+    bf16 copy of COPY_PROBE_ELEMS elements."""
+    fr, fc = _pmc_per_step_kernel(fetch_dir, "FETCH_SIZE")
+    wr, wc = _pmc_per_step_kernel(write_dir, "WRITE_SIZE")
+    if fc is None or wc is None:
+        raise SystemExit("no reference copy in the counter runs (run them with --copy-probe)")
+    nbytes = 2 * COPY_PROBE_ELEMS
+    f_fac = fc * 1024 / nbytes
+    w_fac = wc * 1024 / nbytes
+    sha = source_sha()
+    out = {"_scaling": {"copy_bytes_each_way": nbytes, "fetch_KiB_per_copy": fc,
+                        "write_KiB_per_copy": wc, "fetch_factor": round(f_fac, 4),
+                        "write_factor": round(w_fac, 4)}}
+    for k in fr:
+        fb = fr[k] * 1024 / f_fac
+        wb = wr.get(k, 0.0) * 1024 / w_fac
+        out[k] = {"fetch_bytes": round(fb), "write_bytes": round(wb),
+                  "hbm_bytes_per_launch": round(fb + wb), "source_sha": sha}
+    return out
+
+
+def copy_probe(dev, stream):
+    import torch
+    src = torch.ones(COPY_PROBE_ELEMS, dtype=torch.bfloat16, device=dev)
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.neg(src, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
+
+
 def main():
     a = parse()
+    if a.summarize_trace:
+        print(summarize_trace(a.summarize_trace))
+        print("\nPer step kernel (the quantize + down-projection launch is its two kernels):\n")
+        print("| step kernel | launches | avg us |\n|---|---|---|")
+        for k, (us, cnt) in summarize_trace_by_step_kernel(a.summarize_trace).items():
+            print(f"| {k} | {cnt} | {us} |")
+        return
+    if a.summarize_pmc:
+        print(json.dumps(summarize_pmc(*a.summarize_pmc), indent=1))
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
         print(json.dumps({"error": "this benchmark runs on one GPU only: a step is one GPU's "
@@ -149,6 +287,9 @@ def main():
 
     def log(*x):
         print(*x, file=sys.stderr, flush=True)
+
+    if a.copy_probe:
+        copy_probe(dev, stream)
 
     # ------------------------------------------------------------ layer step
     c = synth.qkv_case()
@@ -309,7 +450,7 @@ def main():
     # ------------------------------------------------------------ CPU oracle
     if not a.no_cpu_baseline and a.only is None:
         log(f"bench: CPU oracle baseline on {a.cpu_rows} tokens")
-        out["cpu_baseline"] = cpu_baseline(a.cpu_rows)
+        out["cpu_baseline"] = cpu_baseline(a.cpu_rows, a.cpu_reps)
     print(json.dumps(out), flush=True)
 
 
