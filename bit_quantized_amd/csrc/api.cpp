@@ -5,8 +5,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <atomic>
-#include <chrono>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -22,17 +20,6 @@ inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 
 constexpr int64_t kMaxDim = int64_t(1) << 30;
 // Kernels address tensors with 32-bit buffer offsets.
 constexpr int64_t kMaxBytes = (int64_t(1) << 31) - 1;
-
-// Per-call tag for the workspace arrival counters of split reductions.  A
-// process-wide counter started at a time-derived value, so counters left in
-// a reused workspace by an earlier call or process never match.
-std::atomic<uint32_t> g_epoch{static_cast<uint32_t>(
-    std::chrono::steady_clock::now().time_since_epoch().count() * 2654435761ull)};
-uint32_t next_epoch() {
-  uint32_t e;
-  do { e = g_epoch.fetch_add(1) + 1; } while (e == 0);
-  return e;
-}
 
 // 1 = current device is gfx950, 0 = not, -1 = unknown yet.  Cached per device.
 int g_arch_ok[64];
@@ -159,7 +146,7 @@ FwdLayout fwd_layout(const ft_linear* L) {
 }
 
 struct BwdLayout {
-  size_t gq_codes, gq_scales, P, p_pad, d_pad, part, dA_part, dA_cnt, dB_part, dB_cnt, total;
+  size_t gq_codes, gq_scales, P, p_pad, d_pad, part, dA_part, dB_part, total;
 };
 BwdLayout bwd_layout(const ft_linear* L) {
   const int R = L->r_stab + L->r_lora;
@@ -174,9 +161,7 @@ BwdLayout bwd_layout(const ft_linear* L) {
   o.d_pad = off; off += align_up(static_cast<size_t>(L->K) * rp * 2);     // [L1 | A], padded
   o.part = off; off += align_up(ft::quant_down_part_bytes(L->M, L->N, R));
   o.dA_part = off; off += align_up(rl ? ft::lora_grad_part_bytes(L->M, L->K, rl) : 0);
-  o.dA_cnt = off; off += align_up(rl ? ft::lora_grad_cnt_bytes(L->K) : 0);
   o.dB_part = off; off += align_up(rl ? ft::lora_grad_part_bytes(L->M, L->N, rl) : 0);
-  o.dB_cnt = off; off += align_up(rl ? ft::lora_grad_cnt_bytes(L->N) : 0);
   o.total = off;
   return o;
 }
@@ -343,18 +328,14 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
   }
   if (rl > 0) {
     const int f32 = grad_dtype == FT_F32 ? 1 : 0;
-    const uint32_t epoch = next_epoch();
     ft::LoraGradArgs a{};
     a.M = L->M; a.I = L->K; a.big = X; a.small = P; a.ld_small = R; a.r0 = L->r_stab; a.rl = rl;
     a.out = dA; a.out_f32 = f32;
     a.part = reinterpret_cast<float*>(ws + lay.dA_part);
-    a.cnt = reinterpret_cast<unsigned long long*>(ws + lay.dA_cnt);
-    a.epoch = epoch;
     ft::LoraGradArgs b = a;
     b.I = L->N; b.big = dY; b.small = U_save;
     b.out = dB;
     b.part = reinterpret_cast<float*>(ws + lay.dB_part);
-    b.cnt = reinterpret_cast<unsigned long long*>(ws + lay.dB_cnt);
     Timed tm("bwd_lora_grads", st);
     if (tm.done(ft::launch_lora_grads(a, b, st)) != hipSuccess) return FT_EDEVICE;
   }

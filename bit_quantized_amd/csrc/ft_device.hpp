@@ -129,63 +129,6 @@ __device__ __forceinline__ u32x4 lds_read_b128(const void* p) {
   return *(const FT_LDS u32x4*)(p);
 }
 
-// ---------------------------------------------------------------- split reductions
-// Arrival counter of one group of `n` workgroups that each wrote a partial
-// result.  The 64-bit slot holds (epoch << 32 | arrivals); a slot still
-// holding another call's epoch (or anything else) counts as zero arrivals,
-// so the workspace needs no clearing.  Returns true in exactly one
-// workgroup of the group: the last to arrive.  Call from one thread after
-// the partial stores and a release fence.
-__device__ __forceinline__ bool arrive_last(unsigned long long* slot, uint32_t epoch, uint32_t n) {
-  const unsigned long long tag = static_cast<unsigned long long>(epoch) << 32;
-  unsigned long long old = __hip_atomic_load(slot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  while (true) {
-    const bool same = (old & 0xFFFFFFFF00000000ull) == tag;
-    const unsigned long long nw = same ? old + 1 : tag | 1ull;
-    const unsigned long long seen = atomicCAS(slot, old, nw);
-    if (seen == old) return (same ? (old & 0xFFFFFFFFull) + 1 : 1ull) == n;
-    old = seen;
-  }
-}
-
-// Cross-workgroup partial results.  The workgroups of one split reduction
-// may run on different XCDs, whose L2 caches are not coherent with each
-// other.  Partials are therefore written with device-scope stores (sc1:
-// written through to the device coherence point) and read back with
-// device-scope loads; each writer waits for its stores to complete before
-// the arrival atomic.  This avoids an agent-scope release fence, which on
-// this part writes back the whole L2 of the XCD.
-__device__ __forceinline__ void store_partial(float* p, float v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ float load_partial(const float* p) {
-  return __hip_atomic_load(const_cast<float*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-// Wait until every store this wave issued has completed.
-__device__ __forceinline__ void wait_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
-
-// Sum of `ny` fp32x4 partials p[y * stride] for y = 0 .. ny-1, added in
-// order of y (the result does not depend on which workgroup reduces);
-// loads go out in batches of 8 so that a batch costs one memory latency.
-__device__ __forceinline__ f32x4 sum_partials(const float* p, uint64_t stride, uint32_t ny) {
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  for (uint32_t y0 = 0; y0 < ny; y0 += 8) {
-    f32x4 v[8];
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      v[k] = f32x4{0.f, 0.f, 0.f, 0.f};
-      if (y0 + k < ny) {
-        const float* q = p + (y0 + k) * stride;
-        v[k] = f32x4{load_partial(q), load_partial(q + 1), load_partial(q + 2), load_partial(q + 3)};
-      }
-    }
-#pragma unroll
-    for (int k = 0; k < 8; ++k)
-      if (y0 + k < ny) s += v[k];
-  }
-  return s;
-}
-
 // Buffer resource for raw buffer loads: offsets at or past `bytes` read as 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,

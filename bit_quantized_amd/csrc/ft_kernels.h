@@ -69,13 +69,11 @@ struct LoraGradArgs {
   int ld_small, r0, rl;
   void* out;                      // [rl, I]
   int out_f32;                    // 0 bf16, 1 fp32
-  float* part;                    // workspace partials
-  unsigned long long* cnt;        // workspace arrival slots (any contents)
-  uint32_t epoch;                 // unique to this call
+  float* part;                    // workspace: fp32 partials per 512-token chunk
 };
-// dA and dB of one backward in a single launch (both problems in one grid).
+// dA and dB of one backward: one launch computes the partials of both
+// problems, a second adds them in chunk order.
 hipError_t launch_lora_grads(const LoraGradArgs& dA, const LoraGradArgs& dB, hipStream_t st);
 size_t lora_grad_part_bytes(int64_t M, int64_t I, int rl);
-size_t lora_grad_cnt_bytes(int64_t I);
 
 }  // namespace ft

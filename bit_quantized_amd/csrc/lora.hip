@@ -16,8 +16,9 @@
 // (token index contiguous) and consumed by 16x16x32 bf16 MFMAs with fp32
 // accumulation; the small operand of the workgroup's 512 tokens is staged
 // transposed once.  All global loads of a workgroup are issued up front.
-// Token chunks are reduced by the last workgroup to finish a column block,
-// in chunk order (deterministic).  HBM bound: big is read once.
+// Each 512-token chunk writes fp32 partials; k_lora_reduce, the next kernel
+// on the stream, adds them in chunk order (deterministic) and rounds once.
+// HBM bound: big is read once.
 #include "ft_device.hpp"
 #include "ft_kernels.h"
 
@@ -38,7 +39,6 @@ __global__ __launch_bounds__(256) void k_lora_grads(const LoraGradArgs pa, const
   constexpr int RP = RG * 16;
   __shared__ __attribute__((aligned(16))) uint16_t bigT[2][IB * PM];
   __shared__ __attribute__((aligned(16))) uint16_t smT[RP * PS];
-  __shared__ int s_last;
   const bool is_a = blockIdx.x < nib_a;
   const LoraGradArgs& a = is_a ? pa : pb;
   const uint32_t cb = is_a ? blockIdx.x : blockIdx.x - nib_a;
@@ -122,33 +122,51 @@ __global__ __launch_bounds__(256) void k_lora_grads(const LoraGradArgs pa, const
     }
   }
 
-  // acc[c][j]: column i = i0 + 16*wave + 4*g + j, rank r = 16*c + l16
+  // acc[c][j]: column i = i0 + 16*wave + 4*g + j, rank r = 16*c + l16;
+  // partials part[chunk][i][RP]
   float* mypart = a.part + static_cast<int64_t>(blockIdx.y) * I * RP;
 #pragma unroll
   for (int c = 0; c < RG; ++c)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int64_t i = i0 + 16 * wave + 4 * g + j;
-      if (i < I) store_partial(&mypart[i * RP + 16 * c + l16], acc[c][j]);
+      if (i < I) mypart[i * RP + 16 * c + l16] = acc[c][j];
     }
-  wait_stores();
-  __syncthreads();
-  if (t == 0) s_last = arrive_last(a.cnt + cb, a.epoch, gridDim.y);
-  __syncthreads();
-  if (!s_last) return;
-  // consecutive threads take consecutive columns i: coalesced out[r][i] stores
-  for (int idx = t; idx < IB * (RP / 4); idx += 256) {
-    const int64_t i = i0 + idx % IB;
-    const int r = (idx / IB) * 4;
-    if (i >= I || r >= rl) continue;
-    const f32x4 sum = sum_partials(a.part + i * RP + r, static_cast<uint64_t>(I) * RP, gridDim.y);
+}
+
+// out[r][i] = sum over chunks y (in order) of part[y][i][r]; a thread owns
+// column i and 4 consecutive ranks, so consecutive threads store
+// consecutive columns of a rank row.  Blocks [0, nblk_a) serve dA.
+template <int RG>
+__global__ __launch_bounds__(256) void k_lora_reduce(const LoraGradArgs pa, const LoraGradArgs pb,
+                                                     uint32_t nblk_a, uint32_t nmc) {
+  constexpr int RP = RG * 16;
+  const bool is_a = blockIdx.x < nblk_a;
+  const LoraGradArgs& a = is_a ? pa : pb;
+  const uint64_t idx = static_cast<uint64_t>(is_a ? blockIdx.x : blockIdx.x - nblk_a) * 256 + threadIdx.x;
+  const int64_t I = a.I;
+  if (idx >= static_cast<uint64_t>(I) * (RP / 4)) return;
+  const int64_t i = static_cast<int64_t>(idx % static_cast<uint64_t>(I));
+  const int r = static_cast<int>(idx / static_cast<uint64_t>(I)) * 4;
+  if (r >= a.rl) return;
+  const float* p = a.part + i * RP + r;
+  const uint64_t stride = static_cast<uint64_t>(I) * RP;
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  for (uint32_t y0 = 0; y0 < nmc; y0 += 8) {
+    f32x4 v[8];
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      if (r + k >= rl) break;
-      const int64_t o = static_cast<int64_t>(r + k) * I + i;
-      if (a.out_f32) static_cast<float*>(a.out)[o] = sum[k];
-      else static_cast<uint16_t*>(a.out)[o] = f32_to_bf16_rne(sum[k]);
-    }
+    for (int k = 0; k < 8; ++k)
+      v[k] = (y0 + k < nmc) ? *reinterpret_cast<const f32x4*>(p + (y0 + k) * stride)
+                            : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k = 0; k < 8; ++k) s += v[k];
+  }
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    if (r + k >= a.rl) break;
+    const int64_t o = static_cast<int64_t>(r + k) * I + i;
+    if (a.out_f32) static_cast<float*>(a.out)[o] = s[k];
+    else static_cast<uint16_t*>(a.out)[o] = f32_to_bf16_rne(s[k]);
   }
 }
 
@@ -160,15 +178,23 @@ size_t lora_grad_part_bytes(int64_t M, int64_t I, int rl) {
   return static_cast<size_t>(nmc) * I * RP * sizeof(float);
 }
 
-size_t lora_grad_cnt_bytes(int64_t I) { return static_cast<size_t>((I + IB - 1) / IB) * 8; }
-
 hipError_t launch_lora_grads(const LoraGradArgs& dA, const LoraGradArgs& dB, hipStream_t st) {
   const uint32_t nib_a = static_cast<uint32_t>((dA.I + IB - 1) / IB);
   const uint32_t nib_b = static_cast<uint32_t>((dB.I + IB - 1) / IB);
   const uint32_t nmc = static_cast<uint32_t>((dA.M + MC - 1) / MC);
   dim3 grid(nib_a + nib_b, nmc);
-#define FT_L(RG) hipLaunchKernelGGL(k_lora_grads<RG>, grid, dim3(256), 0, st, dA, dB, nib_a)
-  switch ((dA.rl + 15) / 16) {
+  const int rg = (dA.rl + 15) / 16;
+  // reduction: I * RP/4 threads per problem
+  const uint32_t nblk_a = static_cast<uint32_t>((dA.I * rg * 4 + 255) / 256);
+  const uint32_t nblk_b = static_cast<uint32_t>((dB.I * rg * 4 + 255) / 256);
+#define FT_L(RG)                                                                              \
+  do {                                                                                        \
+    hipLaunchKernelGGL(k_lora_grads<RG>, grid, dim3(256), 0, st, dA, dB, nib_a);              \
+    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;                        \
+    hipLaunchKernelGGL(k_lora_reduce<RG>, dim3(nblk_a + nblk_b), dim3(256), 0, st, dA, dB,    \
+                       nblk_a, nmc);                                                          \
+  } while (0)
+  switch (rg) {
     case 1: FT_L(1); break;
     case 2: FT_L(2); break;
     case 3: FT_L(3); break;

@@ -14,8 +14,9 @@
 //                     one read of the input                          (HBM bound)
 //   k_quant_down      1x32 blocks along rows fused with the rank-R
 //                     down-projection (bf16 MFMA, fp32 accumulation),
-//                     split over columns with a deterministic
-//                     last-arriving-workgroup reduction             (HBM bound)
+//                     split over columns into fp32 partials          (HBM bound)
+//   k_rank_reduce     ordered sum of those partials, bf16 rounding, and
+//                     the padded rank operands of the 4-bit GEMM     (HBM bound)
 #include "ft_device.hpp"
 #include "ft_kernels.h"
 
@@ -330,61 +331,90 @@ struct RRArgs {
   uint16_t* cp_dst;
 };
 
-// cp_dst[i][r] = cp[r][i] (r < R) or 0 (R <= r < rpad), spread over the
-// grid: a thread makes one 16-byte chunk (8 ranks of row i) from 8 loads
-// that are coalesced across the lanes (consecutive lanes, consecutive i).
-__device__ __forceinline__ void copy_rank_operand(const RRArgs& a) {
-  const RankRows& p = a.cp;
-  const int cpr = a.rpad >> 3;                         // chunks per destination row
-  const uint64_t total = static_cast<uint64_t>(a.cp_rows) * cpr;
-  const uint64_t nthr = static_cast<uint64_t>(gridDim.x) * 256;
-  const uint64_t first = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x;
-  for (uint64_t e = first; e < total; e += nthr) {
-    const int c = static_cast<int>(e / a.cp_rows);       // chunk: ranks 8c .. 8c+7
-    const int64_t i = static_cast<int64_t>(e % a.cp_rows);
+// k_rank_reduce: blocks [0, 4 * rowblocks) each sum one 16-row slab (one
+// wave's accumulators of k_quant_down) over the column splits; the blocks
+// after them copy the GEMM's other rank operand.
+//
+// Sum: thread t < 64 * NRG owns accumulator item t (4 rows x 1 rank); it
+// issues the loads of 8 splits at a time and adds them in split order, so
+// the result does not depend on the launch shape.  The 16 x rpad result goes
+// through LDS to contiguous stores.
+template <int NRG>
+__device__ __forceinline__ void rank_sum_slab(const RRArgs& a, uint32_t b) {
+  constexpr int RP = NRG * 16;
+  __shared__ float sum[16][RP + 1];
+  const int t = threadIdx.x;
+  const uint32_t nrb = (a.rows + 63) / 64;
+  const uint32_t bx = b >> 2, wave = b & 3;
+  const uint64_t slab = static_cast<uint64_t>(NRG) * 256;                 // floats per wave slab
+  const uint64_t stride = static_cast<uint64_t>(nrb) * 4 * slab;          // between splits
+  if (t < 64 * NRG) {
+    const float* p = a.part + (static_cast<uint64_t>(bx) * 4 + wave) * slab + t * 4;
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+    for (uint32_t y0 = 0; y0 < a.splits; y0 += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k)
+        v[k] = (y0 + k < a.splits) ? *reinterpret_cast<const f32x4*>(p + (y0 + k) * stride)
+                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int k = 0; k < 8; ++k) s += v[k];
+    }
+    const int c = t >> 6, lane = t & 63;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) sum[4 * (lane >> 4) + j][16 * c + (lane & 15)] = s[j];
+  }
+  __syncthreads();
+  const int R = a.R, rpad = a.rpad;
+  const uint32_t r0 = bx * 64 + wave * 16;
+  // out_pad: 16 rows x rpad ranks, contiguous; 8 ranks (16 bytes) per thread
+  for (int idx = t; idx < 16 * (rpad >> 3); idx += 256) {
+    const int rl = idx / (rpad >> 3), r8 = (idx % (rpad >> 3)) * 8;
+    if (r0 + rl >= a.rows) continue;
     uint32_t w[4];
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      uint32_t h[2];
-#pragma unroll
-      for (int q = 0; q < 2; ++q) {
-        const int r = 8 * c + 2 * k + q;
-        h[q] = r < p.r0 ? p.p0[r * p.ld + i] : (r < a.R ? p.p1[(r - p.r0) * p.ld + i] : uint16_t(0));
-      }
-      w[k] = h[0] | (h[1] << 16);
+      const int r = r8 + 2 * k;
+      const uint32_t lo = r < R ? f32_to_bf16_rne(sum[rl][r]) : 0u;
+      const uint32_t hi = r + 1 < R ? f32_to_bf16_rne(sum[rl][r + 1]) : 0u;
+      w[k] = lo | (hi << 16);
     }
-    *reinterpret_cast<u32x4*>(a.cp_dst + i * a.rpad + 8 * c) = u32x4{w[0], w[1], w[2], w[3]};
+    *reinterpret_cast<u32x4*>(a.out_pad + static_cast<uint64_t>(r0 + rl) * rpad + r8) =
+        u32x4{w[0], w[1], w[2], w[3]};
   }
+  // out_lr: 16 rows x R ranks, contiguous
+  for (int idx = t; idx < 16 * R; idx += 256) {
+    const int rl = idx / R, r = idx % R;
+    if (r0 + rl < a.rows) a.out_lr[static_cast<uint64_t>(r0 + rl) * R + r] = f32_to_bf16_rne(sum[rl][r]);
+  }
+}
+
+// Copy: cp_dst[i][r] = cp[r][i] (r < R) or 0 (R <= r < rpad).  A thread
+// makes one 16-byte chunk (8 ranks of row i) from 8 loads issued together;
+// consecutive lanes take consecutive i, so each load is coalesced.
+__device__ __forceinline__ void copy_rank_chunk(const RRArgs& a, uint64_t e) {
+  const RankRows& p = a.cp;
+  const uint64_t total = static_cast<uint64_t>(a.cp_rows) * (a.rpad >> 3);
+  if (e >= total) return;
+  const int c = static_cast<int>(e / a.cp_rows);         // chunk: ranks 8c .. 8c+7
+  const int64_t i = static_cast<int64_t>(e % a.cp_rows);
+  uint32_t h[8];
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    const int r = 8 * c + q;
+    h[q] = r < p.r0 ? p.p0[r * p.ld + i] : (r < a.R ? p.p1[(r - p.r0) * p.ld + i] : uint16_t(0));
+  }
+  *reinterpret_cast<u32x4*>(a.cp_dst + i * a.rpad + 8 * c) =
+      u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
 }
 
 template <int NRG>
 __global__ __launch_bounds__(256) void k_rank_reduce(const RRArgs a) {
-  constexpr int RP = NRG * 16;
-  __shared__ float sum[64][RP + 1];
-  const int t = threadIdx.x;
-  const uint32_t m0 = blockIdx.x * 64;
-  const uint64_t slab = static_cast<uint64_t>(4) * NRG * 256;          // floats per row block
-  const uint64_t split_stride = static_cast<uint64_t>(gridDim.x) * slab;
-  const float* base = a.part + blockIdx.x * slab;
-  // item = (wave, c, lane): 4 rows (16 wave + 4 g + j) of rank 16 c + (lane & 15)
-  for (int item = t; item < 4 * NRG * 64; item += 256) {
-    f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    for (uint32_t y = 0; y < a.splits; ++y) s += *reinterpret_cast<const f32x4*>(base + y * split_stride + item * 4);
-    const int wave = item / (NRG * 64), c = (item / 64) % NRG, lane = item % 64;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) sum[16 * wave + 4 * (lane >> 4) + j][16 * c + (lane & 15)] = s[j];
-  }
-  __syncthreads();
-  const int R = a.R, rpad = a.rpad;
-  for (int idx = t; idx < 64 * rpad; idx += 256) {
-    const int rl = idx / rpad, r = idx % rpad;
-    const uint32_t rr = m0 + rl;
-    if (rr >= a.rows) continue;
-    const uint16_t v = r < R ? f32_to_bf16_rne(sum[rl][r]) : uint16_t(0);
-    if (r < R) a.out_lr[static_cast<uint64_t>(rr) * R + r] = v;
-    a.out_pad[static_cast<uint64_t>(rr) * rpad + r] = v;
-  }
-  copy_rank_operand(a);
+  const uint32_t nsum = ((a.rows + 63) / 64) * 4;
+  if (blockIdx.x < nsum)
+    rank_sum_slab<NRG>(a, blockIdx.x);
+  else
+    copy_rank_chunk(a, static_cast<uint64_t>(blockIdx.x - nsum) * 256 + threadIdx.x);
 }
 
 // ---------------------------------------------------------------------------
@@ -458,7 +488,9 @@ hipError_t launch_quant_down(const uint16_t* in, int64_t rows, int64_t cols, int
 #undef FT_QD
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   RRArgs b{part, static_cast<uint32_t>(rows), splits, R, rank_pad(R), out_lr, out_pad, cp, cp_rows, cp_dst};
-#define FT_RR(NRG) hipLaunchKernelGGL((k_rank_reduce<NRG>), dim3(nrb), dim3(256), 0, st, b)
+  const uint64_t ncopy = (static_cast<uint64_t>(cp_rows) * (rank_pad(R) / 8) + 255) / 256;
+  const dim3 rgrid(static_cast<uint32_t>(nrb * 4 + ncopy));
+#define FT_RR(NRG) hipLaunchKernelGGL((k_rank_reduce<NRG>), rgrid, dim3(256), 0, st, b)
   switch (nrg) {
     case 1: FT_RR(1); break;
     case 2: FT_RR(2); break;
