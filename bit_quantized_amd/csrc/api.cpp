@@ -5,12 +5,30 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstring>
 #include <mutex>
 #include <string>
 #include <vector>
 
 #include "ft_kernels.h"
+
+namespace ft {
+
+int cu_count() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  int c = cache[dev].load(std::memory_order_relaxed);
+  if (c <= 0) {
+    if (hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || c <= 0)
+      return 0;
+    cache[dev].store(c, std::memory_order_relaxed);
+  }
+  return c;
+}
+
+}  // namespace ft
 
 namespace {
 

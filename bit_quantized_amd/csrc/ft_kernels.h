@@ -17,6 +17,9 @@ struct RankRows {
   int64_t ld;
 };
 
+// Compute units of the current device (cached per device); 0 if unknown.
+int cu_count();
+
 // quantize.hip
 hipError_t launch_quant_row32(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
                               uint8_t* codes, uint8_t* scales, hipStream_t st);

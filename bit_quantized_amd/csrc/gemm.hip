@@ -651,22 +651,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
     }
 }
 
-int g_cu_count[64];
-
 }  // namespace
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const uint32_t n = static_cast<uint32_t>(((g.NOUT + BN - 1) / BN) * ((g.M + BM - 1) / BM));
   if ((g.RED & 127) == 0) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return hipErrorInvalidDevice;
-    if (g_cu_count[dev] <= 0) {
-      int cus = 0;
-      if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus <= 0)
-        return hipErrorInvalidDevice;
-      g_cu_count[dev] = cus;
-    }
-    const uint32_t grid = n < static_cast<uint32_t>(g_cu_count[dev]) ? n : static_cast<uint32_t>(g_cu_count[dev]);
+    const int cus = cu_count();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    const uint32_t grid = n < static_cast<uint32_t>(cus) ? n : static_cast<uint32_t>(cus);
     const bool odd = ((g.RED / BK) & 1) != 0;
 #define FT_GP(LR, ODD) hipLaunchKernelGGL((k_gemm_pipe<LR, ODD>), dim3(grid), dim3(256), 0, st, g)
     if (g.nlr > 0) { if (odd) FT_GP(true, true); else FT_GP(true, false); }

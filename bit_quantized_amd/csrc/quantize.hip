@@ -206,22 +206,29 @@ __global__ __launch_bounds__(256) void k_quant_row32_t(const uint16_t* __restric
 // with proj given rank-major (one row of `cols` values per rank) as two
 // pieces of r0 and r1 rows.
 //
-// k_quant_down: a workgroup covers 64 rows (16 per wave) and KC = 128*NS
-// columns.  Every global load is issued up front: the lane's NS blocks of 32
-// input values (one block per 128-column step: row = l%16, block l/16) and
-// the projection slice [RP ranks x KC columns], which is copied to LDS with
-// 16-byte stores.  Per step the lane quantizes its block and feeds the same
-// 32 values to four 16x16x32 bf16 MFMAs in the reduction order (block,
-// 8-element group, element), reading the projection in the same order.  The
-// fp32 result of the column range goes to a workspace slab, laid out as the
-// accumulators are held (16 contiguous bytes per lane).
+// k_quant_down: persistent.  The columns are cut into splits of KC = 128*NS;
+// `wg_per_split` workgroups share a split and walk its 64-row blocks
+// (workgroup j takes blocks j, j + G, ...).  A workgroup stages the
+// projection slice of its split [RP ranks x KC columns] in LDS once.  Each
+// wave then streams its own 16 rows of every block it visits, with no
+// barrier between blocks:
+//   - loads: one instruction reads KC/8 lanes x 16 bytes of one row (1 KB
+//     contiguous for KC = 512); the next block's loads are issued as soon as
+//     the current block is in LDS, so they overlap its MFMA phase;
+//   - quantize in the load layout: 4 consecutive lanes hold one 32-element
+//     block, amax by two quad DPP steps; codes go out as 4 bytes per lane
+//     (a row's codes contiguous), scales from every 4th lane;
+//   - the same bf16 values go to the wave's LDS area and come back as
+//     16x16x32 MFMA fragments (row = lane % 16, 8 columns of group
+//     lane / 16) against the projection in LDS: fp32 sums over the split;
+//   - the 16 x RP result goes to a workspace slab, laid out as the
+//     accumulators are held (16 contiguous bytes per lane).
 //
 // k_rank_reduce (the next kernel on the stream, so every slab is visible):
-// sums the slabs of a 64-row block in column-range order (deterministic),
-// rounds once, and writes out_lr [rows, R] and out_pad [rows, rpad] (the
-// same values with zero ranks R .. rpad-1, for the 4-bit GEMM).  It also
-// copies the GEMM's other rank operand transposed, cp_dst[i][r] = cp[r][i],
-// zero-padded to rpad ranks.
+// sums the slabs in split order (deterministic), rounds once, and writes
+// out_lr [rows, R] and out_pad [rows, rpad] (the same values with zero ranks
+// R .. rpad-1, for the 4-bit GEMM).  It also copies the GEMM's other rank
+// operand transposed, cp_dst[i][r] = cp[r][i], zero-padded to rpad ranks.
 struct QDArgs {
   const uint16_t* in;
   uint32_t rows, cols;
@@ -230,50 +237,60 @@ struct QDArgs {
   uint8_t* scales;
   RankRows pr;
   int R;
+  uint32_t wg_per_split;
   float* part;          // [splits][rows/64][4 waves][NRG][64 lanes][4]
 };
 
 template <int NRG, int NS>
-__global__ __launch_bounds__(256) void k_quant_down(const QDArgs a) {
-  constexpr int RP = NRG * 16;          // padded rank
-  constexpr int KC = 128 * NS;          // columns of this workgroup
-  constexpr int PT = KC + 8;            // LDS pitch (bf16) of the staged projection
+__global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
+  constexpr int RP = NRG * 16;
+  constexpr int KC = 128 * NS;
+  constexpr int PT = KC + 8;
+  constexpr int LPR = KC / 8;
+  constexpr int RPI = 64 / LPR;
+  constexpr int NI = 16 / RPI;
   __shared__ __attribute__((aligned(16))) uint16_t pt[RP * PT];
+  __shared__ __attribute__((aligned(16))) uint16_t xt[4][16 * PT];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int g = lane >> 4, lr = lane & 15;
   const uint32_t rows = a.rows, cols = a.cols;
-  const uint32_t m0 = blockIdx.x * 64;
-  const uint32_t row = m0 + wave * 16 + lr;
-  const uint32_t cbeg = blockIdx.y * KC;
-  const int R = a.R;
-  const RankRows& p = a.pr;
-
-  // ---- issue the input loads of all steps
+  const uint32_t nrb = (rows + 63) / 64;
+  const uint32_t G = a.wg_per_split;
+  const uint32_t y = blockIdx.x / G;
+  const uint32_t cbeg = y * KC;
+  const int lrow = lane / LPR, lcol = (lane % LPR) * 8;
+  const uint32_t col = cbeg + lcol;
+  const bool col_ok = col < cols;
+  const uint32_t ld2 = static_cast<uint32_t>(a.ld) * 2;
   const auto rin = make_rsrc(a.in, static_cast<uint64_t>(rows) * a.ld * 2);
-  u32x4 v[NS][4];
+  // Byte offset of this lane's element in row block 0, instruction 0.  Rows
+  // past the end read as zero through the buffer size (32-bit offsets:
+  // rows * ld * 2 < 2^31); columns past the end are masked here.
+  const uint32_t lane_off = col_ok ? (static_cast<uint32_t>(16 * wave + lrow) * ld2 + col * 2) : BUF_OOB;
+  auto load = [&](u32x4* v, uint32_t bx) {
+    const uint32_t base = (bx < nrb && col_ok) ? bx * 64 * ld2 + lane_off : BUF_OOB;
 #pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const uint32_t cb = cbeg + 128 * s + 32 * g;
-    const uint32_t off = (cb < cols && row < rows) ? static_cast<uint32_t>((row * a.ld + cb) * 2) : BUF_OOB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[s][i] = buf_load128(rin, off == BUF_OOB ? off : off + 16 * i);
-  }
-
-  // ---- projection slice: pt[r][c - cbeg] = proj[r][c], 8 columns a chunk
+    for (int i = 0; i < NI; ++i)
+      v[i] = buf_load128(rin, base == BUF_OOB ? BUF_OOB : base + i * RPI * ld2);
+  };
+  u32x4 va[NI];
+  uint32_t bx = blockIdx.x % G;
+  load(va, bx);
   {
+    const RankRows& p = a.pr;
+    const int R = a.R;
     const auto r0s = make_rsrc(p.p0, static_cast<uint64_t>(p.r0) * p.ld * 2);
     const auto r1s = make_rsrc(p.p1, static_cast<uint64_t>(p.r1) * p.ld * 2);
-    constexpr int CPR = KC / 8;          // chunks per rank row
+    constexpr int CPR = KC / 8;
     constexpr int PER = (RP * CPR + 255) / 256;
     u32x4 w[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const int c = t + 256 * e;
       const int r = c / CPR, cc = (c % CPR) * 8;
-      const uint32_t col = cbeg + cc;
-      const bool ok = c < RP * CPR && col < cols;
-      const uint32_t o0 = (ok && r < p.r0) ? static_cast<uint32_t>((r * p.ld + col) * 2) : BUF_OOB;
-      const uint32_t o1 = (ok && r >= p.r0 && r < R) ? static_cast<uint32_t>(((r - p.r0) * p.ld + col) * 2) : BUF_OOB;
+      const uint32_t pc = cbeg + cc;
+      const bool ok = c < RP * CPR && pc < cols;
+      const uint32_t o0 = (ok && r < p.r0) ? static_cast<uint32_t>((r * p.ld + pc) * 2) : BUF_OOB;
+      const uint32_t o1 = (ok && r >= p.r0 && r < R) ? static_cast<uint32_t>(((r - p.r0) * p.ld + pc) * 2) : BUF_OOB;
       w[e] = buf_load128(r0s, o0) | buf_load128(r1s, o1);
     }
 #pragma unroll
@@ -283,42 +300,52 @@ __global__ __launch_bounds__(256) void k_quant_down(const QDArgs a) {
     }
   }
   __syncthreads();
-
-  // ---- quantize + down-project, one 128-column step at a time
-  f32x4 acc[NRG];
+  uint16_t* xw = xt[wave];
+  const int g = lane >> 4, lr = lane & 15;
+  const uint32_t cpr = cols >> 1, spr = cols >> 5;
+  auto quant = [&](const u32x4* v, uint32_t b) {
 #pragma unroll
-  for (int c = 0; c < NRG; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int s = 0; s < NS; ++s) {
-    const uint32_t cb = cbeg + 128 * s + 32 * g;
-    if (row < rows && cb < cols) {
-      uint32_t m = 0;
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) m = max_u16x2(m, abs_bf16x2(v[s][i][j]));
-      const uint32_t sc8 = e8m0_from_amax_bits(hmax_u16x2(m));
-      const float sc = e8m0_to_f32(sc8);
-      u32x4 o;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) o[i] = encode8(v[s][i][0], v[s][i][1], v[s][i][2], v[s][i][3], sc);
-      *reinterpret_cast<u32x4*>(a.codes + static_cast<uint64_t>(row) * (cols >> 1) + (cb >> 1)) = o;
-      a.scales[static_cast<uint64_t>(row) * (cols >> 5) + (cb >> 5)] = static_cast<uint8_t>(sc8);
-    }
-#pragma unroll
-    for (int c = 0; c < NRG; ++c)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const u32x4 b = lds_read_b128(&pt[(16 * c + lr) * PT + 128 * s + 32 * g + 8 * i]);
-        acc[c] = mfma_bf16_16x16x32(v[s][i], b, acc[c]);
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t row = b * 64 + 16 * wave + i * RPI + lrow;
+      uint32_t m = max_u16x2(max_u16x2(abs_bf16x2(v[i][0]), abs_bf16x2(v[i][1])),
+                             max_u16x2(abs_bf16x2(v[i][2]), abs_bf16x2(v[i][3])));
+      uint32_t am = hmax_u16x2(m);
+      am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0xB1, 0xF, 0xF, false)));
+      am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0x4E, 0xF, 0xF, false)));
+      const uint32_t sc8 = e8m0_from_amax_bits(am);
+      const uint32_t o = encode8(v[i][0], v[i][1], v[i][2], v[i][3], e8m0_to_f32(sc8));
+      if (row < rows && col_ok) {
+        *reinterpret_cast<uint32_t*>(a.codes + row * cpr + (col >> 1)) = o;
+        if ((lane & 3) == 0) a.scales[row * spr + (col >> 5)] = static_cast<uint8_t>(sc8);
       }
-  }
-
-  // acc[c][j] holds row m0 + 16*wave + 4*g + j, rank 16*c + lr
-  float* slab = a.part + ((static_cast<uint64_t>(blockIdx.y) * gridDim.x + blockIdx.x) * 4 + wave) * (NRG * 256);
+      *reinterpret_cast<u32x4*>(&xw[(i * RPI + lrow) * PT + lcol]) = v[i];
+    }
+  };
+  auto mma = [&](uint32_t b) {
+    f32x4 acc[NRG];
 #pragma unroll
-  for (int c = 0; c < NRG; ++c) *reinterpret_cast<f32x4*>(slab + (c * 64 + lane) * 4) = acc[c];
+    for (int c = 0; c < NRG; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KC / 32; ++ks) {
+      const u32x4 af = lds_read_b128(&xw[lr * PT + 32 * ks + 8 * g]);
+#pragma unroll
+      for (int c = 0; c < NRG; ++c)
+        acc[c] = mfma_bf16_16x16x32(af, lds_read_b128(&pt[(16 * c + lr) * PT + 32 * ks + 8 * g]), acc[c]);
+      if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
+    }
+    float* slab = a.part + ((static_cast<uint64_t>(y) * nrb + b) * 4 + wave) * (NRG * 256);
+#pragma unroll
+    for (int c = 0; c < NRG; ++c) *reinterpret_cast<f32x4*>(slab + (c * 64 + lane) * 4) = acc[c];
+  };
+  // the next block's loads go out as soon as this block's values are in LDS,
+  // and overlap the MFMA phase
+  for (; bx < nrb; bx += G) {
+    quant(va, bx);
+    load(va, bx + G);
+    mma(bx);
+  }
 }
+
 
 struct RRArgs {
   const float* part;
@@ -472,8 +499,15 @@ hipError_t launch_quant_down(const uint16_t* in, int64_t rows, int64_t cols, int
   const int kc = quant_down_kc(rows, cols);
   const uint32_t nrb = static_cast<uint32_t>((rows + 63) / 64);
   const uint32_t splits = static_cast<uint32_t>((cols + kc - 1) / kc);
-  QDArgs a{in, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols), ld, codes, scales, pr, R, part};
-  dim3 grid(nrb, splits);
+  // workgroups per split: as many as fit on the chip at once (LDS allows one
+  // per CU at KC = 512, two at 256, four at 128), at most one per row block
+  const int cus = cu_count();
+  if (cus <= 0) return hipErrorInvalidDevice;
+  const uint32_t resident = static_cast<uint32_t>(cus) * static_cast<uint32_t>(512 / kc);
+  uint32_t G = resident / splits;
+  G = G < 1 ? 1 : (G > nrb ? nrb : G);
+  QDArgs a{in, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols), ld, codes, scales, pr, R, G, part};
+  const dim3 grid(splits * G);
 #define FT_QD(NRG, NS) hipLaunchKernelGGL((k_quant_down<NRG, NS>), grid, dim3(256), 0, st, a)
 #define FT_QD_NS(NRG) \
   do { if (kc == 512) FT_QD(NRG, 4); else if (kc == 256) FT_QD(NRG, 2); else FT_QD(NRG, 1); } while (0)
