@@ -18,7 +18,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfourtune.so")
-SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "lora.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "lora.hip", "act.hip"]
 ARCH = "gfx950"
 
 COMMON = [

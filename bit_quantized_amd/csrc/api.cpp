@@ -137,6 +137,9 @@ ft_status check_linear(const ft_linear* L) {
   if (L->r_stab < 0 || L->r_lora < 0 || L->r_stab + L->r_lora > FT_MAX_RANK) return FT_ESHAPE;
   if (L->M * (L->r_stab + L->r_lora) * 2 > kMaxBytes) return FT_ESHAPE;
   if (!L->w_codes || !L->w_scales) return FT_EINVAL;
+  if ((L->act_in != FT_ACT_NONE && L->act_in != FT_ACT_GELU_TANH) ||
+      (L->act_out != FT_ACT_NONE && L->act_out != FT_ACT_GELU_TANH))
+    return FT_EINVAL;
   if ((L->wt_codes == nullptr) != (L->wt_scales == nullptr)) return FT_EINVAL;
   if (L->r_stab > 0 && (!L->L1t || !L->L2)) return FT_EINVAL;
   if (L->r_lora > 0 && (!L->At || !L->B)) return FT_EINVAL;
@@ -235,7 +238,7 @@ ft_status fourtune_quantize(int mode, const uint16_t* in, int64_t rows, int64_t 
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (mode) {
     case FT_Q_ROW32:
-      { Timed tm("quant_row32", st); return launched(tm.done(ft::launch_quant_row32(in, rows, cols, ld_in, codes, scales, st))); }
+      { Timed tm("quant_row32", st); return launched(tm.done(ft::launch_quant_row32(in, nullptr, 0, rows, cols, ld_in, codes, scales, st))); }
     case FT_Q_TILE32:
       { Timed tm("quant_tile32", st); return launched(tm.done(ft::launch_quant_tile32(in, rows, cols, ld_in, codes, scales, codes_t, scales_t, st))); }
     default:
@@ -279,11 +282,13 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
   hipError_t e;
   {
     Timed tm("fwd_quant_down", st);
+    // act_in: X is the pre-activation h; the layer's input is gelu(h)
+    const int act = L->act_in == FT_ACT_GELU_TANH ? 1 : 0;
     if (R > 0)
-      e = ft::launch_quant_down(X, L->M, L->K, L->K, qc, qs, rows_Dt(L), U_save, u_pad, rows_V(L),
-                                L->N, v_pad, reinterpret_cast<float*>(ws + lay.part), st);
+      e = ft::launch_quant_down(X, nullptr, act, L->M, L->K, L->K, qc, qs, rows_Dt(L), U_save, u_pad,
+                                rows_V(L), L->N, v_pad, reinterpret_cast<float*>(ws + lay.part), st);
     else
-      e = ft::launch_quant_row32(X, L->M, L->K, L->K, qc, qs, st);
+      e = ft::launch_quant_row32(X, nullptr, act, L->M, L->K, L->K, qc, qs, st);
     tm.done(e);
   }
   if (e != hipSuccess) return FT_EDEVICE;
@@ -297,7 +302,7 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
 }
 
 ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint16_t* X,
-                              const uint16_t* U_save, uint16_t* dX, void* dA, void* dB,
+                              const uint16_t* U_save, const uint16_t* H, uint16_t* dX, void* dA, void* dB,
                               ft_dtype grad_dtype, uint16_t* P_save, uint8_t* gq_codes,
                               uint8_t* gq_scales, void* workspace, size_t ws_bytes,
                               void* stream) {
@@ -308,8 +313,9 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
   if (dX && !L->wt_codes) return FT_EINVAL;
   if (grad_dtype != FT_BF16 && grad_dtype != FT_F32) return FT_EINVAL;
   if (rl > 0 && (!X || !U_save || !dA || !dB)) return FT_EINVAL;
+  if (L->act_out != FT_ACT_NONE && !H) return FT_EINVAL;
   if ((gq_codes == nullptr) != (gq_scales == nullptr)) return FT_EINVAL;
-  const void* ptrs[] = {dY, X, U_save, dX, dA, dB, P_save, gq_codes, gq_scales, workspace};
+  const void* ptrs[] = {dY, X, U_save, H, dX, dA, dB, P_save, gq_codes, gq_scales, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return FT_EALIGN;
   const BwdLayout lay = bwd_layout(L);
@@ -327,11 +333,16 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
   hipError_t e;
   {
     Timed tm("bwd_quant_down", st);
+    // act_out: dY is the gradient of gelu(Y) and H the saved Y; the incoming
+    // gradient of this layer is dY * gelu'(H)
+    const int act = L->act_out == FT_ACT_GELU_TANH ? 2 : 0;
+    const uint16_t* h2 = act ? H : nullptr;
     if (R > 0)
-      e = ft::launch_quant_down(dY, L->M, L->N, L->N, qc, qs, rows_V(L), P, p_pad, rows_Dt(L),
-                                dX ? L->K : 0, d_pad, reinterpret_cast<float*>(ws + lay.part), st);
+      e = ft::launch_quant_down(dY, h2, act, L->M, L->N, L->N, qc, qs, rows_V(L), P, p_pad,
+                                rows_Dt(L), dX ? L->K : 0, d_pad,
+                                reinterpret_cast<float*>(ws + lay.part), st);
     else
-      e = ft::launch_quant_row32(dY, L->M, L->N, L->N, qc, qs, st);
+      e = ft::launch_quant_row32(dY, h2, act, L->M, L->N, L->N, qc, qs, st);
     tm.done(e);
   }
   if (e != hipSuccess) return FT_EDEVICE;
@@ -348,16 +359,44 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
     const int f32 = grad_dtype == FT_F32 ? 1 : 0;
     ft::LoraGradArgs a{};
     a.M = L->M; a.I = L->K; a.big = X; a.small = P; a.ld_small = R; a.r0 = L->r_stab; a.rl = rl;
+    a.big2 = nullptr; a.act = L->act_in == FT_ACT_GELU_TANH ? 1 : 0;
     a.out = dA; a.out_f32 = f32;
     a.part = reinterpret_cast<float*>(ws + lay.dA_part);
     ft::LoraGradArgs b = a;
     b.I = L->N; b.big = dY; b.small = U_save;
+    b.big2 = L->act_out == FT_ACT_GELU_TANH ? H : nullptr;
+    b.act = L->act_out == FT_ACT_GELU_TANH ? 2 : 0;
     b.out = dB;
     b.part = reinterpret_cast<float*>(ws + lay.dB_part);
     Timed tm("bwd_lora_grads", st);
     if (tm.done(ft::launch_lora_grads(a, b, st)) != hipSuccess) return FT_EDEVICE;
   }
   return FT_OK;
+}
+
+ft_status fourtune_act_fwd(int act, const uint16_t* h, int64_t n, uint16_t* out, void* stream) {
+  if (act != FT_ACT_GELU_TANH) return FT_EINVAL;
+  if (!h || !out) return FT_EINVAL;
+  if (n < 0 || n * 2 > kMaxBytes) return FT_ESHAPE;
+  if (!aligned16(h) || !aligned16(out)) return FT_EALIGN;
+  if (n == 0) return FT_OK;
+  if (ft_status s = device_check(); s != FT_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Timed tm("act_fwd", st);
+  return launched(tm.done(ft::launch_act(1, h, nullptr, n, out, st)));
+}
+
+ft_status fourtune_act_bwd(int act, const uint16_t* h, const uint16_t* g, int64_t n, uint16_t* out,
+                           void* stream) {
+  if (act != FT_ACT_GELU_TANH) return FT_EINVAL;
+  if (!h || !g || !out) return FT_EINVAL;
+  if (n < 0 || n * 2 > kMaxBytes) return FT_ESHAPE;
+  if (!aligned16(h) || !aligned16(g) || !aligned16(out)) return FT_EALIGN;
+  if (n == 0) return FT_OK;
+  if (ft_status s = device_check(); s != FT_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Timed tm("act_bwd", st);
+  return launched(tm.done(ft::launch_act(2, h, g, n, out, st)));
 }
 
 void fourtune_timing_enable(int on) {

@@ -129,6 +129,95 @@ __device__ __forceinline__ u32x4 lds_read_b128(const void* p) {
   return *(const FT_LDS u32x4*)(p);
 }
 
+// ---------------------------------------------------------------- activation
+// tanh-form GELU between the two linears of an MLP block (FourTune, "3.3
+// Kernel Fusion for Efficiency / MLP Fusion" names GeLU on the wide
+// intermediate):  gelu(h) = h * (1 + tanh(u)) / 2,  u = sqrt(2/pi) (h + 0.044715 h^3).
+// With z = 2u and e = exp(-|z|) <= 1:
+//   (1 + tanh(u)) / 2 = sigmoid(z) = s,   s = 1/(1+e) (z >= 0) or e/(1+e) (z < 0),
+//   1 - s = e/(1+e) (z >= 0) or 1/(1+e) (z < 0),
+//   gelu'(h) = s + h s (1 - s) dz/dh,     dz/dh = 2 sqrt(2/pi) (1 + 3 * 0.044715 h^2),
+// so neither tail overflows.  exp(-|z|) = 2^(-|z| log2 e) on the hardware
+// exp2, which flushes results below 2^-126; where e < 2^-64 it is computed
+// as e * 2^64 and the scale is taken out in the last multiplication (for
+// z >= 0 such an e changes nothing: 1 + e rounds to 1).  Evaluated in fp32
+// with every operation written out (no contraction), so that every kernel
+// that calls these gets the same bits; the caller rounds to bf16 once.
+constexpr float kGeluC = 0.7978845608028654f;       // sqrt(2 / pi)
+constexpr float kGeluA = 0.044715f;
+constexpr float kLog2e = 1.4426950408889634f;
+
+struct GeluParts {
+  float z;      // 2u
+  float e;      // exp(-|z|), times 2^64 when `deep`
+  float inv;    // 1 / (1 + exp(-|z|))
+  float sc;     // 2^-64 when deep, else 1
+  bool deep;
+};
+
+__device__ __forceinline__ GeluParts gelu_parts(float h) {
+#pragma clang fp contract(off)
+  GeluParts p;
+  const float h2 = h * h;
+  p.z = (2.0f * kGeluC) * (h * (1.0f + kGeluA * h2));
+  const float x = -__builtin_fabsf(p.z) * kLog2e;
+  p.deep = x < -64.0f;
+  p.e = __builtin_amdgcn_exp2f(p.deep ? x + 64.0f : x);
+  p.sc = p.deep ? 5.421010862427522e-20f : 1.0f;            // 2^-64
+  p.inv = 1.0f / (1.0f + (p.deep ? 0.0f : p.e));
+  return p;
+}
+
+// gelu(h) = h s
+__device__ __forceinline__ float gelu_tanh_f32(float h) {
+#pragma clang fp contract(off)
+  const GeluParts p = gelu_parts(h);
+  if (p.z >= 0.0f) return h * p.inv;
+  return ((h * p.e) * p.inv) * p.sc;
+}
+
+// g gelu'(h) = g (s + h s (1 - s) dz/dh)
+__device__ __forceinline__ float gelu_tanh_grad_f32(float h, float g) {
+#pragma clang fp contract(off)
+  const GeluParts p = gelu_parts(h);
+  const float dz = (2.0f * kGeluC) * (1.0f + (3.0f * kGeluA) * (h * h));
+  if (p.z >= 0.0f) {
+    // s = inv, 1 - s = e inv; below 2^-64 the second term is negligible
+    const float t = p.deep ? 0.0f : ((h * p.inv) * (p.e * p.inv)) * dz;
+    return g * (p.inv + t);
+  }
+  // s = e inv, 1 - s = inv:  g s (1 + h (1 - s) dz/dh)
+  const float gs = (g * p.e) * p.inv;
+  if (gs == 0.0f) return gs * p.sc;          // e underflowed (|h| large): exactly +-0
+  return (gs * (1.0f + (h * p.inv) * dz)) * p.sc;
+}
+
+// Activation modes of a bf16 input stream (FT_ACT_* of the C ABI):
+// ACT 0: x as is; ACT 1: gelu(x); ACT 2: x * gelu'(h) with h a second stream.
+// Applied to two packed bf16, rounded to bf16 (nearest even).
+template <int ACT>
+__device__ __forceinline__ uint32_t act_bf16x2(uint32_t x, uint32_t h) {
+  if constexpr (ACT == 1) {
+    return pack_bf16x2_rne(gelu_tanh_f32(bf16lo_to_f32(x)), gelu_tanh_f32(bf16hi_to_f32(x)));
+  } else if constexpr (ACT == 2) {
+    return pack_bf16x2_rne(gelu_tanh_grad_f32(bf16lo_to_f32(h), bf16lo_to_f32(x)),
+                           gelu_tanh_grad_f32(bf16hi_to_f32(h), bf16hi_to_f32(x)));
+  } else {
+    (void)h;
+    return x;
+  }
+}
+template <int ACT>
+__device__ __forceinline__ u32x4 act_bf16x8(u32x4 x, u32x4 h) {
+  if constexpr (ACT == 0) {
+    (void)h;
+    return x;
+  } else {
+    return u32x4{act_bf16x2<ACT>(x[0], h[0]), act_bf16x2<ACT>(x[1], h[1]),
+                 act_bf16x2<ACT>(x[2], h[2]), act_bf16x2<ACT>(x[3], h[3])};
+  }
+}
+
 // Buffer resource for raw buffer loads: offsets at or past `bytes` read as 0.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint64_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0,

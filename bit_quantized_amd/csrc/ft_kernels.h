@@ -20,9 +20,12 @@ struct RankRows {
 // Compute units of the current device (cached per device); 0 if unknown.
 int cu_count();
 
+// Input activation of the row quantizers (FT_ACT_* of the C ABI): 0 none,
+// 1 gelu(in), 2 in * gelu'(in2) with in2 of the same shape and stride.
 // quantize.hip
-hipError_t launch_quant_row32(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
-                              uint8_t* codes, uint8_t* scales, hipStream_t st);
+hipError_t launch_quant_row32(const uint16_t* in, const uint16_t* in2, int act, int64_t rows,
+                              int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
+                              hipStream_t st);
 // codes_t / scales_t: optional transposed copy (both null or both set).
 hipError_t launch_quant_tile32(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
                                uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
@@ -41,10 +44,11 @@ inline int rank_pad(int R) { return R > 0 ? 64 : 0; }
 // [rows, rank_pad(R)], the same values zero-padded, and the transposed copy
 // cp_dst [cp_rows, rank_pad(R)] of the rank-major operand cp.  `part` needs
 // quant_down_part_bytes(rows, cols, R) bytes.
-hipError_t launch_quant_down(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
-                             uint8_t* codes, uint8_t* scales, const RankRows& pr, uint16_t* out_lr,
-                             uint16_t* out_pad, const RankRows& cp, int64_t cp_rows,
-                             uint16_t* cp_dst, float* part, hipStream_t st);
+hipError_t launch_quant_down(const uint16_t* in, const uint16_t* in2, int act, int64_t rows,
+                             int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
+                             const RankRows& pr, uint16_t* out_lr, uint16_t* out_pad,
+                             const RankRows& cp, int64_t cp_rows, uint16_t* cp_dst, float* part,
+                             hipStream_t st);
 size_t quant_down_part_bytes(int64_t rows, int64_t cols, int R);
 
 // gemm.hip: out[m][j] = sum_red deq(a)[m][red] deq(b)[j][red] + sum_r lm[m][r] lo[j][r]
@@ -64,10 +68,13 @@ struct GemmArgs {
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 
-// lora.hip: out[r][i] = sum_m big[m][i] * small[m][r0 + r], r < rl.
+// lora.hip: out[r][i] = sum_m act(big)[m][i] * small[m][r0 + r], r < rl,
+// act as for the row quantizers (big2 is the second input of act 2).
 struct LoraGradArgs {
   int64_t M, I;                   // rows, columns of big
   const uint16_t* big;            // bf16 [M, I]
+  const uint16_t* big2;           // bf16 [M, I], act 2 only
+  int act;
   const uint16_t* small;          // bf16 [M, ld_small], columns r0 .. r0+rl used
   int ld_small, r0, rl;
   void* out;                      // [rl, I]
@@ -78,5 +85,9 @@ struct LoraGradArgs {
 // problems, a second adds them in chunk order.
 hipError_t launch_lora_grads(const LoraGradArgs& dA, const LoraGradArgs& dB, hipStream_t st);
 size_t lora_grad_part_bytes(int64_t M, int64_t I, int rl);
+
+// act.hip: out = bf16(gelu(h)) (act 1) or bf16(g * gelu'(h)) (act 2), n elements.
+hipError_t launch_act(int act, const uint16_t* h, const uint16_t* g, int64_t n, uint16_t* out,
+                      hipStream_t st);
 
 }  // namespace ft

@@ -19,6 +19,11 @@
 // Each 512-token chunk writes fp32 partials; k_lora_reduce, the next kernel
 // on the stream, adds them in chunk order (deterministic) and rounds once.
 // HBM bound: big is read once.
+//
+// Around a GELU ("3.3 ... MLP Fusion"): the second linear of an MLP takes
+// gelu(h) as its input, so its dA recomputes gelu on the saved h as big is
+// loaded; the first linear's incoming gradient is dY * gelu'(h), which its
+// dB recomputes from dY and h the same way.
 #include "ft_device.hpp"
 #include "ft_kernels.h"
 
@@ -33,15 +38,12 @@ constexpr int MC = MS * NSTEP;
 constexpr int PM = MS + 8;  // LDS pitch (bf16) of a transposed big step
 constexpr int PS = MC + 8;  // LDS pitch (bf16) of the transposed small operand
 
-template <int RG>
-__global__ __launch_bounds__(256) void k_lora_grads(const LoraGradArgs pa, const LoraGradArgs pb,
-                                                    uint32_t nib_a) {
+// One workgroup: 64 columns of big (column block cb) x 512 tokens.  ACT is
+// the activation applied to big as it is loaded (rounded to bf16).
+template <int RG, int ACT>
+__device__ __forceinline__ void lora_block(const LoraGradArgs& a, uint32_t cb, uint16_t (*bigT)[IB * PM],
+                                           uint16_t* smT) {
   constexpr int RP = RG * 16;
-  __shared__ __attribute__((aligned(16))) uint16_t bigT[2][IB * PM];
-  __shared__ __attribute__((aligned(16))) uint16_t smT[RP * PS];
-  const bool is_a = blockIdx.x < nib_a;
-  const LoraGradArgs& a = is_a ? pa : pb;
-  const uint32_t cb = is_a ? blockIdx.x : blockIdx.x - nib_a;
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const int g = lane >> 4, l16 = lane & 15;
   const int64_t M = a.M, I = a.I;
@@ -52,14 +54,21 @@ __global__ __launch_bounds__(256) void k_lora_grads(const LoraGradArgs pa, const
   // ---- issue the big loads of every step: thread t covers row pair p = t/8
   // (tokens 2p, 2p+1 of the step) and columns 8*(t%8) .. +8
   const auto rbig = make_rsrc(a.big, static_cast<uint64_t>(M) * I * 2);
+  const auto rbig2 = make_rsrc(a.big2, ACT == 2 ? static_cast<uint64_t>(M) * I * 2 : 0);
   const int pp = t >> 3, cc = (t & 7) * 8;
   const bool col_ok = i0 + cc < I;
-  u32x4 va[NSTEP], vb[NSTEP];
+  u32x4 va[NSTEP], vb[NSTEP], ha[NSTEP], hb[NSTEP];
 #pragma unroll
   for (int s = 0; s < NSTEP; ++s) {
     const int64_t ma = mbeg + s * MS + 2 * pp, mb = ma + 1;
-    va[s] = buf_load128(rbig, col_ok && ma < mend ? static_cast<uint32_t>((ma * I + i0 + cc) * 2) : BUF_OOB);
-    vb[s] = buf_load128(rbig, col_ok && mb < mend ? static_cast<uint32_t>((mb * I + i0 + cc) * 2) : BUF_OOB);
+    const uint32_t oa = col_ok && ma < mend ? static_cast<uint32_t>((ma * I + i0 + cc) * 2) : BUF_OOB;
+    const uint32_t ob = col_ok && mb < mend ? static_cast<uint32_t>((mb * I + i0 + cc) * 2) : BUF_OOB;
+    va[s] = buf_load128(rbig, oa);
+    vb[s] = buf_load128(rbig, ob);
+    if constexpr (ACT == 2) {
+      ha[s] = buf_load128(rbig2, oa);
+      hb[s] = buf_load128(rbig2, ob);
+    }
   }
 
   // ---- stage small[m][r0 + r] of the chunk transposed: smT[r][m - mbeg]
@@ -101,10 +110,12 @@ __global__ __launch_bounds__(256) void k_lora_grads(const LoraGradArgs pa, const
 #pragma unroll
   for (int s = 0; s < NSTEP; ++s) {
     uint16_t* bt = bigT[s & 1];
+    const u32x4 xa = act_bf16x8<ACT>(va[s], ACT == 2 ? ha[s] : va[s]);
+    const u32x4 xb = act_bf16x8<ACT>(vb[s], ACT == 2 ? hb[s] : vb[s]);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = (va[s][j] & 0xFFFFu) | (vb[s][j] << 16);        // column cc+2j
-      const uint32_t hi = (va[s][j] >> 16) | (vb[s][j] & 0xFFFF0000u);    // column cc+2j+1
+      const uint32_t lo = (xa[j] & 0xFFFFu) | (xb[j] << 16);        // column cc+2j
+      const uint32_t hi = (xa[j] >> 16) | (xb[j] & 0xFFFF0000u);    // column cc+2j+1
       *reinterpret_cast<uint32_t*>(&bt[(cc + 2 * j) * PM + 2 * pp]) = lo;
       *reinterpret_cast<uint32_t*>(&bt[(cc + 2 * j + 1) * PM + 2 * pp]) = hi;
     }
@@ -132,6 +143,16 @@ __global__ __launch_bounds__(256) void k_lora_grads(const LoraGradArgs pa, const
       const int64_t i = i0 + 16 * wave + 4 * g + j;
       if (i < I) mypart[i * RP + 16 * c + l16] = acc[c][j];
     }
+}
+
+template <int RG, int ACTA, int ACTB>
+__global__ __launch_bounds__(256) void k_lora_grads(const LoraGradArgs pa, const LoraGradArgs pb,
+                                                    uint32_t nib_a) {
+  constexpr int RP = RG * 16;
+  __shared__ __attribute__((aligned(16))) uint16_t bigT[2][IB * PM];
+  __shared__ __attribute__((aligned(16))) uint16_t smT[RP * PS];
+  if (blockIdx.x < nib_a) lora_block<RG, ACTA>(pa, blockIdx.x, bigT, smT);
+  else lora_block<RG, ACTB>(pb, blockIdx.x - nib_a, bigT, smT);
 }
 
 // out[r][i] = sum over chunks y (in order) of part[y][i][r]; a thread owns
@@ -187,9 +208,11 @@ hipError_t launch_lora_grads(const LoraGradArgs& dA, const LoraGradArgs& dB, hip
   // reduction: I * RP/4 threads per problem
   const uint32_t nblk_a = static_cast<uint32_t>((dA.I * rg * 4 + 255) / 256);
   const uint32_t nblk_b = static_cast<uint32_t>((dB.I * rg * 4 + 255) / 256);
+#define FT_LA(RG, A, B) hipLaunchKernelGGL((k_lora_grads<RG, A, B>), grid, dim3(256), 0, st, dA, dB, nib_a)
 #define FT_L(RG)                                                                              \
   do {                                                                                        \
-    hipLaunchKernelGGL(k_lora_grads<RG>, grid, dim3(256), 0, st, dA, dB, nib_a);              \
+    if (dA.act == 1) { if (dB.act == 2) FT_LA(RG, 1, 2); else FT_LA(RG, 1, 0); }              \
+    else { if (dB.act == 2) FT_LA(RG, 0, 2); else FT_LA(RG, 0, 0); }                          \
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;                        \
     hipLaunchKernelGGL(k_lora_reduce<RG>, dim3(nblk_a + nblk_b), dim3(256), 0, st, dA, dB,    \
                        nblk_a, nmc);                                                          \
@@ -201,6 +224,7 @@ hipError_t launch_lora_grads(const LoraGradArgs& dA, const LoraGradArgs& dB, hip
     default: FT_L(4); break;
   }
 #undef FT_L
+#undef FT_LA
   return hipGetLastError();
 }
 

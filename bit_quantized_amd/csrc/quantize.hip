@@ -23,33 +23,54 @@
 namespace ft {
 
 // ---------------------------------------------------------------------------
-// 1x32 row blocks: each lane owns one block (64 B in, 16 B codes, 1 B scale).
+// 1x32 row blocks.  Four consecutive lanes hold one block (16 bytes = 8
+// values each), so one load instruction of a wave reads 16 consecutive
+// blocks (1 KB) and one store writes their 256 bytes of codes; the block
+// amax takes two quad DPP steps.  Each lane has U blocks in flight.  ACT
+// applies the input activation first (0: none; 1: gelu(in); 2: in *
+// gelu'(in2)), rounded to bf16 as the quantizer's input.
+template <int ACT>
 __global__ __launch_bounds__(256) void k_quant_row32(const uint16_t* __restrict__ in,
+                                                     const uint16_t* __restrict__ in2,
                                                      uint32_t rows, uint32_t cols, int64_t ld,
                                                      uint8_t* __restrict__ codes,
                                                      uint8_t* __restrict__ scales) {
+  constexpr int U = 4;
   const uint32_t bpr = cols >> 5;
-  const uint64_t nblk = static_cast<uint64_t>(rows) * bpr;
-  for (uint64_t b = static_cast<uint64_t>(blockIdx.x) * 256 + threadIdx.x; b < nblk;
-       b += static_cast<uint64_t>(gridDim.x) * 256) {
-    const uint32_t r = static_cast<uint32_t>(b / bpr);
-    const uint32_t cb = static_cast<uint32_t>(b - static_cast<uint64_t>(r) * bpr);
-    const u32x4* src = reinterpret_cast<const u32x4*>(in + r * ld + cb * 32);
-    u32x4 v[4];
+  const uint32_t nblk = rows * bpr;                 // < 2^26 (host checks rows * ld * 2 < 2^31)
+  const int lane = threadIdx.x & 63;
+  const uint32_t q = lane & 3;
+  const uint64_t bytes = static_cast<uint64_t>(rows) * ld * 2;
+  const auto r1 = make_rsrc(in, bytes);
+  const auto r2 = make_rsrc(in2, ACT == 2 ? bytes : 0);
+  const uint32_t ld32 = static_cast<uint32_t>(ld);
+  const uint32_t step = gridDim.x * 4 * 16 * U;
+  for (uint32_t b0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 16 * U; b0 < nblk; b0 += step) {
+    u32x4 v[U], h[U];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = __builtin_nontemporal_load(src + i);
-    uint32_t m = 0;
+    for (int k = 0; k < U; ++k) {
+      const uint32_t b = b0 + 16 * k + (lane >> 2);
+      const uint32_t r = b / bpr, cb = b - r * bpr;
+      const uint32_t off = b < nblk ? (r * ld32 + cb * 32 + q * 8) * 2 : BUF_OOB;
+      v[k] = buf_load128(r1, off);
+      if constexpr (ACT == 2) h[k] = buf_load128(r2, off);
+      else h[k] = v[k];
+    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) m = max_u16x2(m, abs_bf16x2(v[i][j]));
-    const uint32_t s = e8m0_from_amax_bits(hmax_u16x2(m));
-    const float sc = e8m0_to_f32(s);
-    u32x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = encode8(v[i][0], v[i][1], v[i][2], v[i][3], sc);
-    *reinterpret_cast<u32x4*>(codes + static_cast<uint64_t>(r) * (cols >> 1) + cb * 16) = o;
-    scales[b] = static_cast<uint8_t>(s);
+    for (int k = 0; k < U; ++k) {
+      const uint32_t b = b0 + 16 * k + (lane >> 2);
+      const u32x4 x = act_bf16x8<ACT>(v[k], h[k]);
+      uint32_t am = hmax_u16x2(max_u16x2(max_u16x2(abs_bf16x2(x[0]), abs_bf16x2(x[1])),
+                                         max_u16x2(abs_bf16x2(x[2]), abs_bf16x2(x[3]))));
+      am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0xB1, 0xF, 0xF, false)));
+      am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0x4E, 0xF, 0xF, false)));
+      const uint32_t s = e8m0_from_amax_bits(am);
+      const uint32_t o = encode8(x[0], x[1], x[2], x[3], e8m0_to_f32(s));
+      if (b < nblk) {
+        *reinterpret_cast<uint32_t*>(codes + static_cast<uint64_t>(b) * 16 + q * 4) = o;
+        if (q == 0) scales[b] = static_cast<uint8_t>(s);
+      }
+    }
   }
 }
 
@@ -231,6 +252,7 @@ __global__ __launch_bounds__(256) void k_quant_row32_t(const uint16_t* __restric
 // operand transposed, cp_dst[i][r] = cp[r][i], zero-padded to rpad ranks.
 struct QDArgs {
   const uint16_t* in;
+  const uint16_t* in2;  // second input of ACT 2 (gelu' argument), else unused
   uint32_t rows, cols;
   int64_t ld;
   uint8_t* codes;
@@ -241,7 +263,7 @@ struct QDArgs {
   float* part;          // [splits][rows/64][4 waves][NRG][64 lanes][4]
 };
 
-template <int NRG, int NS>
+template <int NRG, int NS, int ACT>
 __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
   constexpr int RP = NRG * 16;
   constexpr int KC = 128 * NS;
@@ -266,15 +288,19 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
   // past the end read as zero through the buffer size (32-bit offsets:
   // rows * ld * 2 < 2^31); columns past the end are masked here.
   const uint32_t lane_off = col_ok ? (static_cast<uint32_t>(16 * wave + lrow) * ld2 + col * 2) : BUF_OOB;
-  auto load = [&](u32x4* v, uint32_t bx) {
+  const auto rin2 = make_rsrc(a.in2, ACT == 2 ? static_cast<uint64_t>(rows) * a.ld * 2 : 0);
+  auto load = [&](u32x4* v, u32x4* h, uint32_t bx) {
     const uint32_t base = (bx < nrb && col_ok) ? bx * 64 * ld2 + lane_off : BUF_OOB;
 #pragma unroll
-    for (int i = 0; i < NI; ++i)
-      v[i] = buf_load128(rin, base == BUF_OOB ? BUF_OOB : base + i * RPI * ld2);
+    for (int i = 0; i < NI; ++i) {
+      const uint32_t off = base == BUF_OOB ? BUF_OOB : base + i * RPI * ld2;
+      v[i] = buf_load128(rin, off);
+      if constexpr (ACT == 2) h[i] = buf_load128(rin2, off);
+    }
   };
-  u32x4 va[NI];
+  u32x4 va[NI], ha[NI];
   uint32_t bx = blockIdx.x % G;
-  load(va, bx);
+  load(va, ha, bx);
   {
     const RankRows& p = a.pr;
     const int R = a.R;
@@ -303,22 +329,23 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
   uint16_t* xw = xt[wave];
   const int g = lane >> 4, lr = lane & 15;
   const uint32_t cpr = cols >> 1, spr = cols >> 5;
-  auto quant = [&](const u32x4* v, uint32_t b) {
+  auto quant = [&](const u32x4* vin, const u32x4* hin, uint32_t b) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const uint32_t row = b * 64 + 16 * wave + i * RPI + lrow;
-      uint32_t m = max_u16x2(max_u16x2(abs_bf16x2(v[i][0]), abs_bf16x2(v[i][1])),
-                             max_u16x2(abs_bf16x2(v[i][2]), abs_bf16x2(v[i][3])));
+      const u32x4 v = act_bf16x8<ACT>(vin[i], ACT == 2 ? hin[i] : vin[i]);
+      uint32_t m = max_u16x2(max_u16x2(abs_bf16x2(v[0]), abs_bf16x2(v[1])),
+                             max_u16x2(abs_bf16x2(v[2]), abs_bf16x2(v[3])));
       uint32_t am = hmax_u16x2(m);
       am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0xB1, 0xF, 0xF, false)));
       am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0x4E, 0xF, 0xF, false)));
       const uint32_t sc8 = e8m0_from_amax_bits(am);
-      const uint32_t o = encode8(v[i][0], v[i][1], v[i][2], v[i][3], e8m0_to_f32(sc8));
+      const uint32_t o = encode8(v[0], v[1], v[2], v[3], e8m0_to_f32(sc8));
       if (row < rows && col_ok) {
         *reinterpret_cast<uint32_t*>(a.codes + row * cpr + (col >> 1)) = o;
         if ((lane & 3) == 0) a.scales[row * spr + (col >> 5)] = static_cast<uint8_t>(sc8);
       }
-      *reinterpret_cast<u32x4*>(&xw[(i * RPI + lrow) * PT + lcol]) = v[i];
+      *reinterpret_cast<u32x4*>(&xw[(i * RPI + lrow) * PT + lcol]) = v;
     }
   };
   auto mma = [&](uint32_t b) {
@@ -340,8 +367,8 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
   // the next block's loads go out as soon as this block's values are in LDS,
   // and overlap the MFMA phase
   for (; bx < nrb; bx += G) {
-    quant(va, bx);
-    load(va, bx + G);
+    quant(va, ha, bx);
+    load(va, ha, bx + G);
     mma(bx);
   }
 }
@@ -447,13 +474,17 @@ __global__ __launch_bounds__(256) void k_rank_reduce(const RRArgs a) {
 // ---------------------------------------------------------------------------
 // host launchers
 
-hipError_t launch_quant_row32(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
-                              uint8_t* codes, uint8_t* scales, hipStream_t st) {
+hipError_t launch_quant_row32(const uint16_t* in, const uint16_t* in2, int act, int64_t rows,
+                              int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
+                              hipStream_t st) {
   const uint64_t nblk = static_cast<uint64_t>(rows) * (cols / 32);
-  uint64_t grid = (nblk + 255) / 256;
-  if (grid > 8192) grid = 8192;
-  hipLaunchKernelGGL(k_quant_row32, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, in,
-                     static_cast<uint32_t>(rows), static_cast<uint32_t>(cols), ld, codes, scales);
+  uint64_t grid = (nblk + 1023) / 1024;             // 1024 blocks per workgroup pass
+  if (grid > 16384) grid = 16384;
+  const dim3 g(static_cast<uint32_t>(grid));
+  const uint32_t r = static_cast<uint32_t>(rows), c = static_cast<uint32_t>(cols);
+  if (act == 1) hipLaunchKernelGGL(k_quant_row32<1>, g, dim3(256), 0, st, in, in2, r, c, ld, codes, scales);
+  else if (act == 2) hipLaunchKernelGGL(k_quant_row32<2>, g, dim3(256), 0, st, in, in2, r, c, ld, codes, scales);
+  else hipLaunchKernelGGL(k_quant_row32<0>, g, dim3(256), 0, st, in, in2, r, c, ld, codes, scales);
   return hipGetLastError();
 }
 
@@ -491,10 +522,11 @@ size_t quant_down_part_bytes(int64_t rows, int64_t cols, int R) {
   return static_cast<size_t>(splits) * ((rows + 63) / 64) * 4 * nrg * 256 * sizeof(float);
 }
 
-hipError_t launch_quant_down(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
-                             uint8_t* codes, uint8_t* scales, const RankRows& pr, uint16_t* out_lr,
-                             uint16_t* out_pad, const RankRows& cp, int64_t cp_rows,
-                             uint16_t* cp_dst, float* part, hipStream_t st) {
+hipError_t launch_quant_down(const uint16_t* in, const uint16_t* in2, int act, int64_t rows,
+                             int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
+                             const RankRows& pr, uint16_t* out_lr, uint16_t* out_pad,
+                             const RankRows& cp, int64_t cp_rows, uint16_t* cp_dst, float* part,
+                             hipStream_t st) {
   const int R = pr.r0 + pr.r1;
   const int kc = quant_down_kc(rows, cols);
   const uint32_t nrb = static_cast<uint32_t>((rows + 63) / 64);
@@ -506,9 +538,11 @@ hipError_t launch_quant_down(const uint16_t* in, int64_t rows, int64_t cols, int
   const uint32_t resident = static_cast<uint32_t>(cus) * static_cast<uint32_t>(512 / kc);
   uint32_t G = resident / splits;
   G = G < 1 ? 1 : (G > nrb ? nrb : G);
-  QDArgs a{in, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols), ld, codes, scales, pr, R, G, part};
+  QDArgs a{in, in2, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols), ld, codes, scales, pr, R, G, part};
   const dim3 grid(splits * G);
-#define FT_QD(NRG, NS) hipLaunchKernelGGL((k_quant_down<NRG, NS>), grid, dim3(256), 0, st, a)
+#define FT_QDA(NRG, NS, ACT) hipLaunchKernelGGL((k_quant_down<NRG, NS, ACT>), grid, dim3(256), 0, st, a)
+#define FT_QD(NRG, NS) \
+  do { if (act == 1) FT_QDA(NRG, NS, 1); else if (act == 2) FT_QDA(NRG, NS, 2); else FT_QDA(NRG, NS, 0); } while (0)
 #define FT_QD_NS(NRG) \
   do { if (kc == 512) FT_QD(NRG, 4); else if (kc == 256) FT_QD(NRG, 2); else FT_QD(NRG, 1); } while (0)
   const int nrg = (R + 15) / 16;
@@ -520,6 +554,7 @@ hipError_t launch_quant_down(const uint16_t* in, int64_t rows, int64_t cols, int
   }
 #undef FT_QD_NS
 #undef FT_QD
+#undef FT_QDA
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   RRArgs b{part, static_cast<uint32_t>(rows), splits, R, rank_pad(R), out_lr, out_pad, cp, cp_rows, cp_dst};
   const uint64_t ncopy = (static_cast<uint64_t>(cp_rows) * (rank_pad(R) / 8) + 255) / 256;

@@ -36,12 +36,16 @@ class QuantizedLinear:
     by fourtune_quantize, which also writes the transposed codes the backward
     reads.  The rank factors are kept in the library's rank-major storage:
     L1t = L1^T [r_s, K], L2 [r_s, N] (frozen), At = A^T [r_l, K], B [r_l, N]
-    (trainable).
+    (trainable).  act_in / act_out (ops.FT_ACT_*) mark an activation before
+    or after the layer: with act_in, X is the pre-activation h; with act_out,
+    the backward's dY is the gradient of act(Y) and needs H = Y.
     """
 
     def __init__(self, W_res: torch.Tensor, L1t: torch.Tensor | None, L2: torch.Tensor | None,
-                 At: torch.Tensor | None, B: torch.Tensor | None, stream=None):
+                 At: torch.Tensor | None, B: torch.Tensor | None, stream=None,
+                 act_in: int = ops.FT_ACT_NONE, act_out: int = ops.FT_ACT_NONE):
         N, K = W_res.shape
+        self.act_in, self.act_out = int(act_in), int(act_out)
         dev = W_res.device
         self.N, self.K = int(N), int(K)
         self.r_s = 0 if L1t is None else int(L1t.shape[0])
@@ -57,11 +61,12 @@ class QuantizedLinear:
         self._ws = {}
 
     @classmethod
-    def from_factors(cls, W_res, L1, L2, A, B, stream=None) -> "QuantizedLinear":
+    def from_factors(cls, W_res, L1, L2, A, B, stream=None, act_in: int = ops.FT_ACT_NONE,
+                     act_out: int = ops.FT_ACT_NONE) -> "QuantizedLinear":
         """From factors in the method's orientation (L1 [K, r_s], A [K, r_l]):
         the down-projections are copied once into the rank-major storage."""
         t = lambda x: None if x is None else x.t().contiguous()
-        return cls(W_res, t(L1), L2, t(A), B, stream=stream)
+        return cls(W_res, t(L1), L2, t(A), B, stream=stream, act_in=act_in, act_out=act_out)
 
     @property
     def R(self):
@@ -70,7 +75,7 @@ class QuantizedLinear:
     def desc(self, M: int) -> ops.FtLinear:
         return ops.make_linear(M, self.K, self.N, self.r_s, self.r_l, self.w_codes,
                                self.w_scales, self.wt_codes, self.wt_scales, self.L1t, self.L2,
-                               self.At, self.B)
+                               self.At, self.B, self.act_in, self.act_out)
 
     def workspace(self, M: int, is_bwd: bool):
         key = (M, bool(is_bwd))
@@ -93,9 +98,11 @@ class QuantizedLinear:
         return (Y, U, qc, qs) if want_codes else (Y, U)
 
     def backward(self, dY: torch.Tensor, X: torch.Tensor, U: torch.Tensor, need_dx: bool = True,
-                 grad_f32: bool = False, stream=None, want_codes: bool = False):
+                 grad_f32: bool = False, stream=None, want_codes: bool = False,
+                 H: torch.Tensor | None = None):
         """Returns (dX, dAt, dB, P) or (dX, dAt, dB, P, gq_codes, gq_scales);
-        dAt = dA^T [r_l, K] and dB [r_l, N], the layouts of At and B."""
+        dAt = dA^T [r_l, K] and dB [r_l, N], the layouts of At and B.  H is
+        the forward's Y, needed when the layer has act_out."""
         M = int(dY.shape[0])
         dev = self.device
         dX = _empty((M, self.K), torch.bfloat16, dev) if need_dx else None
@@ -106,7 +113,7 @@ class QuantizedLinear:
         qc = _empty((M, self.N // 2), torch.uint8, dev) if want_codes else None
         qs = _empty((M, self.N // 32), torch.uint8, dev) if want_codes else None
         ws = self.workspace(M, True)
-        ops.fourtune_linear_bwd(self.desc(M), dY, X, U if self.R else None, dX, dA, dB,
+        ops.fourtune_linear_bwd(self.desc(M), dY, X, U if self.R else None, H, dX, dA, dB,
                                 ops.FT_F32 if grad_f32 else ops.FT_BF16,
                                 P if self.R else None, qc, qs, ws, ws.numel(), stream)
         out = (dX, dA, dB, P)
@@ -115,19 +122,30 @@ class QuantizedLinear:
 
 class FourTuneLinearFunction(torch.autograd.Function):
     """Y = layer(X) with gradients for X, At and B (W_res, L1, L2 frozen).
-    At and B must be the tensors the layer holds."""
+    At and B must be the tensors the layer holds.  With the layer's act_in,
+    X is the pre-activation and Y = layer(act(X)); with act_out the function
+    returns act(Y) (computed by the library's activation entry point) and
+    keeps Y for the backward."""
 
     @staticmethod
     def forward(ctx, X, At, B, layer: QuantizedLinear):
         Y, U = layer.forward(X.contiguous())
-        ctx.save_for_backward(X, U)
         ctx.layer = layer
+        if layer.act_out != ops.FT_ACT_NONE:
+            ctx.save_for_backward(X, U, Y)
+            out = torch.empty_like(Y)
+            ops.fourtune_act_fwd(layer.act_out, Y, Y.numel(), out)
+            return out
+        ctx.save_for_backward(X, U)
         return Y
 
     @staticmethod
     def backward(ctx, dY):
-        X, U = ctx.saved_tensors
         layer = ctx.layer
+        if layer.act_out != ops.FT_ACT_NONE:
+            X, U, H = ctx.saved_tensors
+        else:
+            (X, U), H = ctx.saved_tensors, None
         dX, dA, dB, _ = layer.backward(dY.contiguous().to(torch.bfloat16), X, U,
-                                       need_dx=ctx.needs_input_grad[0])
+                                       need_dx=ctx.needs_input_grad[0], H=H)
         return dX, dA, dB, None

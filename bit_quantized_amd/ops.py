@@ -18,10 +18,12 @@ FT_OK, FT_EINVAL, FT_ESHAPE, FT_EALIGN, FT_EWORKSPACE, FT_EDEVICE, FT_EUNSUPPORT
 FT_BF16, FT_F32 = 0, 1
 FT_Q_ROW32, FT_Q_ROW32_T, FT_Q_TILE32 = 1, 2, 4
 FT_MAX_RANK = 64
+FT_ACT_NONE, FT_ACT_GELU_TANH = 0, 1
 
 EXPORTS = ("fourtune_quantize", "fourtune_workspace_bytes", "fourtune_linear_fwd",
-           "fourtune_linear_bwd", "fourtune_status_string", "fourtune_timing_enable",
-           "fourtune_timing_reset", "fourtune_timing_read")
+           "fourtune_linear_bwd", "fourtune_act_fwd", "fourtune_act_bwd",
+           "fourtune_status_string", "fourtune_timing_enable", "fourtune_timing_reset",
+           "fourtune_timing_read")
 
 
 class FourTuneError(RuntimeError):
@@ -36,7 +38,8 @@ class FtLinear(ctypes.Structure):
                 ("w_codes", ctypes.c_void_p), ("w_scales", ctypes.c_void_p),
                 ("wt_codes", ctypes.c_void_p), ("wt_scales", ctypes.c_void_p),
                 ("L1t", ctypes.c_void_p), ("L2", ctypes.c_void_p),
-                ("At", ctypes.c_void_p), ("B", ctypes.c_void_p)]
+                ("At", ctypes.c_void_p), ("B", ctypes.c_void_p),
+                ("act_in", ctypes.c_int32), ("act_out", ctypes.c_int32)]
 
 
 _lib = None
@@ -58,9 +61,13 @@ def lib() -> ctypes.CDLL:
         L.fourtune_linear_fwd.argtypes = [ctypes.POINTER(FtLinear), vp, vp, vp, vp, vp, vp,
                                           ctypes.c_size_t, vp]
         L.fourtune_linear_fwd.restype = st
-        L.fourtune_linear_bwd.argtypes = [ctypes.POINTER(FtLinear), vp, vp, vp, vp, vp, vp, st,
-                                          vp, vp, vp, vp, ctypes.c_size_t, vp]
+        L.fourtune_linear_bwd.argtypes = [ctypes.POINTER(FtLinear), vp, vp, vp, vp, vp, vp, vp,
+                                          st, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.fourtune_linear_bwd.restype = st
+        L.fourtune_act_fwd.argtypes = [st, vp, i64, vp, vp]
+        L.fourtune_act_fwd.restype = st
+        L.fourtune_act_bwd.argtypes = [st, vp, vp, i64, vp, vp]
+        L.fourtune_act_bwd.restype = st
         L.fourtune_status_string.argtypes = [st]
         L.fourtune_status_string.restype = ctypes.c_char_p
         L.fourtune_timing_enable.argtypes = [st]
@@ -106,14 +113,15 @@ def _check(status: int, where: str):
 
 
 def make_linear(M, K, N, r_stab, r_lora, w_codes, w_scales, wt_codes=None, wt_scales=None,
-                L1t=None, L2=None, At=None, B=None) -> FtLinear:
+                L1t=None, L2=None, At=None, B=None, act_in=FT_ACT_NONE,
+                act_out=FT_ACT_NONE) -> FtLinear:
     """Fill the ft_linear descriptor from tensors (device) or raw addresses.
 
     The factors are rank-major: L1t = L1^T [r_stab, K], L2 [r_stab, N],
     At = A^T [r_lora, K], B [r_lora, N]."""
     return FtLinear(int(M), int(K), int(N), int(r_stab), int(r_lora), _ptr(w_codes),
                     _ptr(w_scales), _ptr(wt_codes), _ptr(wt_scales), _ptr(L1t), _ptr(L2),
-                    _ptr(At), _ptr(B))
+                    _ptr(At), _ptr(B), int(act_in), int(act_out))
 
 
 def fourtune_quantize(mode, x, rows, cols, ld, codes, scales, codes_t=None, scales_t=None,
@@ -135,13 +143,23 @@ def fourtune_linear_fwd(layer: FtLinear, X, Y, U_save, xq_codes, xq_scales, work
     _check(s, "fourtune_linear_fwd")
 
 
-def fourtune_linear_bwd(layer: FtLinear, dY, X, U_save, dX, dA, dB, grad_dtype, P_save,
+def fourtune_linear_bwd(layer: FtLinear, dY, X, U_save, H, dX, dA, dB, grad_dtype, P_save,
                         gq_codes, gq_scales, workspace, ws_bytes, stream=None):
-    s = lib().fourtune_linear_bwd(ctypes.byref(layer), _ptr(dY), _ptr(X), _ptr(U_save),
+    s = lib().fourtune_linear_bwd(ctypes.byref(layer), _ptr(dY), _ptr(X), _ptr(U_save), _ptr(H),
                                   _ptr(dX), _ptr(dA), _ptr(dB), int(grad_dtype), _ptr(P_save),
                                   _ptr(gq_codes), _ptr(gq_scales), _ptr(workspace),
                                   int(ws_bytes), _stream(stream))
     _check(s, "fourtune_linear_bwd")
+
+
+def fourtune_act_fwd(act, h, n, out, stream=None):
+    _check(lib().fourtune_act_fwd(int(act), _ptr(h), int(n), _ptr(out), _stream(stream)),
+           "fourtune_act_fwd")
+
+
+def fourtune_act_bwd(act, h, g, n, out, stream=None):
+    _check(lib().fourtune_act_bwd(int(act), _ptr(h), _ptr(g), int(n), _ptr(out), _stream(stream)),
+           "fourtune_act_bwd")
 
 
 def fourtune_timing_enable(on: bool):

@@ -92,6 +92,14 @@ typedef enum {
   FT_Q_TILE32 = 4    /* 32x32 square tiles, one scale per tile (weights)             */
 } ft_qmode;
 
+/* Activation next to a linear (FourTune, "3.3 Kernel Fusion for Efficiency /
+ * MLP Fusion": the GeLU between the two linears of an MLP block). */
+typedef enum {
+  FT_ACT_NONE = 0,
+  FT_ACT_GELU_TANH = 1   /* gelu(h) = h (1 + tanh(sqrt(2/pi) (h + 0.044715 h^3))) / 2,
+                            evaluated in fp32, rounded to bf16 once                  */
+} ft_act;
+
 #define FT_MAX_RANK 64
 
 /* One triple-branch linear layer.  Host struct; the pointers in it are device
@@ -107,6 +115,11 @@ typedef struct {
   const uint16_t* L2;         /* bf16 [r_stab, N]  (frozen)                           */
   const uint16_t* At;         /* bf16 [r_lora, K] = A^T  (trainable)                  */
   const uint16_t* B;          /* bf16 [r_lora, N]  (trainable)                        */
+  int32_t act_in;             /* FT_ACT_*: the layer's input is act_in(X): X given to the
+                                 forward and backward is the pre-activation h, and act(h)
+                                 is recomputed wherever it is read, never stored         */
+  int32_t act_out;            /* FT_ACT_*: an activation follows this layer: the backward's
+                                 dY is the gradient of act_out(Y), and H = Y is required */
 } ft_linear;
 
 /* Quantize a bf16 matrix `in` [rows, cols] with row stride ld_in elements.
@@ -138,6 +151,9 @@ size_t fourtune_workspace_bytes(const ft_linear* L, int is_bwd);
  *   kernel 1 reads X once and writes Qrow(X) and U = bf16(X D);
  *   kernel 2 computes deq(Qrow(X)) deq(Qtile(W_res))^T + U V in fp32 and
  *   writes Y (bf16 [M, N]) once.
+ * With act_in != FT_ACT_NONE, X is the pre-activation h and kernel 1 applies
+ * act_in to every value as it reads it (the quantized input and U are those
+ * of act_in(h)).
  * U_save  : bf16 [M, R], written; the backward needs it.  May be NULL if R == 0.
  * xq_codes, xq_scales: optional outputs [M, K/2], [M, K/32]; NULL = keep
  *   them in the workspace.
@@ -158,7 +174,11 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
  *   kernel 3 writes the adapter gradients, rank-major like At and B:
  *   dA^T = P[:, r_stab:]^T X ([r_lora, K]) and dB = U[:, r_stab:]^T dY
  *   ([r_lora, N]), in grad_dtype (FT_BF16 or FT_F32).
- * X and U_save are the forward's input and saved U.  dX may be NULL (no
+ * X and U_save are the forward's input and saved U.  H: bf16 [M, N], this
+ * layer's forward output Y; required when act_out != FT_ACT_NONE (then the
+ * incoming gradient is dY * act_out'(H), recomputed wherever it is read),
+ * else ignored.  With act_in != FT_ACT_NONE, X is the pre-activation h and
+ * dA uses act_in(h), recomputed as X is read.  dX may be NULL (no
  * input gradient; then wt_codes and wt_scales may be NULL).  dA, dB may be
  * NULL only when r_lora == 0.
  * P_save : optional bf16 [M, R] output of P; NULL = workspace only.
@@ -167,10 +187,22 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
  * No gradient is produced for W_res, L1 or L2 (frozen).
  * Errors: FT_EINVAL, FT_ESHAPE, FT_EALIGN, FT_EWORKSPACE, FT_EDEVICE. */
 ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint16_t* X,
-                              const uint16_t* U_save, uint16_t* dX, void* dA, void* dB,
+                              const uint16_t* U_save, const uint16_t* H, uint16_t* dX, void* dA,
+                              void* dB,
                               ft_dtype grad_dtype, uint16_t* P_save, uint8_t* gq_codes,
                               uint8_t* gq_scales, void* workspace, size_t ws_bytes,
                               void* stream);
+
+/* The activation on its own, with the same device functions the fused
+ * kernels apply to their inputs (so that a caller, or a test, can see the
+ * exact bf16 values the layers consume).  n elements, contiguous.
+ *   fourtune_act_fwd: out = bf16(act(h))
+ *   fourtune_act_bwd: out = bf16(g * act'(h))   (the input gradient of act)
+ * act must be FT_ACT_GELU_TANH.  Pointers 16-byte aligned; n >= 0.
+ * Errors: FT_EINVAL, FT_ESHAPE, FT_EALIGN, FT_EDEVICE, FT_EUNSUPPORTED. */
+ft_status fourtune_act_fwd(int act, const uint16_t* h, int64_t n, uint16_t* out, void* stream);
+ft_status fourtune_act_bwd(int act, const uint16_t* h, const uint16_t* g, int64_t n,
+                           uint16_t* out, void* stream);
 
 /* Static, human-readable text for a status code. */
 const char* fourtune_status_string(ft_status s);

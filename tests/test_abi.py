@@ -70,9 +70,9 @@ def _fwd(L, X=A16, Y=A16, U=A16, qc=None, qs=None, ws=A16, wsb=1 << 40):
 
 
 def _bwd(L, dY=A16, X=A16, U=A16, dX=A16, dA=A16, dB=A16, gdt=0, P=None, qc=None, qs=None,
-         ws=A16, wsb=1 << 40):
-    return ops.lib().fourtune_linear_bwd(ctypes.byref(L), dY, X, U, dX, dA, dB, gdt, P, qc, qs,
-                                         ws, wsb, None)
+         ws=A16, wsb=1 << 40, H=None):
+    return ops.lib().fourtune_linear_bwd(ctypes.byref(L), dY, X, U, H, dX, dA, dB, gdt, P, qc,
+                                         qs, ws, wsb, None)
 
 
 def test_linear_shape_errors():
@@ -100,9 +100,27 @@ def test_linear_pointer_errors():
     assert _bwd(_layer(), dA=None) == ops.FT_EINVAL
     assert _bwd(_layer(), gdt=7) == ops.FT_EINVAL
     assert _bwd(_layer(), dX=A16 + 2) == ops.FT_EALIGN
+    # activations: enum values checked; act_out needs H, aligned
+    assert _fwd(_layer(act_in=2)) == ops.FT_EINVAL
+    assert _bwd(_layer(act_out=5), H=A16) == ops.FT_EINVAL
+    assert _bwd(_layer(act_out=ops.FT_ACT_GELU_TANH)) == ops.FT_EINVAL
+    assert _bwd(_layer(act_out=ops.FT_ACT_GELU_TANH), H=A16 + 2) == ops.FT_EALIGN
     # ranks zero: no low-rank pointers are needed
     L0 = _layer(rs=0, rl=0, L1t=None, L2=None, At=None, B=None)
     assert _fwd(L0, U=None, wsb=0) == ops.FT_EWORKSPACE
+
+
+def test_act_argument_errors():
+    L = ops.lib()
+    G = ops.FT_ACT_GELU_TANH
+    assert L.fourtune_act_fwd(0, A16, 64, A16, None) == ops.FT_EINVAL       # no activation
+    assert L.fourtune_act_fwd(G, None, 64, A16, None) == ops.FT_EINVAL
+    assert L.fourtune_act_fwd(G, A16, -1, A16, None) == ops.FT_ESHAPE
+    assert L.fourtune_act_fwd(G, A16 + 2, 64, A16, None) == ops.FT_EALIGN
+    assert L.fourtune_act_fwd(G, A16, 0, A16, None) == ops.FT_OK           # empty is a no-op
+    assert L.fourtune_act_bwd(G, A16, None, 64, A16, None) == ops.FT_EINVAL
+    assert L.fourtune_act_bwd(G, A16, A16 + 8, 64, A16, None) == ops.FT_EALIGN
+    assert L.fourtune_act_bwd(3, A16, A16, 64, A16, None) == ops.FT_EINVAL
 
 
 def test_workspace_size_checked_before_launch():

@@ -1,0 +1,240 @@
+"""GPU parity of the MLP glue around the GELU (two linears with the
+activation between them), through the C ABI.
+
+FourTune, "3.3 Kernel Fusion for Efficiency / MLP Fusion": GeLU sits on the
+wide intermediate between the two linears of an MLP block.  The first
+linear's output h is kept; the second linear takes gelu(h) as its input
+(applied as its quantizer reads h), and in the backward the first linear's
+incoming gradient is dX2 * gelu'(h) (applied as its quantizer and its dB
+read dX2 and h).
+
+The GPU evaluates GELU in fp32 and the oracle in float64; both round to
+bf16, so a value lying within fp32 error of a rounding boundary may round
+the other way.  The activation entry points (the same device functions the
+fused kernels call) are therefore checked against the oracle's GELU to
+within one bf16 ulp, and each linear is then checked against the oracle fed
+the GPU's bf16 activation values, so that the codes compare bit for bit.
+"""
+import numpy as np
+import pytest
+import torch
+
+from bit_quantized_amd import ops, synth
+from bit_quantized_amd.layer import QuantizedLinear, bits_of
+from oracle import linear as OL
+from oracle import mxfp4 as OQ
+
+from _gpu import DEV, REL_TOL, check_rounding_flips, require_gpu, say, up
+
+pytestmark = pytest.mark.gpu
+G = ops.FT_ACT_GELU_TANH
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _ord(bits):
+    """bf16 bit patterns as integers ordered like their values (+0 == -0)."""
+    b = bits.astype(np.int32)
+    return np.where(b & 0x8000, -(b & 0x7FFF), b)
+
+
+def check_ulps(got, ref, name, min_exact=0.999):
+    """got within one bf16 ulp of ref everywhere (values below 2^-126 in
+    magnitude on both sides count as equal: fp32's flush region), and
+    bit-identical in at least `min_exact` of the elements."""
+    d = np.abs(_ord(got) - _ord(ref))
+    tiny = (np.abs(OQ.bf16_bits_to_f64(got)) < 2.0 ** -126) & (np.abs(OQ.bf16_bits_to_f64(ref)) < 2.0 ** -126)
+    bad = (d > 1) & ~tiny
+    assert not bad.any(), (name, int(bad.sum()), got[bad][:5], ref[bad][:5])
+    exact = float(np.mean(d == 0))
+    say(name, "bit-identical fraction", exact)
+    assert exact >= min_exact, (name, exact)
+
+
+def _gelu_gpu(h_bits):
+    h = up(h_bits)
+    out = torch.empty_like(h)
+    ops.fourtune_act_fwd(G, h, h.numel(), out)
+    torch.cuda.synchronize()
+    return bits_of(out)
+
+
+def _gelu_grad_gpu(h_bits, g_bits):
+    h, g = up(h_bits), up(g_bits)
+    out = torch.empty_like(h)
+    ops.fourtune_act_bwd(G, h, g, h.numel(), out)
+    torch.cuda.synchronize()
+    return bits_of(out)
+
+
+def _finite_bf16():
+    b = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    return b[(b & 0x7F80) != 0x7F80]          # drop Inf and NaN
+
+
+def test_gelu_every_bf16_value():
+    h = _finite_bf16()
+    say("case gelu over", h.size, "bf16 values")
+    check_ulps(_gelu_gpu(h), OL.gelu_tanh(h), "gelu")
+
+
+@pytest.mark.parametrize("g", [1.0, -0.3711, 1.5e-3, -2.75e4])
+def test_gelu_grad_every_bf16_value(g):
+    h = _finite_bf16()
+    gb = synth.to_bf16_bits(np.full(h.size, g, dtype=np.float32))
+    say("case gelu' over", h.size, "bf16 values, g =", g)
+    check_ulps(_gelu_grad_gpu(h, gb), OL.gelu_tanh_grad(h, gb), f"gelu_grad g={g}")
+
+
+def test_gelu_odd_length_tail():
+    rng = np.random.default_rng(3)
+    h = synth.to_bf16_bits(rng.standard_normal(1003).astype(np.float32) * 3)
+    # the entry points take any n; the last n % 8 values go through the tail path
+    hb = up(np.concatenate([h, np.zeros(5, np.uint16)]))
+    out = torch.zeros_like(hb)
+    ops.fourtune_act_fwd(G, hb, 1003, out)
+    torch.cuda.synchronize()
+    got = bits_of(out)
+    check_ulps(got[:1003], OL.gelu_tanh(h), "gelu tail")
+    assert np.all(got[1003:] == 0)
+
+
+# ------------------------------------------------------------------ the MLP pair
+class MlpPair:
+    """FC1 (K -> F, act_out = GELU) and FC2 (F -> K, act_in = GELU) on the GPU."""
+
+    def __init__(self, M, K, F, rs, rl, seed):
+        self.c1 = synth.flux_linear_case(f"fc1_{M}x{K}x{F}", M, K, F, rs, rl, seed)
+        self.c2 = synth.flux_linear_case(f"fc2_{M}x{F}x{K}", M, F, K, rs, rl, seed + 1)
+        opt = lambda a: up(a) if a.size else None
+        mk = lambda c, **kw: QuantizedLinear.from_factors(
+            up(c.W_res), opt(c.L1), opt(c.L2), opt(c.A), opt(c.B), **kw)
+        self.fc1 = mk(self.c1, act_out=G)
+        self.fc2 = mk(self.c2, act_in=G)
+
+    def run(self):
+        c1, c2 = self.c1, self.c2
+        X1, dY2 = up(c1.X), up(c2.dY)
+        h, U1, xc1, xs1 = self.fc1.forward(X1, want_codes=True)
+        Y2, U2, xc2, xs2 = self.fc2.forward(h, want_codes=True)
+        dX2, dA2, dB2, P2, gc2, gs2 = self.fc2.backward(dY2, h, U2, want_codes=True)
+        dX1, dA1, dB1, P1, gc1, gs1 = self.fc1.backward(dX2, X1, U1, want_codes=True, H=h)
+        torch.cuda.synchronize()
+        u8 = lambda t: t.cpu().numpy()
+        R = lambda t, c: bits_of(t)[:, :c.R] if c.R else None
+        T = lambda t: None if t is None else np.ascontiguousarray(bits_of(t).T)
+        Bb = lambda t: None if t is None else bits_of(t)
+        return dict(h=bits_of(h), U1=R(U1, c1), xc1=u8(xc1), xs1=u8(xs1),
+                    Y2=bits_of(Y2), U2=R(U2, c2), xc2=u8(xc2), xs2=u8(xs2),
+                    dX2=bits_of(dX2), dA2=T(dA2), dB2=Bb(dB2),
+                    P2=R(P2, c2), gc2=u8(gc2), gs2=u8(gs2),
+                    dX1=bits_of(dX1), dA1=T(dA1), dB1=Bb(dB1),
+                    P1=R(P1, c1), gc1=u8(gc1), gs1=u8(gs1))
+
+
+def _absdot(x_bits, w):
+    return np.abs(OQ.bf16_bits_to_f64(x_bits)) @ np.abs(w)
+
+
+def _check_layer_full(tag, c, X, dY, got_fwd, got_bwd, Y_name):
+    """One linear against the oracle in full, given the operands the GPU saw.
+    got_fwd = (Y, U, xc, xs); got_bwd = (dX, dA, dB, P, gc, gs)."""
+    wc, ws = OQ.quantize_tile32(c.W_res)
+    f = OL.linear_fwd(X, wc, ws, c.L1, c.L2, c.A, c.B)
+    b = OL.linear_bwd(dY, X, f["U"], wc, ws, c.L1, c.L2, c.A, c.B)
+    Y, U, xc, xs = got_fwd
+    dX, dA, dB, P, gc, gs = got_bwd
+    np.testing.assert_array_equal(xc, f["xq_codes"], err_msg=tag + " xq codes")
+    np.testing.assert_array_equal(xs, f["xq_scales"], err_msg=tag + " xq scales")
+    np.testing.assert_array_equal(gc, b["gq_codes"], err_msg=tag + " gq codes")
+    np.testing.assert_array_equal(gs, b["gq_scales"], err_msg=tag + " gq scales")
+    res = {Y_name: OL.rel_frobenius(Y, f["Y"]), "dX": OL.rel_frobenius(dX, b["dX"])}
+    if c.r_l:
+        res["dA"] = OL.rel_frobenius(dA, b["dA"])
+        res["dB"] = OL.rel_frobenius(dB, b["dB"])
+    if c.R:
+        res["U"] = OL.rel_frobenius(U, f["U"])
+        res["P"] = OL.rel_frobenius(P, b["P"])
+    say(tag, {k: round(v, 8) for k, v in res.items()})
+    for k, v in res.items():
+        assert v <= REL_TOL, (tag, k, v)
+    if c.R:
+        D = OL.stack_down(c.L1, c.A)
+        V = OL.stack_up(c.L2, c.B)
+        check_rounding_flips(U, f["U"], tag + " U", _absdot(X, D), c.K)
+        check_rounding_flips(P, b["P"], tag + " P", _absdot(dY, V.T), c.N)
+    return f
+
+
+@pytest.mark.parametrize("shape", [
+    (300, 288, 544, 16, 8),     # ragged tokens, several tiles, F not a multiple of 128
+    (130, 256, 1024, 32, 32),   # R = 64
+    (64, 160, 320, 0, 8),       # adapter only
+    (40, 96, 192, 0, 0),        # no low-rank branches (plain quantizer with the activation)
+])
+def test_mlp_pair_chain_full(shape):
+    M, K, F, rs, rl = shape
+    say("case mlp pair", shape)
+    mp = MlpPair(M, K, F, rs, rl, seed=M + F)
+    got = mp.run()
+    c1, c2 = mp.c1, mp.c2
+    a_gpu = _gelu_gpu(got["h"])
+    check_ulps(a_gpu, OL.gelu_tanh(got["h"]), "a = gelu(h)", min_exact=0.99)
+    dh_gpu = _gelu_grad_gpu(got["h"], got["dX2"])
+    check_ulps(dh_gpu, OL.gelu_tanh_grad(got["h"], got["dX2"]), "dh", min_exact=0.99)
+    # FC2 consumes gelu(h): the oracle is fed the GPU's bf16 activation
+    _check_layer_full("fc2", c2, a_gpu, c2.dY,
+                      (got["Y2"], got["U2"], got["xc2"], got["xs2"]),
+                      (got["dX2"], got["dA2"], got["dB2"], got["P2"], got["gc2"], got["gs2"]), "Y2")
+    # FC1's incoming gradient is dX2 * gelu'(h)
+    _check_layer_full("fc1", c1, c1.X, dh_gpu,
+                      (got["h"], got["U1"], got["xc1"], got["xs1"]),
+                      (got["dX1"], got["dA1"], got["dB1"], got["P1"], got["gc1"], got["gs1"]), "h")
+
+
+def test_mlp_pair_chain_full_size_sampled():
+    """FLUX MLP at full size: 4608 tokens, 3072 -> 12288 -> GELU -> 3072, ranks 32/32.
+    Row outputs on sampled rows; codes of the sampled rows; adapter gradients and
+    the down-projections over all rows."""
+    M, K, F = 4608, 3072, 12288
+    say("case mlp pair full size")
+    mp = MlpPair(M, K, F, 32, 32, seed=2)
+    got = mp.run()
+    c1, c2 = mp.c1, mp.c2
+    rng = np.random.default_rng(11)
+    rows = np.unique(np.concatenate([rng.choice(M, 40, replace=False), [0, M - 1]]))
+    a_gpu = _gelu_gpu(got["h"])
+    check_ulps(a_gpu[rows], OL.gelu_tanh(got["h"][rows]), "a rows")
+    dh_gpu = _gelu_grad_gpu(got["h"], got["dX2"])
+    check_ulps(dh_gpu[rows], OL.gelu_tanh_grad(got["h"][rows], got["dX2"][rows]), "dh rows")
+    for tag, c, X, dY, Yk, Uk, xk, gk, Pk, dXk, dAk, dBk in (
+            ("fc2", c2, a_gpu, c2.dY, "Y2", "U2", "2", "2", "P2", "dX2", "dA2", "dB2"),
+            ("fc1", c1, c1.X, dh_gpu, "h", "U1", "1", "1", "P1", "dX1", "dA1", "dB1")):
+        wc, ws = OQ.quantize_tile32(c.W_res)
+        xc, xs = OQ.quantize_row32(X[rows])
+        np.testing.assert_array_equal(got["xc" + xk][rows], xc, err_msg=tag)
+        np.testing.assert_array_equal(got["xs" + xk][rows], xs, err_msg=tag)
+        gc, gs = OQ.quantize_row32(dY[rows])
+        np.testing.assert_array_equal(got["gc" + gk][rows], gc, err_msg=tag)
+        np.testing.assert_array_equal(got["gs" + gk][rows], gs, err_msg=tag)
+        Y, U = OL.linear_fwd_rows(rows, X, wc, ws, c.L1, c.L2, c.A, c.B)
+        dX, P = OL.linear_bwd_rows(rows, dY, wc, ws, c.L1, c.L2, c.A, c.B)
+        D = OL.stack_down(c.L1, c.A)
+        V = OL.stack_up(c.L2, c.B)
+        Uf = OL.down_proj(X, D)
+        Pf = OL.down_proj(dY, V.T)
+        dA = OQ.bf16_bits_to_f64(X).T @ OQ.bf16_bits_to_f64(Pf)[:, c.r_s:]
+        dB = OQ.bf16_bits_to_f64(Uf)[:, c.r_s:].T @ OQ.bf16_bits_to_f64(dY)
+        res = {"Y": OL.rel_frobenius(got[Yk][rows], OQ.f64_to_bf16_bits(Y)),
+               "dX": OL.rel_frobenius(got[dXk][rows], OQ.f64_to_bf16_bits(dX)),
+               "U": OL.rel_frobenius(got[Uk], Uf), "P": OL.rel_frobenius(got[Pk], Pf),
+               "dA": OL.rel_frobenius(got[dAk], OQ.f64_to_bf16_bits(dA)),
+               "dB": OL.rel_frobenius(got[dBk], OQ.f64_to_bf16_bits(dB))}
+        say(tag, {k: round(v, 8) for k, v in res.items()})
+        for k, v in res.items():
+            assert v <= REL_TOL, (tag, k, v)
+        check_rounding_flips(got[Uk], Uf, tag + " U", _absdot(X, D), c.K)
+        check_rounding_flips(got[Pk], Pf, tag + " P", _absdot(dY, V.T), c.N)
