@@ -48,7 +48,8 @@ def parse():
                     help="timed repetitions of the CPU oracle step (the rate is their mean)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stress", action="store_true")
-    ap.add_argument("--only", choices=["step", "stress"], default=None,
+    ap.add_argument("--no-mlp", action="store_true")
+    ap.add_argument("--only", choices=["step", "stress", "mlp"], default=None,
                     help="run only one part (for profiler runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain bf16 elementwise copy of known size (the reference "
@@ -323,7 +324,7 @@ def main():
             lay, X, dY, U, Y, dX, dA, dB, wsf, wsb = sets[i % len(sets)]
             d = lay.desc(M)
             ops.fourtune_linear_fwd(d, X, Y, U, None, None, wsf, wsf.numel(), stream)
-            ops.fourtune_linear_bwd(d, dY, X, U, dX, dA, dB, ops.FT_BF16, None, None, None, wsb,
+            ops.fourtune_linear_bwd(d, dY, X, U, None, dX, dA, dB, ops.FT_BF16, None, None, None, wsb,
                                     wsb.numel(), stream)
 
         for i in range(a.warmup):
@@ -386,6 +387,75 @@ def main():
             "source_sha": sha,
         })
         del sets
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ MLP pair with GELU
+    if not a.no_mlp and a.only in (None, "mlp"):
+        Mm, Km, Fm, rsm, rlm = 4608, 3072, 12288, 32, 32
+        log(f"bench: MLP pair M={Mm} {Km}->{Fm}->GELU->{Km}, ranks {rsm}/{rlm}")
+        c1 = synth.flux_linear_case("mlp_fc1", Mm, Km, Fm, rsm, rlm, seed=2)
+        c2 = synth.flux_linear_case("mlp_fc2", Mm, Fm, Km, rsm, rlm, seed=3)
+        up = lambda x: bf16_tensor(x, dev)
+        msets = []
+        for s_ in range(2):
+            fc1 = QuantizedLinear.from_factors(torch.roll(up(c1.W_res), 32 * s_, 0).contiguous(),
+                                               up(c1.L1), up(c1.L2), up(c1.A), up(c1.B),
+                                               act_out=ops.FT_ACT_GELU_TANH)
+            fc2 = QuantizedLinear.from_factors(torch.roll(up(c2.W_res), 32 * s_, 0).contiguous(),
+                                               up(c2.L1), up(c2.L2), up(c2.A), up(c2.B),
+                                               act_in=ops.FT_ACT_GELU_TANH)
+            X1 = torch.roll(up(c1.X), 97 * s_, 0).contiguous()
+            dY2 = torch.roll(up(c2.dY), 97 * s_, 0).contiguous()
+            bt = lambda *sh: torch.empty(sh, dtype=torch.bfloat16, device=dev)
+            bufs = dict(h=bt(Mm, Fm), U1=bt(Mm, rsm + rlm), Y2=bt(Mm, Km), U2=bt(Mm, rsm + rlm),
+                        dX2=bt(Mm, Fm), dA2=bt(rlm, Fm), dB2=bt(rlm, Km), dX1=bt(Mm, Km),
+                        dA1=bt(rlm, Km), dB1=bt(rlm, Fm))
+            ws = {k: (lay.workspace(Mm, False), lay.workspace(Mm, True)) for k, lay in (("1", fc1), ("2", fc2))}
+            msets.append((fc1, fc2, X1, dY2, bufs, ws))
+        del c1, c2
+        torch.cuda.synchronize()
+
+        def mlp_step(i):
+            fc1, fc2, X1, dY2, b, ws = msets[i % len(msets)]
+            d1, d2 = fc1.desc(Mm), fc2.desc(Mm)
+            (w1f, w1b), (w2f, w2b) = ws["1"], ws["2"]
+            ops.fourtune_linear_fwd(d1, X1, b["h"], b["U1"], None, None, w1f, w1f.numel(), stream)
+            ops.fourtune_linear_fwd(d2, b["h"], b["Y2"], b["U2"], None, None, w2f, w2f.numel(), stream)
+            ops.fourtune_linear_bwd(d2, dY2, b["h"], b["U2"], None, b["dX2"], b["dA2"], b["dB2"],
+                                    ops.FT_BF16, None, None, None, w2b, w2b.numel(), stream)
+            ops.fourtune_linear_bwd(d1, b["dX2"], X1, b["U1"], b["h"], b["dX1"], b["dA1"], b["dB1"],
+                                    ops.FT_BF16, None, None, None, w1b, w1b.numel(), stream)
+
+        nst = max(5, a.steps // 5)
+        for i in range(3):
+            mlp_step(i)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for i in range(nst):
+            mlp_step(i)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        mms = e0.elapsed_time(e1) / nst
+        w1 = layer_work(Mm, Km, Fm, rsm, rlm)
+        w2 = layer_work(Mm, Fm, Km, rsm, rlm)
+        mflop = sum(v["flop"] for v in w1.values()) + sum(v["flop"] for v in w2.values())
+        ops.fourtune_timing_reset()
+        ops.fourtune_timing_enable(True)
+        for i in range(nst):
+            mlp_step(i)
+        torch.cuda.synchronize()
+        ops.fourtune_timing_enable(False)
+        per = {k: round(tot / cnt * 1e3, 2) for k, (tot, cnt) in ops.fourtune_timing_read().items() if cnt}
+        out["mlp_pair"] = {
+            "workload": f"FLUX MLP pair fwd+bwd: {Mm} tokens, {Km}->{Fm} -> tanh-GELU -> {Fm}->{Km}, "
+                        f"r_stab={rsm}, r_lora={rlm}; GELU applied inside the quantizers and the "
+                        f"adapter-gradient kernel",
+            "us_per_step": round(mms * 1e3, 1), "TFLOP/s": round(mflop / (mms * 1e-3) / 1e12, 1),
+            "step_flop": mflop, "steps": nst,
+            "kernel_avg_us_both_linears": per}
+        log("bench: mlp", json.dumps(out["mlp_pair"]))
+        del msets
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ quantizer stress

@@ -19,9 +19,9 @@ __global__ __launch_bounds__(256) void k_act(const uint16_t* __restrict__ h,
   const int64_t nv = n / 8;
   const int64_t stride = static_cast<int64_t>(gridDim.x) * 256;
   for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < nv; i += stride) {
-    const u32x4 x = reinterpret_cast<const u32x4*>(h)[i];
+    const u32x4 x = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(h) + i);
     u32x4 o;
-    if constexpr (ACT == 2) o = act_bf16x8<2>(reinterpret_cast<const u32x4*>(g)[i], x);
+    if constexpr (ACT == 2) o = act_bf16x8<2>(__builtin_nontemporal_load(reinterpret_cast<const u32x4*>(g) + i), x);
     else o = act_bf16x8<1>(x, x);
     reinterpret_cast<u32x4*>(out)[i] = o;
   }
@@ -29,8 +29,8 @@ __global__ __launch_bounds__(256) void k_act(const uint16_t* __restrict__ h,
   if (blockIdx.x == 0 && threadIdx.x == 0) {
     for (int64_t e = nv * 8; e < n; ++e) {
       const float hv = bf16_to_f32(h[e]);
-      out[e] = ACT == 2 ? f32_to_bf16_rne(gelu_tanh_grad_f32(hv, bf16_to_f32(g[e])))
-                        : f32_to_bf16_rne(gelu_tanh_f32(hv));
+      const float r = ACT == 2 ? gelu_tanh_grad_f32(hv, bf16_to_f32(g[e])) : gelu_tanh_f32(hv);
+      out[e] = static_cast<uint16_t>(cvt_pk_bf16(r, 0.0f));
     }
   }
 }

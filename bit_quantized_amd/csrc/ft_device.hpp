@@ -90,6 +90,15 @@ __device__ __forceinline__ uint32_t encode8(uint32_t w0, uint32_t w1, uint32_t w
   return r;
 }
 
+// ---------------------------------------------------------------- scheduling
+// Workgroup i of n -> logical index, so that the workgroups the hardware
+// sends to one XCD (i % 8; each XCD has its own L2) get consecutive logical
+// indices.
+__device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t n) {
+  const uint32_t x = i & 7, j = i >> 3, q = n >> 3, r = n & 7;
+  return x * q + (x < r ? x : r) + j;
+}
+
 // ---------------------------------------------------------------- matrix cores
 // 32x32x64 MXFP4 x MXFP4 -> fp32.  Lane l supplies 32 E2M1 codes (16 bytes)
 // of row/column l%32 for reduction block l/32, and the E8M0 scale of that
@@ -137,71 +146,64 @@ __device__ __forceinline__ u32x4 lds_read_b128(const void* p) {
 //   (1 + tanh(u)) / 2 = sigmoid(z) = s,   s = 1/(1+e) (z >= 0) or e/(1+e) (z < 0),
 //   1 - s = e/(1+e) (z >= 0) or 1/(1+e) (z < 0),
 //   gelu'(h) = s + h s (1 - s) dz/dh,     dz/dh = 2 sqrt(2/pi) (1 + 3 * 0.044715 h^2),
-// so neither tail overflows.  exp(-|z|) = 2^(-|z| log2 e) on the hardware
-// exp2, which flushes results below 2^-126; where e < 2^-64 it is computed
-// as e * 2^64 and the scale is taken out in the last multiplication (for
-// z >= 0 such an e changes nothing: 1 + e rounds to 1).  Evaluated in fp32
-// with every operation written out (no contraction), so that every kernel
-// that calls these gets the same bits; the caller rounds to bf16 once.
-constexpr float kGeluC = 0.7978845608028654f;       // sqrt(2 / pi)
-constexpr float kGeluA = 0.044715f;
+// so neither tail overflows.  The hardware exp2 flushes results below
+// 2^-126, so it computes E = e * 2^64 (at most 2^64) and the scale comes out
+// in the last multiplication of the z < 0 branch.  1/(1+e) is the hardware
+// reciprocal (1 ulp).  In gelu' the polynomial uses h clamped to [-16, 16]:
+// beyond that the second term is below 2^-100 of the first (z >= 0) or the
+// whole value underflows (z < 0), and the clamp keeps 0 * inf out.  fp32
+// throughout, every operation written out (no contraction), so that every
+// kernel that calls these gets the same bits; the caller rounds to bf16 once.
+constexpr float kGeluC2 = 1.5957691216057308f;      // 2 sqrt(2/pi)
+constexpr float kGeluC2A = 0.07135481627260025f;    // 2 sqrt(2/pi) * 0.044715
+constexpr float kGeluC6A = 0.21406444881780076f;    // 6 sqrt(2/pi) * 0.044715
 constexpr float kLog2e = 1.4426950408889634f;
-
-struct GeluParts {
-  float z;      // 2u
-  float e;      // exp(-|z|), times 2^64 when `deep`
-  float inv;    // 1 / (1 + exp(-|z|))
-  float sc;     // 2^-64 when deep, else 1
-  bool deep;
-};
-
-__device__ __forceinline__ GeluParts gelu_parts(float h) {
-#pragma clang fp contract(off)
-  GeluParts p;
-  const float h2 = h * h;
-  p.z = (2.0f * kGeluC) * (h * (1.0f + kGeluA * h2));
-  const float x = -__builtin_fabsf(p.z) * kLog2e;
-  p.deep = x < -64.0f;
-  p.e = __builtin_amdgcn_exp2f(p.deep ? x + 64.0f : x);
-  p.sc = p.deep ? 5.421010862427522e-20f : 1.0f;            // 2^-64
-  p.inv = 1.0f / (1.0f + (p.deep ? 0.0f : p.e));
-  return p;
-}
+constexpr float kTwo64 = 18446744073709551616.0f;   // 2^64
+constexpr float kTwoM64 = 5.421010862427522e-20f;   // 2^-64
 
 // gelu(h) = h s
 __device__ __forceinline__ float gelu_tanh_f32(float h) {
 #pragma clang fp contract(off)
-  const GeluParts p = gelu_parts(h);
-  if (p.z >= 0.0f) return h * p.inv;
-  return ((h * p.e) * p.inv) * p.sc;
+  const float z = h * __builtin_fmaf(kGeluC2A, h * h, kGeluC2);
+  const float E = __builtin_amdgcn_exp2f(__builtin_fmaf(-__builtin_fabsf(z), kLog2e, 64.0f));
+  const float inv = __builtin_amdgcn_rcpf(__builtin_fmaf(E, kTwoM64, 1.0f));
+  const float pos = h * inv;
+  const float neg = ((h * E) * inv) * kTwoM64;
+  return z >= 0.0f ? pos : neg;
 }
 
-// g gelu'(h) = g (s + h s (1 - s) dz/dh)
+// g gelu'(h) = g s (1 + h (1 - s) dz/dh)      (s (1 - s) = e inv^2)
 __device__ __forceinline__ float gelu_tanh_grad_f32(float h, float g) {
 #pragma clang fp contract(off)
-  const GeluParts p = gelu_parts(h);
-  const float dz = (2.0f * kGeluC) * (1.0f + (3.0f * kGeluA) * (h * h));
-  if (p.z >= 0.0f) {
-    // s = inv, 1 - s = e inv; below 2^-64 the second term is negligible
-    const float t = p.deep ? 0.0f : ((h * p.inv) * (p.e * p.inv)) * dz;
-    return g * (p.inv + t);
-  }
-  // s = e inv, 1 - s = inv:  g s (1 + h (1 - s) dz/dh)
-  const float gs = (g * p.e) * p.inv;
-  if (gs == 0.0f) return gs * p.sc;          // e underflowed (|h| large): exactly +-0
-  return (gs * (1.0f + (h * p.inv) * dz)) * p.sc;
+  const float z = h * __builtin_fmaf(kGeluC2A, h * h, kGeluC2);
+  const float E = __builtin_amdgcn_exp2f(__builtin_fmaf(-__builtin_fabsf(z), kLog2e, 64.0f));
+  const float e = E * kTwoM64;
+  const float inv = __builtin_amdgcn_rcpf(__builtin_fmaf(E, kTwoM64, 1.0f));
+  const float hc = __builtin_amdgcn_fmed3f(h, -16.0f, 16.0f);
+  const float dz = __builtin_fmaf(kGeluC6A, hc * hc, kGeluC2);
+  // z >= 0: s = inv, 1 - s = e inv
+  const float pos = (g * inv) * __builtin_fmaf(hc * (e * inv), dz, 1.0f);
+  // z < 0: s = e inv, 1 - s = inv
+  const float neg = (((g * E) * inv) * __builtin_fmaf(hc * inv, dz, 1.0f)) * kTwoM64;
+  return z >= 0.0f ? pos : neg;
 }
 
 // Activation modes of a bf16 input stream (FT_ACT_* of the C ABI):
 // ACT 0: x as is; ACT 1: gelu(x); ACT 2: x * gelu'(h) with h a second stream.
 // Applied to two packed bf16, rounded to bf16 (nearest even).
+// Two fp32 to packed bf16, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float lo, float hi) {
+  const f32x2 x = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(x, bf16x2));
+}
+
 template <int ACT>
 __device__ __forceinline__ uint32_t act_bf16x2(uint32_t x, uint32_t h) {
   if constexpr (ACT == 1) {
-    return pack_bf16x2_rne(gelu_tanh_f32(bf16lo_to_f32(x)), gelu_tanh_f32(bf16hi_to_f32(x)));
+    return cvt_pk_bf16(gelu_tanh_f32(bf16lo_to_f32(x)), gelu_tanh_f32(bf16hi_to_f32(x)));
   } else if constexpr (ACT == 2) {
-    return pack_bf16x2_rne(gelu_tanh_grad_f32(bf16lo_to_f32(h), bf16lo_to_f32(x)),
-                           gelu_tanh_grad_f32(bf16hi_to_f32(h), bf16hi_to_f32(x)));
+    return cvt_pk_bf16(gelu_tanh_grad_f32(bf16lo_to_f32(h), bf16lo_to_f32(x)),
+                       gelu_tanh_grad_f32(bf16hi_to_f32(h), bf16hi_to_f32(x)));
   } else {
     (void)h;
     return x;
@@ -226,6 +228,10 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* p, uint6
 }
 __device__ __forceinline__ u32x4 buf_load128(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 0));
+}
+// The same with the non-temporal (streaming) cache policy, for data read once.
+__device__ __forceinline__ u32x4 buf_load128_nt(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, (int)off, 0, 2));
 }
 __device__ __forceinline__ uint32_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);

@@ -75,13 +75,6 @@ __device__ __forceinline__ uint32_t bload8(__amdgpu_buffer_rsrc_t r, uint32_t of
   return __builtin_amdgcn_raw_buffer_load_b8(r, (int)off, 0, 0);
 }
 
-// Workgroup i of n -> logical index, so that the workgroups the hardware
-// sends to one XCD (i % 8) get consecutive logical indices.
-__device__ __forceinline__ uint32_t xcd_remap(uint32_t i, uint32_t n) {
-  const uint32_t x = i & 7, j = i >> 3, q = n >> 3, r = n & 7;
-  return x * q + (x < r ? x : r) + j;
-}
-
 // Logical tile index -> tile origin: groups of 4 m-tiles with the n-tiles
 // inner, so that consecutive indices share A rows and B columns.
 __device__ __forceinline__ void tile_coords(uint32_t lid, uint32_t mt_n, uint32_t nt_n, int64_t& m0,

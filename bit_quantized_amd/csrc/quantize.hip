@@ -28,8 +28,9 @@ namespace ft {
 // blocks (1 KB) and one store writes their 256 bytes of codes; the block
 // amax takes two quad DPP steps.  Each lane has U blocks in flight.  ACT
 // applies the input activation first (0: none; 1: gelu(in); 2: in *
-// gelu'(in2)), rounded to bf16 as the quantizer's input.
-template <int ACT>
+// gelu'(in2)), rounded to bf16 as the quantizer's input.  CONTIG: rows are
+// contiguous (ld == cols), so block b starts at element 32 b.
+template <int ACT, bool CONTIG>
 __global__ __launch_bounds__(256) void k_quant_row32(const uint16_t* __restrict__ in,
                                                      const uint16_t* __restrict__ in2,
                                                      uint32_t rows, uint32_t cols, int64_t ld,
@@ -50,10 +51,14 @@ __global__ __launch_bounds__(256) void k_quant_row32(const uint16_t* __restrict_
 #pragma unroll
     for (int k = 0; k < U; ++k) {
       const uint32_t b = b0 + 16 * k + (lane >> 2);
-      const uint32_t r = b / bpr, cb = b - r * bpr;
-      const uint32_t off = b < nblk ? (r * ld32 + cb * 32 + q * 8) * 2 : BUF_OOB;
-      v[k] = buf_load128(r1, off);
-      if constexpr (ACT == 2) h[k] = buf_load128(r2, off);
+      uint32_t e0 = b * 32;
+      if constexpr (!CONTIG) {
+        const uint32_t r = b / bpr;
+        e0 = r * ld32 + (b - r * bpr) * 32;
+      }
+      const uint32_t off = b < nblk ? (e0 + q * 8) * 2 : BUF_OOB;
+      v[k] = buf_load128_nt(r1, off);
+      if constexpr (ACT == 2) h[k] = buf_load128_nt(r2, off);
       else h[k] = v[k];
     }
 #pragma unroll
@@ -75,148 +80,196 @@ __global__ __launch_bounds__(256) void k_quant_row32(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// 32x32 tiles.  A workgroup covers 32 rows x 128 columns (4 tiles); thread
-// t reads 16 consecutive elements of row t/8 (columns 16*(t%8) ...).
-// Optionally also writes the transposed codes [cols, rows/2] and scales
-// [cols/32, rows/32]: the same numbers, since a tile has one scale.
+// Workgroup -> (column group x, row group y) of an nx by ny grid.  The
+// logical index runs through bands of 8 row groups, row group fastest, so
+// the workgroups one XCD holds at a time cover 8 consecutive row groups of
+// the same columns: the transposed outputs of those 8 (16 bytes each per
+// column) fill whole 128-byte lines in that XCD's L2.
+__device__ __forceinline__ void band_coords(uint32_t L, uint32_t nx, uint32_t ny, uint32_t& x,
+                                            uint32_t& y) {
+  const uint32_t band = L / (8 * nx);
+  const uint32_t h = ny - band * 8 < 8 ? ny - band * 8 : 8;
+  const uint32_t r = L - band * 8 * nx;
+  x = r / h;
+  y = band * 8 + r % h;
+}
+
+// Loads of a 32-row x 512-column slab: wave w holds rows 8w .. 8w+7, lane l
+// columns 8l .. 8l+7 of each (one 1 KB instruction per row); 4 consecutive
+// lanes hold one 32-column block of a row.
+__device__ __forceinline__ void load_slab(__amdgpu_buffer_rsrc_t r, uint32_t row0, uint32_t col,
+                                          bool ok, uint32_t ld2, u32x4 (&v)[8]) {
+  const uint32_t base = ok ? row0 * ld2 + col * 2 : BUF_OOB;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) v[i] = buf_load128_nt(r, base == BUF_OOB ? BUF_OOB : base + i * ld2);
+}
+
+// ---------------------------------------------------------------------------
+// 32x32 tiles.  A workgroup covers 32 rows x 512 columns (16 tiles).  The
+// tile amax: each lane's 8 x 8 values, a quad DPP step across the tile's 4
+// lanes, then the 4 waves through LDS.  Optionally also the transposed codes
+// [cols, rows/2] and scales [cols/32, rows/32] (the same numbers, since a
+// tile has one scale): the codes go to LDS row-major and come back
+// transposed with ds_read_b64_tr_b4, one 16-byte column segment per lane.
 __global__ __launch_bounds__(256) void k_quant_tile32(const uint16_t* __restrict__ in,
                                                       uint32_t rows, uint32_t cols, int64_t ld,
                                                       uint8_t* __restrict__ codes,
                                                       uint8_t* __restrict__ scales,
                                                       uint8_t* __restrict__ codes_t,
                                                       uint8_t* __restrict__ scales_t) {
-  __shared__ uint32_t red[4][4];
-  __shared__ __attribute__((aligned(16))) uint8_t ct[32 * 64];   // this block's codes, row-major
+  constexpr int CT_P = 264;                                   // LDS pitch of a code row (bytes)
+  __shared__ uint32_t red[4][16];
+  __shared__ __attribute__((aligned(16))) uint8_t ct[32 * CT_P];
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const uint32_t row = blockIdx.y * 32 + (t >> 3);
-  const uint32_t col = blockIdx.x * 128 + (t & 7) * 16;
-  const bool ok = col < cols;  // rows is a multiple of 32, so row < rows
-  u32x4 v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
-  if (ok) {
-    const u32x4* src = reinterpret_cast<const u32x4*>(in + row * ld + col);
-    v0 = __builtin_nontemporal_load(src);
-    v1 = __builtin_nontemporal_load(src + 1);
-  }
+  const uint32_t nx = (cols + 511) / 512, ny = rows / 32;
+  uint32_t x, y;
+  band_coords(xcd_remap(blockIdx.x, nx * ny), nx, ny, x, y);
+  const uint32_t col = x * 512 + 8 * lane;
+  const bool ok = col < cols;
+  u32x4 v[8];
+  load_slab(make_rsrc(in, static_cast<uint64_t>(rows) * ld * 2), y * 32 + 8 * wave, col, ok,
+            static_cast<uint32_t>(ld) * 2, v);
   uint32_t m = 0;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) m = max_u16x2(m, max_u16x2(abs_bf16x2(v0[j]), abs_bf16x2(v1[j])));
-  uint32_t a = hmax_u16x2(m);
-  // reduce over the 16 lanes of this wave that hold the same tile:
-  // lane bit 0 (half of the tile row) and bits 3-5 (row within the wave)
-  a = max(a, (uint32_t)__shfl_xor((int)a, 1));
-  a = max(a, (uint32_t)__shfl_xor((int)a, 8));
-  a = max(a, (uint32_t)__shfl_xor((int)a, 16));
-  a = max(a, (uint32_t)__shfl_xor((int)a, 32));
-  const int tile = (t & 7) >> 1;
-  if ((lane & 0x39) == 0) red[wave][tile] = a;  // lanes 0,2,4,6 of the wave
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) m = max_u16x2(m, abs_bf16x2(v[i][j]));
+  uint32_t am = hmax_u16x2(m);
+  am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0xB1, 0xF, 0xF, false)));
+  am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0x4E, 0xF, 0xF, false)));
+  const int tile = lane >> 2;
+  if ((lane & 3) == 0) red[wave][tile] = am;
   __syncthreads();
-  a = max(max(red[0][tile], red[1][tile]), max(red[2][tile], red[3][tile]));
-  const uint32_t s = e8m0_from_amax_bits(a);
+  am = max(max(red[0][tile], red[1][tile]), max(red[2][tile], red[3][tile]));
+  const uint32_t s = e8m0_from_amax_bits(am);
   const float sc = e8m0_to_f32(s);
-  u32x2 o;
-  o[0] = encode8(v0[0], v0[1], v0[2], v0[3], sc);
-  o[1] = encode8(v1[0], v1[1], v1[2], v1[3], sc);
+  uint32_t o[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) o[i] = encode8(v[i][0], v[i][1], v[i][2], v[i][3], sc);
   if (ok) {
-    *reinterpret_cast<u32x2*>(codes + static_cast<uint64_t>(row) * (cols >> 1) + (col >> 1)) = o;
-    if ((t >> 3) == 0 && (t & 1) == 0) {
-      scales[static_cast<uint64_t>(blockIdx.y) * (cols >> 5) + (col >> 5)] = static_cast<uint8_t>(s);
-      if (scales_t)
-        scales_t[static_cast<uint64_t>(col >> 5) * (rows >> 5) + blockIdx.y] = static_cast<uint8_t>(s);
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<uint32_t*>(codes + static_cast<uint64_t>(y * 32 + 8 * wave + i) * (cols >> 1) + (col >> 1)) = o[i];
+    if (wave == 0 && (lane & 3) == 0) {
+      scales[static_cast<uint64_t>(y) * (cols >> 5) + (col >> 5)] = static_cast<uint8_t>(s);
+      if (scales_t) scales_t[static_cast<uint64_t>(col >> 5) * ny + y] = static_cast<uint8_t>(s);
     }
   }
   if (!codes_t) return;
-  *reinterpret_cast<u32x2*>(&ct[(t >> 3) * 64 + (t & 7) * 8]) = o;
-  __syncthreads();
-  // transposed row c (an input column) gets 16 input rows, 2 per byte
-  const int c = t >> 1, h = t & 1;
-  const uint32_t gc = blockIdx.x * 128 + c;
-  if (gc >= cols) return;
-  uint32_t w[2] = {0, 0};
 #pragma unroll
-  for (int b = 0; b < 8; ++b) {
-    const int r = 16 * h + 2 * b;
-    const uint32_t lo = (ct[r * 64 + (c >> 1)] >> (4 * (c & 1))) & 0xFu;
-    const uint32_t hi = (ct[(r + 1) * 64 + (c >> 1)] >> (4 * (c & 1))) & 0xFu;
-    w[b >> 2] |= (lo | (hi << 4)) << (8 * (b & 3));
+  for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(&ct[(8 * wave + i) * CT_P + 4 * lane]) = o[i];
+  __syncthreads();
+  // 16-lane group g of wave w, pass j: columns 16 cg .. 16 cg + 15; lane q
+  // addresses row q (then 16 + q) and receives column 16 cg + q
+  const int q = lane & 15;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int cg = (wave * 2 + j) * 4 + (lane >> 4);
+    const u32x2 lo = lds_read_tr4(&ct[q * CT_P + cg * 8]);
+    const u32x2 hi = lds_read_tr4(&ct[(16 + q) * CT_P + cg * 8]);
+    const uint32_t c = x * 512 + cg * 16 + q;
+    if (c < cols)
+      *reinterpret_cast<u32x4*>(codes_t + static_cast<uint64_t>(c) * (rows >> 1) + y * 16) =
+          u32x4{lo[0], lo[1], hi[0], hi[1]};
   }
-  *reinterpret_cast<u32x2*>(codes_t + static_cast<uint64_t>(gc) * (rows >> 1) + blockIdx.y * 16 + 8 * h) =
-      u32x2{w[0], w[1]};
 }
 
 // ---------------------------------------------------------------------------
-// Dual output: 1x32 blocks along rows and along columns, from one read.
-// A workgroup covers a 64x64 tile.  Row pass: thread t holds 16 elements
-// of row t/4.  Column pass (through LDS): thread t holds 16 elements of
-// column t/4.
+// Dual output from one read: 1x32 blocks along rows (codes [rows, cols/2])
+// and along columns (the row blocks of the transpose, codes_t [cols,
+// rows/2]).  A workgroup covers 32 rows x 512 columns.  Row blocks: as the
+// row quantizer (quad DPP amax).  Column blocks: each lane takes the max of
+// its 8 rows per column, the 4 waves combine through LDS; the codes are made
+// from vertical pairs (rows 2p, 2p+1 of one column share a scale), so each
+// converted byte already is a byte of the transposed layout, and a lane's
+// 4 bytes are 8 rows of one column.  The 4 waves' words of a column meet in
+// LDS and leave as one 16-byte store.
 __global__ __launch_bounds__(256) void k_quant_row32_t(const uint16_t* __restrict__ in,
                                                        uint32_t rows, uint32_t cols, int64_t ld,
                                                        uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales,
                                                        uint8_t* __restrict__ codes_t,
                                                        uint8_t* __restrict__ scales_t) {
-  constexpr int P = 66;  // LDS row pitch in bf16 (odd number of dwords)
-  __shared__ uint16_t tile[64 * P];
-  const int t = threadIdx.x;
-  const uint32_t r0 = blockIdx.y * 64, c0 = blockIdx.x * 64;
-  {
-    const int lr = t >> 2, lc = (t & 3) * 16;
-    const uint32_t row = r0 + lr, col = c0 + lc;
-    const bool ok = row < rows && col < cols;
-    u32x4 v0 = {0, 0, 0, 0}, v1 = {0, 0, 0, 0};
-    if (ok) {
-      const u32x4* src = reinterpret_cast<const u32x4*>(in + row * ld + col);
-      v0 = __builtin_nontemporal_load(src);
-      v1 = __builtin_nontemporal_load(src + 1);
-    }
-    uint32_t m = 0;
+  __shared__ __attribute__((aligned(16))) uint32_t cmax[4][64][4];
+  __shared__ __attribute__((aligned(16))) uint32_t ctw[4][512 + 4];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const uint32_t nx = (cols + 511) / 512, ny = rows / 32;
+  uint32_t x, y;
+  band_coords(xcd_remap(blockIdx.x, nx * ny), nx, ny, x, y);
+  const uint32_t col = x * 512 + 8 * lane;
+  const bool ok = col < cols;
+  u32x4 v[8];
+  load_slab(make_rsrc(in, static_cast<uint64_t>(rows) * ld * 2), y * 32 + 8 * wave, col, ok,
+            static_cast<uint32_t>(ld) * 2, v);
+
+  // ---- row blocks
 #pragma unroll
-    for (int j = 0; j < 4; ++j) m = max_u16x2(m, max_u16x2(abs_bf16x2(v0[j]), abs_bf16x2(v1[j])));
-    uint32_t a = hmax_u16x2(m);
-    a = max(a, (uint32_t)__shfl_xor((int)a, 1));
-    const uint32_t s = e8m0_from_amax_bits(a);
-    const float sc = e8m0_to_f32(s);
+  for (int i = 0; i < 8; ++i) {
+    uint32_t am = hmax_u16x2(max_u16x2(max_u16x2(abs_bf16x2(v[i][0]), abs_bf16x2(v[i][1])),
+                                       max_u16x2(abs_bf16x2(v[i][2]), abs_bf16x2(v[i][3]))));
+    am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0xB1, 0xF, 0xF, false)));
+    am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0x4E, 0xF, 0xF, false)));
+    const uint32_t s = e8m0_from_amax_bits(am);
+    const uint32_t o = encode8(v[i][0], v[i][1], v[i][2], v[i][3], e8m0_to_f32(s));
+    const uint32_t row = y * 32 + 8 * wave + i;
     if (ok) {
-      u32x2 o;
-      o[0] = encode8(v0[0], v0[1], v0[2], v0[3], sc);
-      o[1] = encode8(v1[0], v1[1], v1[2], v1[3], sc);
-      *reinterpret_cast<u32x2*>(codes + static_cast<uint64_t>(row) * (cols >> 1) + (col >> 1)) = o;
-      if ((t & 1) == 0)
-        scales[static_cast<uint64_t>(row) * (cols >> 5) + (col >> 5)] = static_cast<uint8_t>(s);
-    }
-    uint16_t* dst = tile + lr * P + lc;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      dst[2 * j] = static_cast<uint16_t>(v0[j]);
-      dst[2 * j + 1] = static_cast<uint16_t>(v0[j] >> 16);
-      dst[8 + 2 * j] = static_cast<uint16_t>(v1[j]);
-      dst[8 + 2 * j + 1] = static_cast<uint16_t>(v1[j] >> 16);
+      *reinterpret_cast<uint32_t*>(codes + static_cast<uint64_t>(row) * (cols >> 1) + (col >> 1)) = o;
+      if ((lane & 3) == 0) scales[static_cast<uint64_t>(row) * (cols >> 5) + (col >> 5)] = static_cast<uint8_t>(s);
     }
   }
+
+  // ---- column blocks: amax of columns 2k (low half) and 2k+1 (high half)
+  u32x4 cm = {0, 0, 0, 0};
+#pragma unroll
+  for (int i = 0; i < 8; ++i)
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cm[k] = max_u16x2(cm[k], abs_bf16x2(v[i][k]));
+  *reinterpret_cast<u32x4*>(&cmax[wave][lane][0]) = cm;
   __syncthreads();
-  {
-    const int lc = t >> 2, lr = (t & 3) * 16;
-    const uint32_t col = c0 + lc, row = r0 + lr;
-    uint32_t w[8];
+  u32x4 cw = *reinterpret_cast<const u32x4*>(&cmax[0][lane][0]);
+#pragma unroll
+  for (int w = 1; w < 4; ++w) {
+    const u32x4 o = *reinterpret_cast<const u32x4*>(&cmax[w][lane][0]);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) cw[k] = max_u16x2(cw[k], o[k]);
+  }
+  uint32_t cs[8];
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    cs[2 * k] = e8m0_from_amax_bits(cw[k] & 0xFFFFu);
+    cs[2 * k + 1] = e8m0_from_amax_bits(cw[k] >> 16);
+  }
+  // column j = 2k + h: byte p of its word = rows 8w + 2p (low nibble), 8w + 2p + 1
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+      const float sc = e8m0_to_f32(cs[2 * k + h]);
+      auto vp = [&](int p) {
+        return __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(v[2 * p + 1][k], v[2 * p][k], sel));
+      };
+      uint32_t r = 0;
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(0), sc, 0);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(1), sc, 1);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(2), sc, 2);
+      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(3), sc, 3);
+      ctw[wave][8 * lane + 2 * k + h] = r;
+    }
+  }
+  if (wave == 0 && ok) {
 #pragma unroll
     for (int j = 0; j < 8; ++j)
-      w[j] = static_cast<uint32_t>(tile[(lr + 2 * j) * P + lc]) |
-             (static_cast<uint32_t>(tile[(lr + 2 * j + 1) * P + lc]) << 16);
-    uint32_t m = 0;
+      scales_t[static_cast<uint64_t>(col + j) * ny + y] = static_cast<uint8_t>(cs[j]);
+  }
+  __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 8; ++j) m = max_u16x2(m, abs_bf16x2(w[j]));
-    uint32_t a = hmax_u16x2(m);
-    a = max(a, (uint32_t)__shfl_xor((int)a, 1));
-    const uint32_t s = e8m0_from_amax_bits(a);
-    const float sc = e8m0_to_f32(s);
-    if (col < cols && row < rows) {
-      u32x2 o;
-      o[0] = encode8(w[0], w[1], w[2], w[3], sc);
-      o[1] = encode8(w[4], w[5], w[6], w[7], sc);
-      *reinterpret_cast<u32x2*>(codes_t + static_cast<uint64_t>(col) * (rows >> 1) + (row >> 1)) =
-          o;
-      if ((t & 1) == 0)
-        scales_t[static_cast<uint64_t>(col) * (rows >> 5) + (row >> 5)] = static_cast<uint8_t>(s);
-    }
+  for (int h = 0; h < 2; ++h) {
+    const int cc = t + 256 * h;
+    const uint32_t c = x * 512 + cc;
+    if (c < cols)
+      *reinterpret_cast<u32x4*>(codes_t + static_cast<uint64_t>(c) * (rows >> 1) + y * 16) =
+          u32x4{ctw[0][cc], ctw[1][cc], ctw[2][cc], ctw[3][cc]};
   }
 }
 
@@ -294,7 +347,7 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const uint32_t off = base == BUF_OOB ? BUF_OOB : base + i * RPI * ld2;
-      v[i] = buf_load128(rin, off);
+      v[i] = buf_load128(rin, off);                  // re-read later in the step: cached
       if constexpr (ACT == 2) h[i] = buf_load128(rin2, off);
     }
   };
@@ -482,17 +535,21 @@ hipError_t launch_quant_row32(const uint16_t* in, const uint16_t* in2, int act, 
   if (grid > 16384) grid = 16384;
   const dim3 g(static_cast<uint32_t>(grid));
   const uint32_t r = static_cast<uint32_t>(rows), c = static_cast<uint32_t>(cols);
-  if (act == 1) hipLaunchKernelGGL(k_quant_row32<1>, g, dim3(256), 0, st, in, in2, r, c, ld, codes, scales);
-  else if (act == 2) hipLaunchKernelGGL(k_quant_row32<2>, g, dim3(256), 0, st, in, in2, r, c, ld, codes, scales);
-  else hipLaunchKernelGGL(k_quant_row32<0>, g, dim3(256), 0, st, in, in2, r, c, ld, codes, scales);
+#define FT_QR(A, C) hipLaunchKernelGGL((k_quant_row32<A, C>), g, dim3(256), 0, st, in, in2, r, c, ld, codes, scales)
+#define FT_QRA(A) do { if (ld == cols) FT_QR(A, true); else FT_QR(A, false); } while (0)
+  if (act == 1) FT_QRA(1);
+  else if (act == 2) FT_QRA(2);
+  else FT_QRA(0);
+#undef FT_QRA
+#undef FT_QR
   return hipGetLastError();
 }
 
 hipError_t launch_quant_tile32(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
                                uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
                                uint8_t* scales_t, hipStream_t st) {
-  dim3 grid(static_cast<uint32_t>((cols + 127) / 128), static_cast<uint32_t>(rows / 32));
-  hipLaunchKernelGGL(k_quant_tile32, grid, dim3(256), 0, st, in, static_cast<uint32_t>(rows),
+  const uint32_t n = static_cast<uint32_t>(((cols + 511) / 512) * (rows / 32));
+  hipLaunchKernelGGL(k_quant_tile32, dim3(n), dim3(256), 0, st, in, static_cast<uint32_t>(rows),
                      static_cast<uint32_t>(cols), ld, codes, scales, codes_t, scales_t);
   return hipGetLastError();
 }
@@ -500,8 +557,8 @@ hipError_t launch_quant_tile32(const uint16_t* in, int64_t rows, int64_t cols, i
 hipError_t launch_quant_row32_t(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
                                 uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
                                 uint8_t* scales_t, hipStream_t st) {
-  dim3 grid(static_cast<uint32_t>((cols + 63) / 64), static_cast<uint32_t>((rows + 63) / 64));
-  hipLaunchKernelGGL(k_quant_row32_t, grid, dim3(256), 0, st, in, static_cast<uint32_t>(rows),
+  const uint32_t n = static_cast<uint32_t>(((cols + 511) / 512) * (rows / 32));
+  hipLaunchKernelGGL(k_quant_row32_t, dim3(n), dim3(256), 0, st, in, static_cast<uint32_t>(rows),
                      static_cast<uint32_t>(cols), ld, codes, scales, codes_t, scales_t);
   return hipGetLastError();
 }
