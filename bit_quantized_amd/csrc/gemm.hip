@@ -379,23 +379,38 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
     asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
   };
   // SAME: Cur and Nxt are one register set (the odd step of a tile).
+  // The bookkeeping of a step (DMA addresses, fragment and scale reads,
+  // scale shifts, cursor advance) is spread between the MFMAs of its two
+  // halves, so that it issues while the matrix core is busy instead of
+  // leaving it idle between the halves.
   auto step = [&](Frags& Cur, Frags& Nxt, auto kind, bool after_store, auto same) {
     constexpr bool RANK = decltype(kind)::v == 1;
     constexpr bool SAME = decltype(same)::v == 1;
     const int buf = gs & (NST - 1);
-    const HalfDma hb = half_dma(cb, true);
-    read_frags(buf, 1, Cur.a1, Cur.b1);
-    if constexpr (!SAME) { keep4(Nxt.a1); keep4(Nxt.b1); }
-    __builtin_amdgcn_sched_barrier(0);
+    const int nbuf = (gs + 1) & (NST - 1);
+    auto mma = [&](int i, const u32x4 (&af)[4], const u32x4 (&bf)[4], auto opsel) {
+      constexpr int OP = decltype(opsel)::v;
+      if constexpr (RANK)
+        acc[i >> 2][i & 3] = mfma_bf16_32x32x16(af[i >> 2], bf[i & 3], acc[i >> 2][i & 3]);
+      else
+        acc[i >> 2][i & 3] = mfma_fp4_32x32x64<OP, OP>(af[i >> 2], bf[i & 3], acc[i >> 2][i & 3],
+                                                       Cur.as[i >> 2], Cur.bs[i & 3]);
+    };
+    const MfmaKind<0> op0;
+    const MfmaKind<2> op2;
+    // ---- first half: chunk 0 of this step; chunk 1 is read meanwhile
+    HalfDma hb;
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if constexpr (RANK)
-        acc[i >> 2][i & 3] = mfma_bf16_32x32x16(Cur.a0[i >> 2], Cur.b0[i & 3], acc[i >> 2][i & 3]);
-      else
-        acc[i >> 2][i & 3] = mfma_fp4_32x32x64<0, 0>(Cur.a0[i >> 2], Cur.b0[i & 3], acc[i >> 2][i & 3],
-                                                     Cur.as[i >> 2], Cur.bs[i & 3]);
-      if (i % 3 == 1) {
+      mma(i, Cur.a0, Cur.b0, op0);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i == 0) {
+        hb = half_dma(cb, true);
+        read_frags(buf, 1, Cur.a1, Cur.b1);
+        if constexpr (!SAME) { keep4(Nxt.a1); keep4(Nxt.b1); }
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i % 3 == 1) {
         dma(hb, i / 3, true);
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -412,34 +427,48 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
     else __builtin_amdgcn_s_waitcnt(waitcnt_imm(4 * DMA_HALF, 0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    const HalfDma ha = half_dma(ca, false);
+    // ---- second half: chunk 1; the next step's chunk 0 and scales are read
+    HalfDma ha;
     uint32_t ras[4], rbs[4];
-    read_scales((gs + 1) & (NST - 1), ras, rbs);
-    read_frags((gs + 1) & (NST - 1), 0, Nxt.a0, Nxt.b0);
-    if constexpr (!SAME) { keep4(Cur.a0); keep4(Cur.b0); }
-    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
-      if constexpr (RANK)
-        acc[i >> 2][i & 3] = mfma_bf16_32x32x16(Cur.a1[i >> 2], Cur.b1[i & 3], acc[i >> 2][i & 3]);
-      else
-        acc[i >> 2][i & 3] = mfma_fp4_32x32x64<2, 2>(Cur.a1[i >> 2], Cur.b1[i & 3], acc[i >> 2][i & 3],
-                                                     Cur.as[i >> 2], Cur.bs[i & 3]);
-      if (i % 3 == 1) {
+      mma(i, Cur.a1, Cur.b1, op2);
+      __builtin_amdgcn_sched_barrier(0);
+      if (i == 0) {
+        ha = half_dma(ca, false);
+        read_scales(nbuf, ras, rbs);
+        read_frags(nbuf, 0, Nxt.a0, Nxt.b0);
+        if constexpr (!SAME) { keep4(Cur.a0); keep4(Cur.b0); }
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i % 3 == 1) {
         dma(ha, i / 3, false);
         __builtin_amdgcn_sched_barrier(0);
+      }
+      if (i == 8) {
+        cursor_next(cb, true);
+        cursor_next(ca, false);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      if constexpr (!SAME) {
+        if (i == 12) {
+#pragma unroll
+          for (int j = 0; j < 4; ++j) { Nxt.as[j] = ras[j] >> (8 * grp); Nxt.bs[j] = rbs[j] >> (8 * grp); }
+          __builtin_amdgcn_sched_barrier(0);
+        }
       }
     }
     pin_acc();
     __builtin_amdgcn_sched_barrier(0);
+    if constexpr (SAME) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) { Nxt.as[i] = ras[i] >> (8 * grp); Nxt.bs[i] = rbs[i] >> (8 * grp); }
-    if constexpr (!SAME) { keep_s(Cur.as); keep_s(Cur.bs); }
+      for (int j = 0; j < 4; ++j) { Nxt.as[j] = ras[j] >> (8 * grp); Nxt.bs[j] = rbs[j] >> (8 * grp); }
+    } else {
+      keep_s(Cur.as);
+      keep_s(Cur.bs);
+    }
     keep_s(Nxt.as);
     keep_s(Nxt.bs);
-    cursor_next(cb, true);
-    cursor_next(ca, false);
     ++gs;
     __builtin_amdgcn_sched_barrier(0);
   };
