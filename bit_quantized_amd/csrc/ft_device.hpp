@@ -133,6 +133,19 @@ __device__ __forceinline__ u32x2 lds_read_tr4(const void* p) {
   return __builtin_bit_cast(u32x2, r);
 }
 
+// 64-bit LDS read with a transpose of 16-bit elements across each group of
+// 16 lanes: lane q receives element q % 4 of the 8-byte chunks addressed by
+// lanes q/4, q/4 + 4, q/4 + 8 and q/4 + 12, in that order (layout probed
+// on the target).  With lane j of a group addressing row k0 + j/4, columns
+// c0 + 4 (j % 4) .. +3 of a row-major bf16 tile, lane q receives rows
+// k0 .. k0+3 of column c0 + q: four consecutive reduction indices of one
+// MFMA operand column.  `p` must point into __shared__ memory.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ u32x2 lds_read_tr16(const void* p) {
+  s16x4 r = __builtin_amdgcn_ds_read_tr16_b64_v4i16((FT_LDS s16x4*)(p));
+  return __builtin_bit_cast(u32x2, r);
+}
+
 // 128-bit read from __shared__ memory.
 __device__ __forceinline__ u32x4 lds_read_b128(const void* p) {
   return *(const FT_LDS u32x4*)(p);

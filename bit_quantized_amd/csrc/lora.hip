@@ -6,19 +6,24 @@
 // with X and G unquantized.  Here (X A) is the adapter part of the saved
 // down-projection U = bf16(X [L1|A]) and (G B^T) the adapter part of
 // P = bf16(G [L2;B]^T).  Both gradients have the form
-//   g(i, r) = sum_m big[m][i] * small[m][r0 + r]
-// with big = X (dA) or dY (dB) and small = P or U, and are stored like the
-// factors, rank-major: out[r][i] (dA^T [r, K] and dB [r, N]).  One launch computes
-// both: the first workgroup columns cover dA, the rest dB.
+//   out[r][i] = sum_m small[m][r0 + r] * big[m][i]
+// with big = X (dA) or dY (dB) and small = P or U, stored like the factors,
+// rank-major (dA^T [r, K] and dB [r, N]).  One launch computes both: the
+// first workgroup columns cover dA, the rest dB.
 //
-// The reduction runs over tokens m, which is the row index of both
-// operands, so each 64-token step of big is written to LDS transposed
-// (token index contiguous) and consumed by 16x16x32 bf16 MFMAs with fp32
-// accumulation; the small operand of the workgroup's 512 tokens is staged
-// transposed once.  All global loads of a workgroup are issued up front.
-// Each 512-token chunk writes fp32 partials; k_lora_reduce, the next kernel
-// on the stream, adds them in chunk order (deterministic) and rounds once.
-// HBM bound: big is read once.
+// 16x16x32 bf16 MFMAs with A = small^T (ranks x tokens) and B = big (tokens
+// x columns), fp32 accumulation.  The reduction runs over tokens, the row
+// index of both operands in memory, so both are staged in LDS row-major as
+// loaded (16-byte stores, no transposition) and the operands are read with
+// ds_read_b64_tr_b16, which hands each lane four consecutive tokens of its
+// column.  The MFMA's 32 reduction slots of lane group g take tokens
+// 4g .. 4g+3 and 16+4g .. 16+4g+3 of a 32-token half step, the same for both
+// operands, which keeps each read conflict-free (8 rows per half wave,
+// pitches chosen so 8 consecutive rows start in distinct 8-bank groups).
+// A workgroup covers 64 columns x 512 tokens; all of its global loads go out
+// up front.  Each 512-token chunk writes fp32 partials; k_lora_reduce, the
+// next kernel on the stream, adds them in chunk order (deterministic) and
+// rounds once.  HBM bound: big is read once.
 //
 // Around a GELU ("3.3 ... MLP Fusion"): the second linear of an MLP takes
 // gelu(h) as its input, so its dA recomputes gelu on the saved h as big is
@@ -32,35 +37,37 @@ namespace ft {
 namespace {
 
 constexpr int IB = 64;      // columns of big per workgroup
-constexpr int MS = 64;      // tokens per LDS step
+constexpr int MS = 64;      // tokens per step
 constexpr int NSTEP = 8;    // steps per workgroup
 constexpr int MC = MS * NSTEP;
-constexpr int PM = MS + 8;  // LDS pitch (bf16) of a transposed big step
-constexpr int PS = MC + 8;  // LDS pitch (bf16) of the transposed small operand
+constexpr int PB = 80;      // LDS pitch (bf16) of a big row: 40 dwords
+// LDS pitch (bf16) of a small row: 8 (2 RG - 1) dwords, an odd multiple of 8
+template <int RG> constexpr int small_pitch() { return 16 * (2 * RG - 1); }
 
 // One workgroup: 64 columns of big (column block cb) x 512 tokens.  ACT is
 // the activation applied to big as it is loaded (rounded to bf16).
 template <int RG, int ACT>
-__device__ __forceinline__ void lora_block(const LoraGradArgs& a, uint32_t cb, uint16_t (*bigT)[IB * PM],
-                                           uint16_t* smT) {
+__device__ __forceinline__ void lora_block(const LoraGradArgs& a, uint32_t cb,
+                                           uint16_t (*bigL)[MS * PB], uint16_t* smL) {
   constexpr int RP = RG * 16;
+  constexpr int PS = small_pitch<RG>();
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int g = lane >> 4, l16 = lane & 15;
+  const int g = lane >> 4, q = lane & 15;
   const int64_t M = a.M, I = a.I;
   const int64_t i0 = static_cast<int64_t>(cb) * IB;
   const int64_t mbeg = static_cast<int64_t>(blockIdx.y) * MC;
   const int64_t mend = M < mbeg + MC ? M : mbeg + MC;
 
-  // ---- issue the big loads of every step: thread t covers row pair p = t/8
-  // (tokens 2p, 2p+1 of the step) and columns 8*(t%8) .. +8
+  // ---- big loads of every step: thread t covers rows t/8 and 32 + t/8 of
+  // the step, columns 8 (t % 8) .. +8 (each row's 128 bytes in 8 lanes)
   const auto rbig = make_rsrc(a.big, static_cast<uint64_t>(M) * I * 2);
   const auto rbig2 = make_rsrc(a.big2, ACT == 2 ? static_cast<uint64_t>(M) * I * 2 : 0);
-  const int pp = t >> 3, cc = (t & 7) * 8;
+  const int lr = t >> 3, cc = (t & 7) * 8;
   const bool col_ok = i0 + cc < I;
   u32x4 va[NSTEP], vb[NSTEP], ha[NSTEP], hb[NSTEP];
 #pragma unroll
   for (int s = 0; s < NSTEP; ++s) {
-    const int64_t ma = mbeg + s * MS + 2 * pp, mb = ma + 1;
+    const int64_t ma = mbeg + s * MS + lr, mb = ma + 32;
     const uint32_t oa = col_ok && ma < mend ? static_cast<uint32_t>((ma * I + i0 + cc) * 2) : BUF_OOB;
     const uint32_t ob = col_ok && mb < mend ? static_cast<uint32_t>((mb * I + i0 + cc) * 2) : BUF_OOB;
     va[s] = buf_load128(rbig, oa);
@@ -71,16 +78,17 @@ __device__ __forceinline__ void lora_block(const LoraGradArgs& a, uint32_t cb, u
     }
   }
 
-  // ---- stage small[m][r0 + r] of the chunk transposed: smT[r][m - mbeg]
+  // ---- small[m][r0 + r] of the chunk, row-major: smL[m][r], ranks >= rl zero
   const int rl = a.rl;
   if ((a.r0 & 7) == 0 && (a.ld_small & 7) == 0 && (rl & 7) == 0) {
     const auto rs = make_rsrc(a.small, static_cast<uint64_t>(M) * a.ld_small * 2);
-    constexpr int PER = MC * RP / 8 / 256;          // 16-byte chunks per thread (upper bound)
+    constexpr int CPR = RP / 8;                      // 16-byte chunks per token
+    constexpr int PER = MC * CPR / 256;
     u32x4 w[PER];
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
-      const int c = t + 256 * e;                    // chunk = 8 ranks of token m
-      const int m = c % MC, rc = c / MC;
+      const int c = t + 256 * e;
+      const int m = c / CPR, rc = c % CPR;
       const int64_t gm = mbeg + m;
       w[e] = buf_load128(rs, (8 * rc < rl && gm < mend)
                                  ? static_cast<uint32_t>((gm * a.ld_small + a.r0 + 8 * rc) * 2) : BUF_OOB);
@@ -88,18 +96,13 @@ __device__ __forceinline__ void lora_block(const LoraGradArgs& a, uint32_t cb, u
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const int c = t + 256 * e;
-      const int m = c % MC, rc = c / MC;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        smT[(8 * rc + 2 * k) * PS + m] = static_cast<uint16_t>(w[e][k]);
-        smT[(8 * rc + 2 * k + 1) * PS + m] = static_cast<uint16_t>(w[e][k] >> 16);
-      }
+      *reinterpret_cast<u32x4*>(&smL[(c / CPR) * PS + (c % CPR) * 8]) = w[e];
     }
   } else {
     for (int idx = t; idx < MC * RP; idx += 256) {
-      const int m = idx % MC, r = idx / MC;
+      const int m = idx / RP, r = idx % RP;
       const int64_t gm = mbeg + m;
-      smT[r * PS + m] = (gm < mend && r < rl) ? a.small[gm * a.ld_small + a.r0 + r] : uint16_t(0);
+      smL[m * PS + r] = (gm < mend && r < rl) ? a.small[gm * a.ld_small + a.r0 + r] : uint16_t(0);
     }
   }
 
@@ -109,55 +112,50 @@ __device__ __forceinline__ void lora_block(const LoraGradArgs& a, uint32_t cb, u
 
 #pragma unroll
   for (int s = 0; s < NSTEP; ++s) {
-    uint16_t* bt = bigT[s & 1];
-    const u32x4 xa = act_bf16x8<ACT>(va[s], ACT == 2 ? ha[s] : va[s]);
-    const u32x4 xb = act_bf16x8<ACT>(vb[s], ACT == 2 ? hb[s] : vb[s]);
-#pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t lo = (xa[j] & 0xFFFFu) | (xb[j] << 16);        // column cc+2j
-      const uint32_t hi = (xa[j] >> 16) | (xb[j] & 0xFFFF0000u);    // column cc+2j+1
-      *reinterpret_cast<uint32_t*>(&bt[(cc + 2 * j) * PM + 2 * pp]) = lo;
-      *reinterpret_cast<uint32_t*>(&bt[(cc + 2 * j + 1) * PM + 2 * pp]) = hi;
-    }
+    uint16_t* bl = bigL[s & 1];
+    *reinterpret_cast<u32x4*>(&bl[lr * PB + cc]) = act_bf16x8<ACT>(va[s], ACT == 2 ? ha[s] : va[s]);
+    *reinterpret_cast<u32x4*>(&bl[(32 + lr) * PB + cc]) = act_bf16x8<ACT>(vb[s], ACT == 2 ? hb[s] : vb[s]);
     __syncthreads();
-    // wave w owns columns 16w .. 16w+15 of the block; lane (row l16, group g)
-    // covers tokens 8g .. 8g+7 of each 32-token half of the step
+    // wave w: columns 16w .. 16w+15 of the block; lane q of group g addresses
+    // row 4g + q/4 (+16) of the half step, columns c0 + 4 (q % 4)
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const u32x4 af = *reinterpret_cast<const u32x4*>(&bt[(16 * wave + l16) * PM + 32 * h + 8 * g]);
+    for (int kk = 0; kk < 2; ++kk) {
+      const uint16_t* bp = bl + (kk * 32 + 4 * g + (q >> 2)) * PB + 16 * wave + 4 * (q & 3);
+      const u32x2 b0 = lds_read_tr16(bp), b1 = lds_read_tr16(bp + 16 * PB);
+      const u32x4 bf = {b0[0], b0[1], b1[0], b1[1]};
 #pragma unroll
       for (int c = 0; c < RG; ++c) {
-        const u32x4 bf = *reinterpret_cast<const u32x4*>(&smT[(16 * c + l16) * PS + s * MS + 32 * h + 8 * g]);
-        acc[c] = mfma_bf16_16x16x32(af, bf, acc[c]);
+        const uint16_t* sp = smL + (s * MS + kk * 32 + 4 * g + (q >> 2)) * PS + 16 * c + 4 * (q & 3);
+        const u32x2 a0 = lds_read_tr16(sp), a1 = lds_read_tr16(sp + 16 * PS);
+        acc[c] = mfma_bf16_16x16x32(u32x4{a0[0], a0[1], a1[0], a1[1]}, bf, acc[c]);
       }
     }
   }
 
-  // acc[c][j]: column i = i0 + 16*wave + 4*g + j, rank r = 16*c + l16;
-  // partials part[chunk][i][RP]
-  float* mypart = a.part + static_cast<int64_t>(blockIdx.y) * I * RP;
+  // acc[c][j]: rank r = 16c + 4g + j, column i = i0 + 16 wave + q;
+  // partials part[chunk][r][I], rank-major
+  const int64_t i = i0 + 16 * wave + q;
+  if (i < I) {
+    float* mypart = a.part + static_cast<int64_t>(blockIdx.y) * RP * I;
 #pragma unroll
-  for (int c = 0; c < RG; ++c)
+    for (int c = 0; c < RG; ++c)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int64_t i = i0 + 16 * wave + 4 * g + j;
-      if (i < I) mypart[i * RP + 16 * c + l16] = acc[c][j];
-    }
+      for (int j = 0; j < 4; ++j) mypart[(16 * c + 4 * g + j) * I + i] = acc[c][j];
+  }
 }
 
 template <int RG, int ACTA, int ACTB>
 __global__ __launch_bounds__(256) void k_lora_grads(const LoraGradArgs pa, const LoraGradArgs pb,
                                                     uint32_t nib_a) {
-  constexpr int RP = RG * 16;
-  __shared__ __attribute__((aligned(16))) uint16_t bigT[2][IB * PM];
-  __shared__ __attribute__((aligned(16))) uint16_t smT[RP * PS];
-  if (blockIdx.x < nib_a) lora_block<RG, ACTA>(pa, blockIdx.x, bigT, smT);
-  else lora_block<RG, ACTB>(pb, blockIdx.x - nib_a, bigT, smT);
+  __shared__ __attribute__((aligned(16))) uint16_t bigL[2][MS * PB];
+  __shared__ __attribute__((aligned(16))) uint16_t smL[MC * small_pitch<RG>()];
+  if (blockIdx.x < nib_a) lora_block<RG, ACTA>(pa, blockIdx.x, bigL, smL);
+  else lora_block<RG, ACTB>(pb, blockIdx.x - nib_a, bigL, smL);
 }
 
-// out[r][i] = sum over chunks y (in order) of part[y][i][r]; a thread owns
-// column i and 4 consecutive ranks, so consecutive threads store
-// consecutive columns of a rank row.  Blocks [0, nblk_a) serve dA.
+// out[r][i .. i+3] = sum over chunks y (in order) of part[y][r][i .. i+3];
+// consecutive threads take consecutive column quads of a rank row.  Blocks
+// [0, nblk_a) serve dA.
 template <int RG>
 __global__ __launch_bounds__(256) void k_lora_reduce(const LoraGradArgs pa, const LoraGradArgs pb,
                                                      uint32_t nblk_a, uint32_t nmc) {
@@ -165,13 +163,12 @@ __global__ __launch_bounds__(256) void k_lora_reduce(const LoraGradArgs pa, cons
   const bool is_a = blockIdx.x < nblk_a;
   const LoraGradArgs& a = is_a ? pa : pb;
   const uint64_t idx = static_cast<uint64_t>(is_a ? blockIdx.x : blockIdx.x - nblk_a) * 256 + threadIdx.x;
-  const int64_t I = a.I;
-  if (idx >= static_cast<uint64_t>(I) * (RP / 4)) return;
-  const int64_t i = static_cast<int64_t>(idx % static_cast<uint64_t>(I));
-  const int r = static_cast<int>(idx / static_cast<uint64_t>(I)) * 4;
-  if (r >= a.rl) return;
-  const float* p = a.part + i * RP + r;
-  const uint64_t stride = static_cast<uint64_t>(I) * RP;
+  const int64_t I = a.I, I4 = I / 4;
+  if (idx >= static_cast<uint64_t>(a.rl) * I4) return;
+  const int64_t r = static_cast<int64_t>(idx / I4);
+  const int64_t i = 4 * static_cast<int64_t>(idx % I4);
+  const float* p = a.part + r * I + i;
+  const uint64_t stride = static_cast<uint64_t>(RP) * I;
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
   for (uint32_t y0 = 0; y0 < nmc; y0 += 8) {
     f32x4 v[8];
@@ -182,12 +179,12 @@ __global__ __launch_bounds__(256) void k_lora_reduce(const LoraGradArgs pa, cons
 #pragma unroll
     for (int k = 0; k < 8; ++k) s += v[k];
   }
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    if (r + k >= a.rl) break;
-    const int64_t o = static_cast<int64_t>(r + k) * I + i;
-    if (a.out_f32) static_cast<float*>(a.out)[o] = s[k];
-    else static_cast<uint16_t*>(a.out)[o] = f32_to_bf16_rne(s[k]);
+  const int64_t o = r * I + i;
+  if (a.out_f32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = s;
+  } else {
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) =
+        u32x2{cvt_pk_bf16(s[0], s[1]), cvt_pk_bf16(s[2], s[3])};
   }
 }
 
@@ -205,9 +202,9 @@ hipError_t launch_lora_grads(const LoraGradArgs& dA, const LoraGradArgs& dB, hip
   const uint32_t nmc = static_cast<uint32_t>((dA.M + MC - 1) / MC);
   dim3 grid(nib_a + nib_b, nmc);
   const int rg = (dA.rl + 15) / 16;
-  // reduction: I * RP/4 threads per problem
-  const uint32_t nblk_a = static_cast<uint32_t>((dA.I * rg * 4 + 255) / 256);
-  const uint32_t nblk_b = static_cast<uint32_t>((dB.I * rg * 4 + 255) / 256);
+  // reduction: rl * I / 4 threads per problem
+  const uint32_t nblk_a = static_cast<uint32_t>((dA.rl * (dA.I / 4) + 255) / 256);
+  const uint32_t nblk_b = static_cast<uint32_t>((dB.rl * (dB.I / 4) + 255) / 256);
 #define FT_LA(RG, A, B) hipLaunchKernelGGL((k_lora_grads<RG, A, B>), grid, dim3(256), 0, st, dA, dB, nib_a)
 #define FT_L(RG)                                                                              \
   do {                                                                                        \
