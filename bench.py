@@ -63,8 +63,13 @@ def parse():
 
 
 def layer_work(M, K, N, rs, rl):
-    """Algorithmic FLOP and HBM bytes of each kernel of one fwd+bwd step."""
+    """Algorithmic FLOP and HBM bytes of each kernel of one fwd+bwd step.
+
+    For adapter ranks up to 32 the dB product runs inside the backward
+    quantize kernel (which reads dY anyway), so it is counted there and the
+    adapter-gradient kernel reads only X for dA."""
     R = rs + rl
+    db_fused = 0 < rl <= 32
     w = {
         "fwd_quant_down": {"flop": 2 * M * K * R,
                            "bytes": 2 * M * K + M * K // 2 + M * K // 32 + 2 * M * R + 2 * K * R,
@@ -74,16 +79,18 @@ def layer_work(M, K, N, rs, rl):
                      "bytes": M * K // 2 + M * K // 32 + N * K // 2 + N * K // 1024 + 2 * M * R
                      + 2 * R * N + 2 * M * N,
                      "bound": "mfma"},
-        "bwd_quant_down": {"flop": 2 * M * N * R,
-                           "bytes": 2 * M * N + M * N // 2 + M * N // 32 + 2 * M * R + 2 * N * R,
+        "bwd_quant_down": {"flop": 2 * M * N * R + (2 * M * N * rl if db_fused else 0),
+                           "bytes": 2 * M * N + M * N // 2 + M * N // 32 + 2 * M * R + 2 * N * R
+                           + (2 * M * rl if db_fused else 0),
                            "bound": "hbm"},
         "bwd_gemm_dgrad": {"flop": 2 * M * N * K + 2 * M * R * K,
                            "mfma_flop": 2 * M * N * K,
                            "bytes": M * N // 2 + M * N // 32 + N * K // 2 + N * K // 1024
                            + 2 * M * R + 2 * R * K + 2 * M * K,
                            "bound": "mfma"},
-        "bwd_lora_grads": {"flop": 2 * M * (K + N) * rl,
-                           "bytes": 2 * M * K + 2 * M * N + 4 * M * R + 2 * (K + N) * rl,
+        "bwd_lora_grads": {"flop": 2 * M * K * rl + (0 if db_fused else 2 * M * N * rl),
+                           "bytes": 2 * M * K + 2 * M * rl + 2 * (K + N) * rl
+                           + (0 if db_fused else 2 * M * N + 2 * M * rl),
                            "bound": "hbm"},
     }
     return w

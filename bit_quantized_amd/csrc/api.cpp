@@ -161,9 +161,16 @@ FwdLayout fwd_layout(const ft_linear* L) {
   o.xq_scales = off; off += align_up(static_cast<size_t>(L->M) * (L->K / 32));
   o.u_pad = off; off += align_up(static_cast<size_t>(L->M) * rp * 2);     // U, zero-padded ranks
   o.v_pad = off; off += align_up(static_cast<size_t>(L->N) * rp * 2);     // [L2^T | B^T], padded
-  o.part = off; off += align_up(ft::quant_down_part_bytes(L->M, L->K, R));
+  o.part = off; off += align_up(ft::quant_down_part_bytes(L->M, L->K, R, 0));
   o.total = off;
   return o;
+}
+
+// dB's partial sums come out of the backward quantize kernel (which reads
+// dY anyway) for adapter ranks up to 32; above that the adapter-gradient
+// kernel reads dY again.
+bool db_fused_in_quant(const ft_linear* L) {
+  return L->r_lora > 0 && ft::quant_down_db_chunks(L->M, L->N, L->r_lora) > 0;
 }
 
 struct BwdLayout {
@@ -180,9 +187,12 @@ BwdLayout bwd_layout(const ft_linear* L) {
   o.P = off; off += align_up(static_cast<size_t>(L->M) * R * 2);
   o.p_pad = off; off += align_up(static_cast<size_t>(L->M) * rp * 2);     // P, zero-padded ranks
   o.d_pad = off; off += align_up(static_cast<size_t>(L->K) * rp * 2);     // [L1 | A], padded
-  o.part = off; off += align_up(ft::quant_down_part_bytes(L->M, L->N, R));
+  const bool db_fused = db_fused_in_quant(L);
+  o.part = off; off += align_up(ft::quant_down_part_bytes(L->M, L->N, R, db_fused ? rl : 0));
   o.dA_part = off; off += align_up(rl ? ft::lora_grad_part_bytes(L->M, L->K, rl) : 0);
-  o.dB_part = off; off += align_up(rl ? ft::lora_grad_part_bytes(L->M, L->N, rl) : 0);
+  o.dB_part = off;
+  off += align_up(db_fused ? ft::quant_down_db_bytes(L->M, L->N, rl)
+                           : (rl ? ft::lora_grad_part_bytes(L->M, L->N, rl) : 0));
   o.total = off;
   return o;
 }
@@ -286,7 +296,8 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
     const int act = L->act_in == FT_ACT_GELU_TANH ? 1 : 0;
     if (R > 0)
       e = ft::launch_quant_down(X, nullptr, act, L->M, L->K, L->K, qc, qs, rows_Dt(L), U_save, u_pad,
-                                rows_V(L), L->N, v_pad, reinterpret_cast<float*>(ws + lay.part), st);
+                                rows_V(L), L->N, v_pad, reinterpret_cast<float*>(ws + lay.part),
+                                nullptr, st);
     else
       e = ft::launch_quant_row32(X, nullptr, act, L->M, L->K, L->K, qc, qs, st);
     tm.done(e);
@@ -331,6 +342,8 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
   uint16_t* p_pad = reinterpret_cast<uint16_t*>(ws + lay.p_pad);
   uint16_t* d_pad = reinterpret_cast<uint16_t*>(ws + lay.d_pad);
   hipError_t e;
+  const bool db_fused = db_fused_in_quant(L);
+  ft::DbFuse db{U_save, R, L->r_stab, rl, reinterpret_cast<float*>(ws + lay.dB_part)};
   {
     Timed tm("bwd_quant_down", st);
     // act_out: dY is the gradient of gelu(Y) and H the saved Y; the incoming
@@ -340,7 +353,8 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
     if (R > 0)
       e = ft::launch_quant_down(dY, h2, act, L->M, L->N, L->N, qc, qs, rows_V(L), P, p_pad,
                                 rows_Dt(L), dX ? L->K : 0, d_pad,
-                                reinterpret_cast<float*>(ws + lay.part), st);
+                                reinterpret_cast<float*>(ws + lay.part), db_fused ? &db : nullptr,
+                                st);
     else
       e = ft::launch_quant_row32(dY, h2, act, L->M, L->N, L->N, qc, qs, st);
     tm.done(e);
@@ -368,8 +382,9 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
     b.act = L->act_out == FT_ACT_GELU_TANH ? 2 : 0;
     b.out = dB;
     b.part = reinterpret_cast<float*>(ws + lay.dB_part);
+    b.nchunk = db_fused ? ft::quant_down_db_chunks(L->M, L->N, rl) : 0;
     Timed tm("bwd_lora_grads", st);
-    if (tm.done(ft::launch_lora_grads(a, b, st)) != hipSuccess) return FT_EDEVICE;
+    if (tm.done(ft::launch_lora_grads(a, b, db_fused, st)) != hipSuccess) return FT_EDEVICE;
   }
   return FT_OK;
 }

@@ -124,6 +124,14 @@ __device__ __forceinline__ f32x4 mfma_bf16_16x16x32(u32x4 a, u32x4 b, f32x4 c) {
                                                  __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
 }
 
+// 16x16x16 bf16 -> fp32: lane l supplies 4 reduction values of row (A) or
+// column (B) l % 16, reduction indices 4 (l / 16) .. +3.
+__device__ __forceinline__ f32x4 mfma_bf16_16x16x16(i32x2 a, u32x2 b, f32x4 c) {
+  typedef short s16x4_t __attribute__((ext_vector_type(4)));
+  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(__builtin_bit_cast(s16x4_t, a),
+                                                   __builtin_bit_cast(s16x4_t, b), c, 0, 0, 0);
+}
+
 // 64-bit LDS read with a 16x16 transpose of 4-bit elements across each
 // group of 16 lanes: lane q of a group receives nibble q of the 8 bytes
 // addressed by each of the 16 lanes, in lane order.  `p` must point into

@@ -43,13 +43,26 @@ inline int rank_pad(int R) { return R > 0 ? 64 : 0; }
 // column range into `part`, then their ordered sum).  Also writes out_pad
 // [rows, rank_pad(R)], the same values zero-padded, and the transposed copy
 // cp_dst [cp_rows, rank_pad(R)] of the rank-major operand cp.  `part` needs
-// quant_down_part_bytes(rows, cols, R) bytes.
+// quant_down_part_bytes(rows, cols, R, db ? db->rl : 0) bytes.
+// db (backward, optional): also the adapter-gradient partials
+//   db->part[j][r][c] = sum over the rows workgroup j of a split visits of
+//                       u[row][r0 + r] * act(in)[row][c],   r < rl <= 32,
+// j < quant_down_db_chunks(rows, cols, rl); the rows >= rl of a 16-rank
+// group are zero.  quant_down_db_bytes(rows, cols, rl) bytes.
+struct DbFuse {
+  const uint16_t* u;              // bf16 [rows, ld_u]
+  int64_t ld_u;
+  int r0, rl;
+  float* part;
+};
 hipError_t launch_quant_down(const uint16_t* in, const uint16_t* in2, int act, int64_t rows,
                              int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
                              const RankRows& pr, uint16_t* out_lr, uint16_t* out_pad,
                              const RankRows& cp, int64_t cp_rows, uint16_t* cp_dst, float* part,
-                             hipStream_t st);
-size_t quant_down_part_bytes(int64_t rows, int64_t cols, int R);
+                             const DbFuse* db, hipStream_t st);
+size_t quant_down_part_bytes(int64_t rows, int64_t cols, int R, int rl_db);
+int quant_down_db_chunks(int64_t rows, int64_t cols, int rl);   // 0: dB is not fused for this rl
+size_t quant_down_db_bytes(int64_t rows, int64_t cols, int rl);
 
 // gemm.hip: out[m][j] = sum_red deq(a)[m][red] deq(b)[j][red] + sum_r lm[m][r] lo[j][r]
 // forward: a = Qrow(X) [M, K], b = Qtile(W) [N, K], lm = U, lo = [L2^T | B^T]
@@ -80,10 +93,14 @@ struct LoraGradArgs {
   void* out;                      // [rl, I]
   int out_f32;                    // 0 bf16, 1 fp32
   float* part;                    // workspace: fp32 partials per 512-token chunk
+  int nchunk;                     // partials to add (set by launch_lora_grads unless precomputed)
 };
 // dA and dB of one backward: one launch computes the partials of both
-// problems, a second adds them in chunk order.
-hipError_t launch_lora_grads(const LoraGradArgs& dA, const LoraGradArgs& dB, hipStream_t st);
+// problems, a second adds them in chunk order.  dB_done: dB's partials
+// [dB.nchunk][16 ceil(rl/16)][I] are already in dB.part (made by the
+// backward quantize kernel); only the reduction runs for dB.
+hipError_t launch_lora_grads(const LoraGradArgs& dA, const LoraGradArgs& dB, bool dB_done,
+                             hipStream_t st);
 size_t lora_grad_part_bytes(int64_t M, int64_t I, int rl);
 
 // act.hip: out = bf16(gelu(h)) (act 1) or bf16(g * gelu'(h)) (act 2), n elements.

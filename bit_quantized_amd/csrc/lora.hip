@@ -153,12 +153,12 @@ __global__ __launch_bounds__(256) void k_lora_grads(const LoraGradArgs pa, const
   else lora_block<RG, ACTB>(pb, blockIdx.x - nib_a, bigL, smL);
 }
 
-// out[r][i .. i+3] = sum over chunks y (in order) of part[y][r][i .. i+3];
+// out[r][i .. i+3] = sum over chunks y < nchunk (in order) of part[y][r][i .. i+3];
 // consecutive threads take consecutive column quads of a rank row.  Blocks
 // [0, nblk_a) serve dA.
 template <int RG>
 __global__ __launch_bounds__(256) void k_lora_reduce(const LoraGradArgs pa, const LoraGradArgs pb,
-                                                     uint32_t nblk_a, uint32_t nmc) {
+                                                     uint32_t nblk_a) {
   constexpr int RP = RG * 16;
   const bool is_a = blockIdx.x < nblk_a;
   const LoraGradArgs& a = is_a ? pa : pb;
@@ -169,6 +169,7 @@ __global__ __launch_bounds__(256) void k_lora_reduce(const LoraGradArgs pa, cons
   const int64_t i = 4 * static_cast<int64_t>(idx % I4);
   const float* p = a.part + r * I + i;
   const uint64_t stride = static_cast<uint64_t>(RP) * I;
+  const uint32_t nmc = static_cast<uint32_t>(a.nchunk);
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
   for (uint32_t y0 = 0; y0 < nmc; y0 += 8) {
     f32x4 v[8];
@@ -196,10 +197,14 @@ size_t lora_grad_part_bytes(int64_t M, int64_t I, int rl) {
   return static_cast<size_t>(nmc) * I * RP * sizeof(float);
 }
 
-hipError_t launch_lora_grads(const LoraGradArgs& dA, const LoraGradArgs& dB, hipStream_t st) {
+hipError_t launch_lora_grads(const LoraGradArgs& dA_in, const LoraGradArgs& dB_in, bool dB_done,
+                             hipStream_t st) {
+  LoraGradArgs dA = dA_in, dB = dB_in;
   const uint32_t nib_a = static_cast<uint32_t>((dA.I + IB - 1) / IB);
-  const uint32_t nib_b = static_cast<uint32_t>((dB.I + IB - 1) / IB);
+  const uint32_t nib_b = dB_done ? 0u : static_cast<uint32_t>((dB.I + IB - 1) / IB);
   const uint32_t nmc = static_cast<uint32_t>((dA.M + MC - 1) / MC);
+  dA.nchunk = static_cast<int>(nmc);
+  if (!dB_done) dB.nchunk = static_cast<int>(nmc);
   dim3 grid(nib_a + nib_b, nmc);
   const int rg = (dA.rl + 15) / 16;
   // reduction: rl * I / 4 threads per problem
@@ -212,7 +217,7 @@ hipError_t launch_lora_grads(const LoraGradArgs& dA, const LoraGradArgs& dB, hip
     else { if (dB.act == 2) FT_LA(RG, 0, 2); else FT_LA(RG, 0, 0); }                          \
     if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;                        \
     hipLaunchKernelGGL(k_lora_reduce<RG>, dim3(nblk_a + nblk_b), dim3(256), 0, st, dA, dB,    \
-                       nblk_a, nmc);                                                          \
+                       nblk_a);                                                               \
   } while (0)
   switch (rg) {
     case 1: FT_L(1); break;

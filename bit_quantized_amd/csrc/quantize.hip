@@ -314,9 +314,15 @@ struct QDArgs {
   int R;
   uint32_t wg_per_split;
   float* part;          // [splits][rows/64][4 waves][NRG][64 lanes][4]
+  // adapter gradient dB of the backward (DBR > 0): sum over rows of
+  // u[row][u_r0 + r] * in[row][col], r < u_rl, per workgroup of a split
+  const uint16_t* u;
+  int64_t ld_u;
+  int u_r0, u_rl;
+  float* dbpart;        // [wg_per_split][16 DBR][cols], rank-major
 };
 
-template <int NRG, int NS, int ACT>
+template <int NRG, int NS, int ACT, int DBR>
 __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
   constexpr int RP = NRG * 16;
   constexpr int KC = 128 * NS;
@@ -324,8 +330,13 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
   constexpr int LPR = KC / 8;
   constexpr int RPI = 64 / LPR;
   constexpr int NI = 16 / RPI;
-  __shared__ __attribute__((aligned(16))) uint16_t pt[RP * PT];
-  __shared__ __attribute__((aligned(16))) uint16_t xt[4][16 * PT];
+  constexpr int NT = KC / 16;                 // 16-column tiles of a split (dB)
+  constexpr int LDS_PT = RP * PT * 2, LDS_XT = 4 * 16 * PT * 2;
+  constexpr int LDS_DB = 4 * 16 * (KC + 4) * 4;   // one rank group of the 4 waves' dB partials
+  constexpr int LDS_BYTES = LDS_PT + LDS_XT > LDS_DB ? LDS_PT + LDS_XT : LDS_DB;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
+  uint16_t* pt = reinterpret_cast<uint16_t*>(lds);
+  uint16_t (*xt)[16 * PT] = reinterpret_cast<uint16_t (*)[16 * PT]>(lds + LDS_PT);
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
   const uint32_t rows = a.rows, cols = a.cols;
   const uint32_t nrb = (rows + 63) / 64;
@@ -342,6 +353,11 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
   // rows * ld * 2 < 2^31); columns past the end are masked here.
   const uint32_t lane_off = col_ok ? (static_cast<uint32_t>(16 * wave + lrow) * ld2 + col * 2) : BUF_OOB;
   const auto rin2 = make_rsrc(a.in2, ACT == 2 ? static_cast<uint64_t>(rows) * a.ld * 2 : 0);
+  // dB: lane (group g, q) holds u[row][u_r0 + 16 c + q] of rows 4g .. 4g+3 of
+  // its wave's 16 rows (the A operand of a 16x16x16 MFMA)
+  const int g = lane >> 4, lr = lane & 15;
+  const auto ru = make_rsrc(a.u, DBR ? static_cast<uint64_t>(rows) * a.ld_u * 2 : 0);
+  uint32_t ua[DBR > 0 ? DBR : 1][4];
   auto load = [&](u32x4* v, u32x4* h, uint32_t bx) {
     const uint32_t base = (bx < nrb && col_ok) ? bx * 64 * ld2 + lane_off : BUF_OOB;
 #pragma unroll
@@ -349,6 +365,17 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
       const uint32_t off = base == BUF_OOB ? BUF_OOB : base + i * RPI * ld2;
       v[i] = buf_load128(rin, off);                  // re-read later in the step: cached
       if constexpr (ACT == 2) h[i] = buf_load128(rin2, off);
+    }
+    if constexpr (DBR > 0) {
+#pragma unroll
+      for (int c = 0; c < DBR; ++c)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t row = bx * 64 + 16 * wave + 4 * g + e;
+          const int r = 16 * c + lr;
+          ua[c][e] = buf_load16(ru, (bx < nrb && row < rows && r < a.u_rl)
+                                        ? static_cast<uint32_t>((row * a.ld_u + a.u_r0 + r) * 2) : BUF_OOB);
+        }
     }
   };
   u32x4 va[NI], ha[NI];
@@ -380,8 +407,15 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
   }
   __syncthreads();
   uint16_t* xw = xt[wave];
-  const int g = lane >> 4, lr = lane & 15;
   const uint32_t cpr = cols >> 1, spr = cols >> 5;
+  f32x4 dacc[DBR > 0 ? DBR : 1][DBR > 0 ? NT : 1];
+  if constexpr (DBR > 0) {
+#pragma unroll
+    for (int c = 0; c < DBR; ++c)
+#pragma unroll
+      for (int n = 0; n < NT; ++n) dacc[c][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  i32x2 au[DBR > 0 ? DBR : 1];
   auto quant = [&](const u32x4* vin, const u32x4* hin, uint32_t b) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -416,16 +450,62 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
     float* slab = a.part + ((static_cast<uint64_t>(y) * nrb + b) * 4 + wave) * (NRG * 256);
 #pragma unroll
     for (int c = 0; c < NRG; ++c) *reinterpret_cast<f32x4*>(slab + (c * 64 + lane) * 4) = acc[c];
+    if constexpr (DBR > 0) {
+      // dB += u^T x over this wave's 16 rows: B operand = rows 4g .. 4g+3 of
+      // column 16 n + q, read transposed from the row-major slab
+#pragma unroll
+      for (int n = 0; n < NT; ++n) {
+        const u32x2 bx2 = lds_read_tr16(&xw[(4 * g + (lr >> 2)) * PT + 16 * n + 4 * (lr & 3)]);
+#pragma unroll
+        for (int c = 0; c < DBR; ++c) dacc[c][n] = mfma_bf16_16x16x16(au[c], bx2, dacc[c][n]);
+        if ((n & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+      }
+    }
   };
   // the next block's loads go out as soon as this block's values are in LDS,
   // and overlap the MFMA phase
   for (; bx < nrb; bx += G) {
     quant(va, ha, bx);
+    if constexpr (DBR > 0) {
+      // this block's adapter rows, packed before the prefetch replaces them
+#pragma unroll
+      for (int c = 0; c < DBR; ++c)
+        au[c] = i32x2{static_cast<int>(ua[c][0] | (ua[c][1] << 16)), static_cast<int>(ua[c][2] | (ua[c][3] << 16))};
+    }
     load(va, ha, bx + G);
     mma(bx);
   }
+  if constexpr (DBR > 0) {
+    // per rank group: the 4 waves' dB partials go to LDS (one padded region
+    // each), then all threads add them in wave order and write the
+    // workgroup's partial dbpart[j][r][col] with 16-byte stores
+    constexpr int DP = KC + 4;                 // row pitch: the 4 lane groups hit distinct banks
+    constexpr int Q = KC / 4;                  // float4 items per row
+    float* red = reinterpret_cast<float*>(lds);
+    float* mine = red + wave * (16 * DP);
+    const uint32_t j = blockIdx.x % G;
+    float* dst = a.dbpart + static_cast<uint64_t>(j) * (DBR * 16) * cols;
+#pragma unroll
+    for (int c = 0; c < DBR; ++c) {
+      __syncthreads();
+#pragma unroll
+      for (int n = 0; n < NT; ++n)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) mine[(4 * g + e) * DP + 16 * n + lr] = dacc[c][n][e];
+      __syncthreads();
+#pragma unroll
+      for (int it = 0; it < 16 * Q / 256; ++it) {
+        const int idx = t + 256 * it;
+        const int r = idx / Q, cc = (idx % Q) * 4;
+        f32x4 v = *reinterpret_cast<const f32x4*>(&red[r * DP + cc]);
+#pragma unroll
+        for (int w = 1; w < 4; ++w) v += *reinterpret_cast<const f32x4*>(&red[w * (16 * DP) + r * DP + cc]);
+        if (cbeg + cc < cols)
+          *reinterpret_cast<f32x4*>(&dst[static_cast<uint64_t>(16 * c + r) * cols + cbeg + cc]) = v;
+      }
+    }
+  }
 }
-
 
 struct RRArgs {
   const float* part;
@@ -563,46 +643,96 @@ hipError_t launch_quant_row32_t(const uint16_t* in, int64_t rows, int64_t cols, 
   return hipGetLastError();
 }
 
-// Columns per workgroup of the fused kernel: the largest of 512, 256, 128
-// that still gives at least one workgroup per CU.
-static int quant_down_kc(int64_t rows, int64_t cols) {
+// Plan of the fused kernel: columns per split, splits and workgroups per
+// split.  KC: the largest of 512, 256, 128 that still gives one row block and
+// split per CU of a 256-CU part; with the dB partial (DBR rank groups) at
+// most 512 / DBR, so that its accumulators fit.  Workgroups per split: as
+// many as fit on such a part at once (LDS allows one per CU at KC = 512, two
+// at 256, four at 128), at most one per row block.  Fixed by the shapes only,
+// so the workspace size does not depend on the device.
+struct QDPlan {
+  int kc;
+  uint32_t nrb, splits, G;
+};
+static QDPlan quant_down_plan(int64_t rows, int64_t cols, int dbr) {
+  QDPlan p;
   const int64_t rb = (rows + 63) / 64;
+  p.kc = 128;
   for (int kc = 512; kc > 128; kc /= 2)
-    if (rb * ((cols + kc - 1) / kc) >= 256) return kc;
-  return 128;
+    if (rb * ((cols + kc - 1) / kc) >= 256) { p.kc = kc; break; }
+  if (dbr > 0 && p.kc > 512 / dbr) p.kc = 512 / dbr;
+  p.nrb = static_cast<uint32_t>(rb);
+  p.splits = static_cast<uint32_t>((cols + p.kc - 1) / p.kc);
+  uint32_t G = 256u * static_cast<uint32_t>(512 / p.kc) / p.splits;
+  p.G = G < 1 ? 1 : (G > p.nrb ? p.nrb : G);
+  return p;
 }
 
-size_t quant_down_part_bytes(int64_t rows, int64_t cols, int R) {
+// Adapter rank groups whose dB is fused into the kernel (0: not fused).
+static int quant_down_dbr(int rl) { return rl > 0 && rl <= 32 ? (rl + 15) / 16 : 0; }
+
+size_t quant_down_part_bytes(int64_t rows, int64_t cols, int R, int rl_db) {
   if (R == 0) return 0;
-  const int64_t splits = (cols + quant_down_kc(rows, cols) - 1) / quant_down_kc(rows, cols);
+  const QDPlan p = quant_down_plan(rows, cols, quant_down_dbr(rl_db));
   const int64_t nrg = (R + 15) / 16;
-  return static_cast<size_t>(splits) * ((rows + 63) / 64) * 4 * nrg * 256 * sizeof(float);
+  return static_cast<size_t>(p.splits) * p.nrb * 4 * nrg * 256 * sizeof(float);
+}
+
+int quant_down_db_chunks(int64_t rows, int64_t cols, int rl) {
+  const int dbr = quant_down_dbr(rl);
+  return dbr ? static_cast<int>(quant_down_plan(rows, cols, dbr).G) : 0;
+}
+
+size_t quant_down_db_bytes(int64_t rows, int64_t cols, int rl) {
+  const int dbr = quant_down_dbr(rl);
+  if (!dbr) return 0;
+  const QDPlan p = quant_down_plan(rows, cols, dbr);
+  return static_cast<size_t>(p.G) * dbr * 16 * cols * sizeof(float);
+}
+
+// Forward: act 0 or 1, no dB.  Backward: act 0 or 2, dB fused (1 or 2 rank
+// groups; 2 only at KC <= 256 with R > 16, as the plan guarantees) or not.
+template <int NRG, int NS>
+static void launch_qd(const QDArgs& a, dim3 grid, int act, int dbr, hipStream_t st) {
+#define FT_QDA(ACT, D) hipLaunchKernelGGL((k_quant_down<NRG, NS, ACT, D>), grid, dim3(256), 0, st, a)
+  if (act == 1) {
+    FT_QDA(1, 0);
+  } else if (dbr == 0) {
+    if (act == 2) FT_QDA(2, 0); else FT_QDA(0, 0);
+  } else if (dbr == 1) {
+    if (act == 2) FT_QDA(2, 1); else FT_QDA(0, 1);
+  } else {
+    if constexpr (NS <= 2 && NRG >= 2) {
+      if (act == 2) FT_QDA(2, 2); else FT_QDA(0, 2);
+    }
+  }
+#undef FT_QDA
 }
 
 hipError_t launch_quant_down(const uint16_t* in, const uint16_t* in2, int act, int64_t rows,
                              int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
                              const RankRows& pr, uint16_t* out_lr, uint16_t* out_pad,
                              const RankRows& cp, int64_t cp_rows, uint16_t* cp_dst, float* part,
-                             hipStream_t st) {
+                             const DbFuse* db, hipStream_t st) {
   const int R = pr.r0 + pr.r1;
-  const int kc = quant_down_kc(rows, cols);
-  const uint32_t nrb = static_cast<uint32_t>((rows + 63) / 64);
-  const uint32_t splits = static_cast<uint32_t>((cols + kc - 1) / kc);
-  // workgroups per split: as many as fit on the chip at once (LDS allows one
-  // per CU at KC = 512, two at 256, four at 128), at most one per row block
-  const int cus = cu_count();
-  if (cus <= 0) return hipErrorInvalidDevice;
-  const uint32_t resident = static_cast<uint32_t>(cus) * static_cast<uint32_t>(512 / kc);
-  uint32_t G = resident / splits;
-  G = G < 1 ? 1 : (G > nrb ? nrb : G);
-  QDArgs a{in, in2, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols), ld, codes, scales, pr, R, G, part};
+  const int dbr = db ? quant_down_dbr(db->rl) : 0;
+  if (db && !dbr) return hipErrorInvalidValue;
+  const QDPlan pl = quant_down_plan(rows, cols, dbr);
+  const int kc = pl.kc;
+  const uint32_t nrb = pl.nrb, splits = pl.splits, G = pl.G;
+  QDArgs a{in, in2, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols), ld, codes, scales,
+           pr, R, G, part,
+           db ? db->u : nullptr, db ? db->ld_u : 0, db ? db->r0 : 0, db ? db->rl : 0,
+           db ? db->part : nullptr};
   const dim3 grid(splits * G);
-#define FT_QDA(NRG, NS, ACT) hipLaunchKernelGGL((k_quant_down<NRG, NS, ACT>), grid, dim3(256), 0, st, a)
-#define FT_QD(NRG, NS) \
-  do { if (act == 1) FT_QDA(NRG, NS, 1); else if (act == 2) FT_QDA(NRG, NS, 2); else FT_QDA(NRG, NS, 0); } while (0)
-#define FT_QD_NS(NRG) \
-  do { if (kc == 512) FT_QD(NRG, 4); else if (kc == 256) FT_QD(NRG, 2); else FT_QD(NRG, 1); } while (0)
   const int nrg = (R + 15) / 16;
+  if (dbr > nrg) return hipErrorInvalidValue;
+#define FT_QD_NS(NRG)                                                                         \
+  do {                                                                                        \
+    if (kc == 512) launch_qd<NRG, 4>(a, grid, act, dbr, st);                                  \
+    else if (kc == 256) launch_qd<NRG, 2>(a, grid, act, dbr, st);                             \
+    else launch_qd<NRG, 1>(a, grid, act, dbr, st);                                            \
+  } while (0)
   switch (nrg) {
     case 1: FT_QD_NS(1); break;
     case 2: FT_QD_NS(2); break;
@@ -610,8 +740,6 @@ hipError_t launch_quant_down(const uint16_t* in, const uint16_t* in2, int act, i
     default: FT_QD_NS(4); break;
   }
 #undef FT_QD_NS
-#undef FT_QD
-#undef FT_QDA
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   RRArgs b{part, static_cast<uint32_t>(rows), splits, R, rank_pad(R), out_lr, out_pad, cp, cp_rows, cp_dst};
   const uint64_t ncopy = (static_cast<uint64_t>(cp_rows) * (rank_pad(R) / 8) + 255) / 256;
