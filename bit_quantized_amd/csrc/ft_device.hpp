@@ -258,6 +258,19 @@ __device__ __forceinline__ uint32_t buf_load16(__amdgpu_buffer_rsrc_t r, uint32_
   return __builtin_amdgcn_raw_buffer_load_b16(r, (int)off, 0, 0);
 }
 constexpr uint32_t BUF_OOB = 0x80000000u;   // a buffer offset past every tensor
+// Raw buffer stores: offsets at or past the buffer size are dropped.  They
+// let edge masking be an offset instead of a branch, so every store is issued
+// unconditionally and the compiler can count outstanding memory operations
+// exactly (a store under a branch makes later waits conservative).
+__device__ __forceinline__ void buf_store32(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b32(v, r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store8(__amdgpu_buffer_rsrc_t r, uint32_t off, uint32_t v) {
+  __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(v), r, (int)off, 0, 0);
+}
+__device__ __forceinline__ void buf_store128(__amdgpu_buffer_rsrc_t r, uint32_t off, u32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(v, r, (int)off, 0, 0);
+}
 
 
 }  // namespace ft

@@ -284,11 +284,11 @@ __global__ __launch_bounds__(256) void k_quant_row32_t(const uint16_t* __restric
 // `wg_per_split` workgroups share a split and walk its 64-row blocks
 // (workgroup j takes blocks j, j + G, ...).  A workgroup stages the
 // projection slice of its split [RP ranks x KC columns] in LDS once.  Each
-// wave then streams its own 16 rows of every block it visits, with no
-// barrier between blocks:
+// wave then streams its own 16 rows of every block it visits:
 //   - loads: one instruction reads KC/8 lanes x 16 bytes of one row (1 KB
-//     contiguous for KC = 512); the next block's loads are issued as soon as
-//     the current block is in LDS, so they overlap its MFMA phase;
+//     contiguous for KC = 512); at KC = 512 into one of two register sets,
+//     the loads of block b + 2G issued as soon as block b is quantized, so a
+//     block is always in flight while the wave quantizes and projects;
 //   - quantize in the load layout: 4 consecutive lanes hold one 32-element
 //     block, amax by two quad DPP steps; codes go out as 4 bytes per lane
 //     (a row's codes contiguous), scales from every 4th lane;
@@ -296,7 +296,13 @@ __global__ __launch_bounds__(256) void k_quant_row32_t(const uint16_t* __restric
 //     16x16x32 MFMA fragments (row = lane % 16, 8 columns of group
 //     lane / 16) against the projection in LDS: fp32 sums over the split;
 //   - the 16 x RP result goes to a workspace slab, laid out as the
-//     accumulators are held (16 contiguous bytes per lane).
+//     accumulators are held (16 contiguous bytes per lane);
+//   - backward with the adapter gradient fused (DBR rank groups): after a
+//     barrier every wave reads all four slabs back transposed
+//     (ds_read_b64_tr_b16) for its quarter of the columns and accumulates
+//     dB[r][col] += sum_row u[row][r] x[row][col] with 16x16x16 MFMAs; a
+//     second barrier frees the slabs.  At the end each workgroup writes its
+//     partial, which the adapter-gradient reduce sums in workgroup order.
 //
 // k_rank_reduce (the next kernel on the stream, so every slab is visible):
 // sums the slabs in split order (deterministic), rounds once, and writes
@@ -332,8 +338,7 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
   constexpr int NI = 16 / RPI;
   constexpr int NT = KC / 16;                 // 16-column tiles of a split (dB)
   constexpr int LDS_PT = RP * PT * 2, LDS_XT = 4 * 16 * PT * 2;
-  constexpr int LDS_DB = 4 * 16 * (KC + 4) * 4;   // one rank group of the 4 waves' dB partials
-  constexpr int LDS_BYTES = LDS_PT + LDS_XT > LDS_DB ? LDS_PT + LDS_XT : LDS_DB;
+  constexpr int LDS_BYTES = LDS_PT + LDS_XT;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   uint16_t* pt = reinterpret_cast<uint16_t*>(lds);
   uint16_t (*xt)[16 * PT] = reinterpret_cast<uint16_t (*)[16 * PT]>(lds + LDS_PT);
@@ -353,34 +358,47 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
   // rows * ld * 2 < 2^31); columns past the end are masked here.
   const uint32_t lane_off = col_ok ? (static_cast<uint32_t>(16 * wave + lrow) * ld2 + col * 2) : BUF_OOB;
   const auto rin2 = make_rsrc(a.in2, ACT == 2 ? static_cast<uint64_t>(rows) * a.ld * 2 : 0);
-  // dB: lane (group g, q) holds u[row][u_r0 + 16 c + q] of rows 4g .. 4g+3 of
-  // its wave's 16 rows (the A operand of a 16x16x16 MFMA)
+  // dB: every wave takes all 64 rows of the block and a quarter of its
+  // columns.  For row group h (rows 16h .. 16h+15) lane (group g, q) holds
+  // u[row][u_r0 + 16 c + q] of rows 16h + 4g .. 16h + 4g + 3 (the A operand
+  // of a 16x16x16 MFMA).
   const int g = lane >> 4, lr = lane & 15;
-  const auto ru = make_rsrc(a.u, DBR ? static_cast<uint64_t>(rows) * a.ld_u * 2 : 0);
-  uint32_t ua[DBR > 0 ? DBR : 1][4];
+  // Two register sets at KC = 512 (one workgroup per CU): the loads of block
+  // b + 2G go out right after block b is quantized, so one block is always
+  // in flight while the wave works.  ACT 2 (two inputs) keeps one set (two
+  // would not fit in 256 VGPRs); so do narrower splits, whose several
+  // workgroups per CU hide each other's loads.
+  constexpr int NB = (ACT == 2 || NS < 4) ? 1 : 2;
+  constexpr int UA = DBR > 0 ? 4 * DBR : 1;   // (row group, rank group) pairs
   auto load = [&](u32x4* v, u32x4* h, uint32_t bx) {
-    const uint32_t base = (bx < nrb && col_ok) ? bx * 64 * ld2 + lane_off : BUF_OOB;
+    // past the end stays past the end: the host keeps (rows + 64) * ld * 2
+    // below 2^31, so BUF_OOB plus any row offset here does not wrap
+    const uint32_t base = bx < nrb ? bx * 64 * ld2 + lane_off : BUF_OOB;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const uint32_t off = base == BUF_OOB ? BUF_OOB : base + i * RPI * ld2;
+      const uint32_t off = base + i * RPI * ld2;
       v[i] = buf_load128(rin, off);                  // re-read later in the step: cached
       if constexpr (ACT == 2) h[i] = buf_load128(rin2, off);
     }
-    if constexpr (DBR > 0) {
-#pragma unroll
-      for (int c = 0; c < DBR; ++c)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t row = bx * 64 + 16 * wave + 4 * g + e;
-          const int r = 16 * c + lr;
-          ua[c][e] = buf_load16(ru, (bx < nrb && row < rows && r < a.u_rl)
-                                        ? static_cast<uint32_t>((row * a.ld_u + a.u_r0 + r) * 2) : BUF_OOB);
-        }
-    }
   };
-  u32x4 va[NI], ha[NI];
+  // The adapter operand of block bx, loaded when the block starts (its
+  // quantize and projection phases cover the latency) and held only within
+  // the block: plain 16-bit loads, zero-extended by the load itself.  Indices
+  // are clamped into the tensor: a row past the end meets x = 0, and ranks
+  // past u_rl only feed partial rows the reduce never reads.
+  auto load_u = [&](uint32_t (*uu)[4], uint32_t bx) {
+#pragma unroll
+    for (int hc = 0; hc < 4 * DBR; ++hc)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t row = min(bx * 64 + 16 * (hc >> (DBR - 1)) + 4 * g + e, rows - 1);
+        const int r = min(16 * (hc & (DBR - 1)) + lr, a.u_rl - 1);
+        uu[hc][e] = a.u[row * static_cast<uint32_t>(a.ld_u) + a.u_r0 + r];
+      }
+  };
+  u32x4 va[NB][NI], ha[NI];
   uint32_t bx = blockIdx.x % G;
-  load(va, ha, bx);
+  load(va[0], ha, bx);
   {
     const RankRows& p = a.pr;
     const int R = a.R;
@@ -399,6 +417,7 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
       const uint32_t o1 = (ok && r >= p.r0 && r < R) ? static_cast<uint32_t>(((r - p.r0) * p.ld + pc) * 2) : BUF_OOB;
       w[e] = buf_load128(r0s, o0) | buf_load128(r1s, o1);
     }
+    if constexpr (NB == 2) load(va[1], ha, bx + G);
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const int c = t + 256 * e;
@@ -408,14 +427,17 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
   __syncthreads();
   uint16_t* xw = xt[wave];
   const uint32_t cpr = cols >> 1, spr = cols >> 5;
-  f32x4 dacc[DBR > 0 ? DBR : 1][DBR > 0 ? NT : 1];
+  const auto rcodes = make_rsrc(a.codes, static_cast<uint64_t>(rows) * cpr);
+  const auto rscales = make_rsrc(a.scales, static_cast<uint64_t>(rows) * spr);
+  const auto rpart = make_rsrc(a.part, static_cast<uint64_t>(gridDim.x / G) * nrb * 4 * NRG * 256 * 4);
+  constexpr int NTW = NT / 4;                 // dB column tiles per wave
+  f32x4 dacc[DBR > 0 ? DBR : 1][DBR > 0 ? NTW : 1];
   if constexpr (DBR > 0) {
 #pragma unroll
     for (int c = 0; c < DBR; ++c)
 #pragma unroll
-      for (int n = 0; n < NT; ++n) dacc[c][n] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int n = 0; n < NTW; ++n) dacc[c][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  i32x2 au[DBR > 0 ? DBR : 1];
   auto quant = [&](const u32x4* vin, const u32x4* hin, uint32_t b) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -428,14 +450,13 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
       am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0x4E, 0xF, 0xF, false)));
       const uint32_t sc8 = e8m0_from_amax_bits(am);
       const uint32_t o = encode8(v[0], v[1], v[2], v[3], e8m0_to_f32(sc8));
-      if (row < rows && col_ok) {
-        *reinterpret_cast<uint32_t*>(a.codes + row * cpr + (col >> 1)) = o;
-        if ((lane & 3) == 0) a.scales[row * spr + (col >> 5)] = static_cast<uint8_t>(sc8);
-      }
+      const bool ok = row < rows && col_ok;
+      buf_store32(rcodes, ok ? row * cpr + (col >> 1) : BUF_OOB, o);
+      buf_store8(rscales, ok && (lane & 3) == 0 ? row * spr + (col >> 5) : BUF_OOB, sc8);
       *reinterpret_cast<u32x4*>(&xw[(i * RPI + lrow) * PT + lcol]) = v;
     }
   };
-  auto mma = [&](uint32_t b) {
+  auto mma = [&](uint32_t b, uint32_t (*uu)[4]) {
     f32x4 acc[NRG];
 #pragma unroll
     for (int c = 0; c < NRG; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -447,63 +468,74 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
         acc[c] = mfma_bf16_16x16x32(af, lds_read_b128(&pt[(16 * c + lr) * PT + 32 * ks + 8 * g]), acc[c]);
       if ((ks & 3) == 3) __builtin_amdgcn_sched_barrier(0);
     }
-    float* slab = a.part + ((static_cast<uint64_t>(y) * nrb + b) * 4 + wave) * (NRG * 256);
+    // this wave's slab; nothing is stored for a block past the end
+    const uint32_t slab = b < nrb ? ((y * nrb + b) * 4 + wave) * (NRG * 256 * 4) + lane * 16 : BUF_OOB;
 #pragma unroll
-    for (int c = 0; c < NRG; ++c) *reinterpret_cast<f32x4*>(slab + (c * 64 + lane) * 4) = acc[c];
+    for (int c = 0; c < NRG; ++c)
+      buf_store128(rpart, slab + c * 1024, __builtin_bit_cast(u32x4, acc[c]));
     if constexpr (DBR > 0) {
-      // dB += u^T x over this wave's 16 rows: B operand = rows 4g .. 4g+3 of
-      // column 16 n + q, read transposed from the row-major slab
+      // dB += u^T x over the block's 64 rows and this wave's columns
+      // KC/4 * wave .. +KC/4: B operand = rows 4g .. 4g+3 of row group h at
+      // column 16 n + q, read transposed from wave h's row-major slab (all
+      // four slabs are complete: barrier before this phase)
+      // The empty asm marks the loaded values as used here, so the compiler
+      // neither packs them nor waits for their loads any earlier.
+      i32x2 au[UA];
 #pragma unroll
-      for (int n = 0; n < NT; ++n) {
-        const u32x2 bx2 = lds_read_tr16(&xw[(4 * g + (lr >> 2)) * PT + 16 * n + 4 * (lr & 3)]);
-#pragma unroll
-        for (int c = 0; c < DBR; ++c) dacc[c][n] = mfma_bf16_16x16x16(au[c], bx2, dacc[c][n]);
-        if ((n & 7) == 7) __builtin_amdgcn_sched_barrier(0);
+      for (int hc = 0; hc < 4 * DBR; ++hc) {
+        asm volatile("" : "+v"(uu[hc][0]), "+v"(uu[hc][1]), "+v"(uu[hc][2]), "+v"(uu[hc][3]));
+        au[hc] = i32x2{static_cast<int>(__builtin_amdgcn_perm(uu[hc][1], uu[hc][0], 0x05040100u)),
+                       static_cast<int>(__builtin_amdgcn_perm(uu[hc][3], uu[hc][2], 0x05040100u))};
       }
+      __syncthreads();
+#pragma unroll
+      for (int h = 0; h < 4; ++h) {
+#pragma unroll
+        for (int n = 0; n < NTW; ++n) {
+          const u32x2 bx2 = lds_read_tr16(&xt[h][(4 * g + (lr >> 2)) * PT + (KC / 4) * wave + 16 * n + 4 * (lr & 3)]);
+#pragma unroll
+          for (int c = 0; c < DBR; ++c) dacc[c][n] = mfma_bf16_16x16x16(au[h * DBR + c], bx2, dacc[c][n]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the slabs are rewritten by the next block's quantize
+      __syncthreads();
     }
   };
-  // the next block's loads go out as soon as this block's values are in LDS,
-  // and overlap the MFMA phase
-  for (; bx < nrb; bx += G) {
-    quant(va, ha, bx);
-    if constexpr (DBR > 0) {
-      // this block's adapter rows, packed before the prefetch replaces them
-#pragma unroll
-      for (int c = 0; c < DBR; ++c)
-        au[c] = i32x2{static_cast<int>(ua[c][0] | (ua[c][1] << 16)), static_cast<int>(ua[c][2] | (ua[c][3] << 16))};
+  // one block: its adapter operand (dB), quantize, refill the register set
+  // with the block NB steps ahead, project
+  auto block = [&](u32x4* v, uint32_t b) {
+    uint32_t uu[UA][4];
+    if constexpr (DBR > 0) load_u(uu, b);
+    quant(v, ha, b);
+    load(v, ha, b + NB * G);
+    mma(b, uu);
+  };
+  if constexpr (NB == 1) {
+    for (; bx < nrb; bx += G) block(va[0], bx);
+  } else {
+    // both halves run unconditionally (a block past the end reads zeros and
+    // stores nothing): with straight-line code between the loop's ends the
+    // compiler's count of outstanding loads and stores stays exact, and the
+    // waits before a set is quantized do not drain the other set's loads
+    for (; bx < nrb; bx += 2 * G) {
+      block(va[0], bx);
+      block(va[NB - 1], bx + G);
     }
-    load(va, ha, bx + G);
-    mma(bx);
   }
   if constexpr (DBR > 0) {
-    // per rank group: the 4 waves' dB partials go to LDS (one padded region
-    // each), then all threads add them in wave order and write the
-    // workgroup's partial dbpart[j][r][col] with 16-byte stores
-    constexpr int DP = KC + 4;                 // row pitch: the 4 lane groups hit distinct banks
-    constexpr int Q = KC / 4;                  // float4 items per row
-    float* red = reinterpret_cast<float*>(lds);
-    float* mine = red + wave * (16 * DP);
+    // the workgroup's partial dbpart[j][r][col]: each wave owns its columns
     const uint32_t j = blockIdx.x % G;
     float* dst = a.dbpart + static_cast<uint64_t>(j) * (DBR * 16) * cols;
 #pragma unroll
-    for (int c = 0; c < DBR; ++c) {
-      __syncthreads();
+    for (int c = 0; c < DBR; ++c)
 #pragma unroll
-      for (int n = 0; n < NT; ++n)
+      for (int n = 0; n < NTW; ++n) {
+        const uint32_t cc = cbeg + (KC / 4) * wave + 16 * n + lr;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) mine[(4 * g + e) * DP + 16 * n + lr] = dacc[c][n][e];
-      __syncthreads();
-#pragma unroll
-      for (int it = 0; it < 16 * Q / 256; ++it) {
-        const int idx = t + 256 * it;
-        const int r = idx / Q, cc = (idx % Q) * 4;
-        f32x4 v = *reinterpret_cast<const f32x4*>(&red[r * DP + cc]);
-#pragma unroll
-        for (int w = 1; w < 4; ++w) v += *reinterpret_cast<const f32x4*>(&red[w * (16 * DP) + r * DP + cc]);
-        if (cbeg + cc < cols)
-          *reinterpret_cast<f32x4*>(&dst[static_cast<uint64_t>(16 * c + r) * cols + cbeg + cc]) = v;
+        for (int e = 0; e < 4; ++e)
+          if (cc < cols) dst[static_cast<uint64_t>(16 * c + 4 * g + e) * cols + cc] = dacc[c][n][e];
       }
-    }
   }
 }
 
