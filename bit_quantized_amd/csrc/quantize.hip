@@ -377,8 +377,15 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const uint32_t off = base + i * RPI * ld2;
-      v[i] = buf_load128(rin, off);                  // re-read later in the step: cached
-      if constexpr (ACT == 2) h[i] = buf_load128(rin2, off);
+      // X is read again by the adapter gradients, and so is dY when dB is not
+      // fused here: cached.  With dB fused, dY (and h) are read only here.
+      if constexpr (DBR > 0) {
+        v[i] = buf_load128_nt(rin, off);
+        if constexpr (ACT == 2) h[i] = buf_load128_nt(rin2, off);
+      } else {
+        v[i] = buf_load128(rin, off);
+        if constexpr (ACT == 2) h[i] = buf_load128(rin2, off);
+      }
     }
   };
   // The adapter operand of block bx, loaded when the block starts (its
