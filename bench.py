@@ -183,7 +183,8 @@ def _step_kernel(kname, state):
 
     Dispatches are taken in order: each quantize + down-projection opens a
     new phase (forward, then backward), and the reduction kernel after it
-    belongs to the same launch.  Returns (name, opens_launch)."""
+    belongs to the same launch, as the adapter-gradient reduce belongs to
+    the adapter-gradient launch.  Returns (name, opens_launch)."""
     if "k_quant_down" in kname:
         state["fwd"] = not state.get("fwd", False)
         return ("fwd_quant_down" if state["fwd"] else "bwd_quant_down"), True
@@ -191,6 +192,8 @@ def _step_kernel(kname, state):
         return ("fwd_quant_down" if state.get("fwd") else "bwd_quant_down"), False
     if "k_gemm" in kname:
         return ("fwd_gemm" if state.get("fwd") else "bwd_gemm_dgrad"), True
+    if "k_lora_reduce" in kname:
+        return "bwd_lora_grads", False
     if "k_lora" in kname:
         return "bwd_lora_grads", True
     return None, False
