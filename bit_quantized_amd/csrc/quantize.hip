@@ -146,16 +146,20 @@ __global__ __launch_bounds__(256) void k_quant_tile32(const uint16_t* __restrict
   uint32_t o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = encode8(v[i][0], v[i][1], v[i][2], v[i][3], sc);
-  if (ok) {
+  // streaming (non-temporal) stores: weights are quantized once, ahead of use
+  const auto rcodes = make_rsrc(codes, static_cast<uint64_t>(rows) * (cols >> 1));
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<uint32_t*>(codes + static_cast<uint64_t>(y * 32 + 8 * wave + i) * (cols >> 1) + (col >> 1)) = o[i];
+  for (int i = 0; i < 8; ++i)
+    __builtin_amdgcn_raw_buffer_store_b32(
+        o[i], rcodes, static_cast<int>(ok ? (y * 32 + 8 * wave + i) * (cols >> 1) + (col >> 1) : BUF_OOB), 0, 2);
+  if (ok) {
     if (wave == 0 && (lane & 3) == 0) {
       scales[static_cast<uint64_t>(y) * (cols >> 5) + (col >> 5)] = static_cast<uint8_t>(s);
       if (scales_t) scales_t[static_cast<uint64_t>(col >> 5) * ny + y] = static_cast<uint8_t>(s);
     }
   }
   if (!codes_t) return;
+  const auto rcodes_t = make_rsrc(codes_t, static_cast<uint64_t>(cols) * (rows >> 1));
 #pragma unroll
   for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(&ct[(8 * wave + i) * CT_P + 4 * lane]) = o[i];
   __syncthreads();
@@ -168,108 +172,180 @@ __global__ __launch_bounds__(256) void k_quant_tile32(const uint16_t* __restrict
     const u32x2 lo = lds_read_tr4(&ct[q * CT_P + cg * 8]);
     const u32x2 hi = lds_read_tr4(&ct[(16 + q) * CT_P + cg * 8]);
     const uint32_t c = x * 512 + cg * 16 + q;
-    if (c < cols)
-      *reinterpret_cast<u32x4*>(codes_t + static_cast<uint64_t>(c) * (rows >> 1) + y * 16) =
-          u32x4{lo[0], lo[1], hi[0], hi[1]};
+    __builtin_amdgcn_raw_buffer_store_b128(u32x4{lo[0], lo[1], hi[0], hi[1]}, rcodes_t,
+                                           static_cast<int>(c < cols ? c * (rows >> 1) + y * 16 : BUF_OOB), 0, 2);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Dual output from one read: 1x32 blocks along rows (codes [rows, cols/2])
-// and along columns (the row blocks of the transpose, codes_t [cols,
-// rows/2]).  A workgroup covers 32 rows x 512 columns.  Row blocks: as the
-// row quantizer (quad DPP amax).  Column blocks: each lane takes the max of
-// its 8 rows per column, the 4 waves combine through LDS; the codes are made
-// from vertical pairs (rows 2p, 2p+1 of one column share a scale), so each
-// converted byte already is a byte of the transposed layout, and a lane's
-// 4 bytes are 8 rows of one column.  The 4 waves' words of a column meet in
-// LDS and leave as one 16-byte store.
-__global__ __launch_bounds__(256) void k_quant_row32_t(const uint16_t* __restrict__ in,
+// Dual output from one read: 1x32 blocks along rows (codes [rows, cols/2],
+// scales [rows, cols/32]) and along columns (the row blocks of the
+// transpose: codes_t [cols, rows/2], scales_t [cols, rows/32]).
+//
+// A 512-thread workgroup covers a 256 x 256 tile.  Thread (rg = t / 32,
+// cg = t % 32) holds rows 16 rg .. 16 rg + 15 of columns 8 cg .. 8 cg + 7;
+// a column block (32 rows of one column) is lanes l and l + 32 of one wave:
+//   - loads: one instruction reads two rows x 512 contiguous bytes;
+//   - row blocks: four consecutive lanes hold one block, amax by two quad
+//     DPP steps; one store instruction writes two full 128-byte code lines;
+//   - column blocks: each lane's max over its 16 rows, then the partner
+//     lane's (one shuffle); the codes come from vertical pairs (rows 2p,
+//     2p+1 of one column share a scale), so each converted byte is a byte of
+//     the transposed layout; the partners swap halves so that each owns four
+//     whole 16-byte column blocks;
+//   - the transposed codes meet in LDS (16-byte chunks, XOR-swizzled by
+//     column so that neither the writes nor the reads conflict) and leave as
+//     full 128-byte lines (256 rows of one column), eight per store
+//     instruction; both scale arrays are gathered in LDS into 8-byte runs;
+//   - code stores are non-temporal: the outputs are not read again soon
+//     (measured: 146 -> 133 us on a 16384 x 12288 tensor).
+// Rows are a multiple of 32 and columns of 32 (host checks), so a column
+// block and a lane's 32-column row block are wholly inside or outside.
+__global__ __launch_bounds__(512) void k_quant_row32_t(const uint16_t* __restrict__ in,
                                                        uint32_t rows, uint32_t cols, int64_t ld,
                                                        uint8_t* __restrict__ codes,
                                                        uint8_t* __restrict__ scales,
                                                        uint8_t* __restrict__ codes_t,
                                                        uint8_t* __restrict__ scales_t) {
-  __shared__ __attribute__((aligned(16))) uint32_t cmax[4][64][4];
-  __shared__ __attribute__((aligned(16))) uint32_t ctw[4][512 + 4];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const uint32_t nx = (cols + 511) / 512, ny = rows / 32;
+  __shared__ __attribute__((aligned(16))) uint8_t ct[256 * 128];   // [column][16-byte chunk ^ swz]
+  __shared__ __attribute__((aligned(16))) uint8_t st[256 * 8];     // column scales [column][block]
+  __shared__ __attribute__((aligned(16))) uint8_t sr[256 * 8];     // row scales [row][block]
+  const int t = threadIdx.x;
+  const int rg = t >> 5, cg = t & 31;
+  const bool upper = (rg & 1) != 0;                        // second 16 rows of the column block
+  const uint32_t nx = (cols + 255) / 256, ny = (rows + 255) / 256;
   uint32_t x, y;
   band_coords(xcd_remap(blockIdx.x, nx * ny), nx, ny, x, y);
-  const uint32_t col = x * 512 + 8 * lane;
-  const bool ok = col < cols;
-  u32x4 v[8];
-  load_slab(make_rsrc(in, static_cast<uint64_t>(rows) * ld * 2), y * 32 + 8 * wave, col, ok,
-            static_cast<uint32_t>(ld) * 2, v);
+  const uint32_t row0 = y * 256 + 16 * rg;                 // this thread's first row
+  const uint32_t col = x * 256 + 8 * cg;                   // this lane's first column
+  // rows come in whole 32-row blocks, so both partners agree on this
+  const bool ok = y * 256 + 32 * (rg >> 1) < rows && col < cols;
+  const uint32_t ld2 = static_cast<uint32_t>(ld) * 2;
+  const uint32_t cpr = cols >> 1, spr = cols >> 5, ncb = rows >> 5;
+  const auto rin = make_rsrc(in, static_cast<uint64_t>(rows) * ld * 2);
+  u32x4 v[16];
+  {
+    const uint32_t base = ok ? row0 * ld2 + col * 2 : BUF_OOB;
+#pragma unroll
+    for (int i = 0; i < 16; ++i) v[i] = buf_load128_nt(rin, ok ? base + i * ld2 : BUF_OOB);
+  }
 
   // ---- row blocks
+  const auto rcodes = make_rsrc(codes, static_cast<uint64_t>(rows) * cpr);
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
+  for (int i = 0; i < 16; ++i) {
     uint32_t am = hmax_u16x2(max_u16x2(max_u16x2(abs_bf16x2(v[i][0]), abs_bf16x2(v[i][1])),
                                        max_u16x2(abs_bf16x2(v[i][2]), abs_bf16x2(v[i][3]))));
     am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0xB1, 0xF, 0xF, false)));
     am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0x4E, 0xF, 0xF, false)));
-    const uint32_t s = e8m0_from_amax_bits(am);
-    const uint32_t o = encode8(v[i][0], v[i][1], v[i][2], v[i][3], e8m0_to_f32(s));
-    const uint32_t row = y * 32 + 8 * wave + i;
-    if (ok) {
-      *reinterpret_cast<uint32_t*>(codes + static_cast<uint64_t>(row) * (cols >> 1) + (col >> 1)) = o;
-      if ((lane & 3) == 0) scales[static_cast<uint64_t>(row) * (cols >> 5) + (col >> 5)] = static_cast<uint8_t>(s);
-    }
+    const uint32_t s8 = e8m0_from_amax_bits(am);
+    const uint32_t o = encode8(v[i][0], v[i][1], v[i][2], v[i][3], e8m0_to_f32(s8));
+    __builtin_amdgcn_raw_buffer_store_b32(o, rcodes, static_cast<int>(ok ? (row0 + i) * cpr + (col >> 1) : BUF_OOB), 0, 2);
+    if ((cg & 3) == 0) sr[(16 * rg + i) * 8 + (cg >> 2)] = static_cast<uint8_t>(s8);
   }
 
   // ---- column blocks: amax of columns 2k (low half) and 2k+1 (high half)
+  // over the 32 rows of both partners
   u32x4 cm = {0, 0, 0, 0};
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 16; ++i)
 #pragma unroll
     for (int k = 0; k < 4; ++k) cm[k] = max_u16x2(cm[k], abs_bf16x2(v[i][k]));
-  *reinterpret_cast<u32x4*>(&cmax[wave][lane][0]) = cm;
-  __syncthreads();
-  u32x4 cw = *reinterpret_cast<const u32x4*>(&cmax[0][lane][0]);
 #pragma unroll
-  for (int w = 1; w < 4; ++w) {
-    const u32x4 o = *reinterpret_cast<const u32x4*>(&cmax[w][lane][0]);
-#pragma unroll
-    for (int k = 0; k < 4; ++k) cw[k] = max_u16x2(cw[k], o[k]);
-  }
+  for (int k = 0; k < 4; ++k) cm[k] = max_u16x2(cm[k], static_cast<uint32_t>(__shfl_xor(static_cast<int>(cm[k]), 32)));
+  // half[j] = this lane's 8 bytes (its 16 rows) of column 8 cg + j
+  uint32_t half[8][2];
   uint32_t cs[8];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    cs[2 * k] = e8m0_from_amax_bits(cw[k] & 0xFFFFu);
-    cs[2 * k + 1] = e8m0_from_amax_bits(cw[k] >> 16);
-  }
-  // column j = 2k + h: byte p of its word = rows 8w + 2p (low nibble), 8w + 2p + 1
 #pragma unroll
   for (int k = 0; k < 4; ++k) {
 #pragma unroll
     for (int h = 0; h < 2; ++h) {
+      const uint32_t s8 = e8m0_from_amax_bits(h ? cm[k] >> 16 : cm[k] & 0xFFFFu);
+      cs[2 * k + h] = s8;
+      const float sc = e8m0_to_f32(s8);
       const uint32_t sel = h ? 0x07060302u : 0x05040100u;
-      const float sc = e8m0_to_f32(cs[2 * k + h]);
-      auto vp = [&](int p) {
-        return __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(v[2 * p + 1][k], v[2 * p][k], sel));
-      };
-      uint32_t r = 0;
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(0), sc, 0);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(1), sc, 1);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(2), sc, 2);
-      r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(3), sc, 3);
-      ctw[wave][8 * lane + 2 * k + h] = r;
+      // byte p of word m = rows 8m + 2p (low nibble) and 8m + 2p + 1
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        auto vp = [&](int p) {
+          return __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(v[8 * m + 2 * p + 1][k], v[8 * m + 2 * p][k], sel));
+        };
+        uint32_t r = 0;
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(0), sc, 0);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(1), sc, 1);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(2), sc, 2);
+        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(3), sc, 3);
+        half[2 * k + h][m] = r;
+      }
     }
   }
-  if (wave == 0 && ok) {
+  // the lower partner keeps columns 0..3 of its 8, the upper one 4..7: each
+  // sends the halves of the other four columns and receives their partner
+  // halves; the lower 16 rows are the first 8 bytes of a column block
+  const int jb = upper ? 4 : 0;
+  uint32_t blk[4][4];
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      scales_t[static_cast<uint64_t>(col + j) * ny + y] = static_cast<uint8_t>(cs[j]);
+  for (int j = 0; j < 4; ++j) {
+#pragma unroll
+    for (int m = 0; m < 2; ++m) {
+      const uint32_t send = upper ? half[j][m] : half[4 + j][m];
+      const uint32_t got = static_cast<uint32_t>(__shfl_xor(static_cast<int>(send), 32));
+      const uint32_t mine = upper ? half[4 + j][m] : half[j][m];
+      blk[j][m] = upper ? got : mine;
+      blk[j][2 + m] = upper ? mine : got;
+    }
   }
-  __syncthreads();
+  const int swz = cg & 7;
+  const int cb = rg >> 1;                                  // 32-row block of the tile
 #pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const int cc = t + 256 * h;
-    const uint32_t c = x * 512 + cc;
-    if (c < cols)
-      *reinterpret_cast<u32x4*>(codes_t + static_cast<uint64_t>(c) * (rows >> 1) + y * 16) =
-          u32x4{ctw[0][cc], ctw[1][cc], ctw[2][cc], ctw[3][cc]};
+  for (int j = 0; j < 4; ++j) {
+    const int c = 8 * cg + jb + j;                         // column within the tile
+    *reinterpret_cast<u32x4*>(&ct[c * 128 + ((cb ^ swz) << 4)]) = u32x4{blk[j][0], blk[j][1], blk[j][2], blk[j][3]};
+  }
+  // column scales: the same split (constant indices: a lane-dependent index
+  // into cs would put the array in scratch)
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if ((j >= 4) == upper) st[(8 * cg + j) * 8 + cb] = static_cast<uint8_t>(cs[j]);
+  __syncthreads();
+
+  // ---- transposed codes: chunk u = t + 512 s is column u / 8, 16-byte
+  // piece u % 8 (rows 32 q .. 32 q + 31) of the column's 128-byte line
+  const auto rcodes_t = make_rsrc(codes_t, static_cast<uint64_t>(cols) * (rows >> 1));
+#pragma unroll
+  for (int s2 = 0; s2 < 4; ++s2) {
+    const int u = t + 512 * s2, c = u >> 3, q = u & 7;
+    const u32x4 w = *reinterpret_cast<const u32x4*>(&ct[c * 128 + ((q ^ ((c >> 3) & 7)) << 4)]);
+    const uint32_t gc = x * 256 + c, gr = y * 256 + 32 * q;
+    const bool in = gc < cols && gr < rows;
+    __builtin_amdgcn_raw_buffer_store_b128(w, rcodes_t, static_cast<int>(in ? gc * (rows >> 1) + (gr >> 1) : BUF_OOB), 0, 2);
+  }
+  // ---- scales: threads 0..255 write row t's 8 row-scale bytes, threads
+  // 256..511 column t-256's 8 column-scale bytes (one 8-byte store when the
+  // run is aligned and whole)
+  if (t < 256) {
+    const auto rscales = make_rsrc(scales, static_cast<uint64_t>(rows) * spr);
+    const uint32_t gr = y * 256 + t;
+    const u32x2 rs = *reinterpret_cast<const u32x2*>(&sr[t * 8]);
+    if ((spr & 7) == 0) {
+      __builtin_amdgcn_raw_buffer_store_b64(rs, rscales, static_cast<int>(gr < rows ? gr * spr + 8 * x : BUF_OOB), 0, 0);
+    } else {
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+        buf_store8(rscales, gr < rows && 8 * x + b < spr ? gr * spr + 8 * x + b : BUF_OOB, rs[b >> 2] >> (8 * (b & 3)));
+    }
+  } else {
+    const auto rscales_t = make_rsrc(scales_t, static_cast<uint64_t>(cols) * ncb);
+    const int tc = t - 256;
+    const uint32_t gc = x * 256 + tc;
+    const u32x2 cs2 = *reinterpret_cast<const u32x2*>(&st[tc * 8]);
+    if ((ncb & 7) == 0) {
+      __builtin_amdgcn_raw_buffer_store_b64(cs2, rscales_t, static_cast<int>(gc < cols ? gc * ncb + 8 * y : BUF_OOB), 0, 0);
+    } else {
+#pragma unroll
+      for (int b = 0; b < 8; ++b)
+        buf_store8(rscales_t, gc < cols && 8 * y + b < ncb ? gc * ncb + 8 * y + b : BUF_OOB, cs2[b >> 2] >> (8 * (b & 3)));
+    }
   }
 }
 
@@ -676,8 +752,8 @@ hipError_t launch_quant_tile32(const uint16_t* in, int64_t rows, int64_t cols, i
 hipError_t launch_quant_row32_t(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
                                 uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
                                 uint8_t* scales_t, hipStream_t st) {
-  const uint32_t n = static_cast<uint32_t>(((cols + 511) / 512) * (rows / 32));
-  hipLaunchKernelGGL(k_quant_row32_t, dim3(n), dim3(256), 0, st, in, static_cast<uint32_t>(rows),
+  const uint32_t n = static_cast<uint32_t>(((cols + 255) / 256) * ((rows + 255) / 256));
+  hipLaunchKernelGGL(k_quant_row32_t, dim3(n), dim3(512), 0, st, in, static_cast<uint32_t>(rows),
                      static_cast<uint32_t>(cols), ld, codes, scales, codes_t, scales_t);
   return hipGetLastError();
 }

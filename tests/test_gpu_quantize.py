@@ -102,7 +102,8 @@ def test_tile32_adversarial():
     np.testing.assert_array_equal(c, ec)
 
 
-@pytest.mark.parametrize("shape", [(32, 32), (64, 64), (96, 160), (160, 96), (544, 288)])
+@pytest.mark.parametrize("shape", [(32, 32), (64, 64), (96, 160), (160, 96), (544, 288), (512, 512),
+                                   (800, 1056)])
 def test_row32_t(shape):
     x = synth.stress_activation(seed=shape[0], rows=shape[0], cols=shape[1], zero_tile_frac=0.1)
     say("row32_t", shape)
