@@ -252,7 +252,7 @@ ft_status fourtune_quantize(int mode, const uint16_t* in, int64_t rows, int64_t 
   hipStream_t st = static_cast<hipStream_t>(stream);
   switch (mode) {
     case FT_Q_ROW32:
-      { Timed tm("quant_row32", st); return launched(tm.done(ft::launch_quant_row32(in, nullptr, 0, rows, cols, ld_in, codes, scales, st))); }
+      { Timed tm("quant_row32", st); return launched(tm.done(ft::launch_quant_row32(in, nullptr, 0, rows, cols, ld_in, codes, scales, st, true))); }
     case FT_Q_TILE32:
       { Timed tm("quant_tile32", st); return launched(tm.done(ft::launch_quant_tile32(in, rows, cols, ld_in, codes, scales, codes_t, scales_t, st))); }
     default:

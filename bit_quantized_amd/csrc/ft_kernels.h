@@ -25,7 +25,7 @@ int cu_count();
 // quantize.hip
 hipError_t launch_quant_row32(const uint16_t* in, const uint16_t* in2, int act, int64_t rows,
                               int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
-                              hipStream_t st);
+                              hipStream_t st, bool streaming = false);
 // codes_t / scales_t: optional transposed copy (both null or both set).
 hipError_t launch_quant_tile32(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
                                uint8_t* codes, uint8_t* scales, uint8_t* codes_t,

@@ -30,7 +30,7 @@ namespace ft {
 // applies the input activation first (0: none; 1: gelu(in); 2: in *
 // gelu'(in2)), rounded to bf16 as the quantizer's input.  CONTIG: rows are
 // contiguous (ld == cols), so block b starts at element 32 b.
-template <int ACT, bool CONTIG>
+template <int ACT, bool CONTIG, bool NTS>
 __global__ __launch_bounds__(256) void k_quant_row32(const uint16_t* __restrict__ in,
                                                      const uint16_t* __restrict__ in2,
                                                      uint32_t rows, uint32_t cols, int64_t ld,
@@ -46,6 +46,8 @@ __global__ __launch_bounds__(256) void k_quant_row32(const uint16_t* __restrict_
   const auto r2 = make_rsrc(in2, ACT == 2 ? bytes : 0);
   const uint32_t ld32 = static_cast<uint32_t>(ld);
   const uint32_t step = gridDim.x * 4 * 16 * U;
+  const auto rcodes = make_rsrc(codes, static_cast<uint64_t>(nblk) * 16);
+  const auto rscales = make_rsrc(scales, nblk);
   for (uint32_t b0 = (blockIdx.x * 4 + (threadIdx.x >> 6)) * 16 * U; b0 < nblk; b0 += step) {
     u32x4 v[U], h[U];
 #pragma unroll
@@ -71,10 +73,10 @@ __global__ __launch_bounds__(256) void k_quant_row32(const uint16_t* __restrict_
       am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0x4E, 0xF, 0xF, false)));
       const uint32_t s = e8m0_from_amax_bits(am);
       const uint32_t o = encode8(x[0], x[1], x[2], x[3], e8m0_to_f32(s));
-      if (b < nblk) {
-        *reinterpret_cast<uint32_t*>(codes + static_cast<uint64_t>(b) * 16 + q * 4) = o;
-        if (q == 0) scales[b] = static_cast<uint8_t>(s);
-      }
+      // unconditional stores, masked by offset (exact wait counts)
+      __builtin_amdgcn_raw_buffer_store_b32(o, rcodes, static_cast<int>(b < nblk ? b * 16 + q * 4 : BUF_OOB), 0,
+                                            NTS ? 2 : 0);
+      buf_store8(rscales, b < nblk && q == 0 ? b : BUF_OOB, s);
     }
   }
 }
@@ -724,15 +726,18 @@ __global__ __launch_bounds__(256) void k_rank_reduce(const RRArgs a) {
 
 hipError_t launch_quant_row32(const uint16_t* in, const uint16_t* in2, int act, int64_t rows,
                               int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
-                              hipStream_t st) {
+                              hipStream_t st, bool streaming) {
   const uint64_t nblk = static_cast<uint64_t>(rows) * (cols / 32);
   uint64_t grid = (nblk + 1023) / 1024;             // 1024 blocks per workgroup pass
   if (grid > 16384) grid = 16384;
   const dim3 g(static_cast<uint32_t>(grid));
   const uint32_t r = static_cast<uint32_t>(rows), c = static_cast<uint32_t>(cols);
-#define FT_QR(A, C) hipLaunchKernelGGL((k_quant_row32<A, C>), g, dim3(256), 0, st, in, in2, r, c, ld, codes, scales)
-#define FT_QRA(A) do { if (ld == cols) FT_QR(A, true); else FT_QR(A, false); } while (0)
-  if (act == 1) FT_QRA(1);
+#define FT_QR(A, C, N) hipLaunchKernelGGL((k_quant_row32<A, C, N>), g, dim3(256), 0, st, in, in2, r, c, ld, codes, scales)
+#define FT_QRA(A) do { if (ld == cols) FT_QR(A, true, false); else FT_QR(A, false, false); } while (0)
+  if (streaming && act == 0) {
+    // stand-alone quantization: the codes are not read again right away
+    if (ld == cols) FT_QR(0, true, true); else FT_QR(0, false, true);
+  } else if (act == 1) FT_QRA(1);
   else if (act == 2) FT_QRA(2);
   else FT_QRA(0);
 #undef FT_QRA
