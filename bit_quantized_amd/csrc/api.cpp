@@ -135,9 +135,10 @@ ft_status check_linear(const ft_linear* L) {
   if ((L->K & 31) || (L->N & 31)) return FT_ESHAPE;
   if (L->M * L->K * 2 > kMaxBytes || L->M * L->N * 2 > kMaxBytes || L->N * L->K / 2 > kMaxBytes)
     return FT_ESHAPE;
-  // the fused quantizer addresses whole 64-row blocks with 32-bit offsets:
-  // the padded activations must stay below 2^31 bytes as well
-  if ((L->M + 64) * std::max(L->K, L->N) * 2 > kMaxBytes) return FT_ESHAPE;
+  // the fused quantizer and the GEMM address whole 64-row blocks and
+  // 256-row tiles with 32-bit offsets: the padded activations and outputs
+  // must stay below 2^31 bytes as well
+  if ((L->M + 256) * std::max(L->K, L->N) * 2 > kMaxBytes) return FT_ESHAPE;
   if (L->r_stab < 0 || L->r_lora < 0 || L->r_stab + L->r_lora > FT_MAX_RANK) return FT_ESHAPE;
   if (L->M * (L->r_stab + L->r_lora) * 2 > kMaxBytes) return FT_ESHAPE;
   if (!L->w_codes || !L->w_scales) return FT_EINVAL;

@@ -139,16 +139,18 @@ struct Frags {
 
 template <int K> struct MfmaKind { static constexpr int v = K; };   // 0: MXFP4, 1: bf16 ranks
 
-// LR: the tiles start with two rank steps (64 padded ranks).  ODD: the
-// number of reduction steps RED/128 is odd.
-template <bool LR, bool ODD>
+// LR: the tiles start with two rank steps (64 padded ranks).  An odd
+// number of reduction steps RED/128 is padded by one step whose loads are
+// pushed out of range: zero codes and zero scale bytes add exactly 0, and
+// every tile then has an even number of steps for the even/odd registers.
+template <bool LR>
 __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[NST * ST_BYTES + 4 * OUT_WAVE];
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
   const int wm = wave >> 1, wn = wave & 1;
-  const int l32 = lane & 31, grp = lane >> 5, odd = lane & 1;
+  const int l32 = lane & 31, grp = lane >> 5;
   const int64_t M = g.M, RED = g.RED, NOUT = g.NOUT;
 
   const uint32_t mt_n = static_cast<uint32_t>((M + BM - 1) / BM);
@@ -157,7 +159,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   const uint32_t full = ntiles / G, nlast = ntiles % G;
   const uint32_t my_tiles = full + (bid < nlast ? 1u : 0u);
   constexpr int NLR = LR ? 2 : 0;
-  const int nks = static_cast<int>(RED / BK);
+  const int nks_real = static_cast<int>(RED / BK);
+  const int nks = nks_real + (nks_real & 1);             // padded to even
   const int spt = nks + NLR;                             // steps per tile
   const int total = static_cast<int>(my_tiles) * spt;
   const bool tiny = spt < 3;                              // see the barrier waits
@@ -188,8 +191,6 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
     code_row[q] = row * row_bytes + (ch << 4);
     lr_row[q] = row * LR_BYTES + (ch << 4);
   }
-  const uint32_t sa_lane = static_cast<uint32_t>(64 * wave + lane) * row_sc;
-  const uint32_t sb_lane = (wave == 0 && lane < 8) ? static_cast<uint32_t>(lane) * row_sc : OOB;
 
   // DMA cursor: the (tile, step) whose A or B half is loaded next, with the
   // tile's base offsets.  A cursors use m0, B cursors j0.
@@ -232,8 +233,9 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
     h.lr = lrs;
     h.rows = lrs ? (is_b ? r_lo : r_lm) : (is_b ? rb_codes : ra_codes);
     h.sc = is_b ? rb_sc : ra_sc;
-    h.base = !live ? OOB : (lrs ? c.lr + static_cast<uint32_t>(c.s) * 64 : c.code + static_cast<uint32_t>(ks) * 64);
-    h.sbase = (!live || lrs) ? OOB : c.sc + static_cast<uint32_t>(ks) * 4;
+    const bool pad = !lrs && ks >= nks_real;                 // the padding step
+    h.base = (!live || pad) ? OOB : (lrs ? c.lr + static_cast<uint32_t>(c.s) * 64 : c.code + static_cast<uint32_t>(ks) * 64);
+    h.sbase = (!live || lrs || pad) ? OOB : c.sc + static_cast<uint32_t>(ks) * 4;
     uint8_t* st = lds + (c.gs & (NST - 1)) * ST_BYTES;
     h.dst = st + (is_b ? ST_A : 0) + 64 * wave * ROWB;
     h.sdst = is_b ? st + ST_A + ST_B + ST_SA + wave * 256 : st + ST_A + ST_B + 64 * wave * 4;
@@ -245,10 +247,18 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
     if (item < 4) {
       const uint32_t lane_off = h.lr ? lr_row[item] : code_row[item];
       dma16(h.rows, h.dst + item * 16 * ROWB, lane_off + h.base);
-    } else if (!is_b) {
-      dma4(h.sc, h.sdst, sa_lane + h.sbase);
     } else {
-      dma4(h.sc, h.sdst, sb_lane == OOB ? OOB : sb_lane + h.sbase);
+      // the scale lane offsets are recomputed from an opaque copy of the
+      // thread id at each use: kept in registers across the K loop they were
+      // spilled, and each reload's full memory wait drained the pipeline
+      uint32_t tl = static_cast<uint32_t>(t);
+      asm volatile("" : "+v"(tl));
+      if (!is_b) {
+        dma4(h.sc, h.sdst, tl * row_sc + h.sbase);                 // row 64 wave + lane
+      } else {
+        const uint32_t sb = (tl < 8) ? tl * row_sc : OOB;         // wave 0, lanes 0..7
+        dma4(h.sc, h.sdst, sb == OOB ? OOB : sb + h.sbase);
+      }
     }
   };
   auto read_frags = [&](int buf, int c, u32x4 (&af)[4], u32x4 (&bf)[4]) {
@@ -287,9 +297,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   // Output of the finished tile (m0, j0): 8 strips of 16 rows per wave,
   // then the accumulators are cleared for the next tile.
   uint8_t* ostage = lds + NST * ST_BYTES + wave * OUT_WAVE;
-  const uint32_t psel = pair_sel(odd);
   const auto r_out = rsrc(g.out, static_cast<uint64_t>(M) * NOUT * 2);
+  // 32-bit output offsets: (M + 256) * NOUT * 2 < 2^31 (host check), so a
+  // row past M lands past the end of the buffer and is dropped without a
+  // test; only columns past NOUT are masked.
+  const uint32_t out_row = static_cast<uint32_t>(NOUT) * 2;
   auto store_tile = [&](int64_t m0, int64_t j0) {
+    // lane-dependent addresses are rebuilt for each tile from an opaque copy
+    // of the lane id: hoisted out of the tile loop, they stay live across the
+    // K loop and push it into scratch
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lgrp = ln >> 5, lodd = ln & 1, ll32 = ln & 31;
+    const uint32_t psel = pair_sel(lodd);
+    const uint32_t gcol = static_cast<uint32_t>(j0) + wn * 128 + (ln & 15) * 8;
+    const uint32_t out_base = gcol < static_cast<uint32_t>(NOUT)
+                                  ? (static_cast<uint32_t>(m0) + wm * 128 + (ln >> 4)) * out_row + gcol * 2
+                                  : OOB;
 #pragma unroll
     for (int mt = 0; mt < 4; ++mt)
 #pragma unroll
@@ -300,19 +324,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
             const uint32_t v = pair_bf16(acc[mt][nt][8 * h + 2 * p], acc[mt][nt][8 * h + 2 * p + 1], psel);
-            const int row = 8 * (p >> 1) + 4 * grp + 2 * (p & 1) + odd;     // 0 .. 15
+            const int row = 8 * (p >> 1) + 4 * lgrp + 2 * (p & 1) + lodd;   // 0 .. 15
             const int sw = (row & 1) | (((row >> 2) & 1) << 1);             // 64-byte segment swizzle
-            const int col = nt * 32 + (l32 & ~1);
+            const int col = nt * 32 + (ll32 & ~1);
             *reinterpret_cast<uint32_t*>(ostage + row * 256 + (((col >> 5) ^ sw) << 6) + (col & 31) * 2) = v;
           }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const int idx = e * 64 + lane, row = idx >> 4, c16 = idx & 15;
+          const int idx = e * 64 + ln, row = idx >> 4, c16 = idx & 15;
           const int sw = (row & 1) | (((row >> 2) & 1) << 1);
           const u32x4 v = lds_read_b128(ostage + row * 256 + ((((c16 >> 2) ^ sw) << 6) | ((c16 & 3) << 4)));
-          const int64_t grow = m0 + wm * 128 + mt * 32 + 16 * h + row;
-          const int64_t gcol = j0 + wn * 128 + c16 * 8;
-          const uint32_t off = (grow < M && gcol < NOUT) ? static_cast<uint32_t>((grow * NOUT + gcol) * 2) : OOB;
+          const uint32_t off = out_base == OOB ? OOB : out_base + static_cast<uint32_t>(mt * 32 + 16 * h + 4 * e) * out_row;
           __builtin_amdgcn_raw_buffer_store_b128(v, r_out, static_cast<int>(off), 0, 0);
         }
       }
@@ -357,7 +379,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   int gs = 0;   // global step of this workgroup
 
   // One step.  Cur holds this step's chunk-0 fragments and scales; Nxt gets
-  // the next step's (Nxt may be Cur: one wait on in-flight MFMAs).  DMA
+  // the next step's.  DMA
   // order per wave: ..., B half of stage gs+3 (first half of step gs), A
   // half of stage gs+4 (second half), [a tile's 32 output stores after its
   // last step], ...  after_store: one of the last two steps ended a tile.
@@ -378,14 +400,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   auto keep_s = [](const uint32_t (&x)[4]) {
     asm volatile("" ::"v"(x[0]), "v"(x[1]), "v"(x[2]), "v"(x[3]));
   };
-  // SAME: Cur and Nxt are one register set (the odd step of a tile).
   // The bookkeeping of a step (DMA addresses, fragment and scale reads,
   // scale shifts, cursor advance) is spread between the MFMAs of its two
   // halves, so that it issues while the matrix core is busy instead of
   // leaving it idle between the halves.
-  auto step = [&](Frags& Cur, Frags& Nxt, auto kind, bool after_store, auto same) {
+  auto step = [&](Frags& Cur, Frags& Nxt, auto kind, bool after_store) {
     constexpr bool RANK = decltype(kind)::v == 1;
-    constexpr bool SAME = decltype(same)::v == 1;
     const int buf = gs & (NST - 1);
     const int nbuf = (gs + 1) & (NST - 1);
     auto mma = [&](int i, const u32x4 (&af)[4], const u32x4 (&bf)[4], auto opsel) {
@@ -407,7 +427,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
       if (i == 0) {
         hb = half_dma(cb, true);
         read_frags(buf, 1, Cur.a1, Cur.b1);
-        if constexpr (!SAME) { keep4(Nxt.a1); keep4(Nxt.b1); }
+        keep4(Nxt.a1);
+        keep4(Nxt.b1);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (i % 3 == 1) {
@@ -438,7 +459,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
         ha = half_dma(ca, false);
         read_scales(nbuf, ras, rbs);
         read_frags(nbuf, 0, Nxt.a0, Nxt.b0);
-        if constexpr (!SAME) { keep4(Cur.a0); keep4(Cur.b0); }
+        keep4(Cur.a0);
+        keep4(Cur.b0);
         __builtin_amdgcn_sched_barrier(0);
       }
       if (i % 3 == 1) {
@@ -450,47 +472,39 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
         cursor_next(ca, false);
         __builtin_amdgcn_sched_barrier(0);
       }
-      if constexpr (!SAME) {
-        if (i == 12) {
+      if (i == 12) {
 #pragma unroll
-          for (int j = 0; j < 4; ++j) { Nxt.as[j] = ras[j] >> (8 * grp); Nxt.bs[j] = rbs[j] >> (8 * grp); }
-          __builtin_amdgcn_sched_barrier(0);
-        }
+        for (int j = 0; j < 4; ++j) { Nxt.as[j] = ras[j] >> (8 * grp); Nxt.bs[j] = rbs[j] >> (8 * grp); }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
     pin_acc();
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (SAME) {
-#pragma unroll
-      for (int j = 0; j < 4; ++j) { Nxt.as[j] = ras[j] >> (8 * grp); Nxt.bs[j] = rbs[j] >> (8 * grp); }
-    } else {
-      keep_s(Cur.as);
-      keep_s(Cur.bs);
-    }
+    keep_s(Cur.as);
+    keep_s(Cur.bs);
     keep_s(Nxt.as);
     keep_s(Nxt.bs);
     ++gs;
     __builtin_amdgcn_sched_barrier(0);
   };
 
-  const MfmaKind<0> fp4, two;
-  const MfmaKind<1> rank, one;
+  const MfmaKind<0> fp4;
+  const MfmaKind<1> rank;
   for (uint32_t k = 0; k < my_tiles; ++k) {
     const bool after = k > 0;
     if constexpr (LR) {
-      step(E, O, rank, after, two);
-      step(O, E, rank, after, two);
+      step(E, O, rank, after);
+      step(O, E, rank, after);
       for (int p = 0; p < nks / 2; ++p) {
-        step(E, O, fp4, false, two);
-        step(O, E, fp4, false, two);
+        step(E, O, fp4, false);
+        step(O, E, fp4, false);
       }
     } else {
       for (int p = 0; p < nks / 2; ++p) {
-        step(E, O, fp4, after && p == 0, two);
-        step(O, E, fp4, after && p == 0, two);
+        step(E, O, fp4, after && p == 0);
+        step(O, E, fp4, after && p == 0);
       }
     }
-    if constexpr (ODD) step(E, E, fp4, !LR && after && nks == 1, one);
     int64_t m0, j0;
     tile_of(k, m0, j0);
     store_tile(m0, j0);
@@ -681,10 +695,8 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     const int cus = cu_count();
     if (cus <= 0) return hipErrorInvalidDevice;
     const uint32_t grid = n < static_cast<uint32_t>(cus) ? n : static_cast<uint32_t>(cus);
-    const bool odd = ((g.RED / BK) & 1) != 0;
-#define FT_GP(LR, ODD) hipLaunchKernelGGL((k_gemm_pipe<LR, ODD>), dim3(grid), dim3(256), 0, st, g)
-    if (g.nlr > 0) { if (odd) FT_GP(true, true); else FT_GP(true, false); }
-    else { if (odd) FT_GP(false, true); else FT_GP(false, false); }
+#define FT_GP(LR) hipLaunchKernelGGL((k_gemm_pipe<LR>), dim3(grid), dim3(256), 0, st, g)
+    if (g.nlr > 0) FT_GP(true); else FT_GP(false);
 #undef FT_GP
   } else {
     hipLaunchKernelGGL(k_gemm, dim3(n), dim3(256), 0, st, g);

@@ -35,6 +35,8 @@ def test_tiny_case_full():
     (520, 1024, 768, 32, 16),    # several k steps, aligned scales
     (4200, 1120, 800, 32, 16),   # several column splits of 256 with a ragged last one
     (96, 256, 320, 5, 3),        # ranks that are not multiples of 8
+    (200, 640, 384, 0, 0),       # odd 128-step counts both ways (padded step), no ranks
+    (200, 640, 384, 16, 8),      # the same with rank steps
 ])
 def test_ragged_shapes_full(shape):
     M, K, N, rs, rl = shape
