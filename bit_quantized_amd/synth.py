@@ -136,6 +136,43 @@ def flux_linear_case(name: str, M: int, K: int, N: int, r_s: int, r_l: int,
                       meta={"seed": seed, "x_kind": x_kind})
 
 
+def outlier_weight_cases(seed: int = 5, M: int = 128, K: int = 256, N: int = 256,
+                         r_s: int = 16, n_out: int = 4, out_scale: float = 8.0):
+    """The stabilizer ablation: one weight, quantized with and without it.
+
+    W = N(0, 0.02) + sum of n_out rank-1 terms out_scale * u e_c^T, each on
+    one input channel c (u a random unit vector): a few weight columns carry
+    entries ~25x the rest, as outlier channels do.  X ~ N(0,1) with 2 input
+    channels x40, dY ~ 1e-3 N(0,1).  Returns (with, without): `with` keeps
+    the top-r_s SVD of W as the stabilizer (L1, L2) and quantizes only the
+    residual; `without` quantizes W itself (r_s = 0).  Neither has an
+    adapter.  meta["W"] is W in bf16, the weight both stand for.
+    """
+    rng = np.random.Generator(np.random.PCG64(seed))
+    X = to_bf16_bits(_outlier_channels(rng, _normal(rng, (M, K)), 2, 40.0))
+    W = 0.02 * rng.standard_normal((N, K))
+    for c in rng.choice(K, n_out, replace=False):
+        u = rng.standard_normal(N)
+        W[:, c] += out_scale * u / np.linalg.norm(u)
+    dY = to_bf16_bits(_normal(rng, (M, N), 1e-3))
+    Wb = to_bf16_bits(W)
+    Wf = bf16_bits_to_f32(Wb).astype(np.float64)
+    Uw, Sw, Vwt = np.linalg.svd(Wf, full_matrices=False)
+    sq = np.sqrt(Sw[:r_s])
+    L1 = to_bf16_bits(Vwt[:r_s].T * sq)                            # [K, r_s]
+    L2 = to_bf16_bits(sq[:, None] * Uw[:, :r_s].T)                 # [r_s, N]
+    W_res = to_bf16_bits(Wf - (bf16_bits_to_f32(L1).astype(np.float64)
+                               @ bf16_bits_to_f32(L2).astype(np.float64)).T)
+    noA = np.zeros((K, 0), np.uint16)
+    noB = np.zeros((0, N), np.uint16)
+    meta = {"seed": seed, "W": Wb}
+    with_stab = LinearCase("outlier_w_stab", M, K, N, r_s, 0, X, W_res, L1, L2, noA, noB, dY,
+                           meta=dict(meta))
+    without = LinearCase("outlier_w_nostab", M, K, N, 0, 0, X, Wb, np.zeros((K, 0), np.uint16),
+                         np.zeros((0, N), np.uint16), noA, noB, dY, meta=dict(meta))
+    return with_stab, without
+
+
 def qkv_case(seed: int = 1) -> LinearCase:
     """FLUX fused QKV projection: 4608 tokens, 3072 -> 9216, r_s=32, r_l=16."""
     return flux_linear_case("qkv_4608x3072x9216", 4608, 3072, 9216, 32, 16, seed)
