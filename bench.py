@@ -49,7 +49,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-stress", action="store_true")
     ap.add_argument("--no-mlp", action="store_true")
-    ap.add_argument("--only", choices=["step", "stress", "mlp"], default=None,
+    ap.add_argument("--no-fusion", action="store_true")
+    ap.add_argument("--only", choices=["step", "stress", "mlp", "fusion"], default=None,
                     help="run only one part (for profiler runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain bf16 elementwise copy of known size (the reference "
@@ -466,6 +467,81 @@ def main():
             "kernel_avg_us_both_linears": per}
         log("bench: mlp", json.dumps(out["mlp_pair"]))
         del msets
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ fusion breakdown
+    # The same QKV step with the low-rank branches unfused: the library's
+    # 4-bit path without ranks (quantize + 4-bit GEMM, forward and dgrad) and
+    # each low-rank product as a separate bf16 matrix product, each branch sum
+    # as a separate elementwise add.  Against the fused step this is the
+    # "LoRA fusion" factor of the pages' fusion breakdown (section 4, Fig. 9).
+    if not a.no_fusion and a.only in (None, "fusion"):
+        c = synth.qkv_case()
+        M, K, N, rs, rl = c.M, c.K, c.N, c.r_s, c.r_l
+        log(f"bench: fusion breakdown, QKV linear M={M} K={K} N={N} r_s={rs} r_l={rl}")
+        up = lambda x: bf16_tensor(x, dev)
+        bt = lambda *sh: torch.empty(sh, dtype=torch.bfloat16, device=dev)
+        fsets = []
+        for s_ in range(2):
+            X = torch.roll(up(c.X), 97 * s_, 0).contiguous()
+            dY = torch.roll(up(c.dY), 97 * s_, 0).contiguous()
+            W = torch.roll(up(c.W_res), 32 * s_, 0).contiguous()
+            L1, L2, A, B = up(c.L1), up(c.L2), up(c.A), up(c.B)
+            fused = QuantizedLinear.from_factors(W, L1, L2, A, B)
+            plain = QuantizedLinear.from_factors(W, None, None, None, None)
+            del W
+            D = torch.cat([L1, A], 1).contiguous()          # [K, R]
+            V = torch.cat([L2, B], 0).contiguous()          # [R, N]
+            b = dict(X=X, dY=dY, D=D, V=V, Dt=D.t().contiguous(), Vt=V.t().contiguous(),
+                     U=bt(M, rs + rl), Y=bt(M, N), T=bt(M, N), dX=bt(M, K), T2=bt(M, K),
+                     P=bt(M, rs + rl), dA=bt(rl, K), dB=bt(rl, N), dAk=bt(K, rl))
+            ws = (fused.workspace(M, False), fused.workspace(M, True),
+                  plain.workspace(M, False), plain.workspace(M, True))
+            fsets.append((fused, plain, b, ws))
+        torch.cuda.synchronize()
+
+        def fused_step(i):
+            fused, _, b, (wf, wb, _, _) = fsets[i % 2]
+            d = fused.desc(M)
+            ops.fourtune_linear_fwd(d, b["X"], b["Y"], b["U"], None, None, wf, wf.numel(), stream)
+            ops.fourtune_linear_bwd(d, b["dY"], b["X"], b["U"], None, b["dX"], b["dA"], b["dB"],
+                                    ops.FT_BF16, None, None, None, wb, wb.numel(), stream)
+
+        def unfused_step(i):
+            _, plain, b, (_, _, pf, pb) = fsets[i % 2]
+            d = plain.desc(M)
+            ops.fourtune_linear_fwd(d, b["X"], b["Y"], None, None, None, pf, pf.numel(), stream)
+            torch.matmul(b["X"], b["D"], out=b["U"])                       # U = X [L1|A]
+            torch.matmul(b["U"], b["V"], out=b["T"])                       # U [L2;B]
+            b["Y"].add_(b["T"])
+            ops.fourtune_linear_bwd(d, b["dY"], b["X"], None, None, b["dX"], None, None,
+                                    ops.FT_BF16, None, None, None, pb, pb.numel(), stream)
+            torch.matmul(b["dY"], b["Vt"], out=b["P"])                     # P = dY [L2;B]^T
+            torch.matmul(b["P"], b["Dt"], out=b["T2"])                     # P [L1|A]^T
+            b["dX"].add_(b["T2"])
+            torch.matmul(b["X"].t(), b["P"][:, rs:], out=b["dAk"])         # dA = X^T (dY B^T)
+            torch.matmul(b["U"][:, rs:].t(), b["dY"], out=b["dB"])         # dB = (X A)^T dY
+
+        res = {}
+        nst = max(5, a.steps // 5)
+        for name, fn in (("fused_us", fused_step), ("unfused_us", unfused_step)):
+            for i in range(3):
+                fn(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(nst):
+                fn(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            res[name] = round(e0.elapsed_time(e1) / nst * 1e3, 1)
+        out["fusion_breakdown"] = {
+            "workload": f"QKV linear fwd+bwd, {M} tokens, {K}->{N}, r_stab={rs}, r_lora={rl}",
+            "unfused": "library 4-bit quantize + GEMM without ranks; low-rank products as separate "
+                       "bf16 matrix products (torch / hipBLASLt) and separate elementwise adds",
+            **res, "lora_fusion_speedup": round(res["unfused_us"] / res["fused_us"], 3), "steps": nst}
+        log("bench: fusion", json.dumps(out["fusion_breakdown"]))
+        del fsets
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ quantizer stress
