@@ -584,14 +584,19 @@ def main():
                                             stream)
         q_w = lambda: ops.fourtune_quantize(ops.FT_Q_TILE32, W, wn, wn, wn, cw, sw, None, None,
                                             stream)
+        cwt = torch.empty((wn, wn // 2), dtype=u8, device=dev)
+        swt = torch.empty((wn // 32, wn // 32), dtype=u8, device=dev)
+        q_w2 = lambda: ops.fourtune_quantize(ops.FT_Q_TILE32, W, wn, wn, wn, cw, sw, cwt, swt,
+                                             stream)
         q_r = lambda: ops.fourtune_quantize(ops.FT_Q_ROW32, T, rows, cols, cols, c1, s1, None,
                                             None, stream)
-        q_t(); q_w(); q_r()
+        q_t(); q_w(); q_w2(); q_r()
         torch.cuda.synchronize()
         res = {}
         for name, fn, nbytes in (
                 ("quant_row32_t", q_t, rows * cols * (2 + 2 * (0.5 + 1 / 32))),
                 ("quant_tile32", q_w, wn * wn * (2 + 0.5 + 1 / 1024)),
+                ("quant_tile32_both_layouts", q_w2, wn * wn * (2 + 2 * (0.5 + 1 / 1024))),
                 ("quant_row32", q_r, rows * cols * (2 + 0.5 + 1 / 32))):
             med, mn = timed(fn)
             res[name] = {"median_us": round(med, 2), "min_us": round(mn, 2),

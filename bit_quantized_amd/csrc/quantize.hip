@@ -148,7 +148,8 @@ __global__ __launch_bounds__(256) void k_quant_tile32(const uint16_t* __restrict
   uint32_t o[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) o[i] = encode8(v[i][0], v[i][1], v[i][2], v[i][3], sc);
-  // streaming (non-temporal) stores: weights are quantized once, ahead of use
+  // streaming (non-temporal) stores of whole 128-byte code lines: weights
+  // are quantized once, ahead of use
   const auto rcodes = make_rsrc(codes, static_cast<uint64_t>(rows) * (cols >> 1));
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -174,8 +175,11 @@ __global__ __launch_bounds__(256) void k_quant_tile32(const uint16_t* __restrict
     const u32x2 lo = lds_read_tr4(&ct[q * CT_P + cg * 8]);
     const u32x2 hi = lds_read_tr4(&ct[(16 + q) * CT_P + cg * 8]);
     const uint32_t c = x * 512 + cg * 16 + q;
+    // cached: each 16-byte piece is an eighth of a 128-byte line that other
+    // workgroups complete, and only L2 merges them (non-temporal partial
+    // lines measured 3x slower)
     __builtin_amdgcn_raw_buffer_store_b128(u32x4{lo[0], lo[1], hi[0], hi[1]}, rcodes_t,
-                                           static_cast<int>(c < cols ? c * (rows >> 1) + y * 16 : BUF_OOB), 0, 2);
+                                           static_cast<int>(c < cols ? c * (rows >> 1) + y * 16 : BUF_OOB), 0, 0);
   }
 }
 
