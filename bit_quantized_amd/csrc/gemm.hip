@@ -36,7 +36,12 @@
 //     that refill a stage are spread between the MFMAs.
 //   - Even and odd steps use separate fragment and scale registers, so that
 //     no LDS read or VALU result ever targets a register an MFMA still in
-//     flight reads (such writes stall the wave until the MFMA is done).
+//     flight reads (such writes stall the wave until the MFMA is done).  An
+//     odd number of reduction steps is padded by one all-zero step, so every
+//     tile has an even number.
+//   - No register spills: a spilled value's reload waits for all memory
+//     operations (vmcnt(0)) and so drains the load pipeline; lane-dependent
+//     offsets used rarely are rebuilt where they are used instead.
 //   - Scales: one E8M0 byte per 32-block; a lane passes the word holding the
 //     bytes of its row and the step's blocks and selects the byte with
 //     op_sel.
