@@ -50,7 +50,8 @@ def parse():
     ap.add_argument("--no-stress", action="store_true")
     ap.add_argument("--no-mlp", action="store_true")
     ap.add_argument("--no-fusion", action="store_true")
-    ap.add_argument("--only", choices=["step", "stress", "mlp", "fusion"], default=None,
+    ap.add_argument("--no-block", action="store_true")
+    ap.add_argument("--only", choices=["step", "stress", "mlp", "fusion", "block"], default=None,
                     help="run only one part (for profiler runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain bf16 elementwise copy of known size (the reference "
@@ -542,6 +543,67 @@ def main():
             **res, "lora_fusion_speedup": round(res["unfused_us"] / res["fused_us"], 3), "steps": nst}
         log("bench: fusion", json.dumps(out["fusion_breakdown"]))
         del fsets
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ DiT block
+    # Every linear of one double-stream DiT block at batch 2: per stream QKV,
+    # out-projection and the MLP pair (GELU glue), plus the modulation linear
+    # at M = 2; forward of all, then backward of all.  Inputs are drawn on the
+    # device (the kernels' timing does not depend on the values).
+    if not a.no_block and a.only in (None, "block"):
+        rs_, rl_ = 32, 16
+        g = torch.Generator(device=dev)
+        g.manual_seed(6)
+        rnd = lambda *sh, sc=1.0: (torch.randn(sh, generator=g, device=dev) * sc).to(torch.bfloat16)
+        bt = lambda *sh: torch.empty(sh, dtype=torch.bfloat16, device=dev)
+        blk, bflop = [], 0
+        for name, Mb, Kb, Nb in synth.dit_block_linears():
+            act_in = ops.FT_ACT_GELU_TANH if name.endswith("fc2") else ops.FT_ACT_NONE
+            act_out = ops.FT_ACT_GELU_TANH if name.endswith("fc1") else ops.FT_ACT_NONE
+            lay = QuantizedLinear.from_factors(rnd(Nb, Kb, sc=0.02), rnd(Kb, rs_, sc=0.1),
+                                               rnd(rs_, Nb, sc=0.1), rnd(Kb, rl_, sc=0.01),
+                                               rnd(rl_, Nb, sc=0.01), act_in=act_in, act_out=act_out)
+            blk.append(dict(name=name, M=Mb, lay=lay, X=rnd(Mb, Kb), dY=rnd(Mb, Nb, sc=1e-3),
+                            Y=bt(Mb, Nb), U=bt(Mb, rs_ + rl_), dX=bt(Mb, Kb), dA=bt(rl_, Kb),
+                            dB=bt(rl_, Nb), wf=lay.workspace(Mb, False), wb=lay.workspace(Mb, True)))
+            bflop += sum(v["flop"] for v in layer_work(Mb, Kb, Nb, rs_, rl_).values())
+        by = {e["name"]: e for e in blk}
+        for st_ in ("img", "txt"):          # fc2 reads fc1's output h; fc1's gradient is fc2's dX
+            by[st_ + "_fc2"]["X"] = by[st_ + "_fc1"]["Y"]
+            by[st_ + "_fc1"]["dY"] = by[st_ + "_fc2"]["dX"]
+        torch.cuda.synchronize()
+
+        def block_step():
+            for e in blk:
+                d = e["lay"].desc(e["M"])
+                ops.fourtune_linear_fwd(d, e["X"], e["Y"], e["U"], None, None, e["wf"], e["wf"].numel(),
+                                        stream)
+            for e in reversed(blk):
+                d = e["lay"].desc(e["M"])
+                H = by[e["name"][:4] + "fc1"]["Y"] if e["name"].endswith("fc1") else None
+                ops.fourtune_linear_bwd(d, e["dY"], e["X"], e["U"], H, e["dX"], e["dA"], e["dB"],
+                                        ops.FT_BF16, None, None, None, e["wb"], e["wb"].numel(), stream)
+
+        for _ in range(2):
+            block_step()
+        torch.cuda.synchronize()
+        nst = max(3, a.steps // 10)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(nst):
+            block_step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        bms = e0.elapsed_time(e1) / nst
+        out["dit_block"] = {
+            "workload": "all linears of one double-stream DiT block at batch 2, fwd+bwd: per stream "
+                        "(image 8192 tokens, text 1024) QKV 3072->9216, out-projection 3072->3072, "
+                        "MLP 3072->12288->GELU->3072, and the modulation linear 3072->18432 at M=2; "
+                        "r_stab=32, r_lora=16",
+            "us_per_step": round(bms * 1e3, 1), "TFLOP/s": round(bflop / (bms * 1e-3) / 1e12, 1),
+            "step_flop": bflop, "steps": nst}
+        log("bench: block", json.dumps(out["dit_block"]))
+        del blk, by
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ quantizer stress
