@@ -159,7 +159,9 @@ size_t fourtune_workspace_bytes(const ft_linear* L, int is_bwd);
  *   them in the workspace.
  * workspace: device memory of at least fourtune_workspace_bytes(L, 0) bytes;
  *   contents on entry are ignored and on return unspecified.
- * Requirements: M >= 1, K % 32 == 0, N % 32 == 0, R <= 64.
+ * Requirements: M >= 1, K % 32 == 0, N % 32 == 0, R <= 64, and every
+ *   activation padded to 256 more rows below 2^31 bytes:
+ *   (M + 256) * max(K, N) * 2 < 2^31 (the kernels use 32-bit offsets).
  * Errors: FT_EINVAL, FT_ESHAPE, FT_EALIGN, FT_EWORKSPACE, FT_EDEVICE. */
 ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y,
                               uint16_t* U_save, uint8_t* xq_codes, uint8_t* xq_scales,
@@ -167,13 +169,16 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
 
 /* Backward, Eq. (3) and the adapter gradients of section 3.2:
  *   kernel 1 reads dY once and writes Qrow(dY) (1x32 blocks along N, the
- *   reduction dimension of the input gradient) and P = bf16(dY V^T);
+ *   reduction dimension of the input gradient) and P = bf16(dY V^T); for
+ *   r_lora <= 32 it also makes per-workgroup partial sums of dB from the dY
+ *   it holds, so dY is read once for the whole backward;
  *   kernel 2 computes deq(Qrow(dY)) deq(Qtile(W_res)) + P D^T from the
  *   32x32-tile codes in transposed order (wt_codes, wt_scales) and writes dX
  *   (bf16 [M, K]) once;
  *   kernel 3 writes the adapter gradients, rank-major like At and B:
  *   dA^T = P[:, r_stab:]^T X ([r_lora, K]) and dB = U[:, r_stab:]^T dY
- *   ([r_lora, N]), in grad_dtype (FT_BF16 or FT_F32).
+ *   ([r_lora, N]), in grad_dtype (FT_BF16 or FT_F32); every partial sum is
+ *   added in a fixed order, so the gradients are deterministic.
  * X and U_save are the forward's input and saved U.  H: bf16 [M, N], this
  * layer's forward output Y; required when act_out != FT_ACT_NONE (then the
  * incoming gradient is dY * act_out'(H), recomputed wherever it is read),
@@ -185,6 +190,7 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
  * gq_codes, gq_scales: optional outputs [M, N/2], [M, N/32].
  * workspace: at least fourtune_workspace_bytes(L, 1) bytes.
  * No gradient is produced for W_res, L1 or L2 (frozen).
+ * Requirements: as for the forward.
  * Errors: FT_EINVAL, FT_ESHAPE, FT_EALIGN, FT_EWORKSPACE, FT_EDEVICE. */
 ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint16_t* X,
                               const uint16_t* U_save, const uint16_t* H, uint16_t* dX, void* dA,

@@ -81,6 +81,11 @@ def test_linear_shape_errors():
         assert _fwd(L) == ops.FT_ESHAPE
         assert _bwd(L) == ops.FT_ESHAPE
     assert ops.lib().fourtune_linear_fwd(None, A16, A16, A16, None, None, A16, 1, None) == ops.FT_EINVAL
+    # within M * K * 2 < 2^31, but not once padded by 256 rows
+    M = (2 ** 31 - 1) // 64
+    assert M * 32 * 2 < 2 ** 31 and (M + 256) * 32 * 2 >= 2 ** 31
+    assert _fwd(_layer(M=M, K=32, N=32)) == ops.FT_ESHAPE
+    assert _bwd(_layer(M=M, K=32, N=32)) == ops.FT_ESHAPE
 
 
 def test_linear_pointer_errors():
