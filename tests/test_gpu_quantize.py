@@ -12,7 +12,7 @@ from _gpu import DEV, require_gpu, say, u8, up
 pytestmark = pytest.mark.gpu
 
 
-def _run(mode, bits, ld=None):
+def _run(mode, bits, ld=None, dual=False):
     rows, cols = bits.shape
     if ld is not None and ld != cols:
         padded = np.zeros((rows, ld), dtype=np.uint16)
@@ -30,6 +30,9 @@ def _run(mode, bits, ld=None):
     if mode == ops.FT_Q_ROW32_T:
         ct = torch.empty((cols, rows // 2), dtype=torch.uint8, device=DEV)
         st = torch.empty((cols, rows // 32), dtype=torch.uint8, device=DEV)
+    elif dual:
+        ct = torch.empty((cols, rows // 2), dtype=torch.uint8, device=DEV)
+        st = torch.empty((cols // 32, rows // 32), dtype=torch.uint8, device=DEV)
     ops.fourtune_quantize(mode, x, rows, cols, ld, c, s, ct, st)
     torch.cuda.synchronize()
     return u8(c), u8(s), (u8(ct) if ct is not None else None), (u8(st) if st is not None else None)
@@ -79,18 +82,25 @@ def test_row32_every_bf16_value_at_every_scale_regime():
     np.testing.assert_array_equal(c, ec)
 
 
-@pytest.mark.parametrize("shape", [(32, 32), (96, 160), (64, 416), (128, 4096)])
-def test_tile32(shape):
+@pytest.mark.parametrize("dual", [False, True])
+@pytest.mark.parametrize("shape", [(32, 32), (96, 160), (64, 416), (128, 4096), (320, 544)])
+def test_tile32(shape, dual):
     rng = np.random.default_rng(shape[1])
     w = synth.to_bf16_bits(rng.standard_normal(shape) * 0.02 *
                            np.exp2(rng.integers(-10, 10, (shape[0] // 32, 1, shape[1] // 32, 1)))
                            .repeat(32, 1).repeat(32, 3).reshape(shape))
     w[:32, :32] = 0            # an all-zero tile
-    say("tile32", shape)
-    c, s, _, _ = _run(ops.FT_Q_TILE32, w)
+    say("tile32", shape, "dual" if dual else "")
+    c, s, ct, st = _run(ops.FT_Q_TILE32, w, dual=dual)
     ec, es = OQ.quantize_tile32(w)
     np.testing.assert_array_equal(s, es)
     np.testing.assert_array_equal(c, ec)
+    if dual:
+        # a 32x32 tile's scale does not depend on the orientation, so the
+        # transposed codes are the tile quantization of the transpose
+        ect, est = OQ.quantize_tile32(np.ascontiguousarray(w.T))
+        np.testing.assert_array_equal(st, est)
+        np.testing.assert_array_equal(ct, ect)
 
 
 def test_tile32_adversarial():
