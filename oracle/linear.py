@@ -30,12 +30,30 @@ Readings where the pages are silent: U and P are rounded to bf16 (the
 low-rank products run as bf16 matrix products with bf16 outputs); every sum
 is accumulated exactly enough in float64 and rounded once to the output
 dtype (bf16 by default).
+
+Precision settings ("4.3 Ablation Study", "Impact of Precision
+Configurations", Table 4): W4A4G4 is the method above; A16 keeps the
+forward's activation in bf16 in the backbone product (Y's first term reads
+X itself instead of deq(Q_row32(X))), G16 keeps the incoming gradient in
+bf16 in the input-gradient product (dX's first term reads dY itself).  The
+weight stays 4-bit (deq(Q_tile32(W_res))) in all four; the low-rank
+branches and the adapter gradients do not change.  The pages name the four
+settings only; this reading is the plain one of their labels (W, A, G the
+bit widths of weight, activation and gradient in the backbone products).
 """
+
 from __future__ import annotations
 
 import numpy as np
 
 from . import mxfp4 as q
+
+PRECISIONS = ("W4A4G4", "W4A16G4", "W4A4G16", "W4A16G16")
+
+
+def _check_precision(precision: str) -> None:
+    if precision not in PRECISIONS:
+        raise ValueError(precision)
 
 
 def _round_out(x: np.ndarray, out_dtype: str) -> np.ndarray:
@@ -72,15 +90,21 @@ def down_proj(x_bits: np.ndarray, D: np.ndarray) -> np.ndarray:
     return q.f64_to_bf16_bits(q.bf16_bits_to_f64(x_bits) @ D)
 
 
-def linear_fwd(X, w_codes, w_scales, L1, L2, A, B, out_dtype="bf16"):
+def linear_fwd(X, w_codes, w_scales, L1, L2, A, B, out_dtype="bf16", precision="W4A4G4"):
     """Forward of the triple-branch linear.
 
     Inputs are bf16 bit arrays except w_codes / w_scales, the 32x32-tile
     MXFP4 form of W_res.  Returns dict with Y (out_dtype), U (bf16 bits
-    [M, R]), and the activation codes/scales (row32 of X).
+    [M, R]), and the activation codes/scales (row32 of X; None under A16,
+    which does not quantize X).
     """
-    xq_codes, xq_scales = q.quantize_row32(X)
-    Xh = q.dequantize_row32(xq_codes, xq_scales)          # [M, K]
+    _check_precision(precision)
+    if "A16" in precision:
+        xq_codes = xq_scales = None
+        Xh = q.bf16_bits_to_f64(X)
+    else:
+        xq_codes, xq_scales = q.quantize_row32(X)
+        Xh = q.dequantize_row32(xq_codes, xq_scales)      # [M, K]
     Wh = q.dequantize_tile32(w_codes, w_scales)           # [N, K]
     U = down_proj(X, stack_down(L1, A))                   # [M, R] bf16
     Y = Xh @ Wh.T + q.bf16_bits_to_f64(U) @ stack_up(L2, B)
@@ -88,15 +112,21 @@ def linear_fwd(X, w_codes, w_scales, L1, L2, A, B, out_dtype="bf16"):
 
 
 def linear_bwd(dY, X, U, w_codes, w_scales, L1, L2, A, B, out_dtype="bf16",
-               grad_dtype="bf16"):
+               grad_dtype="bf16", precision="W4A4G4"):
     """Backward of the triple-branch linear (straight-through Q).
 
     U is the forward's saved bf16(X D).  Returns dict with dX, dA, dB, P and
-    the gradient codes/scales (row32 of dY, blocks along N).
+    the gradient codes/scales (row32 of dY, blocks along N; None under G16,
+    which does not quantize dY).
     """
+    _check_precision(precision)
     r_s = np.asarray(L1).shape[1]
-    gq_codes, gq_scales = q.quantize_row32(dY)
-    Gh = q.dequantize_row32(gq_codes, gq_scales)          # [M, N]
+    if "G16" in precision:
+        gq_codes = gq_scales = None
+        Gh = q.bf16_bits_to_f64(dY)
+    else:
+        gq_codes, gq_scales = q.quantize_row32(dY)
+        Gh = q.dequantize_row32(gq_codes, gq_scales)      # [M, N]
     Wh = q.dequantize_tile32(w_codes, w_scales)           # [N, K]
     V = stack_up(L2, B)                                    # [R, N]
     P = down_proj(dY, V.T)                                 # [M, R] bf16
@@ -110,26 +140,34 @@ def linear_bwd(dY, X, U, w_codes, w_scales, L1, L2, A, B, out_dtype="bf16",
             "gq_codes": gq_codes, "gq_scales": gq_scales}
 
 
-def linear_fwd_rows(rows, X, w_codes, w_scales, L1, L2, A, B):
+def linear_fwd_rows(rows, X, w_codes, w_scales, L1, L2, A, B, precision="W4A4G4"):
     """Float64 forward outputs (Y before rounding, U) for selected rows only.
 
     Each row of the layer depends only on the same row of X, so large
     layers can be checked on a sample of rows.
     """
+    _check_precision(precision)
     Xs = np.asarray(X)[rows]
-    xq_codes, xq_scales = q.quantize_row32(Xs)
-    Xh = q.dequantize_row32(xq_codes, xq_scales)
+    if "A16" in precision:
+        Xh = q.bf16_bits_to_f64(Xs)
+    else:
+        xq_codes, xq_scales = q.quantize_row32(Xs)
+        Xh = q.dequantize_row32(xq_codes, xq_scales)
     Wh = q.dequantize_tile32(w_codes, w_scales)
     U = down_proj(Xs, stack_down(L1, A))
     Y = Xh @ Wh.T + q.bf16_bits_to_f64(U) @ stack_up(L2, B)
     return Y, U
 
 
-def linear_bwd_rows(rows, dY, w_codes, w_scales, L1, L2, A, B):
+def linear_bwd_rows(rows, dY, w_codes, w_scales, L1, L2, A, B, precision="W4A4G4"):
     """Float64 dX before rounding, and P, for selected rows only."""
+    _check_precision(precision)
     Gs = np.asarray(dY)[rows]
-    gq_codes, gq_scales = q.quantize_row32(Gs)
-    Gh = q.dequantize_row32(gq_codes, gq_scales)
+    if "G16" in precision:
+        Gh = q.bf16_bits_to_f64(Gs)
+    else:
+        gq_codes, gq_scales = q.quantize_row32(Gs)
+        Gh = q.dequantize_row32(gq_codes, gq_scales)
     Wh = q.dequantize_tile32(w_codes, w_scales)
     P = down_proj(Gs, stack_up(L2, B).T)
     dX = Gh @ Wh + q.bf16_bits_to_f64(P) @ stack_down(L1, A).T

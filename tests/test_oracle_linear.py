@@ -7,6 +7,9 @@
 * branch structure: zero ranks, zero residual;
 * the adjoint identity of the backbone product;
 * autograd on random inputs within bf16 rounding error;
+* the precision settings of Table 4: exact agreement with autograd where
+  the 16-bit side reads its input unquantized, disagreement where a 4-bit
+  side rounds a lossy block;
 * GELU against torch's float64 tanh-GELU and its autograd.
 """
 from fractions import Fraction
@@ -59,6 +62,66 @@ def test_exact_against_autograd_on_ternary_inputs(shape):
     np.testing.assert_array_equal(bwd["dX"], dX)
     np.testing.assert_array_equal(bwd["dA"], dA)
     np.testing.assert_array_equal(bwd["dB"], dB)
+
+
+@pytest.mark.parametrize("precision", L.PRECISIONS)
+def test_precision_settings_exact_on_lossless_inputs(precision):
+    # On ternary inputs Q(X) = X and Q(dY) = dY, so every precision setting
+    # gives the same exact result as the plain layer's autograd.
+    c = _case_ternary(11, 8, 64, 96, 4, 3)
+    wc, ws = q.quantize_tile32(c["W"])
+    fwd = L.linear_fwd(c["X"], wc, ws, c["L1"], c["L2"], c["A"], c["B"], out_dtype="f64",
+                       precision=precision)
+    bwd = L.linear_bwd(c["dY"], c["X"], fwd["U"], wc, ws, c["L1"], c["L2"], c["A"], c["B"],
+                       out_dtype="f64", grad_dtype="f64", precision=precision)
+    Y, dX, dA, dB = _autograd(c)
+    np.testing.assert_array_equal(fwd["Y"], Y)
+    np.testing.assert_array_equal(bwd["dX"], dX)
+    np.testing.assert_array_equal(bwd["dA"], dA)
+    np.testing.assert_array_equal(bwd["dB"], dB)
+    assert (fwd["xq_codes"] is None) == ("A16" in precision)
+    assert (bwd["gq_codes"] is None) == ("G16" in precision)
+
+
+@pytest.mark.parametrize("precision", L.PRECISIONS)
+def test_precision_settings_on_lossy_integer_inputs(precision):
+    # X and dY are integers in [-7, 7]: a block holding a 7 is lossy under
+    # MXFP4 (scale 1, 7 rounds to 6), while the ternary weight stays exact.
+    # With K = N = 32 every sum is an integer below 2^8, so U and P are exact
+    # in bf16 and the plain layer's autograd is exact: a 16-bit side must
+    # equal it, a 4-bit side must not.
+    rng = np.random.default_rng(5)
+    M, K, N, r_s, r_l = 8, 32, 32, 2, 3
+    ints = lambda shape: synth.to_bf16_bits(rng.integers(-7, 8, size=shape).astype(np.float32))
+    c = dict(X=ints((M, K)), W=_ternary(rng, (N, K)), L1=_ternary(rng, (K, r_s)),
+             L2=_ternary(rng, (r_s, N)), A=_ternary(rng, (K, r_l)), B=_ternary(rng, (r_l, N)),
+             dY=ints((M, N)))
+    c["X"][:, 0] = synth.to_bf16_bits(np.float32(7.0))     # every block lossy
+    c["dY"][:, 0] = synth.to_bf16_bits(np.float32(-7.0))
+    wc, ws = q.quantize_tile32(c["W"])
+    fwd = L.linear_fwd(c["X"], wc, ws, c["L1"], c["L2"], c["A"], c["B"], out_dtype="f64",
+                       precision=precision)
+    bwd = L.linear_bwd(c["dY"], c["X"], fwd["U"], wc, ws, c["L1"], c["L2"], c["A"], c["B"],
+                       out_dtype="f64", grad_dtype="f64", precision=precision)
+    Y, dX, dA, dB = _autograd(c)
+    assert np.array_equal(fwd["Y"], Y) == ("A16" in precision)
+    assert np.array_equal(bwd["dX"], dX) == ("G16" in precision)
+    # the adapter gradients and the low-rank branches do not depend on it
+    np.testing.assert_array_equal(bwd["dA"], dA)
+    np.testing.assert_array_equal(bwd["dB"], dB)
+    base_f = L.linear_fwd(c["X"], wc, ws, c["L1"], c["L2"], c["A"], c["B"], out_dtype="f64")
+    base_b = L.linear_bwd(c["dY"], c["X"], base_f["U"], wc, ws, c["L1"], c["L2"], c["A"], c["B"],
+                          out_dtype="f64", grad_dtype="f64")
+    assert np.array_equal(fwd["Y"], base_f["Y"]) == ("A16" not in precision)
+    assert np.array_equal(bwd["dX"], base_b["dX"]) == ("G16" not in precision)
+    # row-sampled forms agree with the full ones
+    rows = np.array([0, 5, 7])
+    Yr, _ = L.linear_fwd_rows(rows, c["X"], wc, ws, c["L1"], c["L2"], c["A"], c["B"],
+                              precision=precision)
+    dXr, _ = L.linear_bwd_rows(rows, c["dY"], wc, ws, c["L1"], c["L2"], c["A"], c["B"],
+                               precision=precision)
+    np.testing.assert_array_equal(Yr, fwd["Y"][rows])
+    np.testing.assert_array_equal(dXr, bwd["dX"][rows])
 
 
 def test_against_autograd_random_inputs_within_bf16_error():
