@@ -146,6 +146,12 @@ ft_status check_linear(const ft_linear* L) {
       (L->act_out != FT_ACT_NONE && L->act_out != FT_ACT_GELU_TANH))
     return FT_EINVAL;
   if ((L->wt_codes == nullptr) != (L->wt_scales == nullptr)) return FT_EINVAL;
+  if (L->precision < FT_W4A4G4 || L->precision > FT_W4A16G16) return FT_EINVAL;
+  // a 16-bit product reads the weight dequantized to bf16, with 32-bit
+  // offsets over its padded rows
+  if (L->precision != FT_W4A4G4 &&
+      (std::max(L->K, L->N) + 256) * std::min(L->K, L->N) * 2 > kMaxBytes)
+    return FT_ESHAPE;
   if (L->r_stab > 0 && (!L->L1t || !L->L2)) return FT_EINVAL;
   if (L->r_lora > 0 && (!L->At || !L->B)) return FT_EINVAL;
   const void* ptrs[] = {L->w_codes, L->w_scales, L->wt_codes, L->wt_scales, L->L1t, L->L2, L->At, L->B};
@@ -154,16 +160,23 @@ ft_status check_linear(const ft_linear* L) {
   return FT_OK;
 }
 
+inline bool a16(const ft_linear* L) { return (L->precision & FT_W4A16G4) != 0; }
+inline bool g16(const ft_linear* L) { return (L->precision & FT_W4A4G16) != 0; }
+
 struct FwdLayout {
-  size_t xq_codes, xq_scales, u_pad, v_pad, part, total;
+  size_t xq_codes, xq_scales, u_pad, v_pad, part, w16, x16, total;
 };
 FwdLayout fwd_layout(const ft_linear* L) {
   const int R = L->r_stab + L->r_lora;
   const size_t rp = static_cast<size_t>(ft::rank_pad(R));
+  const bool bf = a16(L);
   FwdLayout o;
   size_t off = 0;
-  o.xq_codes = off; off += align_up(static_cast<size_t>(L->M) * (L->K / 2));
-  o.xq_scales = off; off += align_up(static_cast<size_t>(L->M) * (L->K / 32));
+  o.xq_codes = off; off += bf ? 0 : align_up(static_cast<size_t>(L->M) * (L->K / 2));
+  o.xq_scales = off; off += bf ? 0 : align_up(static_cast<size_t>(L->M) * (L->K / 32));
+  // A16: the weight in bf16 [N, K], and act_in(X) when there is an act_in
+  o.w16 = off; off += bf ? align_up(static_cast<size_t>(L->N) * L->K * 2) : 0;
+  o.x16 = off; off += bf && L->act_in != FT_ACT_NONE ? align_up(static_cast<size_t>(L->M) * L->K * 2) : 0;
   o.u_pad = off; off += align_up(static_cast<size_t>(L->M) * rp * 2);     // U, zero-padded ranks
   o.v_pad = off; off += align_up(static_cast<size_t>(L->N) * rp * 2);     // [L2^T | B^T], padded
   o.part = off; off += align_up(ft::quant_down_part_bytes(L->M, L->K, R, 0));
@@ -179,16 +192,21 @@ bool db_fused_in_quant(const ft_linear* L) {
 }
 
 struct BwdLayout {
-  size_t gq_codes, gq_scales, P, p_pad, d_pad, part, dA_part, dB_part, total;
+  size_t gq_codes, gq_scales, P, p_pad, d_pad, part, dA_part, dB_part, w16, g16, total;
 };
 BwdLayout bwd_layout(const ft_linear* L) {
   const int R = L->r_stab + L->r_lora;
   const int rl = L->r_lora;
   const size_t rp = static_cast<size_t>(ft::rank_pad(R));
+  const bool bf = g16(L);
   BwdLayout o;
   size_t off = 0;
-  o.gq_codes = off; off += align_up(static_cast<size_t>(L->M) * (L->N / 2));
-  o.gq_scales = off; off += align_up(static_cast<size_t>(L->M) * (L->N / 32));
+  o.gq_codes = off; off += bf ? 0 : align_up(static_cast<size_t>(L->M) * (L->N / 2));
+  o.gq_scales = off; off += bf ? 0 : align_up(static_cast<size_t>(L->M) * (L->N / 32));
+  // G16: the transposed weight in bf16 [K, N], and dY * act_out'(H) when
+  // there is an act_out
+  o.w16 = off; off += bf ? align_up(static_cast<size_t>(L->K) * L->N * 2) : 0;
+  o.g16 = off; off += bf && L->act_out != FT_ACT_NONE ? align_up(static_cast<size_t>(L->M) * L->N * 2) : 0;
   o.P = off; off += align_up(static_cast<size_t>(L->M) * R * 2);
   o.p_pad = off; off += align_up(static_cast<size_t>(L->M) * rp * 2);     // P, zero-padded ranks
   o.d_pad = off; off += align_up(static_cast<size_t>(L->K) * rp * 2);     // [L1 | A], padded
@@ -265,10 +283,26 @@ ft_status fourtune_quantize(int mode, const uint16_t* in, int64_t rows, int64_t 
   }
 }
 
+ft_status fourtune_dequantize(int mode, const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                              int64_t cols, uint16_t* out, void* stream) {
+  if (mode != FT_Q_TILE32) return FT_EINVAL;
+  if (!codes || !scales || !out) return FT_EINVAL;
+  if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return FT_ESHAPE;
+  if ((rows & 31) || (cols & 31)) return FT_ESHAPE;
+  if (rows * cols * 2 > kMaxBytes) return FT_ESHAPE;
+  if (!aligned16(codes) || !aligned16(scales) || !aligned16(out)) return FT_EALIGN;
+  if (rows == 0 || cols == 0) return FT_OK;
+  if (ft_status s = device_check(); s != FT_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  Timed tm("dequant_tile32", st);
+  return launched(tm.done(ft::launch_dequant_tile32(codes, scales, rows, cols, out, st)));
+}
+
 size_t fourtune_workspace_bytes(const ft_linear* L, int is_bwd) {
   if (!L || L->M < 1 || L->K < 32 || L->N < 32 || (L->K & 31) || (L->N & 31)) return 0;
   if (L->M > kMaxDim || L->K > kMaxDim || L->N > kMaxDim) return 0;
   if (L->r_stab < 0 || L->r_lora < 0 || L->r_stab + L->r_lora > FT_MAX_RANK) return 0;
+  if (L->precision < FT_W4A4G4 || L->precision > FT_W4A16G16) return 0;
   return is_bwd ? bwd_layout(L).total : fwd_layout(L).total;
 }
 
@@ -280,6 +314,7 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
   if (!X || !Y) return FT_EINVAL;
   if (R > 0 && !U_save) return FT_EINVAL;
   if ((xq_codes == nullptr) != (xq_scales == nullptr)) return FT_EINVAL;
+  if (a16(L) && xq_codes) return FT_EINVAL;
   const void* ptrs[] = {X, Y, U_save, xq_codes, xq_scales, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return FT_EALIGN;
@@ -290,22 +325,23 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint8_t* qc = xq_codes ? xq_codes : ws + lay.xq_codes;
-  uint8_t* qs = xq_scales ? xq_scales : ws + lay.xq_scales;
+  const bool bf = a16(L);
+  // A16: no codes; the quantize stores of kernel 1 are dropped
+  uint8_t* qc = bf ? nullptr : xq_codes ? xq_codes : ws + lay.xq_codes;
+  uint8_t* qs = bf ? nullptr : xq_scales ? xq_scales : ws + lay.xq_scales;
   uint16_t* u_pad = reinterpret_cast<uint16_t*>(ws + lay.u_pad);
   uint16_t* v_pad = reinterpret_cast<uint16_t*>(ws + lay.v_pad);
-  hipError_t e;
-  {
+  hipError_t e = hipSuccess;
+  // act_in: X is the pre-activation h; the layer's input is gelu(h)
+  const int act = L->act_in == FT_ACT_GELU_TANH ? 1 : 0;
+  if (R > 0) {
     Timed tm("fwd_quant_down", st);
-    // act_in: X is the pre-activation h; the layer's input is gelu(h)
-    const int act = L->act_in == FT_ACT_GELU_TANH ? 1 : 0;
-    if (R > 0)
-      e = ft::launch_quant_down(X, nullptr, act, L->M, L->K, L->K, qc, qs, rows_Dt(L), U_save, u_pad,
-                                rows_V(L), L->N, v_pad, reinterpret_cast<float*>(ws + lay.part),
-                                nullptr, st);
-    else
-      e = ft::launch_quant_row32(X, nullptr, act, L->M, L->K, L->K, qc, qs, st);
-    tm.done(e);
+    e = tm.done(ft::launch_quant_down(X, nullptr, act, L->M, L->K, L->K, qc, qs, rows_Dt(L), U_save,
+                                      u_pad, rows_V(L), L->N, v_pad,
+                                      reinterpret_cast<float*>(ws + lay.part), nullptr, st));
+  } else if (!bf) {
+    Timed tm("fwd_quant_down", st);
+    e = tm.done(ft::launch_quant_row32(X, nullptr, act, L->M, L->K, L->K, qc, qs, st));
   }
   if (e != hipSuccess) return FT_EDEVICE;
   ft::GemmArgs g{};
@@ -313,6 +349,22 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
   g.a_codes = qc; g.a_scales = qs;
   g.b_codes = L->w_codes; g.b_scales = L->w_scales;
   g.lm = u_pad; g.lo = v_pad; g.nlr = ft::rank_pad(R) / 32; g.out = Y;
+  if (bf) {
+    uint16_t* w16 = reinterpret_cast<uint16_t*>(ws + lay.w16);
+    {
+      Timed tm("fwd_dequant_w", st);
+      if (tm.done(ft::launch_dequant_tile32(L->w_codes, L->w_scales, L->N, L->K, w16, st)) != hipSuccess)
+        return FT_EDEVICE;
+    }
+    const uint16_t* x16 = X;
+    if (act) {
+      uint16_t* xa = reinterpret_cast<uint16_t*>(ws + lay.x16);
+      Timed tm("fwd_act", st);
+      if (tm.done(ft::launch_act(1, X, nullptr, L->M * L->K, xa, st)) != hipSuccess) return FT_EDEVICE;
+      x16 = xa;
+    }
+    g.a16 = x16; g.b16 = w16;
+  }
   Timed tm("fwd_gemm", st);
   return launched(tm.done(ft::launch_gemm(g, st)));
 }
@@ -331,6 +383,7 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
   if (rl > 0 && (!X || !U_save || !dA || !dB)) return FT_EINVAL;
   if (L->act_out != FT_ACT_NONE && !H) return FT_EINVAL;
   if ((gq_codes == nullptr) != (gq_scales == nullptr)) return FT_EINVAL;
+  if (g16(L) && gq_codes) return FT_EINVAL;
   const void* ptrs[] = {dY, X, U_save, H, dX, dA, dB, P_save, gq_codes, gq_scales, workspace};
   for (const void* p : ptrs)
     if (p && !aligned16(p)) return FT_EALIGN;
@@ -341,28 +394,29 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   uint8_t* ws = static_cast<uint8_t*>(workspace);
-  uint8_t* qc = gq_codes ? gq_codes : ws + lay.gq_codes;
-  uint8_t* qs = gq_scales ? gq_scales : ws + lay.gq_scales;
+  const bool bf = g16(L);
+  // G16: no codes; the quantize stores of kernel 1 are dropped
+  uint8_t* qc = bf ? nullptr : gq_codes ? gq_codes : ws + lay.gq_codes;
+  uint8_t* qs = bf ? nullptr : gq_scales ? gq_scales : ws + lay.gq_scales;
   uint16_t* P = P_save ? P_save : reinterpret_cast<uint16_t*>(ws + lay.P);
   uint16_t* p_pad = reinterpret_cast<uint16_t*>(ws + lay.p_pad);
   uint16_t* d_pad = reinterpret_cast<uint16_t*>(ws + lay.d_pad);
-  hipError_t e;
+  hipError_t e = hipSuccess;
   const bool db_fused = db_fused_in_quant(L);
   ft::DbFuse db{U_save, R, L->r_stab, rl, reinterpret_cast<float*>(ws + lay.dB_part)};
-  {
+  // act_out: dY is the gradient of gelu(Y) and H the saved Y; the incoming
+  // gradient of this layer is dY * gelu'(H)
+  const int act = L->act_out == FT_ACT_GELU_TANH ? 2 : 0;
+  const uint16_t* h2 = act ? H : nullptr;
+  if (R > 0) {
     Timed tm("bwd_quant_down", st);
-    // act_out: dY is the gradient of gelu(Y) and H the saved Y; the incoming
-    // gradient of this layer is dY * gelu'(H)
-    const int act = L->act_out == FT_ACT_GELU_TANH ? 2 : 0;
-    const uint16_t* h2 = act ? H : nullptr;
-    if (R > 0)
-      e = ft::launch_quant_down(dY, h2, act, L->M, L->N, L->N, qc, qs, rows_V(L), P, p_pad,
-                                rows_Dt(L), dX ? L->K : 0, d_pad,
-                                reinterpret_cast<float*>(ws + lay.part), db_fused ? &db : nullptr,
-                                st);
-    else
-      e = ft::launch_quant_row32(dY, h2, act, L->M, L->N, L->N, qc, qs, st);
-    tm.done(e);
+    e = tm.done(ft::launch_quant_down(dY, h2, act, L->M, L->N, L->N, qc, qs, rows_V(L), P, p_pad,
+                                      rows_Dt(L), dX ? L->K : 0, d_pad,
+                                      reinterpret_cast<float*>(ws + lay.part),
+                                      db_fused ? &db : nullptr, st));
+  } else if (!bf) {
+    Timed tm("bwd_quant_down", st);
+    e = tm.done(ft::launch_quant_row32(dY, h2, act, L->M, L->N, L->N, qc, qs, st));
   }
   if (e != hipSuccess) return FT_EDEVICE;
   if (dX) {
@@ -371,6 +425,22 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
     g.a_codes = qc; g.a_scales = qs;
     g.b_codes = L->wt_codes; g.b_scales = L->wt_scales;
     g.lm = p_pad; g.lo = d_pad; g.nlr = ft::rank_pad(R) / 32; g.out = dX;
+    if (bf) {
+      uint16_t* w16 = reinterpret_cast<uint16_t*>(ws + lay.w16);
+      {
+        Timed tm("bwd_dequant_w", st);
+        if (tm.done(ft::launch_dequant_tile32(L->wt_codes, L->wt_scales, L->K, L->N, w16, st)) != hipSuccess)
+          return FT_EDEVICE;
+      }
+      const uint16_t* g16p = dY;
+      if (act) {
+        uint16_t* ga = reinterpret_cast<uint16_t*>(ws + lay.g16);
+        Timed tm("bwd_act", st);
+        if (tm.done(ft::launch_act(2, H, dY, L->M * L->N, ga, st)) != hipSuccess) return FT_EDEVICE;
+        g16p = ga;
+      }
+      g.a16 = g16p; g.b16 = w16;
+    }
     Timed tm("bwd_gemm_dgrad", st);
     if (tm.done(ft::launch_gemm(g, st)) != hipSuccess) return FT_EDEVICE;
   }

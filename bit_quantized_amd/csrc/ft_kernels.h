@@ -64,6 +64,12 @@ size_t quant_down_part_bytes(int64_t rows, int64_t cols, int R, int rl_db);
 int quant_down_db_chunks(int64_t rows, int64_t cols, int rl);   // 0: dB is not fused for this rl
 size_t quant_down_db_bytes(int64_t rows, int64_t cols, int rl);
 
+// Dequantize 32x32-tile MXFP4 data to bf16: out [rows, cols] from codes
+// [rows, cols/2] and tile scales [rows/32, cols/32]; rows % 32 == 0,
+// cols % 32 == 0.
+hipError_t launch_dequant_tile32(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                 int64_t cols, uint16_t* out, hipStream_t st);
+
 // gemm.hip: out[m][j] = sum_red deq(a)[m][red] deq(b)[j][red] + sum_r lm[m][r] lo[j][r]
 // forward: a = Qrow(X) [M, K], b = Qtile(W) [N, K], lm = U, lo = [L2^T | B^T]
 // dgrad  : a = Qrow(dY) [M, N], b = Qtile(W)^T [K, N], lm = P, lo = [L1 | A]
@@ -78,6 +84,10 @@ struct GemmArgs {
   const uint16_t* lo;             // bf16 [NOUT, 32 * nlr]
   int nlr;                        // 32-rank groups: 0 or 2 (rank_pad)
   uint16_t* out;                  // bf16 [M, NOUT]
+  // bf16 main product instead of the 4-bit one (a16 set: codes and scales
+  // are not read): out = a16 b16^T + lm lo^T; RED % 32 == 0.
+  const uint16_t* a16;            // bf16 [M, RED]
+  const uint16_t* b16;            // bf16 [NOUT, RED]
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 

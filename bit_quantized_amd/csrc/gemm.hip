@@ -145,10 +145,13 @@ struct Frags {
 template <int K> struct MfmaKind { static constexpr int v = K; };   // 0: MXFP4, 1: bf16 ranks
 
 // LR: the tiles start with two rank steps (64 padded ranks).  An odd
-// number of reduction steps RED/128 is padded by one step whose loads are
-// pushed out of range: zero codes and zero scale bytes add exactly 0, and
-// every tile then has an even number of steps for the even/odd registers.
-template <bool LR>
+// number of reduction steps is padded by one step whose loads are pushed
+// out of range: zero codes and zero scale bytes add exactly 0, and every
+// tile then has an even number of steps for the even/odd registers.
+// BF: the main product is bf16 x bf16 (a16, b16): its steps are rank-kind
+// steps of 32 reduction elements (64 bytes of a row, as a 4-bit step), and
+// no scales are loaded.
+template <bool LR, bool BF>
 __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[NST * ST_BYTES + 4 * OUT_WAVE];
 
@@ -164,7 +167,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   const uint32_t full = ntiles / G, nlast = ntiles % G;
   const uint32_t my_tiles = full + (bid < nlast ? 1u : 0u);
   constexpr int NLR = LR ? 2 : 0;
-  const int nks_real = static_cast<int>(RED / BK);
+  const int nks_real = static_cast<int>(BF ? RED / 32 : RED / BK);
   const int nks = nks_real + (nks_real & 1);             // padded to even
   const int spt = nks + NLR;                             // steps per tile
   const int total = static_cast<int>(my_tiles) * spt;
@@ -176,13 +179,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
     tile_coords(k * G + xcd_remap(bid, n_round), mt_n, nt_n, m0, j0);
   };
 
-  const uint32_t row_bytes = static_cast<uint32_t>(RED >> 1);
+  const uint32_t row_bytes = static_cast<uint32_t>(BF ? RED * 2 : RED >> 1);
   const uint32_t row_sc = static_cast<uint32_t>(RED >> 5);
   constexpr uint32_t LR_BYTES = 64 * 2;                  // a padded rank row: 64 bf16
-  const auto ra_codes = rsrc(g.a_codes, static_cast<uint64_t>(M) * row_bytes);
-  const auto ra_sc = rsrc(g.a_scales, static_cast<uint64_t>(M) * row_sc);
-  const auto rb_codes = rsrc(g.b_codes, static_cast<uint64_t>(NOUT) * row_bytes);
-  const auto rb_sc = rsrc(g.b_scales, static_cast<uint64_t>(NOUT >> 5) * row_sc);
+  const auto ra_codes = rsrc(BF ? static_cast<const void*>(g.a16) : g.a_codes, static_cast<uint64_t>(M) * row_bytes);
+  const auto ra_sc = rsrc(g.a_scales, BF ? 0 : static_cast<uint64_t>(M) * row_sc);
+  const auto rb_codes = rsrc(BF ? static_cast<const void*>(g.b16) : g.b_codes, static_cast<uint64_t>(NOUT) * row_bytes);
+  const auto rb_sc = rsrc(g.b_scales, BF ? 0 : static_cast<uint64_t>(NOUT >> 5) * row_sc);
   const auto r_lm = rsrc(g.lm, LR ? static_cast<uint64_t>(M) * LR_BYTES : 0);
   const auto r_lo = rsrc(g.lo, LR ? static_cast<uint64_t>(NOUT) * LR_BYTES : 0);
 
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
     h.sc = is_b ? rb_sc : ra_sc;
     const bool pad = !lrs && ks >= nks_real;                 // the padding step
     h.base = (!live || pad) ? OOB : (lrs ? c.lr + static_cast<uint32_t>(c.s) * 64 : c.code + static_cast<uint32_t>(ks) * 64);
-    h.sbase = (!live || lrs || pad) ? OOB : c.sc + static_cast<uint32_t>(ks) * 4;
+    h.sbase = (BF || !live || lrs || pad) ? OOB : c.sc + static_cast<uint32_t>(ks) * 4;
     uint8_t* st = lds + (c.gs & (NST - 1)) * ST_BYTES;
     h.dst = st + (is_b ? ST_A : 0) + 64 * wave * ROWB;
     h.sdst = is_b ? st + ST_A + ST_B + ST_SA + wave * 256 : st + ST_A + ST_B + 64 * wave * 4;
@@ -501,13 +504,23 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
       step(E, O, rank, after);
       step(O, E, rank, after);
       for (int p = 0; p < nks / 2; ++p) {
-        step(E, O, fp4, false);
-        step(O, E, fp4, false);
+        if constexpr (BF) {
+          step(E, O, rank, false);
+          step(O, E, rank, false);
+        } else {
+          step(E, O, fp4, false);
+          step(O, E, fp4, false);
+        }
       }
     } else {
       for (int p = 0; p < nks / 2; ++p) {
-        step(E, O, fp4, after && p == 0);
-        step(O, E, fp4, after && p == 0);
+        if constexpr (BF) {
+          step(E, O, rank, after && p == 0);
+          step(O, E, rank, after && p == 0);
+        } else {
+          step(E, O, fp4, after && p == 0);
+          step(O, E, fp4, after && p == 0);
+        }
       }
     }
     int64_t m0, j0;
@@ -696,13 +709,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
 
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const uint32_t n = static_cast<uint32_t>(((g.NOUT + BN - 1) / BN) * ((g.M + BM - 1) / BM));
-  if ((g.RED & 127) == 0) {
+  const bool bf = g.a16 != nullptr;
+  if ((g.RED & 127) == 0 || (bf && (g.RED & 31) == 0)) {
     const int cus = cu_count();
     if (cus <= 0) return hipErrorInvalidDevice;
     const uint32_t grid = n < static_cast<uint32_t>(cus) ? n : static_cast<uint32_t>(cus);
-#define FT_GP(LR) hipLaunchKernelGGL((k_gemm_pipe<LR>), dim3(grid), dim3(256), 0, st, g)
-    if (g.nlr > 0) FT_GP(true); else FT_GP(false);
+#define FT_GP(LR, BF) hipLaunchKernelGGL((k_gemm_pipe<LR, BF>), dim3(grid), dim3(256), 0, st, g)
+    if (bf) {
+      if (g.nlr > 0) FT_GP(true, true); else FT_GP(false, true);
+    } else {
+      if (g.nlr > 0) FT_GP(true, false); else FT_GP(false, false);
+    }
 #undef FT_GP
+  } else if (bf) {
+    return hipErrorInvalidValue;
   } else {
     hipLaunchKernelGGL(k_gemm, dim3(n), dim3(256), 0, st, g);
   }

@@ -18,6 +18,7 @@
 //                     split over columns into fp32 partials          (HBM bound)
 //   k_rank_reduce     ordered sum of those partials, bf16 rounding, and
 //                     the padded rank operands of the 4-bit GEMM     (HBM bound)
+//   k_dequant_tile32  32x32-tile codes back to bf16 (16-bit products) (HBM bound)
 #include "ft_device.hpp"
 #include "ft_kernels.h"
 
@@ -563,8 +564,9 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
   __syncthreads();
   uint16_t* xw = xt[wave];
   const uint32_t cpr = cols >> 1, spr = cols >> 5;
-  const auto rcodes = make_rsrc(a.codes, static_cast<uint64_t>(rows) * cpr);
-  const auto rscales = make_rsrc(a.scales, static_cast<uint64_t>(rows) * spr);
+  // no codes wanted (a 16-bit product follows): empty buffers drop the stores
+  const auto rcodes = make_rsrc(a.codes, a.codes ? static_cast<uint64_t>(rows) * cpr : 0);
+  const auto rscales = make_rsrc(a.scales, a.scales ? static_cast<uint64_t>(rows) * spr : 0);
   const auto rpart = make_rsrc(a.part, static_cast<uint64_t>(gridDim.x / G) * nrb * 4 * NRG * 256 * 4);
   constexpr int NTW = NT / 4;                 // dB column tiles per wave
   f32x4 dacc[DBR > 0 ? DBR : 1][DBR > 0 ? NTW : 1];
@@ -775,6 +777,50 @@ __global__ __launch_bounds__(256) void k_rank_reduce(const RRArgs a) {
 // ---------------------------------------------------------------------------
 // host launchers
 
+// ---------------------------------------------------------------------------
+// 32x32-tile MXFP4 back to bf16, the weight operand of a 16-bit product.
+// Lane i takes 4 code bytes (8 values) of a row: a load instruction reads
+// 256 contiguous bytes, a store writes 1 KB of bf16.  Each value is built
+// directly as bf16 bits, exactly: an E2M1 magnitude m = 1..7 is 2^E (1 + f)
+// with E = m/2 - 1 and f = 1/2 for odd m > 1, so times the tile's 2^(s-127)
+// its bf16 exponent field is E + s; where that is below 1 the value is a bf16
+// subnormal, (2 + 2f) * 2^(E + s + 5) units of 2^-133 (a left shift, since
+// E + s >= -1); at 255 and above it is infinite (no finite weight gives a
+// scale that large).
+__device__ __forceinline__ uint32_t e2m1_to_bf16(uint32_t n, int s) {
+  const uint32_t m = n & 7u, sg = (n & 8u) << 12;
+  const int ex = static_cast<int>(m >> 1) - 1 + s;
+  const uint32_t f = m > 1u ? (m & 1u) : 0u;
+  const uint32_t normal = (static_cast<uint32_t>(ex) << 7) | (f << 6);
+  const uint32_t sub = (2u + f) << (ex + 5 > 0 ? ex + 5 : 0);
+  const uint32_t mag = m == 0u ? 0u : ex >= 255 ? 0x7F80u : ex >= 1 ? normal : sub;
+  return sg | mag;
+}
+
+__global__ __launch_bounds__(256) void k_dequant_tile32(const uint8_t* __restrict__ codes,
+                                                        const uint8_t* __restrict__ scales,
+                                                        uint32_t rows, uint32_t cols,
+                                                        uint16_t* __restrict__ out) {
+  const uint32_t cpr = cols >> 1, spr = cols >> 5, lpr = cols >> 3;   // lanes per row
+  const uint32_t total = rows * lpr;
+  const auto rc = make_rsrc(codes, static_cast<uint64_t>(rows) * cpr);
+  const auto rs = make_rsrc(scales, static_cast<uint64_t>(rows >> 5) * spr);
+  const auto ro = make_rsrc(out, static_cast<uint64_t>(rows) * cols * 2);
+  for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
+    const uint32_t r = i / lpr, c8 = i - r * lpr;
+    const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<int>(r * cpr + 4 * c8), 0, 0);
+    const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b8(rs, static_cast<int>((r >> 5) * spr + (c8 >> 2)), 0, 0);
+    const int sc = static_cast<int>(sb);
+    u32x4 o;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const uint32_t byte = w >> (8 * j);
+      o[j] = e2m1_to_bf16(byte & 0xFu, sc) | (e2m1_to_bf16((byte >> 4) & 0xFu, sc) << 16);
+    }
+    buf_store128(ro, (r * cols + 8 * c8) * 2, o);
+  }
+}
+
 hipError_t launch_quant_row32(const uint16_t* in, const uint16_t* in2, int act, int64_t rows,
                               int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
                               hipStream_t st, bool streaming) {
@@ -819,6 +865,17 @@ hipError_t launch_quant_row32_t(const uint16_t* in, int64_t rows, int64_t cols, 
   const uint32_t n = static_cast<uint32_t>(((cols + 255) / 256) * ((rows + 255) / 256));
   hipLaunchKernelGGL(k_quant_dual<false>, dim3(n), dim3(512), 0, st, in, static_cast<uint32_t>(rows),
                      static_cast<uint32_t>(cols), ld, codes, scales, codes_t, scales_t);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_tile32(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                 int64_t cols, uint16_t* out, hipStream_t st) {
+  const int64_t lanes = rows * (cols / 8);
+  int64_t grid = (lanes + 1023) / 1024;                    // about 4 row pieces per lane
+  if (grid < 1) grid = 1;
+  if (grid > 16384) grid = 16384;
+  hipLaunchKernelGGL(k_dequant_tile32, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, codes,
+                     scales, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols), out);
   return hipGetLastError();
 }
 

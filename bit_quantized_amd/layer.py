@@ -38,14 +38,19 @@ class QuantizedLinear:
     L1t = L1^T [r_s, K], L2 [r_s, N] (frozen), At = A^T [r_l, K], B [r_l, N]
     (trainable).  act_in / act_out (ops.FT_ACT_*) mark an activation before
     or after the layer: with act_in, X is the pre-activation h; with act_out,
-    the backward's dY is the gradient of act(Y) and needs H = Y.
+    the backward's dY is the gradient of act(Y) and needs H = Y.  precision:
+    ops.FT_W4A4G4 (the method) .. ops.FT_W4A16G16, or its name.
     """
 
     def __init__(self, W_res: torch.Tensor, L1t: torch.Tensor | None, L2: torch.Tensor | None,
                  At: torch.Tensor | None, B: torch.Tensor | None, stream=None,
-                 act_in: int = ops.FT_ACT_NONE, act_out: int = ops.FT_ACT_NONE):
+                 act_in: int = ops.FT_ACT_NONE, act_out: int = ops.FT_ACT_NONE,
+                 precision=ops.FT_W4A4G4):
         N, K = W_res.shape
         self.act_in, self.act_out = int(act_in), int(act_out)
+        if isinstance(precision, str):
+            precision = ops.PRECISION_NAMES[precision]
+        self.precision = int(precision)
         dev = W_res.device
         self.N, self.K = int(N), int(K)
         self.r_s = 0 if L1t is None else int(L1t.shape[0])
@@ -62,11 +67,20 @@ class QuantizedLinear:
 
     @classmethod
     def from_factors(cls, W_res, L1, L2, A, B, stream=None, act_in: int = ops.FT_ACT_NONE,
-                     act_out: int = ops.FT_ACT_NONE) -> "QuantizedLinear":
+                     act_out: int = ops.FT_ACT_NONE, precision=ops.FT_W4A4G4) -> "QuantizedLinear":
         """From factors in the method's orientation (L1 [K, r_s], A [K, r_l]):
         the down-projections are copied once into the rank-major storage."""
         t = lambda x: None if x is None else x.t().contiguous()
-        return cls(W_res, t(L1), L2, t(A), B, stream=stream, act_in=act_in, act_out=act_out)
+        return cls(W_res, t(L1), L2, t(A), B, stream=stream, act_in=act_in, act_out=act_out,
+                   precision=precision)
+
+    @property
+    def a16(self) -> bool:
+        return bool(self.precision & ops.FT_W4A16G4)
+
+    @property
+    def g16(self) -> bool:
+        return bool(self.precision & ops.FT_W4A4G16)
 
     @property
     def R(self):
@@ -75,7 +89,7 @@ class QuantizedLinear:
     def desc(self, M: int) -> ops.FtLinear:
         return ops.make_linear(M, self.K, self.N, self.r_s, self.r_l, self.w_codes,
                                self.w_scales, self.wt_codes, self.wt_scales, self.L1t, self.L2,
-                               self.At, self.B, self.act_in, self.act_out)
+                               self.At, self.B, self.act_in, self.act_out, self.precision)
 
     def workspace(self, M: int, is_bwd: bool):
         key = (M, bool(is_bwd))
@@ -85,13 +99,15 @@ class QuantizedLinear:
         return self._ws[key]
 
     def forward(self, X: torch.Tensor, stream=None, want_codes: bool = False):
-        """Returns (Y, U) or (Y, U, xq_codes, xq_scales)."""
+        """Returns (Y, U) or (Y, U, xq_codes, xq_scales); the codes are None
+        when the layer's precision keeps activations in bf16 (A16)."""
         M = int(X.shape[0])
         dev = self.device
         Y = _empty((M, self.N), torch.bfloat16, dev)
         U = _empty((M, max(self.R, 1)), torch.bfloat16, dev)
-        qc = _empty((M, self.K // 2), torch.uint8, dev) if want_codes else None
-        qs = _empty((M, self.K // 32), torch.uint8, dev) if want_codes else None
+        codes = want_codes and not self.a16
+        qc = _empty((M, self.K // 2), torch.uint8, dev) if codes else None
+        qs = _empty((M, self.K // 32), torch.uint8, dev) if codes else None
         ws = self.workspace(M, False)
         ops.fourtune_linear_fwd(self.desc(M), X, Y, U if self.R else None, qc, qs, ws,
                                 ws.numel(), stream)
@@ -102,7 +118,8 @@ class QuantizedLinear:
                  H: torch.Tensor | None = None):
         """Returns (dX, dAt, dB, P) or (dX, dAt, dB, P, gq_codes, gq_scales);
         dAt = dA^T [r_l, K] and dB [r_l, N], the layouts of At and B.  H is
-        the forward's Y, needed when the layer has act_out."""
+        the forward's Y, needed when the layer has act_out.  The codes are
+        None when the layer's precision keeps gradients in bf16 (G16)."""
         M = int(dY.shape[0])
         dev = self.device
         dX = _empty((M, self.K), torch.bfloat16, dev) if need_dx else None
@@ -110,8 +127,9 @@ class QuantizedLinear:
         dA = _empty((self.r_l, self.K), gdt, dev) if self.r_l else None
         dB = _empty((self.r_l, self.N), gdt, dev) if self.r_l else None
         P = _empty((M, max(self.R, 1)), torch.bfloat16, dev)
-        qc = _empty((M, self.N // 2), torch.uint8, dev) if want_codes else None
-        qs = _empty((M, self.N // 32), torch.uint8, dev) if want_codes else None
+        codes = want_codes and not self.g16
+        qc = _empty((M, self.N // 2), torch.uint8, dev) if codes else None
+        qs = _empty((M, self.N // 32), torch.uint8, dev) if codes else None
         ws = self.workspace(M, True)
         ops.fourtune_linear_bwd(self.desc(M), dY, X, U if self.R else None, H, dX, dA, dB,
                                 ops.FT_F32 if grad_f32 else ops.FT_BF16,

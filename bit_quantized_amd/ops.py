@@ -19,8 +19,11 @@ FT_BF16, FT_F32 = 0, 1
 FT_Q_ROW32, FT_Q_ROW32_T, FT_Q_TILE32 = 1, 2, 4
 FT_MAX_RANK = 64
 FT_ACT_NONE, FT_ACT_GELU_TANH = 0, 1
+FT_W4A4G4, FT_W4A16G4, FT_W4A4G16, FT_W4A16G16 = 0, 1, 2, 3
+PRECISION_NAMES = {"W4A4G4": FT_W4A4G4, "W4A16G4": FT_W4A16G4, "W4A4G16": FT_W4A4G16,
+                   "W4A16G16": FT_W4A16G16}
 
-EXPORTS = ("fourtune_quantize", "fourtune_workspace_bytes", "fourtune_linear_fwd",
+EXPORTS = ("fourtune_quantize", "fourtune_dequantize", "fourtune_workspace_bytes", "fourtune_linear_fwd",
            "fourtune_linear_bwd", "fourtune_act_fwd", "fourtune_act_bwd",
            "fourtune_status_string", "fourtune_timing_enable", "fourtune_timing_reset",
            "fourtune_timing_read")
@@ -39,7 +42,8 @@ class FtLinear(ctypes.Structure):
                 ("wt_codes", ctypes.c_void_p), ("wt_scales", ctypes.c_void_p),
                 ("L1t", ctypes.c_void_p), ("L2", ctypes.c_void_p),
                 ("At", ctypes.c_void_p), ("B", ctypes.c_void_p),
-                ("act_in", ctypes.c_int32), ("act_out", ctypes.c_int32)]
+                ("act_in", ctypes.c_int32), ("act_out", ctypes.c_int32),
+                ("precision", ctypes.c_int32)]
 
 
 _lib = None
@@ -56,6 +60,8 @@ def lib() -> ctypes.CDLL:
         vp, i64, st = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         L.fourtune_quantize.argtypes = [st, vp, i64, i64, i64, vp, vp, vp, vp, vp]
         L.fourtune_quantize.restype = st
+        L.fourtune_dequantize.argtypes = [st, vp, vp, i64, i64, vp, vp]
+        L.fourtune_dequantize.restype = st
         L.fourtune_workspace_bytes.argtypes = [ctypes.POINTER(FtLinear), st]
         L.fourtune_workspace_bytes.restype = ctypes.c_size_t
         L.fourtune_linear_fwd.argtypes = [ctypes.POINTER(FtLinear), vp, vp, vp, vp, vp, vp,
@@ -114,14 +120,17 @@ def _check(status: int, where: str):
 
 def make_linear(M, K, N, r_stab, r_lora, w_codes, w_scales, wt_codes=None, wt_scales=None,
                 L1t=None, L2=None, At=None, B=None, act_in=FT_ACT_NONE,
-                act_out=FT_ACT_NONE) -> FtLinear:
+                act_out=FT_ACT_NONE, precision=FT_W4A4G4) -> FtLinear:
     """Fill the ft_linear descriptor from tensors (device) or raw addresses.
 
     The factors are rank-major: L1t = L1^T [r_stab, K], L2 [r_stab, N],
-    At = A^T [r_lora, K], B [r_lora, N]."""
+    At = A^T [r_lora, K], B [r_lora, N].  precision: FT_W4A4G4 .. FT_W4A16G16
+    or its name."""
+    if isinstance(precision, str):
+        precision = PRECISION_NAMES[precision]
     return FtLinear(int(M), int(K), int(N), int(r_stab), int(r_lora), _ptr(w_codes),
                     _ptr(w_scales), _ptr(wt_codes), _ptr(wt_scales), _ptr(L1t), _ptr(L2),
-                    _ptr(At), _ptr(B), int(act_in), int(act_out))
+                    _ptr(At), _ptr(B), int(act_in), int(act_out), int(precision))
 
 
 def fourtune_quantize(mode, x, rows, cols, ld, codes, scales, codes_t=None, scales_t=None,
@@ -129,6 +138,12 @@ def fourtune_quantize(mode, x, rows, cols, ld, codes, scales, codes_t=None, scal
     s = lib().fourtune_quantize(int(mode), _ptr(x), int(rows), int(cols), int(ld), _ptr(codes),
                                 _ptr(scales), _ptr(codes_t), _ptr(scales_t), _stream(stream))
     _check(s, "fourtune_quantize")
+
+
+def fourtune_dequantize(mode, codes, scales, rows, cols, out, stream=None):
+    s = lib().fourtune_dequantize(int(mode), _ptr(codes), _ptr(scales), int(rows), int(cols),
+                                  _ptr(out), _stream(stream))
+    _check(s, "fourtune_dequantize")
 
 
 def fourtune_workspace_bytes(layer: FtLinear, is_bwd: bool) -> int:

@@ -100,6 +100,21 @@ typedef enum {
                             evaluated in fp32, rounded to bf16 once                  */
 } ft_act;
 
+/* Precision of the two backbone products (FourTune, "4.3 Ablation Study /
+ * Impact of Precision Configurations", Table 4).  The weight is 4-bit in
+ * all four; A16 keeps the forward's input in bf16 in the backbone product,
+ * G16 the incoming gradient in the input-gradient product.  A 16-bit side
+ * multiplies bf16 by the weight's MXFP4 tiles dequantized to bf16 (exact:
+ * every dequantized value is a short bf16 number), made in the workspace by
+ * each call; the low-rank branches and the adapter gradients are the same
+ * in all four.  Only W4A4G4 runs both products on the 4-bit matrix cores. */
+typedef enum {
+  FT_W4A4G4 = 0,
+  FT_W4A16G4 = 1,    /* bit 0: A16 */
+  FT_W4A4G16 = 2,    /* bit 1: G16 */
+  FT_W4A16G16 = 3
+} ft_precision;
+
 #define FT_MAX_RANK 64
 
 /* One triple-branch linear layer.  Host struct; the pointers in it are device
@@ -120,6 +135,7 @@ typedef struct {
                                  is recomputed wherever it is read, never stored         */
   int32_t act_out;            /* FT_ACT_*: an activation follows this layer: the backward's
                                  dY is the gradient of act_out(Y), and H = Y is required */
+  int32_t precision;          /* FT_W4A4G4 (0, the method) .. FT_W4A16G16                */
 } ft_linear;
 
 /* Quantize a bf16 matrix `in` [rows, cols] with row stride ld_in elements.
@@ -143,6 +159,21 @@ ft_status fourtune_quantize(int mode, const uint16_t* in, int64_t rows, int64_t 
                             int64_t ld_in, uint8_t* codes, uint8_t* scales,
                             uint8_t* codes_t, uint8_t* scales_t, void* stream);
 
+/* MXFP4 back to bf16: each value is its E2M1 element times its block's
+ * power-of-two scale (FourTune, "2.3 Model Quantization"; the 16-bit
+ * precision settings of "4.3 Ablation Study" multiply by the weight in this
+ * form).
+ * mode FT_Q_TILE32 only: codes [rows, cols/2] and tile scales [rows/32,
+ * cols/32] in, out bf16 [rows, cols].  Exact for every code and scale byte
+ * (bf16 subnormals included) except scale bytes 253 and 254, which no finite
+ * bf16 input is quantized to and whose largest elements overflow to Inf.
+ * Requirements: rows % 32 == 0, cols % 32 == 0, rows, cols >= 0,
+ * rows * cols * 2 < 2^31, pointers 16-byte aligned.  rows == 0 is a no-op.
+ * Errors: FT_EINVAL (mode, NULLs), FT_ESHAPE, FT_EALIGN, FT_EDEVICE,
+ * FT_EUNSUPPORTED. */
+ft_status fourtune_dequantize(int mode, const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                              int64_t cols, uint16_t* out, void* stream);
+
 /* Bytes of device workspace fwd (is_bwd = 0) or bwd (is_bwd = 1) needs for
  * layer L (shapes and ranks only are read).  Returns 0 for invalid shapes. */
 size_t fourtune_workspace_bytes(const ft_linear* L, int is_bwd);
@@ -154,14 +185,19 @@ size_t fourtune_workspace_bytes(const ft_linear* L, int is_bwd);
  * With act_in != FT_ACT_NONE, X is the pre-activation h and kernel 1 applies
  * act_in to every value as it reads it (the quantized input and U are those
  * of act_in(h)).
+ * Under A16 (precision bit 0) kernel 1 computes U only, the weight's tiles
+ * are dequantized to bf16 in the workspace, and kernel 2 multiplies bf16 X
+ * (act_in(X) when set, made in the workspace first) by them.
  * U_save  : bf16 [M, R], written; the backward needs it.  May be NULL if R == 0.
  * xq_codes, xq_scales: optional outputs [M, K/2], [M, K/32]; NULL = keep
- *   them in the workspace.
+ *   them in the workspace.  Must be NULL under A16 (there are no codes).
  * workspace: device memory of at least fourtune_workspace_bytes(L, 0) bytes;
  *   contents on entry are ignored and on return unspecified.
  * Requirements: M >= 1, K % 32 == 0, N % 32 == 0, R <= 64, and every
  *   activation padded to 256 more rows below 2^31 bytes:
- *   (M + 256) * max(K, N) * 2 < 2^31 (the kernels use 32-bit offsets).
+ *   (M + 256) * max(K, N) * 2 < 2^31 (the kernels use 32-bit offsets);
+ *   under A16 or G16 the same for the dequantized weight,
+ *   (max(K, N) + 256) * min(K, N) * 2 < 2^31; precision in 0..3.
  * Errors: FT_EINVAL, FT_ESHAPE, FT_EALIGN, FT_EWORKSPACE, FT_EDEVICE. */
 ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y,
                               uint16_t* U_save, uint8_t* xq_codes, uint8_t* xq_scales,
@@ -186,8 +222,13 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
  * dA uses act_in(h), recomputed as X is read.  dX may be NULL (no
  * input gradient; then wt_codes and wt_scales may be NULL).  dA, dB may be
  * NULL only when r_lora == 0.
+ * Under G16 (precision bit 1) kernel 1 computes P and the dB partials
+ * only, the transposed weight tiles are dequantized to bf16 in the
+ * workspace, and kernel 2 multiplies bf16 dY (dY * act_out'(H) when set,
+ * made in the workspace first) by them.
  * P_save : optional bf16 [M, R] output of P; NULL = workspace only.
- * gq_codes, gq_scales: optional outputs [M, N/2], [M, N/32].
+ * gq_codes, gq_scales: optional outputs [M, N/2], [M, N/32]; must be NULL
+ *   under G16.
  * workspace: at least fourtune_workspace_bytes(L, 1) bytes.
  * No gradient is produced for W_res, L1 or L2 (frozen).
  * Requirements: as for the forward.

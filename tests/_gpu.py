@@ -31,14 +31,15 @@ def up(bits):
 
 
 def u8(t):
-    return t.detach().cpu().numpy()
+    return None if t is None else t.detach().cpu().numpy()
 
 
 class GpuCase:
     """A LinearCase resident on the device with its quantized weight."""
 
-    def __init__(self, case):
+    def __init__(self, case, precision="W4A4G4"):
         self.c = case
+        self.precision = precision
         self.X = up(case.X)
         self.dY = up(case.dY)
         W = up(case.W_res)
@@ -46,7 +47,8 @@ class GpuCase:
         self.layer = QuantizedLinear.from_factors(W, opt(case.L1) if case.r_s else None,
                                                   opt(case.L2) if case.r_s else None,
                                                   opt(case.A) if case.r_l else None,
-                                                  opt(case.B) if case.r_l else None)
+                                                  opt(case.B) if case.r_l else None,
+                                                  precision=precision)
         del W
 
     def run(self, grad_f32=False):
@@ -113,17 +115,24 @@ def check_weight_codes(c, got):
     return wc, ws
 
 
-def check_full(case, got, grad_f32=False):
+def _codes_equal(got, ref, name):
+    """Codes and scales bit for bit; a 16-bit side has none on either side."""
+    assert (got is None) == (ref is None), name
+    if ref is not None:
+        np.testing.assert_array_equal(got, ref, err_msg=name)
+
+
+def check_full(case, got, grad_f32=False, precision="W4A4G4"):
     """Full-size oracle comparison for cases the oracle finishes in seconds."""
     c = case
     wc, ws = check_weight_codes(c, got)
-    f = OL.linear_fwd(c.X, wc, ws, c.L1, c.L2, c.A, c.B)
+    f = OL.linear_fwd(c.X, wc, ws, c.L1, c.L2, c.A, c.B, precision=precision)
     b = OL.linear_bwd(c.dY, c.X, f["U"], wc, ws, c.L1, c.L2, c.A, c.B,
-                      grad_dtype="f32" if grad_f32 else "bf16")
-    np.testing.assert_array_equal(got["xq_codes"], f["xq_codes"])
-    np.testing.assert_array_equal(got["xq_scales"], f["xq_scales"])
-    np.testing.assert_array_equal(got["gq_codes"], b["gq_codes"])
-    np.testing.assert_array_equal(got["gq_scales"], b["gq_scales"])
+                      grad_dtype="f32" if grad_f32 else "bf16", precision=precision)
+    for k in ("xq_codes", "xq_scales"):
+        _codes_equal(got[k], f[k], k)
+    for k in ("gq_codes", "gq_scales"):
+        _codes_equal(got[k], b[k], k)
     res = {}
     if c.R:
         res["U_bits"] = bit_agreement(got["U"], f["U"])
@@ -149,18 +158,24 @@ def check_full(case, got, grad_f32=False):
     return res
 
 
-def check_sampled(case, got, rows):
+def check_sampled(case, got, rows, precision="W4A4G4"):
     """Large cases: outputs of sampled rows, and the adapter gradients in full."""
     c = case
     wc, ws = check_weight_codes(c, got)
-    xc, xs = OQ.quantize_row32(c.X[rows])
-    np.testing.assert_array_equal(got["xq_codes"][rows], xc)
-    np.testing.assert_array_equal(got["xq_scales"][rows], xs)
-    gc, gs = OQ.quantize_row32(c.dY[rows])
-    np.testing.assert_array_equal(got["gq_codes"][rows], gc)
-    np.testing.assert_array_equal(got["gq_scales"][rows], gs)
-    Y, U = OL.linear_fwd_rows(rows, c.X, wc, ws, c.L1, c.L2, c.A, c.B)
-    dX, P = OL.linear_bwd_rows(rows, c.dY, wc, ws, c.L1, c.L2, c.A, c.B)
+    if "A16" in precision:
+        assert got["xq_codes"] is None
+    else:
+        xc, xs = OQ.quantize_row32(c.X[rows])
+        np.testing.assert_array_equal(got["xq_codes"][rows], xc)
+        np.testing.assert_array_equal(got["xq_scales"][rows], xs)
+    if "G16" in precision:
+        assert got["gq_codes"] is None
+    else:
+        gc, gs = OQ.quantize_row32(c.dY[rows])
+        np.testing.assert_array_equal(got["gq_codes"][rows], gc)
+        np.testing.assert_array_equal(got["gq_scales"][rows], gs)
+    Y, U = OL.linear_fwd_rows(rows, c.X, wc, ws, c.L1, c.L2, c.A, c.B, precision=precision)
+    dX, P = OL.linear_bwd_rows(rows, c.dY, wc, ws, c.L1, c.L2, c.A, c.B, precision=precision)
     res = {"Y": OL.rel_frobenius(got["Y"][rows], OQ.f64_to_bf16_bits(Y)),
            "dX": OL.rel_frobenius(got["dX"][rows], OQ.f64_to_bf16_bits(dX))}
     if c.R:

@@ -147,3 +147,49 @@ def test_valid_call_without_gpu_reports_unsupported():
     if torch.cuda.is_available():
         pytest.skip("a GPU is present")
     assert _fwd(_layer()) == ops.FT_EUNSUPPORTED
+
+
+def _dq(mode=ops.FT_Q_TILE32, c=A16, s=A16, rows=64, cols=64, out=A16):
+    return ops.lib().fourtune_dequantize(mode, c, s, rows, cols, out, None)
+
+
+def test_dequantize_argument_errors():
+    assert _dq(mode=ops.FT_Q_ROW32) == ops.FT_EINVAL
+    assert _dq(c=None) == ops.FT_EINVAL
+    assert _dq(out=None) == ops.FT_EINVAL
+    assert _dq(rows=48) == ops.FT_ESHAPE
+    assert _dq(cols=40) == ops.FT_ESHAPE
+    assert _dq(rows=-32) == ops.FT_ESHAPE
+    assert _dq(rows=1 << 16, cols=1 << 15) == ops.FT_ESHAPE       # 2^32 bytes of bf16
+    assert _dq(s=A16 + 8) == ops.FT_EALIGN
+    assert _dq(rows=0) == ops.FT_OK
+
+
+def test_precision_argument_errors_and_workspace():
+    assert _fwd(_layer(precision=4)) == ops.FT_EINVAL
+    assert _fwd(_layer(precision=-1)) == ops.FT_EINVAL
+    assert ops.fourtune_workspace_bytes(_layer(precision=7), False) == 0
+    # a 16-bit side has no codes to hand out
+    assert _fwd(_layer(precision=ops.FT_W4A16G4), qc=A16, qs=A16) == ops.FT_EINVAL
+    assert _bwd(_layer(precision=ops.FT_W4A4G16), qc=A16, qs=A16) == ops.FT_EINVAL
+    # ... while the other side still may
+    M, K, N = 4096, 1024, 2048
+    base = {b: ops.fourtune_workspace_bytes(_layer(M=M, K=K, N=N), b) for b in (False, True)}
+    a16 = {b: ops.fourtune_workspace_bytes(_layer(M=M, K=K, N=N, precision="W4A16G4"), b)
+           for b in (False, True)}
+    g16 = {b: ops.fourtune_workspace_bytes(_layer(M=M, K=K, N=N, precision="W4A4G16"), b)
+           for b in (False, True)}
+    # A16 drops X's codes and scales and adds the bf16 weight [N, K]
+    assert a16[False] == base[False] - M * K // 2 - M * K // 32 + N * K * 2
+    assert a16[True] == base[True]
+    # G16 drops dY's codes and scales and adds the transposed bf16 weight
+    assert g16[True] == base[True] - M * N // 2 - M * N // 32 + K * N * 2
+    assert g16[False] == base[False]
+    # with an activation next to the layer, its bf16 output is made as well
+    act = ops.fourtune_workspace_bytes(_layer(M=M, K=K, N=N, precision="W4A16G16",
+                                              act_in=ops.FT_ACT_GELU_TANH), False)
+    assert act == a16[False] + M * K * 2
+    # the dequantized weight must fit 32-bit offsets with its padded rows
+    big = _layer(M=64, K=(1 << 16), N=(1 << 14) - 32, precision="W4A16G4")
+    assert _fwd(big) == ops.FT_ESHAPE
+    assert _fwd(_layer(M=64, K=(1 << 16), N=(1 << 14) - 32)) != ops.FT_ESHAPE

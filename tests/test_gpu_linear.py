@@ -45,6 +45,28 @@ def test_ragged_shapes_full(shape):
     check_full(c, GpuCase(c).run())
 
 
+@pytest.mark.parametrize("precision", ["W4A16G4", "W4A4G16", "W4A16G16"])
+@pytest.mark.parametrize("shape", [
+    (300, 288, 544, 16, 8),      # ragged, several tiles and 32-element bf16 steps
+    (200, 640, 384, 0, 0),       # no low-rank branches, odd step count padded
+    (2, 3072, 1024, 32, 16),     # two tokens, long reduction
+])
+def test_precision_settings_full(shape, precision):
+    """The 16-bit settings of the precision ablation: the bf16 side is
+    multiplied by the weight tiles dequantized to bf16, the rest as in
+    W4A4G4."""
+    M, K, N, rs, rl = shape
+    c = synth.flux_linear_case(f"{precision}_{M}x{K}x{N}_r{rs}_{rl}", M, K, N, rs, rl, seed=M + N)
+    say("case", c.name)
+    check_full(c, GpuCase(c, precision).run(), precision=precision)
+
+
+def test_precision_w4a16g16_qkv_full_size_sampled():
+    c = synth.qkv_case()
+    say("case", c.name, "W4A16G16")
+    check_sampled(c, GpuCase(c, "W4A16G16").run(), _rows(c.M, seed=3), precision="W4A16G16")
+
+
 def test_fp32_adapter_gradients():
     c = synth.flux_linear_case("f32grads", 200, 256, 320, 8, 16, seed=5)
     say("case", c.name)

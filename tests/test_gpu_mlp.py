@@ -106,14 +106,14 @@ def test_gelu_odd_length_tail():
 class MlpPair:
     """FC1 (K -> F, act_out = GELU) and FC2 (F -> K, act_in = GELU) on the GPU."""
 
-    def __init__(self, M, K, F, rs, rl, seed):
+    def __init__(self, M, K, F, rs, rl, seed, precision="W4A4G4"):
         self.c1 = synth.flux_linear_case(f"fc1_{M}x{K}x{F}", M, K, F, rs, rl, seed)
         self.c2 = synth.flux_linear_case(f"fc2_{M}x{F}x{K}", M, F, K, rs, rl, seed + 1)
         opt = lambda a: up(a) if a.size else None
         mk = lambda c, **kw: QuantizedLinear.from_factors(
             up(c.W_res), opt(c.L1), opt(c.L2), opt(c.A), opt(c.B), **kw)
-        self.fc1 = mk(self.c1, act_out=G)
-        self.fc2 = mk(self.c2, act_in=G)
+        self.fc1 = mk(self.c1, act_out=G, precision=precision)
+        self.fc2 = mk(self.c2, act_in=G, precision=precision)
 
     def run(self):
         c1, c2 = self.c1, self.c2
@@ -123,7 +123,7 @@ class MlpPair:
         dX2, dA2, dB2, P2, gc2, gs2 = self.fc2.backward(dY2, h, U2, want_codes=True)
         dX1, dA1, dB1, P1, gc1, gs1 = self.fc1.backward(dX2, X1, U1, want_codes=True, H=h)
         torch.cuda.synchronize()
-        u8 = lambda t: t.cpu().numpy()
+        u8 = lambda t: None if t is None else t.cpu().numpy()
         R = lambda t, c: bits_of(t)[:, :c.R] if c.R else None
         T = lambda t: None if t is None else np.ascontiguousarray(bits_of(t).T)
         Bb = lambda t: None if t is None else bits_of(t)
@@ -139,18 +139,19 @@ def _absdot(x_bits, w):
     return np.abs(OQ.bf16_bits_to_f64(x_bits)) @ np.abs(w)
 
 
-def _check_layer_full(tag, c, X, dY, got_fwd, got_bwd, Y_name):
+def _check_layer_full(tag, c, X, dY, got_fwd, got_bwd, Y_name, precision="W4A4G4"):
     """One linear against the oracle in full, given the operands the GPU saw.
     got_fwd = (Y, U, xc, xs); got_bwd = (dX, dA, dB, P, gc, gs)."""
     wc, ws = OQ.quantize_tile32(c.W_res)
-    f = OL.linear_fwd(X, wc, ws, c.L1, c.L2, c.A, c.B)
-    b = OL.linear_bwd(dY, X, f["U"], wc, ws, c.L1, c.L2, c.A, c.B)
+    f = OL.linear_fwd(X, wc, ws, c.L1, c.L2, c.A, c.B, precision=precision)
+    b = OL.linear_bwd(dY, X, f["U"], wc, ws, c.L1, c.L2, c.A, c.B, precision=precision)
     Y, U, xc, xs = got_fwd
     dX, dA, dB, P, gc, gs = got_bwd
-    np.testing.assert_array_equal(xc, f["xq_codes"], err_msg=tag + " xq codes")
-    np.testing.assert_array_equal(xs, f["xq_scales"], err_msg=tag + " xq scales")
-    np.testing.assert_array_equal(gc, b["gq_codes"], err_msg=tag + " gq codes")
-    np.testing.assert_array_equal(gs, b["gq_scales"], err_msg=tag + " gq scales")
+    for got_c, ref_c, name in ((xc, f["xq_codes"], "xq codes"), (xs, f["xq_scales"], "xq scales"),
+                               (gc, b["gq_codes"], "gq codes"), (gs, b["gq_scales"], "gq scales")):
+        assert (got_c is None) == (ref_c is None), tag + " " + name
+        if ref_c is not None:
+            np.testing.assert_array_equal(got_c, ref_c, err_msg=tag + " " + name)
     res = {Y_name: OL.rel_frobenius(Y, f["Y"]), "dX": OL.rel_frobenius(dX, b["dX"])}
     if c.r_l:
         res["dA"] = OL.rel_frobenius(dA, b["dA"])
@@ -175,10 +176,10 @@ def _check_layer_full(tag, c, X, dY, got_fwd, got_bwd, Y_name):
     (64, 160, 320, 0, 8),       # adapter only
     (40, 96, 192, 0, 0),        # no low-rank branches (plain quantizer with the activation)
 ])
-def test_mlp_pair_chain_full(shape):
+def test_mlp_pair_chain_full(shape, precision="W4A4G4"):
     M, K, F, rs, rl = shape
-    say("case mlp pair", shape)
-    mp = MlpPair(M, K, F, rs, rl, seed=M + F)
+    say("case mlp pair", shape, precision)
+    mp = MlpPair(M, K, F, rs, rl, seed=M + F, precision=precision)
     got = mp.run()
     c1, c2 = mp.c1, mp.c2
     a_gpu = _gelu_gpu(got["h"])
@@ -188,11 +189,21 @@ def test_mlp_pair_chain_full(shape):
     # FC2 consumes gelu(h): the oracle is fed the GPU's bf16 activation
     _check_layer_full("fc2", c2, a_gpu, c2.dY,
                       (got["Y2"], got["U2"], got["xc2"], got["xs2"]),
-                      (got["dX2"], got["dA2"], got["dB2"], got["P2"], got["gc2"], got["gs2"]), "Y2")
+                      (got["dX2"], got["dA2"], got["dB2"], got["P2"], got["gc2"], got["gs2"]), "Y2",
+                      precision)
     # FC1's incoming gradient is dX2 * gelu'(h)
     _check_layer_full("fc1", c1, c1.X, dh_gpu,
                       (got["h"], got["U1"], got["xc1"], got["xs1"]),
-                      (got["dX1"], got["dA1"], got["dB1"], got["P1"], got["gc1"], got["gs1"]), "h")
+                      (got["dX1"], got["dA1"], got["dB1"], got["P1"], got["gc1"], got["gs1"]), "h",
+                      precision)
+
+
+@pytest.mark.parametrize("shape", [(300, 288, 544, 16, 8), (40, 96, 192, 0, 0)])
+def test_mlp_pair_chain_w4a16g16_full(shape):
+    """The 16-bit setting around the GELU: FC2's bf16 input gelu(h) and FC1's
+    bf16 incoming gradient dX2 * gelu'(h) are made by the activation kernels
+    before the 16-bit products."""
+    test_mlp_pair_chain_full(shape, precision="W4A16G16")
 
 
 def test_mlp_pair_chain_full_size_sampled():

@@ -183,3 +183,42 @@ def test_stress_full_size_tile32_sampled():
         ec, es = OQ.quantize_tile32(blk)
         assert s[i, j] == es[0, 0]
         np.testing.assert_array_equal(c[32 * i:32 * i + 32, 16 * j:16 * j + 16], ec)
+
+
+def _dequant(codes, scales):
+    rows, cols = codes.shape[0], codes.shape[1] * 2
+    c = torch.from_numpy(np.ascontiguousarray(codes)).to(DEV)
+    s = torch.from_numpy(np.ascontiguousarray(scales)).to(DEV)
+    out = torch.empty((rows, cols), dtype=torch.int16, device=DEV)
+    ops.fourtune_dequantize(ops.FT_Q_TILE32, c, s, rows, cols, out)
+    torch.cuda.synchronize()
+    return out.cpu().numpy().view(np.uint16)
+
+
+@pytest.mark.parametrize("shape", [(32, 32), (96, 160), (320, 544), (1024, 4096)])
+def test_dequant_tile32_every_code_and_scale(shape):
+    """Arbitrary code bytes (every nibble, both signs of zero) under scale bytes
+    0..252 (the whole range a finite input is quantized to: bf16 subnormal
+    results included) against the oracle's exact values rounded to bf16."""
+    rng = np.random.default_rng(shape[1])
+    rows, cols = shape
+    codes = rng.integers(0, 256, size=(rows, cols // 2), dtype=np.uint8)
+    scales = rng.integers(0, 253, size=(rows // 32, cols // 32), dtype=np.uint8)
+    scales.flat[:3] = (0, 1, 252)
+    say("dequant tile32", shape)
+    got = _dequant(codes, scales)
+    np.testing.assert_array_equal(got, OQ.f64_to_bf16_bits(OQ.dequantize_tile32(codes, scales)))
+
+
+def test_dequant_tile32_of_quantized_weight():
+    """Dequantizing Qtile(W) (plain and transposed copies) gives the oracle's
+    deq(Qtile(W)) and deq(Qtile(W))^T bit for bit."""
+    rng = np.random.default_rng(9)
+    w = synth.to_bf16_bits(rng.standard_normal((288, 640)) * 0.02 *
+                           np.exp2(rng.integers(-20, 20, (9, 1, 20, 1))).repeat(32, 1).repeat(32, 3)
+                           .reshape(288, 640))
+    say("dequant of a quantized weight")
+    c, s, ct, st = _run(ops.FT_Q_TILE32, w, dual=True)
+    ref = OQ.f64_to_bf16_bits(OQ.dequantize_tile32(*OQ.quantize_tile32(w)))
+    np.testing.assert_array_equal(_dequant(c, s), ref)
+    np.testing.assert_array_equal(_dequant(ct, st), np.ascontiguousarray(ref.T))
