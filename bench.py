@@ -51,7 +51,9 @@ def parse():
     ap.add_argument("--no-mlp", action="store_true")
     ap.add_argument("--no-fusion", action="store_true")
     ap.add_argument("--no-block", action="store_true")
-    ap.add_argument("--only", choices=["step", "stress", "mlp", "fusion", "block"], default=None,
+    ap.add_argument("--no-precision", action="store_true")
+    ap.add_argument("--only", choices=["step", "stress", "mlp", "fusion", "block", "precision"],
+                    default=None,
                     help="run only one part (for profiler runs)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain bf16 elementwise copy of known size (the reference "
@@ -604,6 +606,79 @@ def main():
             "step_flop": bflop, "steps": nst}
         log("bench: block", json.dumps(out["dit_block"]))
         del blk, by
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ precision settings
+    # The QKV step (fwd+bwd) in the four precision settings of the pages'
+    # precision ablation (section 4.3, Table 4).  A 16-bit side multiplies bf16
+    # by the weight tiles dequantized to bf16 in each call (as QLoRA-style
+    # training does), on the bf16 matrix cores.
+    if not a.no_precision and a.only in (None, "precision"):
+        c = synth.qkv_case()
+        M, K, N, rs, rl = c.M, c.K, c.N, c.r_s, c.r_l
+        X0, dY0, W0 = (bf16_tensor(x, dev) for x in (c.X, c.dY, c.W_res))
+        L1, L2, A, B = (bf16_tensor(x, dev) for x in (c.L1, c.L2, c.A, c.B))
+        bt = lambda *sh: torch.empty(sh, dtype=torch.bfloat16, device=dev)
+        wk = layer_work(M, K, N, rs, rl)
+        pflop = sum(v["flop"] for v in wk.values())
+        res = {}
+        for pname in ("W4A4G4", "W4A16G4", "W4A4G16", "W4A16G16"):
+            psets = []
+            for s_ in range(2):
+                lay = QuantizedLinear.from_factors(torch.roll(W0, 32 * s_, 0).contiguous(), L1, L2, A, B,
+                                                   precision=pname)
+                psets.append((lay, torch.roll(X0, 97 * s_, 0).contiguous(),
+                              torch.roll(dY0, 97 * s_, 0).contiguous(), bt(M, rs + rl), bt(M, N),
+                              bt(M, K), bt(rl, K), bt(rl, N), lay.workspace(M, False),
+                              lay.workspace(M, True)))
+            torch.cuda.synchronize()
+
+            def pstep(i):
+                lay, X, dY, U, Y, dX, dA, dB, wsf, wsb = psets[i % len(psets)]
+                d = lay.desc(M)
+                ops.fourtune_linear_fwd(d, X, Y, U, None, None, wsf, wsf.numel(), stream)
+                ops.fourtune_linear_bwd(d, dY, X, U, None, dX, dA, dB, ops.FT_BF16, None, None, None,
+                                        wsb, wsb.numel(), stream)
+
+            nst = max(5, a.steps // 5)
+            for i in range(3):
+                pstep(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(nst):
+                pstep(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            pms = e0.elapsed_time(e1) / nst
+            ops.fourtune_timing_reset()
+            ops.fourtune_timing_enable(True)
+            for i in range(nst):
+                pstep(i)
+            torch.cuda.synchronize()
+            ops.fourtune_timing_enable(False)
+            per = {k: round(tot / cnt * 1e3, 2) for k, (tot, cnt) in ops.fourtune_timing_read().items()
+                   if cnt}
+            ent = {"us_per_step": round(pms * 1e3, 1), "TFLOP/s": round(pflop / (pms * 1e-3) / 1e12, 1),
+                   "kernel_avg_us": per}
+            # a 16-bit product runs on the bf16 matrix cores: its own peak
+            for side, kname, on in (("A16", "fwd_gemm", "A16" in pname), ("G16", "bwd_gemm_dgrad", "G16" in pname)):
+                if on and kname in per:
+                    ach = wk[kname]["mfma_flop"] / (per[kname] * 1e-6) / 1e12
+                    ent[kname + "_bf16"] = {"achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
+                                            "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
+            res[pname] = ent
+            log("bench: precision", pname, json.dumps(ent))
+            del psets
+            torch.cuda.empty_cache()
+        base = res["W4A4G4"]["us_per_step"]
+        out["precision_settings"] = {
+            "workload": f"QKV linear fwd+bwd (M={M}, K={K}, N={N}, r_stab={rs}, r_lora={rl}) in the "
+                        "precision settings of the precision ablation; 16-bit sides read the weight "
+                        "tiles dequantized to bf16 by each call",
+            **res,
+            "time_vs_W4A4G4": {k: round(v["us_per_step"] / base, 3) for k, v in res.items()}}
+        del X0, dY0, W0
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ quantizer stress

@@ -779,8 +779,9 @@ __global__ __launch_bounds__(256) void k_rank_reduce(const RRArgs a) {
 
 // ---------------------------------------------------------------------------
 // 32x32-tile MXFP4 back to bf16, the weight operand of a 16-bit product.
-// Lane i takes 4 code bytes (8 values) of a row: a load instruction reads
-// 256 contiguous bytes, a store writes 1 KB of bf16.  Each value is built
+// Lane i takes 16 code bytes (32 values, one tile row piece, one scale) of a
+// row: a load instruction reads 1 KB contiguous, four stores write the 4 KB
+// of bf16 they make.  Each value is built
 // directly as bf16 bits, exactly: an E2M1 magnitude m = 1..7 is 2^E (1 + f)
 // with E = m/2 - 1 and f = 1/2 for odd m > 1, so times the tile's 2^(s-127)
 // its bf16 exponent field is E + s; where that is below 1 the value is a bf16
@@ -801,23 +802,42 @@ __global__ __launch_bounds__(256) void k_dequant_tile32(const uint8_t* __restric
                                                         const uint8_t* __restrict__ scales,
                                                         uint32_t rows, uint32_t cols,
                                                         uint16_t* __restrict__ out) {
-  const uint32_t cpr = cols >> 1, spr = cols >> 5, lpr = cols >> 3;   // lanes per row
-  const uint32_t total = rows * lpr;
+  const uint32_t cpr = cols >> 1, spr = cols >> 5;
+  const uint32_t total = rows * spr;                      // 32-value row pieces, one per lane
   const auto rc = make_rsrc(codes, static_cast<uint64_t>(rows) * cpr);
   const auto rs = make_rsrc(scales, static_cast<uint64_t>(rows >> 5) * spr);
   const auto ro = make_rsrc(out, static_cast<uint64_t>(rows) * cols * 2);
-  for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += gridDim.x * 256) {
-    const uint32_t r = i / lpr, c8 = i - r * lpr;
-    const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(rc, static_cast<int>(r * cpr + 4 * c8), 0, 0);
-    const uint32_t sb = __builtin_amdgcn_raw_buffer_load_b8(rs, static_cast<int>((r >> 5) * spr + (c8 >> 2)), 0, 0);
-    const int sc = static_cast<int>(sb);
-    u32x4 o;
+  const uint32_t stride = gridDim.x * 256;
+  // two pieces per lane per pass, both loads issued before either is used;
+  // a piece past the end reads zeros and stores nothing
+  for (uint32_t i = blockIdx.x * 256 + threadIdx.x; i < total; i += 2 * stride) {
+    uint32_t p[2], r[2], c[2];
+    u32x4 w[2];
+    uint32_t sb[2];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const uint32_t byte = w >> (8 * j);
-      o[j] = e2m1_to_bf16(byte & 0xFu, sc) | (e2m1_to_bf16((byte >> 4) & 0xFu, sc) << 16);
+    for (int h = 0; h < 2; ++h) {
+      p[h] = i + h * stride;
+      const bool ok = p[h] < total;
+      r[h] = ok ? p[h] / spr : 0;
+      c[h] = ok ? p[h] - r[h] * spr : 0;
+      w[h] = buf_load128_nt(rc, ok ? r[h] * cpr + 16 * c[h] : BUF_OOB);
+      sb[h] = __builtin_amdgcn_raw_buffer_load_b8(rs, static_cast<int>(ok ? (r[h] >> 5) * spr + c[h] : BUF_OOB), 0, 0);
     }
-    buf_store128(ro, (r * cols + 8 * c8) * 2, o);
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int sc = static_cast<int>(sb[h]);
+      const uint32_t base = p[h] < total ? (r[h] * cols + 32 * c[h]) * 2 : BUF_OOB;
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        u32x4 o;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const uint32_t byte = w[h][q] >> (8 * j);
+          o[j] = e2m1_to_bf16(byte & 0xFu, sc) | (e2m1_to_bf16((byte >> 4) & 0xFu, sc) << 16);
+        }
+        buf_store128(ro, base == BUF_OOB ? BUF_OOB : base + 16 * q, o);
+      }
+    }
   }
 }
 
@@ -870,8 +890,8 @@ hipError_t launch_quant_row32_t(const uint16_t* in, int64_t rows, int64_t cols, 
 
 hipError_t launch_dequant_tile32(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                  int64_t cols, uint16_t* out, hipStream_t st) {
-  const int64_t lanes = rows * (cols / 8);
-  int64_t grid = (lanes + 1023) / 1024;                    // about 4 row pieces per lane
+  const int64_t lanes = rows * (cols / 32);
+  int64_t grid = (lanes + 511) / 512;                      // two row pieces per lane
   if (grid < 1) grid = 1;
   if (grid > 16384) grid = 16384;
   hipLaunchKernelGGL(k_dequant_tile32, dim3(static_cast<uint32_t>(grid)), dim3(256), 0, st, codes,
