@@ -53,6 +53,11 @@
 //     (v_cvt_pk_bf16_f32, round to nearest even), neighbouring lanes swap
 //     halves so that each holds two adjacent columns of one row, and 16-row
 //     strips go through a small per-wave LDS area to 16-byte global stores.
+//     The stores are non-temporal (each instruction writes whole 128-byte
+//     lines): the output is not read again by this layer, and keeping it out
+//     of the caches leaves the inputs the next kernels read there (measured
+//     on the QKV step: GEMMs unchanged, the adapter-gradient and forward
+//     quantize launches after them 2-3 us faster each).
 #include "ft_device.hpp"
 #include "ft_kernels.h"
 
@@ -343,7 +348,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
           const int sw = (row & 1) | (((row >> 2) & 1) << 1);
           const u32x4 v = lds_read_b128(ostage + row * 256 + ((((c16 >> 2) ^ sw) << 6) | ((c16 & 3) << 4)));
           const uint32_t off = out_base == OOB ? OOB : out_base + static_cast<uint32_t>(mt * 32 + 16 * h + 4 * e) * out_row;
-          __builtin_amdgcn_raw_buffer_store_b128(v, r_out, static_cast<int>(off), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b128(v, r_out, static_cast<int>(off), 0, 2);
         }
       }
 #pragma unroll
