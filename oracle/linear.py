@@ -49,11 +49,42 @@ import numpy as np
 from . import mxfp4 as q
 
 PRECISIONS = ("W4A4G4", "W4A16G4", "W4A4G16", "W4A16G16")
+W_BLOCKS = ("tile32", "row32")
 
 
 def _check_precision(precision: str) -> None:
     if precision not in PRECISIONS:
         raise ValueError(precision)
+
+
+def weight_fwd(w_codes, w_scales, w_block="tile32") -> np.ndarray:
+    """deq(Q(W_res)) [N, K] as the forward's backbone product reads it.
+
+    tile32: the method's 32x32 tiles ("3.2").  row32: the group-wise
+    alternative of the block-shape ablation ("4.3", Table 5), 1x32 blocks
+    along K, codes [N, K/2] and scales [N, K/32]."""
+    if w_block == "tile32":
+        return q.dequantize_tile32(w_codes, w_scales)
+    if w_block == "row32":
+        return q.dequantize_row32(w_codes, w_scales)
+    raise ValueError(w_block)
+
+
+def weight_dgrad(w_codes, w_scales, w_block="tile32", wt=None) -> np.ndarray:
+    """The [N, K] weight the input-gradient product reads.
+
+    tile32: the forward's own numbers (a square tile's scale does not depend
+    on the orientation).  row32: 1x32 blocks along K do not survive the
+    transpose, so the dgrad needs its own quantization of W_res^T with
+    blocks along N: wt = (codes [K, N/2], scales [K, N/32]) = Q_row32(W_res^T),
+    and the product reads deq(wt)^T."""
+    if w_block == "tile32":
+        return q.dequantize_tile32(w_codes, w_scales)
+    if w_block == "row32":
+        if wt is None:
+            raise ValueError("row32 weights need the quantized transpose wt")
+        return q.dequantize_row32(*wt).T
+    raise ValueError(w_block)
 
 
 def _round_out(x: np.ndarray, out_dtype: str) -> np.ndarray:
@@ -90,7 +121,8 @@ def down_proj(x_bits: np.ndarray, D: np.ndarray) -> np.ndarray:
     return q.f64_to_bf16_bits(q.bf16_bits_to_f64(x_bits) @ D)
 
 
-def linear_fwd(X, w_codes, w_scales, L1, L2, A, B, out_dtype="bf16", precision="W4A4G4"):
+def linear_fwd(X, w_codes, w_scales, L1, L2, A, B, out_dtype="bf16", precision="W4A4G4",
+               w_block="tile32"):
     """Forward of the triple-branch linear.
 
     Inputs are bf16 bit arrays except w_codes / w_scales, the 32x32-tile
@@ -105,19 +137,19 @@ def linear_fwd(X, w_codes, w_scales, L1, L2, A, B, out_dtype="bf16", precision="
     else:
         xq_codes, xq_scales = q.quantize_row32(X)
         Xh = q.dequantize_row32(xq_codes, xq_scales)      # [M, K]
-    Wh = q.dequantize_tile32(w_codes, w_scales)           # [N, K]
+    Wh = weight_fwd(w_codes, w_scales, w_block)           # [N, K]
     U = down_proj(X, stack_down(L1, A))                   # [M, R] bf16
     Y = Xh @ Wh.T + q.bf16_bits_to_f64(U) @ stack_up(L2, B)
     return {"Y": _round_out(Y, out_dtype), "U": U, "xq_codes": xq_codes, "xq_scales": xq_scales}
 
 
 def linear_bwd(dY, X, U, w_codes, w_scales, L1, L2, A, B, out_dtype="bf16",
-               grad_dtype="bf16", precision="W4A4G4"):
+               grad_dtype="bf16", precision="W4A4G4", w_block="tile32", wt=None):
     """Backward of the triple-branch linear (straight-through Q).
 
     U is the forward's saved bf16(X D).  Returns dict with dX, dA, dB, P and
     the gradient codes/scales (row32 of dY, blocks along N; None under G16,
-    which does not quantize dY).
+    which does not quantize dY).  w_block / wt: see weight_dgrad.
     """
     _check_precision(precision)
     r_s = np.asarray(L1).shape[1]
@@ -127,7 +159,7 @@ def linear_bwd(dY, X, U, w_codes, w_scales, L1, L2, A, B, out_dtype="bf16",
     else:
         gq_codes, gq_scales = q.quantize_row32(dY)
         Gh = q.dequantize_row32(gq_codes, gq_scales)      # [M, N]
-    Wh = q.dequantize_tile32(w_codes, w_scales)           # [N, K]
+    Wh = weight_dgrad(w_codes, w_scales, w_block, wt)     # [N, K]
     V = stack_up(L2, B)                                    # [R, N]
     P = down_proj(dY, V.T)                                 # [M, R] bf16
     dX = Gh @ Wh + q.bf16_bits_to_f64(P) @ stack_down(L1, A).T
@@ -140,7 +172,8 @@ def linear_bwd(dY, X, U, w_codes, w_scales, L1, L2, A, B, out_dtype="bf16",
             "gq_codes": gq_codes, "gq_scales": gq_scales}
 
 
-def linear_fwd_rows(rows, X, w_codes, w_scales, L1, L2, A, B, precision="W4A4G4"):
+def linear_fwd_rows(rows, X, w_codes, w_scales, L1, L2, A, B, precision="W4A4G4",
+                    w_block="tile32"):
     """Float64 forward outputs (Y before rounding, U) for selected rows only.
 
     Each row of the layer depends only on the same row of X, so large
@@ -153,13 +186,14 @@ def linear_fwd_rows(rows, X, w_codes, w_scales, L1, L2, A, B, precision="W4A4G4"
     else:
         xq_codes, xq_scales = q.quantize_row32(Xs)
         Xh = q.dequantize_row32(xq_codes, xq_scales)
-    Wh = q.dequantize_tile32(w_codes, w_scales)
+    Wh = weight_fwd(w_codes, w_scales, w_block)
     U = down_proj(Xs, stack_down(L1, A))
     Y = Xh @ Wh.T + q.bf16_bits_to_f64(U) @ stack_up(L2, B)
     return Y, U
 
 
-def linear_bwd_rows(rows, dY, w_codes, w_scales, L1, L2, A, B, precision="W4A4G4"):
+def linear_bwd_rows(rows, dY, w_codes, w_scales, L1, L2, A, B, precision="W4A4G4",
+                    w_block="tile32", wt=None):
     """Float64 dX before rounding, and P, for selected rows only."""
     _check_precision(precision)
     Gs = np.asarray(dY)[rows]
@@ -168,7 +202,7 @@ def linear_bwd_rows(rows, dY, w_codes, w_scales, L1, L2, A, B, precision="W4A4G4
     else:
         gq_codes, gq_scales = q.quantize_row32(Gs)
         Gh = q.dequantize_row32(gq_codes, gq_scales)
-    Wh = q.dequantize_tile32(w_codes, w_scales)
+    Wh = weight_dgrad(w_codes, w_scales, w_block, wt)
     P = down_proj(Gs, stack_up(L2, B).T)
     dX = Gh @ Wh + q.bf16_bits_to_f64(P) @ stack_down(L1, A).T
     return dX, P

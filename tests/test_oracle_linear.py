@@ -7,6 +7,9 @@
 * branch structure: zero ranks, zero residual;
 * the adjoint identity of the backbone product;
 * autograd on random inputs within bf16 rounding error;
+* group-wise (1x32) weights of the block-shape ablation: both products
+  against nibble-by-nibble triple loops, the dgrad reading its own
+  quantization of W^T, and exact autograd on lossless inputs;
 * the precision settings of Table 4: exact agreement with autograd where
   the 16-bit side reads its input unquantized, disagreement where a 4-bit
   side rounds a lossy block;
@@ -268,3 +271,72 @@ def test_rel_frobenius_basic():
     a = np.array([3.0, 4.0])
     assert L.rel_frobenius(a, a) == 0.0
     assert abs(L.rel_frobenius(np.array([3.0, 4.5]), a) - 0.1) < 1e-15
+
+
+# ---------------------------------------------------------------- row32 weights
+def _val(code, sc):
+    """One E2M1 code times its E8M0 scale, decoded by hand (exact)."""
+    grid = [Fraction(0), Fraction(1, 2), Fraction(1), Fraction(3, 2), Fraction(2),
+            Fraction(3), Fraction(4), Fraction(6)]
+    v = grid[code & 7] * (Fraction(2) ** (int(sc) - 127))
+    return -v if code & 8 else v
+
+
+def _nib(codes, r, c):
+    return (int(codes[r, c // 2]) >> (4 * (c % 2))) & 0xF
+
+
+def test_row32_weights_brute_force_both_products():
+    # Group-wise weights (the block-shape ablation's alternative): the forward
+    # reads Q_row32(W) with blocks along K, the dgrad Q_row32(W^T) with blocks
+    # along N; both decoded here nibble by nibble.
+    rng = np.random.default_rng(31)
+    M, K, N = 3, 64, 64
+    X = synth.to_bf16_bits(rng.standard_normal((M, K)))
+    dY = synth.to_bf16_bits(rng.standard_normal((M, N)))
+    W = synth.to_bf16_bits(rng.standard_normal((N, K)) * 0.1 *
+                           np.exp2(rng.integers(-6, 6, size=(N, 1))))    # rows of different scale
+    wc, ws = q.quantize_row32(W)
+    wt = q.quantize_row32(np.ascontiguousarray(W.T))
+    z = lambda r, c: np.zeros((r, c), dtype=np.uint16)
+    fwd = L.linear_fwd(X, wc, ws, z(K, 0), z(0, N), z(K, 0), z(0, N), out_dtype="f64",
+                       w_block="row32")
+    bwd = L.linear_bwd(dY, X, fwd["U"], wc, ws, z(K, 0), z(0, N), z(K, 0), z(0, N),
+                       out_dtype="f64", w_block="row32", wt=wt)
+    xc, xs = q.quantize_row32(X)
+    gc, gs = q.quantize_row32(dY)
+    for m in range(M):
+        for n in range(N):
+            acc = sum(_val(_nib(xc, m, k), xs[m, k // 32]) * _val(_nib(wc, n, k), ws[n, k // 32])
+                      for k in range(K))
+            assert float(acc) == fwd["Y"][m, n]
+        for k in range(K):
+            acc = sum(_val(_nib(gc, m, n), gs[m, n // 32]) * _val(_nib(wt[0], k, n), wt[1][k, n // 32])
+                      for n in range(N))
+            assert float(acc) == bwd["dX"][m, k]
+    # rows of different scale make the two groupings differ: the dgrad reads
+    # its own quantization of W^T, not the forward's numbers
+    assert not np.array_equal(L.weight_dgrad(wc, ws, "row32", wt), L.weight_fwd(wc, ws, "row32"))
+
+
+def test_row32_weights_exact_on_ternary_inputs():
+    c = _case_ternary(13, 8, 64, 96, 4, 3)
+    wc, ws = q.quantize_row32(c["W"])
+    wt = q.quantize_row32(np.ascontiguousarray(c["W"].T))
+    fwd = L.linear_fwd(c["X"], wc, ws, c["L1"], c["L2"], c["A"], c["B"], out_dtype="f64",
+                       w_block="row32")
+    bwd = L.linear_bwd(c["dY"], c["X"], fwd["U"], wc, ws, c["L1"], c["L2"], c["A"], c["B"],
+                       out_dtype="f64", grad_dtype="f64", w_block="row32", wt=wt)
+    Y, dX, dA, dB = _autograd(c)
+    np.testing.assert_array_equal(fwd["Y"], Y)
+    np.testing.assert_array_equal(bwd["dX"], dX)
+    np.testing.assert_array_equal(bwd["dA"], dA)
+    np.testing.assert_array_equal(bwd["dB"], dB)
+    rows = np.array([1, 6])
+    Yr, _ = L.linear_fwd_rows(rows, c["X"], wc, ws, c["L1"], c["L2"], c["A"], c["B"], w_block="row32")
+    dXr, _ = L.linear_bwd_rows(rows, c["dY"], wc, ws, c["L1"], c["L2"], c["A"], c["B"],
+                               w_block="row32", wt=wt)
+    np.testing.assert_array_equal(Yr, Y[rows])
+    np.testing.assert_array_equal(dXr, dX[rows])
+    with pytest.raises(ValueError):
+        L.weight_dgrad(wc, ws, "row32")
