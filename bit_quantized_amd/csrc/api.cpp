@@ -147,6 +147,9 @@ ft_status check_linear(const ft_linear* L) {
     return FT_EINVAL;
   if ((L->wt_codes == nullptr) != (L->wt_scales == nullptr)) return FT_EINVAL;
   if (L->precision < FT_W4A4G4 || L->precision > FT_W4A16G16) return FT_EINVAL;
+  if (L->w_block != FT_WBLOCK_TILE32 && L->w_block != FT_WBLOCK_ROW32) return FT_EINVAL;
+  // group-wise weights: 4-bit products only (the dequantizer reads tiles)
+  if (L->w_block == FT_WBLOCK_ROW32 && L->precision != FT_W4A4G4) return FT_EINVAL;
   // a 16-bit product reads the weight dequantized to bf16, with 32-bit
   // offsets over its padded rows
   if (L->precision != FT_W4A4G4 &&
@@ -303,6 +306,7 @@ size_t fourtune_workspace_bytes(const ft_linear* L, int is_bwd) {
   if (L->M > kMaxDim || L->K > kMaxDim || L->N > kMaxDim) return 0;
   if (L->r_stab < 0 || L->r_lora < 0 || L->r_stab + L->r_lora > FT_MAX_RANK) return 0;
   if (L->precision < FT_W4A4G4 || L->precision > FT_W4A16G16) return 0;
+  if (L->w_block != FT_WBLOCK_TILE32 && L->w_block != FT_WBLOCK_ROW32) return 0;
   return is_bwd ? bwd_layout(L).total : fwd_layout(L).total;
 }
 
@@ -348,6 +352,7 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
   g.M = L->M; g.RED = L->K; g.NOUT = L->N;
   g.a_codes = qc; g.a_scales = qs;
   g.b_codes = L->w_codes; g.b_scales = L->w_scales;
+  g.b_row_scales = L->w_block == FT_WBLOCK_ROW32;
   g.lm = u_pad; g.lo = v_pad; g.nlr = ft::rank_pad(R) / 32; g.out = Y;
   if (bf) {
     uint16_t* w16 = reinterpret_cast<uint16_t*>(ws + lay.w16);
@@ -424,6 +429,7 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
     g.M = L->M; g.RED = L->N; g.NOUT = L->K;
     g.a_codes = qc; g.a_scales = qs;
     g.b_codes = L->wt_codes; g.b_scales = L->wt_scales;
+    g.b_row_scales = L->w_block == FT_WBLOCK_ROW32;
     g.lm = p_pad; g.lo = d_pad; g.nlr = ft::rank_pad(R) / 32; g.out = dX;
     if (bf) {
       uint16_t* w16 = reinterpret_cast<uint16_t*>(ws + lay.w16);

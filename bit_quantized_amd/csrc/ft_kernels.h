@@ -79,7 +79,8 @@ struct GemmArgs {
   const uint8_t* a_codes;         // [M, RED/2]
   const uint8_t* a_scales;        // [M, RED/32]
   const uint8_t* b_codes;         // [NOUT, RED/2]
-  const uint8_t* b_scales;        // [NOUT/32, RED/32] (one scale per 32x32 tile)
+  const uint8_t* b_scales;        // [NOUT/32, RED/32] (one scale per 32x32 tile), or
+                                  // [NOUT, RED/32] with b_row_scales (1x32 row blocks)
   const uint16_t* lm;             // bf16 [M, 32 * nlr], may be null when nlr == 0
   const uint16_t* lo;             // bf16 [NOUT, 32 * nlr]
   int nlr;                        // 32-rank groups: 0 or 2 (rank_pad)
@@ -88,6 +89,7 @@ struct GemmArgs {
   // are not read): out = a16 b16^T + lm lo^T; RED % 32 == 0.
   const uint16_t* a16;            // bf16 [M, RED]
   const uint16_t* b16;            // bf16 [NOUT, RED]
+  int b_row_scales;               // b quantized in 1x32 row blocks (group-wise weights)
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 

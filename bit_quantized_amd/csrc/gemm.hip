@@ -153,11 +153,14 @@ template <int K> struct MfmaKind { static constexpr int v = K; };   // 0: MXFP4,
 // number of reduction steps is padded by one step whose loads are pushed
 // out of range: zero codes and zero scale bytes add exactly 0, and every
 // tile then has an even number of steps for the even/odd registers.
-// BF: the main product is bf16 x bf16 (a16, b16): its steps are rank-kind
-// steps of 32 reduction elements (64 bytes of a row, as a 4-bit step), and
-// no scales are loaded.
-template <bool LR, bool BF>
+// BMODE 0: b has one scale per 32x32 tile (the method's weight).  BMODE 1:
+// b has 1x32 row blocks like a (group-wise weights): its scale words are
+// loaded and read per row, as a's are.  BMODE 2 (BF): the main product is
+// bf16 x bf16 (a16, b16): its steps are rank-kind steps of 32 reduction
+// elements (64 bytes of a row, as a 4-bit step), and no scales are loaded.
+template <bool LR, int BMODE>
 __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
+  constexpr bool BF = BMODE == 2, BROW = BMODE == 1;
   __shared__ __attribute__((aligned(16))) uint8_t lds[NST * ST_BYTES + 4 * OUT_WAVE];
 
   const int t = threadIdx.x, lane = t & 63;
@@ -190,7 +193,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   const auto ra_codes = rsrc(BF ? static_cast<const void*>(g.a16) : g.a_codes, static_cast<uint64_t>(M) * row_bytes);
   const auto ra_sc = rsrc(g.a_scales, BF ? 0 : static_cast<uint64_t>(M) * row_sc);
   const auto rb_codes = rsrc(BF ? static_cast<const void*>(g.b16) : g.b_codes, static_cast<uint64_t>(NOUT) * row_bytes);
-  const auto rb_sc = rsrc(g.b_scales, BF ? 0 : static_cast<uint64_t>(NOUT >> 5) * row_sc);
+  const auto rb_sc = rsrc(g.b_scales, BF ? 0 : static_cast<uint64_t>(BROW ? NOUT : NOUT >> 5) * row_sc);
   const auto r_lm = rsrc(g.lm, LR ? static_cast<uint64_t>(M) * LR_BYTES : 0);
   const auto r_lo = rsrc(g.lo, LR ? static_cast<uint64_t>(NOUT) * LR_BYTES : 0);
 
@@ -216,7 +219,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
     if (c.k < my_tiles) tile_of(c.k, m0, j0);
     const uint32_t o = static_cast<uint32_t>(is_b ? j0 : m0);
     c.code = o * row_bytes;
-    c.sc = is_b ? (o >> 5) * row_sc : o * row_sc;
+    c.sc = (is_b && !BROW) ? (o >> 5) * row_sc : o * row_sc;
     c.lr = o * LR_BYTES;
   };
   auto cursor_next = [&](Cursor& c, bool is_b) {
@@ -251,7 +254,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
     h.sbase = (BF || !live || lrs || pad) ? OOB : c.sc + static_cast<uint32_t>(ks) * 4;
     uint8_t* st = lds + (c.gs & (NST - 1)) * ST_BYTES;
     h.dst = st + (is_b ? ST_A : 0) + 64 * wave * ROWB;
-    h.sdst = is_b ? st + ST_A + ST_B + ST_SA + wave * 256 : st + ST_A + ST_B + 64 * wave * 4;
+    h.sdst = is_b ? st + ST_A + ST_B + ST_SA + (BROW ? 64 * wave * 4 : wave * 256)
+                  : st + ST_A + ST_B + 64 * wave * 4;
     return h;
   };
   // DMA instruction `item` (0..4) of a half.  Offsets stay below 2^32: lane
@@ -266,7 +270,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
       // spilled, and each reload's full memory wait drained the pipeline
       uint32_t tl = static_cast<uint32_t>(t);
       asm volatile("" : "+v"(tl));
-      if (!is_b) {
+      if (!is_b || BROW) {
         dma4(h.sc, h.sdst, tl * row_sc + h.sbase);                 // row 64 wave + lane
       } else {
         const uint32_t sb = (tl < 8) ? tl * row_sc : OOB;         // wave 0, lanes 0..7
@@ -295,7 +299,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       as[i] = ssa[wm * 128 + i * 32 + l32];
-      bs[i] = ssb[wn * 4 + i];
+      bs[i] = BROW ? ssb[wn * 128 + i * 32 + l32] : ssb[wn * 4 + i];
     }
   };
 
@@ -542,6 +546,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
 // by one and code chunks past the row end read as zero.  Two LDS buffers;
 // the loads of step k+1 are in flight while step k runs.  The rank part
 // comes first, from fragments loaded straight from the padded rank rows.
+template <bool BROW>
 __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (BM + BN) * ROWB];  // 64 KB
   uint8_t* const lds_a = lds;                      // 2 A buffers
@@ -566,7 +571,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
   const auto ra_codes = rsrc(g.a_codes, static_cast<uint64_t>(M) * row_bytes);
   const auto ra_sc = rsrc(g.a_scales, static_cast<uint64_t>(M) * row_sc);
   const auto rb_codes = rsrc(g.b_codes, static_cast<uint64_t>(NOUT) * row_bytes);
-  const auto rb_sc = rsrc(g.b_scales, static_cast<uint64_t>(NOUT >> 5) * row_sc);
+  const auto rb_sc = rsrc(g.b_scales, static_cast<uint64_t>(BROW ? NOUT : NOUT >> 5) * row_sc);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -605,7 +610,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     sa_off[i] = static_cast<uint32_t>(m0 + wm * 128 + i * 32 + l32) * row_sc;
-    sb_off[i] = static_cast<uint32_t>((j0 + wn * 128 + i * 32) >> 5) * row_sc;
+    sb_off[i] = static_cast<uint32_t>(BROW ? j0 + wn * 128 + i * 32 + l32 : (j0 + wn * 128 + i * 32) >> 5) * row_sc;
   }
 
   // Loaded values are only moved into registers here; scale bytes are
@@ -627,7 +632,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
       for (int j = 0; j < 4; ++j) {
         const bool in = kb0 + j < row_sc;
         sa_raw[i][j] = bload8(ra_sc, in ? sa_off[i] + kb0 + j : OOB);
-        sb_raw[i][j] = bload8(rb_sc, (in && j0 + wn * 128 + i * 32 < NOUT) ? sb_off[i] + kb0 + j : OOB);
+        sb_raw[i][j] = bload8(rb_sc, (in && j0 + wn * 128 + i * 32 + (BROW ? l32 : 0) < NOUT) ? sb_off[i] + kb0 + j : OOB);
       }
   };
   auto store_lds = [&](int buf) {
@@ -719,17 +724,21 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     const int cus = cu_count();
     if (cus <= 0) return hipErrorInvalidDevice;
     const uint32_t grid = n < static_cast<uint32_t>(cus) ? n : static_cast<uint32_t>(cus);
-#define FT_GP(LR, BF) hipLaunchKernelGGL((k_gemm_pipe<LR, BF>), dim3(grid), dim3(256), 0, st, g)
+#define FT_GP(LR, MODE) hipLaunchKernelGGL((k_gemm_pipe<LR, MODE>), dim3(grid), dim3(256), 0, st, g)
     if (bf) {
-      if (g.nlr > 0) FT_GP(true, true); else FT_GP(false, true);
+      if (g.nlr > 0) FT_GP(true, 2); else FT_GP(false, 2);
+    } else if (g.b_row_scales) {
+      if (g.nlr > 0) FT_GP(true, 1); else FT_GP(false, 1);
     } else {
-      if (g.nlr > 0) FT_GP(true, false); else FT_GP(false, false);
+      if (g.nlr > 0) FT_GP(true, 0); else FT_GP(false, 0);
     }
 #undef FT_GP
   } else if (bf) {
     return hipErrorInvalidValue;
+  } else if (g.b_row_scales) {
+    hipLaunchKernelGGL(k_gemm<true>, dim3(n), dim3(256), 0, st, g);
   } else {
-    hipLaunchKernelGGL(k_gemm, dim3(n), dim3(256), 0, st, g);
+    hipLaunchKernelGGL(k_gemm<false>, dim3(n), dim3(256), 0, st, g);
   }
   return hipGetLastError();
 }

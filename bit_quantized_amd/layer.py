@@ -39,13 +39,15 @@ class QuantizedLinear:
     (trainable).  act_in / act_out (ops.FT_ACT_*) mark an activation before
     or after the layer: with act_in, X is the pre-activation h; with act_out,
     the backward's dY is the gradient of act(Y) and needs H = Y.  precision:
-    ops.FT_W4A4G4 (the method) .. ops.FT_W4A16G16, or its name.
+    ops.FT_W4A4G4 (the method) .. ops.FT_W4A16G16, or its name.  w_block:
+    "tile32" (the method) or "row32" (group-wise 1x32 blocks: W_res and
+    W_res^T are quantized separately, by one FT_Q_ROW32_T pass).
     """
 
     def __init__(self, W_res: torch.Tensor, L1t: torch.Tensor | None, L2: torch.Tensor | None,
                  At: torch.Tensor | None, B: torch.Tensor | None, stream=None,
                  act_in: int = ops.FT_ACT_NONE, act_out: int = ops.FT_ACT_NONE,
-                 precision=ops.FT_W4A4G4):
+                 precision=ops.FT_W4A4G4, w_block: str = "tile32"):
         N, K = W_res.shape
         self.act_in, self.act_out = int(act_in), int(act_out)
         if isinstance(precision, str):
@@ -56,23 +58,31 @@ class QuantizedLinear:
         self.r_s = 0 if L1t is None else int(L1t.shape[0])
         self.r_l = 0 if At is None else int(At.shape[0])
         self.L1t, self.L2, self.At, self.B = L1t, L2, At, B
+        self.w_block = {"tile32": ops.FT_WBLOCK_TILE32, "row32": ops.FT_WBLOCK_ROW32}[w_block]
         self.w_codes = _empty((N, K // 2), torch.uint8, dev)
-        self.w_scales = _empty((N // 32, K // 32), torch.uint8, dev)
         self.wt_codes = _empty((K, N // 2), torch.uint8, dev)
-        self.wt_scales = _empty((K // 32, N // 32), torch.uint8, dev)
-        ops.fourtune_quantize(ops.FT_Q_TILE32, W_res, N, K, K, self.w_codes, self.w_scales,
+        if self.w_block == ops.FT_WBLOCK_TILE32:
+            self.w_scales = _empty((N // 32, K // 32), torch.uint8, dev)
+            self.wt_scales = _empty((K // 32, N // 32), torch.uint8, dev)
+            mode = ops.FT_Q_TILE32
+        else:
+            self.w_scales = _empty((N, K // 32), torch.uint8, dev)
+            self.wt_scales = _empty((K, N // 32), torch.uint8, dev)
+            mode = ops.FT_Q_ROW32_T
+        ops.fourtune_quantize(mode, W_res, N, K, K, self.w_codes, self.w_scales,
                               self.wt_codes, self.wt_scales, stream=stream)
         self.device = dev
         self._ws = {}
 
     @classmethod
     def from_factors(cls, W_res, L1, L2, A, B, stream=None, act_in: int = ops.FT_ACT_NONE,
-                     act_out: int = ops.FT_ACT_NONE, precision=ops.FT_W4A4G4) -> "QuantizedLinear":
+                     act_out: int = ops.FT_ACT_NONE, precision=ops.FT_W4A4G4,
+                     w_block: str = "tile32") -> "QuantizedLinear":
         """From factors in the method's orientation (L1 [K, r_s], A [K, r_l]):
         the down-projections are copied once into the rank-major storage."""
         t = lambda x: None if x is None else x.t().contiguous()
         return cls(W_res, t(L1), L2, t(A), B, stream=stream, act_in=act_in, act_out=act_out,
-                   precision=precision)
+                   precision=precision, w_block=w_block)
 
     @property
     def a16(self) -> bool:
@@ -89,7 +99,8 @@ class QuantizedLinear:
     def desc(self, M: int) -> ops.FtLinear:
         return ops.make_linear(M, self.K, self.N, self.r_s, self.r_l, self.w_codes,
                                self.w_scales, self.wt_codes, self.wt_scales, self.L1t, self.L2,
-                               self.At, self.B, self.act_in, self.act_out, self.precision)
+                               self.At, self.B, self.act_in, self.act_out, self.precision,
+                               self.w_block)
 
     def workspace(self, M: int, is_bwd: bool):
         key = (M, bool(is_bwd))

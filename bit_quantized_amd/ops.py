@@ -20,6 +20,7 @@ FT_Q_ROW32, FT_Q_ROW32_T, FT_Q_TILE32 = 1, 2, 4
 FT_MAX_RANK = 64
 FT_ACT_NONE, FT_ACT_GELU_TANH = 0, 1
 FT_W4A4G4, FT_W4A16G4, FT_W4A4G16, FT_W4A16G16 = 0, 1, 2, 3
+FT_WBLOCK_TILE32, FT_WBLOCK_ROW32 = 0, 1
 PRECISION_NAMES = {"W4A4G4": FT_W4A4G4, "W4A16G4": FT_W4A16G4, "W4A4G16": FT_W4A4G16,
                    "W4A16G16": FT_W4A16G16}
 
@@ -43,7 +44,7 @@ class FtLinear(ctypes.Structure):
                 ("L1t", ctypes.c_void_p), ("L2", ctypes.c_void_p),
                 ("At", ctypes.c_void_p), ("B", ctypes.c_void_p),
                 ("act_in", ctypes.c_int32), ("act_out", ctypes.c_int32),
-                ("precision", ctypes.c_int32)]
+                ("precision", ctypes.c_int32), ("w_block", ctypes.c_int32)]
 
 
 _lib = None
@@ -120,17 +121,18 @@ def _check(status: int, where: str):
 
 def make_linear(M, K, N, r_stab, r_lora, w_codes, w_scales, wt_codes=None, wt_scales=None,
                 L1t=None, L2=None, At=None, B=None, act_in=FT_ACT_NONE,
-                act_out=FT_ACT_NONE, precision=FT_W4A4G4) -> FtLinear:
+                act_out=FT_ACT_NONE, precision=FT_W4A4G4,
+                w_block=FT_WBLOCK_TILE32) -> FtLinear:
     """Fill the ft_linear descriptor from tensors (device) or raw addresses.
 
     The factors are rank-major: L1t = L1^T [r_stab, K], L2 [r_stab, N],
     At = A^T [r_lora, K], B [r_lora, N].  precision: FT_W4A4G4 .. FT_W4A16G16
-    or its name."""
+    or its name; w_block: FT_WBLOCK_TILE32 or FT_WBLOCK_ROW32."""
     if isinstance(precision, str):
         precision = PRECISION_NAMES[precision]
     return FtLinear(int(M), int(K), int(N), int(r_stab), int(r_lora), _ptr(w_codes),
                     _ptr(w_scales), _ptr(wt_codes), _ptr(wt_scales), _ptr(L1t), _ptr(L2),
-                    _ptr(At), _ptr(B), int(act_in), int(act_out), int(precision))
+                    _ptr(At), _ptr(B), int(act_in), int(act_out), int(precision), int(w_block))
 
 
 def fourtune_quantize(mode, x, rows, cols, ld, codes, scales, codes_t=None, scales_t=None,

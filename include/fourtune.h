@@ -115,6 +115,18 @@ typedef enum {
   FT_W4A16G16 = 3
 } ft_precision;
 
+/* Block shape of the residual weight's quantization (FourTune, "4.3
+ * Ablation Study / Impact of Quantization Granularity", Table 5).  TILE32 is
+ * the method: 32x32 tiles, so the dgrad reads the same numbers transposed.
+ * ROW32 is the group-wise alternative: 1x32 blocks along the reduction of
+ * each product, so the forward reads Qrow32(W_res) and the dgrad a separate
+ * quantization Qrow32(W_res^T) (which FT_Q_ROW32_T of W_res writes beside
+ * the first from one read).  ROW32 requires precision FT_W4A4G4. */
+typedef enum {
+  FT_WBLOCK_TILE32 = 0,
+  FT_WBLOCK_ROW32 = 1
+} ft_wblock;
+
 #define FT_MAX_RANK 64
 
 /* One triple-branch linear layer.  Host struct; the pointers in it are device
@@ -123,9 +135,10 @@ typedef struct {
   int64_t M, K, N;            /* tokens, input features, output features            */
   int32_t r_stab, r_lora;     /* stabilizer and adapter ranks, r_stab + r_lora <= 64 */
   const uint8_t* w_codes;     /* Qtile(W_res) codes  [N, K/2]                         */
-  const uint8_t* w_scales;    /* Qtile(W_res) scales [N/32, K/32]                     */
+  const uint8_t* w_scales;    /* Qtile(W_res) scales [N/32, K/32]; ROW32: [N, K/32]   */
   const uint8_t* wt_codes;    /* the same codes transposed [K, N/2]; backward only,  */
-  const uint8_t* wt_scales;   /*   scales [K/32, N/32]; may be NULL for the forward   */
+  const uint8_t* wt_scales;   /*   scales [K/32, N/32]; may be NULL for the forward;  */
+                              /*   ROW32: Qrow32(W_res^T), scales [K, N/32]           */
   const uint16_t* L1t;        /* bf16 [r_stab, K] = L1^T  (frozen)                    */
   const uint16_t* L2;         /* bf16 [r_stab, N]  (frozen)                           */
   const uint16_t* At;         /* bf16 [r_lora, K] = A^T  (trainable)                  */
@@ -136,6 +149,7 @@ typedef struct {
   int32_t act_out;            /* FT_ACT_*: an activation follows this layer: the backward's
                                  dY is the gradient of act_out(Y), and H = Y is required */
   int32_t precision;          /* FT_W4A4G4 (0, the method) .. FT_W4A16G16                */
+  int32_t w_block;            /* FT_WBLOCK_TILE32 (0, the method) or FT_WBLOCK_ROW32    */
 } ft_linear;
 
 /* Quantize a bf16 matrix `in` [rows, cols] with row stride ld_in elements.

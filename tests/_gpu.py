@@ -37,9 +37,10 @@ def u8(t):
 class GpuCase:
     """A LinearCase resident on the device with its quantized weight."""
 
-    def __init__(self, case, precision="W4A4G4"):
+    def __init__(self, case, precision="W4A4G4", w_block="tile32"):
         self.c = case
         self.precision = precision
+        self.w_block = w_block
         self.X = up(case.X)
         self.dY = up(case.dY)
         W = up(case.W_res)
@@ -48,7 +49,7 @@ class GpuCase:
                                                   opt(case.L2) if case.r_s else None,
                                                   opt(case.A) if case.r_l else None,
                                                   opt(case.B) if case.r_l else None,
-                                                  precision=precision)
+                                                  precision=precision, w_block=w_block)
         del W
 
     def run(self, grad_f32=False):
@@ -61,7 +62,7 @@ class GpuCase:
                    P=bits_of(P)[:, :self.c.R] if self.c.R else None, gq_codes=u8(gc),
                    gq_scales=u8(gs), w_codes=u8(self.layer.w_codes),
                    w_scales=u8(self.layer.w_scales), wt_codes=u8(self.layer.wt_codes),
-                   wt_scales=u8(self.layer.wt_scales))
+                   wt_scales=u8(self.layer.wt_scales), w_block=self.w_block)
         # dA comes back as dA^T [r_l, K] (the layout of the stored A^T)
         if self.c.r_l:
             if grad_f32:
@@ -105,14 +106,19 @@ def _absdots(c):
 
 def check_weight_codes(c, got):
     """Qtile(W) and the transposed copy the backward reads, which must be
-    Qtile(W^T): the same numbers, since a 32x32 tile has one scale."""
-    wc, ws = OQ.quantize_tile32(c.W_res)
+    Qtile(W^T): the same numbers, since a 32x32 tile has one scale.  With
+    group-wise weights: Qrow32(W) and the separate Qrow32(W^T).  Returns
+    the oracle's (codes, scales) and the keyword arguments of its weight."""
+    row = got.get("w_block", "tile32") == "row32"
+    quant = OQ.quantize_row32 if row else OQ.quantize_tile32
+    wc, ws = quant(c.W_res)
     np.testing.assert_array_equal(got["w_codes"], wc)
     np.testing.assert_array_equal(got["w_scales"], ws)
-    wtc, wts = OQ.quantize_tile32(np.ascontiguousarray(c.W_res.T))
+    wtc, wts = quant(np.ascontiguousarray(c.W_res.T))
     np.testing.assert_array_equal(got["wt_codes"], wtc)
     np.testing.assert_array_equal(got["wt_scales"], wts)
-    return wc, ws
+    kw = dict(w_block="row32") if row else {}
+    return wc, ws, kw, (dict(w_block="row32", wt=(wtc, wts)) if row else {})
 
 
 def _codes_equal(got, ref, name):
@@ -125,10 +131,10 @@ def _codes_equal(got, ref, name):
 def check_full(case, got, grad_f32=False, precision="W4A4G4"):
     """Full-size oracle comparison for cases the oracle finishes in seconds."""
     c = case
-    wc, ws = check_weight_codes(c, got)
-    f = OL.linear_fwd(c.X, wc, ws, c.L1, c.L2, c.A, c.B, precision=precision)
+    wc, ws, fkw, bkw = check_weight_codes(c, got)
+    f = OL.linear_fwd(c.X, wc, ws, c.L1, c.L2, c.A, c.B, precision=precision, **fkw)
     b = OL.linear_bwd(c.dY, c.X, f["U"], wc, ws, c.L1, c.L2, c.A, c.B,
-                      grad_dtype="f32" if grad_f32 else "bf16", precision=precision)
+                      grad_dtype="f32" if grad_f32 else "bf16", precision=precision, **bkw)
     for k in ("xq_codes", "xq_scales"):
         _codes_equal(got[k], f[k], k)
     for k in ("gq_codes", "gq_scales"):
@@ -161,7 +167,7 @@ def check_full(case, got, grad_f32=False, precision="W4A4G4"):
 def check_sampled(case, got, rows, precision="W4A4G4"):
     """Large cases: outputs of sampled rows, and the adapter gradients in full."""
     c = case
-    wc, ws = check_weight_codes(c, got)
+    wc, ws, fkw, bkw = check_weight_codes(c, got)
     if "A16" in precision:
         assert got["xq_codes"] is None
     else:
@@ -174,8 +180,9 @@ def check_sampled(case, got, rows, precision="W4A4G4"):
         gc, gs = OQ.quantize_row32(c.dY[rows])
         np.testing.assert_array_equal(got["gq_codes"][rows], gc)
         np.testing.assert_array_equal(got["gq_scales"][rows], gs)
-    Y, U = OL.linear_fwd_rows(rows, c.X, wc, ws, c.L1, c.L2, c.A, c.B, precision=precision)
-    dX, P = OL.linear_bwd_rows(rows, c.dY, wc, ws, c.L1, c.L2, c.A, c.B, precision=precision)
+    Y, U = OL.linear_fwd_rows(rows, c.X, wc, ws, c.L1, c.L2, c.A, c.B, precision=precision, **fkw)
+    dX, P = OL.linear_bwd_rows(rows, c.dY, wc, ws, c.L1, c.L2, c.A, c.B, precision=precision,
+                               **bkw)
     res = {"Y": OL.rel_frobenius(got["Y"][rows], OQ.f64_to_bf16_bits(Y)),
            "dX": OL.rel_frobenius(got["dX"][rows], OQ.f64_to_bf16_bits(dX))}
     if c.R:

@@ -193,3 +193,17 @@ def test_precision_argument_errors_and_workspace():
     big = _layer(M=64, K=(1 << 16), N=(1 << 14) - 32, precision="W4A16G4")
     assert _fwd(big) == ops.FT_ESHAPE
     assert _fwd(_layer(M=64, K=(1 << 16), N=(1 << 14) - 32)) != ops.FT_ESHAPE
+
+
+def test_weight_block_argument_errors():
+    assert _fwd(_layer(w_block=2)) == ops.FT_EINVAL
+    assert _fwd(_layer(w_block=-1)) == ops.FT_EINVAL
+    assert ops.fourtune_workspace_bytes(_layer(w_block=3), False) == 0
+    # group-wise weights have no tile dequantizer: 4-bit products only
+    assert _fwd(_layer(w_block=ops.FT_WBLOCK_ROW32, precision="W4A16G4")) == ops.FT_EINVAL
+    assert _bwd(_layer(w_block=ops.FT_WBLOCK_ROW32, precision="W4A4G16")) == ops.FT_EINVAL
+    # otherwise the shape checks pass and only the missing GPU stops the call
+    assert _fwd(_layer(w_block=ops.FT_WBLOCK_ROW32)) == ops.FT_EUNSUPPORTED
+    # the workspace does not depend on the weight's block shape
+    assert (ops.fourtune_workspace_bytes(_layer(w_block=ops.FT_WBLOCK_ROW32), True)
+            == ops.fourtune_workspace_bytes(_layer(), True))

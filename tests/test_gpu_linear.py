@@ -67,6 +67,27 @@ def test_precision_w4a16g16_qkv_full_size_sampled():
     check_sampled(c, GpuCase(c, "W4A16G16").run(), _rows(c.M, seed=3), precision="W4A16G16")
 
 
+@pytest.mark.parametrize("shape", [
+    (300, 288, 544, 16, 8),      # ragged; K % 128 != 0: the register-staged kernel both ways
+    (520, 1024, 768, 32, 16),    # the pipelined kernel both ways
+    (200, 640, 384, 0, 0),       # odd step counts (padded step), no ranks
+])
+def test_row32_weights_full(shape):
+    """Group-wise (1x32) weights, the block-shape ablation's alternative: the
+    GEMMs read per-row weight scales, the dgrad a separate quantization of
+    W^T (both written by one FT_Q_ROW32_T pass, checked bit for bit)."""
+    M, K, N, rs, rl = shape
+    c = synth.flux_linear_case(f"row32w_{M}x{K}x{N}_r{rs}_{rl}", M, K, N, rs, rl, seed=M + 2 * N)
+    say("case", c.name)
+    check_full(c, GpuCase(c, w_block="row32").run())
+
+
+def test_row32_weights_qkv_full_size_sampled():
+    c = synth.qkv_case()
+    say("case", c.name, "row32 weights")
+    check_sampled(c, GpuCase(c, w_block="row32").run(), _rows(c.M, seed=4))
+
+
 def test_fp32_adapter_gradients():
     c = synth.flux_linear_case("f32grads", 200, 256, 320, 8, 16, seed=5)
     say("case", c.name)
