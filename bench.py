@@ -52,7 +52,9 @@ def parse():
     ap.add_argument("--no-fusion", action="store_true")
     ap.add_argument("--no-block", action="store_true")
     ap.add_argument("--no-precision", action="store_true")
-    ap.add_argument("--only", choices=["step", "stress", "mlp", "fusion", "block", "precision"],
+    ap.add_argument("--no-wblock", action="store_true")
+    ap.add_argument("--only", choices=["step", "stress", "mlp", "fusion", "block", "precision",
+                                       "wblock"],
                     default=None,
                     help="run only one part (for profiler runs)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -678,6 +680,82 @@ def main():
                         "tiles dequantized to bf16 by each call",
             **res,
             "time_vs_W4A4G4": {k: round(v["us_per_step"] / base, 3) for k, v in res.items()}}
+        del X0, dY0, W0
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ weight block shape
+    # The time side of the pages' block-shape ablation (section 4.3, "Impact of
+    # Quantization Granularity", Table 5): the QKV step with the method's
+    # 32x32-tile weight against group-wise 1x32 blocks, and what preparing each
+    # costs (tiles: one quantization, the transposed copy a relayout of the
+    # same numbers; groups: W and W^T quantized separately, from one read).
+    if not a.no_wblock and a.only in (None, "wblock"):
+        c = synth.qkv_case()
+        M, K, N, rs, rl = c.M, c.K, c.N, c.r_s, c.r_l
+        X0, dY0, W0 = (bf16_tensor(x, dev) for x in (c.X, c.dY, c.W_res))
+        L1, L2, A, B = (bf16_tensor(x, dev) for x in (c.L1, c.L2, c.A, c.B))
+        bt = lambda *sh: torch.empty(sh, dtype=torch.bfloat16, device=dev)
+        pflop = sum(v["flop"] for v in layer_work(M, K, N, rs, rl).values())
+        res = {}
+        for wbk in ("tile32", "row32"):
+            wsets = []
+            for s_ in range(2):
+                lay = QuantizedLinear.from_factors(torch.roll(W0, 32 * s_, 0).contiguous(), L1, L2, A, B,
+                                                   w_block=wbk)
+                wsets.append((lay, torch.roll(X0, 97 * s_, 0).contiguous(),
+                              torch.roll(dY0, 97 * s_, 0).contiguous(), bt(M, rs + rl), bt(M, N),
+                              bt(M, K), bt(rl, K), bt(rl, N), lay.workspace(M, False),
+                              lay.workspace(M, True)))
+            torch.cuda.synchronize()
+
+            def wstep(i):
+                lay, X, dY, U, Y, dX, dA, dB, wsf, wsb = wsets[i % len(wsets)]
+                d = lay.desc(M)
+                ops.fourtune_linear_fwd(d, X, Y, U, None, None, wsf, wsf.numel(), stream)
+                ops.fourtune_linear_bwd(d, dY, X, U, None, dX, dA, dB, ops.FT_BF16, None, None, None,
+                                        wsb, wsb.numel(), stream)
+
+            nst = max(5, a.steps // 5)
+            for i in range(3):
+                wstep(i)
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for i in range(nst):
+                wstep(i)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            wms = e0.elapsed_time(e1) / nst
+            ops.fourtune_timing_reset()
+            ops.fourtune_timing_enable(True)
+            for i in range(nst):
+                wstep(i)
+            # the weight's preparation: both layouts the step reads
+            lay = wsets[0][0]
+            mode = ops.FT_Q_TILE32 if wbk == "tile32" else ops.FT_Q_ROW32_T
+            for _ in range(nst):
+                ops.fourtune_quantize(mode, W0, N, K, K, lay.w_codes, lay.w_scales, lay.wt_codes,
+                                      lay.wt_scales, stream=stream)
+            torch.cuda.synchronize()
+            ops.fourtune_timing_enable(False)
+            per = {k: round(tot / cnt * 1e3, 2) for k, (tot, cnt) in ops.fourtune_timing_read().items()
+                   if cnt}
+            qname = "quant_tile32" if wbk == "tile32" else "quant_row32_t"
+            res[wbk] = {"us_per_step": round(wms * 1e3, 1), "TFLOP/s": round(pflop / (wms * 1e-3) / 1e12, 1),
+                        "kernel_avg_us": {k: v for k, v in per.items() if k != qname},
+                        "weight_prep_us": per.get(qname),
+                        "weight_bytes": N * K // 2 * 2 + (2 * (N // 32) * (K // 32) if wbk == "tile32"
+                                                          else 2 * N * K // 32)}
+            log("bench: wblock", wbk, json.dumps(res[wbk]))
+            del wsets
+            torch.cuda.empty_cache()
+        out["weight_block"] = {
+            "workload": f"QKV linear fwd+bwd (M={M}, K={K}, N={N}, r_stab={rs}, r_lora={rl}) with the "
+                        "residual weight in 32x32 tiles (the method) or 1x32 groups along each "
+                        "product's reduction (both orientations stored); weight_prep_us quantizes "
+                        f"the bf16 weight [{N}, {K}] into both layouts",
+            **res,
+            "step_time_row32_vs_tile32": round(res["row32"]["us_per_step"] / res["tile32"]["us_per_step"], 3)}
         del X0, dY0, W0
         torch.cuda.empty_cache()
 
