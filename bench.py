@@ -610,77 +610,93 @@ def main():
         del blk, by
         torch.cuda.empty_cache()
 
-    # ------------------------------------------------------------ precision settings
-    # The QKV step (fwd+bwd) in the four precision settings of the pages'
-    # precision ablation (section 4.3, Table 4).  A 16-bit side multiplies bf16
-    # by the weight tiles dequantized to bf16 in each call (as QLoRA-style
-    # training does), on the bf16 matrix cores.
-    if not a.no_precision and a.only in (None, "precision"):
+    # ------------------------------------------------------------ layer variants
+    # The QKV step (fwd+bwd) with the layer built in several ways, timed in
+    # interleaved rounds (median over rounds) so that clock drift during the
+    # run does not favour one variant: two rotated input sets per variant.
+    def qkv_variants(kws, rounds=3):
         c = synth.qkv_case()
         M, K, N, rs, rl = c.M, c.K, c.N, c.r_s, c.r_l
         X0, dY0, W0 = (bf16_tensor(x, dev) for x in (c.X, c.dY, c.W_res))
         L1, L2, A, B = (bf16_tensor(x, dev) for x in (c.L1, c.L2, c.A, c.B))
         bt = lambda *sh: torch.empty(sh, dtype=torch.bfloat16, device=dev)
-        wk = layer_work(M, K, N, rs, rl)
-        pflop = sum(v["flop"] for v in wk.values())
-        res = {}
-        for pname in ("W4A4G4", "W4A16G4", "W4A4G16", "W4A16G16"):
-            psets = []
+        sets = {}
+        for name, kw in kws.items():
+            sets[name] = []
             for s_ in range(2):
-                lay = QuantizedLinear.from_factors(torch.roll(W0, 32 * s_, 0).contiguous(), L1, L2, A, B,
-                                                   precision=pname)
-                psets.append((lay, torch.roll(X0, 97 * s_, 0).contiguous(),
-                              torch.roll(dY0, 97 * s_, 0).contiguous(), bt(M, rs + rl), bt(M, N),
-                              bt(M, K), bt(rl, K), bt(rl, N), lay.workspace(M, False),
-                              lay.workspace(M, True)))
-            torch.cuda.synchronize()
+                lay = QuantizedLinear.from_factors(torch.roll(W0, 32 * s_, 0).contiguous(), L1, L2, A, B, **kw)
+                sets[name].append((lay, torch.roll(X0, 97 * s_, 0).contiguous(),
+                                   torch.roll(dY0, 97 * s_, 0).contiguous(), bt(M, rs + rl), bt(M, N),
+                                   bt(M, K), bt(rl, K), bt(rl, N), lay.workspace(M, False),
+                                   lay.workspace(M, True)))
+        torch.cuda.synchronize()
 
-            def pstep(i):
-                lay, X, dY, U, Y, dX, dA, dB, wsf, wsb = psets[i % len(psets)]
-                d = lay.desc(M)
-                ops.fourtune_linear_fwd(d, X, Y, U, None, None, wsf, wsf.numel(), stream)
-                ops.fourtune_linear_bwd(d, dY, X, U, None, dX, dA, dB, ops.FT_BF16, None, None, None,
-                                        wsb, wsb.numel(), stream)
+        def vstep(name, i):
+            lay, X, dY, U, Y, dX, dA, dB, wsf, wsb = sets[name][i % 2]
+            d = lay.desc(M)
+            ops.fourtune_linear_fwd(d, X, Y, U, None, None, wsf, wsf.numel(), stream)
+            ops.fourtune_linear_bwd(d, dY, X, U, None, dX, dA, dB, ops.FT_BF16, None, None, None,
+                                    wsb, wsb.numel(), stream)
 
-            nst = max(5, a.steps // 5)
+        nst = max(5, a.steps // 5)
+        times = {name: [] for name in kws}
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for name in kws:
             for i in range(3):
-                pstep(i)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(nst):
-                pstep(i)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            pms = e0.elapsed_time(e1) / nst
+                vstep(name, i)
+        torch.cuda.synchronize()
+        for _ in range(rounds):
+            for name in kws:
+                e0.record(stream)
+                for i in range(nst):
+                    vstep(name, i)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                times[name].append(e0.elapsed_time(e1) / nst * 1e3)
+        res = {}
+        for name in kws:
             ops.fourtune_timing_reset()
             ops.fourtune_timing_enable(True)
             for i in range(nst):
-                pstep(i)
+                vstep(name, i)
             torch.cuda.synchronize()
             ops.fourtune_timing_enable(False)
             per = {k: round(tot / cnt * 1e3, 2) for k, (tot, cnt) in ops.fourtune_timing_read().items()
                    if cnt}
-            ent = {"us_per_step": round(pms * 1e3, 1), "TFLOP/s": round(pflop / (pms * 1e-3) / 1e12, 1),
-                   "kernel_avg_us": per}
+            res[name] = {"us_per_step": round(float(np.median(times[name])), 1),
+                         "us_per_step_rounds": [round(t, 1) for t in times[name]],
+                         "kernel_avg_us": per}
+        extra = (sets, W0, (M, K, N, rs, rl))
+        return res, extra
+
+    # ------------------------------------------------------------ precision settings
+    # The four precision settings of the pages' precision ablation (section
+    # 4.3, Table 4).  A 16-bit side multiplies bf16 by the weight tiles
+    # dequantized to bf16 in each call (as QLoRA-style training does), on the
+    # bf16 matrix cores.
+    if not a.no_precision and a.only in (None, "precision"):
+        names = ("W4A4G4", "W4A16G4", "W4A4G16", "W4A16G16")
+        res, (sets_, W0, (M, K, N, rs, rl)) = qkv_variants({n: {"precision": n} for n in names})
+        wk = layer_work(M, K, N, rs, rl)
+        pflop = sum(v["flop"] for v in wk.values())
+        for pname, ent in res.items():
+            ent["TFLOP/s"] = round(pflop / (ent["us_per_step"] * 1e-6) / 1e12, 1)
+            per = ent["kernel_avg_us"]
             # a 16-bit product runs on the bf16 matrix cores: its own peak
-            for side, kname, on in (("A16", "fwd_gemm", "A16" in pname), ("G16", "bwd_gemm_dgrad", "G16" in pname)):
+            for kname, on in (("fwd_gemm", "A16" in pname), ("bwd_gemm_dgrad", "G16" in pname)):
                 if on and kname in per:
                     ach = wk[kname]["mfma_flop"] / (per[kname] * 1e-6) / 1e12
                     ent[kname + "_bf16"] = {"achieved": round(ach, 1), "peak": PEAK_BF16_TFLOPS,
                                             "unit": "TFLOP/s", "frac": round(ach / PEAK_BF16_TFLOPS, 4)}
-            res[pname] = ent
             log("bench: precision", pname, json.dumps(ent))
-            del psets
-            torch.cuda.empty_cache()
         base = res["W4A4G4"]["us_per_step"]
         out["precision_settings"] = {
             "workload": f"QKV linear fwd+bwd (M={M}, K={K}, N={N}, r_stab={rs}, r_lora={rl}) in the "
                         "precision settings of the precision ablation; 16-bit sides read the weight "
-                        "tiles dequantized to bf16 by each call",
+                        "tiles dequantized to bf16 by each call; interleaved rounds, median",
             **res,
             "time_vs_W4A4G4": {k: round(v["us_per_step"] / base, 3) for k, v in res.items()}}
-        del X0, dY0, W0
+        del sets_, W0
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ weight block shape
@@ -690,73 +706,33 @@ def main():
     # costs (tiles: one quantization, the transposed copy a relayout of the
     # same numbers; groups: W and W^T quantized separately, from one read).
     if not a.no_wblock and a.only in (None, "wblock"):
-        c = synth.qkv_case()
-        M, K, N, rs, rl = c.M, c.K, c.N, c.r_s, c.r_l
-        X0, dY0, W0 = (bf16_tensor(x, dev) for x in (c.X, c.dY, c.W_res))
-        L1, L2, A, B = (bf16_tensor(x, dev) for x in (c.L1, c.L2, c.A, c.B))
-        bt = lambda *sh: torch.empty(sh, dtype=torch.bfloat16, device=dev)
+        res, (sets_, W0, (M, K, N, rs, rl)) = qkv_variants({w: {"w_block": w} for w in ("tile32", "row32")})
         pflop = sum(v["flop"] for v in layer_work(M, K, N, rs, rl).values())
-        res = {}
-        for wbk in ("tile32", "row32"):
-            wsets = []
-            for s_ in range(2):
-                lay = QuantizedLinear.from_factors(torch.roll(W0, 32 * s_, 0).contiguous(), L1, L2, A, B,
-                                                   w_block=wbk)
-                wsets.append((lay, torch.roll(X0, 97 * s_, 0).contiguous(),
-                              torch.roll(dY0, 97 * s_, 0).contiguous(), bt(M, rs + rl), bt(M, N),
-                              bt(M, K), bt(rl, K), bt(rl, N), lay.workspace(M, False),
-                              lay.workspace(M, True)))
-            torch.cuda.synchronize()
-
-            def wstep(i):
-                lay, X, dY, U, Y, dX, dA, dB, wsf, wsb = wsets[i % len(wsets)]
-                d = lay.desc(M)
-                ops.fourtune_linear_fwd(d, X, Y, U, None, None, wsf, wsf.numel(), stream)
-                ops.fourtune_linear_bwd(d, dY, X, U, None, dX, dA, dB, ops.FT_BF16, None, None, None,
-                                        wsb, wsb.numel(), stream)
-
-            nst = max(5, a.steps // 5)
-            for i in range(3):
-                wstep(i)
-            torch.cuda.synchronize()
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for i in range(nst):
-                wstep(i)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            wms = e0.elapsed_time(e1) / nst
+        nst = max(5, a.steps // 5)
+        for wbk, ent in res.items():
+            ent["TFLOP/s"] = round(pflop / (ent["us_per_step"] * 1e-6) / 1e12, 1)
+            lay = sets_[wbk][0][0]
+            mode = ops.FT_Q_TILE32 if wbk == "tile32" else ops.FT_Q_ROW32_T
+            qname = "quant_tile32" if wbk == "tile32" else "quant_row32_t"
             ops.fourtune_timing_reset()
             ops.fourtune_timing_enable(True)
-            for i in range(nst):
-                wstep(i)
-            # the weight's preparation: both layouts the step reads
-            lay = wsets[0][0]
-            mode = ops.FT_Q_TILE32 if wbk == "tile32" else ops.FT_Q_ROW32_T
             for _ in range(nst):
                 ops.fourtune_quantize(mode, W0, N, K, K, lay.w_codes, lay.w_scales, lay.wt_codes,
                                       lay.wt_scales, stream=stream)
             torch.cuda.synchronize()
             ops.fourtune_timing_enable(False)
-            per = {k: round(tot / cnt * 1e3, 2) for k, (tot, cnt) in ops.fourtune_timing_read().items()
-                   if cnt}
-            qname = "quant_tile32" if wbk == "tile32" else "quant_row32_t"
-            res[wbk] = {"us_per_step": round(wms * 1e3, 1), "TFLOP/s": round(pflop / (wms * 1e-3) / 1e12, 1),
-                        "kernel_avg_us": {k: v for k, v in per.items() if k != qname},
-                        "weight_prep_us": per.get(qname),
-                        "weight_bytes": N * K // 2 * 2 + (2 * (N // 32) * (K // 32) if wbk == "tile32"
-                                                          else 2 * N * K // 32)}
-            log("bench: wblock", wbk, json.dumps(res[wbk]))
-            del wsets
-            torch.cuda.empty_cache()
+            tot, cnt = ops.fourtune_timing_read()[qname]
+            ent["weight_prep_us"] = round(tot / cnt * 1e3, 2)
+            ent["weight_bytes"] = N * K + (2 * (N // 32) * (K // 32) if wbk == "tile32" else 2 * N * K // 32)
+            log("bench: wblock", wbk, json.dumps(ent))
         out["weight_block"] = {
             "workload": f"QKV linear fwd+bwd (M={M}, K={K}, N={N}, r_stab={rs}, r_lora={rl}) with the "
                         "residual weight in 32x32 tiles (the method) or 1x32 groups along each "
                         "product's reduction (both orientations stored); weight_prep_us quantizes "
-                        f"the bf16 weight [{N}, {K}] into both layouts",
+                        f"the bf16 weight [{N}, {K}] into both layouts; interleaved rounds, median",
             **res,
             "step_time_row32_vs_tile32": round(res["row32"]["us_per_step"] / res["tile32"]["us_per_step"], 3)}
-        del X0, dY0, W0
+        del sets_, W0
         torch.cuda.empty_cache()
 
     # ------------------------------------------------------------ quantizer stress
