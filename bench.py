@@ -336,12 +336,12 @@ def main():
         del X0, dY0, W0
         torch.cuda.synchronize()
 
-        def step(i):
+        def step(i, st=stream):
             lay, X, dY, U, Y, dX, dA, dB, wsf, wsb = sets[i % len(sets)]
             d = lay.desc(M)
-            ops.fourtune_linear_fwd(d, X, Y, U, None, None, wsf, wsf.numel(), stream)
+            ops.fourtune_linear_fwd(d, X, Y, U, None, None, wsf, wsf.numel(), st)
             ops.fourtune_linear_bwd(d, dY, X, U, None, dX, dA, dB, ops.FT_BF16, None, None, None, wsb,
-                                    wsb.numel(), stream)
+                                    wsb.numel(), st)
 
         for i in range(a.warmup):
             step(i)
@@ -354,6 +354,36 @@ def main():
         torch.cuda.synchronize()
         ms = e0.elapsed_time(e1) / a.steps
         log(f"bench: {ms * 1e3:.1f} us/step, {step_flop / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
+
+        # For reference, the same steps replayed from HIP graphs, one per input
+        # set (the library records no memset, so a step is eight kernel nodes).
+        # Measured slower than launching them one by one on this stack, so the
+        # headline stays with the direct launches.
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
+            for i in range(len(sets)):
+                step(i, None)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graphs = []
+        for i in range(len(sets)):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr):
+                step(i, None)
+            graphs.append(gr)
+        torch.cuda.synchronize()
+        for i in range(a.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for i in range(a.steps):
+            graphs[i % len(graphs)].replay()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms_graph = e0.elapsed_time(e1) / a.steps
+        log(f"bench: graph replay {ms_graph * 1e3:.1f} us/step")
+        del graphs
 
         # same steps again with every launch bracketed by HIP events
         ops.fourtune_timing_reset()
@@ -398,6 +428,7 @@ def main():
                          "peak": dk["peak"], "unit": dk["unit"], "frac": dk["frac"],
                          "traffic": traffic},
             "kernels": kernels,
+            "ms_per_step_graph_replay": round(ms_graph, 5),
             "ms_per_step_with_kernel_events": round(ms_instr, 5),
             "sum_kernel_us": round(sum(v["avg_us"] for v in kernels.values()), 2),
             "source_sha": sha,

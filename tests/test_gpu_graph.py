@@ -1,0 +1,73 @@
+"""The layer's forward and backward captured in one HIP graph
+(torch.cuda.graph around the C-ABI calls) and replayed.  No kernel of the
+library records a memset, so the graph holds only kernel nodes; every replay
+must reproduce the eager result bit for bit, with the program's own eager
+work and synchronizations between the replays (the kernels are
+deterministic)."""
+import numpy as np
+import pytest
+import torch
+
+from bit_quantized_amd import ops, synth
+
+from _gpu import DEV, GpuCase, require_gpu, say
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    require_gpu()
+
+
+def _buffers(lay, M):
+    bt = lambda *sh: torch.empty(sh, dtype=torch.bfloat16, device=DEV)
+    R = max(lay.R, 1)
+    return dict(Y=bt(M, lay.N), U=bt(M, R), dX=bt(M, lay.K), dA=bt(lay.r_l, lay.K),
+                dB=bt(lay.r_l, lay.N), P=bt(M, R))
+
+
+def _step(lay, M, X, dY, b, wsf, wsb):
+    d = lay.desc(M)
+    ops.fourtune_linear_fwd(d, X, b["Y"], b["U"], None, None, wsf, wsf.numel())
+    ops.fourtune_linear_bwd(d, dY, X, b["U"], None, b["dX"], b["dA"], b["dB"], ops.FT_BF16, b["P"],
+                            None, None, wsb, wsb.numel())
+
+
+@pytest.mark.parametrize("precision", ["W4A4G4", "W4A16G16"])
+def test_graph_replays_match_eager(precision):
+    c = synth.flux_linear_case("graph", 300, 288, 544, 16, 8, seed=12)
+    other = synth.flux_linear_case("graph_other", 200, 256, 320, 8, 8, seed=13)
+    say("case graph", precision)
+    g = GpuCase(c, precision)
+    lay, M = g.layer, c.M
+    X, dY = g.X, g.dY
+    b = _buffers(lay, M)
+    wsf, wsb = lay.workspace(M, False), lay.workspace(M, True)
+    _step(lay, M, X, dY, b, wsf, wsb)
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in b.items()}
+    # warm up on a side stream, then capture
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        _step(lay, M, X, dY, b, wsf, wsb)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        _step(lay, M, X, dY, b, wsf, wsb)
+    torch.cuda.synchronize()
+    g2 = GpuCase(other, precision)
+    for r in range(4):
+        for t in b.values():
+            t.fill_(0.0)
+        g2.run()                              # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in b.items():
+            np.testing.assert_array_equal(v.view(torch.int16).cpu().numpy(),
+                                          ref[k].view(torch.int16).cpu().numpy(),
+                                          err_msg=f"replay {r} {k}")
+    say("graph replays bit-identical", precision)
