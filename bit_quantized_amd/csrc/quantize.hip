@@ -468,7 +468,11 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
   constexpr int NI = 16 / RPI;
   constexpr int NT = KC / 16;                 // 16-column tiles of a split (dB)
   constexpr int LDS_PT = RP * PT * 2, LDS_XT = 4 * 16 * PT * 2;
-  constexpr int LDS_BYTES = LDS_PT + LDS_XT;
+  // per wave: the codes [16 rows][KC/2 bytes] and scales [16 rows][KC/32]
+  // of its rows in a block, gathered so that they leave as 16-byte stores
+  constexpr int CSC = 16 * (KC / 2), CSS = 16 * (KC / 32);
+  constexpr int LDS_CS = 4 * (CSC + CSS);
+  constexpr int LDS_BYTES = LDS_PT + LDS_XT + LDS_CS;
   __shared__ __attribute__((aligned(16))) uint8_t lds[LDS_BYTES];
   uint16_t* pt = reinterpret_cast<uint16_t*>(lds);
   uint16_t (*xt)[16 * PT] = reinterpret_cast<uint16_t (*)[16 * PT]>(lds + LDS_PT);
@@ -576,10 +580,11 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
 #pragma unroll
       for (int n = 0; n < NTW; ++n) dacc[c][n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
+  uint8_t* csc = lds + LDS_PT + LDS_XT + wave * (CSC + CSS);
+  uint8_t* css = csc + CSC;
   auto quant = [&](const u32x4* vin, const u32x4* hin, uint32_t b) {
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
-      const uint32_t row = b * 64 + 16 * wave + i * RPI + lrow;
       const u32x4 v = act_bf16x8<ACT>(vin[i], ACT == 2 ? hin[i] : vin[i]);
       uint32_t m = max_u16x2(max_u16x2(abs_bf16x2(v[0]), abs_bf16x2(v[1])),
                              max_u16x2(abs_bf16x2(v[2]), abs_bf16x2(v[3])));
@@ -588,10 +593,49 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
       am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0x4E, 0xF, 0xF, false)));
       const uint32_t sc8 = e8m0_from_amax_bits(am);
       const uint32_t o = encode8(v[0], v[1], v[2], v[3], e8m0_to_f32(sc8));
-      const bool ok = row < rows && col_ok;
-      buf_store32(rcodes, ok ? row * cpr + (col >> 1) : BUF_OOB, o);
-      buf_store8(rscales, ok && (lane & 3) == 0 ? row * spr + (col >> 5) : BUF_OOB, sc8);
-      *reinterpret_cast<u32x4*>(&xw[(i * RPI + lrow) * PT + lcol]) = v;
+      const int rl = i * RPI + lrow;
+      *reinterpret_cast<uint32_t*>(&csc[rl * (KC / 2) + (lcol >> 1)]) = o;
+      if ((lane & 3) == 0) css[rl * (KC / 32) + (lcol >> 5)] = static_cast<uint8_t>(sc8);
+      *reinterpret_cast<u32x4*>(&xw[rl * PT + lcol]) = v;
+    }
+    // the wave's codes leave as 16-byte pieces (one 32-value block each),
+    // its scales as one run per row where the split is whole and the rows
+    // of the scale array are 4-byte aligned, else byte by byte
+    const uint32_t row0 = b * 64 + 16 * wave;
+#pragma unroll
+    for (int q = 0; q < CSC / 1024; ++q) {
+      const int c = q * 64 + lane, rl = c / (KC / 32), pc = c % (KC / 32);
+      const uint32_t row = row0 + rl;
+      const bool ok = row < rows && cbeg + 32 * pc < cols;
+      buf_store128(rcodes, ok ? row * cpr + (cbeg >> 1) + 16 * pc : BUF_OOB,
+                   *reinterpret_cast<const u32x4*>(&csc[c * 16]));
+    }
+    // (both forms are always issued, the one not taken with out-of-range
+    // offsets: no branch, so the compiler's memory counts stay exact)
+    const bool runs = cbeg + KC <= cols && (spr & 3) == 0;
+    if constexpr (KC >= 512) {
+      // KC/32 >= 16 scale bytes per row: lane l < 16 * PPR stores 16 bytes
+      constexpr int PPR = KC / 512;               // 16-byte pieces per row
+      const int rl = lane / PPR, pc = lane % PPR;
+      const uint32_t row = row0 + rl;
+      const bool ok = runs && lane < 16 * PPR && row < rows;
+      buf_store128(rscales, ok ? row * spr + (cbeg >> 5) + 16 * pc : BUF_OOB,
+                   *reinterpret_cast<const u32x4*>(&css[lane < 16 * PPR ? lane * 16 : 0]));
+    } else {
+      // fewer than 16 scale bytes per row: 4-byte runs
+      constexpr int WPR = KC / 128;               // 4-byte words per row
+      const int rl = lane / WPR, pc = lane % WPR;
+      const uint32_t row = row0 + rl;
+      const bool ok = runs && lane < 16 * WPR && row < rows;
+      buf_store32(rscales, ok ? row * spr + (cbeg >> 5) + 4 * pc : BUF_OOB,
+                  *reinterpret_cast<const uint32_t*>(&css[lane < 16 * WPR ? lane * 4 : 0]));
+    }
+#pragma unroll
+    for (int q = 0; q < (CSS + 63) / 64; ++q) {
+      const int c = q * 64 + lane, rl = c / (KC / 32), pc = c % (KC / 32);
+      const uint32_t row = row0 + rl;
+      const bool ok = !runs && c < CSS && row < rows && cbeg + 32 * pc < cols;
+      buf_store8(rscales, ok ? row * spr + (cbeg >> 5) + pc : BUF_OOB, css[c < CSS ? c : 0]);
     }
   };
   auto mma = [&](uint32_t b, uint32_t (*uu)[4]) {
