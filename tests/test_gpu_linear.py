@@ -88,6 +88,29 @@ def test_row32_weights_qkv_full_size_sampled():
     check_sampled(c, GpuCase(c, w_block="row32").run(), _rows(c.M, seed=4))
 
 
+def _random_shapes(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for _ in range(n):
+        M = int(rng.integers(1, 700))
+        K = 32 * int(rng.integers(1, 40))
+        N = 32 * int(rng.integers(1, 40))
+        rs = int(rng.integers(0, 33))
+        rl = int(rng.integers(0, 65 - rs)) if rng.random() < 0.8 else 0
+        out.append((M, K, N, rs, min(rl, 64 - rs)))
+    return out
+
+
+@pytest.mark.parametrize("shape", _random_shapes(10, 2027))
+def test_random_shapes_full(shape):
+    """A seeded sweep of shapes: any M, K and N multiples of 32 (so both GEMM
+    kernels and every split width of the fused quantizer), ranks 0..64."""
+    M, K, N, rs, rl = shape
+    c = synth.flux_linear_case(f"rand_{M}x{K}x{N}_r{rs}_{rl}", M, K, N, rs, rl, seed=M * 7 + K + N)
+    say("case", c.name)
+    check_full(c, GpuCase(c).run())
+
+
 def test_fp32_adapter_gradients():
     c = synth.flux_linear_case("f32grads", 200, 256, 320, 8, 16, seed=5)
     say("case", c.name)
