@@ -415,10 +415,10 @@ __global__ __launch_bounds__(512) void k_quant_dual(const uint16_t* __restrict__
 // (workgroup j takes blocks j, j + G, ...).  A workgroup stages the
 // projection slice of its split [RP ranks x KC columns] in LDS once.  Each
 // wave then streams its own 16 rows of every block it visits:
-//   - loads: one instruction reads KC/8 lanes x 16 bytes of one row (1 KB
-//     contiguous for KC = 512); at KC = 512 into one of two register sets,
-//     the loads of block b + 2G issued as soon as block b is quantized, so a
-//     block is always in flight while the wave quantizes and projects;
+//   - loads: one instruction reads KC/8 lanes x 16 bytes of rows (two rows
+//     of 512 bytes at KC = 256); the loads of block b + G go out as soon as
+//     block b is quantized, so a block is in flight while the wave projects,
+//     and the two workgroups a CU holds at KC = 256 hide each other's waits;
 //   - quantize in the load layout: 4 consecutive lanes hold one 32-element
 //     block, amax by two quad DPP steps; codes go out as 4 bytes per lane
 //     (a row's codes contiguous), scales from every 4th lane;
@@ -497,12 +497,6 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
   // u[row][u_r0 + 16 c + q] of rows 16h + 4g .. 16h + 4g + 3 (the A operand
   // of a 16x16x16 MFMA).
   const int g = lane >> 4, lr = lane & 15;
-  // Two register sets at KC = 512 (one workgroup per CU): the loads of block
-  // b + 2G go out right after block b is quantized, so one block is always
-  // in flight while the wave works.  ACT 2 (two inputs) keeps one set (two
-  // would not fit in 256 VGPRs); so do narrower splits, whose several
-  // workgroups per CU hide each other's loads.
-  constexpr int NB = (ACT == 2 || NS < 4) ? 1 : 2;
   constexpr int UA = DBR > 0 ? 4 * DBR : 1;   // (row group, rank group) pairs
   auto load = [&](u32x4* v, u32x4* h, uint32_t bx) {
     // past the end stays past the end: the host keeps (rows + 64) * ld * 2
@@ -537,9 +531,9 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
         uu[hc][e] = a.u[row * static_cast<uint32_t>(a.ld_u) + a.u_r0 + r];
       }
   };
-  u32x4 va[NB][NI], ha[NI];
+  u32x4 va[NI], ha[NI];
   uint32_t bx = blockIdx.x % G;
-  load(va[0], ha, bx);
+  load(va, ha, bx);
   {
     const RankRows& p = a.pr;
     const int R = a.R;
@@ -558,7 +552,6 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
       const uint32_t o1 = (ok && r >= p.r0 && r < R) ? static_cast<uint32_t>(((r - p.r0) * p.ld + pc) * 2) : BUF_OOB;
       w[e] = buf_load128(r0s, o0) | buf_load128(r1s, o1);
     }
-    if constexpr (NB == 2) load(va[1], ha, bx + G);
 #pragma unroll
     for (int e = 0; e < PER; ++e) {
       const int c = t + 256 * e;
@@ -684,27 +677,18 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
       __syncthreads();
     }
   };
-  // one block: its adapter operand (dB), quantize, refill the register set
-  // with the block NB steps ahead, project
-  auto block = [&](u32x4* v, uint32_t b) {
+  // one block: its adapter operand (dB), quantize, refill the registers
+  // with the workgroup's next block, project.  The body is straight-line (a
+  // block past the end reads zeros and stores nothing), so the compiler's
+  // count of outstanding loads and stores stays exact.
+  auto block = [&](uint32_t b) {
     uint32_t uu[UA][4];
     if constexpr (DBR > 0) load_u(uu, b);
-    quant(v, ha, b);
-    load(v, ha, b + NB * G);
+    quant(va, ha, b);
+    load(va, ha, b + G);
     mma(b, uu);
   };
-  if constexpr (NB == 1) {
-    for (; bx < nrb; bx += G) block(va[0], bx);
-  } else {
-    // both halves run unconditionally (a block past the end reads zeros and
-    // stores nothing): with straight-line code between the loop's ends the
-    // compiler's count of outstanding loads and stores stays exact, and the
-    // waits before a set is quantized do not drain the other set's loads
-    for (; bx < nrb; bx += 2 * G) {
-      block(va[0], bx);
-      block(va[NB - 1], bx + G);
-    }
-  }
+  for (; bx < nrb; bx += G) block(bx);
   if constexpr (DBR > 0) {
     // the workgroup's partial dbpart[j][r][col]: each wave owns its columns
     const uint32_t j = blockIdx.x % G;
@@ -944,12 +928,13 @@ hipError_t launch_dequant_tile32(const uint8_t* codes, const uint8_t* scales, in
 }
 
 // Plan of the fused kernel: columns per split, splits and workgroups per
-// split.  KC: the largest of 512, 256, 128 that still gives one row block and
-// split per CU of a 256-CU part; with the dB partial (DBR rank groups) at
-// most 512 / DBR, so that its accumulators fit.  Workgroups per split: as
-// many as fit on such a part at once (LDS allows one per CU at KC = 512, two
-// at 256, four at 128), at most one per row block.  Fixed by the shapes only,
-// so the workspace size does not depend on the device.
+// split.  KC: 256 when that still gives one row block and split per CU of a
+// 256-CU part, else 128.  (KC = 512, one workgroup per CU with two register
+// sets, measured slower on every layer of a DiT block: QKV backward 46.8 ->
+// 42.1 us, MLP forward 56 -> 47.6 us at 256, while 128 was slower again.)
+// Workgroups per split: as many as fit on such a part at once (LDS allows
+// two per CU at KC = 256, four at 128), at most one per row block.  Fixed by
+// the shapes only, so the workspace size does not depend on the device.
 struct QDPlan {
   int kc;
   uint32_t nrb, splits, G;
@@ -957,10 +942,8 @@ struct QDPlan {
 static QDPlan quant_down_plan(int64_t rows, int64_t cols, int dbr) {
   QDPlan p;
   const int64_t rb = (rows + 63) / 64;
-  p.kc = 128;
-  for (int kc = 512; kc > 128; kc /= 2)
-    if (rb * ((cols + kc - 1) / kc) >= 256) { p.kc = kc; break; }
-  if (dbr > 0 && p.kc > 512 / dbr) p.kc = 512 / dbr;
+  p.kc = rb * ((cols + 255) / 256) >= 256 ? 256 : 128;
+  (void)dbr;                                   // both widths hold the dB accumulators
   p.nrb = static_cast<uint32_t>(rb);
   p.splits = static_cast<uint32_t>((cols + p.kc - 1) / p.kc);
   uint32_t G = 256u * static_cast<uint32_t>(512 / p.kc) / p.splits;
@@ -1029,8 +1012,7 @@ hipError_t launch_quant_down(const uint16_t* in, const uint16_t* in2, int act, i
   if (dbr > nrg) return hipErrorInvalidValue;
 #define FT_QD_NS(NRG)                                                                         \
   do {                                                                                        \
-    if (kc == 512) launch_qd<NRG, 4>(a, grid, act, dbr, st);                                  \
-    else if (kc == 256) launch_qd<NRG, 2>(a, grid, act, dbr, st);                             \
+    if (kc == 256) launch_qd<NRG, 2>(a, grid, act, dbr, st);                                  \
     else launch_qd<NRG, 1>(a, grid, act, dbr, st);                                            \
   } while (0)
   switch (nrg) {
