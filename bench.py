@@ -53,6 +53,9 @@ def parse():
     ap.add_argument("--no-block", action="store_true")
     ap.add_argument("--no-precision", action="store_true")
     ap.add_argument("--no-wblock", action="store_true")
+    ap.add_argument("--graph-replay", action="store_true",
+                    help="also time the step replayed from HIP graphs (reported beside the "
+                         "direct launches)")
     ap.add_argument("--only", choices=["step", "stress", "mlp", "fusion", "block", "precision",
                                        "wblock"],
                     default=None,
@@ -273,6 +276,37 @@ def copy_probe(dev, stream):
     del src, dst
 
 
+def time_graph_replay(step, sets, stream, e0, e1, a):
+    """Mean step time (ms) of the layer step replayed from HIP graphs, one
+    graph per input set, captured after a warm-up on a side stream."""
+    import torch
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        for i in range(len(sets)):
+            step(i, None)
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graphs = []
+    for i in range(len(sets)):
+        gr = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(gr):
+            step(i, None)
+        graphs.append(gr)
+    torch.cuda.synchronize()
+    for i in range(a.warmup):
+        graphs[i % len(graphs)].replay()
+    torch.cuda.synchronize()
+    e0.record(stream)
+    for i in range(a.steps):
+        graphs[i % len(graphs)].replay()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / a.steps
+    print(f"bench: graph replay {ms * 1e3:.1f} us/step", file=sys.stderr, flush=True)
+    return ms
+
+
 def main():
     a = parse()
     if a.summarize_trace:
@@ -355,35 +389,13 @@ def main():
         ms = e0.elapsed_time(e1) / a.steps
         log(f"bench: {ms * 1e3:.1f} us/step, {step_flop / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
 
-        # For reference, the same steps replayed from HIP graphs, one per input
-        # set (the library records no memset, so a step is eight kernel nodes).
-        # Measured slower than launching them one by one on this stack, so the
-        # headline stays with the direct launches.
-        side = torch.cuda.Stream()
-        side.wait_stream(stream)
-        with torch.cuda.stream(side):
-            for i in range(len(sets)):
-                step(i, None)
-        stream.wait_stream(side)
-        torch.cuda.synchronize()
-        graphs = []
-        for i in range(len(sets)):
-            gr = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(gr):
-                step(i, None)
-            graphs.append(gr)
-        torch.cuda.synchronize()
-        for i in range(a.warmup):
-            graphs[i % len(graphs)].replay()
-        torch.cuda.synchronize()
-        e0.record(stream)
-        for i in range(a.steps):
-            graphs[i % len(graphs)].replay()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        ms_graph = e0.elapsed_time(e1) / a.steps
-        log(f"bench: graph replay {ms_graph * 1e3:.1f} us/step")
-        del graphs
+        # Optionally, the same steps replayed from HIP graphs, one per input set
+        # (the library records no memset, so a step is eight kernel nodes).
+        # Measured no faster than launching them one by one on this stack, so
+        # the headline stays with the direct launches.
+        ms_graph = None
+        if a.graph_replay:
+            ms_graph = time_graph_replay(step, sets, stream, e0, e1, a)
 
         # same steps again with every launch bracketed by HIP events
         ops.fourtune_timing_reset()
@@ -428,7 +440,7 @@ def main():
                          "peak": dk["peak"], "unit": dk["unit"], "frac": dk["frac"],
                          "traffic": traffic},
             "kernels": kernels,
-            "ms_per_step_graph_replay": round(ms_graph, 5),
+            "ms_per_step_graph_replay": None if ms_graph is None else round(ms_graph, 5),
             "ms_per_step_with_kernel_events": round(ms_instr, 5),
             "sum_kernel_us": round(sum(v["avg_us"] for v in kernels.values()), 2),
             "source_sha": sha,
