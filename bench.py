@@ -14,9 +14,15 @@ quantizer stress shapes together with the dual-layout activation quantizer.
 
 Prints ONE JSON line.  `value` = algorithmic FLOP of the step / measured
 step time.  The roofline entry is for the kernel with the largest share of
-the step, timed with HIP events on the stream it runs on.
+the step, timed with HIP events on the stream it runs on.  Beside the
+headline the line carries: the oracle's CPU rate on the same layer
+(cpu_baseline), the FLUX MLP pair with its GELU glue (mlp_pair), the fused
+against the unfused low-rank branches (fusion_breakdown), all linears of a
+DiT block (dit_block), the four precision settings of the precision
+ablation (precision_settings), tiles against group-wise weights
+(weight_block) and the quantizers at the stress shapes (quantizer_stress).
 
-    python bench.py [--steps 50] [--warmup 10] [--gpus 1]
+    python bench.py [--steps 50] [--warmup 10] [--gpus 1] [--only PART]
 """
 from __future__ import annotations
 
