@@ -189,7 +189,8 @@ ft_status fourtune_dequantize(int mode, const uint8_t* codes, const uint8_t* sca
                               int64_t cols, uint16_t* out, void* stream);
 
 /* Bytes of device workspace fwd (is_bwd = 0) or bwd (is_bwd = 1) needs for
- * layer L (shapes and ranks only are read).  Returns 0 for invalid shapes. */
+ * layer L (shapes, ranks, precision and w_block only are read).  Returns 0
+ * for invalid shapes or enum values. */
 size_t fourtune_workspace_bytes(const ft_linear* L, int is_bwd);
 
 /* Forward, Eq. (2), with the fusions of "3.3 Kernel Fusion":
@@ -211,7 +212,8 @@ size_t fourtune_workspace_bytes(const ft_linear* L, int is_bwd);
  *   activation padded to 256 more rows below 2^31 bytes:
  *   (M + 256) * max(K, N) * 2 < 2^31 (the kernels use 32-bit offsets);
  *   under A16 or G16 the same for the dequantized weight,
- *   (max(K, N) + 256) * min(K, N) * 2 < 2^31; precision in 0..3.
+ *   (max(K, N) + 256) * min(K, N) * 2 < 2^31; precision in 0..3; w_block
+ *   FT_WBLOCK_TILE32 or FT_WBLOCK_ROW32 (ROW32 with FT_W4A4G4 only).
  * Errors: FT_EINVAL, FT_ESHAPE, FT_EALIGN, FT_EWORKSPACE, FT_EDEVICE. */
 ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y,
                               uint16_t* U_save, uint8_t* xq_codes, uint8_t* xq_scales,
