@@ -152,9 +152,20 @@ def cpu_baseline(rows, reps=1):
         OL.linear_bwd(dY, X, f["U"], wc, ws, c.L1, c.L2, c.A, c.B)
     dt = (time.perf_counter() - t0) / reps
     flop = sum(v["flop"] for v in layer_work(rows, c.K, c.N, c.r_s, c.r_l).values())
-    threads = max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"]
-                  or [1])
+    blas = [i for i in threadpool_info() if i.get("user_api") == "blas"]
+    threads = max([i.get("num_threads", 1) for i in blas] or [1])
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    blas_vendor = ", ".join(sorted({f"{i.get('internal_api')} {i.get('version')}" for i in blas})) or None
     return {"value": flop / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "cpu_model": cpu_model, "blas": blas_vendor,
             "seconds_per_step": round(dt, 3), "reps": reps,
             "sample": f"float64 numpy oracle, {reps} x forward+backward of the same QKV linear on "
                       f"its first {rows} of {c.M} tokens (X and dY quantization, both 4-bit products, "
@@ -434,6 +445,21 @@ def main():
         dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
         dk = kernels[dom]
         traffic = load_traffic(dom, sha)
+        # the whole step against the sum of its kernels' roofline times: a
+        # GEMM at the MXFP4 peak for its 4-bit FLOP plus the bf16 peak for its
+        # fused low-rank FLOP, every other kernel at the HBM peak for its bytes
+        roof_us = {}
+        for name, wk in work.items():
+            if wk["bound"] == "mfma":
+                t = wk["mfma_flop"] / (PEAK_FP4_TFLOPS * 1e6) + \
+                    (wk["flop"] - wk["mfma_flop"]) / (PEAK_BF16_TFLOPS * 1e6)
+            else:
+                t = wk["bytes"] / (PEAK_HBM_GBS * 1e3)
+            roof_us[name] = round(t, 2)
+        layer_roof = {"sum_roofline_us": round(sum(roof_us.values()), 2),
+                      "step_us": round(ms * 1e3, 2),
+                      "frac": round(sum(roof_us.values()) / (ms * 1e3), 4),
+                      "per_kernel_roofline_us": roof_us}
         out.update({
             "value": round(step_flop / (ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s",
             "n_gpus": 1, "steps": a.steps, "warmup": a.warmup, "ms_per_step": round(ms, 5),
@@ -449,6 +475,7 @@ def main():
             "ms_per_step_graph_replay": None if ms_graph is None else round(ms_graph, 5),
             "ms_per_step_with_kernel_events": round(ms_instr, 5),
             "sum_kernel_us": round(sum(v["avg_us"] for v in kernels.values()), 2),
+            "layer_roofline": layer_roof,
             "source_sha": sha,
         })
         del sets
@@ -748,21 +775,24 @@ def main():
         del sets_, W0
         torch.cuda.empty_cache()
 
-    # ------------------------------------------------------------ weight block shape
-    # The time side of the pages' block-shape ablation (section 4.3, "Impact of
-    # Quantization Granularity", Table 5): the QKV step with the method's
-    # 32x32-tile weight against group-wise 1x32 blocks, and what preparing each
-    # costs (tiles: one quantization, the transposed copy a relayout of the
-    # same numbers; groups: W and W^T quantized separately, from one read).
+    # ------------------------------------------------------------ weight layout
+    # The QKV step with the residual weight stored three ways: the method's
+    # 32x32 tiles stored once, the dgrad reading the same bytes transposed
+    # (section 3.2); the same tiles plus a stored transposed layout copy that
+    # the dgrad reads row-wise (twice the resident 4-bit bytes); and the
+    # group-wise 1x32 blocks of the block-shape ablation (section 4.3,
+    # "Impact of Quantization Granularity", Table 5), which need W and W^T
+    # quantized separately.  weight_bytes: resident codes and scales.
     if not a.no_wblock and a.only in (None, "wblock"):
-        res, (sets_, W0, (M, K, N, rs, rl)) = qkv_variants({w: {"w_block": w} for w in ("tile32", "row32")})
+        variants = ("tile32", "tile32_t", "row32")
+        res, (sets_, W0, (M, K, N, rs, rl)) = qkv_variants({w: {"w_block": w} for w in variants})
         pflop = sum(v["flop"] for v in layer_work(M, K, N, rs, rl).values())
         nst = max(5, a.steps // 5)
         for wbk, ent in res.items():
             ent["TFLOP/s"] = round(pflop / (ent["us_per_step"] * 1e-6) / 1e12, 1)
             lay = sets_[wbk][0][0]
-            mode = ops.FT_Q_TILE32 if wbk == "tile32" else ops.FT_Q_ROW32_T
-            qname = "quant_tile32" if wbk == "tile32" else "quant_row32_t"
+            mode = ops.FT_Q_ROW32_T if wbk == "row32" else ops.FT_Q_TILE32
+            qname = "quant_row32_t" if wbk == "row32" else "quant_tile32"
             ops.fourtune_timing_reset()
             ops.fourtune_timing_enable(True)
             for _ in range(nst):
@@ -772,15 +802,19 @@ def main():
             ops.fourtune_timing_enable(False)
             tot, cnt = ops.fourtune_timing_read()[qname]
             ent["weight_prep_us"] = round(tot / cnt * 1e3, 2)
-            ent["weight_bytes"] = N * K + (2 * (N // 32) * (K // 32) if wbk == "tile32" else 2 * N * K // 32)
+            ent["weight_bytes"] = lay.weight_bytes()
+            ent["dgrad_us"] = ent["kernel_avg_us"].get("bwd_gemm_dgrad")
             log("bench: wblock", wbk, json.dumps(ent))
         out["weight_block"] = {
             "workload": f"QKV linear fwd+bwd (M={M}, K={K}, N={N}, r_stab={rs}, r_lora={rl}) with the "
-                        "residual weight in 32x32 tiles (the method) or 1x32 groups along each "
-                        "product's reduction (both orientations stored); weight_prep_us quantizes "
-                        f"the bf16 weight [{N}, {K}] into both layouts; interleaved rounds, median",
+                        "residual weight as 32x32 tiles stored once (the method: the dgrad reads them "
+                        "transposed), the tiles plus a stored transposed copy (tile32_t), or 1x32 "
+                        "groups along each product's reduction (row32, both orientations stored); "
+                        f"weight_prep_us quantizes the bf16 weight [{N}, {K}] into the stored "
+                        "layouts; interleaved rounds, median",
             **res,
-            "step_time_row32_vs_tile32": round(res["row32"]["us_per_step"] / res["tile32"]["us_per_step"], 3)}
+            "step_time_vs_tile32": {w: round(res[w]["us_per_step"] / res["tile32"]["us_per_step"], 3)
+                                    for w in variants}}
         del sets_, W0
         torch.cuda.empty_cache()
 

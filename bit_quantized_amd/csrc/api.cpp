@@ -9,7 +9,6 @@
 #include <atomic>
 #include <cstring>
 #include <mutex>
-#include <string>
 #include <vector>
 
 #include "ft_kernels.h"
@@ -40,41 +39,43 @@ constexpr int64_t kMaxDim = int64_t(1) << 30;
 // Kernels address tensors with 32-bit buffer offsets.
 constexpr int64_t kMaxBytes = (int64_t(1) << 31) - 1;
 
-// 1 = current device is gfx950, 0 = not, -1 = unknown yet.  Cached per device.
-int g_arch_ok[64];
-std::once_flag g_arch_once;
+// 1 = current device is gfx950, 0 = not, 0 also before the first query
+// (then the query runs; racing first calls both store the same answer).
+// Cached per device.
+std::atomic<int> g_arch_ok[64];
 
 ft_status device_check() {
-  std::call_once(g_arch_once, [] {
-    for (int& v : g_arch_ok) v = -1;
-  });
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return FT_EUNSUPPORTED;
   if (dev < 0 || dev >= 64) return FT_EUNSUPPORTED;
-  if (g_arch_ok[dev] < 0) {
+  int ok = g_arch_ok[dev].load(std::memory_order_acquire);
+  if (ok == 0) {
     hipDeviceProp_t prop;
     if (hipGetDeviceProperties(&prop, dev) != hipSuccess) return FT_EUNSUPPORTED;
-    g_arch_ok[dev] = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : 0;
+    ok = std::strncmp(prop.gcnArchName, "gfx950", 6) == 0 ? 1 : -1;
+    g_arch_ok[dev].store(ok, std::memory_order_release);
   }
-  return g_arch_ok[dev] == 1 ? FT_OK : FT_EUNSUPPORTED;
+  return ok == 1 ? FT_OK : FT_EUNSUPPORTED;
 }
 
 ft_status launched(hipError_t e) { return e == hipSuccess ? FT_OK : FT_EDEVICE; }
 
 // ---- optional per-kernel timing (benchmarks): hipEvents around each launch
+// Kernel names are string literals (static storage), so the pointers handed
+// out by fourtune_timing_read stay valid for the life of the process.
 struct TimingState {
   std::mutex mu;
-  bool on = false;
+  std::atomic<bool> on{false};
   std::vector<hipEvent_t> pool;
   struct Pending { int slot; hipEvent_t a, b; };
   std::vector<Pending> pending;
-  std::vector<std::string> names;
+  std::vector<const char*> names;
   std::vector<double> total_ms;
   std::vector<int64_t> counts;
   int slot(const char* n) {
     for (size_t i = 0; i < names.size(); ++i)
-      if (names[i] == n) return static_cast<int>(i);
-    names.emplace_back(n);
+      if (std::strcmp(names[i], n) == 0) return static_cast<int>(i);
+    names.push_back(n);
     total_ms.push_back(0.0);
     counts.push_back(0);
     return static_cast<int>(names.size() - 1);
@@ -110,7 +111,7 @@ struct Timed {
   int slot = -1;
   hipStream_t st;
   Timed(const char* name, hipStream_t s) : st(s) {
-    if (!g_tm.on) return;
+    if (!g_tm.on.load(std::memory_order_relaxed)) return;
     std::lock_guard<std::mutex> lk(g_tm.mu);
     slot = g_tm.slot(name);
     a = g_tm.take();
@@ -147,7 +148,11 @@ ft_status check_linear(const ft_linear* L) {
     return FT_EINVAL;
   if ((L->wt_codes == nullptr) != (L->wt_scales == nullptr)) return FT_EINVAL;
   if (L->precision < FT_W4A4G4 || L->precision > FT_W4A16G16) return FT_EINVAL;
-  if (L->w_block != FT_WBLOCK_TILE32 && L->w_block != FT_WBLOCK_ROW32) return FT_EINVAL;
+  if (L->w_block != FT_WBLOCK_TILE32 && L->w_block != FT_WBLOCK_ROW32 &&
+      L->w_block != FT_WBLOCK_TILE32_T)
+    return FT_EINVAL;
+  // the method's tiles serve the dgrad as they are: no second weight
+  if (L->w_block == FT_WBLOCK_TILE32 && L->wt_codes) return FT_EINVAL;
   // group-wise weights: 4-bit products only (the dequantizer reads tiles)
   if (L->w_block == FT_WBLOCK_ROW32 && L->precision != FT_W4A4G4) return FT_EINVAL;
   // a 16-bit product reads the weight dequantized to bf16, with 32-bit
@@ -262,6 +267,7 @@ ft_status fourtune_quantize(int mode, const uint16_t* in, int64_t rows, int64_t 
     return FT_EINVAL;
   }
   if (rows < 0 || cols < 0 || rows > kMaxDim || cols > kMaxDim) return FT_ESHAPE;
+  if (ld_in < 0 || ld_in > kMaxDim) return FT_ESHAPE;
   if (rows * ld_in * 2 > kMaxBytes) return FT_ESHAPE;
   if (cols & 31) return FT_ESHAPE;
   if (mode != FT_Q_ROW32 && (rows & 31)) return FT_ESHAPE;
@@ -306,7 +312,9 @@ size_t fourtune_workspace_bytes(const ft_linear* L, int is_bwd) {
   if (L->M > kMaxDim || L->K > kMaxDim || L->N > kMaxDim) return 0;
   if (L->r_stab < 0 || L->r_lora < 0 || L->r_stab + L->r_lora > FT_MAX_RANK) return 0;
   if (L->precision < FT_W4A4G4 || L->precision > FT_W4A16G16) return 0;
-  if (L->w_block != FT_WBLOCK_TILE32 && L->w_block != FT_WBLOCK_ROW32) return 0;
+  if (L->w_block != FT_WBLOCK_TILE32 && L->w_block != FT_WBLOCK_ROW32 &&
+      L->w_block != FT_WBLOCK_TILE32_T)
+    return 0;
   return is_bwd ? bwd_layout(L).total : fwd_layout(L).total;
 }
 
@@ -383,7 +391,9 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
   const int R = L->r_stab + L->r_lora;
   const int rl = L->r_lora;
   if (!dY) return FT_EINVAL;
-  if (dX && !L->wt_codes) return FT_EINVAL;
+  // a separately stored dgrad weight (group-wise blocks, or the tiles'
+  // transposed layout copy) is needed only for dX
+  if (dX && L->w_block != FT_WBLOCK_TILE32 && !L->wt_codes) return FT_EINVAL;
   if (grad_dtype != FT_BF16 && grad_dtype != FT_F32) return FT_EINVAL;
   if (rl > 0 && (!X || !U_save || !dA || !dB)) return FT_EINVAL;
   if (L->act_out != FT_ACT_NONE && !H) return FT_EINVAL;
@@ -415,10 +425,13 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
   const uint16_t* h2 = act ? H : nullptr;
   if (R > 0) {
     Timed tm("bwd_quant_down", st);
+    // the pipelined dgrad on the forward's tiles (N % 128 == 0, 4-bit)
+    // reads [L1 | A] as nibble planes through its transposing b read
+    const bool planes = L->w_block == FT_WBLOCK_TILE32 && !bf && (L->N % 128) == 0;
     e = tm.done(ft::launch_quant_down(dY, h2, act, L->M, L->N, L->N, qc, qs, rows_V(L), P, p_pad,
                                       rows_Dt(L), dX ? L->K : 0, d_pad,
                                       reinterpret_cast<float*>(ws + lay.part),
-                                      db_fused ? &db : nullptr, st));
+                                      db_fused ? &db : nullptr, st, planes));
   } else if (!bf) {
     Timed tm("bwd_quant_down", st);
     e = tm.done(ft::launch_quant_row32(dY, h2, act, L->M, L->N, L->N, qc, qs, st));
@@ -428,16 +441,26 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
     ft::GemmArgs g{};
     g.M = L->M; g.RED = L->N; g.NOUT = L->K;
     g.a_codes = qc; g.a_scales = qs;
-    g.b_codes = L->wt_codes; g.b_scales = L->wt_scales;
-    g.b_row_scales = L->w_block == FT_WBLOCK_ROW32;
+    if (L->w_block == FT_WBLOCK_TILE32) {
+      // the forward's tiles [N, K/2], read transposed (section 3.2)
+      g.b_codes = L->w_codes; g.b_scales = L->w_scales;
+      g.b_transposed = 1;
+    } else {
+      g.b_codes = L->wt_codes; g.b_scales = L->wt_scales;
+      g.b_row_scales = L->w_block == FT_WBLOCK_ROW32;
+    }
     g.lm = p_pad; g.lo = d_pad; g.nlr = ft::rank_pad(R) / 32; g.out = dX;
     if (bf) {
       uint16_t* w16 = reinterpret_cast<uint16_t*>(ws + lay.w16);
       {
         Timed tm("bwd_dequant_w", st);
-        if (tm.done(ft::launch_dequant_tile32(L->wt_codes, L->wt_scales, L->K, L->N, w16, st)) != hipSuccess)
-          return FT_EDEVICE;
+        const hipError_t de =
+            L->w_block == FT_WBLOCK_TILE32
+                ? ft::launch_dequant_tile32_t(L->w_codes, L->w_scales, L->N, L->K, w16, st)
+                : ft::launch_dequant_tile32(L->wt_codes, L->wt_scales, L->K, L->N, w16, st);
+        if (tm.done(de) != hipSuccess) return FT_EDEVICE;
       }
+      g.b_transposed = 0;
       const uint16_t* g16p = dY;
       if (act) {
         uint16_t* ga = reinterpret_cast<uint16_t*>(ws + lay.g16);
@@ -496,8 +519,7 @@ ft_status fourtune_act_bwd(int act, const uint16_t* h, const uint16_t* g, int64_
 }
 
 void fourtune_timing_enable(int on) {
-  std::lock_guard<std::mutex> lk(g_tm.mu);
-  g_tm.on = on != 0;
+  g_tm.on.store(on != 0, std::memory_order_relaxed);
 }
 
 void fourtune_timing_reset(void) {
@@ -512,7 +534,7 @@ int fourtune_timing_read(const char** names, double* total_ms, int64_t* counts, 
   g_tm.drain();
   const int n = static_cast<int>(g_tm.names.size());
   for (int i = 0; i < n && i < max_entries; ++i) {
-    if (names) names[i] = g_tm.names[i].c_str();
+    if (names) names[i] = g_tm.names[i];
     if (total_ms) total_ms[i] = g_tm.total_ms[i];
     if (counts) counts[i] = g_tm.counts[i];
   }

@@ -42,7 +42,9 @@ inline int rank_pad(int R) { return R > 0 ? 64 : 0; }
 // (pr rank-major, `cols` values per rank), as two launches (partial sums per
 // column range into `part`, then their ordered sum).  Also writes out_pad
 // [rows, rank_pad(R)], the same values zero-padded, and the transposed copy
-// cp_dst [cp_rows, rank_pad(R)] of the rank-major operand cp.  `part` needs
+// cp_dst [cp_rows, rank_pad(R)] of the rank-major operand cp (cp_planes: cp
+// as the nibble planes [256, cp_rows / 2] bytes of the GEMM's transposing
+// b read, same size; quantize.hip, copy_rank_planes).  `part` needs
 // quant_down_part_bytes(rows, cols, R, db ? db->rl : 0) bytes.
 // db (backward, optional): also the adapter-gradient partials
 //   db->part[j][r][c] = sum over the rows workgroup j of a split visits of
@@ -59,7 +61,7 @@ hipError_t launch_quant_down(const uint16_t* in, const uint16_t* in2, int act, i
                              int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
                              const RankRows& pr, uint16_t* out_lr, uint16_t* out_pad,
                              const RankRows& cp, int64_t cp_rows, uint16_t* cp_dst, float* part,
-                             const DbFuse* db, hipStream_t st);
+                             const DbFuse* db, hipStream_t st, bool cp_planes = false);
 size_t quant_down_part_bytes(int64_t rows, int64_t cols, int R, int rl_db);
 int quant_down_db_chunks(int64_t rows, int64_t cols, int rl);   // 0: dB is not fused for this rl
 size_t quant_down_db_bytes(int64_t rows, int64_t cols, int rl);
@@ -69,10 +71,15 @@ size_t quant_down_db_bytes(int64_t rows, int64_t cols, int rl);
 // cols % 32 == 0.
 hipError_t launch_dequant_tile32(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                  int64_t cols, uint16_t* out, hipStream_t st);
+// The same, written transposed: out [cols, rows].
+hipError_t launch_dequant_tile32_t(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                   int64_t cols, uint16_t* out, hipStream_t st);
 
 // gemm.hip: out[m][j] = sum_red deq(a)[m][red] deq(b)[j][red] + sum_r lm[m][r] lo[j][r]
 // forward: a = Qrow(X) [M, K], b = Qtile(W) [N, K], lm = U, lo = [L2^T | B^T]
-// dgrad  : a = Qrow(dY) [M, N], b = Qtile(W)^T [K, N], lm = P, lo = [L1 | A]
+// dgrad  : a = Qrow(dY) [M, N], b = Qtile(W) [N, K] read transposed
+//          (b_transposed), lm = P, lo = [L1 | A] (with b_transposed and a
+//          reduction that is a multiple of 128: lo as nibble planes)
 // The rank operands are the zero-padded copies, rank_pad(R) = 32 * nlr ranks.
 struct GemmArgs {
   int64_t M, RED, NOUT;           // rows, reduction length, output columns
@@ -90,6 +97,10 @@ struct GemmArgs {
   const uint16_t* a16;            // bf16 [M, RED]
   const uint16_t* b16;            // bf16 [NOUT, RED]
   int b_row_scales;               // b quantized in 1x32 row blocks (group-wise weights)
+  // b given as the 32x32-tile weight of the other product, stored
+  // [RED, NOUT/2] with tile scales [RED/32, NOUT/32]: b[j][red] is read as
+  // element (red, j) (the dgrad on the forward's weight)
+  int b_transposed;
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 

@@ -4,16 +4,18 @@
 //   forward, Eq. (2):  Y  = GEMM4(Q(X), Q(R)) + X L_stab + X (A B)
 //   dgrad,   Eq. (3):  dX = GEMM4(Q(G), Q(R)^T) + G L_stab^T + G (A B)^T
 // "3.2": the weight is quantized in square 32x32 tiles, so the transposed
-// product uses the same codes and scales; they are kept a second time in
-// transposed order (a layout copy of the same numbers, made when the weight
-// is quantized), which makes both products the same kernel.  "3.3 Kernel
+// product reads the same codes and scales: the dgrad stages [reduction rows
+// x output columns] pieces of the one packed weight in LDS and takes its
+// operand fragments with the 4-bit transposing LDS read (ds_read_b64_tr_b4),
+// and each 32x32 tile's scale byte serves both directions.  "3.3 Kernel
 // Fusion / LoRA Fusion": the 4-bit product and the up-projections are
 // accumulated together and the output is written once.
 //
 // One kernel computes, for both directions,
 //   out[m][j] = sum_red deq(a)[m][red] deq(b)[j][red] + sum_r lm[m][r] lo[j][r]
 //   forward: a = Qrow(X) [M, K],  b = Qtile(W) [N, K],   lm = U, lo = [L2^T | B^T]
-//   dgrad  : a = Qrow(G) [M, N],  b = Qtile(W)^T [K, N], lm = P, lo = [L1 | A]
+//   dgrad  : a = Qrow(G) [M, N],  b = Qtile(W) [N, K] read transposed,
+//            lm = P, lo = [L1 | A]
 // with lm and lo zero-padded to 32 * nlr ranks (written that way by the
 // fused quantize + down-projection kernel that runs just before).
 //
@@ -134,11 +136,22 @@ constexpr int waitcnt_imm(int vm, int lgkm) {
   return (vm & 0xF) | ((vm >> 4) << 14) | (7 << 4) | (lgkm << 8);
 }
 
+// The LDS destination of a DMA goes in as an opaque (wave-uniform) LDS
+// address.  The compiler then does not track the DMA's LDS write, and adds
+// no memory wait of its own before the LDS reads of the stages, which the
+// kernel orders itself (explicit vmcnt waits and barriers per stage).  With
+// the destination visible it drains every DMA in flight (vmcnt(0)) before
+// each ds_read_b64_tr_b4.
+__device__ __forceinline__ FT_LDS void* opaque_lds(uint8_t* p) {
+  uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((FT_LDS uint8_t*)(p)));
+  asm volatile("" : "+s"(a));
+  return (FT_LDS void*)(static_cast<uintptr_t>(a));
+}
 __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FT_LDS void*)(lds), 16, (int)off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, opaque_lds(lds), 16, (int)off, 0, 0, 0);
 }
 __device__ __forceinline__ void dma4(__amdgpu_buffer_rsrc_t r, uint8_t* lds, uint32_t off) {
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (FT_LDS void*)(lds), 4, (int)off, 0, 0, 0);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, opaque_lds(lds), 4, (int)off, 0, 0, 0);
 }
 
 // Fragments and scales of one step: chunk 0 (a0, b0), chunk 1 (a1, b1).
@@ -148,6 +161,7 @@ struct Frags {
 };
 
 template <int K> struct MfmaKind { static constexpr int v = K; };   // 0: MXFP4, 1: bf16 ranks
+template <bool B> struct Flag { static constexpr bool v = B; };
 
 // LR: the tiles start with two rank steps (64 padded ranks).  An odd
 // number of reduction steps is padded by one step whose loads are pushed
@@ -158,10 +172,20 @@ template <int K> struct MfmaKind { static constexpr int v = K; };   // 0: MXFP4,
 // loaded and read per row, as a's are.  BMODE 2 (BF): the main product is
 // bf16 x bf16 (a16, b16): its steps are rank-kind steps of 32 reduction
 // elements (64 bytes of a row, as a 4-bit step), and no scales are loaded.
+// BMODE 3 (BT): b is the 32x32-tile weight stored [RED, NOUT/2] (the dgrad
+// reading the forward's weight): a 4-bit step stages 128 reduction rows x
+// 128 bytes (256 output columns) in LDS, 16-byte slots swizzled by
+// (row >> 1) & 7, and each operand fragment is two ds_read_b64_tr_b4 (16
+// reduction rows of 16 columns per 16-lane group), conflict-free per half
+// wave; the tile scales of a step are 4 runs of 8 bytes (one per reduction
+// block, strided by NOUT/32), loaded as 3 aligned words each and turned
+// into per-column words (byte j = reduction block j) by byte permutes.
 template <bool LR, int BMODE>
 __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
-  constexpr bool BF = BMODE == 2, BROW = BMODE == 1;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * ST_BYTES + 4 * OUT_WAVE];
+  constexpr bool BF = BMODE == 2, BROW = BMODE == 1, BT = BMODE == 3;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[NST * ST_BYTES];
+  // the output strips: a separate LDS object (the stages are DMA targets)
+  __shared__ __attribute__((aligned(16))) uint8_t lds_out[4 * OUT_WAVE];
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -192,10 +216,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   constexpr uint32_t LR_BYTES = 64 * 2;                  // a padded rank row: 64 bf16
   const auto ra_codes = rsrc(BF ? static_cast<const void*>(g.a16) : g.a_codes, static_cast<uint64_t>(M) * row_bytes);
   const auto ra_sc = rsrc(g.a_scales, BF ? 0 : static_cast<uint64_t>(M) * row_sc);
-  const auto rb_codes = rsrc(BF ? static_cast<const void*>(g.b16) : g.b_codes, static_cast<uint64_t>(NOUT) * row_bytes);
-  const auto rb_sc = rsrc(g.b_scales, BF ? 0 : static_cast<uint64_t>(BROW ? NOUT : NOUT >> 5) * row_sc);
+  // BT: b rows are reduction rows of NOUT/2 bytes; its scale grid is
+  // [RED/32, NOUT/32], read in whole aligned words (the size is rounded up
+  // to a word so the last bytes are not cut off by the range check)
+  const uint32_t bt_row = static_cast<uint32_t>(NOUT >> 1), bt_ks = static_cast<uint32_t>(NOUT >> 5);
+  const auto rb_codes = rsrc(BF ? static_cast<const void*>(g.b16) : g.b_codes,
+                             BT ? static_cast<uint64_t>(RED) * bt_row : static_cast<uint64_t>(NOUT) * row_bytes);
+  const auto rb_sc = rsrc(g.b_scales, BF ? 0
+                                      : BT ? ((static_cast<uint64_t>(RED >> 5) * bt_ks + 3) & ~uint64_t(3))
+                                           : static_cast<uint64_t>(BROW ? NOUT : NOUT >> 5) * row_sc);
   const auto r_lm = rsrc(g.lm, LR ? static_cast<uint64_t>(M) * LR_BYTES : 0);
-  const auto r_lo = rsrc(g.lo, LR ? static_cast<uint64_t>(NOUT) * LR_BYTES : 0);
+  // BT: lo is given as nibble planes, [2 rank steps x 128 rows, NOUT/2]
+  // bytes (see half_dma)
+  const auto r_lo = rsrc(g.lo, !LR ? 0 : BT ? static_cast<uint64_t>(256) * bt_row
+                                         : static_cast<uint64_t>(NOUT) * LR_BYTES);
 
   // Per-lane parts of the DMA source offsets (rows relative to the tile
   // origin; A and B tiles have the same shape).  Instruction q of wave w
@@ -206,6 +240,25 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
     const uint32_t row = 64 * wave + 16 * q + (lane >> 2), ch = (lane & 3) ^ swz16(row);
     code_row[q] = row * row_bytes + (ch << 4);
     lr_row[q] = row * LR_BYTES + (ch << 4);
+  }
+  // BT keeps lane constants only; the rest of each offset is wave-uniform.
+  //  - rows 64 wave + 16 q + lane / 4: the chunk swizzle (row >> 2) & 3 is
+  //    (lane >> 4) for every q, so lane part (lane >> 2) * pitch + chunk;
+  //  - stored rows 32 wave + 8 q + lane / 8 of a BT 4-bit step of b: the
+  //    slot swizzle (row >> 1) & 7 is (lane >> 4) ^ 4 (q & 1), so two lane
+  //    parts, for even and odd q;
+  //  - fragment reads (read_frags_bt): see there.
+  uint32_t bt_ca = 0, bt_cl = 0, bt_p[2] = {0, 0}, bt_fb = 0, bt_lc = 0;
+  if constexpr (BT) {
+    bt_lc = l32 * ROWB + ((grp ^ ((l32 >> 2) & 3)) << 4);
+    const uint32_t ch = (lane & 3) ^ (lane >> 4);
+    bt_ca = (lane >> 2) * row_bytes + (ch << 4);
+    bt_cl = (lane >> 2) * LR_BYTES + (ch << 4);
+    const uint32_t sl = (lane & 7) ^ (lane >> 4);
+    bt_p[0] = (lane >> 3) * bt_row + (sl << 4);
+    bt_p[1] = (lane >> 3) * bt_row + ((sl ^ 4) << 4);
+    const uint32_t q = lane & 15, hf = (lane >> 4) & 1, sw = (q >> 1) & 7;
+    bt_fb = (32 * (lane >> 5) + q) * 128 + 8 * hf + (((4 * wn) ^ (sw & 4)) << 4) + ((sw & 3) << 4);
   }
 
   // DMA cursor: the (tile, step) whose A or B half is loaded next, with the
@@ -218,8 +271,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
     int64_t m0 = 0, j0 = 0;
     if (c.k < my_tiles) tile_of(c.k, m0, j0);
     const uint32_t o = static_cast<uint32_t>(is_b ? j0 : m0);
-    c.code = o * row_bytes;
-    c.sc = (is_b && !BROW) ? (o >> 5) * row_sc : o * row_sc;
+    if (BT && is_b) {
+      // the tile's first byte column and scale column of every stored row
+      c.code = o >> 1;
+      c.sc = o >> 5;
+    } else {
+      c.code = o * row_bytes;
+      c.sc = (is_b && !BROW) ? (o >> 5) * row_sc : o * row_sc;
+    }
     c.lr = o * LR_BYTES;
   };
   auto cursor_next = [&](Cursor& c, bool is_b) {
@@ -250,8 +309,17 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
     h.rows = lrs ? (is_b ? r_lo : r_lm) : (is_b ? rb_codes : ra_codes);
     h.sc = is_b ? rb_sc : ra_sc;
     const bool pad = !lrs && ks >= nks_real;                 // the padding step
-    h.base = (!live || pad) ? OOB : (lrs ? c.lr + static_cast<uint32_t>(c.s) * 64 : c.code + static_cast<uint32_t>(ks) * 64);
-    h.sbase = (BF || !live || lrs || pad) ? OOB : c.sc + static_cast<uint32_t>(ks) * 4;
+    const bool bt = BT && is_b;
+    // a 4-bit step advances 128 reduction elements: 64 bytes along a row, or
+    // (BT) 128 stored rows, and 4 scale bytes along a row or (BT) 4 rows of
+    // the scale grid
+    // BT b: rank steps too read 128 stored rows (of lo's nibble planes)
+    const uint32_t kstep = bt ? static_cast<uint32_t>(lrs ? c.s : ks) * 128 * bt_row
+                              : static_cast<uint32_t>(ks) * 64;
+    const uint32_t sstep = bt ? static_cast<uint32_t>(ks) * 4 * bt_ks : static_cast<uint32_t>(ks) * 4;
+    h.base = (!live || pad) ? OOB
+             : (lrs && !bt) ? c.lr + static_cast<uint32_t>(c.s) * 64 : c.code + kstep;
+    h.sbase = (BF || !live || lrs || pad) ? OOB : c.sc + sstep;
     uint8_t* st = lds + (c.gs & (NST - 1)) * ST_BYTES;
     h.dst = st + (is_b ? ST_A : 0) + 64 * wave * ROWB;
     h.sdst = is_b ? st + ST_A + ST_B + ST_SA + (BROW ? 64 * wave * 4 : wave * 256)
@@ -262,7 +330,21 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   // parts are below 2^31 and OOB is 2^31.
   auto dma = [&](const HalfDma& h, int item, bool is_b) {
     if (item < 4) {
-      const uint32_t lane_off = h.lr ? lr_row[item] : code_row[item];
+      uint32_t lane_off;
+      if constexpr (BT) {
+        // BT 4-bit step of b: stored row 32 wave + 8 item + lane / 8 (1 KB =
+        // 8 rows of 128 bytes per instruction), physical slot lane % 8
+        // holding logical slot (lane % 8) ^ ((row >> 1) & 7); otherwise as
+        // above.  Lane constants plus a uniform part, one selected: no branch.
+        uint32_t tp = bt_p[item & 1], ca = bt_ca, cl = bt_cl;
+        asm volatile("" : "+v"(tp), "+v"(ca), "+v"(cl));
+        const uint32_t t_off = tp + static_cast<uint32_t>(32 * wave + 8 * item) * bt_row;
+        const uint32_t r_off = h.lr ? cl + static_cast<uint32_t>(64 * wave + 16 * item) * LR_BYTES
+                                    : ca + static_cast<uint32_t>(64 * wave + 16 * item) * row_bytes;
+        lane_off = is_b ? t_off : r_off;
+      } else {
+        lane_off = h.lr ? lr_row[item] : code_row[item];
+      }
       dma16(h.rows, h.dst + item * 16 * ROWB, lane_off + h.base);
     } else {
       // the scale lane offsets are recomputed from an opaque copy of the
@@ -272,26 +354,80 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
       asm volatile("" : "+v"(tl));
       if (!is_b || BROW) {
         dma4(h.sc, h.sdst, tl * row_sc + h.sbase);                 // row 64 wave + lane
+      } else if constexpr (BT) {
+        // wave 0, lanes 4 j + d (d < 3): word d of the run of reduction
+        // block j, from the aligned word at or below the run's start
+        const uint32_t j = tl >> 2, d = tl & 3;
+        const uint32_t sb = (tl < 16 && d < 3) ? ((j * bt_ks) & ~3u) + 4 * d : OOB;
+        dma4(h.sc, h.sdst, sb == OOB ? OOB : sb + h.sbase);
       } else {
         const uint32_t sb = (tl < 8) ? tl * row_sc : OOB;         // wave 0, lanes 0..7
         dma4(h.sc, h.sdst, sb == OOB ? OOB : sb + h.sbase);
       }
     }
   };
-  auto read_frags = [&](int buf, int c, u32x4 (&af)[4], u32x4 (&bf)[4]) {
+  auto read_frags_rows = [&](int buf, int c, u32x4 (&af)[4], u32x4 (&bf)[4], bool with_b) {
     const uint8_t* st = lds + buf * ST_BYTES;
+    if constexpr (BT) {
+      // a's lane part from an opaque copy of a lane constant: the compiler
+      // otherwise precomputes an address per fragment and chunk, and spills
+      // them in this variant.  Row 32 i + l32 of the wave's half; chunk
+      // (2 c + grp) ^ ((l32 >> 2) & 3) is c = 0's with byte bit 5 toggled.
+      uint32_t lc = bt_lc;
+      asm volatile("" : "+v"(lc));
+      const uint32_t base = static_cast<uint32_t>(buf * ST_BYTES + wm * 128 * ROWB) + (lc ^ (32u * c));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) af[i] = lds_read_b128(lds + base + i * 32 * ROWB);
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wm * 128 + i * 32 + l32;
       af[i] = lds_read_b128(st + row * ROWB + (((2 * c + grp) ^ swz16(row)) << 4));
     }
+    if (!with_b) return;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = wn * 128 + i * 32 + l32;
       bf[i] = lds_read_b128(st + ST_A + row * ROWB + (((2 * c + grp) ^ swz16(row)) << 4));
     }
   };
-  // raw scale words (the lane's byte is selected later by a shift)
+  // BT, a 4-bit step: the b fragments of chunk c from the stored reduction
+  // rows.  Lane (column half hf = bit 4, reduction group grp, q = lane % 16)
+  // addresses reduction row 64 c + 32 grp + 16 h + q at the 8 bytes of
+  // columns 16 hf .. 16 hf + 15 of its 32-column tile; the transposing read
+  // hands lane q of each 16-lane group those 16 rows of column q, so two
+  // reads (h = 0, 1) give a lane its 32 reduction values in nibble order.
+  // The slot of column tile i is (4 wn + i) ^ sw, sw = (row >> 1) & 7 =
+  // (q >> 1) & 7 for every row read, = ((4 wn) ^ (sw & 4)) | (i ^ (sw & 3)):
+  // with the lane constant bt_fb (holding the i = 0 slot) and a uniform part
+  // that is a multiple of 256, tile i's address is (uniform + bt_fb) ^ 16 i.
+  // Each address is one integer offset from the LDS array: longer address
+  // chains lose the array's alias information on the way to the
+  // memory-wait pass, which then drains every DMA in flight before the read.
+  auto read_frags_bt = [&](int buf, int c, u32x4 (&bf)[4]) {
+    uint32_t fb = bt_fb;
+    asm volatile("" : "+v"(fb));
+    const uint32_t rb = static_cast<uint32_t>(buf * ST_BYTES + ST_A + 64 * c * 128) + fb;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint32_t a = rb ^ (16u * i);
+      asm volatile("" : "+v"(a));
+      const u32x2 lo = lds_read_tr4(lds + a);
+      const u32x2 hi = lds_read_tr4(lds + a + 16 * 128);
+      bf[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+    }
+  };
+  // Fragments of chunk c of a step; bt (a Flag): b read transposed (every
+  // BT step: a rank step's lo comes as nibble planes that this read turns
+  // into bf16 fragments).
+  auto read_frags = [&](int buf, int c, u32x4 (&af)[4], u32x4 (&bf)[4], auto bt) {
+    constexpr bool tr = BT && decltype(bt)::v;
+    read_frags_rows(buf, c, af, bf, !tr);
+    if constexpr (tr) read_frags_bt(buf, c, bf);
+  };
+  // raw scale words (the lane's byte is selected later by a shift).  BT:
+  // the b words come from load_scales_bt / shuffle_scales_bt below.
   auto read_scales = [&](int buf, uint32_t (&as)[4], uint32_t (&bs)[4]) {
     const uint8_t* st = lds + buf * ST_BYTES;
     const uint32_t* ssa = reinterpret_cast<const uint32_t*>(st + ST_A + ST_B);
@@ -299,8 +435,40 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       as[i] = ssa[wm * 128 + i * 32 + l32];
-      bs[i] = BROW ? ssb[wn * 128 + i * 32 + l32] : ssb[wn * 4 + i];
+      if constexpr (!BT) bs[i] = BROW ? ssb[wn * 128 + i * 32 + l32] : ssb[wn * 4 + i];
     }
+  };
+  // BT b scales in two parts, the LDS reads issued a few MFMAs ahead of the
+  // byte shuffles that use them.  Run j (reduction block j of the step)
+  // holds the scale bytes of the tile's 8 column blocks from byte
+  // (j * NOUT/32) % 4 of its 3 words (words 4 j .. 4 j + 2 of the region):
+  // load the two words around this wave's 4 column tiles, then
+  auto load_scales_bt = [&](int buf, uint32_t (&raw)[8]) {
+    const uint32_t* ssb = reinterpret_cast<const uint32_t*>(lds + buf * ST_BYTES + ST_A + ST_B + ST_SA);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      raw[2 * j] = ssb[4 * j + wn];
+      raw[2 * j + 1] = ssb[4 * j + wn + 1];
+    }
+  };
+  // ... align each run's 4 bytes and transpose the 4x4 bytes: bs[i] byte j =
+  // scale of (reduction block j, column tile i).  The byte offsets come
+  // from an opaque copy of NOUT/32 at each use (hoisted out of the loop
+  // they cost scalar registers the kernel does not have).
+  auto shuffle_scales_bt = [&](const uint32_t (&raw)[8], uint32_t (&bs)[4]) {
+    uint32_t ksc = bt_ks;
+    asm volatile("" : "+s"(ksc));
+    uint32_t w[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = __builtin_amdgcn_alignbyte(raw[2 * j + 1], raw[2 * j], (j * ksc) & 3);
+    const uint32_t l01 = __builtin_amdgcn_perm(w[1], w[0], 0x05010400u);
+    const uint32_t h01 = __builtin_amdgcn_perm(w[1], w[0], 0x07030602u);
+    const uint32_t l23 = __builtin_amdgcn_perm(w[3], w[2], 0x05010400u);
+    const uint32_t h23 = __builtin_amdgcn_perm(w[3], w[2], 0x07030602u);
+    bs[0] = __builtin_amdgcn_perm(l23, l01, 0x05040100u);
+    bs[1] = __builtin_amdgcn_perm(l23, l01, 0x07060302u);
+    bs[2] = __builtin_amdgcn_perm(h23, h01, 0x05040100u);
+    bs[3] = __builtin_amdgcn_perm(h23, h01, 0x07060302u);
   };
 
   f32x16 acc[4][4];
@@ -313,7 +481,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
 
   // Output of the finished tile (m0, j0): 8 strips of 16 rows per wave,
   // then the accumulators are cleared for the next tile.
-  uint8_t* ostage = lds + NST * ST_BYTES + wave * OUT_WAVE;
+  uint8_t* ostage = lds_out + wave * OUT_WAVE;
   const auto r_out = rsrc(g.out, static_cast<uint64_t>(M) * NOUT * 2);
   // 32-bit output offsets: (M + 256) * NOUT * 2 < 2^31 (host check), so a
   // row past M lands past the end of the buffer and is dropped without a
@@ -388,7 +556,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   __builtin_amdgcn_sched_barrier(0);
   Frags E, O;
   read_scales(0, E.as, E.bs);
-  read_frags(0, 0, E.a0, E.b0);
+  if constexpr (BT) {
+    uint32_t raw[8];
+    load_scales_bt(0, raw);
+    shuffle_scales_bt(raw, E.bs);
+  }
+  read_frags(0, 0, E.a0, E.b0, Flag<BT>{});
 #pragma unroll
   for (int i = 0; i < 4; ++i) { E.as[i] >>= 8 * grp; E.bs[i] >>= 8 * grp; }
   __builtin_amdgcn_sched_barrier(0);
@@ -421,6 +594,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   // scale shifts, cursor advance) is spread between the MFMAs of its two
   // halves, so that it issues while the matrix core is busy instead of
   // leaving it idle between the halves.
+  // kind: this step's MfmaKind.
   auto step = [&](Frags& Cur, Frags& Nxt, auto kind, bool after_store) {
     constexpr bool RANK = decltype(kind)::v == 1;
     const int buf = gs & (NST - 1);
@@ -432,6 +606,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
       else
         acc[i >> 2][i & 3] = mfma_fp4_32x32x64<OP, OP>(af[i >> 2], bf[i & 3], acc[i >> 2][i & 3],
                                                        Cur.as[i >> 2], Cur.bs[i & 3]);
+      // BT: each instruction is pinned at its place in the step (an empty
+      // use of its result): unpinned, the compiler sinks the half's 16 MFMAs
+      // below the step's DMA issues and LDS reads, which then no longer
+      // overlap them
+      if constexpr (BT) asm volatile("" : "+a"(acc[i >> 2][i & 3]));
     };
     const MfmaKind<0> op0;
     const MfmaKind<2> op2;
@@ -443,7 +622,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
       __builtin_amdgcn_sched_barrier(0);
       if (i == 0) {
         hb = half_dma(cb, true);
-        read_frags(buf, 1, Cur.a1, Cur.b1);
+        read_frags(buf, 1, Cur.a1, Cur.b1, Flag<BT>{});
         keep4(Nxt.a1);
         keep4(Nxt.b1);
         __builtin_amdgcn_sched_barrier(0);
@@ -468,6 +647,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
     // ---- second half: chunk 1; the next step's chunk 0 and scales are read
     HalfDma ha;
     uint32_t ras[4], rbs[4];
+    uint32_t sraw[BT ? 8 : 1];
 #pragma unroll
     for (int i = 0; i < 16; ++i) {
       mma(i, Cur.a1, Cur.b1, op2);
@@ -475,7 +655,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
       if (i == 0) {
         ha = half_dma(ca, false);
         read_scales(nbuf, ras, rbs);
-        read_frags(nbuf, 0, Nxt.a0, Nxt.b0);
+        read_frags(nbuf, 0, Nxt.a0, Nxt.b0, Flag<BT>{});
         keep4(Cur.a0);
         keep4(Cur.b0);
         __builtin_amdgcn_sched_barrier(0);
@@ -487,11 +667,25 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
       if (i == 8) {
         cursor_next(cb, true);
         cursor_next(ca, false);
+
         __builtin_amdgcn_sched_barrier(0);
       }
+      // BT: the next step's b scale words: raw words read at i == 4 (held
+      // only until i == 12), shuffled in place into Nxt's words (the step
+      // that last read them is long done)
+      if constexpr (BT) {
+        if (i == 4) {
+          load_scales_bt(nbuf, sraw);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      }
       if (i == 12) {
+        if constexpr (BT) shuffle_scales_bt(sraw, Nxt.bs);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) { Nxt.as[j] = ras[j] >> (8 * grp); Nxt.bs[j] = rbs[j] >> (8 * grp); }
+        for (int j = 0; j < 4; ++j) {
+          Nxt.as[j] = ras[j] >> (8 * grp);
+          Nxt.bs[j] = (BT ? Nxt.bs[j] : rbs[j]) >> (8 * grp);
+        }
         __builtin_amdgcn_sched_barrier(0);
       }
     }
@@ -546,8 +740,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
 // by one and code chunks past the row end read as zero.  Two LDS buffers;
 // the loads of step k+1 are in flight while step k runs.  The rank part
 // comes first, from fragments loaded straight from the padded rank rows.
-template <bool BROW>
+// BMODE as for k_gemm_pipe (0 tiles, 1 row blocks, 3 tiles stored
+// [RED, NOUT/2] and read transposed, with the same LDS layout and
+// transposing reads as there).
+template <int BMODE>
 __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
+  constexpr bool BROW = BMODE == 1, BT = BMODE == 3;
   __shared__ __attribute__((aligned(16))) uint8_t lds[2 * (BM + BN) * ROWB];  // 64 KB
   uint8_t* const lds_a = lds;                      // 2 A buffers
   uint8_t* const lds_b = lds + 2 * BM * ROWB;      // 2 B buffers
@@ -566,12 +764,15 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
 
   const uint32_t row_bytes = static_cast<uint32_t>(RED >> 1);
   const uint32_t row_sc = static_cast<uint32_t>(RED >> 5);
+  const uint32_t bt_row = static_cast<uint32_t>(NOUT >> 1), bt_ks = static_cast<uint32_t>(NOUT >> 5);
   const int nks = static_cast<int>((RED + BK - 1) / BK);
 
   const auto ra_codes = rsrc(g.a_codes, static_cast<uint64_t>(M) * row_bytes);
   const auto ra_sc = rsrc(g.a_scales, static_cast<uint64_t>(M) * row_sc);
-  const auto rb_codes = rsrc(g.b_codes, static_cast<uint64_t>(NOUT) * row_bytes);
-  const auto rb_sc = rsrc(g.b_scales, static_cast<uint64_t>(BROW ? NOUT : NOUT >> 5) * row_sc);
+  const auto rb_codes = rsrc(g.b_codes, BT ? static_cast<uint64_t>(RED) * bt_row
+                                           : static_cast<uint64_t>(NOUT) * row_bytes);
+  const auto rb_sc = rsrc(g.b_scales, BT ? static_cast<uint64_t>(RED >> 5) * bt_ks
+                                         : static_cast<uint64_t>(BROW ? NOUT : NOUT >> 5) * row_sc);
 
   f32x16 acc[4][4];
 #pragma unroll
@@ -604,13 +805,19 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
   for (int i = 0; i < 4; ++i) {
     const uint32_t row = (t >> 2) + 64 * i, ch = t & 3;
     a_off[i] = static_cast<uint32_t>(m0 + row) * row_bytes + ch * 16;
-    b_off[i] = static_cast<uint32_t>(j0 + row) * row_bytes + ch * 16;
+    if constexpr (BT) {
+      // stored reduction row t / 8 + 32 i of the step, logical slot t % 8
+      b_off[i] = ((t >> 3) + 32 * i) * bt_row + static_cast<uint32_t>(j0 >> 1) + (t & 7) * 16;
+    } else {
+      b_off[i] = static_cast<uint32_t>(j0 + row) * row_bytes + ch * 16;
+    }
   }
   uint32_t sa_off[4], sb_off[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     sa_off[i] = static_cast<uint32_t>(m0 + wm * 128 + i * 32 + l32) * row_sc;
-    sb_off[i] = static_cast<uint32_t>(BROW ? j0 + wn * 128 + i * 32 + l32 : (j0 + wn * 128 + i * 32) >> 5) * row_sc;
+    sb_off[i] = BT ? static_cast<uint32_t>((j0 + wn * 128 + i * 32) >> 5)
+                   : static_cast<uint32_t>(BROW ? j0 + wn * 128 + i * 32 + l32 : (j0 + wn * 128 + i * 32) >> 5) * row_sc;
   }
 
   // Loaded values are only moved into registers here; scale bytes are
@@ -623,7 +830,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
     for (int i = 0; i < 4; ++i) {
       const bool kin = k0 + (t & 3) * 32 < RED;
       ra[i] = bload128(ra_codes, kin ? a_off[i] + (k0 >> 1) : OOB);
-      rb[i] = bload128(rb_codes, kin ? b_off[i] + (k0 >> 1) : OOB);
+      if constexpr (BT) {
+        const bool rin = k0 + (t >> 3) + 32 * i < RED;
+        rb[i] = bload128(rb_codes, rin ? b_off[i] + k0 * bt_row : OOB);
+      } else {
+        rb[i] = bload128(rb_codes, kin ? b_off[i] + (k0 >> 1) : OOB);
+      }
     }
     const uint32_t kb0 = k0 >> 5;
 #pragma unroll
@@ -632,7 +844,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
       for (int j = 0; j < 4; ++j) {
         const bool in = kb0 + j < row_sc;
         sa_raw[i][j] = bload8(ra_sc, in ? sa_off[i] + kb0 + j : OOB);
-        sb_raw[i][j] = bload8(rb_sc, (in && j0 + wn * 128 + i * 32 + (BROW ? l32 : 0) < NOUT) ? sb_off[i] + kb0 + j : OOB);
+        if constexpr (BT)
+          sb_raw[i][j] = bload8(rb_sc, (in && j0 + wn * 128 + i * 32 < NOUT) ? (kb0 + j) * bt_ks + sb_off[i] : OOB);
+        else
+          sb_raw[i][j] = bload8(rb_sc, (in && j0 + wn * 128 + i * 32 + (BROW ? l32 : 0) < NOUT) ? sb_off[i] + kb0 + j : OOB);
       }
   };
   auto store_lds = [&](int buf) {
@@ -642,7 +857,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
     for (int i = 0; i < 4; ++i) {
       const int row = (t >> 2) + 64 * i, ch = t & 3;
       *reinterpret_cast<u32x4*>(la + row * ROWB + ((ch ^ swz16(row)) << 4)) = ra[i];
-      *reinterpret_cast<u32x4*>(lb + row * ROWB + ((ch ^ swz16(row)) << 4)) = rb[i];
+      if constexpr (BT) {
+        const int brow = (t >> 3) + 32 * i;
+        *reinterpret_cast<u32x4*>(lb + brow * 128 + (((t & 7) ^ ((brow >> 1) & 7)) << 4)) = rb[i];
+      } else {
+        *reinterpret_cast<u32x4*>(lb + row * ROWB + ((ch ^ swz16(row)) << 4)) = rb[i];
+      }
     }
   };
 
@@ -679,7 +899,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
       for (int i = 0; i < 4; ++i) {
         const int ra_row = wm * 128 + i * 32 + l32, rb_row = wn * 128 + i * 32 + l32;
         af[i] = lds_read_b128(la + ra_row * ROWB + (((2 * c + grp) ^ swz16(ra_row)) << 4));
-        bf[i] = lds_read_b128(lb + rb_row * ROWB + (((2 * c + grp) ^ swz16(rb_row)) << 4));
+        if constexpr (BT) {
+          // as read_frags_bt of k_gemm_pipe
+          const int q = lane & 15, hf = (lane >> 4) & 1, sw = (q >> 1) & 7;
+          const uint8_t* rbp = lb + (64 * c + 32 * grp + q) * 128 + 8 * hf + (((4 * wn + i) ^ sw) << 4);
+          const u32x2 lo = lds_read_tr4(rbp);
+          const u32x2 hi = lds_read_tr4(rbp + 16 * 128);
+          bf[i] = u32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+          bf[i] = lds_read_b128(lb + rb_row * ROWB + (((2 * c + grp) ^ swz16(rb_row)) << 4));
+        }
       }
 #pragma unroll
       for (int mt = 0; mt < 4; ++mt)
@@ -729,6 +958,8 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
       if (g.nlr > 0) FT_GP(true, 2); else FT_GP(false, 2);
     } else if (g.b_row_scales) {
       if (g.nlr > 0) FT_GP(true, 1); else FT_GP(false, 1);
+    } else if (g.b_transposed) {
+      if (g.nlr > 0) FT_GP(true, 3); else FT_GP(false, 3);
     } else {
       if (g.nlr > 0) FT_GP(true, 0); else FT_GP(false, 0);
     }
@@ -736,9 +967,11 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   } else if (bf) {
     return hipErrorInvalidValue;
   } else if (g.b_row_scales) {
-    hipLaunchKernelGGL(k_gemm<true>, dim3(n), dim3(256), 0, st, g);
+    hipLaunchKernelGGL(k_gemm<1>, dim3(n), dim3(256), 0, st, g);
+  } else if (g.b_transposed) {
+    hipLaunchKernelGGL(k_gemm<3>, dim3(n), dim3(256), 0, st, g);
   } else {
-    hipLaunchKernelGGL(k_gemm<false>, dim3(n), dim3(256), 0, st, g);
+    hipLaunchKernelGGL(k_gemm<0>, dim3(n), dim3(256), 0, st, g);
   }
   return hipGetLastError();
 }

@@ -714,6 +714,7 @@ struct RRArgs {
   RankRows cp;
   int64_t cp_rows;
   uint16_t* cp_dst;
+  int cp_planes;        // cp_dst as nibble planes (copy_rank_planes) instead
 };
 
 // k_rank_reduce: blocks [0, 4 * rowblocks) each sum one 16-row slab (one
@@ -793,11 +794,61 @@ __device__ __forceinline__ void copy_rank_chunk(const RRArgs& a, uint64_t e) {
       u32x4{h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4] | (h[5] << 16), h[6] | (h[7] << 16)};
 }
 
+// The other rank operand as nibble planes, for a GEMM that reads its b
+// operand with the 4-bit transposing LDS read (ds_read_b64_tr_b4): 64 ranks
+// (zero past R) of cp_rows columns become 256 plane rows of cp_rows / 2
+// bytes, plane row 128 s + R for ranks 32 s .. 32 s + 31 holding, for
+// every column, nibble R % 4 of rank 32 s + R / 4's bf16 value (low nibble:
+// even column).  Such a read takes, for 16 lanes, 16 consecutive plane rows
+// of one column each, so lane k of a 32-column block receives the 4 nibbles
+// of 4 consecutive ranks in order: 8 bf16 ranks of its column per two
+// reads, the bf16 fragment of a rank step, from the same staging, lane
+// offsets and reads as the 4-bit steps.  A thread makes the 4 plane rows of
+// one rank and 32 columns (64 bytes read, 4 x 16 bytes written).
+__device__ __forceinline__ void copy_rank_planes(const RRArgs& a, uint64_t e) {
+  const RankRows& p = a.cp;
+  const uint32_t pieces = static_cast<uint32_t>(a.cp_rows / 32);
+  if (e >= static_cast<uint64_t>(64) * pieces) return;
+  const int r = static_cast<int>(e / pieces);
+  const uint32_t piece = static_cast<uint32_t>(e % pieces);
+  const uint16_t* src = r < p.r0 ? p.p0 + static_cast<int64_t>(r) * p.ld
+                      : r < a.R ? p.p1 + static_cast<int64_t>(r - p.r0) * p.ld : nullptr;
+  uint32_t v[16];                                        // 32 bf16, two per word
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    const u32x4 w = src ? *reinterpret_cast<const u32x4*>(src + 32 * piece + 8 * k) : u32x4{0, 0, 0, 0};
+#pragma unroll
+    for (int j = 0; j < 4; ++j) v[4 * k + j] = w[j];
+  }
+  uint8_t* dst = reinterpret_cast<uint8_t*>(a.cp_dst);
+  const uint64_t pitch = static_cast<uint64_t>(a.cp_rows / 2);
+#pragma unroll
+  for (int nib = 0; nib < 4; ++nib) {
+    // byte m: columns 2m (low nibble) and 2m + 1, i.e. the two bf16 of word m
+    uint32_t o[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      uint32_t b = 0;
+#pragma unroll
+      for (int m = 0; m < 4; ++m) {
+        const uint32_t w = v[4 * q + m];
+        const uint32_t lo = (w >> (4 * nib)) & 0xFu, hi = (w >> (16 + 4 * nib)) & 0xFu;
+        b |= (lo | (hi << 4)) << (8 * m);
+      }
+      o[q] = b;
+    }
+    const uint64_t prow = static_cast<uint64_t>(128 * (r >> 5) + 4 * (r & 31) + nib);
+    *reinterpret_cast<u32x4*>(dst + prow * pitch + 16 * piece) = u32x4{o[0], o[1], o[2], o[3]};
+  }
+}
+
 template <int NRG>
 __global__ __launch_bounds__(256) void k_rank_reduce(const RRArgs a) {
   const uint32_t nsum = ((a.rows + 63) / 64) * 4;
   if (blockIdx.x < nsum)
     rank_sum_slab<NRG>(a, blockIdx.x);
+  else if (a.cp_planes)
+    copy_rank_planes(a, static_cast<uint64_t>(blockIdx.x - nsum) * 256 + threadIdx.x);
   else
     copy_rank_chunk(a, static_cast<uint64_t>(blockIdx.x - nsum) * 256 + threadIdx.x);
 }
@@ -869,6 +920,45 @@ __global__ __launch_bounds__(256) void k_dequant_tile32(const uint8_t* __restric
   }
 }
 
+// The same dequantization written transposed: out [cols, rows] =
+// deq(codes)^T (a 16-bit dgrad's weight operand, from the forward's tiles).
+// A workgroup takes 64 x 64 values: thread t dequantizes 16 values of row
+// t / 4 into LDS at their transposed places, then writes 32 contiguous bytes
+// of output row (column) t / 4.  rows and cols are multiples of 32, so a
+// 32-value piece is wholly inside or outside.
+__global__ __launch_bounds__(256) void k_dequant_tile32_t(const uint8_t* __restrict__ codes,
+                                                          const uint8_t* __restrict__ scales,
+                                                          uint32_t rows, uint32_t cols,
+                                                          uint16_t* __restrict__ out) {
+  __shared__ uint16_t tr[64][64 + 2];
+  const uint32_t nbx = (cols + 63) / 64;
+  const uint32_t r0 = (blockIdx.x / nbx) * 64, c0 = (blockIdx.x % nbx) * 64;
+  const int t = threadIdx.x;
+  const uint32_t cpr = cols >> 1, spr = cols >> 5;
+  {
+    const int rl = t >> 2, cl = (t & 3) * 16;               // 16 values: columns cl .. cl+15
+    const uint32_t r = r0 + rl, c = c0 + cl;
+    const bool ok = r < rows && c < cols;
+    const auto rc = make_rsrc(codes, static_cast<uint64_t>(rows) * cpr);
+    const u32x2 w = __builtin_bit_cast(
+        u32x2, __builtin_amdgcn_raw_buffer_load_b64(rc, static_cast<int>(ok ? r * cpr + (c >> 1) : BUF_OOB), 0, 0));
+    const int sc = ok ? scales[(r >> 5) * spr + (c >> 5)] : 0;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) tr[cl + k][rl] = static_cast<uint16_t>(e2m1_to_bf16((w[k >> 3] >> (4 * (k & 7))) & 0xFu, sc));
+  }
+  __syncthreads();
+  const int cl = t >> 2, rl = (t & 3) * 16;                 // output row c0 + cl, 16 values from rl
+  const uint32_t c = c0 + cl, r = r0 + rl;
+  const bool ok = c < cols && r < rows;
+  const auto ro = make_rsrc(out, static_cast<uint64_t>(rows) * cols * 2);
+  uint32_t v[8];
+#pragma unroll
+  for (int k = 0; k < 8; ++k) v[k] = tr[cl][rl + 2 * k] | (static_cast<uint32_t>(tr[cl][rl + 2 * k + 1]) << 16);
+  const uint32_t base = ok ? (c * rows + r) * 2 : BUF_OOB;
+  buf_store128(ro, base, u32x4{v[0], v[1], v[2], v[3]});
+  buf_store128(ro, base == BUF_OOB ? BUF_OOB : base + 16, u32x4{v[4], v[5], v[6], v[7]});
+}
+
 hipError_t launch_quant_row32(const uint16_t* in, const uint16_t* in2, int act, int64_t rows,
                               int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
                               hipStream_t st, bool streaming) {
@@ -913,6 +1003,14 @@ hipError_t launch_quant_row32_t(const uint16_t* in, int64_t rows, int64_t cols, 
   const uint32_t n = static_cast<uint32_t>(((cols + 255) / 256) * ((rows + 255) / 256));
   hipLaunchKernelGGL(k_quant_dual<false>, dim3(n), dim3(512), 0, st, in, static_cast<uint32_t>(rows),
                      static_cast<uint32_t>(cols), ld, codes, scales, codes_t, scales_t);
+  return hipGetLastError();
+}
+
+hipError_t launch_dequant_tile32_t(const uint8_t* codes, const uint8_t* scales, int64_t rows,
+                                   int64_t cols, uint16_t* out, hipStream_t st) {
+  const int64_t nb = ((rows + 63) / 64) * ((cols + 63) / 64);
+  hipLaunchKernelGGL(k_dequant_tile32_t, dim3(static_cast<uint32_t>(nb)), dim3(256), 0, st, codes,
+                     scales, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols), out);
   return hipGetLastError();
 }
 
@@ -996,7 +1094,7 @@ hipError_t launch_quant_down(const uint16_t* in, const uint16_t* in2, int act, i
                              int64_t cols, int64_t ld, uint8_t* codes, uint8_t* scales,
                              const RankRows& pr, uint16_t* out_lr, uint16_t* out_pad,
                              const RankRows& cp, int64_t cp_rows, uint16_t* cp_dst, float* part,
-                             const DbFuse* db, hipStream_t st) {
+                             const DbFuse* db, hipStream_t st, bool cp_planes) {
   const int R = pr.r0 + pr.r1;
   const int dbr = db ? quant_down_dbr(db->rl) : 0;
   if (db && !dbr) return hipErrorInvalidValue;
@@ -1023,8 +1121,10 @@ hipError_t launch_quant_down(const uint16_t* in, const uint16_t* in2, int act, i
   }
 #undef FT_QD_NS
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  RRArgs b{part, static_cast<uint32_t>(rows), splits, R, rank_pad(R), out_lr, out_pad, cp, cp_rows, cp_dst};
-  const uint64_t ncopy = (static_cast<uint64_t>(cp_rows) * (rank_pad(R) / 8) + 255) / 256;
+  RRArgs b{part, static_cast<uint32_t>(rows), splits, R, rank_pad(R), out_lr, out_pad, cp, cp_rows, cp_dst,
+           cp_planes ? 1 : 0};
+  const uint64_t ncopy = cp_planes ? (static_cast<uint64_t>(64) * (cp_rows / 32) + 255) / 256
+                                   : (static_cast<uint64_t>(cp_rows) * (rank_pad(R) / 8) + 255) / 256;
   const dim3 rgrid(static_cast<uint32_t>(nrb * 4 + ncopy));
 #define FT_RR(NRG) hipLaunchKernelGGL((k_rank_reduce<NRG>), rgrid, dim3(256), 0, st, b)
   switch (nrg) {

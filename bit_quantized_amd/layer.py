@@ -33,15 +33,17 @@ class QuantizedLinear:
     """One triple-branch linear on the GPU.
 
     W_res (bf16 [N, K]) is quantized once on the device to 32x32 MXFP4 tiles
-    by fourtune_quantize, which also writes the transposed codes the backward
-    reads.  The rank factors are kept in the library's rank-major storage:
+    by fourtune_quantize; the forward reads them row-wise and the backward's
+    input gradient reads the same bytes transposed.  The rank factors are kept in the library's rank-major storage:
     L1t = L1^T [r_s, K], L2 [r_s, N] (frozen), At = A^T [r_l, K], B [r_l, N]
     (trainable).  act_in / act_out (ops.FT_ACT_*) mark an activation before
     or after the layer: with act_in, X is the pre-activation h; with act_out,
     the backward's dY is the gradient of act(Y) and needs H = Y.  precision:
     ops.FT_W4A4G4 (the method) .. ops.FT_W4A16G16, or its name.  w_block:
-    "tile32" (the method) or "row32" (group-wise 1x32 blocks: W_res and
-    W_res^T are quantized separately, by one FT_Q_ROW32_T pass).
+    "tile32" (the method), "tile32_t" (the tiles plus a stored transposed
+    layout copy that the input gradient reads instead; a measured
+    alternative) or "row32" (group-wise 1x32 blocks: W_res and W_res^T are
+    quantized separately, by one FT_Q_ROW32_T pass).
     """
 
     def __init__(self, W_res: torch.Tensor, L1t: torch.Tensor | None, L2: torch.Tensor | None,
@@ -58,14 +60,20 @@ class QuantizedLinear:
         self.r_s = 0 if L1t is None else int(L1t.shape[0])
         self.r_l = 0 if At is None else int(At.shape[0])
         self.L1t, self.L2, self.At, self.B = L1t, L2, At, B
-        self.w_block = {"tile32": ops.FT_WBLOCK_TILE32, "row32": ops.FT_WBLOCK_ROW32}[w_block]
+        self.w_block = {"tile32": ops.FT_WBLOCK_TILE32, "row32": ops.FT_WBLOCK_ROW32,
+                        "tile32_t": ops.FT_WBLOCK_TILE32_T}[w_block]
         self.w_codes = _empty((N, K // 2), torch.uint8, dev)
-        self.wt_codes = _empty((K, N // 2), torch.uint8, dev)
         if self.w_block == ops.FT_WBLOCK_TILE32:
             self.w_scales = _empty((N // 32, K // 32), torch.uint8, dev)
+            self.wt_codes = self.wt_scales = None
+            mode = ops.FT_Q_TILE32
+        elif self.w_block == ops.FT_WBLOCK_TILE32_T:
+            self.w_scales = _empty((N // 32, K // 32), torch.uint8, dev)
+            self.wt_codes = _empty((K, N // 2), torch.uint8, dev)
             self.wt_scales = _empty((K // 32, N // 32), torch.uint8, dev)
             mode = ops.FT_Q_TILE32
         else:
+            self.wt_codes = _empty((K, N // 2), torch.uint8, dev)
             self.w_scales = _empty((N, K // 32), torch.uint8, dev)
             self.wt_scales = _empty((K, N // 32), torch.uint8, dev)
             mode = ops.FT_Q_ROW32_T
@@ -95,6 +103,12 @@ class QuantizedLinear:
     @property
     def R(self):
         return self.r_s + self.r_l
+
+    def weight_bytes(self) -> int:
+        """Device bytes the quantized residual weight occupies (codes and
+        scales, every stored layout)."""
+        ts = (self.w_codes, self.w_scales, self.wt_codes, self.wt_scales)
+        return int(sum(t.numel() for t in ts if t is not None))
 
     def desc(self, M: int) -> ops.FtLinear:
         return ops.make_linear(M, self.K, self.N, self.r_s, self.r_l, self.w_codes,
@@ -177,4 +191,10 @@ class FourTuneLinearFunction(torch.autograd.Function):
             (X, U), H = ctx.saved_tensors, None
         dX, dA, dB, _ = layer.backward(dY.contiguous().to(torch.bfloat16), X, U,
                                        need_dx=ctx.needs_input_grad[0], H=H)
+        if dX is not None and layer.act_in != ops.FT_ACT_NONE:
+            # the library's dX is the gradient of the layer's input act(X);
+            # X's gradient is that times act'(X), by the same device function
+            dh = torch.empty_like(dX)
+            ops.fourtune_act_bwd(layer.act_in, X, dX, dX.numel(), dh)
+            dX = dh
         return dX, dA, dB, None

@@ -20,7 +20,7 @@ FT_Q_ROW32, FT_Q_ROW32_T, FT_Q_TILE32 = 1, 2, 4
 FT_MAX_RANK = 64
 FT_ACT_NONE, FT_ACT_GELU_TANH = 0, 1
 FT_W4A4G4, FT_W4A16G4, FT_W4A4G16, FT_W4A16G16 = 0, 1, 2, 3
-FT_WBLOCK_TILE32, FT_WBLOCK_ROW32 = 0, 1
+FT_WBLOCK_TILE32, FT_WBLOCK_ROW32, FT_WBLOCK_TILE32_T = 0, 1, 2
 PRECISION_NAMES = {"W4A4G4": FT_W4A4G4, "W4A16G4": FT_W4A16G4, "W4A4G16": FT_W4A4G16,
                    "W4A16G16": FT_W4A16G16}
 
@@ -127,7 +127,8 @@ def make_linear(M, K, N, r_stab, r_lora, w_codes, w_scales, wt_codes=None, wt_sc
 
     The factors are rank-major: L1t = L1^T [r_stab, K], L2 [r_stab, N],
     At = A^T [r_lora, K], B [r_lora, N].  precision: FT_W4A4G4 .. FT_W4A16G16
-    or its name; w_block: FT_WBLOCK_TILE32 or FT_WBLOCK_ROW32."""
+    or its name; w_block: FT_WBLOCK_TILE32, FT_WBLOCK_ROW32 or
+    FT_WBLOCK_TILE32_T."""
     if isinstance(precision, str):
         precision = PRECISION_NAMES[precision]
     return FtLinear(int(M), int(K), int(N), int(r_stab), int(r_lora), _ptr(w_codes),

@@ -39,10 +39,10 @@
  * [r_lora, K] (the torch.nn.Linear.weight orientation of the
  * down-projections), L2 [r_stab, N] and B [r_lora, N] as they are.  The
  * adapter gradients come back the same way: dA^T [r_lora, K] and dB
- * [r_lora, N].  The backward also takes the weight's MXFP4 codes in
- * transposed order, [K, N/2] with scales [K/32, N/32] (FT_Q_TILE32 writes
- * them beside the plain order): with one scale per 32x32
- * tile the transpose of the quantized weight is exactly these numbers.
+ * [r_lora, N].  The weight is stored once, as MXFP4 32x32 tiles [N, K/2]
+ * with tile scales [N/32, K/32]: the forward reads its rows, the input
+ * gradient reads the same bytes transposed (one scale per tile, so the
+ * transpose of the quantized weight is exactly these numbers).
  *
  * Memory layouts (all row-major, no padding between rows):
  *   bf16 tensors are arrays of uint16_t bit patterns.
@@ -115,16 +115,23 @@ typedef enum {
   FT_W4A16G16 = 3
 } ft_precision;
 
-/* Block shape of the residual weight's quantization (FourTune, "4.3
- * Ablation Study / Impact of Quantization Granularity", Table 5).  TILE32 is
- * the method: 32x32 tiles, so the dgrad reads the same numbers transposed.
+/* Storage of the residual weight (FourTune, "3.2 4-Bit Backward Pass via
+ * Block-Quantization"; "4.3 Ablation Study / Impact of Quantization
+ * Granularity", Table 5).
+ * TILE32 is the method: 32x32 tiles stored once, [N, K/2] codes and
+ * [N/32, K/32] scales; the dgrad reads the same bytes transposed.
+ * TILE32_T: the same tiles plus a stored transposed layout copy of them
+ * (wt_codes [K, N/2], wt_scales [K/32, N/32], as FT_Q_TILE32 writes into
+ * codes_t / scales_t), which the dgrad reads row-wise instead; a measured
+ * alternative that holds the 4-bit weight twice.
  * ROW32 is the group-wise alternative: 1x32 blocks along the reduction of
  * each product, so the forward reads Qrow32(W_res) and the dgrad a separate
  * quantization Qrow32(W_res^T) (which FT_Q_ROW32_T of W_res writes beside
  * the first from one read).  ROW32 requires precision FT_W4A4G4. */
 typedef enum {
   FT_WBLOCK_TILE32 = 0,
-  FT_WBLOCK_ROW32 = 1
+  FT_WBLOCK_ROW32 = 1,
+  FT_WBLOCK_TILE32_T = 2
 } ft_wblock;
 
 #define FT_MAX_RANK 64
@@ -134,11 +141,12 @@ typedef enum {
 typedef struct {
   int64_t M, K, N;            /* tokens, input features, output features            */
   int32_t r_stab, r_lora;     /* stabilizer and adapter ranks, r_stab + r_lora <= 64 */
-  const uint8_t* w_codes;     /* Qtile(W_res) codes  [N, K/2]                         */
+  const uint8_t* w_codes;     /* Qtile(W_res) codes  [N, K/2] (ROW32: Qrow32(W_res))  */
   const uint8_t* w_scales;    /* Qtile(W_res) scales [N/32, K/32]; ROW32: [N, K/32]   */
-  const uint8_t* wt_codes;    /* the same codes transposed [K, N/2]; backward only,  */
-  const uint8_t* wt_scales;   /*   scales [K/32, N/32]; may be NULL for the forward;  */
-                              /*   ROW32: Qrow32(W_res^T), scales [K, N/32]           */
+  const uint8_t* wt_codes;    /* the dgrad's separately stored weight, read only by a */
+  const uint8_t* wt_scales;   /*   backward with dX: NULL for TILE32 (the method);   */
+                              /*   TILE32_T: transposed copy [K, N/2], [K/32, N/32];  */
+                              /*   ROW32: Qrow32(W_res^T) [K, N/2], scales [K, N/32]  */
   const uint16_t* L1t;        /* bf16 [r_stab, K] = L1^T  (frozen)                    */
   const uint16_t* L2;         /* bf16 [r_stab, N]  (frozen)                           */
   const uint16_t* At;         /* bf16 [r_lora, K] = A^T  (trainable)                  */
@@ -149,7 +157,7 @@ typedef struct {
   int32_t act_out;            /* FT_ACT_*: an activation follows this layer: the backward's
                                  dY is the gradient of act_out(Y), and H = Y is required */
   int32_t precision;          /* FT_W4A4G4 (0, the method) .. FT_W4A16G16                */
-  int32_t w_block;            /* FT_WBLOCK_TILE32 (0, the method) or FT_WBLOCK_ROW32    */
+  int32_t w_block;            /* FT_WBLOCK_TILE32 (0, the method), _ROW32 or _TILE32_T */
 } ft_linear;
 
 /* Quantize a bf16 matrix `in` [rows, cols] with row stride ld_in elements.
@@ -224,9 +232,9 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
  *   reduction dimension of the input gradient) and P = bf16(dY V^T); for
  *   r_lora <= 32 it also makes per-workgroup partial sums of dB from the dY
  *   it holds, so dY is read once for the whole backward;
- *   kernel 2 computes deq(Qrow(dY)) deq(Qtile(W_res)) + P D^T from the
- *   32x32-tile codes in transposed order (wt_codes, wt_scales) and writes dX
- *   (bf16 [M, K]) once;
+ *   kernel 2 computes deq(Qrow(dY)) deq(Qtile(W_res)) + P D^T, reading the
+ *   forward's 32x32-tile codes and scales (w_codes, w_scales) transposed,
+ *   and writes dX (bf16 [M, K]) once;
  *   kernel 3 writes the adapter gradients, rank-major like At and B:
  *   dA^T = P[:, r_stab:]^T X ([r_lora, K]) and dB = U[:, r_stab:]^T dY
  *   ([r_lora, N]), in grad_dtype (FT_BF16 or FT_F32); every partial sum is
@@ -235,13 +243,15 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
  * layer's forward output Y; required when act_out != FT_ACT_NONE (then the
  * incoming gradient is dY * act_out'(H), recomputed wherever it is read),
  * else ignored.  With act_in != FT_ACT_NONE, X is the pre-activation h and
- * dA uses act_in(h), recomputed as X is read.  dX may be NULL (no
- * input gradient; then wt_codes and wt_scales may be NULL).  dA, dB may be
- * NULL only when r_lora == 0.
+ * dA uses act_in(h), recomputed as X is read; dX is still the gradient of
+ * the layer's input act_in(h) (the caller applies act_in'(h), e.g. with
+ * fourtune_act_bwd).  dX may be NULL (no input gradient; then wt_codes and
+ * wt_scales may be NULL for every w_block).  dA, dB may be NULL only when
+ * r_lora == 0.
  * Under G16 (precision bit 1) kernel 1 computes P and the dB partials
- * only, the transposed weight tiles are dequantized to bf16 in the
- * workspace, and kernel 2 multiplies bf16 dY (dY * act_out'(H) when set,
- * made in the workspace first) by them.
+ * only, the weight tiles are dequantized to bf16 in the workspace in
+ * transposed order ([K, N]), and kernel 2 multiplies bf16 dY
+ * (dY * act_out'(H) when set, made in the workspace first) by them.
  * P_save : optional bf16 [M, R] output of P; NULL = workspace only.
  * gq_codes, gq_scales: optional outputs [M, N/2], [M, N/32]; must be NULL
  *   under G16.

@@ -56,10 +56,14 @@ def test_quantize_argument_errors():
     assert _q(ops.FT_Q_ROW32, ld=68) == ops.FT_EALIGN     # ld not a multiple of 8
     assert _q(ops.FT_Q_ROW32, x=A16 + 2) == ops.FT_EALIGN
     assert _q(ops.FT_Q_ROW32, rows=0) == ops.FT_OK        # empty is a no-op
+    # a row stride out of range is refused before any product is formed
+    assert _q(ops.FT_Q_ROW32, ld=1 << 62) == ops.FT_ESHAPE
+    assert _q(ops.FT_Q_ROW32, ld=-8) == ops.FT_ESHAPE
+    assert _q(ops.FT_Q_ROW32, rows=0, ld=1 << 62) == ops.FT_ESHAPE
 
 
 def _layer(M=64, K=64, N=64, rs=8, rl=8, **kw):
-    d = dict(w_codes=A16, w_scales=A16, wt_codes=A16, wt_scales=A16, L1t=A16, L2=A16, At=A16,
+    d = dict(w_codes=A16, w_scales=A16, wt_codes=None, wt_scales=None, L1t=A16, L2=A16, At=A16,
              B=A16)
     d.update(kw)
     return ops.make_linear(M, K, N, rs, rl, **d)
@@ -93,9 +97,17 @@ def test_linear_pointer_errors():
     assert _fwd(_layer(L1t=None)) == ops.FT_EINVAL
     assert _fwd(_layer(B=None)) == ops.FT_EINVAL
     assert _fwd(_layer(L2=None)) == ops.FT_EINVAL
-    assert _fwd(_layer(wt_scales=None)) == ops.FT_EINVAL        # transposed codes without scales
-    assert _bwd(_layer(wt_codes=None, wt_scales=None)) == ops.FT_EINVAL   # dX needs them
-    assert _fwd(_layer(wt_codes=A16 + 4)) == ops.FT_EALIGN
+    T, R = ops.FT_WBLOCK_TILE32_T, ops.FT_WBLOCK_ROW32
+    assert _fwd(_layer(w_block=T, wt_codes=A16)) == ops.FT_EINVAL   # second codes without scales
+    # the method's tiles serve the dgrad as they are: a second weight is refused
+    assert _fwd(_layer(wt_codes=A16, wt_scales=A16)) == ops.FT_EINVAL
+    assert _bwd(_layer(wt_codes=A16, wt_scales=A16)) == ops.FT_EINVAL
+    # the stored-copy and group-wise layouts need their second weight for dX only
+    assert _bwd(_layer(w_block=T)) == ops.FT_EINVAL
+    assert _bwd(_layer(w_block=R)) == ops.FT_EINVAL
+    assert _bwd(_layer(w_block=T), dX=None) == ops.FT_EUNSUPPORTED
+    assert _bwd(_layer()) == ops.FT_EUNSUPPORTED               # only the missing GPU stops it
+    assert _fwd(_layer(w_block=T, wt_codes=A16 + 4, wt_scales=A16)) == ops.FT_EALIGN
     assert _fwd(_layer(), X=None) == ops.FT_EINVAL
     assert _fwd(_layer(), U=None) == ops.FT_EINVAL
     assert _fwd(_layer(), qc=A16) == ops.FT_EINVAL              # codes without scales
@@ -196,9 +208,10 @@ def test_precision_argument_errors_and_workspace():
 
 
 def test_weight_block_argument_errors():
-    assert _fwd(_layer(w_block=2)) == ops.FT_EINVAL
+    assert _fwd(_layer(w_block=3)) == ops.FT_EINVAL
     assert _fwd(_layer(w_block=-1)) == ops.FT_EINVAL
     assert ops.fourtune_workspace_bytes(_layer(w_block=3), False) == 0
+    assert ops.fourtune_workspace_bytes(_layer(w_block=ops.FT_WBLOCK_TILE32_T), False) > 0
     # group-wise weights have no tile dequantizer: 4-bit products only
     assert _fwd(_layer(w_block=ops.FT_WBLOCK_ROW32, precision="W4A16G4")) == ops.FT_EINVAL
     assert _bwd(_layer(w_block=ops.FT_WBLOCK_ROW32, precision="W4A4G16")) == ops.FT_EINVAL

@@ -4,10 +4,12 @@ import numpy as np
 import pytest
 import torch
 
-from bit_quantized_amd import synth
-from bit_quantized_amd.layer import FourTuneLinearFunction, bits_of
+from bit_quantized_amd import ops, synth
+from bit_quantized_amd.layer import FourTuneLinearFunction, QuantizedLinear, bits_of
+from oracle import linear as OL
+from oracle import mxfp4 as OQ
 
-from _gpu import GpuCase, check_full, check_sampled, require_gpu, say, up
+from _gpu import REL_TOL, GpuCase, check_full, check_sampled, require_gpu, say, up
 
 pytestmark = pytest.mark.gpu
 
@@ -37,6 +39,12 @@ def test_tiny_case_full():
     (96, 256, 320, 5, 3),        # ranks that are not multiples of 8
     (200, 640, 384, 0, 0),       # odd 128-step counts both ways (padded step), no ranks
     (200, 640, 384, 16, 8),      # the same with rank steps
+    # the dgrad reads the forward's tiles transposed; K / 32 not a multiple
+    # of 4 puts each reduction block's run of tile scales at a byte offset
+    # inside its first word (pipelined dgrad: N % 128 == 0)
+    (300, 288, 512, 16, 8),      # K / 32 = 9
+    (96, 160, 256, 0, 0),        # K / 32 = 5, no ranks
+    (260, 224, 384, 32, 16),     # K / 32 = 7
 ])
 def test_ragged_shapes_full(shape):
     M, K, N, rs, rl = shape
@@ -80,6 +88,43 @@ def test_row32_weights_full(shape):
     c = synth.flux_linear_case(f"row32w_{M}x{K}x{N}_r{rs}_{rl}", M, K, N, rs, rl, seed=M + 2 * N)
     say("case", c.name)
     check_full(c, GpuCase(c, w_block="row32").run())
+
+
+@pytest.mark.parametrize("shape", [
+    (300, 288, 544, 16, 8),      # register-staged dgrad
+    (520, 1024, 768, 32, 16),    # pipelined dgrad
+    (96, 160, 256, 0, 0),        # pipelined, no ranks
+])
+def test_tile32_transposed_copy_full(shape):
+    """The measured alternative to the method's single weight: the tiles
+    plus a stored transposed layout copy (FT_WBLOCK_TILE32_T), which the
+    dgrad reads row-wise.  The copy must hold exactly Qtile(W^T) and give
+    the same layer."""
+    M, K, N, rs, rl = shape
+    c = synth.flux_linear_case(f"tile32t_{M}x{K}x{N}_r{rs}_{rl}", M, K, N, rs, rl, seed=M + 3 * N)
+    say("case", c.name)
+    check_full(c, GpuCase(c, w_block="tile32_t").run())
+
+
+def test_tile32_reads_agree_bitwise():
+    """The dgrad on the one packed weight (transposing LDS reads) and on the
+    stored transposed copy (row reads) add the same products in the same
+    order: dX must agree bit for bit."""
+    c = synth.flux_linear_case("tile32_vs_copy", 700, 1024, 1536, 32, 16, seed=11)
+    say("case", c.name)
+    a = GpuCase(c).run()
+    b = GpuCase(c, w_block="tile32_t").run()
+    for k in ("Y", "dX", "dA", "dB", "U", "P", "gq_codes"):
+        np.testing.assert_array_equal(a[k], b[k], err_msg=k)
+
+
+def test_multi_tile_walk_full():
+    """4608 x 4608 x 4608 (ranks 32/16): 324 output tiles each way on 256
+    workgroups, so some workgroups of both GEMMs walk two tiles and the
+    load pipeline runs across a tile boundary; compared in full."""
+    c = synth.flux_linear_case("multi_tile_4608", 4608, 4608, 4608, 32, 16, seed=12)
+    say("case", c.name)
+    check_full(c, GpuCase(c).run())
 
 
 def test_row32_weights_qkv_full_size_sampled():
@@ -137,6 +182,42 @@ def test_deterministic():
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
 
 
+def test_autograd_function_act_in():
+    """A layer whose input is gelu(h) used through the autograd Function:
+    h's gradient is the layer's input gradient times gelu'(h).  Checked
+    against the oracle fed the GPU's gelu(h) values, with the oracle's own
+    gelu' applied to the oracle's input gradient."""
+    c = synth.flux_linear_case("act_in_autograd", 256, 512, 384, 16, 8, seed=9)
+    say("case act_in autograd")
+    g = GpuCase(c)
+    layer = QuantizedLinear.from_factors(up(c.W_res), up(c.L1), up(c.L2), up(c.A), up(c.B),
+                                         act_in=ops.FT_ACT_GELU_TANH)
+    h = g.X.clone().requires_grad_(True)
+    At = layer.At.clone().requires_grad_(True)
+    B = layer.B.clone().requires_grad_(True)
+    Y = FourTuneLinearFunction.apply(h, At, B, layer)
+    Y.backward(g.dY)
+    torch.cuda.synchronize()
+    a = torch.empty_like(g.X)
+    ops.fourtune_act_fwd(ops.FT_ACT_GELU_TANH, g.X, g.X.numel(), a)
+    torch.cuda.synchronize()
+    a_bits = bits_of(a)
+    wc, ws = OQ.quantize_tile32(c.W_res)
+    f = OL.linear_fwd(a_bits, wc, ws, c.L1, c.L2, c.A, c.B)
+    b = OL.linear_bwd(c.dY, a_bits, f["U"], wc, ws, c.L1, c.L2, c.A, c.B)
+    dh_ref = OL.gelu_tanh_grad(c.X, b["dX"])
+    errs = {"Y": OL.rel_frobenius(bits_of(Y), f["Y"]),
+            "dh": OL.rel_frobenius(bits_of(h.grad), dh_ref),
+            "dA": OL.rel_frobenius(np.ascontiguousarray(bits_of(At.grad).T), b["dA"]),
+            "dB": OL.rel_frobenius(bits_of(B.grad), b["dB"])}
+    say("act_in autograd", errs)
+    for k, v in errs.items():
+        assert v <= REL_TOL, (k, v)
+    # the input gradient is not the library's dX itself
+    dX_lib = layer.backward(g.dY, g.X, layer.forward(g.X)[1])[0]
+    assert not np.array_equal(bits_of(h.grad), bits_of(dX_lib))
+
+
 def test_autograd_function_matches_library():
     c = synth.flux_linear_case("autograd", 128, 256, 192, 8, 8, seed=8)
     say("case autograd")
@@ -174,8 +255,9 @@ def test_mlp_pair_full_size_sampled():
         check_sampled(c, GpuCase(c).run(), _rows(c.M, seed=1))
 
 
-@pytest.mark.parametrize("name", ["img_out", "txt_qkv", "txt_mod", "img_mod"])
+@pytest.mark.parametrize("name", [n for n, *_ in synth.dit_block_linears()])
 def test_dit_block_linears_sampled(name):
+    """Every linear of the double-stream DiT block at batch 2."""
     c = synth.dit_block_case(name)
     say("case", c.name)
     check_sampled(c, GpuCase(c).run(), _rows(c.M, n=min(48, c.M - 1), seed=2) if c.M > 2

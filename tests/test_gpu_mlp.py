@@ -15,6 +15,8 @@ fused kernels call) are therefore checked against the oracle's GELU to
 within one bf16 ulp, and each linear is then checked against the oracle fed
 the GPU's bf16 activation values, so that the codes compare bit for bit.
 """
+import copy
+
 import numpy as np
 import pytest
 import torch
@@ -24,7 +26,8 @@ from bit_quantized_amd.layer import QuantizedLinear, bits_of
 from oracle import linear as OL
 from oracle import mxfp4 as OQ
 
-from _gpu import DEV, REL_TOL, check_rounding_flips, require_gpu, say, up
+from _gpu import (DEV, REL_TOL, _check_down_proj, _check_outputs_elementwise, require_gpu, say,
+                  up)
 
 pytestmark = pytest.mark.gpu
 G = ops.FT_ACT_GELU_TANH
@@ -135,10 +138,6 @@ class MlpPair:
                     P1=R(P1, c1), gc1=u8(gc1), gs1=u8(gs1))
 
 
-def _absdot(x_bits, w):
-    return np.abs(OQ.bf16_bits_to_f64(x_bits)) @ np.abs(w)
-
-
 def _check_layer_full(tag, c, X, dY, got_fwd, got_bwd, Y_name, precision="W4A4G4"):
     """One linear against the oracle in full, given the operands the GPU saw.
     got_fwd = (Y, U, xc, xs); got_bwd = (dX, dA, dB, P, gc, gs)."""
@@ -162,11 +161,14 @@ def _check_layer_full(tag, c, X, dY, got_fwd, got_bwd, Y_name, precision="W4A4G4
     say(tag, {k: round(v, 8) for k, v in res.items()})
     for k, v in res.items():
         assert v <= REL_TOL, (tag, k, v)
+    # elementwise, against the oracle fed the operands the GPU saw
+    cc = copy.copy(c)
+    cc.X, cc.dY = X, dY
+    got = {"Y": Y, "dX": dX, "dA": dA, "dB": dB, "U": U, "P": P}
     if c.R:
-        D = OL.stack_down(c.L1, c.A)
-        V = OL.stack_up(c.L2, c.B)
-        check_rounding_flips(U, f["U"], tag + " U", _absdot(X, D), c.K)
-        check_rounding_flips(P, b["P"], tag + " P", _absdot(dY, V.T), c.N)
+        _check_down_proj(cc, got)
+    wkw = {}
+    _check_outputs_elementwise(cc, got, np.arange(c.M), wc, ws, wkw, wkw, precision)
     return f
 
 
@@ -247,5 +249,9 @@ def test_mlp_pair_chain_full_size_sampled():
         say(tag, {k: round(v, 8) for k, v in res.items()})
         for k, v in res.items():
             assert v <= REL_TOL, (tag, k, v)
-        check_rounding_flips(got[Uk], Uf, tag + " U", _absdot(X, D), c.K)
-        check_rounding_flips(got[Pk], Pf, tag + " P", _absdot(dY, V.T), c.N)
+        cc = copy.copy(c)
+        cc.X, cc.dY = X, dY
+        g = {"Y": got[Yk], "dX": got[dXk], "dA": got[dAk], "dB": got[dBk], "U": got[Uk],
+             "P": got[Pk]}
+        _check_down_proj(cc, g)
+        _check_outputs_elementwise(cc, g, rows, wc, ws, {}, {}, "W4A4G4")
