@@ -104,6 +104,9 @@ struct TimingState {
   }
 };
 TimingState g_tm;
+// Set by the entry point that allocates nothing while it runs: no timing
+// events are created for its launches (creating one allocates).
+thread_local bool t_no_timing = false;
 
 // Brackets one launch with events when timing is on.
 struct Timed {
@@ -111,7 +114,7 @@ struct Timed {
   int slot = -1;
   hipStream_t st;
   Timed(const char* name, hipStream_t s) : st(s) {
-    if (!g_tm.on.load(std::memory_order_relaxed)) return;
+    if (t_no_timing || !g_tm.on.load(std::memory_order_relaxed)) return;
     std::lock_guard<std::mutex> lk(g_tm.mu);
     slot = g_tm.slot(name);
     a = g_tm.take();
@@ -491,6 +494,22 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
     if (tm.done(ft::launch_lora_grads(a, b, db_fused, st)) != hipSuccess) return FT_EDEVICE;
   }
   return FT_OK;
+}
+
+ft_status fourtune_linear_fwd_noalloc(const ft_linear* L, const uint16_t* X, uint16_t* Y,
+                                      uint16_t* U_save, uint8_t* xq_codes, uint8_t* xq_scales,
+                                      void* stream) {
+  if (ft_status s = check_linear(L); s != FT_OK) return s;
+  if (fwd_layout(L).total > ft::kNoAllocScratchBytes) return FT_EWORKSPACE;
+  if (ft_status s = device_check(); s != FT_OK) return s;
+  void* ws = ft::noalloc_scratch();
+  if (!ws) return FT_EDEVICE;
+  struct Quiet {
+    Quiet() { t_no_timing = true; }
+    ~Quiet() { t_no_timing = false; }
+  } quiet;
+  return fourtune_linear_fwd(L, X, Y, U_save, xq_codes, xq_scales, ws, ft::kNoAllocScratchBytes,
+                             stream);
 }
 
 ft_status fourtune_act_fwd(int act, const uint16_t* h, int64_t n, uint16_t* out, void* stream) {

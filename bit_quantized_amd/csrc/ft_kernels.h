@@ -126,6 +126,12 @@ hipError_t launch_lora_grads(const LoraGradArgs& dA, const LoraGradArgs& dB, boo
                              hipStream_t st);
 size_t lora_grad_part_bytes(int64_t M, int64_t I, int rl);
 
+// scratch.hip: the workspace of the forward that allocates nothing, a
+// device array of kNoAllocScratchBytes (FT_NOALLOC_SCRATCH_BYTES of the C
+// ABI) per GPU; nullptr if the current device's copy cannot be located.
+constexpr size_t kNoAllocScratchBytes = size_t(64) << 20;
+void* noalloc_scratch();
+
 // act.hip: out = bf16(gelu(h)) (act 1) or bf16(g * gelu'(h)) (act 2), n elements.
 hipError_t launch_act(int act, const uint16_t* h, const uint16_t* g, int64_t n, uint16_t* out,
                       hipStream_t st);

@@ -18,6 +18,7 @@ FT_OK, FT_EINVAL, FT_ESHAPE, FT_EALIGN, FT_EWORKSPACE, FT_EDEVICE, FT_EUNSUPPORT
 FT_BF16, FT_F32 = 0, 1
 FT_Q_ROW32, FT_Q_ROW32_T, FT_Q_TILE32 = 1, 2, 4
 FT_MAX_RANK = 64
+FT_NOALLOC_SCRATCH_BYTES = 64 << 20
 FT_ACT_NONE, FT_ACT_GELU_TANH = 0, 1
 FT_W4A4G4, FT_W4A16G4, FT_W4A4G16, FT_W4A16G16 = 0, 1, 2, 3
 FT_WBLOCK_TILE32, FT_WBLOCK_ROW32, FT_WBLOCK_TILE32_T = 0, 1, 2
@@ -25,7 +26,7 @@ PRECISION_NAMES = {"W4A4G4": FT_W4A4G4, "W4A16G4": FT_W4A16G4, "W4A4G16": FT_W4A
                    "W4A16G16": FT_W4A16G16}
 
 EXPORTS = ("fourtune_quantize", "fourtune_dequantize", "fourtune_workspace_bytes", "fourtune_linear_fwd",
-           "fourtune_linear_bwd", "fourtune_act_fwd", "fourtune_act_bwd",
+           "fourtune_linear_fwd_noalloc", "fourtune_linear_bwd", "fourtune_act_fwd", "fourtune_act_bwd",
            "fourtune_status_string", "fourtune_timing_enable", "fourtune_timing_reset",
            "fourtune_timing_read")
 
@@ -68,6 +69,8 @@ def lib() -> ctypes.CDLL:
         L.fourtune_linear_fwd.argtypes = [ctypes.POINTER(FtLinear), vp, vp, vp, vp, vp, vp,
                                           ctypes.c_size_t, vp]
         L.fourtune_linear_fwd.restype = st
+        L.fourtune_linear_fwd_noalloc.argtypes = [ctypes.POINTER(FtLinear), vp, vp, vp, vp, vp, vp]
+        L.fourtune_linear_fwd_noalloc.restype = st
         L.fourtune_linear_bwd.argtypes = [ctypes.POINTER(FtLinear), vp, vp, vp, vp, vp, vp, vp,
                                           st, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.fourtune_linear_bwd.restype = st
@@ -159,6 +162,12 @@ def fourtune_linear_fwd(layer: FtLinear, X, Y, U_save, xq_codes, xq_scales, work
                                   _ptr(xq_codes), _ptr(xq_scales), _ptr(workspace),
                                   int(ws_bytes), _stream(stream))
     _check(s, "fourtune_linear_fwd")
+
+
+def fourtune_linear_fwd_noalloc(layer: FtLinear, X, Y, U_save, xq_codes, xq_scales, stream=None):
+    s = lib().fourtune_linear_fwd_noalloc(ctypes.byref(layer), _ptr(X), _ptr(Y), _ptr(U_save),
+                                          _ptr(xq_codes), _ptr(xq_scales), _stream(stream))
+    _check(s, "fourtune_linear_fwd_noalloc")
 
 
 def fourtune_linear_bwd(layer: FtLinear, dY, X, U_save, H, dX, dA, dB, grad_dtype, P_save,

@@ -56,7 +56,10 @@
  *     descriptor itself, which is host memory read during the call only.
  *   - Work is enqueued on `stream` (a hipStream_t, NULL = default stream);
  *     the call returns without synchronizing.  The library allocates and
- *     frees nothing and keeps no pointer after it returns.
+ *     frees nothing and keeps no pointer after it returns (exceptions: the
+ *     opt-in per-kernel timing helpers at the end, which create events and
+ *     wait for them, and the scratch array of fourtune_linear_fwd_noalloc,
+ *     set up on its first call on a GPU).
  *   - All checks run on the host before anything is enqueued: a call that
  *     returns an error has enqueued no work and written no device memory.
  *   - Device pointers must be 16-byte aligned.  Inputs must be finite; NaN
@@ -226,6 +229,28 @@ size_t fourtune_workspace_bytes(const ft_linear* L, int is_bwd);
 ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y,
                               uint16_t* U_save, uint8_t* xq_codes, uint8_t* xq_scales,
                               void* workspace, size_t ws_bytes, void* stream);
+
+/* The forward above for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, results and checks as fourtune_linear_fwd
+ * without workspace and ws_bytes: the workspace is a device array of
+ * FT_NOALLOC_SCRATCH_BYTES that the library holds on each GPU until the
+ * process ends, located on the first call made with that GPU current.
+ * The call itself allocates nothing (no hipMalloc, no library routine that
+ * allocates; the per-kernel timing below is skipped for it).
+ * Layers whose forward workspace (fourtune_workspace_bytes(L, 0)) exceeds
+ * FT_NOALLOC_SCRATCH_BYTES are refused with FT_EWORKSPACE before anything
+ * is enqueued.  Every call on one GPU shares that GPU's array and leaves
+ * it in an unspecified state (nothing in it needs clearing between
+ * calls): calls that overlap on one GPU (different streams, or host
+ * threads racing) race on it and give unspecified results; calls in order
+ * on one stream are safe.
+ * Errors: as fourtune_linear_fwd; FT_EDEVICE also if the array cannot be
+ * located on the current GPU. */
+#define FT_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+ft_status fourtune_linear_fwd_noalloc(const ft_linear* L, const uint16_t* X, uint16_t* Y,
+                                      uint16_t* U_save, uint8_t* xq_codes, uint8_t* xq_scales,
+                                      void* stream);
 
 /* Backward, Eq. (3) and the adapter gradients of section 3.2:
  *   kernel 1 reads dY once and writes Qrow(dY) (1x32 blocks along N, the

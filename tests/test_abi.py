@@ -220,3 +220,22 @@ def test_weight_block_argument_errors():
     # the workspace does not depend on the weight's block shape
     assert (ops.fourtune_workspace_bytes(_layer(w_block=ops.FT_WBLOCK_ROW32), True)
             == ops.fourtune_workspace_bytes(_layer(), True))
+
+
+def _fwd_noalloc(L, X=A16, Y=A16, U=A16, qc=None, qs=None):
+    return ops.lib().fourtune_linear_fwd_noalloc(ctypes.byref(L), X, Y, U, qc, qs, None)
+
+
+def test_noalloc_forward_argument_errors():
+    """The forward without workspace argument checks like the forward, and
+    refuses a layer whose workspace exceeds the library's scratch array
+    before touching any device."""
+    assert ops.lib().fourtune_linear_fwd_noalloc(None, A16, A16, A16, None, None, None) == ops.FT_EINVAL
+    assert _fwd_noalloc(_layer(K=48)) == ops.FT_ESHAPE
+    assert _fwd_noalloc(_layer(w_codes=None)) == ops.FT_EINVAL
+    big = _layer(M=65536, K=4096, N=4096)
+    assert ops.fourtune_workspace_bytes(big, False) > ops.FT_NOALLOC_SCRATCH_BYTES
+    assert _fwd_noalloc(big) == ops.FT_EWORKSPACE
+    small = _layer(M=64, K=256, N=256)
+    assert ops.fourtune_workspace_bytes(small, False) <= ops.FT_NOALLOC_SCRATCH_BYTES
+    assert _fwd_noalloc(small) == ops.FT_EUNSUPPORTED      # only the missing GPU stops it
