@@ -20,7 +20,8 @@ headline the line carries: the oracle's CPU rate on the same layer
 against the unfused low-rank branches (fusion_breakdown), all linears of a
 DiT block (dit_block), the four precision settings of the precision
 ablation (precision_settings), tiles against group-wise weights
-(weight_block) and the quantizers at the stress shapes (quantizer_stress).
+(weight_block), the step at larger ranks (rank_variants) and the quantizers
+at the stress shapes (quantizer_stress).
 
     python bench.py [--steps 50] [--warmup 10] [--gpus 1] [--only PART]
 """
@@ -59,11 +60,12 @@ def parse():
     ap.add_argument("--no-block", action="store_true")
     ap.add_argument("--no-precision", action="store_true")
     ap.add_argument("--no-wblock", action="store_true")
+    ap.add_argument("--no-ranks", action="store_true")
     ap.add_argument("--graph-replay", action="store_true",
                     help="also time the step replayed from HIP graphs (reported beside the "
                          "direct launches)")
     ap.add_argument("--only", choices=["step", "stress", "mlp", "fusion", "block", "precision",
-                                       "wblock"],
+                                       "wblock", "ranks"],
                     default=None,
                     help="run only one part (for profiler runs)")
     ap.add_argument("--copy-probe", action="store_true",
@@ -690,20 +692,28 @@ def main():
     # The QKV step (fwd+bwd) with the layer built in several ways, timed in
     # interleaved rounds (median over rounds) so that clock drift during the
     # run does not favour one variant: two rotated input sets per variant.
+    # A variant's "ranks": (r_stab, r_lora) other than the QKV case's 32/16,
+    # with factors drawn the same way (the inputs and the weight are the same).
     def qkv_variants(kws, rounds=3):
         c = synth.qkv_case()
         M, K, N, rs, rl = c.M, c.K, c.N, c.r_s, c.r_l
         X0, dY0, W0 = (bf16_tensor(x, dev) for x in (c.X, c.dY, c.W_res))
-        L1, L2, A, B = (bf16_tensor(x, dev) for x in (c.L1, c.L2, c.A, c.B))
+        factors = {(rs, rl): tuple(bf16_tensor(x, dev) for x in (c.L1, c.L2, c.A, c.B))}
         bt = lambda *sh: torch.empty(sh, dtype=torch.bfloat16, device=dev)
         sets = {}
         for name, kw in kws.items():
+            kw = dict(kw)
+            vrs, vrl = kw.pop("ranks", (rs, rl))
+            if (vrs, vrl) not in factors:
+                vc = synth.flux_linear_case(f"qkv_r{vrs}_{vrl}", 8, K, N, vrs, vrl, seed=1)
+                factors[(vrs, vrl)] = tuple(bf16_tensor(x, dev) for x in (vc.L1, vc.L2, vc.A, vc.B))
+            L1, L2, A, B = factors[(vrs, vrl)]
             sets[name] = []
             for s_ in range(2):
                 lay = QuantizedLinear.from_factors(torch.roll(W0, 32 * s_, 0).contiguous(), L1, L2, A, B, **kw)
                 sets[name].append((lay, torch.roll(X0, 97 * s_, 0).contiguous(),
-                                   torch.roll(dY0, 97 * s_, 0).contiguous(), bt(M, rs + rl), bt(M, N),
-                                   bt(M, K), bt(rl, K), bt(rl, N), lay.workspace(M, False),
+                                   torch.roll(dY0, 97 * s_, 0).contiguous(), bt(M, vrs + vrl), bt(M, N),
+                                   bt(M, K), bt(vrl, K), bt(vrl, N), lay.workspace(M, False),
                                    lay.workspace(M, True)))
         torch.cuda.synchronize()
 
@@ -815,6 +825,29 @@ def main():
             **res,
             "step_time_vs_tile32": {w: round(res[w]["us_per_step"] / res["tile32"]["us_per_step"], 3)
                                     for w in variants}}
+        del sets_, W0
+        torch.cuda.empty_cache()
+
+    # ------------------------------------------------------------ ranks
+    # The QKV step at larger stabilizer and adapter ranks: above R = 64 the
+    # GEMMs take four 32-rank steps per tile instead of two and the fused
+    # quantizer 5 to 8 rank groups.
+    if not a.no_ranks and a.only in (None, "ranks"):
+        variants = {"r32_16": (32, 16), "r32_32": (32, 32), "r32_64": (32, 64), "r64_64": (64, 64)}
+        res, (sets_, W0, (M, K, N, rs, rl)) = qkv_variants({k: {"ranks": v} for k, v in variants.items()})
+        for name, (vrs, vrl) in variants.items():
+            ent = res[name]
+            pflop = sum(v["flop"] for v in layer_work(M, K, N, vrs, vrl).values())
+            ent["r_stab"], ent["r_lora"] = vrs, vrl
+            ent["TFLOP/s"] = round(pflop / (ent["us_per_step"] * 1e-6) / 1e12, 1)
+            log("bench: ranks", name, json.dumps(ent))
+        out["rank_variants"] = {
+            "workload": f"QKV linear fwd+bwd (M={M}, K={K}, N={N}) at stabilizer/adapter ranks "
+                        "32/16 (the benchmark's), 32/32, 32/64 and 64/64; TFLOP/s counts each "
+                        "variant's own rank work; interleaved rounds, median",
+            **res,
+            "step_time_vs_r32_16": {k: round(res[k]["us_per_step"] / res["r32_16"]["us_per_step"], 3)
+                                    for k in variants}}
         del sets_, W0
         torch.cuda.empty_cache()
 

@@ -199,7 +199,7 @@ FwdLayout fwd_layout(const ft_linear* L) {
 // dY anyway) for adapter ranks up to 32; above that the adapter-gradient
 // kernel reads dY again.
 bool db_fused_in_quant(const ft_linear* L) {
-  return L->r_lora > 0 && ft::quant_down_db_chunks(L->M, L->N, L->r_lora) > 0;
+  return L->r_lora > 0 && ft::quant_down_db_chunks(L->M, L->N, L->r_stab + L->r_lora, L->r_lora) > 0;
 }
 
 struct BwdLayout {
@@ -225,7 +225,7 @@ BwdLayout bwd_layout(const ft_linear* L) {
   o.part = off; off += align_up(ft::quant_down_part_bytes(L->M, L->N, R, db_fused ? rl : 0));
   o.dA_part = off; off += align_up(rl ? ft::lora_grad_part_bytes(L->M, L->K, rl) : 0);
   o.dB_part = off;
-  off += align_up(db_fused ? ft::quant_down_db_bytes(L->M, L->N, rl)
+  off += align_up(db_fused ? ft::quant_down_db_bytes(L->M, L->N, R, rl)
                            : (rl ? ft::lora_grad_part_bytes(L->M, L->N, rl) : 0));
   o.total = off;
   return o;
@@ -489,7 +489,7 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
     b.act = L->act_out == FT_ACT_GELU_TANH ? 2 : 0;
     b.out = dB;
     b.part = reinterpret_cast<float*>(ws + lay.dB_part);
-    b.nchunk = db_fused ? ft::quant_down_db_chunks(L->M, L->N, rl) : 0;
+    b.nchunk = db_fused ? ft::quant_down_db_chunks(L->M, L->N, R, rl) : 0;
     Timed tm("bwd_lora_grads", st);
     if (tm.done(ft::launch_lora_grads(a, b, db_fused, st)) != hipSuccess) return FT_EDEVICE;
   }

@@ -33,10 +33,10 @@ hipError_t launch_quant_tile32(const uint16_t* in, int64_t rows, int64_t cols, i
 hipError_t launch_quant_row32_t(const uint16_t* in, int64_t rows, int64_t cols, int64_t ld,
                                 uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
                                 uint8_t* scales_t, hipStream_t st);
-// Ranks of the zero-padded rank operands the GEMM reads: 64 (FT_MAX_RANK)
-// whenever there is a rank part, so that every tile has the same two rank
-// steps.
-inline int rank_pad(int R) { return R > 0 ? 64 : 0; }
+// Ranks of the zero-padded rank operands the GEMM reads: 64 whenever there
+// is a rank part (two 32-rank steps per tile), 128 (FT_MAX_RANK, four steps)
+// above 64.
+inline int rank_pad(int R) { return R > 64 ? 128 : R > 0 ? 64 : 0; }
 
 // Row quantization fused with the down-projection out_lr = bf16(in . pr^T)
 // (pr rank-major, `cols` values per rank), as two launches (partial sums per
@@ -63,8 +63,8 @@ hipError_t launch_quant_down(const uint16_t* in, const uint16_t* in2, int act, i
                              const RankRows& cp, int64_t cp_rows, uint16_t* cp_dst, float* part,
                              const DbFuse* db, hipStream_t st, bool cp_planes = false);
 size_t quant_down_part_bytes(int64_t rows, int64_t cols, int R, int rl_db);
-int quant_down_db_chunks(int64_t rows, int64_t cols, int rl);   // 0: dB is not fused for this rl
-size_t quant_down_db_bytes(int64_t rows, int64_t cols, int rl);
+int quant_down_db_chunks(int64_t rows, int64_t cols, int R, int rl);   // 0: dB is not fused for this rl
+size_t quant_down_db_bytes(int64_t rows, int64_t cols, int R, int rl);
 
 // Dequantize 32x32-tile MXFP4 data to bf16: out [rows, cols] from codes
 // [rows, cols/2] and tile scales [rows/32, cols/32]; rows % 32 == 0,
@@ -90,7 +90,7 @@ struct GemmArgs {
                                   // [NOUT, RED/32] with b_row_scales (1x32 row blocks)
   const uint16_t* lm;             // bf16 [M, 32 * nlr], may be null when nlr == 0
   const uint16_t* lo;             // bf16 [NOUT, 32 * nlr]
-  int nlr;                        // 32-rank groups: 0 or 2 (rank_pad)
+  int nlr;                        // 32-rank groups: 0, 2 or 4 (rank_pad / 32)
   uint16_t* out;                  // bf16 [M, NOUT]
   // bf16 main product instead of the 4-bit one (a16 set: codes and scales
   // are not read): out = a16 b16^T + lm lo^T; RED % 32 == 0.

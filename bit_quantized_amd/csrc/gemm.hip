@@ -163,7 +163,8 @@ struct Frags {
 template <int K> struct MfmaKind { static constexpr int v = K; };   // 0: MXFP4, 1: bf16 ranks
 template <bool B> struct Flag { static constexpr bool v = B; };
 
-// LR: the tiles start with two rank steps (64 padded ranks).  An odd
+// NLR_: the tiles start with NLR_ rank steps (32 NLR_ padded ranks: 2 or 4
+// steps, rank rows of 64 or 128 bf16).  An odd
 // number of reduction steps is padded by one step whose loads are pushed
 // out of range: zero codes and zero scale bytes add exactly 0, and every
 // tile then has an even number of steps for the even/odd registers.
@@ -180,8 +181,9 @@ template <bool B> struct Flag { static constexpr bool v = B; };
 // wave; the tile scales of a step are 4 runs of 8 bytes (one per reduction
 // block, strided by NOUT/32), loaded as 3 aligned words each and turned
 // into per-column words (byte j = reduction block j) by byte permutes.
-template <bool LR, int BMODE>
+template <int NLR_, int BMODE>
 __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
+  constexpr bool LR = NLR_ > 0;
   constexpr bool BF = BMODE == 2, BROW = BMODE == 1, BT = BMODE == 3;
   __shared__ __attribute__((aligned(16))) uint8_t lds[NST * ST_BYTES];
   // the output strips: a separate LDS object (the stages are DMA targets)
@@ -198,7 +200,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   const uint32_t ntiles = mt_n * nt_n, G = gridDim.x, bid = blockIdx.x;
   const uint32_t full = ntiles / G, nlast = ntiles % G;
   const uint32_t my_tiles = full + (bid < nlast ? 1u : 0u);
-  constexpr int NLR = LR ? 2 : 0;
+  constexpr int NLR = NLR_;                              // rank steps: 0, 2 or 4
   const int nks_real = static_cast<int>(BF ? RED / 32 : RED / BK);
   const int nks = nks_real + (nks_real & 1);             // padded to even
   const int spt = nks + NLR;                             // steps per tile
@@ -213,7 +215,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
 
   const uint32_t row_bytes = static_cast<uint32_t>(BF ? RED * 2 : RED >> 1);
   const uint32_t row_sc = static_cast<uint32_t>(RED >> 5);
-  constexpr uint32_t LR_BYTES = 64 * 2;                  // a padded rank row: 64 bf16
+  constexpr uint32_t LR_BYTES = NLR * 64;                // a padded rank row: 32 NLR bf16
   const auto ra_codes = rsrc(BF ? static_cast<const void*>(g.a16) : g.a_codes, static_cast<uint64_t>(M) * row_bytes);
   const auto ra_sc = rsrc(g.a_scales, BF ? 0 : static_cast<uint64_t>(M) * row_sc);
   // BT: b rows are reduction rows of NOUT/2 bytes; its scale grid is
@@ -228,32 +230,32 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   const auto r_lm = rsrc(g.lm, LR ? static_cast<uint64_t>(M) * LR_BYTES : 0);
   // BT: lo is given as nibble planes, [2 rank steps x 128 rows, NOUT/2]
   // bytes (see half_dma)
-  const auto r_lo = rsrc(g.lo, !LR ? 0 : BT ? static_cast<uint64_t>(256) * bt_row
+  const auto r_lo = rsrc(g.lo, !LR ? 0 : BT ? static_cast<uint64_t>(128 * NLR) * bt_row
                                          : static_cast<uint64_t>(NOUT) * LR_BYTES);
 
   // Per-lane parts of the DMA source offsets (rows relative to the tile
   // origin; A and B tiles have the same shape).  Instruction q of wave w
   // fills 1 KB of LDS (16 rows of 64 bytes); lane i lands at byte 16 i.
-  uint32_t code_row[4], lr_row[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const uint32_t row = 64 * wave + 16 * q + (lane >> 2), ch = (lane & 3) ^ swz16(row);
-    code_row[q] = row * row_bytes + (ch << 4);
-    lr_row[q] = row * LR_BYTES + (ch << 4);
-  }
-  // BT keeps lane constants only; the rest of each offset is wave-uniform.
+  // Only lane constants are kept; the rest of each offset is wave-uniform.
   //  - rows 64 wave + 16 q + lane / 4: the chunk swizzle (row >> 2) & 3 is
   //    (lane >> 4) for every q, so lane part (lane >> 2) * pitch + chunk;
   //  - stored rows 32 wave + 8 q + lane / 8 of a BT 4-bit step of b: the
   //    slot swizzle (row >> 1) & 7 is (lane >> 4) ^ 4 (q & 1), so two lane
   //    parts, for even and odd q;
   //  - fragment reads (read_frags_bt): see there.
-  uint32_t bt_ca = 0, bt_cl = 0, bt_p[2] = {0, 0}, bt_fb = 0, bt_lc = 0;
-  if constexpr (BT) {
-    bt_lc = l32 * ROWB + ((grp ^ ((l32 >> 2) & 3)) << 4);
+  // (Per-instruction offsets held across the K loop were spilled at four
+  // rank steps, and each reload's memory wait drained the pipeline.)
+  //  - row-major fragment reads (read_frags_rows): row 32 i + l32 of a
+  //    wave's half, chunk (2 c + grp) ^ ((l32 >> 2) & 3), which is c = 0's
+  //    with byte bit 5 toggled.
+  uint32_t bt_ca, bt_cl, bt_p[2] = {0, 0}, bt_fb = 0, bt_lc;
+  {
     const uint32_t ch = (lane & 3) ^ (lane >> 4);
     bt_ca = (lane >> 2) * row_bytes + (ch << 4);
     bt_cl = (lane >> 2) * LR_BYTES + (ch << 4);
+    bt_lc = l32 * ROWB + ((grp ^ ((l32 >> 2) & 3)) << 4);
+  }
+  if constexpr (BT) {
     const uint32_t sl = (lane & 7) ^ (lane >> 4);
     bt_p[0] = (lane >> 3) * bt_row + (sl << 4);
     bt_p[1] = (lane >> 3) * bt_row + ((sl ^ 4) << 4);
@@ -343,7 +345,10 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
                                     : ca + static_cast<uint32_t>(64 * wave + 16 * item) * row_bytes;
         lane_off = is_b ? t_off : r_off;
       } else {
-        lane_off = h.lr ? lr_row[item] : code_row[item];
+        uint32_t ca = bt_ca, cl = bt_cl;
+        asm volatile("" : "+v"(ca), "+v"(cl));
+        lane_off = h.lr ? cl + static_cast<uint32_t>(64 * wave + 16 * item) * LR_BYTES
+                        : ca + static_cast<uint32_t>(64 * wave + 16 * item) * row_bytes;
       }
       dma16(h.rows, h.dst + item * 16 * ROWB, lane_off + h.base);
     } else {
@@ -366,31 +371,20 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
       }
     }
   };
+  // The lane part comes from an opaque copy of a lane constant: the
+  // compiler otherwise precomputes an address per fragment and chunk, and
+  // spills them.
   auto read_frags_rows = [&](int buf, int c, u32x4 (&af)[4], u32x4 (&bf)[4], bool with_b) {
-    const uint8_t* st = lds + buf * ST_BYTES;
-    if constexpr (BT) {
-      // a's lane part from an opaque copy of a lane constant: the compiler
-      // otherwise precomputes an address per fragment and chunk, and spills
-      // them in this variant.  Row 32 i + l32 of the wave's half; chunk
-      // (2 c + grp) ^ ((l32 >> 2) & 3) is c = 0's with byte bit 5 toggled.
-      uint32_t lc = bt_lc;
-      asm volatile("" : "+v"(lc));
-      const uint32_t base = static_cast<uint32_t>(buf * ST_BYTES + wm * 128 * ROWB) + (lc ^ (32u * c));
+    uint32_t lc = bt_lc;
+    asm volatile("" : "+v"(lc));
+    const uint32_t lcc = lc ^ (32u * c);
+    const uint32_t base = static_cast<uint32_t>(buf * ST_BYTES + wm * 128 * ROWB) + lcc;
 #pragma unroll
-      for (int i = 0; i < 4; ++i) af[i] = lds_read_b128(lds + base + i * 32 * ROWB);
-      return;
-    }
+    for (int i = 0; i < 4; ++i) af[i] = lds_read_b128(lds + base + i * 32 * ROWB);
+    if (BT || !with_b) return;
+    const uint32_t bbase = static_cast<uint32_t>(buf * ST_BYTES + ST_A + wn * 128 * ROWB) + lcc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wm * 128 + i * 32 + l32;
-      af[i] = lds_read_b128(st + row * ROWB + (((2 * c + grp) ^ swz16(row)) << 4));
-    }
-    if (!with_b) return;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int row = wn * 128 + i * 32 + l32;
-      bf[i] = lds_read_b128(st + ST_A + row * ROWB + (((2 * c + grp) ^ swz16(row)) << 4));
-    }
+    for (int i = 0; i < 4; ++i) bf[i] = lds_read_b128(lds + bbase + i * 32 * ROWB);
   };
   // BT, a 4-bit step: the b fragments of chunk c from the stored reduction
   // rows.  Lane (column half hf = bit 4, reduction group grp, q = lane % 16)
@@ -704,8 +698,11 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   for (uint32_t k = 0; k < my_tiles; ++k) {
     const bool after = k > 0;
     if constexpr (LR) {
-      step(E, O, rank, after);
-      step(O, E, rank, after);
+#pragma unroll
+      for (int r = 0; r < NLR / 2; ++r) {
+        step(E, O, rank, after && r == 0);
+        step(O, E, rank, after && r == 0);
+      }
       for (int p = 0; p < nks / 2; ++p) {
         if constexpr (BF) {
           step(E, O, rank, false);
@@ -953,16 +950,14 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     const int cus = cu_count();
     if (cus <= 0) return hipErrorInvalidDevice;
     const uint32_t grid = n < static_cast<uint32_t>(cus) ? n : static_cast<uint32_t>(cus);
-#define FT_GP(LR, MODE) hipLaunchKernelGGL((k_gemm_pipe<LR, MODE>), dim3(grid), dim3(256), 0, st, g)
-    if (bf) {
-      if (g.nlr > 0) FT_GP(true, 2); else FT_GP(false, 2);
-    } else if (g.b_row_scales) {
-      if (g.nlr > 0) FT_GP(true, 1); else FT_GP(false, 1);
-    } else if (g.b_transposed) {
-      if (g.nlr > 0) FT_GP(true, 3); else FT_GP(false, 3);
-    } else {
-      if (g.nlr > 0) FT_GP(true, 0); else FT_GP(false, 0);
-    }
+#define FT_GP(NL, MODE) hipLaunchKernelGGL((k_gemm_pipe<NL, MODE>), dim3(grid), dim3(256), 0, st, g)
+#define FT_GPN(MODE) do { if (g.nlr == 4) FT_GP(4, MODE); else if (g.nlr > 0) FT_GP(2, MODE); else FT_GP(0, MODE); } while (0)
+    if (g.nlr != 0 && g.nlr != 2 && g.nlr != 4) return hipErrorInvalidValue;
+    if (bf) FT_GPN(2);
+    else if (g.b_row_scales) FT_GPN(1);
+    else if (g.b_transposed) FT_GPN(3);
+    else FT_GPN(0);
+#undef FT_GPN
 #undef FT_GP
   } else if (bf) {
     return hipErrorInvalidValue;

@@ -193,12 +193,14 @@ __global__ __launch_bounds__(256) void k_lora_reduce(const LoraGradArgs pa, cons
 
 size_t lora_grad_part_bytes(int64_t M, int64_t I, int rl) {
   const int64_t nmc = (M + MC - 1) / MC;
-  const int RP = ((rl + 15) / 16) * 16;
+  const int RP = ((rl < 64 ? rl : 64) + 15) / 16 * 16;     // ranks of one pass
   return static_cast<size_t>(nmc) * I * RP * sizeof(float);
 }
 
-hipError_t launch_lora_grads(const LoraGradArgs& dA_in, const LoraGradArgs& dB_in, bool dB_done,
-                             hipStream_t st) {
+// One pass over at most 64 ranks (4 groups of 16: the rank operand of a
+// 512-token chunk fills most of the LDS at 64).
+static hipError_t lora_grads_pass(const LoraGradArgs& dA_in, const LoraGradArgs& dB_in, bool dB_done,
+                                  hipStream_t st) {
   LoraGradArgs dA = dA_in, dB = dB_in;
   const uint32_t nib_a = static_cast<uint32_t>((dA.I + IB - 1) / IB);
   const uint32_t nib_b = dB_done ? 0u : static_cast<uint32_t>((dB.I + IB - 1) / IB);
@@ -228,6 +230,25 @@ hipError_t launch_lora_grads(const LoraGradArgs& dA_in, const LoraGradArgs& dB_i
 #undef FT_L
 #undef FT_LA
   return hipGetLastError();
+}
+
+hipError_t launch_lora_grads(const LoraGradArgs& dA, const LoraGradArgs& dB, bool dB_done,
+                             hipStream_t st) {
+  if (dA.rl <= 64) return lora_grads_pass(dA, dB, dB_done, st);
+  // more than 64 ranks (never with dB_done: the quantizer fuses dB only up
+  // to 64): ranks 0 .. 63, then the rest, one after the other on the stream,
+  // so the second pass reuses the partial buffers
+  if (dB_done) return hipErrorInvalidValue;
+  const size_t es = dA.out_f32 ? 4 : 2;
+  LoraGradArgs a0 = dA, b0 = dB, a1 = dA, b1 = dB;
+  a0.rl = b0.rl = 64;
+  a1.rl = b1.rl = dA.rl - 64;
+  a1.r0 += 64;
+  b1.r0 += 64;
+  a1.out = static_cast<char*>(dA.out) + 64 * dA.I * es;
+  b1.out = static_cast<char*>(dB.out) + 64 * dB.I * (dB.out_f32 ? 4 : 2);
+  if (hipError_t e = lora_grads_pass(a0, b0, false, st); e != hipSuccess) return e;
+  return lora_grads_pass(a1, b1, false, st);
 }
 
 }  // namespace ft

@@ -526,8 +526,8 @@ __global__ __launch_bounds__(256, 1) void k_quant_down(const QDArgs a) {
     for (int hc = 0; hc < 4 * DBR; ++hc)
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        const uint32_t row = min(bx * 64 + 16 * (hc >> (DBR - 1)) + 4 * g + e, rows - 1);
-        const int r = min(16 * (hc & (DBR - 1)) + lr, a.u_rl - 1);
+        const uint32_t row = min(bx * 64 + 16 * (hc / DBR) + 4 * g + e, rows - 1);
+        const int r = min(16 * (hc % DBR) + lr, a.u_rl - 1);
         uu[hc][e] = a.u[row * static_cast<uint32_t>(a.ld_u) + a.u_r0 + r];
       }
   };
@@ -734,8 +734,9 @@ __device__ __forceinline__ void rank_sum_slab(const RRArgs& a, uint32_t b) {
   const uint32_t bx = b >> 2, wave = b & 3;
   const uint64_t slab = static_cast<uint64_t>(NRG) * 256;                 // floats per wave slab
   const uint64_t stride = static_cast<uint64_t>(nrb) * 4 * slab;          // between splits
-  if (t < 64 * NRG) {
-    const float* p = a.part + (static_cast<uint64_t>(bx) * 4 + wave) * slab + t * 4;
+  // (more than 4 rank groups: a thread owns items t and t + 256)
+  for (int it = t; it < 64 * NRG; it += 256) {
+    const float* p = a.part + (static_cast<uint64_t>(bx) * 4 + wave) * slab + it * 4;
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
     for (uint32_t y0 = 0; y0 < a.splits; y0 += 8) {
       f32x4 v[8];
@@ -746,7 +747,7 @@ __device__ __forceinline__ void rank_sum_slab(const RRArgs& a, uint32_t b) {
 #pragma unroll
       for (int k = 0; k < 8; ++k) s += v[k];
     }
-    const int c = t >> 6, lane = t & 63;
+    const int c = it >> 6, lane = it & 63;
 #pragma unroll
     for (int j = 0; j < 4; ++j) sum[4 * (lane >> 4) + j][16 * c + (lane & 15)] = s[j];
   }
@@ -795,8 +796,8 @@ __device__ __forceinline__ void copy_rank_chunk(const RRArgs& a, uint64_t e) {
 }
 
 // The other rank operand as nibble planes, for a GEMM that reads its b
-// operand with the 4-bit transposing LDS read (ds_read_b64_tr_b4): 64 ranks
-// (zero past R) of cp_rows columns become 256 plane rows of cp_rows / 2
+// operand with the 4-bit transposing LDS read (ds_read_b64_tr_b4): rpad ranks
+// (zero past R) of cp_rows columns become 4 rpad plane rows of cp_rows / 2
 // bytes, plane row 128 s + R for ranks 32 s .. 32 s + 31 holding, for
 // every column, nibble R % 4 of rank 32 s + R / 4's bf16 value (low nibble:
 // even column).  Such a read takes, for 16 lanes, 16 consecutive plane rows
@@ -808,7 +809,7 @@ __device__ __forceinline__ void copy_rank_chunk(const RRArgs& a, uint64_t e) {
 __device__ __forceinline__ void copy_rank_planes(const RRArgs& a, uint64_t e) {
   const RankRows& p = a.cp;
   const uint32_t pieces = static_cast<uint32_t>(a.cp_rows / 32);
-  if (e >= static_cast<uint64_t>(64) * pieces) return;
+  if (e >= static_cast<uint64_t>(a.rpad) * pieces) return;
   const int r = static_cast<int>(e / pieces);
   const uint32_t piece = static_cast<uint32_t>(e % pieces);
   const uint16_t* src = r < p.r0 ? p.p0 + static_cast<int64_t>(r) * p.ld
@@ -1026,67 +1027,84 @@ hipError_t launch_dequant_tile32(const uint8_t* codes, const uint8_t* scales, in
 }
 
 // Plan of the fused kernel: columns per split, splits and workgroups per
-// split.  KC: 256 when that still gives one row block and split per CU of a
-// 256-CU part, else 128.  (KC = 512, one workgroup per CU with two register
+// split.  KC: 256 when that still gives one row block and split per CU of
+// the device, else 128.  (KC = 512, one workgroup per CU with two register
 // sets, measured slower on every layer of a DiT block: QKV backward 46.8 ->
 // 42.1 us, MLP forward 56 -> 47.6 us at 256, while 128 was slower again.)
-// Workgroups per split: as many as fit on such a part at once (LDS allows
-// two per CU at KC = 256, four at 128), at most one per row block.  Fixed by
-// the shapes only, so the workspace size does not depend on the device.
+// Workgroups per split: as many as fit on the device at once (LDS allows
+// two per CU at KC = 256, four at 128, half that for ranks above 64), at
+// most one per row block.  The device's CU count (256 on an MI355X; 256 when
+// no device is current, as for a workspace query on a host without one)
+// sets the plan, so the workspace size is that of the device it runs on.
 struct QDPlan {
   int kc;
   uint32_t nrb, splits, G;
 };
-static QDPlan quant_down_plan(int64_t rows, int64_t cols, int dbr) {
+static uint32_t plan_cus() {
+  const int c = cu_count();
+  return c > 0 ? static_cast<uint32_t>(c) : 256u;
+}
+static QDPlan quant_down_plan(int64_t rows, int64_t cols, int R, int dbr) {
   QDPlan p;
+  const uint32_t cus = plan_cus();
   const int64_t rb = (rows + 63) / 64;
-  p.kc = rb * ((cols + 255) / 256) >= 256 ? 256 : 128;
+  p.kc = rb * ((cols + 255) / 256) >= cus ? 256 : 128;
   (void)dbr;                                   // both widths hold the dB accumulators
   p.nrb = static_cast<uint32_t>(rb);
   p.splits = static_cast<uint32_t>((cols + p.kc - 1) / p.kc);
-  uint32_t G = 256u * static_cast<uint32_t>(512 / p.kc) / p.splits;
+  const uint32_t per_cu = static_cast<uint32_t>(512 / p.kc) / (R > 64 ? 2u : 1u);
+  uint32_t G = cus * per_cu / p.splits;
   p.G = G < 1 ? 1 : (G > p.nrb ? p.nrb : G);
   return p;
 }
 
 // Adapter rank groups whose dB is fused into the kernel (0: not fused).
-static int quant_down_dbr(int rl) { return rl > 0 && rl <= 32 ? (rl + 15) / 16 : 0; }
+static int quant_down_dbr(int rl) { return rl > 0 && rl <= 64 ? (rl + 15) / 16 : 0; }
+
+// Rank groups of 16 the kernel is instantiated for: 1-4, 6 and 8 (5 and 7
+// run as 6 and 8, the extra ranks zero).
+static int quant_down_nrg(int R) {
+  const int g = (R + 15) / 16;
+  return g <= 4 ? g : g <= 6 ? 6 : 8;
+}
 
 size_t quant_down_part_bytes(int64_t rows, int64_t cols, int R, int rl_db) {
   if (R == 0) return 0;
-  const QDPlan p = quant_down_plan(rows, cols, quant_down_dbr(rl_db));
-  const int64_t nrg = (R + 15) / 16;
+  const QDPlan p = quant_down_plan(rows, cols, R, quant_down_dbr(rl_db));
+  const int64_t nrg = quant_down_nrg(R);
   return static_cast<size_t>(p.splits) * p.nrb * 4 * nrg * 256 * sizeof(float);
 }
 
-int quant_down_db_chunks(int64_t rows, int64_t cols, int rl) {
+int quant_down_db_chunks(int64_t rows, int64_t cols, int R, int rl) {
   const int dbr = quant_down_dbr(rl);
-  return dbr ? static_cast<int>(quant_down_plan(rows, cols, dbr).G) : 0;
+  return dbr ? static_cast<int>(quant_down_plan(rows, cols, R, dbr).G) : 0;
 }
 
-size_t quant_down_db_bytes(int64_t rows, int64_t cols, int rl) {
+size_t quant_down_db_bytes(int64_t rows, int64_t cols, int R, int rl) {
   const int dbr = quant_down_dbr(rl);
   if (!dbr) return 0;
-  const QDPlan p = quant_down_plan(rows, cols, dbr);
+  const QDPlan p = quant_down_plan(rows, cols, R, dbr);
   return static_cast<size_t>(p.G) * dbr * 16 * cols * sizeof(float);
 }
 
-// Forward: act 0 or 1, no dB.  Backward: act 0 or 2, dB fused (1 or 2 rank
-// groups; 2 only at KC <= 256 with R > 16, as the plan guarantees) or not.
+// Forward: act 0 or 1, no dB.  Backward: act 0 or 2, dB fused (1 to 4 rank
+// groups, never more than the kernel's NRG: r_l <= R) or not.
 template <int NRG, int NS>
 static void launch_qd(const QDArgs& a, dim3 grid, int act, int dbr, hipStream_t st) {
 #define FT_QDA(ACT, D) hipLaunchKernelGGL((k_quant_down<NRG, NS, ACT, D>), grid, dim3(256), 0, st, a)
+#define FT_QDB(D)                                                                               do {                                                                                            if constexpr (D <= NRG) {                                                                       if (act == 2) FT_QDA(2, D); else FT_QDA(0, D);                                              }                                                                                           } while (0)
   if (act == 1) {
     FT_QDA(1, 0);
-  } else if (dbr == 0) {
-    if (act == 2) FT_QDA(2, 0); else FT_QDA(0, 0);
-  } else if (dbr == 1) {
-    if (act == 2) FT_QDA(2, 1); else FT_QDA(0, 1);
   } else {
-    if constexpr (NS <= 2 && NRG >= 2) {
-      if (act == 2) FT_QDA(2, 2); else FT_QDA(0, 2);
+    switch (dbr) {
+      case 0: FT_QDB(0); break;
+      case 1: FT_QDB(1); break;
+      case 2: FT_QDB(2); break;
+      case 3: FT_QDB(3); break;
+      default: FT_QDB(4); break;
     }
   }
+#undef FT_QDB
 #undef FT_QDA
 }
 
@@ -1098,7 +1116,7 @@ hipError_t launch_quant_down(const uint16_t* in, const uint16_t* in2, int act, i
   const int R = pr.r0 + pr.r1;
   const int dbr = db ? quant_down_dbr(db->rl) : 0;
   if (db && !dbr) return hipErrorInvalidValue;
-  const QDPlan pl = quant_down_plan(rows, cols, dbr);
+  const QDPlan pl = quant_down_plan(rows, cols, R, dbr);
   const int kc = pl.kc;
   const uint32_t nrb = pl.nrb, splits = pl.splits, G = pl.G;
   QDArgs a{in, in2, static_cast<uint32_t>(rows), static_cast<uint32_t>(cols), ld, codes, scales,
@@ -1106,7 +1124,7 @@ hipError_t launch_quant_down(const uint16_t* in, const uint16_t* in2, int act, i
            db ? db->u : nullptr, db ? db->ld_u : 0, db ? db->r0 : 0, db ? db->rl : 0,
            db ? db->part : nullptr};
   const dim3 grid(splits * G);
-  const int nrg = (R + 15) / 16;
+  const int nrg = quant_down_nrg(R);
   if (dbr > nrg) return hipErrorInvalidValue;
 #define FT_QD_NS(NRG)                                                                         \
   do {                                                                                        \
@@ -1117,13 +1135,15 @@ hipError_t launch_quant_down(const uint16_t* in, const uint16_t* in2, int act, i
     case 1: FT_QD_NS(1); break;
     case 2: FT_QD_NS(2); break;
     case 3: FT_QD_NS(3); break;
-    default: FT_QD_NS(4); break;
+    case 4: FT_QD_NS(4); break;
+    case 6: FT_QD_NS(6); break;
+    default: FT_QD_NS(8); break;
   }
 #undef FT_QD_NS
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
   RRArgs b{part, static_cast<uint32_t>(rows), splits, R, rank_pad(R), out_lr, out_pad, cp, cp_rows, cp_dst,
            cp_planes ? 1 : 0};
-  const uint64_t ncopy = cp_planes ? (static_cast<uint64_t>(64) * (cp_rows / 32) + 255) / 256
+  const uint64_t ncopy = cp_planes ? (static_cast<uint64_t>(rank_pad(R)) * (cp_rows / 32) + 255) / 256
                                    : (static_cast<uint64_t>(cp_rows) * (rank_pad(R) / 8) + 255) / 256;
   const dim3 rgrid(static_cast<uint32_t>(nrb * 4 + ncopy));
 #define FT_RR(NRG) hipLaunchKernelGGL((k_rank_reduce<NRG>), rgrid, dim3(256), 0, st, b)
@@ -1131,7 +1151,9 @@ hipError_t launch_quant_down(const uint16_t* in, const uint16_t* in2, int act, i
     case 1: FT_RR(1); break;
     case 2: FT_RR(2); break;
     case 3: FT_RR(3); break;
-    default: FT_RR(4); break;
+    case 4: FT_RR(4); break;
+    case 6: FT_RR(6); break;
+    default: FT_RR(8); break;
   }
 #undef FT_RR
   return hipGetLastError();

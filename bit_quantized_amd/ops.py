@@ -17,7 +17,7 @@ LIB_PATH = os.path.join(HERE, "libfourtune.so")
 FT_OK, FT_EINVAL, FT_ESHAPE, FT_EALIGN, FT_EWORKSPACE, FT_EDEVICE, FT_EUNSUPPORTED = range(7)
 FT_BF16, FT_F32 = 0, 1
 FT_Q_ROW32, FT_Q_ROW32_T, FT_Q_TILE32 = 1, 2, 4
-FT_MAX_RANK = 64
+FT_MAX_RANK = 128
 FT_NOALLOC_SCRATCH_BYTES = 64 << 20
 FT_ACT_NONE, FT_ACT_GELU_TANH = 0, 1
 FT_W4A4G4, FT_W4A16G4, FT_W4A4G16, FT_W4A16G16 = 0, 1, 2, 3

@@ -26,7 +26,7 @@
  *                        given as MXFP4 32x32 tiles
  *   L1  [K, r_stab], L2 [r_stab, N]        frozen stabilizer, bf16
  *   A   [K, r_lora], B  [r_lora, N]        trainable adapter, bf16
- *   D = [L1 | A]  [K, R],  V = [L2 ; B]  [R, N],  R = r_stab + r_lora <= 64
+ *   D = [L1 | A]  [K, R],  V = [L2 ; B]  [R, N],  R = r_stab + r_lora <= 128
  *
  *   forward : Y  = deq(Qrow(X)) deq(Qtile(W_res))^T + U V,   U = bf16(X D)
  *   backward: dX = deq(Qrow(dY)) deq(Qtile(W_res)) + P D^T,  P = bf16(dY V^T)
@@ -79,7 +79,7 @@ extern "C" {
 typedef enum {
   FT_OK = 0,
   FT_EINVAL = 1,       /* null pointer where one is required, bad enum value   */
-  FT_ESHAPE = 2,       /* size not allowed (K or N not multiple of 32, R > 64)  */
+  FT_ESHAPE = 2,       /* size not allowed (K or N not multiple of 32, R > 128) */
   FT_EALIGN = 3,       /* device pointer not 16-byte aligned, or bad row stride */
   FT_EWORKSPACE = 4,   /* workspace smaller than fourtune_workspace_bytes       */
   FT_EDEVICE = 5,      /* a HIP launch failed                                   */
@@ -137,13 +137,13 @@ typedef enum {
   FT_WBLOCK_TILE32_T = 2
 } ft_wblock;
 
-#define FT_MAX_RANK 64
+#define FT_MAX_RANK 128
 
 /* One triple-branch linear layer.  Host struct; the pointers in it are device
  * pointers.  Either rank may be 0 (then its two pointers may be NULL). */
 typedef struct {
   int64_t M, K, N;            /* tokens, input features, output features            */
-  int32_t r_stab, r_lora;     /* stabilizer and adapter ranks, r_stab + r_lora <= 64 */
+  int32_t r_stab, r_lora;     /* stabilizer and adapter ranks, r_stab + r_lora <= 128 */
   const uint8_t* w_codes;     /* Qtile(W_res) codes  [N, K/2] (ROW32: Qrow32(W_res))  */
   const uint8_t* w_scales;    /* Qtile(W_res) scales [N/32, K/32]; ROW32: [N, K/32]   */
   const uint8_t* wt_codes;    /* the dgrad's separately stored weight, read only by a */
@@ -219,7 +219,7 @@ size_t fourtune_workspace_bytes(const ft_linear* L, int is_bwd);
  *   them in the workspace.  Must be NULL under A16 (there are no codes).
  * workspace: device memory of at least fourtune_workspace_bytes(L, 0) bytes;
  *   contents on entry are ignored and on return unspecified.
- * Requirements: M >= 1, K % 32 == 0, N % 32 == 0, R <= 64, and every
+ * Requirements: M >= 1, K % 32 == 0, N % 32 == 0, R <= 128, and every
  *   activation padded to 256 more rows below 2^31 bytes:
  *   (M + 256) * max(K, N) * 2 < 2^31 (the kernels use 32-bit offsets);
  *   under A16 or G16 the same for the dequantized weight,

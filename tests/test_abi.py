@@ -80,7 +80,7 @@ def _bwd(L, dY=A16, X=A16, U=A16, dX=A16, dA=A16, dB=A16, gdt=0, P=None, qc=None
 
 
 def test_linear_shape_errors():
-    for L in (_layer(M=0), _layer(K=48), _layer(N=40), _layer(K=0), _layer(rs=40, rl=30),
+    for L in (_layer(M=0), _layer(K=48), _layer(N=40), _layer(K=0), _layer(rs=70, rl=60),
               _layer(rs=-1)):
         assert _fwd(L) == ops.FT_ESHAPE
         assert _bwd(L) == ops.FT_ESHAPE

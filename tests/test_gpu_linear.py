@@ -45,6 +45,16 @@ def test_tiny_case_full():
     (300, 288, 512, 16, 8),      # K / 32 = 9
     (96, 160, 256, 0, 0),        # K / 32 = 5, no ranks
     (260, 224, 384, 32, 16),     # K / 32 = 7
+    # more than 64 ranks: four rank steps per GEMM tile, 5 to 8 rank groups
+    # in the fused quantizer, dB fused up to r_l = 64, two adapter-gradient
+    # passes above that
+    (300, 288, 544, 32, 64),     # R = 96, ragged in every dimension
+    (260, 224, 384, 32, 64),     # R = 96, pipelined dgrad on the packed weight
+    (130, 512, 288, 64, 64),     # R = 128, the cap
+    (200, 640, 384, 48, 40),     # R = 88 (run as 96), dB over 3 rank groups
+    (96, 256, 320, 5, 70),       # r_l > 64, ranks not multiples of 8
+    (64, 256, 256, 0, 128),      # adapter only, 128 ranks
+    (4200, 1120, 800, 32, 64),   # several column splits with a ragged last one
 ])
 def test_ragged_shapes_full(shape):
     M, K, N, rs, rl = shape
@@ -140,16 +150,16 @@ def _random_shapes(n, seed):
         M = int(rng.integers(1, 700))
         K = 32 * int(rng.integers(1, 40))
         N = 32 * int(rng.integers(1, 40))
-        rs = int(rng.integers(0, 33))
-        rl = int(rng.integers(0, 65 - rs)) if rng.random() < 0.8 else 0
-        out.append((M, K, N, rs, min(rl, 64 - rs)))
+        rs = int(rng.integers(0, 65))
+        rl = int(rng.integers(0, 129 - rs)) if rng.random() < 0.8 else 0
+        out.append((M, K, N, rs, min(rl, 128 - rs)))
     return out
 
 
-@pytest.mark.parametrize("shape", _random_shapes(10, 2027))
+@pytest.mark.parametrize("shape", _random_shapes(12, 2027))
 def test_random_shapes_full(shape):
     """A seeded sweep of shapes: any M, K and N multiples of 32 (so both GEMM
-    kernels and every split width of the fused quantizer), ranks 0..64."""
+    kernels and every split width of the fused quantizer), ranks 0..128."""
     M, K, N, rs, rl = shape
     c = synth.flux_linear_case(f"rand_{M}x{K}x{N}_r{rs}_{rl}", M, K, N, rs, rl, seed=M * 7 + K + N)
     say("case", c.name)
@@ -246,6 +256,14 @@ def test_qkv_full_size_sampled():
     c = synth.qkv_case()
     say("case", c.name)
     check_sampled(c, GpuCase(c).run(), _rows(c.M))
+
+
+def test_qkv_full_size_rank96_sampled():
+    """The QKV linear at its full size with an adapter of rank 64 (R = 96):
+    four rank steps per GEMM tile, dB fused over four rank groups."""
+    c = synth.flux_linear_case("qkv_4608x3072x9216_r32_64", 4608, 3072, 9216, 32, 64, seed=3)
+    say("case", c.name)
+    check_sampled(c, GpuCase(c).run(), _rows(c.M, seed=5))
 
 
 def test_mlp_pair_full_size_sampled():
