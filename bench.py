@@ -677,13 +677,37 @@ def main():
         e1.record(stream)
         torch.cuda.synchronize()
         bms = e0.elapsed_time(e1) / nst
+        # each linear on its own: fwd and bwd, event-timed over the same
+        # number of repetitions (the modulation linears run the split GEMMs)
+        per_lin = {}
+        for e in blk:
+            d = e["lay"].desc(e["M"])
+            H = by[e["name"][:4] + "fc1"]["Y"] if e["name"].endswith("fc1") else None
+
+            def lf(e=e, d=d):
+                ops.fourtune_linear_fwd(d, e["X"], e["Y"], e["U"], None, None, e["wf"], e["wf"].numel(),
+                                        stream)
+
+            def lb(e=e, d=d, H=H):
+                ops.fourtune_linear_bwd(d, e["dY"], e["X"], e["U"], H, e["dX"], e["dA"], e["dB"],
+                                        ops.FT_BF16, None, None, None, e["wb"], e["wb"].numel(), stream)
+            ent = {}
+            for kind, fn in (("fwd", lf), ("bwd", lb)):
+                fn()
+                e0.record(stream)
+                for _ in range(nst):
+                    fn()
+                e1.record(stream)
+                torch.cuda.synchronize()
+                ent[kind + "_us"] = round(e0.elapsed_time(e1) / nst * 1e3, 1)
+            per_lin[e["name"]] = ent
         out["dit_block"] = {
             "workload": "all linears of one double-stream DiT block at batch 2, fwd+bwd: per stream "
                         "(image 8192 tokens, text 1024) QKV 3072->9216, out-projection 3072->3072, "
                         "MLP 3072->12288->GELU->3072, and the modulation linear 3072->18432 at M=2; "
                         "r_stab=32, r_lora=16",
             "us_per_step": round(bms * 1e3, 1), "TFLOP/s": round(bflop / (bms * 1e-3) / 1e12, 1),
-            "step_flop": bflop, "steps": nst}
+            "step_flop": bflop, "steps": nst, "per_linear": per_lin}
         log("bench: block", json.dumps(out["dit_block"]))
         del blk, by
         torch.cuda.empty_cache()

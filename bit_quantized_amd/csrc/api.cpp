@@ -175,7 +175,7 @@ inline bool a16(const ft_linear* L) { return (L->precision & FT_W4A16G4) != 0; }
 inline bool g16(const ft_linear* L) { return (L->precision & FT_W4A4G16) != 0; }
 
 struct FwdLayout {
-  size_t xq_codes, xq_scales, u_pad, v_pad, part, w16, x16, total;
+  size_t xq_codes, xq_scales, u_pad, v_pad, part, w16, x16, sk_part, total;
 };
 FwdLayout fwd_layout(const ft_linear* L) {
   const int R = L->r_stab + L->r_lora;
@@ -191,6 +191,8 @@ FwdLayout fwd_layout(const ft_linear* L) {
   o.u_pad = off; off += align_up(static_cast<size_t>(L->M) * rp * 2);     // U, zero-padded ranks
   o.v_pad = off; off += align_up(static_cast<size_t>(L->N) * rp * 2);     // [L2^T | B^T], padded
   o.part = off; off += align_up(ft::quant_down_part_bytes(L->M, L->K, R, 0));
+  // the GEMM's split sums when the output has few tiles (a few rows)
+  o.sk_part = off; off += bf ? 0 : align_up(ft::gemm_split_bytes(L->M, L->K, L->N));
   o.total = off;
   return o;
 }
@@ -203,7 +205,7 @@ bool db_fused_in_quant(const ft_linear* L) {
 }
 
 struct BwdLayout {
-  size_t gq_codes, gq_scales, P, p_pad, d_pad, part, dA_part, dB_part, w16, g16, total;
+  size_t gq_codes, gq_scales, P, p_pad, d_pad, part, dA_part, dB_part, w16, g16, sk_part, total;
 };
 BwdLayout bwd_layout(const ft_linear* L) {
   const int R = L->r_stab + L->r_lora;
@@ -227,6 +229,7 @@ BwdLayout bwd_layout(const ft_linear* L) {
   o.dB_part = off;
   off += align_up(db_fused ? ft::quant_down_db_bytes(L->M, L->N, R, rl)
                            : (rl ? ft::lora_grad_part_bytes(L->M, L->N, rl) : 0));
+  o.sk_part = off; off += bf ? 0 : align_up(ft::gemm_split_bytes(L->M, L->N, L->K));
   o.total = off;
   return o;
 }
@@ -365,6 +368,11 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
   g.b_codes = L->w_codes; g.b_scales = L->w_scales;
   g.b_row_scales = L->w_block == FT_WBLOCK_ROW32;
   g.lm = u_pad; g.lo = v_pad; g.nlr = ft::rank_pad(R) / 32; g.out = Y;
+  if (!bf) {
+    const ft::SplitPlan sp = ft::gemm_split_plan(L->M, L->K, L->N);
+    g.splits = sp.splits; g.split_pairs = sp.pairs;
+    g.part = reinterpret_cast<float*>(ws + lay.sk_part);
+  }
   if (bf) {
     uint16_t* w16 = reinterpret_cast<uint16_t*>(ws + lay.w16);
     {
@@ -430,7 +438,10 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
     Timed tm("bwd_quant_down", st);
     // the pipelined dgrad on the forward's tiles (N % 128 == 0, 4-bit)
     // reads [L1 | A] as nibble planes through its transposing b read
-    const bool planes = L->w_block == FT_WBLOCK_TILE32 && !bf && (L->N % 128) == 0;
+    // (not when the dgrad splits its reduction: the split sums' kernel
+    // reads the plain [K, ranks] copy)
+    const bool planes = L->w_block == FT_WBLOCK_TILE32 && !bf && (L->N % 128) == 0 &&
+                        ft::gemm_split_plan(L->M, L->N, L->K).splits <= 1;
     e = tm.done(ft::launch_quant_down(dY, h2, act, L->M, L->N, L->N, qc, qs, rows_V(L), P, p_pad,
                                       rows_Dt(L), dX ? L->K : 0, d_pad,
                                       reinterpret_cast<float*>(ws + lay.part),
@@ -453,6 +464,11 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
       g.b_row_scales = L->w_block == FT_WBLOCK_ROW32;
     }
     g.lm = p_pad; g.lo = d_pad; g.nlr = ft::rank_pad(R) / 32; g.out = dX;
+    if (!bf) {
+      const ft::SplitPlan sp = ft::gemm_split_plan(L->M, L->N, L->K);
+      g.splits = sp.splits; g.split_pairs = sp.pairs;
+      g.part = reinterpret_cast<float*>(ws + lay.sk_part);
+    }
     if (bf) {
       uint16_t* w16 = reinterpret_cast<uint16_t*>(ws + lay.w16);
       {

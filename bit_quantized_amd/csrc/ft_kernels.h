@@ -101,8 +101,26 @@ struct GemmArgs {
   // [RED, NOUT/2] with tile scales [RED/32, NOUT/32]: b[j][red] is read as
   // element (red, j) (the dgrad on the forward's weight)
   int b_transposed;
+  // Split reduction, for outputs of few tiles (gemm_split_plan): splits
+  // units per tile, each over split_pairs pairs of 128-element steps, write
+  // fp32 sums to part [splits, M, NOUT]; a second kernel adds them in split
+  // order, adds lm lo^T and rounds to out.  splits <= 1: one pass.
+  int splits, split_pairs;
+  float* part;
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+// The split plan of a 4-bit product [M, RED] x [RED, NOUT] (RED % 128 == 0):
+// splits > 1 when the output has at most 128 tiles of 256 x 256 and the
+// shorter units outweigh the traffic of their sums (gemm.hip); fixed by the
+// shapes, not the device.
+struct SplitPlan {
+  int splits, pairs;
+};
+SplitPlan gemm_split_plan(int64_t M, int64_t RED, int64_t NOUT);
+inline size_t gemm_split_bytes(int64_t M, int64_t RED, int64_t NOUT) {
+  const SplitPlan p = gemm_split_plan(M, RED, NOUT);
+  return p.splits > 1 ? static_cast<size_t>(p.splits) * M * NOUT * sizeof(float) : 0;
+}
 
 // lora.hip: out[r][i] = sum_m act(big)[m][i] * small[m][r0 + r], r < rl,
 // act as for the row quantizers (big2 is the second input of act 2).

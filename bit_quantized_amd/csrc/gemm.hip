@@ -63,6 +63,8 @@
 #include "ft_device.hpp"
 #include "ft_kernels.h"
 
+#include <algorithm>
+
 namespace ft {
 
 namespace {
@@ -197,20 +199,30 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
 
   const uint32_t mt_n = static_cast<uint32_t>((M + BM - 1) / BM);
   const uint32_t nt_n = static_cast<uint32_t>((NOUT + BN - 1) / BN);
-  const uint32_t ntiles = mt_n * nt_n, G = gridDim.x, bid = blockIdx.x;
+  // Split reduction (few output tiles): unit u is tile u / S over steps
+  // (u % S) * nks .. + nks of the reduction, its fp32 sums stored to
+  // g.part; S = 1 otherwise (a unit is a whole tile).
+  // (only without rank steps: a split launch leaves the rank part to the
+  // kernel that adds the splits)
+  const uint32_t S = (!LR && g.splits > 1) ? static_cast<uint32_t>(g.splits) : 1u;
+  const uint32_t ntiles = mt_n * nt_n * S, G = gridDim.x, bid = blockIdx.x;
   const uint32_t full = ntiles / G, nlast = ntiles % G;
   const uint32_t my_tiles = full + (bid < nlast ? 1u : 0u);
   constexpr int NLR = NLR_;                              // rank steps: 0, 2 or 4
   const int nks_real = static_cast<int>(BF ? RED / 32 : RED / BK);
-  const int nks = nks_real + (nks_real & 1);             // padded to even
+  const int nks = S > 1 ? 2 * g.split_pairs             // steps per unit; a split past
+                        : nks_real + (nks_real & 1);     // the end loads zeros; padded to even
   const int spt = nks + NLR;                             // steps per tile
   const int total = static_cast<int>(my_tiles) * spt;
   const bool tiny = spt < 3;                              // see the barrier waits
 
-  // k-th tile of this workgroup: rounds of G tiles, XCD-compact in a round
-  auto tile_of = [&](uint32_t k, int64_t& m0, int64_t& j0) {
+  // k-th tile of this workgroup: rounds of G tiles, XCD-compact in a round;
+  // ko: the unit's first reduction step
+  auto tile_of = [&](uint32_t k, int64_t& m0, int64_t& j0, int& ko) {
     const uint32_t n_round = k < full ? G : nlast;
-    tile_coords(k * G + xcd_remap(bid, n_round), mt_n, nt_n, m0, j0);
+    const uint32_t u = k * G + xcd_remap(bid, n_round);
+    tile_coords(u / S, mt_n, nt_n, m0, j0);
+    ko = static_cast<int>(u % S) * nks;
   };
 
   const uint32_t row_bytes = static_cast<uint32_t>(BF ? RED * 2 : RED >> 1);
@@ -266,12 +278,13 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   // DMA cursor: the (tile, step) whose A or B half is loaded next, with the
   // tile's base offsets.  A cursors use m0, B cursors j0.
   struct Cursor {
-    int gs, s;
+    int gs, s, ko;
     uint32_t k, code, sc, lr;
   };
   auto cursor_tile = [&](Cursor& c, bool is_b) {
     int64_t m0 = 0, j0 = 0;
-    if (c.k < my_tiles) tile_of(c.k, m0, j0);
+    c.ko = 0;
+    if (c.k < my_tiles) tile_of(c.k, m0, j0, c.ko);
     const uint32_t o = static_cast<uint32_t>(is_b ? j0 : m0);
     if (BT && is_b) {
       // the tile's first byte column and scale column of every stored row
@@ -306,7 +319,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
     HalfDma h;
     const bool live = c.gs < total;
     const bool lrs = LR && c.s < NLR;
-    const int ks = c.s - NLR;
+    const int ks = c.s - NLR + c.ko;                         // reduction step
     h.lr = lrs;
     h.rows = lrs ? (is_b ? r_lo : r_lm) : (is_b ? rb_codes : ra_codes);
     h.sc = is_b ? rb_sc : ra_sc;
@@ -525,8 +538,41 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
         for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
   };
 
+  // Split units: the fp32 sums of rows below M to g.part[split][row][col],
+  // 128 bytes of a row per half wave; row groups past M are skipped whole
+  // (a uniform test: a few-row output stores a few groups).  The stores are
+  // then drained, so the waits of the next unit's steps, which budget for a
+  // tile's 32 bf16 stores, still hold.
+  auto store_part = [&](int64_t m0, int64_t j0, int split) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    float* dst = g.part + static_cast<int64_t>(split) * M * NOUT;
+    const int64_t col0 = j0 + wn * 128 + (ln & 31);
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int64_t rbase = m0 + wm * 128 + 32 * mt + 8 * q;
+        if (rbase >= M) continue;
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int64_t row = rbase + 4 * (ln >> 5) + e, col = col0 + 32 * nt;
+            if (row < M && col < NOUT) dst[row * NOUT + col] = acc[mt][nt][4 * q + e];
+          }
+      }
+    __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0xF));
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  };
+
   // ---- prologue: stages 0..2 and the A half of stage 3
-  Cursor ca{0, 0, 0, 0, 0, 0}, cb{0, 0, 0, 0, 0, 0};
+  Cursor ca{0, 0, 0, 0, 0, 0, 0}, cb{0, 0, 0, 0, 0, 0, 0};
   cursor_tile(ca, false);
   cursor_tile(cb, true);
   for (int s = 0; s < NST - 1; ++s) {
@@ -724,7 +770,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
       }
     }
     int64_t m0, j0;
-    tile_of(k, m0, j0);
+    int ko;
+    tile_of(k, m0, j0, ko);
+    if constexpr (!LR) {
+      if (S > 1) {
+        store_part(m0, j0, ko / nks);
+        continue;
+      }
+    }
     store_tile(m0, j0);
   }
   // DMAs into LDS must land before the workgroup can end
@@ -943,9 +996,135 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
 
 }  // namespace
 
+// A unit's work against the cost of its sums (times in us): a step pair
+// takes about 2.1; a unit ends by storing its rows' fp32 sums, at about 25
+// GB/s per workgroup; the adding kernel reads them all (5 TB/s) and costs
+// about 3 more.  S is the cheapest count under that model that keeps every
+// unit in one round of 256; shapes alone decide it, so the workspace size
+// does not depend on the device.
+SplitPlan gemm_split_plan(int64_t M, int64_t RED, int64_t NOUT) {
+  SplitPlan p{1, 0};
+  if (M <= 0 || RED <= 0 || (RED & 127) != 0 || (NOUT & 3) != 0) return p;
+  const int64_t tiles = ((M + BM - 1) / BM) * ((NOUT + BN - 1) / BN);
+  const int64_t steps = RED / BK, pairs = (steps + 1) / 2;
+  if (tiles > 128 || pairs < 2) return p;
+  const int64_t smax = std::min<int64_t>(pairs, 256 / tiles);
+  const double unit_rows = static_cast<double>(std::min<int64_t>(M, BM));
+  double best = 2.1 * pairs;
+  for (int64_t sc = 2; sc <= smax; ++sc) {
+    const int64_t per = (pairs + sc - 1) / sc;
+    const int64_t used = (pairs + per - 1) / per;        // no empty split
+    const double t = 2.1 * per + unit_rows * BN * 4 / 25e3 +
+                     static_cast<double>(used) * M * NOUT * 4 / 5e6 + 3.0;
+    if (t < best) {
+      best = t;
+      p.splits = static_cast<int>(used);
+      p.pairs = static_cast<int>(per);
+    }
+  }
+  return p;
+}
+
+namespace {
+// out[m][j] = bf16(sum over splits s (in order) of part[s][m][j] + sum over
+// ranks r of lm[m][r] lo[j][r]).  Workgroup: 8 rows x 256 columns; thread
+// t owns column j0 + t.  Its first 8 splits' sums and its rank row of lo
+// are loaded before the rows of lm are staged in LDS, so that one memory
+// latency covers all three; later splits follow 8 at a time.
+constexpr int SR_ROWS = 8;
+__global__ __launch_bounds__(256) void k_split_reduce(const GemmArgs g) {
+  __shared__ __attribute__((aligned(16))) uint16_t slm[SR_ROWS * 128];
+  // 32-bit indices (the sums are below 2^31 bytes); the row and split
+  // tests are uniform and the column is clamped into the row, so every
+  // load is a buffer load with a selected offset: no branches, and the
+  // loads of a batch all issue before the first wait
+  const uint32_t M = static_cast<uint32_t>(g.M), NOUT = static_cast<uint32_t>(g.NOUT);
+  const uint32_t j = blockIdx.x * 256 + threadIdx.x;
+  const uint32_t jc = j < NOUT ? j : NOUT - 1;
+  const uint32_t m0 = blockIdx.y * SR_ROWS;
+  const int rp = 32 * g.nlr, S = g.splits;
+  const auto rpart = rsrc(g.part, static_cast<uint64_t>(S) * M * NOUT * 4);
+  const auto rlo = rsrc(g.lo, static_cast<uint64_t>(NOUT) * rp * 2);
+  auto load_batch = [&](int sp0, float (&v)[SR_ROWS][8]) {
+#pragma unroll
+    for (int i = 0; i < SR_ROWS; ++i)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) {
+        const bool ok = sp0 + k < S && m0 + i < M;
+        const uint32_t row = (static_cast<uint32_t>(sp0 + k) * M + m0 + i) * NOUT;
+        v[i][k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                                                rpart, static_cast<int>(ok ? (row + jc) * 4 : OOB), 0, 0));
+      }
+  };
+  float v[SR_ROWS][8];
+  load_batch(0, v);
+  u32x4 vo[16];
+#pragma unroll
+  for (int c = 0; c < 16; ++c) vo[c] = bload128(rlo, 8 * c < rp ? (jc * rp + 8 * c) * 2 : OOB);
+  for (int e = threadIdx.x; e < SR_ROWS * rp / 8; e += 256) {
+    const int r = e / (rp / 8), c = e % (rp / 8);
+    const auto rlm = rsrc(g.lm, static_cast<uint64_t>(M) * rp * 2);
+    const u32x4 w = bload128(rlm, m0 + r < M ? ((m0 + r) * rp + 8 * c) * 2 : OOB);
+    *reinterpret_cast<u32x4*>(slm + r * rp + 8 * c) = w;
+  }
+  __syncthreads();
+  float acc[SR_ROWS];
+#pragma unroll
+  for (int i = 0; i < SR_ROWS; ++i) {
+    acc[i] = 0.f;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) acc[i] += v[i][k];
+  }
+  for (int sp0 = 8; sp0 < S; sp0 += 8) {
+    load_batch(sp0, v);
+#pragma unroll
+    for (int i = 0; i < SR_ROWS; ++i)
+#pragma unroll
+      for (int k = 0; k < 8; ++k) acc[i] += v[i][k];
+  }
+  for (int c = 0; 8 * c < rp; ++c) {
+    u32x4 vc = vo[0];
+#pragma unroll
+    for (int q = 1; q < 16; ++q) vc = c == q ? vo[q] : vc;
+#pragma unroll
+    for (int i = 0; i < SR_ROWS; ++i) {
+      const u32x4 uw = *reinterpret_cast<const u32x4*>(slm + i * rp + 8 * c);
+      float s = acc[i];
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        s = __builtin_fmaf(bf16lo_to_f32(uw[w]), bf16lo_to_f32(vc[w]), s);
+        s = __builtin_fmaf(bf16hi_to_f32(uw[w]), bf16hi_to_f32(vc[w]), s);
+      }
+      acc[i] = s;
+    }
+  }
+  if (j >= NOUT) return;
+#pragma unroll
+  for (int i = 0; i < SR_ROWS; ++i)
+    if (m0 + i < M) g.out[static_cast<uint64_t>(m0 + i) * NOUT + j] = f32_to_bf16_rne(acc[i]);
+}
+}  // namespace
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const uint32_t n = static_cast<uint32_t>(((g.NOUT + BN - 1) / BN) * ((g.M + BM - 1) / BM));
   const bool bf = g.a16 != nullptr;
+  if (g.splits > 1) {
+    // split reduction: the units without rank steps, then the sums
+    if (bf || (g.RED & 127) != 0 || !g.part || g.split_pairs < 1 || (g.NOUT & 3) != 0)
+      return hipErrorInvalidValue;
+    if (g.nlr != 0 && g.nlr != 2 && g.nlr != 4) return hipErrorInvalidValue;
+    const int cus = cu_count();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    const uint32_t units = n * static_cast<uint32_t>(g.splits);
+    const uint32_t grid = units < static_cast<uint32_t>(cus) ? units : static_cast<uint32_t>(cus);
+    if (g.b_row_scales) hipLaunchKernelGGL((k_gemm_pipe<0, 1>), dim3(grid), dim3(256), 0, st, g);
+    else if (g.b_transposed) hipLaunchKernelGGL((k_gemm_pipe<0, 3>), dim3(grid), dim3(256), 0, st, g);
+    else hipLaunchKernelGGL((k_gemm_pipe<0, 0>), dim3(grid), dim3(256), 0, st, g);
+    if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
+    const dim3 rgrid(static_cast<uint32_t>((g.NOUT + 255) / 256), static_cast<uint32_t>((g.M + SR_ROWS - 1) / SR_ROWS));
+    hipLaunchKernelGGL(k_split_reduce, rgrid, dim3(256), 0, st, g);
+    return hipGetLastError();
+  }
   if ((g.RED & 127) == 0 || (bf && (g.RED & 31) == 0)) {
     const int cus = cu_count();
     if (cus <= 0) return hipErrorInvalidDevice;

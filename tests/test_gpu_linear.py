@@ -55,6 +55,15 @@ def test_tiny_case_full():
     (96, 256, 320, 5, 70),       # r_l > 64, ranks not multiples of 8
     (64, 256, 256, 0, 128),      # adapter only, 128 ranks
     (4200, 1120, 800, 32, 64),   # several column splits with a ragged last one
+    # few rows: both GEMMs split their reduction over units that write fp32
+    # sums, added (with the rank part) by a second kernel
+    (2, 3072, 18432, 32, 16),    # the modulation linear of a DiT block
+    (16, 1024, 768, 32, 16),     # 3 output tiles each way
+    (64, 2048, 4096, 16, 8),     # the largest row count that splits
+    (5, 512, 288, 8, 8),         # ragged columns, 2 step pairs
+    (16, 1152, 768, 0, 0),       # no ranks; odd step count: the last split pads
+    (1024, 3072, 768, 32, 16),   # many rows, few tiles: the forward splits
+    (600, 4096, 1024, 16, 8),    # ragged rows past a 256-row tile
 ])
 def test_ragged_shapes_full(shape):
     M, K, N, rs, rl = shape
