@@ -167,18 +167,22 @@ __global__ __launch_bounds__(256) void k_lora_reduce(const LoraGradArgs pa, cons
   if (idx >= static_cast<uint64_t>(a.rl) * I4) return;
   const int64_t r = static_cast<int64_t>(idx / I4);
   const int64_t i = 4 * static_cast<int64_t>(idx % I4);
-  const float* p = a.part + r * I + i;
   const uint64_t stride = static_cast<uint64_t>(RP) * I;
   const uint32_t nmc = static_cast<uint32_t>(a.nchunk);
+  // 16 chunks' loads at once, as buffer loads (past the last chunk: zero),
+  // so that a batch costs one memory latency; added in chunk order
+  const auto rpart = make_rsrc(a.part, stride * nmc * 4);
+  const uint32_t base = static_cast<uint32_t>((r * I + i) * 4);
   f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  for (uint32_t y0 = 0; y0 < nmc; y0 += 8) {
-    f32x4 v[8];
+  for (uint32_t y0 = 0; y0 < nmc; y0 += 16) {
+    f32x4 v[16];
 #pragma unroll
-    for (int k = 0; k < 8; ++k)
-      v[k] = (y0 + k < nmc) ? *reinterpret_cast<const f32x4*>(p + (y0 + k) * stride)
-                            : f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t off = y0 + k < nmc ? base + static_cast<uint32_t>((y0 + k) * stride * 4) : BUF_OOB;
+      v[k] = __builtin_bit_cast(f32x4, buf_load128(rpart, off));
+    }
 #pragma unroll
-    for (int k = 0; k < 8; ++k) s += v[k];
+    for (int k = 0; k < 16; ++k) s += v[k];
   }
   const int64_t o = r * I + i;
   if (a.out_f32) {

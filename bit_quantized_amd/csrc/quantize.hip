@@ -734,18 +734,23 @@ __device__ __forceinline__ void rank_sum_slab(const RRArgs& a, uint32_t b) {
   const uint32_t bx = b >> 2, wave = b & 3;
   const uint64_t slab = static_cast<uint64_t>(NRG) * 256;                 // floats per wave slab
   const uint64_t stride = static_cast<uint64_t>(nrb) * 4 * slab;          // between splits
-  // (more than 4 rank groups: a thread owns items t and t + 256)
+  // (more than 4 rank groups: a thread owns items t and t + 256).  The
+  // loads of 16 splits go out together as buffer loads, the ones past the
+  // last split answered with zero: no branch between them, so a batch
+  // costs one memory latency (the sum still runs in split order).
+  const auto rpart = make_rsrc(a.part, stride * a.splits * 4);
   for (int it = t; it < 64 * NRG; it += 256) {
-    const float* p = a.part + (static_cast<uint64_t>(bx) * 4 + wave) * slab + it * 4;
+    const uint32_t base = static_cast<uint32_t>(((static_cast<uint64_t>(bx) * 4 + wave) * slab + it * 4) * 4);
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
-    for (uint32_t y0 = 0; y0 < a.splits; y0 += 8) {
-      f32x4 v[8];
+    for (uint32_t y0 = 0; y0 < a.splits; y0 += 16) {
+      f32x4 v[16];
 #pragma unroll
-      for (int k = 0; k < 8; ++k)
-        v[k] = (y0 + k < a.splits) ? *reinterpret_cast<const f32x4*>(p + (y0 + k) * stride)
-                                   : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int k = 0; k < 16; ++k) {
+        const uint32_t off = y0 + k < a.splits ? base + static_cast<uint32_t>((y0 + k) * stride * 4) : BUF_OOB;
+        v[k] = __builtin_bit_cast(f32x4, buf_load128(rpart, off));
+      }
 #pragma unroll
-      for (int k = 0; k < 8; ++k) s += v[k];
+      for (int k = 0; k < 16; ++k) s += v[k];
     }
     const int c = it >> 6, lane = it & 63;
 #pragma unroll
