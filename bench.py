@@ -642,12 +642,21 @@ def main():
         for name, Mb, Kb, Nb in synth.dit_block_linears():
             act_in = ops.FT_ACT_GELU_TANH if name.endswith("fc2") else ops.FT_ACT_NONE
             act_out = ops.FT_ACT_GELU_TANH if name.endswith("fc1") else ops.FT_ACT_NONE
-            lay = QuantizedLinear.from_factors(rnd(Nb, Kb, sc=0.02), rnd(Kb, rs_, sc=0.1),
-                                               rnd(rs_, Nb, sc=0.1), rnd(Kb, rl_, sc=0.01),
-                                               rnd(rl_, Nb, sc=0.01), act_in=act_in, act_out=act_out)
+            Wb, L1b, L2b, Ab, Bb = (rnd(Nb, Kb, sc=0.02), rnd(Kb, rs_, sc=0.1), rnd(rs_, Nb, sc=0.1),
+                                    rnd(Kb, rl_, sc=0.01), rnd(rl_, Nb, sc=0.01))
+            lay = QuantizedLinear.from_factors(Wb, L1b, L2b, Ab, Bb, act_in=act_in, act_out=act_out)
+            # the same layer without ranks, for the unfused variant below
+            plain = QuantizedLinear.from_factors(Wb, None, None, None, None, act_in=act_in,
+                                                 act_out=act_out)
+            Db = torch.cat([L1b, Ab], 1).contiguous()
+            Vb = torch.cat([L2b, Bb], 0).contiguous()
+            del Wb
             blk.append(dict(name=name, M=Mb, lay=lay, X=rnd(Mb, Kb), dY=rnd(Mb, Nb, sc=1e-3),
                             Y=bt(Mb, Nb), U=bt(Mb, rs_ + rl_), dX=bt(Mb, Kb), dA=bt(rl_, Kb),
-                            dB=bt(rl_, Nb), wf=lay.workspace(Mb, False), wb=lay.workspace(Mb, True)))
+                            dB=bt(rl_, Nb), wf=lay.workspace(Mb, False), wb=lay.workspace(Mb, True),
+                            plain=plain, D=Db, V=Vb, Dt=Db.t().contiguous(), Vt=Vb.t().contiguous(),
+                            pf=plain.workspace(Mb, False), pb=plain.workspace(Mb, True),
+                            act_in=act_in != ops.FT_ACT_NONE, act_out=act_out != ops.FT_ACT_NONE))
             bflop += sum(v["flop"] for v in layer_work(Mb, Kb, Nb, rs_, rl_).values())
         by = {e["name"]: e for e in blk}
         for st_ in ("img", "txt"):          # fc2 reads fc1's output h; fc1's gradient is fc2's dX
@@ -701,6 +710,52 @@ def main():
                 torch.cuda.synchronize()
                 ent[kind + "_us"] = round(e0.elapsed_time(e1) / nst * 1e3, 1)
             per_lin[e["name"]] = ent
+        # The block with the low-rank branches unfused (the pages' fusion
+        # breakdown, section 4, Fig. 9, at block level): per linear the
+        # library's 4-bit path without ranks (quantize + GEMM; GELU still
+        # inside its quantizers) and every low-rank product, GELU of the
+        # branch input and branch sum as separate torch operations.
+        def unfused_block():
+            for e in blk:
+                d = e["plain"].desc(e["M"])
+                ops.fourtune_linear_fwd(d, e["X"], e["Y"], None, None, None, e["pf"], e["pf"].numel(),
+                                        stream)
+                xa = torch.nn.functional.gelu(e["X"], approximate="tanh") if e["act_in"] else e["X"]
+                torch.matmul(xa, e["D"], out=e["U"])
+                e["Y"].add_(torch.matmul(e["U"], e["V"]))
+            for e in reversed(blk):
+                d = e["plain"].desc(e["M"])
+                H = by[e["name"][:4] + "fc1"]["Y"] if e["name"].endswith("fc1") else None
+                ops.fourtune_linear_bwd(d, e["dY"], e["X"], None, H, e["dX"], None, None, ops.FT_BF16,
+                                        None, None, None, e["pb"], e["pb"].numel(), stream)
+                gr = (torch.ops.aten.gelu_backward(e["dY"], H, approximate="tanh") if e["act_out"]
+                      else e["dY"])
+                xa = torch.nn.functional.gelu(e["X"], approximate="tanh") if e["act_in"] else e["X"]
+                P = torch.matmul(gr, e["Vt"])
+                e["dX"].add_(torch.matmul(P, e["Dt"]))
+                e["dA"].copy_(torch.matmul(xa.t(), P[:, rs_:].contiguous()).t())
+                torch.matmul(e["U"][:, rs_:].t(), gr, out=e["dB"])
+
+        for _ in range(2):
+            unfused_block()
+        torch.cuda.synchronize()
+        e0.record(stream)
+        for _ in range(nst):
+            unfused_block()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ums = e0.elapsed_time(e1) / nst
+        out["fusion_breakdown_block"] = {
+            "workload": "the DiT block above (every linear, fwd+bwd)",
+            "unfused_us": round(ums * 1e3, 1),
+            "lora_fused_us": round(bms * 1e3, 1),
+            "all_fused_us": None,
+            "all_fused": "not built: fusing the MLP's GELU and the second linear's quantize and "
+                         "down-projection into the first linear's GEMM epilogue writes fp32 "
+                         "down-projection partials that cost as many bytes as the read of h it "
+                         "saves (see the design notes)",
+            "lora_fusion_speedup": round(ums / bms, 3)}
+        log("bench: block fusion", json.dumps(out["fusion_breakdown_block"]))
         out["dit_block"] = {
             "workload": "all linears of one double-stream DiT block at batch 2, fwd+bwd: per stream "
                         "(image 8192 tokens, text 1024) QKV 3072->9216, out-projection 3072->3072, "
