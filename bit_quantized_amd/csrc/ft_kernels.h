@@ -117,8 +117,16 @@ struct SplitPlan {
   int splits, pairs;
 };
 SplitPlan gemm_split_plan(int64_t M, int64_t RED, int64_t NOUT);
+// Outputs of at most 16 rows with a 4-bit product over a multiple of 128
+// and b stored row-wise (not the transposed read): one streaming kernel
+// (k_gemm_rows), no split; launch_gemm takes that path by itself.
+inline bool gemm_rows_ok(int64_t M, int64_t RED, bool bf, bool b_transposed) {
+  return M >= 1 && M <= 16 && RED > 0 && (RED & 127) == 0 && !bf && !b_transposed;
+}
 inline size_t gemm_split_bytes(int64_t M, int64_t RED, int64_t NOUT) {
   const SplitPlan p = gemm_split_plan(M, RED, NOUT);
+  // (with few rows the streaming kernel may run instead; the bytes stay
+  // reserved either way)
   return p.splits > 1 ? static_cast<size_t>(p.splits) * M * NOUT * sizeof(float) : 0;
 }
 

@@ -1002,6 +1002,100 @@ __global__ __launch_bounds__(256, 1) void k_gemm(const GemmArgs g) {
 // about 3 more.  S is the cheapest count under that model that keeps every
 // unit in one round of 256; shapes alone decide it, so the workspace size
 // does not depend on the device.
+namespace {
+// ---------------------------------------------------------------------------
+// k_gemm_rows: outputs of at most 16 rows (a modulation linear at M = 2),
+// streaming b.  Waves 2 q and 2 q + 1 own 16 output columns (b rows), each
+// one half of the reduction, as scaled 16x16x128 fp4 MFMAs: lane (r, g) (r =
+// lane % 16, g = lane / 16) supplies 32 reduction values (16 bytes) of a
+// row r and of b row r for chunk c, block 4 c + g, with its block's scale
+// byte.  a's rows are the same for every wave (L2-resident); b's 32 rows of
+// a workgroup are read once from HBM.  Chunks go in batches of 6, the next
+// batch's loads issued before the current batch's MFMAs, so each wave keeps
+// 12 KB in flight and a CU (two or three workgroups) over 100 KB.  The
+// second half's sums join the first's through LDS (in that order); the rank
+// part is two or four 16x16x32 bf16 MFMAs into the same accumulators (same
+// layout), and the output is rounded once.  BROW: b has 1x32 row scales,
+// else one scale per 32x32 tile.
+constexpr int RB_NB = 6;
+template <bool BROW>
+__global__ __launch_bounds__(256) void k_gemm_rows(const GemmArgs g) {
+  __shared__ f32x4 part[2][64];
+  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
+  const int r = lane & 15, kg = lane >> 4, q = wave >> 1, kh = wave & 1;
+  const uint32_t M = static_cast<uint32_t>(g.M), RED = static_cast<uint32_t>(g.RED);
+  const uint32_t NOUT = static_cast<uint32_t>(g.NOUT);
+  const uint32_t nch = RED / BK, rowb = RED / 2, rsc = RED / 32;
+  const uint32_t nh = (nch + 1) / 2, cbeg = kh * nh, cend = kh ? nch : nh;
+  const uint32_t n = blockIdx.x * 32 + q * 16 + r;
+  const bool aok = static_cast<uint32_t>(r) < M, bok = n < NOUT;
+  const auto ra = rsrc(g.a_codes, static_cast<uint64_t>(M) * rowb);
+  const auto ras = rsrc(g.a_scales, static_cast<uint64_t>(M) * rsc);
+  const auto rb = rsrc(g.b_codes, static_cast<uint64_t>(NOUT) * rowb);
+  const auto rbs = rsrc(g.b_scales, static_cast<uint64_t>(BROW ? NOUT : (NOUT + 31) / 32) * rsc);
+  const uint32_t a_row = aok ? static_cast<uint32_t>(r) * rowb : OOB;
+  const uint32_t b_row = bok ? n * rowb : OOB;
+  const uint32_t a_srow = aok ? static_cast<uint32_t>(r) * rsc : OOB;
+  const uint32_t b_srow = bok ? (BROW ? n : n / 32) * rsc : OOB;
+  struct Batch {
+    u32x4 a[RB_NB], b[RB_NB];
+    uint32_t as[RB_NB], bs[RB_NB];
+  };
+  // chunk c: codes at 64 c + 16 g of the row, scale bytes 4 c .. 4 c + 3 of
+  // the row's scale run as one word (the lane's byte is g)
+  auto load = [&](uint32_t c0, Batch& B) {
+#pragma unroll
+    for (int c = 0; c < RB_NB; ++c) {
+      const bool in = c0 + c < cend;
+      const uint32_t co = (c0 + c) * 64 + 16 * kg, so = 4 * (c0 + c);
+      B.a[c] = bload128(ra, in && a_row != OOB ? a_row + co : OOB);
+      B.b[c] = bload128(rb, in && b_row != OOB ? b_row + co : OOB);
+      B.as[c] = __builtin_amdgcn_raw_buffer_load_b32(ras, static_cast<int>(in && a_srow != OOB ? a_srow + so : OOB), 0, 0);
+      B.bs[c] = __builtin_amdgcn_raw_buffer_load_b32(rbs, static_cast<int>(in && b_srow != OOB ? b_srow + so : OOB), 0, 0);
+    }
+  };
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const Batch& B) {
+#pragma unroll
+    for (int c = 0; c < RB_NB; ++c) {
+      const uint32_t sa = (B.as[c] >> (8 * kg)) & 0xFFu, sb = (B.bs[c] >> (8 * kg)) & 0xFFu;
+      const i32x8 av = {(int)B.a[c][0], (int)B.a[c][1], (int)B.a[c][2], (int)B.a[c][3], 0, 0, 0, 0};
+      const i32x8 bv = {(int)B.b[c][0], (int)B.b[c][1], (int)B.b[c][2], (int)B.b[c][3], 0, 0, 0, 0};
+      acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(av, bv, acc, 4, 4, 0, (int)sa, 0, (int)sb);
+    }
+  };
+  Batch E, O;
+  load(cbeg, E);
+  for (uint32_t c0 = cbeg; c0 < cend; c0 += 2 * RB_NB) {
+    load(c0 + RB_NB, O);
+    compute(E);
+    if (c0 + 2 * RB_NB < cend) load(c0 + 2 * RB_NB, E);
+    compute(O);
+  }
+  if (kh) part[q][lane] = acc;
+  __syncthreads();
+  if (kh) return;
+  acc += part[q][lane];
+  // rank part: 32 ranks per MFMA, lane (r, g) ranks 8 g .. 8 g + 7
+  const int rp = 32 * g.nlr;
+  if (rp > 0) {
+    const auto rlm = rsrc(g.lm, static_cast<uint64_t>(M) * rp * 2);
+    const auto rlo = rsrc(g.lo, static_cast<uint64_t>(NOUT) * rp * 2);
+    for (int k = 0; k < rp; k += 32) {
+      const u32x4 ua = bload128(rlm, aok ? (static_cast<uint32_t>(r) * rp + k + 8 * kg) * 2 : OOB);
+      const u32x4 vb = bload128(rlo, bok ? (n * rp + k + 8 * kg) * 2 : OOB);
+      acc = mfma_bf16_16x16x32(ua, vb, acc);
+    }
+  }
+  // lane (r, g) holds column n, rows 4 g .. 4 g + 3
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t row = 4 * kg + i;
+    if (row < M && bok) g.out[static_cast<uint64_t>(row) * NOUT + n] = f32_to_bf16_rne(acc[i]);
+  }
+}
+}  // namespace
+
 SplitPlan gemm_split_plan(int64_t M, int64_t RED, int64_t NOUT) {
   SplitPlan p{1, 0};
   if (M <= 0 || RED <= 0 || (RED & 127) != 0 || (NOUT & 3) != 0) return p;
@@ -1027,11 +1121,12 @@ SplitPlan gemm_split_plan(int64_t M, int64_t RED, int64_t NOUT) {
 
 namespace {
 // out[m][j] = bf16(sum over splits s (in order) of part[s][m][j] + sum over
-// ranks r of lm[m][r] lo[j][r]).  Workgroup: 8 rows x 256 columns; thread
-// t owns column j0 + t.  Its first 8 splits' sums and its rank row of lo
+// ranks r of lm[m][r] lo[j][r]).  Workgroup: 4 rows x 256 columns; thread
+// t owns column j0 + t.  Its first 16 splits' sums and its rank row of lo
 // are loaded before the rows of lm are staged in LDS, so that one memory
-// latency covers all three; later splits follow 8 at a time.
-constexpr int SR_ROWS = 8;
+// latency covers all three; later splits follow 16 at a time.
+constexpr int SR_ROWS = 4;          // rows per workgroup
+constexpr int SR_NS = 16;           // splits per batch of loads
 __global__ __launch_bounds__(256) void k_split_reduce(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint16_t slm[SR_ROWS * 128];
   // 32-bit indices (the sums are below 2^31 bytes); the row and split
@@ -1045,18 +1140,18 @@ __global__ __launch_bounds__(256) void k_split_reduce(const GemmArgs g) {
   const int rp = 32 * g.nlr, S = g.splits;
   const auto rpart = rsrc(g.part, static_cast<uint64_t>(S) * M * NOUT * 4);
   const auto rlo = rsrc(g.lo, static_cast<uint64_t>(NOUT) * rp * 2);
-  auto load_batch = [&](int sp0, float (&v)[SR_ROWS][8]) {
+  auto load_batch = [&](int sp0, float (&v)[SR_ROWS][SR_NS]) {
 #pragma unroll
     for (int i = 0; i < SR_ROWS; ++i)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) {
+      for (int k = 0; k < SR_NS; ++k) {
         const bool ok = sp0 + k < S && m0 + i < M;
         const uint32_t row = (static_cast<uint32_t>(sp0 + k) * M + m0 + i) * NOUT;
         v[i][k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                 rpart, static_cast<int>(ok ? (row + jc) * 4 : OOB), 0, 0));
       }
   };
-  float v[SR_ROWS][8];
+  float v[SR_ROWS][SR_NS];
   load_batch(0, v);
   u32x4 vo[16];
 #pragma unroll
@@ -1073,14 +1168,14 @@ __global__ __launch_bounds__(256) void k_split_reduce(const GemmArgs g) {
   for (int i = 0; i < SR_ROWS; ++i) {
     acc[i] = 0.f;
 #pragma unroll
-    for (int k = 0; k < 8; ++k) acc[i] += v[i][k];
+    for (int k = 0; k < SR_NS; ++k) acc[i] += v[i][k];
   }
-  for (int sp0 = 8; sp0 < S; sp0 += 8) {
+  for (int sp0 = SR_NS; sp0 < S; sp0 += SR_NS) {
     load_batch(sp0, v);
 #pragma unroll
     for (int i = 0; i < SR_ROWS; ++i)
 #pragma unroll
-      for (int k = 0; k < 8; ++k) acc[i] += v[i][k];
+      for (int k = 0; k < SR_NS; ++k) acc[i] += v[i][k];
   }
   for (int c = 0; 8 * c < rp; ++c) {
     u32x4 vc = vo[0];
@@ -1108,6 +1203,14 @@ __global__ __launch_bounds__(256) void k_split_reduce(const GemmArgs g) {
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const uint32_t n = static_cast<uint32_t>(((g.NOUT + BN - 1) / BN) * ((g.M + BM - 1) / BM));
   const bool bf = g.a16 != nullptr;
+  if (gemm_rows_ok(g.M, g.RED, bf, g.b_transposed != 0)) {
+    // at most 16 rows: stream b, 32 output columns per workgroup
+    if (g.nlr != 0 && g.nlr != 2 && g.nlr != 4) return hipErrorInvalidValue;
+    const dim3 grid(static_cast<uint32_t>((g.NOUT + 31) / 32));
+    if (g.b_row_scales) hipLaunchKernelGGL(k_gemm_rows<true>, grid, dim3(256), 0, st, g);
+    else hipLaunchKernelGGL(k_gemm_rows<false>, grid, dim3(256), 0, st, g);
+    return hipGetLastError();
+  }
   if (g.splits > 1) {
     // split reduction: the units without rank steps, then the sums
     if (bf || (g.RED & 127) != 0 || !g.part || g.split_pairs < 1 || (g.NOUT & 3) != 0)

@@ -98,6 +98,8 @@ def test_precision_w4a16g16_qkv_full_size_sampled():
     (300, 288, 544, 16, 8),      # ragged; K % 128 != 0: the register-staged kernel both ways
     (520, 1024, 768, 32, 16),    # the pipelined kernel both ways
     (200, 640, 384, 0, 0),       # odd step counts (padded step), no ranks
+    (2, 3072, 1024, 32, 16),     # two rows: the streaming kernel both ways (per-row b scales)
+    (13, 1152, 640, 16, 8),      # 13 rows, 9 steps (a partial batch)
 ])
 def test_row32_weights_full(shape):
     """Group-wise (1x32) weights, the block-shape ablation's alternative: the
@@ -113,6 +115,7 @@ def test_row32_weights_full(shape):
     (300, 288, 544, 16, 8),      # register-staged dgrad
     (520, 1024, 768, 32, 16),    # pipelined dgrad
     (96, 160, 256, 0, 0),        # pipelined, no ranks
+    (2, 3072, 1024, 32, 16),     # two rows: the streaming kernel reads the copy
 ])
 def test_tile32_transposed_copy_full(shape):
     """The measured alternative to the method's single weight: the tiles
