@@ -73,6 +73,9 @@ def parse():
                          "kernel that scales rocprofv3's FETCH_SIZE / WRITE_SIZE to bytes)")
     ap.add_argument("--summarize-trace", metavar="DIR",
                     help="print a markdown summary of a rocprofv3 --kernel-trace --stats run and exit")
+    ap.add_argument("--summarize-counters", metavar="DIR",
+                    help="print per-launch means of the counters of a rocprofv3 --pmc run of "
+                         "this script (JSON), with derived matrix-core busy and wait fractions")
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print per-launch HBM traffic (JSON) from two rocprofv3 --pmc runs of "
                          "this script with --copy-probe (FETCH_SIZE, then WRITE_SIZE) and exit")
@@ -262,6 +265,27 @@ def _pmc_per_step_kernel(d, counter):
     return per, (sum(copy) / len(copy) if copy else None)
 
 
+def summarize_counters(d):
+    """Per step kernel, the mean of every counter of a `rocprofv3 --pmc` run
+    per launch, with two derived fractions: matrix-core busy =
+    SQ_VALU_MFMA_BUSY_CYCLES over the SIMD cycles of the launch (GRBM_GUI_ACTIVE,
+    which counts each of the 8 XCDs, over 8, times 256 CUs x 4 SIMDs), and
+    waiting = SQ_WAIT_ANY over SQ_WAVE_CYCLES."""
+    rows = sorted(_csv_rows(d, "counter_collection.csv"), key=lambda r: int(r["Dispatch_Id"]))
+    names = sorted({r["Counter_Name"] for r in rows})
+    per = {}
+    for c in names:
+        vals, _ = _pmc_per_step_kernel(d, c)
+        for k, v in vals.items():
+            per.setdefault(k, {})[c] = v
+    for k, cs in per.items():
+        if "SQ_VALU_MFMA_BUSY_CYCLES" in cs and cs.get("GRBM_GUI_ACTIVE"):
+            cs["mfma_busy_frac"] = cs["SQ_VALU_MFMA_BUSY_CYCLES"] / (cs["GRBM_GUI_ACTIVE"] / 8 * 1024)
+        if "SQ_WAIT_ANY" in cs and cs.get("SQ_WAVE_CYCLES"):
+            cs["wait_frac"] = cs["SQ_WAIT_ANY"] / cs["SQ_WAVE_CYCLES"]
+    return {k: {c: round(v, 4) for c, v in cs.items()} for k, cs in per.items()}
+
+
 def summarize_pmc(fetch_dir, write_dir):
     """HBM bytes per launch: FETCH_SIZE and WRITE_SIZE (KiB per dispatch) of each
     kernel, each divided by the same counter's reading per byte of a plain
@@ -337,6 +361,9 @@ def main():
         return
     if a.summarize_pmc:
         print(json.dumps(summarize_pmc(*a.summarize_pmc), indent=1))
+        return
+    if a.summarize_counters:
+        print(json.dumps(summarize_counters(a.summarize_counters), indent=1))
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if a.gpus != 1 or world != 1:
