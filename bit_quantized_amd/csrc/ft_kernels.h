@@ -43,14 +43,14 @@ inline int rank_pad(int R) { return R > 64 ? 128 : R > 0 ? 64 : 0; }
 // column range into `part`, then their ordered sum).  Also writes out_pad
 // [rows, rank_pad(R)], the same values zero-padded, and the transposed copy
 // cp_dst [cp_rows, rank_pad(R)] of the rank-major operand cp (cp_planes: cp
-// as the nibble planes [256, cp_rows / 2] bytes of the GEMM's transposing
-// b read, same size; quantize.hip, copy_rank_planes).  `part` needs
-// quant_down_part_bytes(rows, cols, R, db ? db->rl : 0) bytes.
+// as the nibble planes [4 rank_pad(R), cp_rows / 2] bytes of the GEMM's
+// transposing b read, same size; quantize.hip, copy_rank_planes).  `part`
+// needs quant_down_part_bytes(rows, cols, R, db ? db->rl : 0) bytes.
 // db (backward, optional): also the adapter-gradient partials
 //   db->part[j][r][c] = sum over the rows workgroup j of a split visits of
-//                       u[row][r0 + r] * act(in)[row][c],   r < rl <= 32,
-// j < quant_down_db_chunks(rows, cols, rl); the rows >= rl of a 16-rank
-// group are zero.  quant_down_db_bytes(rows, cols, rl) bytes.
+//                       u[row][r0 + r] * act(in)[row][c],   r < rl <= 64,
+// j < quant_down_db_chunks(rows, cols, R, rl); the rows >= rl of a 16-rank
+// group are zero.  quant_down_db_bytes(rows, cols, R, rl) bytes.
 struct DbFuse {
   const uint16_t* u;              // bf16 [rows, ld_u]
   int64_t ld_u;

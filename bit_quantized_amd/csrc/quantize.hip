@@ -1097,7 +1097,12 @@ size_t quant_down_db_bytes(int64_t rows, int64_t cols, int R, int rl) {
 template <int NRG, int NS>
 static void launch_qd(const QDArgs& a, dim3 grid, int act, int dbr, hipStream_t st) {
 #define FT_QDA(ACT, D) hipLaunchKernelGGL((k_quant_down<NRG, NS, ACT, D>), grid, dim3(256), 0, st, a)
-#define FT_QDB(D)                                                                               do {                                                                                            if constexpr (D <= NRG) {                                                                       if (act == 2) FT_QDA(2, D); else FT_QDA(0, D);                                              }                                                                                           } while (0)
+#define FT_QDB(D)                                        \
+  do {                                                   \
+    if constexpr (D <= NRG) {                            \
+      if (act == 2) FT_QDA(2, D); else FT_QDA(0, D);     \
+    }                                                    \
+  } while (0)
   if (act == 1) {
     FT_QDA(1, 0);
   } else {
