@@ -31,6 +31,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -532,16 +533,25 @@ def main():
                         dX2=bt(Mm, Fm), dA2=bt(rlm, Fm), dB2=bt(rlm, Km), dX1=bt(Mm, Km),
                         dA1=bt(rlm, Km), dB1=bt(rlm, Fm))
             ws = {k: (lay.workspace(Mm, False), lay.workspace(Mm, True)) for k, lay in (("1", fc1), ("2", fc2))}
+            nmlp = ops.fourtune_mlp_workspace_bytes(fc1.desc(Mm), fc2.desc(Mm))
+            ws["mlp"] = torch.empty(nmlp, dtype=torch.uint8, device=dev)
             msets.append((fc1, fc2, X1, dY2, bufs, ws))
         del c1, c2
         torch.cuda.synchronize()
 
-        def mlp_step(i):
+        def mlp_step(i, fused=True):
             fc1, fc2, X1, dY2, b, ws = msets[i % len(msets)]
             d1, d2 = fc1.desc(Mm), fc2.desc(Mm)
             (w1f, w1b), (w2f, w2b) = ws["1"], ws["2"]
-            ops.fourtune_linear_fwd(d1, X1, b["h"], b["U1"], None, None, w1f, w1f.numel(), stream)
-            ops.fourtune_linear_fwd(d2, b["h"], b["Y2"], b["U2"], None, None, w2f, w2f.numel(), stream)
+            if fused:
+                # FC1's GEMM epilogue makes FC2's quantized input and down-projection partials
+                wm = ws["mlp"]
+                ops.fourtune_mlp_fwd(d1, d2, X1, b["h"], b["Y2"], b["U1"], b["U2"], None, None, wm,
+                                     wm.numel(), stream)
+            else:
+                ops.fourtune_linear_fwd(d1, X1, b["h"], b["U1"], None, None, w1f, w1f.numel(), stream)
+                ops.fourtune_linear_fwd(d2, b["h"], b["Y2"], b["U2"], None, None, w2f, w2f.numel(),
+                                        stream)
             ops.fourtune_linear_bwd(d2, dY2, b["h"], b["U2"], None, b["dX2"], b["dA2"], b["dB2"],
                                     ops.FT_BF16, None, None, None, w2b, w2b.numel(), stream)
             ops.fourtune_linear_bwd(d1, b["dX2"], X1, b["U1"], b["h"], b["dX1"], b["dA1"], b["dB1"],
@@ -550,31 +560,47 @@ def main():
         nst = max(5, a.steps // 5)
         for i in range(3):
             mlp_step(i)
+            mlp_step(i, fused=False)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for i in range(nst):
-            mlp_step(i)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        mms = e0.elapsed_time(e1) / nst
+        # fused and unfused forwards in alternating rounds (median per variant),
+        # so that clock drift favours neither
+        t_var = {True: [], False: []}
+        for rnd in range(6):
+            for fz in ((True, False) if rnd % 2 == 0 else (False, True)):
+                e0.record(stream)
+                for i in range(nst):
+                    mlp_step(i, fused=fz)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t_var[fz].append(e0.elapsed_time(e1) / nst)
+        mms_fused = statistics.median(t_var[True])
+        mms = statistics.median(t_var[False])
         w1 = layer_work(Mm, Km, Fm, rsm, rlm)
         w2 = layer_work(Mm, Fm, Km, rsm, rlm)
         mflop = sum(v["flop"] for v in w1.values()) + sum(v["flop"] for v in w2.values())
-        ops.fourtune_timing_reset()
-        ops.fourtune_timing_enable(True)
-        for i in range(nst):
-            mlp_step(i)
-        torch.cuda.synchronize()
-        ops.fourtune_timing_enable(False)
-        per = {k: round(tot / cnt * 1e3, 2) for k, (tot, cnt) in ops.fourtune_timing_read().items() if cnt}
+        per_var = {}
+        for fz in (True, False):
+            ops.fourtune_timing_reset()
+            ops.fourtune_timing_enable(True)
+            for i in range(nst):
+                mlp_step(i, fused=fz)
+            torch.cuda.synchronize()
+            ops.fourtune_timing_enable(False)
+            per_var[fz] = {k: round(tot / cnt * 1e3, 2)
+                           for k, (tot, cnt) in ops.fourtune_timing_read().items() if cnt}
         out["mlp_pair"] = {
             "workload": f"FLUX MLP pair fwd+bwd: {Mm} tokens, {Km}->{Fm} -> tanh-GELU -> {Fm}->{Km}, "
                         f"r_stab={rsm}, r_lora={rlm}; GELU applied inside the quantizers and the "
                         f"adapter-gradient kernel",
             "us_per_step": round(mms * 1e3, 1), "TFLOP/s": round(mflop / (mms * 1e-3) / 1e12, 1),
             "step_flop": mflop, "steps": nst,
-            "kernel_avg_us_both_linears": per}
+            # the same step with the forward's MLP fusion (fourtune_mlp_fwd: FC1's
+            # GEMM epilogue makes FC2's quantized input and down-projection sums)
+            "mlp_fused_us_per_step": round(mms_fused * 1e3, 1),
+            "mlp_fusion_speedup": round(mms / mms_fused, 3),
+            "kernel_avg_us_both_linears": per_var[False],
+            "kernel_avg_us_both_linears_mlp_fused": per_var[True]}
         log("bench: mlp", json.dumps(out["mlp_pair"]))
         del msets
         torch.cuda.empty_cache()
@@ -691,8 +717,23 @@ def main():
             by[st_ + "_fc1"]["dY"] = by[st_ + "_fc2"]["dX"]
         torch.cuda.synchronize()
 
-        def block_step():
+        mlp_ws = {}
+        for st_ in ("img", "txt"):
+            f1, f2 = by[st_ + "_fc1"], by[st_ + "_fc2"]
+            n_ = ops.fourtune_mlp_workspace_bytes(f1["lay"].desc(f1["M"]), f2["lay"].desc(f2["M"]))
+            mlp_ws[st_] = torch.empty(n_, dtype=torch.uint8, device=dev)
+
+        def block_step(mlp_fused=False):
             for e in blk:
+                nm = e["name"]
+                if mlp_fused and nm.endswith("fc2"):
+                    continue                      # made together with its fc1 below
+                if mlp_fused and nm.endswith("fc1"):
+                    e2 = by[nm[:4] + "fc2"]
+                    w_ = mlp_ws[nm[:3]]
+                    ops.fourtune_mlp_fwd(e["lay"].desc(e["M"]), e2["lay"].desc(e2["M"]), e["X"], e["Y"],
+                                         e2["Y"], e["U"], e2["U"], None, None, w_, w_.numel(), stream)
+                    continue
                 d = e["lay"].desc(e["M"])
                 ops.fourtune_linear_fwd(d, e["X"], e["Y"], e["U"], None, None, e["wf"], e["wf"].numel(),
                                         stream)
@@ -704,15 +745,21 @@ def main():
 
         for _ in range(2):
             block_step()
+            block_step(mlp_fused=True)
         torch.cuda.synchronize()
         nst = max(3, a.steps // 10)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(nst):
-            block_step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        bms = e0.elapsed_time(e1) / nst
+        t_blk = {False: [], True: []}
+        for rnd in range(4):
+            for fz in ((False, True) if rnd % 2 == 0 else (True, False)):
+                e0.record(stream)
+                for _ in range(nst):
+                    block_step(mlp_fused=fz)
+                e1.record(stream)
+                torch.cuda.synchronize()
+                t_blk[fz].append(e0.elapsed_time(e1) / nst)
+        bms = statistics.median(t_blk[False])
+        bms_all = statistics.median(t_blk[True])
         # each linear on its own: fwd and bwd, event-timed over the same
         # number of repetitions (the modulation linears run the split GEMMs)
         per_lin = {}
@@ -776,12 +823,10 @@ def main():
             "workload": "the DiT block above (every linear, fwd+bwd)",
             "unfused_us": round(ums * 1e3, 1),
             "lora_fused_us": round(bms * 1e3, 1),
-            "all_fused_us": None,
-            "all_fused": "not built: fusing the MLP's GELU and the second linear's quantize and "
-                         "down-projection into the first linear's GEMM epilogue writes fp32 "
-                         "down-projection partials that cost as many bytes as the read of h it "
-                         "saves (see the design notes)",
-            "lora_fusion_speedup": round(ums / bms, 3)}
+            "all_fused_us": round(bms_all * 1e3, 1),
+            "lora_fusion_speedup": round(ums / bms, 3),
+            "mlp_fusion_speedup": round(bms / bms_all, 3),
+            "all_fusion_speedup": round(ums / bms_all, 3)}
         log("bench: block fusion", json.dumps(out["fusion_breakdown_block"]))
         out["dit_block"] = {
             "workload": "all linears of one double-stream DiT block at batch 2, fwd+bwd: per stream "

@@ -243,6 +243,79 @@ ft::RankRows rows_V(const ft_linear* L) {
   return ft::RankRows{L->L2, L->B, L->r_stab, L->r_lora, L->N};
 }
 
+// The second linear's input and down-projection partials that the first
+// linear's GEMM of a fused MLP forward writes (fourtune_mlp_fwd).
+struct MlpEpi {
+  uint8_t* codes;
+  uint8_t* scales;
+  float* part;
+  ft::RankRows pr;
+  int R, nrg;
+};
+
+// The forward's kernels after the checks.  k1 = false: kernel 1's results
+// (the quantized input and the padded rank operands) are already in place;
+// epi: the GEMM also makes the next linear's input (MLP fusion).
+ft_status fwd_run(const ft_linear* L, const uint16_t* X, uint16_t* Y, uint16_t* U_save,
+                  uint8_t* xq_codes, uint8_t* xq_scales, uint8_t* ws, const FwdLayout& lay,
+                  hipStream_t st, bool k1, const MlpEpi* epi) {
+  const int R = L->r_stab + L->r_lora;
+  const bool bf = a16(L);
+  // A16: no codes; the quantize stores of kernel 1 are dropped
+  uint8_t* qc = bf ? nullptr : xq_codes ? xq_codes : ws + lay.xq_codes;
+  uint8_t* qs = bf ? nullptr : xq_scales ? xq_scales : ws + lay.xq_scales;
+  uint16_t* u_pad = reinterpret_cast<uint16_t*>(ws + lay.u_pad);
+  uint16_t* v_pad = reinterpret_cast<uint16_t*>(ws + lay.v_pad);
+  hipError_t e = hipSuccess;
+  // act_in: X is the pre-activation h; the layer's input is gelu(h)
+  const int act = L->act_in == FT_ACT_GELU_TANH ? 1 : 0;
+  if (!k1) {
+    // (the second linear of a fused MLP: made by the first one's GEMM)
+  } else if (R > 0) {
+    Timed tm("fwd_quant_down", st);
+    e = tm.done(ft::launch_quant_down(X, nullptr, act, L->M, L->K, L->K, qc, qs, rows_Dt(L), U_save,
+                                      u_pad, rows_V(L), L->N, v_pad,
+                                      reinterpret_cast<float*>(ws + lay.part), nullptr, st));
+  } else if (!bf) {
+    Timed tm("fwd_quant_down", st);
+    e = tm.done(ft::launch_quant_row32(X, nullptr, act, L->M, L->K, L->K, qc, qs, st));
+  }
+  if (e != hipSuccess) return FT_EDEVICE;
+  ft::GemmArgs g{};
+  g.M = L->M; g.RED = L->K; g.NOUT = L->N;
+  g.a_codes = qc; g.a_scales = qs;
+  g.b_codes = L->w_codes; g.b_scales = L->w_scales;
+  g.b_row_scales = L->w_block == FT_WBLOCK_ROW32;
+  g.lm = u_pad; g.lo = v_pad; g.nlr = ft::rank_pad(R) / 32; g.out = Y;
+  if (!bf) {
+    const ft::SplitPlan sp = ft::gemm_split_plan(L->M, L->K, L->N);
+    g.splits = sp.splits; g.split_pairs = sp.pairs;
+    g.part = reinterpret_cast<float*>(ws + lay.sk_part);
+  }
+  if (bf) {
+    uint16_t* w16 = reinterpret_cast<uint16_t*>(ws + lay.w16);
+    {
+      Timed tm("fwd_dequant_w", st);
+      if (tm.done(ft::launch_dequant_tile32(L->w_codes, L->w_scales, L->N, L->K, w16, st)) != hipSuccess)
+        return FT_EDEVICE;
+    }
+    const uint16_t* x16 = X;
+    if (act) {
+      uint16_t* xa = reinterpret_cast<uint16_t*>(ws + lay.x16);
+      Timed tm("fwd_act", st);
+      if (tm.done(ft::launch_act(1, X, nullptr, L->M * L->K, xa, st)) != hipSuccess) return FT_EDEVICE;
+      x16 = xa;
+    }
+    g.a16 = x16; g.b16 = w16;
+  }
+  if (epi) {
+    g.e_codes = epi->codes; g.e_scales = epi->scales; g.e_part = epi->part;
+    g.e_pr = epi->pr; g.e_R = epi->R; g.e_nrg = epi->nrg;
+  }
+  Timed tm(epi ? "fwd_gemm_mlp" : "fwd_gemm", st);
+  return launched(tm.done(ft::launch_gemm(g, st)));
+}
+
 }  // namespace
 
 extern "C" {
@@ -340,57 +413,66 @@ ft_status fourtune_linear_fwd(const ft_linear* L, const uint16_t* X, uint16_t* Y
   if (ws_bytes < lay.total) return FT_EWORKSPACE;
   if (!workspace) return FT_EINVAL;
   if (ft_status s = device_check(); s != FT_OK) return s;
+  return fwd_run(L, X, Y, U_save, xq_codes, xq_scales, static_cast<uint8_t*>(workspace), lay,
+                 static_cast<hipStream_t>(stream), true, nullptr);
+}
 
+size_t fourtune_mlp_workspace_bytes(const ft_linear* fc1, const ft_linear* fc2) {
+  const size_t a = fourtune_workspace_bytes(fc1, 0), b = fourtune_workspace_bytes(fc2, 0);
+  return a && b ? a + b : 0;
+}
+
+ft_status fourtune_mlp_fwd(const ft_linear* fc1, const ft_linear* fc2, const uint16_t* X,
+                           uint16_t* H, uint16_t* Y, uint16_t* U1_save, uint16_t* U2_save,
+                           uint8_t* aq_codes, uint8_t* aq_scales, void* workspace,
+                           size_t ws_bytes, void* stream) {
+  if (ft_status s = check_linear(fc1); s != FT_OK) return s;
+  if (ft_status s = check_linear(fc2); s != FT_OK) return s;
+  if (fc2->M != fc1->M || fc2->K != fc1->N) return FT_ESHAPE;
+  if (fc2->act_in != FT_ACT_GELU_TANH) return FT_EINVAL;
+  const int R1 = fc1->r_stab + fc1->r_lora, R2 = fc2->r_stab + fc2->r_lora;
+  if (!X || !H || !Y) return FT_EINVAL;
+  if ((R1 > 0 && !U1_save) || (R2 > 0 && !U2_save)) return FT_EINVAL;
+  if ((aq_codes == nullptr) != (aq_scales == nullptr)) return FT_EINVAL;
+  if (a16(fc2) && aq_codes) return FT_EINVAL;
+  const void* ptrs[] = {X, H, Y, U1_save, U2_save, aq_codes, aq_scales, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FT_EALIGN;
+  const FwdLayout l1 = fwd_layout(fc1), l2 = fwd_layout(fc2);
+  if (ws_bytes < l1.total + l2.total) return FT_EWORKSPACE;
+  if (!workspace) return FT_EINVAL;
+  if (ft_status s = device_check(); s != FT_OK) return s;
   hipStream_t st = static_cast<hipStream_t>(stream);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const bool bf = a16(L);
-  // A16: no codes; the quantize stores of kernel 1 are dropped
-  uint8_t* qc = bf ? nullptr : xq_codes ? xq_codes : ws + lay.xq_codes;
-  uint8_t* qs = bf ? nullptr : xq_scales ? xq_scales : ws + lay.xq_scales;
-  uint16_t* u_pad = reinterpret_cast<uint16_t*>(ws + lay.u_pad);
-  uint16_t* v_pad = reinterpret_cast<uint16_t*>(ws + lay.v_pad);
-  hipError_t e = hipSuccess;
-  // act_in: X is the pre-activation h; the layer's input is gelu(h)
-  const int act = L->act_in == FT_ACT_GELU_TANH ? 1 : 0;
-  if (R > 0) {
-    Timed tm("fwd_quant_down", st);
-    e = tm.done(ft::launch_quant_down(X, nullptr, act, L->M, L->K, L->K, qc, qs, rows_Dt(L), U_save,
-                                      u_pad, rows_V(L), L->N, v_pad,
-                                      reinterpret_cast<float*>(ws + lay.part), nullptr, st));
-  } else if (!bf) {
-    Timed tm("fwd_quant_down", st);
-    e = tm.done(ft::launch_quant_row32(X, nullptr, act, L->M, L->K, L->K, qc, qs, st));
+  uint8_t* ws1 = static_cast<uint8_t*>(workspace);
+  uint8_t* ws2 = ws1 + l1.total;
+  const int64_t M = fc1->M, N1 = fc1->N;
+  // the down-projection partials per 256-column split of h, 32-bit offsets
+  const int64_t nsplit = (N1 + 255) / 256;
+  const int nrg = ft::rank_reduce_nrg(R2);
+  const bool fused = !a16(fc1) && !a16(fc2) && fc1->w_block != FT_WBLOCK_ROW32 &&
+                     ft::gemm_mlp_ok(M, fc1->K, N1, R2) &&
+                     nsplit * ((M + 63) / 64) * 4 * nrg * 1024 <= kMaxBytes;
+  if (!fused) {
+    if (ft_status s = fwd_run(fc1, X, H, U1_save, nullptr, nullptr, ws1, l1, st, true, nullptr);
+        s != FT_OK)
+      return s;
+    return fwd_run(fc2, H, Y, U2_save, aq_codes, aq_scales, ws2, l2, st, true, nullptr);
   }
-  if (e != hipSuccess) return FT_EDEVICE;
-  ft::GemmArgs g{};
-  g.M = L->M; g.RED = L->K; g.NOUT = L->N;
-  g.a_codes = qc; g.a_scales = qs;
-  g.b_codes = L->w_codes; g.b_scales = L->w_scales;
-  g.b_row_scales = L->w_block == FT_WBLOCK_ROW32;
-  g.lm = u_pad; g.lo = v_pad; g.nlr = ft::rank_pad(R) / 32; g.out = Y;
-  if (!bf) {
-    const ft::SplitPlan sp = ft::gemm_split_plan(L->M, L->K, L->N);
-    g.splits = sp.splits; g.split_pairs = sp.pairs;
-    g.part = reinterpret_cast<float*>(ws + lay.sk_part);
+  uint8_t* qc2 = aq_codes ? aq_codes : ws2 + l2.xq_codes;
+  uint8_t* qs2 = aq_scales ? aq_scales : ws2 + l2.xq_scales;
+  float* part2 = reinterpret_cast<float*>(ws2 + l2.part);
+  const MlpEpi epi{qc2, qs2, part2, rows_Dt(fc2), R2, nrg};
+  if (ft_status s = fwd_run(fc1, X, H, U1_save, nullptr, nullptr, ws1, l1, st, true, &epi); s != FT_OK)
+    return s;
+  if (R2 > 0) {
+    Timed tm("fwd_rank_reduce", st);
+    if (tm.done(ft::launch_rank_reduce(part2, M, static_cast<int>(nsplit), R2, U2_save,
+                                       reinterpret_cast<uint16_t*>(ws2 + l2.u_pad), rows_V(fc2),
+                                       fc2->N, reinterpret_cast<uint16_t*>(ws2 + l2.v_pad), st)) !=
+        hipSuccess)
+      return FT_EDEVICE;
   }
-  if (bf) {
-    uint16_t* w16 = reinterpret_cast<uint16_t*>(ws + lay.w16);
-    {
-      Timed tm("fwd_dequant_w", st);
-      if (tm.done(ft::launch_dequant_tile32(L->w_codes, L->w_scales, L->N, L->K, w16, st)) != hipSuccess)
-        return FT_EDEVICE;
-    }
-    const uint16_t* x16 = X;
-    if (act) {
-      uint16_t* xa = reinterpret_cast<uint16_t*>(ws + lay.x16);
-      Timed tm("fwd_act", st);
-      if (tm.done(ft::launch_act(1, X, nullptr, L->M * L->K, xa, st)) != hipSuccess) return FT_EDEVICE;
-      x16 = xa;
-    }
-    g.a16 = x16; g.b16 = w16;
-  }
-  Timed tm("fwd_gemm", st);
-  return launched(tm.done(ft::launch_gemm(g, st)));
+  return fwd_run(fc2, H, Y, U2_save, qc2, qs2, ws2, l2, st, false, nullptr);
 }
 
 ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint16_t* X,

@@ -63,6 +63,13 @@ hipError_t launch_quant_down(const uint16_t* in, const uint16_t* in2, int act, i
                              const RankRows& cp, int64_t cp_rows, uint16_t* cp_dst, float* part,
                              const DbFuse* db, hipStream_t st, bool cp_planes = false);
 size_t quant_down_part_bytes(int64_t rows, int64_t cols, int R, int rl_db);
+// The second kernel of launch_quant_down on its own: out_lr, out_pad and
+// cp_dst as there, from partials [splits][ceil(rows/64)][4][nrg][64][4]
+// fp32 (nrg = rank_reduce_nrg(R)) that another kernel wrote.
+int rank_reduce_nrg(int R);
+hipError_t launch_rank_reduce(const float* part, int64_t rows, int splits, int R, uint16_t* out_lr,
+                              uint16_t* out_pad, const RankRows& cp, int64_t cp_rows,
+                              uint16_t* cp_dst, hipStream_t st, bool cp_planes = false);
 int quant_down_db_chunks(int64_t rows, int64_t cols, int R, int rl);   // 0: dB is not fused for this rl
 size_t quant_down_db_bytes(int64_t rows, int64_t cols, int R, int rl);
 
@@ -107,6 +114,22 @@ struct GemmArgs {
   // order, adds lm lo^T and rounds to out.  splits <= 1: one pass.
   int splits, split_pairs;
   float* part;
+  // MLP fusion (e_codes set): the forward of the first linear of an MLP
+  // block, whose output h feeds gelu and the second linear.  Besides out =
+  // h, each tile's epilogue writes, from the same rounded values, the
+  // second linear's quantized input Qrow(gelu(h)) (e_codes [M, NOUT/2],
+  // e_scales [M, NOUT/32]) and the fp32 sums of its down-projection
+  // gelu(h) D2 over the tile's 256 columns (e_part, in the partial layout
+  // of the fused quantizer's 256-column splits, which launch_rank_reduce
+  // adds up: [ceil(NOUT/256)][ceil(M/64)][4][e_nrg][64][4]).  e_pr: D2^T
+  // rank-major, e_R ranks of NOUT values; e_nrg = rank_reduce_nrg(e_R)
+  // (0 when e_R == 0: codes and scales only).  Pipelined kernel, b as
+  // 32x32 tiles, no split (gemm_mlp_ok).
+  uint8_t* e_codes;
+  uint8_t* e_scales;
+  float* e_part;
+  RankRows e_pr;
+  int e_R, e_nrg;
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
 // The split plan of a 4-bit product [M, RED] x [RED, NOUT] (RED % 128 == 0):
@@ -122,6 +145,13 @@ SplitPlan gemm_split_plan(int64_t M, int64_t RED, int64_t NOUT);
 // (k_gemm_rows), no split; launch_gemm takes that path by itself.
 inline bool gemm_rows_ok(int64_t M, int64_t RED, bool bf, bool b_transposed) {
   return M >= 1 && M <= 16 && RED > 0 && (RED & 127) == 0 && !bf && !b_transposed;
+}
+// The MLP-fused forward GEMM applies: a 4-bit product over a multiple of
+// 128 on 32x32-tile weights that runs the pipelined kernel in one pass
+// (more than 16 rows, no split), with D2 of at most 64 ranks.
+inline bool gemm_mlp_ok(int64_t M, int64_t RED, int64_t NOUT, int R2) {
+  return M > 16 && RED > 0 && (RED & 127) == 0 && (NOUT & 31) == 0 && R2 >= 0 && R2 <= 64 &&
+         gemm_split_plan(M, RED, NOUT).splits <= 1;
 }
 inline size_t gemm_split_bytes(int64_t M, int64_t RED, int64_t NOUT) {
   const SplitPlan p = gemm_split_plan(M, RED, NOUT);

@@ -183,7 +183,19 @@ template <bool B> struct Flag { static constexpr bool v = B; };
 // wave; the tile scales of a step are 4 runs of 8 bytes (one per reduction
 // block, strided by NOUT/32), loaded as 3 aligned words each and turned
 // into per-column words (byte j = reduction block j) by byte permutes.
-template <int NLR_, int BMODE>
+// A workgroup barrier for LDS data passed between waves: this wave's LDS
+// accesses complete, then s_barrier; the memory clobber keeps the compiler
+// from moving memory accesses across it.  (No wait on vector memory: the
+// loads and stores in flight stay in flight.)
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+}
+
+// EPI > 0: the MLP-fused epilogue (GemmArgs::e_codes) with EPI - 1 rank
+// groups of 16 in the second linear's down-projection.
+template <int NLR_, int BMODE, int EPI = 0>
 __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   constexpr bool LR = NLR_ > 0;
   constexpr bool BF = BMODE == 2, BROW = BMODE == 1, BT = BMODE == 3;
@@ -204,7 +216,7 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   // g.part; S = 1 otherwise (a unit is a whole tile).
   // (only without rank steps: a split launch leaves the rank part to the
   // kernel that adds the splits)
-  const uint32_t S = (!LR && g.splits > 1) ? static_cast<uint32_t>(g.splits) : 1u;
+  const uint32_t S = (!LR && EPI == 0 && g.splits > 1) ? static_cast<uint32_t>(g.splits) : 1u;
   const uint32_t ntiles = mt_n * nt_n * S, G = gridDim.x, bid = blockIdx.x;
   const uint32_t full = ntiles / G, nlast = ntiles % G;
   const uint32_t my_tiles = full + (bid < nlast ? 1u : 0u);
@@ -538,6 +550,127 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
         for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
   };
 
+  // MLP fusion: the tile's h strips as above, and from each the second
+  // linear's input a = gelu(h), computed by the fused quantizer's own
+  // activation function from the same bf16 values (so the same bits):
+  //   - quantized in 1x32 row blocks where each strip is read back: 4
+  //     consecutive lanes hold one block (quad DPP amax), 4 code bytes per
+  //     lane and one scale byte per block go out as buffer stores;
+  //   - written back over the strip, where all four waves' strips then hold
+  //     the 16 rows x 256 columns of a for the down-projection: wave wn
+  //     takes rank groups wn EGW .. wn EGW + EGW - 1 of D2 over all 256
+  //     columns (16x16x32 bf16 MFMAs; D2's fragments for the tile are
+  //     loaded once, before the first strip) and stores its fp32 sums into
+  //     the quantizer's partial slab of these rows and this column split.
+  // Two barriers per strip: the strips are complete before they are read
+  // across waves, and read before the next strip overwrites them.
+  constexpr int ENRG = EPI > 0 ? EPI - 1 : 0;
+  constexpr int EGW = (ENRG + 1) / 2;
+  auto store_tile_mlp = [&](int64_t m0, int64_t j0) {
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int lgrp = ln >> 5, lodd = ln & 1, ll32 = ln & 31;
+    const uint32_t psel = pair_sel(lodd);
+    const uint32_t gcol = static_cast<uint32_t>(j0) + wn * 128 + (ln & 15) * 8;
+    const bool col_ok = gcol < static_cast<uint32_t>(NOUT);
+    const uint32_t srow0 = static_cast<uint32_t>(m0) + wm * 128;
+    const uint32_t out_base = col_ok ? (srow0 + (ln >> 4)) * out_row + gcol * 2 : OOB;
+    const uint32_t cpr = static_cast<uint32_t>(NOUT >> 1), spr = static_cast<uint32_t>(NOUT >> 5);
+    const auto r_ec = rsrc(g.e_codes, static_cast<uint64_t>(M) * cpr);
+    const auto r_es = rsrc(g.e_scales, static_cast<uint64_t>(M) * spr);
+    const uint32_t nrb = static_cast<uint32_t>((M + 63) >> 6);
+    const auto r_ep = rsrc(g.e_part, static_cast<uint64_t>(nt_n) * nrb * 4 * ENRG * 1024);
+    // D2 fragments: rank 16 (wn EGW + gi) + ln % 16, columns j0 + 32 ks +
+    // 8 (ln / 16) .. +7; zero past the ranks and columns
+    u32x4 bfr[EGW > 0 ? EGW : 1][8];
+    if constexpr (ENRG > 0) {
+      const RankRows& p = g.e_pr;
+      const auto rp0 = rsrc(p.p0, static_cast<uint64_t>(p.r0) * p.ld * 2);
+      const auto rp1 = rsrc(p.p1, static_cast<uint64_t>(p.r1) * p.ld * 2);
+#pragma unroll
+      for (int gi = 0; gi < EGW; ++gi)
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks) {
+          const int r = 16 * (wn * EGW + gi) + (ln & 15);
+          const uint32_t c = static_cast<uint32_t>(j0) + 32 * ks + 8 * (ln >> 4);
+          const bool ok = r < g.e_R && c < static_cast<uint32_t>(NOUT);
+          const uint32_t o0 = ok && r < p.r0 ? static_cast<uint32_t>((r * p.ld + c) * 2) : OOB;
+          const uint32_t o1 = ok && r >= p.r0 ? static_cast<uint32_t>(((r - p.r0) * p.ld + c) * 2) : OOB;
+          bfr[gi][ks] = bload128(rp0, o0) | bload128(rp1, o1);
+        }
+    }
+#pragma unroll
+    for (int mt = 0; mt < 4; ++mt)
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t srow = srow0 + 32 * mt + 16 * h;     // the strip's first row
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+          for (int p = 0; p < 4; ++p) {
+            const uint32_t v = pair_bf16(acc[mt][nt][8 * h + 2 * p], acc[mt][nt][8 * h + 2 * p + 1], psel);
+            const int row = 8 * (p >> 1) + 4 * lgrp + 2 * (p & 1) + lodd;
+            const int sw = (row & 1) | (((row >> 2) & 1) << 1);
+            const int col = nt * 32 + (ll32 & ~1);
+            *reinterpret_cast<uint32_t*>(ostage + row * 256 + (((col >> 5) ^ sw) << 6) + (col & 31) * 2) = v;
+          }
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int idx = e * 64 + ln, row = idx >> 4, c16 = idx & 15;
+          const int sw = (row & 1) | (((row >> 2) & 1) << 1);
+          uint8_t* sp = ostage + row * 256 + ((((c16 >> 2) ^ sw) << 6) | ((c16 & 3) << 4));
+          const u32x4 v = lds_read_b128(sp);
+          const uint32_t off = out_base == OOB ? OOB : out_base + static_cast<uint32_t>(mt * 32 + 16 * h + 4 * e) * out_row;
+          __builtin_amdgcn_raw_buffer_store_b128(v, r_out, static_cast<int>(off), 0, 2);
+          const u32x4 av = act_bf16x8<1>(v, v);
+          const uint32_t m = max_u16x2(max_u16x2(abs_bf16x2(av[0]), abs_bf16x2(av[1])),
+                                       max_u16x2(abs_bf16x2(av[2]), abs_bf16x2(av[3])));
+          uint32_t am = hmax_u16x2(m);
+          am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0xB1, 0xF, 0xF, false)));
+          am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0x4E, 0xF, 0xF, false)));
+          const uint32_t sc8 = e8m0_from_amax_bits(am);
+          const uint32_t code = encode8(av[0], av[1], av[2], av[3], e8m0_to_f32(sc8));
+          const uint32_t grow = srow + row;
+          __builtin_amdgcn_raw_buffer_store_b32(code, r_ec, static_cast<int>(col_ok ? grow * cpr + (gcol >> 1) : OOB), 0, 0);
+          __builtin_amdgcn_raw_buffer_store_b8(static_cast<uint8_t>(sc8), r_es,
+                                               static_cast<int>(col_ok && (ln & 3) == 0 ? grow * spr + (gcol >> 5) : OOB), 0, 0);
+          *reinterpret_cast<u32x4*>(sp) = av;
+        }
+        if constexpr (ENRG > 0) {
+          lds_barrier();
+          f32x4 pacc[EGW];
+#pragma unroll
+          for (int gi = 0; gi < EGW; ++gi) pacc[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
+          const int ar = ln & 15;
+          const int asw = (ar & 1) | (((ar >> 2) & 1) << 1);
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) {
+            const uint8_t* src = lds_out + (wm * 2 + (ks >> 2)) * OUT_WAVE + ar * 256 +
+                                 ((((ks & 3) ^ asw) << 6) | (16 * (ln >> 4)));
+            const u32x4 af = lds_read_b128(src);
+#pragma unroll
+            for (int gi = 0; gi < EGW; ++gi) pacc[gi] = mfma_bf16_16x16x32(af, bfr[gi][ks], pacc[gi]);
+          }
+          lds_barrier();
+          const uint32_t rb = srow >> 6, sl = (srow >> 4) & 3;
+#pragma unroll
+          for (int gi = 0; gi < EGW; ++gi) {
+            const int gr = wn * EGW + gi;
+            const uint32_t off = rb < nrb && gr < ENRG
+                                     ? ((((static_cast<uint32_t>(j0) >> 8) * nrb + rb) * 4 + sl) * ENRG + gr) * 1024 + ln * 16
+                                     : OOB;
+            __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, pacc[gi]), r_ep, static_cast<int>(off), 0, 0);
+          }
+        }
+      }
+#pragma unroll
+    for (int a = 0; a < 4; ++a)
+#pragma unroll
+      for (int b = 0; b < 4; ++b)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[a][b][r] = 0.f;
+  };
+
   // Split units: the fp32 sums of rows below M to g.part[split][row][col],
   // 128 bytes of a row per half wave; row groups past M are skipped whole
   // (a uniform test: a few-row output stores a few groups).  The stores are
@@ -772,13 +905,14 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
     int64_t m0, j0;
     int ko;
     tile_of(k, m0, j0, ko);
-    if constexpr (!LR) {
+    if constexpr (!LR && EPI == 0) {
       if (S > 1) {
         store_part(m0, j0, ko / nks);
         continue;
       }
     }
-    store_tile(m0, j0);
+    if constexpr (EPI > 0) store_tile_mlp(m0, j0);
+    else store_tile(m0, j0);
   }
   // DMAs into LDS must land before the workgroup can end
   __builtin_amdgcn_s_waitcnt(waitcnt_imm(0, 0xF));
@@ -1203,6 +1337,28 @@ __global__ __launch_bounds__(256) void k_split_reduce(const GemmArgs g) {
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const uint32_t n = static_cast<uint32_t>(((g.NOUT + BN - 1) / BN) * ((g.M + BM - 1) / BM));
   const bool bf = g.a16 != nullptr;
+  if (g.e_codes) {
+    // MLP fusion: the pipelined kernel on 32x32-tile weights, one pass
+    if (bf || g.M <= 16 || (g.RED & 127) != 0 || g.b_row_scales || g.b_transposed || g.splits > 1 ||
+        !g.e_scales || g.e_nrg < 0 || g.e_nrg > 4 || (g.e_nrg > 0 && !g.e_part) || (g.NOUT & 31) != 0)
+      return hipErrorInvalidValue;
+    if (g.nlr != 0 && g.nlr != 2 && g.nlr != 4) return hipErrorInvalidValue;
+    const int cus = cu_count();
+    if (cus <= 0) return hipErrorInvalidDevice;
+    const uint32_t grid = n < static_cast<uint32_t>(cus) ? n : static_cast<uint32_t>(cus);
+#define FT_GE(NL, E) hipLaunchKernelGGL((k_gemm_pipe<NL, 0, E>), dim3(grid), dim3(256), 0, st, g)
+#define FT_GEN(E) do { if (g.nlr == 4) FT_GE(4, E); else if (g.nlr > 0) FT_GE(2, E); else FT_GE(0, E); } while (0)
+    switch (g.e_nrg) {
+      case 0: FT_GEN(1); break;
+      case 1: FT_GEN(2); break;
+      case 2: FT_GEN(3); break;
+      case 3: FT_GEN(4); break;
+      default: FT_GEN(5); break;
+    }
+#undef FT_GEN
+#undef FT_GE
+    return hipGetLastError();
+  }
   if (gemm_rows_ok(g.M, g.RED, bf, g.b_transposed != 0)) {
     // at most 16 rows: stream b, 32 output columns per workgroup
     if (g.nlr != 0 && g.nlr != 2 && g.nlr != 4) return hipErrorInvalidValue;

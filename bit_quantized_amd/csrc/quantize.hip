@@ -1151,8 +1151,21 @@ hipError_t launch_quant_down(const uint16_t* in, const uint16_t* in2, int act, i
   }
 #undef FT_QD_NS
   if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-  RRArgs b{part, static_cast<uint32_t>(rows), splits, R, rank_pad(R), out_lr, out_pad, cp, cp_rows, cp_dst,
-           cp_planes ? 1 : 0};
+  (void)nrb;
+  return launch_rank_reduce(part, rows, static_cast<int>(splits), R, out_lr, out_pad, cp, cp_rows,
+                            cp_dst, st, cp_planes);
+}
+
+int rank_reduce_nrg(int R) { return R > 0 ? quant_down_nrg(R) : 0; }
+
+hipError_t launch_rank_reduce(const float* part, int64_t rows, int splits, int R, uint16_t* out_lr,
+                              uint16_t* out_pad, const RankRows& cp, int64_t cp_rows,
+                              uint16_t* cp_dst, hipStream_t st, bool cp_planes) {
+  if (R <= 0 || splits < 1) return hipErrorInvalidValue;
+  const uint32_t nrb = static_cast<uint32_t>((rows + 63) / 64);
+  const int nrg = quant_down_nrg(R);
+  RRArgs b{part, static_cast<uint32_t>(rows), static_cast<uint32_t>(splits), R, rank_pad(R), out_lr,
+           out_pad, cp, cp_rows, cp_dst, cp_planes ? 1 : 0};
   const uint64_t ncopy = cp_planes ? (static_cast<uint64_t>(rank_pad(R)) * (cp_rows / 32) + 255) / 256
                                    : (static_cast<uint64_t>(cp_rows) * (rank_pad(R) / 8) + 255) / 256;
   const dim3 rgrid(static_cast<uint32_t>(nrb * 4 + ncopy));

@@ -163,6 +163,35 @@ class QuantizedLinear:
         return out + (qc, qs) if want_codes else out
 
 
+_mlp_ws = {}
+
+
+def mlp_forward(fc1: QuantizedLinear, fc2: QuantizedLinear, X: torch.Tensor, stream=None,
+                want_codes: bool = False):
+    """The MLP block's two forwards with FC1's GEMM fused with FC2's
+    quantization (fourtune_mlp_fwd); fc2 must have act_in = GELU.  Returns
+    (h, U1, Y, U2) or (h, U1, Y, U2, aq_codes, aq_scales), aq being FC2's
+    quantized input Qrow(gelu(h))."""
+    M = int(X.shape[0])
+    dev = fc1.device
+    H = _empty((M, fc1.N), torch.bfloat16, dev)
+    Y = _empty((M, fc2.N), torch.bfloat16, dev)
+    U1 = _empty((M, max(fc1.R, 1)), torch.bfloat16, dev)
+    U2 = _empty((M, max(fc2.R, 1)), torch.bfloat16, dev)
+    codes = want_codes and not fc2.a16
+    qc = _empty((M, fc2.K // 2), torch.uint8, dev) if codes else None
+    qs = _empty((M, fc2.K // 32), torch.uint8, dev) if codes else None
+    d1, d2 = fc1.desc(M), fc2.desc(M)
+    key = (id(fc1), id(fc2), M)
+    if key not in _mlp_ws:
+        n = ops.fourtune_mlp_workspace_bytes(d1, d2)
+        _mlp_ws[key] = _empty((max(n, 256),), torch.uint8, dev)
+    ws = _mlp_ws[key]
+    ops.fourtune_mlp_fwd(d1, d2, X, H, Y, U1 if fc1.R else None, U2 if fc2.R else None, qc, qs,
+                         ws, ws.numel(), stream)
+    return (H, U1, Y, U2, qc, qs) if want_codes else (H, U1, Y, U2)
+
+
 class FourTuneLinearFunction(torch.autograd.Function):
     """Y = layer(X) with gradients for X, At and B (W_res, L1, L2 frozen).
     At and B must be the tensors the layer holds.  With the layer's act_in,

@@ -291,6 +291,41 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
                               uint8_t* gq_scales, void* workspace, size_t ws_bytes,
                               void* stream);
 
+/* The forward of an MLP block's two linears with the GeLU between them,
+ * FC1's GEMM fused with FC2's quantization (FourTune, "3.3 Kernel Fusion for
+ * Efficiency / MLP Fusion"):
+ *   fc1: X [M, K1] -> H [M, N1], the pre-activation h, written for the
+ *        backward (fc1->act_out is not read here);
+ *   fc2: gelu(H) [M, N1] -> Y [M, N2]; fc2->act_in must be
+ *        FT_ACT_GELU_TANH, fc2->M == fc1->M, fc2->K == fc1->N.
+ * Kernels: fc1's kernel 1 (as fourtune_linear_fwd); fc1's GEMM, whose
+ * epilogue also applies the GeLU to the rounded h it holds and writes FC2's
+ * quantized input Qrow(gelu(h)) and the fp32 sums of FC2's down-projection
+ * gelu(h) [L1|A] over each 256 columns of h; a kernel that adds those sums
+ * in column order and rounds them to U2; FC2's GEMM.  So FC2's kernel 1,
+ * a second full read of H, does not run.
+ * Results: H, U1_save, U2_save, Y and the optional aq_codes [M, N1/2] and
+ * aq_scales [M, N1/32] (FC2's quantized input) are those of
+ * fourtune_linear_fwd(fc1, X) followed by fourtune_linear_fwd(fc2, H): the
+ * same bits where FC2's kernel 1 would sum 256-column splits (when
+ * ceil(M/64) * ceil(N1/256) is at least the device's CU count), else U2
+ * (and so Y) up to the order of U2's fp32 sums.
+ * The epilogue fusion applies when both layers are FT_W4A4G4, fc1's
+ * w_block is TILE32 or TILE32_T, K1 % 128 == 0, M > 16, FC1's GEMM runs in
+ * one pass over its reduction (it splits the reduction only for outputs
+ * of at most 128 tiles of 256 x 256, by a cost model of the shapes), and
+ * R2 = fc2 ranks <= 64; otherwise the two forwards run one after the
+ * other (the same results).
+ * workspace: at least fourtune_mlp_workspace_bytes(fc1, fc2) bytes.
+ * Requirements and errors: those of fourtune_linear_fwd for each layer;
+ * FT_ESHAPE if the layers do not chain; FT_EINVAL if fc2->act_in is not
+ * FT_ACT_GELU_TANH. */
+size_t fourtune_mlp_workspace_bytes(const ft_linear* fc1, const ft_linear* fc2);
+ft_status fourtune_mlp_fwd(const ft_linear* fc1, const ft_linear* fc2, const uint16_t* X,
+                           uint16_t* H, uint16_t* Y, uint16_t* U1_save, uint16_t* U2_save,
+                           uint8_t* aq_codes, uint8_t* aq_scales, void* workspace,
+                           size_t ws_bytes, void* stream);
+
 /* The activation on its own, with the same device functions the fused
  * kernels apply to their inputs (so that a caller, or a test, can see the
  * exact bf16 values the layers consume).  n elements, contiguous.

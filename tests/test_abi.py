@@ -222,6 +222,38 @@ def test_weight_block_argument_errors():
             == ops.fourtune_workspace_bytes(_layer(), True))
 
 
+def _mlp(f1, f2, X=A16, H=A16, Y=A16, U1=A16, U2=A16, qc=None, qs=None, ws=A16, wsb=1 << 40):
+    return ops.lib().fourtune_mlp_fwd(ctypes.byref(f1), ctypes.byref(f2), X, H, Y, U1, U2, qc, qs,
+                                      ws, wsb, None)
+
+
+def test_mlp_forward_argument_errors():
+    """The fused MLP forward checks both layers, that they chain (M equal,
+    fc2.K == fc1.N, fc2's input activation set), its pointers and its
+    workspace before touching any device."""
+    G = ops.FT_ACT_GELU_TANH
+    f1 = _layer(M=300, K=256, N=544)
+    f2 = _layer(M=300, K=544, N=256, act_in=G)
+    need = ops.fourtune_mlp_workspace_bytes(f1, f2)
+    assert need == ops.fourtune_workspace_bytes(f1, False) + ops.fourtune_workspace_bytes(f2, False)
+    assert ops.fourtune_mlp_workspace_bytes(f1, _layer(K=40)) == 0
+    assert _mlp(f1, _layer(M=300, K=512, N=256, act_in=G)) == ops.FT_ESHAPE     # fc2.K != fc1.N
+    assert _mlp(f1, _layer(M=200, K=544, N=256, act_in=G)) == ops.FT_ESHAPE     # M differs
+    assert _mlp(f1, _layer(M=300, K=544, N=256)) == ops.FT_EINVAL               # no GELU input
+    assert _mlp(_layer(M=300, K=256, N=544, w_codes=None), f2) == ops.FT_EINVAL
+    assert _mlp(f1, f2, H=None) == ops.FT_EINVAL
+    assert _mlp(f1, f2, U2=None) == ops.FT_EINVAL
+    assert _mlp(f1, f2, qc=A16) == ops.FT_EINVAL                                # codes without scales
+    assert _mlp(f1, f2, Y=A16 + 4) == ops.FT_EALIGN
+    assert _mlp(f1, f2, qc=A16, qs=A16 + 2) == ops.FT_EALIGN
+    assert _mlp(f1, f2, wsb=need - 1) == ops.FT_EWORKSPACE
+    assert _mlp(f1, f2, ws=None, wsb=need) == ops.FT_EINVAL
+    # A16 on fc2: no quantized input to hand out
+    assert _mlp(f1, _layer(M=300, K=544, N=256, act_in=G, precision=ops.FT_W4A16G4),
+                qc=A16, qs=A16) == ops.FT_EINVAL
+    assert _mlp(f1, f2) == ops.FT_EUNSUPPORTED          # only the missing GPU stops it
+
+
 def _fwd_noalloc(L, X=A16, Y=A16, U=A16, qc=None, qs=None):
     return ops.lib().fourtune_linear_fwd_noalloc(ctypes.byref(L), X, Y, U, qc, qs, None)
 

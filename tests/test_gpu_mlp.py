@@ -22,12 +22,12 @@ import pytest
 import torch
 
 from bit_quantized_amd import ops, synth
-from bit_quantized_amd.layer import QuantizedLinear, bits_of
+from bit_quantized_amd.layer import QuantizedLinear, bits_of, mlp_forward
 from oracle import linear as OL
 from oracle import mxfp4 as OQ
 
-from _gpu import (DEV, REL_TOL, _check_down_proj, _check_outputs_elementwise, require_gpu, say,
-                  up)
+from _gpu import (DEV, REL_TOL, _check_down_proj, _check_outputs_elementwise,
+                  check_rounding_flips, require_gpu, say, up)
 
 pytestmark = pytest.mark.gpu
 G = ops.FT_ACT_GELU_TANH
@@ -255,3 +255,121 @@ def test_mlp_pair_chain_full_size_sampled():
              "P": got[Pk]}
         _check_down_proj(cc, g)
         _check_outputs_elementwise(cc, g, rows, wc, ws, {}, {}, "W4A4G4")
+
+
+# ------------------------------------------------------------------ the fused MLP forward
+# FourTune, "3.3 Kernel Fusion for Efficiency / MLP Fusion": FC1's GEMM
+# epilogue applies the GeLU to the h it holds and writes FC2's quantized
+# input and FC2's down-projection partials (fourtune_mlp_fwd).
+def _fused_kernels():
+    """Launch counts per kernel name since the last timing reset."""
+    return {k: cnt for k, (tot, cnt) in ops.fourtune_timing_read().items() if cnt}
+
+
+def _run_fused(mp, X1):
+    """Both paths on the same input: the two forwards one after the other,
+    then the fused call (its kernel names recorded, to show that the
+    epilogue fusion ran)."""
+    h_u, U1_u, _, _ = mp.fc1.forward(X1, want_codes=True)
+    Y_u, U2_u, ac_u, as_u = mp.fc2.forward(h_u, want_codes=True)
+    torch.cuda.synchronize()
+    ops.fourtune_timing_reset()
+    ops.fourtune_timing_enable(True)
+    try:
+        h, U1, Y, U2, ac, as_ = mlp_forward(mp.fc1, mp.fc2, X1, want_codes=True)
+        torch.cuda.synchronize()
+    finally:
+        ops.fourtune_timing_enable(False)
+    names = _fused_kernels()
+    ops.fourtune_timing_reset()
+    R = lambda t, c: bits_of(t)[:, :c.R] if c.R else None
+    fused = dict(h=bits_of(h), U1=R(U1, mp.c1), Y=bits_of(Y), U2=R(U2, mp.c2),
+                 ac=ac.cpu().numpy(), as_=as_.cpu().numpy())
+    plain = dict(h=bits_of(h_u), U1=R(U1_u, mp.c1), Y=bits_of(Y_u), U2=R(U2_u, mp.c2),
+                 ac=ac_u.cpu().numpy(), as_=as_u.cpu().numpy())
+    return fused, plain, names
+
+
+def _same_bits(a, b, name):
+    if a is None:
+        assert b is None, name
+        return
+    np.testing.assert_array_equal(a, b, err_msg=name)
+
+
+@pytest.mark.parametrize("shape", [
+    (300, 256, 544, 16, 8),     # ragged rows (2 row tiles), F = 544: last column tile of 32
+    (520, 384, 1280, 32, 32),   # R2 = 64: four rank groups, two per wave
+    (600, 128, 2304, 32, 16),   # R2 = 48: three rank groups (the second wave's second empty)
+    (130, 256, 768, 0, 8),      # adapter only, R2 = 8: one rank group
+    (272, 128, 288, 0, 0),      # no ranks: codes and scales only
+    (1040, 128, 16384, 16, 16), # 5 x 64 = 320 tiles: workgroups that walk two tiles
+])
+def test_mlp_fused_forward_full(shape):
+    M, K, F, rs, rl = shape
+    say("case fused mlp forward", shape)
+    mp = MlpPair(M, K, F, rs, rl, seed=3 * M + F)
+    X1 = up(mp.c1.X)
+    got, ref, names = _run_fused(mp, X1)
+    say("kernels", names)
+    # FC1's kernel 1, its fused GEMM, the partials' sum, FC2's GEMM: FC2's
+    # quantize kernel does not run
+    assert names.get("fwd_gemm_mlp") == 1 and names.get("fwd_gemm") == 1, names
+    assert names.get("fwd_quant_down") == 1, names
+    assert names.get("fwd_rank_reduce", 0) == (1 if mp.c2.R else 0), names
+    # h and U1 come out of the same kernels as the unfused forward
+    _same_bits(got["h"], ref["h"], "h")
+    _same_bits(got["U1"], ref["U1"], "U1")
+    # FC2's quantized input: the unfused quantizer's bits, and the oracle's
+    # quantization of the GPU's bf16 gelu(h)
+    _same_bits(got["ac"], ref["ac"], "aq codes")
+    _same_bits(got["as_"], ref["as_"], "aq scales")
+    a_gpu = _gelu_gpu(got["h"])
+    xc, xs = OQ.quantize_row32(a_gpu)
+    np.testing.assert_array_equal(got["ac"], xc, err_msg="aq codes vs oracle")
+    np.testing.assert_array_equal(got["as_"], xs, err_msg="aq scales vs oracle")
+    c2 = copy.copy(mp.c2)
+    c2.X = a_gpu
+    if c2.R:
+        # U2 = bf16(gelu(h) D2): a correct rounding of the exact sum but for
+        # the fp32 accumulation order
+        D = OL.stack_down(c2.L1, c2.A)
+        A = OQ.bf16_bits_to_f64(a_gpu)
+        check_rounding_flips(got["U2"], A @ D, "U2", np.abs(A) @ np.abs(D), c2.K)
+    # Y against the oracle fed the GPU's activation and U2: exact sums of
+    # the dequantized operands plus U2 V2
+    wc, ws = OQ.quantize_tile32(c2.W_res)
+    Xh = OQ.dequantize_row32(xc, xs)
+    Wf = OL.weight_fwd(wc, ws, "tile32")
+    Uv = OQ.bf16_bits_to_f64(got["U2"]) if c2.R else np.zeros((M, 0))
+    V = OL.stack_up(c2.L2, c2.B)
+    ey = Xh @ Wf.T + Uv @ V
+    ty = np.abs(Xh) @ np.abs(Wf).T + np.abs(Uv) @ np.abs(V)
+    check_rounding_flips(got["Y"], ey, "Y", ty, c2.K + c2.R)
+    res = {"Y": OL.rel_frobenius(got["Y"], OQ.f64_to_bf16_bits(ey))}
+    say("rel", res)
+    assert res["Y"] <= REL_TOL
+
+
+def test_mlp_fused_forward_full_size():
+    """FLUX MLP forward at full size (4608 tokens, 3072 -> 12288 -> GELU ->
+    3072, ranks 32/32; 864 output tiles, 3-4 per workgroup): the fused call
+    gives the unfused forwards' bits (FC2's quantizer sums 256-column splits
+    at this size), and FC2's codes and U2 agree with the oracle on sampled rows."""
+    M, K, F = 4608, 3072, 12288
+    say("case fused mlp forward full size")
+    mp = MlpPair(M, K, F, 32, 32, seed=2)
+    got, ref, names = _run_fused(mp, up(mp.c1.X))
+    assert names.get("fwd_gemm_mlp") == 1 and names.get("fwd_rank_reduce") == 1, names
+    assert names.get("fwd_quant_down") == 1, names
+    for k in ("h", "U1", "ac", "as_", "U2", "Y"):
+        _same_bits(got[k], ref[k], k)
+    rng = np.random.default_rng(5)
+    rows = np.unique(np.concatenate([rng.choice(M, 24, replace=False), [0, M - 1]]))
+    a_rows = _gelu_gpu(got["h"][rows])
+    xc, xs = OQ.quantize_row32(a_rows)
+    np.testing.assert_array_equal(got["ac"][rows], xc)
+    np.testing.assert_array_equal(got["as_"][rows], xs)
+    D = OL.stack_down(mp.c2.L1, mp.c2.A)
+    A = OQ.bf16_bits_to_f64(a_rows)
+    check_rounding_flips(got["U2"][rows], A @ D, "U2 rows", np.abs(A) @ np.abs(D), F)
