@@ -84,105 +84,54 @@ __global__ __launch_bounds__(256) void k_quant_row32(const uint16_t* __restrict_
 }
 
 // ---------------------------------------------------------------------------
-// Workgroup -> (column group x, row group y) of an nx by ny grid.  The
-// logical index runs through bands of 8 row groups, row group fastest, so
-// the workgroups one XCD holds at a time cover 8 consecutive row groups of
-// the same columns: the transposed outputs of those 8 (16 bytes each per
-// column) fill whole 128-byte lines in that XCD's L2.
-__device__ __forceinline__ void band_coords(uint32_t L, uint32_t nx, uint32_t ny, uint32_t& x,
-                                            uint32_t& y) {
-  const uint32_t band = L / (8 * nx);
-  const uint32_t h = ny - band * 8 < 8 ? ny - band * 8 : 8;
-  const uint32_t r = L - band * 8 * nx;
-  x = r / h;
-  y = band * 8 + r % h;
-}
-
-// Loads of a 32-row x 512-column slab: wave w holds rows 8w .. 8w+7, lane l
-// columns 8l .. 8l+7 of each (one 1 KB instruction per row); 4 consecutive
-// lanes hold one 32-column block of a row.
-__device__ __forceinline__ void load_slab(__amdgpu_buffer_rsrc_t r, uint32_t row0, uint32_t col,
-                                          bool ok, uint32_t ld2, u32x4 (&v)[8]) {
-  const uint32_t base = ok ? row0 * ld2 + col * 2 : BUF_OOB;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) v[i] = buf_load128_nt(r, base == BUF_OOB ? BUF_OOB : base + i * ld2);
-}
-
-// ---------------------------------------------------------------------------
-// 32x32 tiles.  A workgroup covers 32 rows x 512 columns (16 tiles).  The
-// tile amax: each lane's 8 x 8 values, a quad DPP step across the tile's 4
-// lanes, then the 4 waves through LDS.  Optionally also the transposed codes
-// [cols, rows/2] and scales [cols/32, rows/32] (the same numbers, since a
-// tile has one scale): the codes go to LDS row-major and come back
-// transposed with ds_read_b64_tr_b4, one 16-byte column segment per lane.
+// 32x32 tiles, one layout.  Each wave quantizes 32 rows x 256 columns (8
+// tiles) on its own: lane l holds columns 8 (l % 32) .. +7 of rows 2 i +
+// l / 32 (i < 16), so every load instruction reads two whole 512-byte row
+// pieces and every code store writes two whole 128-byte code lines.  The 8
+// lanes of a tile (a quad in each half of the wave) reduce its amax with
+// two quad DPP steps and one exchange between the halves; no LDS and no
+// barrier, so each wave streams at its own pace.  A workgroup's 4 waves
+// take the same 256 columns of 128 consecutive rows, and workgroups run in
+// plain row-major order (an XCD-compact order in bands of 8 row groups
+// made this one 10% slower: 70.7 against 63.5 us on 12288^2).
 __global__ __launch_bounds__(256) void k_quant_tile32(const uint16_t* __restrict__ in,
                                                       uint32_t rows, uint32_t cols, int64_t ld,
                                                       uint8_t* __restrict__ codes,
-                                                      uint8_t* __restrict__ scales,
-                                                      uint8_t* __restrict__ codes_t,
-                                                      uint8_t* __restrict__ scales_t) {
-  constexpr int CT_P = 264;                                   // LDS pitch of a code row (bytes)
-  __shared__ uint32_t red[4][16];
-  __shared__ __attribute__((aligned(16))) uint8_t ct[32 * CT_P];
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const uint32_t nx = (cols + 511) / 512, ny = rows / 32;
-  uint32_t x, y;
-  band_coords(xcd_remap(blockIdx.x, nx * ny), nx, ny, x, y);
-  const uint32_t col = x * 512 + 8 * lane;
+                                                      uint8_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t nx = (cols + 255) / 256, ny = rows / 32;
+  const uint32_t x = blockIdx.x % nx, y = (blockIdx.x / nx) * 4 + wave;
+  if (y >= ny) return;
+  const uint32_t col = x * 256 + 8 * (lane & 31);
   const bool ok = col < cols;
-  u32x4 v[8];
-  load_slab(make_rsrc(in, static_cast<uint64_t>(rows) * ld * 2), y * 32 + 8 * wave, col, ok,
-            static_cast<uint32_t>(ld) * 2, v);
+  const uint32_t ld2 = static_cast<uint32_t>(ld) * 2;
+  const uint32_t row0 = y * 32 + (lane >> 5);
+  const auto rin = make_rsrc(in, static_cast<uint64_t>(rows) * ld * 2);
+  const uint32_t base = ok ? row0 * ld2 + col * 2 : BUF_OOB;
+  u32x4 v[16];
+#pragma unroll
+  for (int i = 0; i < 16; ++i) v[i] = buf_load128_nt(rin, base == BUF_OOB ? BUF_OOB : base + 2 * i * ld2);
   uint32_t m = 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 16; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) m = max_u16x2(m, abs_bf16x2(v[i][j]));
   uint32_t am = hmax_u16x2(m);
   am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0xB1, 0xF, 0xF, false)));
   am = max(am, static_cast<uint32_t>(__builtin_amdgcn_update_dpp(0, static_cast<int>(am), 0x4E, 0xF, 0xF, false)));
-  const int tile = lane >> 2;
-  if ((lane & 3) == 0) red[wave][tile] = am;
-  __syncthreads();
-  am = max(max(red[0][tile], red[1][tile]), max(red[2][tile], red[3][tile]));
+  am = max(am, static_cast<uint32_t>(__builtin_amdgcn_ds_bpermute((lane ^ 32) << 2, static_cast<int>(am))));
   const uint32_t s = e8m0_from_amax_bits(am);
   const float sc = e8m0_to_f32(s);
-  uint32_t o[8];
+  // streaming (non-temporal) stores: weights are quantized once, ahead of use
+  const uint32_t cpr = cols >> 1;
+  const auto rcodes = make_rsrc(codes, static_cast<uint64_t>(rows) * cpr);
+  const uint32_t cbase = ok ? row0 * cpr + (col >> 1) : BUF_OOB;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) o[i] = encode8(v[i][0], v[i][1], v[i][2], v[i][3], sc);
-  // streaming (non-temporal) stores of whole 128-byte code lines: weights
-  // are quantized once, ahead of use
-  const auto rcodes = make_rsrc(codes, static_cast<uint64_t>(rows) * (cols >> 1));
-#pragma unroll
-  for (int i = 0; i < 8; ++i)
-    __builtin_amdgcn_raw_buffer_store_b32(
-        o[i], rcodes, static_cast<int>(ok ? (y * 32 + 8 * wave + i) * (cols >> 1) + (col >> 1) : BUF_OOB), 0, 2);
-  if (ok) {
-    if (wave == 0 && (lane & 3) == 0) {
-      scales[static_cast<uint64_t>(y) * (cols >> 5) + (col >> 5)] = static_cast<uint8_t>(s);
-      if (scales_t) scales_t[static_cast<uint64_t>(col >> 5) * ny + y] = static_cast<uint8_t>(s);
-    }
-  }
-  if (!codes_t) return;
-  const auto rcodes_t = make_rsrc(codes_t, static_cast<uint64_t>(cols) * (rows >> 1));
-#pragma unroll
-  for (int i = 0; i < 8; ++i) *reinterpret_cast<uint32_t*>(&ct[(8 * wave + i) * CT_P + 4 * lane]) = o[i];
-  __syncthreads();
-  // 16-lane group g of wave w, pass j: columns 16 cg .. 16 cg + 15; lane q
-  // addresses row q (then 16 + q) and receives column 16 cg + q
-  const int q = lane & 15;
-#pragma unroll
-  for (int j = 0; j < 2; ++j) {
-    const int cg = (wave * 2 + j) * 4 + (lane >> 4);
-    const u32x2 lo = lds_read_tr4(&ct[q * CT_P + cg * 8]);
-    const u32x2 hi = lds_read_tr4(&ct[(16 + q) * CT_P + cg * 8]);
-    const uint32_t c = x * 512 + cg * 16 + q;
-    // cached: each 16-byte piece is an eighth of a 128-byte line that other
-    // workgroups complete, and only L2 merges them (non-temporal partial
-    // lines measured 3x slower)
-    __builtin_amdgcn_raw_buffer_store_b128(u32x4{lo[0], lo[1], hi[0], hi[1]}, rcodes_t,
-                                           static_cast<int>(c < cols ? c * (rows >> 1) + y * 16 : BUF_OOB), 0, 0);
-  }
+  for (int i = 0; i < 16; ++i)
+    __builtin_amdgcn_raw_buffer_store_b32(encode8(v[i][0], v[i][1], v[i][2], v[i][3], sc), rcodes,
+                                          static_cast<int>(cbase == BUF_OOB ? BUF_OOB : cbase + 2 * i * cpr), 0, 2);
+  const auto rscales = make_rsrc(scales, static_cast<uint64_t>(ny) * (cols >> 5));
+  buf_store8(rscales, ok && lane < 32 && (lane & 3) == 0 ? y * (cols >> 5) + (col >> 5) : BUF_OOB, s);
 }
 
 // ---------------------------------------------------------------------------
@@ -216,22 +165,26 @@ __global__ __launch_bounds__(256) void k_quant_tile32(const uint16_t* __restrict
 // scale goes through LDS; one lane per tile writes the tile's two scale
 // bytes.  Measured on a 12288 x 12288 weight: 93 -> 89 us against 32-row
 // slabs with an LDS transpose.
+//
+// Registers are capped for 4 waves per SIMD (two workgroups per CU):
+// ROW32_T then takes 128 registers (one spilled value) instead of 141 and
+// runs in 121 instead of 129 us on the stress activation.
 template <bool TILE>
-__global__ __launch_bounds__(512) void k_quant_dual(const uint16_t* __restrict__ in,
-                                                    uint32_t rows, uint32_t cols, int64_t ld,
-                                                    uint8_t* __restrict__ codes,
-                                                    uint8_t* __restrict__ scales,
-                                                    uint8_t* __restrict__ codes_t,
-                                                    uint8_t* __restrict__ scales_t) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4)))
+void k_quant_dual(const uint16_t* __restrict__ in, uint32_t rows, uint32_t cols, int64_t ld,
+                  uint8_t* __restrict__ codes, uint8_t* __restrict__ scales,
+                  uint8_t* __restrict__ codes_t, uint8_t* __restrict__ scales_t) {
   __shared__ __attribute__((aligned(16))) uint8_t ct[256 * 128];   // [column][16-byte chunk ^ swz]
   __shared__ __attribute__((aligned(16))) uint8_t st[256 * 8];     // column scales [column][block]
   __shared__ __attribute__((aligned(16))) uint8_t sr[256 * 8];     // row scales [row][block]
   const int t = threadIdx.x;
   const int rg = t >> 5, cg = t & 31;
   const bool upper = (rg & 1) != 0;                        // second 16 rows of the column block
-  const uint32_t nx = (cols + 255) / 256, ny = (rows + 255) / 256;
-  uint32_t x, y;
-  band_coords(xcd_remap(blockIdx.x, nx * ny), nx, ny, x, y);
+  // plain row-major workgroup order: measured faster than bands of 8 row
+  // groups made XCD-compact (ROW32_T 127 against 133 us, TILE32 with both
+  // layouts 82 against 89 us at the stress shapes)
+  const uint32_t nx = (cols + 255) / 256;
+  const uint32_t x = blockIdx.x % nx, y = blockIdx.x / nx;
   const uint32_t row0 = y * 256 + 16 * rg;                 // this thread's first row
   const uint32_t col = x * 256 + 8 * cg;                   // this lane's first column
   // rows come in whole 32-row blocks, so both partners agree on this
@@ -242,8 +195,13 @@ __global__ __launch_bounds__(512) void k_quant_dual(const uint16_t* __restrict__
   u32x4 v[16];
   {
     const uint32_t base = ok ? row0 * ld2 + col * 2 : BUF_OOB;
+    // row i's offset rides in the uniform soffset, so one lane register
+    // addresses all 16 loads (a lane out of range has its vector offset
+    // past the end, and the range check keeps it there)
 #pragma unroll
-    for (int i = 0; i < 16; ++i) v[i] = buf_load128_nt(rin, ok ? base + i * ld2 : BUF_OOB);
+    for (int i = 0; i < 16; ++i)
+      v[i] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rin, static_cast<int>(base),
+                                                                              static_cast<int>(i * ld2), 2));
   }
 
   // ---- TILE: one scale per 32x32 tile, the max over the thread's 16 x 8
@@ -271,6 +229,7 @@ __global__ __launch_bounds__(512) void k_quant_dual(const uint16_t* __restrict__
 
   // ---- row blocks (TILE: with the tile's scale)
   const auto rcodes = make_rsrc(codes, static_cast<uint64_t>(rows) * cpr);
+  const uint32_t cbase = ok ? row0 * cpr + (col >> 1) : BUF_OOB;
 #pragma unroll
   for (int i = 0; i < 16; ++i) {
     uint32_t s8;
@@ -284,7 +243,7 @@ __global__ __launch_bounds__(512) void k_quant_dual(const uint16_t* __restrict__
       s8 = e8m0_from_amax_bits(am);
     }
     const uint32_t o = encode8(v[i][0], v[i][1], v[i][2], v[i][3], TILE ? tsc : e8m0_to_f32(s8));
-    __builtin_amdgcn_raw_buffer_store_b32(o, rcodes, static_cast<int>(ok ? (row0 + i) * cpr + (col >> 1) : BUF_OOB), 0, 2);
+    __builtin_amdgcn_raw_buffer_store_b32(o, rcodes, static_cast<int>(cbase), static_cast<int>(i * cpr), 2);
     if constexpr (!TILE) {
       if ((cg & 3) == 0) sr[(16 * rg + i) * 8 + (cg >> 2)] = static_cast<uint8_t>(s8);
     }
@@ -304,54 +263,58 @@ __global__ __launch_bounds__(512) void k_quant_dual(const uint16_t* __restrict__
 #pragma unroll
     for (int k = 0; k < 4; ++k) cm[k] = max_u16x2(cm[k], static_cast<uint32_t>(__shfl_xor(static_cast<int>(cm[k]), 32)));
   }
-  // half[j] = this lane's 8 bytes (its 16 rows) of column 8 cg + j
-  uint32_t half[8][2];
-  uint32_t cs[8];
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const uint32_t s8 = TILE ? ts8 : e8m0_from_amax_bits(h ? cm[k] >> 16 : cm[k] & 0xFFFFu);
-      cs[2 * k + h] = s8;
-      const float sc = TILE ? tsc : e8m0_to_f32(s8);
-      const uint32_t sel = h ? 0x07060302u : 0x05040100u;
-      // byte p of word m = rows 8m + 2p (low nibble) and 8m + 2p + 1
-#pragma unroll
-      for (int m = 0; m < 2; ++m) {
-        auto vp = [&](int p) {
-          return __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(v[8 * m + 2 * p + 1][k], v[8 * m + 2 * p][k], sel));
-        };
-        uint32_t r = 0;
-        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(0), sc, 0);
-        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(1), sc, 1);
-        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(2), sc, 2);
-        r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(3), sc, 3);
-        half[2 * k + h][m] = r;
-      }
-    }
-  }
-  // the lower partner keeps columns 0..3 of its 8, the upper one 4..7: each
-  // sends the halves of the other four columns and receives their partner
-  // halves; the lower 16 rows are the first 8 bytes of a column block
+  // The lower partner keeps columns 0..3 of its 8, the upper one 4..7: each
+  // sends the halves (its 16 rows, 8 bytes) of the other four columns and
+  // receives their partner halves; the lower 16 rows are the first 8 bytes
+  // of a column block.  Columns j and 4 + j travel together, so they are
+  // made together: the pairs of words k and k + 2 of the loads (columns
+  // 2k, 2k + 1 and 2k + 4, 2k + 5), after which those words are dead.
   const int jb = upper ? 4 : 0;
-  uint32_t blk[4][4];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-#pragma unroll
-    for (int m = 0; m < 2; ++m) {
-      const uint32_t send = upper ? half[j][m] : half[4 + j][m];
-      const uint32_t got = static_cast<uint32_t>(__shfl_xor(static_cast<int>(send), 32));
-      const uint32_t mine = upper ? half[4 + j][m] : half[j][m];
-      blk[j][m] = upper ? got : mine;
-      blk[j][2 + m] = upper ? mine : got;
-    }
-  }
   const int swz = cg & 7;
   const int cb = rg >> 1;                                  // 32-row block of the tile
+  uint32_t cs[8];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int c = 8 * cg + jb + j;                         // column within the tile
-    *reinterpret_cast<u32x4*>(&ct[c * 128 + ((cb ^ swz) << 4)]) = u32x4{blk[j][0], blk[j][1], blk[j][2], blk[j][3]};
+  for (int kp = 0; kp < 2; ++kp) {
+    uint32_t hf[2][2][2];                                  // [k = kp, kp + 2][column parity][16-row half]
+#pragma unroll
+    for (int wk = 0; wk < 2; ++wk) {
+      const int k = kp + 2 * wk;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const uint32_t s8 = TILE ? ts8 : e8m0_from_amax_bits(h ? cm[k] >> 16 : cm[k] & 0xFFFFu);
+        cs[2 * k + h] = s8;
+        const float sc = TILE ? tsc : e8m0_to_f32(s8);
+        const uint32_t sel = h ? 0x07060302u : 0x05040100u;
+        // byte p of word m = rows 8m + 2p (low nibble) and 8m + 2p + 1
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          auto vp = [&](int p) {
+            return __builtin_bit_cast(bf16x2, __builtin_amdgcn_perm(v[8 * m + 2 * p + 1][k], v[8 * m + 2 * p][k], sel));
+          };
+          uint32_t r = 0;
+          r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(0), sc, 0);
+          r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(1), sc, 1);
+          r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(2), sc, 2);
+          r = __builtin_amdgcn_cvt_scalef32_pk_fp4_bf16(r, vp(3), sc, 3);
+          hf[wk][h][m] = r;
+        }
+      }
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int j = 2 * kp + h;                            // columns j (wk 0) and 4 + j (wk 1)
+      uint32_t blk[4];
+#pragma unroll
+      for (int m = 0; m < 2; ++m) {
+        const uint32_t send = upper ? hf[0][h][m] : hf[1][h][m];
+        const uint32_t got = static_cast<uint32_t>(__shfl_xor(static_cast<int>(send), 32));
+        const uint32_t mine = upper ? hf[1][h][m] : hf[0][h][m];
+        blk[m] = upper ? got : mine;
+        blk[2 + m] = upper ? mine : got;
+      }
+      const int c = 8 * cg + jb + j;                       // column within the tile
+      *reinterpret_cast<u32x4*>(&ct[c * 128 + ((cb ^ swz) << 4)]) = u32x4{blk[0], blk[1], blk[2], blk[3]};
+    }
   }
   // column scales: the same split (constant indices: a lane-dependent index
   // into cs would put the array in scratch)
@@ -990,11 +953,11 @@ hipError_t launch_quant_tile32(const uint16_t* in, int64_t rows, int64_t cols, i
                                uint8_t* codes, uint8_t* scales, uint8_t* codes_t,
                                uint8_t* scales_t, hipStream_t st) {
   if (!codes_t) {
-    // one layout: 32-row slabs (more workgroups in flight than the 256x256
-    // tiles the transpose needs)
-    const uint32_t n = static_cast<uint32_t>(((cols + 511) / 512) * (rows / 32));
+    // one layout: 32 x 256 pieces, each wave on its own (more workgroups
+    // in flight than the 256x256 tiles the transpose needs)
+    const uint32_t n = static_cast<uint32_t>(((cols + 255) / 256) * ((rows / 32 + 3) / 4));
     hipLaunchKernelGGL(k_quant_tile32, dim3(n), dim3(256), 0, st, in, static_cast<uint32_t>(rows),
-                       static_cast<uint32_t>(cols), ld, codes, scales, codes_t, scales_t);
+                       static_cast<uint32_t>(cols), ld, codes, scales);
   } else {
     const uint32_t n = static_cast<uint32_t>(((cols + 255) / 256) * ((rows + 255) / 256));
     hipLaunchKernelGGL(k_quant_dual<true>, dim3(n), dim3(512), 0, st, in, static_cast<uint32_t>(rows),
