@@ -1255,14 +1255,18 @@ SplitPlan gemm_split_plan(int64_t M, int64_t RED, int64_t NOUT) {
 
 namespace {
 // out[m][j] = bf16(sum over splits s (in order) of part[s][m][j] + sum over
-// ranks r of lm[m][r] lo[j][r]).  Workgroup: 4 rows x 256 columns; thread
-// t owns column j0 + t.  Its first 16 splits' sums and its rank row of lo
-// are loaded before the rows of lm are staged in LDS, so that one memory
-// latency covers all three; later splits follow 16 at a time.
-constexpr int SR_ROWS = 4;          // rows per workgroup
-constexpr int SR_NS = 16;           // splits per batch of loads
+// ranks r of lm[m][r] lo[j][r]).  Workgroup: ROWS rows x 256 columns;
+// thread t owns column j0 + t.  Its first batch of splits' sums and its
+// rank row of lo are loaded before the rows of lm are staged in LDS, so that
+// one memory latency covers all three; later splits follow a batch at a
+// time.  NLR (rank steps, 32 ranks each) is a template parameter so that the
+// lo row sits in registers indexed by constants.  ROWS = 4 for outputs of a
+// few rows; 16 otherwise, so that each lo row read serves 16 rows (with 4,
+// a 1024-row output spent 32 us here, mostly re-reading lo).
+template <int NLR, int ROWS, int NS>
 __global__ __launch_bounds__(256) void k_split_reduce(const GemmArgs g) {
-  __shared__ __attribute__((aligned(16))) uint16_t slm[SR_ROWS * 128];
+  constexpr int RP = 32 * NLR;
+  __shared__ __attribute__((aligned(16))) uint16_t slm[ROWS * (RP > 0 ? RP : 8)];
   // 32-bit indices (the sums are below 2^31 bytes); the row and split
   // tests are uniform and the column is clamped into the row, so every
   // load is a buffer load with a selected offset: no branches, and the
@@ -1270,66 +1274,82 @@ __global__ __launch_bounds__(256) void k_split_reduce(const GemmArgs g) {
   const uint32_t M = static_cast<uint32_t>(g.M), NOUT = static_cast<uint32_t>(g.NOUT);
   const uint32_t j = blockIdx.x * 256 + threadIdx.x;
   const uint32_t jc = j < NOUT ? j : NOUT - 1;
-  const uint32_t m0 = blockIdx.y * SR_ROWS;
-  const int rp = 32 * g.nlr, S = g.splits;
+  const uint32_t m0 = blockIdx.y * ROWS;
+  const int S = g.splits;
   const auto rpart = rsrc(g.part, static_cast<uint64_t>(S) * M * NOUT * 4);
-  const auto rlo = rsrc(g.lo, static_cast<uint64_t>(NOUT) * rp * 2);
-  auto load_batch = [&](int sp0, float (&v)[SR_ROWS][SR_NS]) {
+  auto load_batch = [&](int sp0, float (&v)[ROWS][NS]) {
 #pragma unroll
-    for (int i = 0; i < SR_ROWS; ++i)
+    for (int i = 0; i < ROWS; ++i)
 #pragma unroll
-      for (int k = 0; k < SR_NS; ++k) {
+      for (int k = 0; k < NS; ++k) {
         const bool ok = sp0 + k < S && m0 + i < M;
         const uint32_t row = (static_cast<uint32_t>(sp0 + k) * M + m0 + i) * NOUT;
         v[i][k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
                                                 rpart, static_cast<int>(ok ? (row + jc) * 4 : OOB), 0, 0));
       }
   };
-  float v[SR_ROWS][SR_NS];
+  float v[ROWS][NS];
   load_batch(0, v);
-  u32x4 vo[16];
+  u32x4 vo[RP > 0 ? RP / 8 : 1];
+  if constexpr (RP > 0) {
+    const auto rlo = rsrc(g.lo, static_cast<uint64_t>(NOUT) * RP * 2);
 #pragma unroll
-  for (int c = 0; c < 16; ++c) vo[c] = bload128(rlo, 8 * c < rp ? (jc * rp + 8 * c) * 2 : OOB);
-  for (int e = threadIdx.x; e < SR_ROWS * rp / 8; e += 256) {
-    const int r = e / (rp / 8), c = e % (rp / 8);
-    const auto rlm = rsrc(g.lm, static_cast<uint64_t>(M) * rp * 2);
-    const u32x4 w = bload128(rlm, m0 + r < M ? ((m0 + r) * rp + 8 * c) * 2 : OOB);
-    *reinterpret_cast<u32x4*>(slm + r * rp + 8 * c) = w;
+    for (int c = 0; c < RP / 8; ++c) vo[c] = bload128(rlo, (jc * RP + 8 * c) * 2);
+    const auto rlm = rsrc(g.lm, static_cast<uint64_t>(M) * RP * 2);
+    for (int e = threadIdx.x; e < ROWS * RP / 8; e += 256) {
+      const int r = e / (RP / 8), c = e % (RP / 8);
+      const u32x4 w = bload128(rlm, m0 + r < M ? ((m0 + r) * RP + 8 * c) * 2 : OOB);
+      *reinterpret_cast<u32x4*>(slm + r * RP + 8 * c) = w;
+    }
+    __syncthreads();
   }
-  __syncthreads();
-  float acc[SR_ROWS];
+  float acc[ROWS];
 #pragma unroll
-  for (int i = 0; i < SR_ROWS; ++i) {
+  for (int i = 0; i < ROWS; ++i) {
     acc[i] = 0.f;
 #pragma unroll
-    for (int k = 0; k < SR_NS; ++k) acc[i] += v[i][k];
+    for (int k = 0; k < NS; ++k) acc[i] += v[i][k];
   }
-  for (int sp0 = SR_NS; sp0 < S; sp0 += SR_NS) {
+  for (int sp0 = NS; sp0 < S; sp0 += NS) {
     load_batch(sp0, v);
 #pragma unroll
-    for (int i = 0; i < SR_ROWS; ++i)
+    for (int i = 0; i < ROWS; ++i)
 #pragma unroll
-      for (int k = 0; k < SR_NS; ++k) acc[i] += v[i][k];
+      for (int k = 0; k < NS; ++k) acc[i] += v[i][k];
   }
-  for (int c = 0; 8 * c < rp; ++c) {
-    u32x4 vc = vo[0];
+  if constexpr (RP > 0) {
+    // The lm rows are the same for every lane: they are read through an
+    // opaque lane offset of 0, so the compiler keeps them in vector
+    // registers (as uniform values it would hold them in scalar registers,
+    // and spill), and that offset is made to depend on the previous row's
+    // result, so each row's reads issue when that row is next (hoisted all
+    // at once, the 16 rows' reads took more registers than there are).
+    int z = 0;
+    float prev = 0.f;
 #pragma unroll
-    for (int q = 1; q < 16; ++q) vc = c == q ? vo[q] : vc;
-#pragma unroll
-    for (int i = 0; i < SR_ROWS; ++i) {
-      const u32x4 uw = *reinterpret_cast<const u32x4*>(slm + i * rp + 8 * c);
+    for (int i = 0; i < ROWS; ++i) {
+      asm volatile("" : "+v"(z) : "v"(prev));
+      const uint16_t* sl = slm + z;
       float s = acc[i];
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
-        s = __builtin_fmaf(bf16lo_to_f32(uw[w]), bf16lo_to_f32(vc[w]), s);
-        s = __builtin_fmaf(bf16hi_to_f32(uw[w]), bf16hi_to_f32(vc[w]), s);
+      for (int c = 0; c < RP / 8; ++c) {
+        const u32x4 uw = *reinterpret_cast<const u32x4*>(sl + i * RP + 8 * c);
+        // (an opaque copy: lo is unpacked row by row, not held unpacked)
+        u32x4 vc = vo[c];
+        asm volatile("" : "+v"(vc));
+#pragma unroll
+        for (int w = 0; w < 4; ++w) {
+          s = __builtin_fmaf(bf16lo_to_f32(uw[w]), bf16lo_to_f32(vc[w]), s);
+          s = __builtin_fmaf(bf16hi_to_f32(uw[w]), bf16hi_to_f32(vc[w]), s);
+        }
       }
       acc[i] = s;
+      prev = s;
     }
   }
   if (j >= NOUT) return;
 #pragma unroll
-  for (int i = 0; i < SR_ROWS; ++i)
+  for (int i = 0; i < ROWS; ++i)
     if (m0 + i < M) g.out[static_cast<uint64_t>(m0 + i) * NOUT + j] = f32_to_bf16_rne(acc[i]);
 }
 }  // namespace
@@ -1380,8 +1400,18 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     else if (g.b_transposed) hipLaunchKernelGGL((k_gemm_pipe<0, 3>), dim3(grid), dim3(256), 0, st, g);
     else hipLaunchKernelGGL((k_gemm_pipe<0, 0>), dim3(grid), dim3(256), 0, st, g);
     if (hipError_t e = hipGetLastError(); e != hipSuccess) return e;
-    const dim3 rgrid(static_cast<uint32_t>((g.NOUT + 255) / 256), static_cast<uint32_t>((g.M + SR_ROWS - 1) / SR_ROWS));
-    hipLaunchKernelGGL(k_split_reduce, rgrid, dim3(256), 0, st, g);
+    const bool few = g.M <= 64;
+    const int rows = few ? 4 : 16;
+    const dim3 rgrid(static_cast<uint32_t>((g.NOUT + 255) / 256), static_cast<uint32_t>((g.M + rows - 1) / rows));
+#define FT_SR(NL)                                                                        \
+  do {                                                                                   \
+    if (few) hipLaunchKernelGGL((k_split_reduce<NL, 4, 8>), rgrid, dim3(256), 0, st, g);  \
+    else hipLaunchKernelGGL((k_split_reduce<NL, 16, 2>), rgrid, dim3(256), 0, st, g);     \
+  } while (0)
+    if (g.nlr == 4) FT_SR(4);
+    else if (g.nlr == 2) FT_SR(2);
+    else FT_SR(0);
+#undef FT_SR
     return hipGetLastError();
   }
   if ((g.RED & 127) == 0 || (bf && (g.RED & 31) == 0)) {
