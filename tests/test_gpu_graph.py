@@ -10,7 +10,7 @@ import torch
 
 from bit_quantized_amd import ops, synth
 
-from _gpu import DEV, GpuCase, require_gpu, say
+from _gpu import DEV, GpuCase, require_gpu, say, up as _up
 
 pytestmark = pytest.mark.gpu
 
@@ -71,3 +71,61 @@ def test_graph_replays_match_eager(precision):
                                           ref[k].view(torch.int16).cpu().numpy(),
                                           err_msg=f"replay {r} {k}")
     say("graph replays bit-identical", precision)
+
+
+def test_graph_replays_mlp_fused():
+    """The MLP block's fused forward (FC1's GEMM making FC2's quantized GELU
+    input and down-projection sums) and both backwards in one graph: every
+    replay reproduces the eager result bit for bit."""
+    from bit_quantized_amd.layer import QuantizedLinear
+    G = ops.FT_ACT_GELU_TANH
+    M, K, F = 300, 256, 544
+    c1 = synth.flux_linear_case("graph_fc1", M, K, F, 16, 8, seed=21)
+    c2 = synth.flux_linear_case("graph_fc2", M, F, K, 16, 8, seed=22)
+    mk = lambda c, **kw: QuantizedLinear.from_factors(_up(c.W_res), _up(c.L1), _up(c.L2), _up(c.A),
+                                                      _up(c.B), **kw)
+    fc1, fc2 = mk(c1, act_out=G), mk(c2, act_in=G)
+    say("case graph mlp fused", (M, K, F))
+    X, dY = _up(c1.X), _up(c2.dY)
+    bt = lambda *sh: torch.empty(sh, dtype=torch.bfloat16, device=DEV)
+    b = dict(h=bt(M, F), U1=bt(M, fc1.R), Y=bt(M, K), U2=bt(M, fc2.R), dX2=bt(M, F),
+             dA2=bt(fc2.r_l, F), dB2=bt(fc2.r_l, K), dX1=bt(M, K), dA1=bt(fc1.r_l, K),
+             dB1=bt(fc1.r_l, F))
+    d1, d2 = fc1.desc(M), fc2.desc(M)
+    nm = ops.fourtune_mlp_workspace_bytes(d1, d2)
+    wm = torch.empty(nm, dtype=torch.uint8, device=DEV)
+    w1b, w2b = fc1.workspace(M, True), fc2.workspace(M, True)
+
+    def step():
+        ops.fourtune_mlp_fwd(d1, d2, X, b["h"], b["Y"], b["U1"], b["U2"], None, None, wm, nm)
+        ops.fourtune_linear_bwd(d2, dY, b["h"], b["U2"], None, b["dX2"], b["dA2"], b["dB2"],
+                                ops.FT_BF16, None, None, None, w2b, w2b.numel())
+        ops.fourtune_linear_bwd(d1, b["dX2"], X, b["U1"], b["h"], b["dX1"], b["dA1"], b["dB1"],
+                                ops.FT_BF16, None, None, None, w1b, w1b.numel())
+
+    step()
+    torch.cuda.synchronize()
+    ref = {k: v.clone() for k, v in b.items()}
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    other = GpuCase(synth.flux_linear_case("graph_mlp_other", 200, 256, 320, 8, 8, seed=23))
+    for r in range(4):
+        for t in b.values():
+            t.fill_(0.0)
+        other.run()                           # unrelated eager work between replays
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for k, v in b.items():
+            np.testing.assert_array_equal(v.view(torch.int16).cpu().numpy(),
+                                          ref[k].view(torch.int16).cpu().numpy(),
+                                          err_msg=f"replay {r} {k}")
+    say("mlp graph replays bit-identical")
