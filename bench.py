@@ -535,16 +535,22 @@ def main():
             ws = {k: (lay.workspace(Mm, False), lay.workspace(Mm, True)) for k, lay in (("1", fc1), ("2", fc2))}
             nmlp = ops.fourtune_mlp_workspace_bytes(fc1.desc(Mm), fc2.desc(Mm))
             ws["mlp"] = torch.empty(nmlp, dtype=torch.uint8, device=dev)
+            nmlpb = ops.fourtune_mlp_bwd_workspace_bytes(fc1.desc(Mm), fc2.desc(Mm))
+            ws["mlp_bwd"] = torch.empty(nmlpb, dtype=torch.uint8, device=dev)
             msets.append((fc1, fc2, X1, dY2, bufs, ws))
         del c1, c2
         torch.cuda.synchronize()
 
-        def mlp_step(i, fused=True):
+        # variants: 0 the two linears one after the other; 1 the MLP fusion of
+        # the pages (fourtune_mlp_fwd: FC1's GEMM epilogue makes FC2's quantized
+        # input and down-projection sums); 2 that and its mirror in the backward
+        # (fourtune_mlp_bwd: FC2's dgrad epilogue makes FC1's incoming gradient,
+        # its quantization and its down-projection sums)
+        def mlp_step(i, var=0):
             fc1, fc2, X1, dY2, b, ws = msets[i % len(msets)]
             d1, d2 = fc1.desc(Mm), fc2.desc(Mm)
             (w1f, w1b), (w2f, w2b) = ws["1"], ws["2"]
-            if fused:
-                # FC1's GEMM epilogue makes FC2's quantized input and down-projection partials
+            if var:
                 wm = ws["mlp"]
                 ops.fourtune_mlp_fwd(d1, d2, X1, b["h"], b["Y2"], b["U1"], b["U2"], None, None, wm,
                                      wm.numel(), stream)
@@ -552,55 +558,65 @@ def main():
                 ops.fourtune_linear_fwd(d1, X1, b["h"], b["U1"], None, None, w1f, w1f.numel(), stream)
                 ops.fourtune_linear_fwd(d2, b["h"], b["Y2"], b["U2"], None, None, w2f, w2f.numel(),
                                         stream)
-            ops.fourtune_linear_bwd(d2, dY2, b["h"], b["U2"], None, b["dX2"], b["dA2"], b["dB2"],
-                                    ops.FT_BF16, None, None, None, w2b, w2b.numel(), stream)
-            ops.fourtune_linear_bwd(d1, b["dX2"], X1, b["U1"], b["h"], b["dX1"], b["dA1"], b["dB1"],
-                                    ops.FT_BF16, None, None, None, w1b, w1b.numel(), stream)
+            if var == 2:
+                wmb = ws["mlp_bwd"]
+                ops.fourtune_mlp_bwd(d1, d2, dY2, X1, b["h"], b["U1"], b["U2"], b["dX1"], b["dA1"],
+                                     b["dB1"], b["dA2"], b["dB2"], ops.FT_BF16, wmb, wmb.numel(),
+                                     stream)
+            else:
+                ops.fourtune_linear_bwd(d2, dY2, b["h"], b["U2"], None, b["dX2"], b["dA2"], b["dB2"],
+                                        ops.FT_BF16, None, None, None, w2b, w2b.numel(), stream)
+                ops.fourtune_linear_bwd(d1, b["dX2"], X1, b["U1"], b["h"], b["dX1"], b["dA1"],
+                                        b["dB1"], ops.FT_BF16, None, None, None, w1b, w1b.numel(),
+                                        stream)
 
         nst = max(5, a.steps // 5)
         for i in range(3):
-            mlp_step(i)
-            mlp_step(i, fused=False)
+            for var in range(3):
+                mlp_step(i, var)
         torch.cuda.synchronize()
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        # fused and unfused forwards in alternating rounds (median per variant),
-        # so that clock drift favours neither
-        t_var = {True: [], False: []}
+        # the variants in rotating order over rounds (median per variant), so
+        # that clock drift favours none
+        t_var = {0: [], 1: [], 2: []}
         for rnd in range(6):
-            for fz in ((True, False) if rnd % 2 == 0 else (False, True)):
+            for k in range(3):
+                var = (rnd + k) % 3
                 e0.record(stream)
                 for i in range(nst):
-                    mlp_step(i, fused=fz)
+                    mlp_step(i, var)
                 e1.record(stream)
                 torch.cuda.synchronize()
-                t_var[fz].append(e0.elapsed_time(e1) / nst)
-        mms_fused = statistics.median(t_var[True])
-        mms = statistics.median(t_var[False])
+                t_var[var].append(e0.elapsed_time(e1) / nst)
+        mms = statistics.median(t_var[0])
+        mms_fused = statistics.median(t_var[1])
+        mms_both = statistics.median(t_var[2])
         w1 = layer_work(Mm, Km, Fm, rsm, rlm)
         w2 = layer_work(Mm, Fm, Km, rsm, rlm)
         mflop = sum(v["flop"] for v in w1.values()) + sum(v["flop"] for v in w2.values())
         per_var = {}
-        for fz in (True, False):
+        for var in range(3):
             ops.fourtune_timing_reset()
             ops.fourtune_timing_enable(True)
             for i in range(nst):
-                mlp_step(i, fused=fz)
+                mlp_step(i, var)
             torch.cuda.synchronize()
             ops.fourtune_timing_enable(False)
-            per_var[fz] = {k: round(tot / cnt * 1e3, 2)
-                           for k, (tot, cnt) in ops.fourtune_timing_read().items() if cnt}
+            per_var[var] = {k: round(tot / cnt * 1e3, 2)
+                            for k, (tot, cnt) in ops.fourtune_timing_read().items() if cnt}
         out["mlp_pair"] = {
             "workload": f"FLUX MLP pair fwd+bwd: {Mm} tokens, {Km}->{Fm} -> tanh-GELU -> {Fm}->{Km}, "
                         f"r_stab={rsm}, r_lora={rlm}; GELU applied inside the quantizers and the "
                         f"adapter-gradient kernel",
             "us_per_step": round(mms * 1e3, 1), "TFLOP/s": round(mflop / (mms * 1e-3) / 1e12, 1),
             "step_flop": mflop, "steps": nst,
-            # the same step with the forward's MLP fusion (fourtune_mlp_fwd: FC1's
-            # GEMM epilogue makes FC2's quantized input and down-projection sums)
             "mlp_fused_us_per_step": round(mms_fused * 1e3, 1),
             "mlp_fusion_speedup": round(mms / mms_fused, 3),
-            "kernel_avg_us_both_linears": per_var[False],
-            "kernel_avg_us_both_linears_mlp_fused": per_var[True]}
+            "mlp_fused_fwd_bwd_us_per_step": round(mms_both * 1e3, 1),
+            "mlp_fused_fwd_bwd_speedup": round(mms / mms_both, 3),
+            "kernel_avg_us_both_linears": per_var[0],
+            "kernel_avg_us_both_linears_mlp_fused": per_var[1],
+            "kernel_avg_us_both_linears_mlp_fused_fwd_bwd": per_var[2]}
         log("bench: mlp", json.dumps(out["mlp_pair"]))
         del msets
         torch.cuda.empty_cache()
@@ -717,13 +733,17 @@ def main():
             by[st_ + "_fc1"]["dY"] = by[st_ + "_fc2"]["dX"]
         torch.cuda.synchronize()
 
-        mlp_ws = {}
+        mlp_ws, mlp_wsb = {}, {}
         for st_ in ("img", "txt"):
             f1, f2 = by[st_ + "_fc1"], by[st_ + "_fc2"]
-            n_ = ops.fourtune_mlp_workspace_bytes(f1["lay"].desc(f1["M"]), f2["lay"].desc(f2["M"]))
+            dd1, dd2 = f1["lay"].desc(f1["M"]), f2["lay"].desc(f2["M"])
+            n_ = ops.fourtune_mlp_workspace_bytes(dd1, dd2)
             mlp_ws[st_] = torch.empty(n_, dtype=torch.uint8, device=dev)
+            n_ = ops.fourtune_mlp_bwd_workspace_bytes(dd1, dd2)
+            mlp_wsb[st_] = torch.empty(n_, dtype=torch.uint8, device=dev)
 
-        def block_step(mlp_fused=False):
+        # mlp_fused: 1 the forward MLP fusion, 2 also its mirror in the backward
+        def block_step(mlp_fused=0):
             for e in blk:
                 nm = e["name"]
                 if mlp_fused and nm.endswith("fc2"):
@@ -738,28 +758,41 @@ def main():
                 ops.fourtune_linear_fwd(d, e["X"], e["Y"], e["U"], None, None, e["wf"], e["wf"].numel(),
                                         stream)
             for e in reversed(blk):
+                nm = e["name"]
+                if mlp_fused == 2 and nm.endswith("fc1"):
+                    continue                      # made together with its fc2 below
+                if mlp_fused == 2 and nm.endswith("fc2"):
+                    e1 = by[nm[:4] + "fc1"]
+                    w_ = mlp_wsb[nm[:3]]
+                    ops.fourtune_mlp_bwd(e1["lay"].desc(e1["M"]), e["lay"].desc(e["M"]), e["dY"],
+                                         e1["X"], e1["Y"], e1["U"], e["U"], e1["dX"], e1["dA"],
+                                         e1["dB"], e["dA"], e["dB"], ops.FT_BF16, w_, w_.numel(),
+                                         stream)
+                    continue
                 d = e["lay"].desc(e["M"])
-                H = by[e["name"][:4] + "fc1"]["Y"] if e["name"].endswith("fc1") else None
+                H = by[nm[:4] + "fc1"]["Y"] if nm.endswith("fc1") else None
                 ops.fourtune_linear_bwd(d, e["dY"], e["X"], e["U"], H, e["dX"], e["dA"], e["dB"],
                                         ops.FT_BF16, None, None, None, e["wb"], e["wb"].numel(), stream)
 
         for _ in range(2):
-            block_step()
-            block_step(mlp_fused=True)
+            for v_ in range(3):
+                block_step(mlp_fused=v_)
         torch.cuda.synchronize()
         nst = max(3, a.steps // 10)
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        t_blk = {False: [], True: []}
+        t_blk = {0: [], 1: [], 2: []}
         for rnd in range(4):
-            for fz in ((False, True) if rnd % 2 == 0 else (True, False)):
+            for k_ in range(3):
+                v_ = (rnd + k_) % 3
                 e0.record(stream)
                 for _ in range(nst):
-                    block_step(mlp_fused=fz)
+                    block_step(mlp_fused=v_)
                 e1.record(stream)
                 torch.cuda.synchronize()
-                t_blk[fz].append(e0.elapsed_time(e1) / nst)
-        bms = statistics.median(t_blk[False])
-        bms_all = statistics.median(t_blk[True])
+                t_blk[v_].append(e0.elapsed_time(e1) / nst)
+        bms = statistics.median(t_blk[0])
+        bms_all = statistics.median(t_blk[1])
+        bms_all2 = statistics.median(t_blk[2])
         # each linear on its own: fwd and bwd, event-timed over the same
         # number of repetitions (the modulation linears run the split GEMMs)
         per_lin = {}
@@ -824,6 +857,7 @@ def main():
             "unfused_us": round(ums * 1e3, 1),
             "lora_fused_us": round(bms * 1e3, 1),
             "all_fused_us": round(bms_all * 1e3, 1),
+            "all_fused_with_mirrored_backward_us": round(bms_all2 * 1e3, 1),
             "lora_fusion_speedup": round(ums / bms, 3),
             "mlp_fusion_speedup": round(bms / bms_all, 3),
             "all_fusion_speedup": round(ums / bms_all, 3)}

@@ -18,7 +18,8 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libfourtune.so")
-SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "lora.hip", "act.hip", "scratch.hip"]
+SOURCES = ["api.cpp", "quantize.hip", "gemm.hip", "gemm_mlp.hip", "lora.hip", "act.hip",
+           "scratch.hip"]
 ARCH = "gfx950"
 
 COMMON = [

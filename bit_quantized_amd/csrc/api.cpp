@@ -316,6 +316,135 @@ ft_status fwd_run(const ft_linear* L, const uint16_t* X, uint16_t* Y, uint16_t* 
   return launched(tm.done(ft::launch_gemm(g, st)));
 }
 
+// Hooks of the MLP block's fused backward (fourtune_mlp_bwd).
+// On the second linear: epi and h: its dgrad's epilogue writes dY1 (to dX)
+// and makes the first linear's quantized dY1 and P1 partial sums.
+// On the first linear: k1_done: those are in place; dB is formed from
+// db_big = dY1 by the adapter-gradient kernel, its partials in db_part.
+struct BwdHook {
+  const MlpEpi* epi;
+  const uint16_t* h;
+  bool k1_done;
+  const uint16_t* db_big;
+  float* db_part;
+};
+
+// The backward's kernels after the checks.
+ft_status bwd_run(const ft_linear* L, const uint16_t* dY, const uint16_t* X,
+                  const uint16_t* U_save, const uint16_t* H, uint16_t* dX, void* dA, void* dB,
+                  ft_dtype grad_dtype, uint16_t* P_save, uint8_t* gq_codes, uint8_t* gq_scales,
+                  uint8_t* ws, const BwdLayout& lay, hipStream_t st, const BwdHook* hook) {
+  const int R = L->r_stab + L->r_lora;
+  const int rl = L->r_lora;
+  const bool bf = g16(L);
+  // G16: no codes; the quantize stores of kernel 1 are dropped
+  uint8_t* qc = bf ? nullptr : gq_codes ? gq_codes : ws + lay.gq_codes;
+  uint8_t* qs = bf ? nullptr : gq_scales ? gq_scales : ws + lay.gq_scales;
+  uint16_t* P = P_save ? P_save : reinterpret_cast<uint16_t*>(ws + lay.P);
+  uint16_t* p_pad = reinterpret_cast<uint16_t*>(ws + lay.p_pad);
+  uint16_t* d_pad = reinterpret_cast<uint16_t*>(ws + lay.d_pad);
+  hipError_t e = hipSuccess;
+  // the first linear of a fused MLP backward: kernel 1's results come from
+  // the second linear's dgrad and the partial sums' kernel, and dB is
+  // formed by the adapter-gradient kernel from dY1
+  const bool k1 = !(hook && hook->k1_done);
+  const bool db_fused = k1 && db_fused_in_quant(L);
+  ft::DbFuse db{U_save, R, L->r_stab, rl, reinterpret_cast<float*>(ws + lay.dB_part)};
+  // act_out: dY is the gradient of gelu(Y) and H the saved Y; the incoming
+  // gradient of this layer is dY * gelu'(H)
+  const int act = L->act_out == FT_ACT_GELU_TANH ? 2 : 0;
+  const uint16_t* h2 = act ? H : nullptr;
+  if (!k1) {
+    // (made by the second linear's dgrad epilogue and the partial sums' kernel)
+  } else if (R > 0) {
+    Timed tm("bwd_quant_down", st);
+    // the pipelined dgrad on the forward's tiles (N % 128 == 0, 4-bit)
+    // reads [L1 | A] as nibble planes through its transposing b read
+    // (not when the dgrad splits its reduction: the split sums' kernel
+    // reads the plain [K, ranks] copy)
+    const bool planes = L->w_block == FT_WBLOCK_TILE32 && !bf && (L->N % 128) == 0 &&
+                        ft::gemm_split_plan(L->M, L->N, L->K).splits <= 1;
+    e = tm.done(ft::launch_quant_down(dY, h2, act, L->M, L->N, L->N, qc, qs, rows_V(L), P, p_pad,
+                                      rows_Dt(L), dX ? L->K : 0, d_pad,
+                                      reinterpret_cast<float*>(ws + lay.part),
+                                      db_fused ? &db : nullptr, st, planes));
+  } else if (!bf) {
+    Timed tm("bwd_quant_down", st);
+    e = tm.done(ft::launch_quant_row32(dY, h2, act, L->M, L->N, L->N, qc, qs, st));
+  }
+  if (e != hipSuccess) return FT_EDEVICE;
+  if (dX) {
+    ft::GemmArgs g{};
+    g.M = L->M; g.RED = L->N; g.NOUT = L->K;
+    g.a_codes = qc; g.a_scales = qs;
+    if (L->w_block == FT_WBLOCK_TILE32) {
+      // the forward's tiles [N, K/2], read transposed (section 3.2)
+      g.b_codes = L->w_codes; g.b_scales = L->w_scales;
+      g.b_transposed = 1;
+    } else {
+      g.b_codes = L->wt_codes; g.b_scales = L->wt_scales;
+      g.b_row_scales = L->w_block == FT_WBLOCK_ROW32;
+    }
+    g.lm = p_pad; g.lo = d_pad; g.nlr = ft::rank_pad(R) / 32; g.out = dX;
+    if (!bf) {
+      const ft::SplitPlan sp = ft::gemm_split_plan(L->M, L->N, L->K);
+      g.splits = sp.splits; g.split_pairs = sp.pairs;
+      g.part = reinterpret_cast<float*>(ws + lay.sk_part);
+    }
+    if (bf) {
+      uint16_t* w16 = reinterpret_cast<uint16_t*>(ws + lay.w16);
+      {
+        Timed tm("bwd_dequant_w", st);
+        const hipError_t de =
+            L->w_block == FT_WBLOCK_TILE32
+                ? ft::launch_dequant_tile32_t(L->w_codes, L->w_scales, L->N, L->K, w16, st)
+                : ft::launch_dequant_tile32(L->wt_codes, L->wt_scales, L->K, L->N, w16, st);
+        if (tm.done(de) != hipSuccess) return FT_EDEVICE;
+      }
+      g.b_transposed = 0;
+      const uint16_t* g16p = dY;
+      if (act) {
+        uint16_t* ga = reinterpret_cast<uint16_t*>(ws + lay.g16);
+        Timed tm("bwd_act", st);
+        if (tm.done(ft::launch_act(2, H, dY, L->M * L->N, ga, st)) != hipSuccess) return FT_EDEVICE;
+        g16p = ga;
+      }
+      g.a16 = g16p; g.b16 = w16;
+    }
+    if (hook && hook->epi) {
+      // the second linear of a fused MLP backward: dX here is dY1
+      const MlpEpi* ep = hook->epi;
+      g.e_codes = ep->codes; g.e_scales = ep->scales; g.e_part = ep->part;
+      g.e_pr = ep->pr; g.e_R = ep->R; g.e_nrg = ep->nrg; g.e_h = hook->h;
+    }
+    Timed tm(hook && hook->epi ? "bwd_gemm_dgrad_mlp" : "bwd_gemm_dgrad", st);
+    if (tm.done(ft::launch_gemm(g, st)) != hipSuccess) return FT_EDEVICE;
+  }
+  if (rl > 0) {
+    const int f32 = grad_dtype == FT_F32 ? 1 : 0;
+    ft::LoraGradArgs a{};
+    a.M = L->M; a.I = L->K; a.big = X; a.small = P; a.ld_small = R; a.r0 = L->r_stab; a.rl = rl;
+    a.big2 = nullptr; a.act = L->act_in == FT_ACT_GELU_TANH ? 1 : 0;
+    a.out = dA; a.out_f32 = f32;
+    a.part = reinterpret_cast<float*>(ws + lay.dA_part);
+    ft::LoraGradArgs b = a;
+    b.I = L->N; b.big = dY; b.small = U_save;
+    b.big2 = L->act_out == FT_ACT_GELU_TANH ? H : nullptr;
+    b.act = L->act_out == FT_ACT_GELU_TANH ? 2 : 0;
+    b.out = dB;
+    b.part = reinterpret_cast<float*>(ws + lay.dB_part);
+    if (!k1) {
+      // dY1 = dY * gelu'(H) is already formed
+      b.big = hook->db_big; b.big2 = nullptr; b.act = 0;
+      b.part = hook->db_part;
+    }
+    b.nchunk = db_fused ? ft::quant_down_db_chunks(L->M, L->N, R, rl) : 0;
+    Timed tm("bwd_lora_grads", st);
+    if (tm.done(ft::launch_lora_grads(a, b, db_fused, st)) != hipSuccess) return FT_EDEVICE;
+  }
+  return FT_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -475,6 +604,90 @@ ft_status fourtune_mlp_fwd(const ft_linear* fc1, const ft_linear* fc2, const uin
   return fwd_run(fc2, H, Y, U2_save, qc2, qs2, ws2, l2, st, false, nullptr);
 }
 
+size_t fourtune_mlp_bwd_workspace_bytes(const ft_linear* fc1, const ft_linear* fc2) {
+  const size_t a = fourtune_workspace_bytes(fc1, 1), b = fourtune_workspace_bytes(fc2, 1);
+  if (!a || !b) return 0;
+  // dY1 (or, unfused, dX2) [M, N1] bf16 and the first linear's dB partials
+  // when the adapter-gradient kernel forms dB
+  const size_t dy = align_up(static_cast<size_t>(fc1->M) * fc1->N * 2);
+  const size_t dbp = fc1->r_lora ? align_up(ft::lora_grad_part_bytes(fc1->M, fc1->N, fc1->r_lora)) : 0;
+  return a + b + dy + dbp;
+}
+
+ft_status fourtune_mlp_bwd(const ft_linear* fc1, const ft_linear* fc2, const uint16_t* dY,
+                           const uint16_t* X, const uint16_t* H, const uint16_t* U1_save,
+                           const uint16_t* U2_save, uint16_t* dX, void* dA1, void* dB1, void* dA2,
+                           void* dB2, ft_dtype grad_dtype, void* workspace, size_t ws_bytes,
+                           void* stream) {
+  if (ft_status s = check_linear(fc1); s != FT_OK) return s;
+  if (ft_status s = check_linear(fc2); s != FT_OK) return s;
+  if (fc2->M != fc1->M || fc2->K != fc1->N) return FT_ESHAPE;
+  if (fc2->act_in != FT_ACT_GELU_TANH || fc1->act_out != FT_ACT_GELU_TANH) return FT_EINVAL;
+  if (grad_dtype != FT_BF16 && grad_dtype != FT_F32) return FT_EINVAL;
+  if (!dY || !X || !H || !dX) return FT_EINVAL;
+  if (fc1->w_block != FT_WBLOCK_TILE32 && !fc1->wt_codes) return FT_EINVAL;
+  if (fc2->w_block != FT_WBLOCK_TILE32 && !fc2->wt_codes) return FT_EINVAL;
+  const int R1 = fc1->r_stab + fc1->r_lora, R2 = fc2->r_stab + fc2->r_lora;
+  if ((R1 > 0 && !U1_save) || (R2 > 0 && !U2_save)) return FT_EINVAL;
+  if ((fc1->r_lora > 0 && (!dA1 || !dB1)) || (fc2->r_lora > 0 && (!dA2 || !dB2))) return FT_EINVAL;
+  const void* ptrs[] = {dY, X, H, U1_save, U2_save, dX, dA1, dB1, dA2, dB2, workspace};
+  for (const void* p : ptrs)
+    if (p && !aligned16(p)) return FT_EALIGN;
+  const BwdLayout l1 = bwd_layout(fc1), l2 = bwd_layout(fc2);
+  const int64_t M = fc1->M, F = fc1->N;
+  const size_t dy_bytes = align_up(static_cast<size_t>(M) * F * 2);
+  const size_t dbp_bytes = fc1->r_lora ? align_up(ft::lora_grad_part_bytes(M, F, fc1->r_lora)) : 0;
+  if (ws_bytes < l1.total + l2.total + dy_bytes + dbp_bytes) return FT_EWORKSPACE;
+  if (!workspace) return FT_EINVAL;
+  if (ft_status s = device_check(); s != FT_OK) return s;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  uint8_t* ws1 = static_cast<uint8_t*>(workspace);
+  uint8_t* ws2 = ws1 + l1.total;
+  uint16_t* dy1 = reinterpret_cast<uint16_t*>(ws2 + l2.total);
+  float* dbp = reinterpret_cast<float*>(ws2 + l2.total + dy_bytes);
+  // the first linear's P1 partial sums per 256-column split of dY1
+  const int64_t nsplit = (F + 255) / 256;
+  const int nrg = ft::rank_reduce_nrg(R1);
+  const bool fused = !a16(fc1) && !g16(fc1) && !a16(fc2) && !g16(fc2) &&
+                     fc2->w_block == FT_WBLOCK_TILE32 && (fc2->N % 128) == 0 && M > 16 && R1 <= 64 &&
+                     ft::gemm_split_plan(M, fc2->N, F).splits <= 1 &&
+                     nsplit * ((M + 63) / 64) * 4 * nrg * 1024 <= kMaxBytes;
+  if (!fused) {
+    // the two backwards one after the other, through dX2 [M, N1]
+    if (ft_status s = bwd_run(fc2, dY, H, U2_save, nullptr, dy1, dA2, dB2, grad_dtype, nullptr,
+                              nullptr, nullptr, ws2, l2, st, nullptr);
+        s != FT_OK)
+      return s;
+    return bwd_run(fc1, dy1, X, U1_save, H, dX, dA1, dB1, grad_dtype, nullptr, nullptr, nullptr,
+                   ws1, l1, st, nullptr);
+  }
+  // the second linear, its dgrad making dY1, Qrow(dY1) and the P1 partials
+  const MlpEpi epi{ws1 + l1.gq_codes, ws1 + l1.gq_scales, reinterpret_cast<float*>(ws1 + l1.part),
+                   rows_V(fc1), R1, nrg};
+  const BwdHook h2{&epi, H, false, nullptr, nullptr};
+  if (ft_status s = bwd_run(fc2, dY, H, U2_save, nullptr, dy1, dA2, dB2, grad_dtype, nullptr,
+                            nullptr, nullptr, ws2, l2, st, &h2);
+      s != FT_OK)
+    return s;
+  if (R1 > 0) {
+    // P1 and its padded copy, and the first linear's [L1 | A] for its dgrad
+    // (as nibble planes where that dgrad reads its b transposed in one pass)
+    const bool planes = fc1->w_block == FT_WBLOCK_TILE32 && (F % 128) == 0 &&
+                        ft::gemm_split_plan(M, F, fc1->K).splits <= 1;
+    Timed tm("bwd_rank_reduce", st);
+    if (tm.done(ft::launch_rank_reduce(reinterpret_cast<float*>(ws1 + l1.part), M,
+                                       static_cast<int>(nsplit), R1,
+                                       reinterpret_cast<uint16_t*>(ws1 + l1.P),
+                                       reinterpret_cast<uint16_t*>(ws1 + l1.p_pad), rows_Dt(fc1),
+                                       fc1->K, reinterpret_cast<uint16_t*>(ws1 + l1.d_pad), st,
+                                       planes)) != hipSuccess)
+      return FT_EDEVICE;
+  }
+  const BwdHook h1{nullptr, nullptr, true, dy1, dbp};
+  return bwd_run(fc1, dy1, X, U1_save, H, dX, dA1, dB1, grad_dtype, nullptr, nullptr, nullptr, ws1,
+                 l1, st, &h1);
+}
+
 ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint16_t* X,
                               const uint16_t* U_save, const uint16_t* H, uint16_t* dX, void* dA, void* dB,
                               ft_dtype grad_dtype, uint16_t* P_save, uint8_t* gq_codes,
@@ -500,98 +713,8 @@ ft_status fourtune_linear_bwd(const ft_linear* L, const uint16_t* dY, const uint
   if (!workspace) return FT_EINVAL;
   if (ft_status s = device_check(); s != FT_OK) return s;
 
-  hipStream_t st = static_cast<hipStream_t>(stream);
-  uint8_t* ws = static_cast<uint8_t*>(workspace);
-  const bool bf = g16(L);
-  // G16: no codes; the quantize stores of kernel 1 are dropped
-  uint8_t* qc = bf ? nullptr : gq_codes ? gq_codes : ws + lay.gq_codes;
-  uint8_t* qs = bf ? nullptr : gq_scales ? gq_scales : ws + lay.gq_scales;
-  uint16_t* P = P_save ? P_save : reinterpret_cast<uint16_t*>(ws + lay.P);
-  uint16_t* p_pad = reinterpret_cast<uint16_t*>(ws + lay.p_pad);
-  uint16_t* d_pad = reinterpret_cast<uint16_t*>(ws + lay.d_pad);
-  hipError_t e = hipSuccess;
-  const bool db_fused = db_fused_in_quant(L);
-  ft::DbFuse db{U_save, R, L->r_stab, rl, reinterpret_cast<float*>(ws + lay.dB_part)};
-  // act_out: dY is the gradient of gelu(Y) and H the saved Y; the incoming
-  // gradient of this layer is dY * gelu'(H)
-  const int act = L->act_out == FT_ACT_GELU_TANH ? 2 : 0;
-  const uint16_t* h2 = act ? H : nullptr;
-  if (R > 0) {
-    Timed tm("bwd_quant_down", st);
-    // the pipelined dgrad on the forward's tiles (N % 128 == 0, 4-bit)
-    // reads [L1 | A] as nibble planes through its transposing b read
-    // (not when the dgrad splits its reduction: the split sums' kernel
-    // reads the plain [K, ranks] copy)
-    const bool planes = L->w_block == FT_WBLOCK_TILE32 && !bf && (L->N % 128) == 0 &&
-                        ft::gemm_split_plan(L->M, L->N, L->K).splits <= 1;
-    e = tm.done(ft::launch_quant_down(dY, h2, act, L->M, L->N, L->N, qc, qs, rows_V(L), P, p_pad,
-                                      rows_Dt(L), dX ? L->K : 0, d_pad,
-                                      reinterpret_cast<float*>(ws + lay.part),
-                                      db_fused ? &db : nullptr, st, planes));
-  } else if (!bf) {
-    Timed tm("bwd_quant_down", st);
-    e = tm.done(ft::launch_quant_row32(dY, h2, act, L->M, L->N, L->N, qc, qs, st));
-  }
-  if (e != hipSuccess) return FT_EDEVICE;
-  if (dX) {
-    ft::GemmArgs g{};
-    g.M = L->M; g.RED = L->N; g.NOUT = L->K;
-    g.a_codes = qc; g.a_scales = qs;
-    if (L->w_block == FT_WBLOCK_TILE32) {
-      // the forward's tiles [N, K/2], read transposed (section 3.2)
-      g.b_codes = L->w_codes; g.b_scales = L->w_scales;
-      g.b_transposed = 1;
-    } else {
-      g.b_codes = L->wt_codes; g.b_scales = L->wt_scales;
-      g.b_row_scales = L->w_block == FT_WBLOCK_ROW32;
-    }
-    g.lm = p_pad; g.lo = d_pad; g.nlr = ft::rank_pad(R) / 32; g.out = dX;
-    if (!bf) {
-      const ft::SplitPlan sp = ft::gemm_split_plan(L->M, L->N, L->K);
-      g.splits = sp.splits; g.split_pairs = sp.pairs;
-      g.part = reinterpret_cast<float*>(ws + lay.sk_part);
-    }
-    if (bf) {
-      uint16_t* w16 = reinterpret_cast<uint16_t*>(ws + lay.w16);
-      {
-        Timed tm("bwd_dequant_w", st);
-        const hipError_t de =
-            L->w_block == FT_WBLOCK_TILE32
-                ? ft::launch_dequant_tile32_t(L->w_codes, L->w_scales, L->N, L->K, w16, st)
-                : ft::launch_dequant_tile32(L->wt_codes, L->wt_scales, L->K, L->N, w16, st);
-        if (tm.done(de) != hipSuccess) return FT_EDEVICE;
-      }
-      g.b_transposed = 0;
-      const uint16_t* g16p = dY;
-      if (act) {
-        uint16_t* ga = reinterpret_cast<uint16_t*>(ws + lay.g16);
-        Timed tm("bwd_act", st);
-        if (tm.done(ft::launch_act(2, H, dY, L->M * L->N, ga, st)) != hipSuccess) return FT_EDEVICE;
-        g16p = ga;
-      }
-      g.a16 = g16p; g.b16 = w16;
-    }
-    Timed tm("bwd_gemm_dgrad", st);
-    if (tm.done(ft::launch_gemm(g, st)) != hipSuccess) return FT_EDEVICE;
-  }
-  if (rl > 0) {
-    const int f32 = grad_dtype == FT_F32 ? 1 : 0;
-    ft::LoraGradArgs a{};
-    a.M = L->M; a.I = L->K; a.big = X; a.small = P; a.ld_small = R; a.r0 = L->r_stab; a.rl = rl;
-    a.big2 = nullptr; a.act = L->act_in == FT_ACT_GELU_TANH ? 1 : 0;
-    a.out = dA; a.out_f32 = f32;
-    a.part = reinterpret_cast<float*>(ws + lay.dA_part);
-    ft::LoraGradArgs b = a;
-    b.I = L->N; b.big = dY; b.small = U_save;
-    b.big2 = L->act_out == FT_ACT_GELU_TANH ? H : nullptr;
-    b.act = L->act_out == FT_ACT_GELU_TANH ? 2 : 0;
-    b.out = dB;
-    b.part = reinterpret_cast<float*>(ws + lay.dB_part);
-    b.nchunk = db_fused ? ft::quant_down_db_chunks(L->M, L->N, R, rl) : 0;
-    Timed tm("bwd_lora_grads", st);
-    if (tm.done(ft::launch_lora_grads(a, b, db_fused, st)) != hipSuccess) return FT_EDEVICE;
-  }
-  return FT_OK;
+  return bwd_run(L, dY, X, U_save, H, dX, dA, dB, grad_dtype, P_save, gq_codes, gq_scales,
+                 static_cast<uint8_t*>(workspace), lay, static_cast<hipStream_t>(stream), nullptr);
 }
 
 ft_status fourtune_linear_fwd_noalloc(const ft_linear* L, const uint16_t* X, uint16_t* Y,

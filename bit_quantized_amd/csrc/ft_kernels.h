@@ -125,13 +125,21 @@ struct GemmArgs {
   // rank-major, e_R ranks of NOUT values; e_nrg = rank_reduce_nrg(e_R)
   // (0 when e_R == 0: codes and scales only).  Pipelined kernel, b as
   // 32x32 tiles, no split (gemm_mlp_ok).
+  // e_h set (the backward mirror, on the dgrad of the second linear with b
+  // read transposed): the output is written as dY1 = bf16(acc gelu'(h))
+  // with h = e_h [M, NOUT] (the first linear's saved output), and dY1 is
+  // what is quantized and projected (e_pr: the first linear's V1).
   uint8_t* e_codes;
   uint8_t* e_scales;
   float* e_part;
   RankRows e_pr;
   int e_R, e_nrg;
+  const uint16_t* e_h;
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+// The fused-epilogue instantiations (g.e_codes set), gemm_mlp.hip;
+// launch_gemm hands such calls over.
+hipError_t launch_gemm_mlp(const GemmArgs& g, hipStream_t st);
 // The split plan of a 4-bit product [M, RED] x [RED, NOUT] (RED % 128 == 0):
 // splits > 1 when the output has at most 128 tiles of 256 x 256 and the
 // shorter units outweigh the traffic of their sums (gemm.hip); fixed by the

@@ -192,6 +192,32 @@ def mlp_forward(fc1: QuantizedLinear, fc2: QuantizedLinear, X: torch.Tensor, str
     return (H, U1, Y, U2, qc, qs) if want_codes else (H, U1, Y, U2)
 
 
+def mlp_backward(fc1: QuantizedLinear, fc2: QuantizedLinear, dY: torch.Tensor, X: torch.Tensor,
+                 H: torch.Tensor, U1: torch.Tensor, U2: torch.Tensor, grad_f32: bool = False,
+                 stream=None):
+    """The MLP block's backward with FC2's input-gradient GEMM making FC1's
+    incoming gradient and its quantization (fourtune_mlp_bwd); fc1 must have
+    act_out = GELU and fc2 act_in = GELU.  Returns (dX, dA1t, dB1, dA2t, dB2)."""
+    M = int(dY.shape[0])
+    dev = fc1.device
+    gdt = torch.float32 if grad_f32 else torch.bfloat16
+    dX = _empty((M, fc1.K), torch.bfloat16, dev)
+    dA1 = _empty((fc1.r_l, fc1.K), gdt, dev) if fc1.r_l else None
+    dB1 = _empty((fc1.r_l, fc1.N), gdt, dev) if fc1.r_l else None
+    dA2 = _empty((fc2.r_l, fc2.K), gdt, dev) if fc2.r_l else None
+    dB2 = _empty((fc2.r_l, fc2.N), gdt, dev) if fc2.r_l else None
+    d1, d2 = fc1.desc(M), fc2.desc(M)
+    key = (id(fc1), id(fc2), M, "bwd")
+    if key not in _mlp_ws:
+        n = ops.fourtune_mlp_bwd_workspace_bytes(d1, d2)
+        _mlp_ws[key] = _empty((max(n, 256),), torch.uint8, dev)
+    ws = _mlp_ws[key]
+    ops.fourtune_mlp_bwd(d1, d2, dY, X, H, U1 if fc1.R else None, U2 if fc2.R else None, dX, dA1,
+                         dB1, dA2, dB2, ops.FT_F32 if grad_f32 else ops.FT_BF16, ws, ws.numel(),
+                         stream)
+    return dX, dA1, dB1, dA2, dB2
+
+
 class FourTuneLinearFunction(torch.autograd.Function):
     """Y = layer(X) with gradients for X, At and B (W_res, L1, L2 frozen).
     At and B must be the tensors the layer holds.  With the layer's act_in,

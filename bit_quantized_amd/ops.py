@@ -27,7 +27,8 @@ PRECISION_NAMES = {"W4A4G4": FT_W4A4G4, "W4A16G4": FT_W4A16G4, "W4A4G16": FT_W4A
 
 EXPORTS = ("fourtune_quantize", "fourtune_dequantize", "fourtune_workspace_bytes", "fourtune_linear_fwd",
            "fourtune_linear_fwd_noalloc", "fourtune_linear_bwd", "fourtune_mlp_workspace_bytes",
-           "fourtune_mlp_fwd", "fourtune_act_fwd", "fourtune_act_bwd",
+           "fourtune_mlp_fwd", "fourtune_mlp_bwd_workspace_bytes", "fourtune_mlp_bwd",
+           "fourtune_act_fwd", "fourtune_act_bwd",
            "fourtune_status_string", "fourtune_timing_enable", "fourtune_timing_reset",
            "fourtune_timing_read")
 
@@ -80,6 +81,11 @@ def lib() -> ctypes.CDLL:
         L.fourtune_mlp_fwd.argtypes = [ctypes.POINTER(FtLinear), ctypes.POINTER(FtLinear), vp, vp, vp,
                                        vp, vp, vp, vp, vp, ctypes.c_size_t, vp]
         L.fourtune_mlp_fwd.restype = st
+        L.fourtune_mlp_bwd_workspace_bytes.argtypes = [ctypes.POINTER(FtLinear), ctypes.POINTER(FtLinear)]
+        L.fourtune_mlp_bwd_workspace_bytes.restype = ctypes.c_size_t
+        L.fourtune_mlp_bwd.argtypes = [ctypes.POINTER(FtLinear), ctypes.POINTER(FtLinear), vp, vp, vp,
+                                       vp, vp, vp, vp, vp, vp, vp, st, vp, ctypes.c_size_t, vp]
+        L.fourtune_mlp_bwd.restype = st
         L.fourtune_act_fwd.argtypes = [st, vp, i64, vp, vp]
         L.fourtune_act_fwd.restype = st
         L.fourtune_act_bwd.argtypes = [st, vp, vp, i64, vp, vp]
@@ -195,6 +201,19 @@ def fourtune_mlp_fwd(fc1: FtLinear, fc2: FtLinear, X, H, Y, U1_save, U2_save, aq
                                _ptr(U1_save), _ptr(U2_save), _ptr(aq_codes), _ptr(aq_scales),
                                _ptr(workspace), int(ws_bytes), _stream(stream))
     _check(s, "fourtune_mlp_fwd")
+
+
+def fourtune_mlp_bwd_workspace_bytes(fc1: FtLinear, fc2: FtLinear) -> int:
+    return int(lib().fourtune_mlp_bwd_workspace_bytes(ctypes.byref(fc1), ctypes.byref(fc2)))
+
+
+def fourtune_mlp_bwd(fc1: FtLinear, fc2: FtLinear, dY, X, H, U1_save, U2_save, dX, dA1, dB1, dA2, dB2,
+                     grad_dtype, workspace, ws_bytes, stream=None):
+    s = lib().fourtune_mlp_bwd(ctypes.byref(fc1), ctypes.byref(fc2), _ptr(dY), _ptr(X), _ptr(H),
+                               _ptr(U1_save), _ptr(U2_save), _ptr(dX), _ptr(dA1), _ptr(dB1),
+                               _ptr(dA2), _ptr(dB2), int(grad_dtype), _ptr(workspace),
+                               int(ws_bytes), _stream(stream))
+    _check(s, "fourtune_mlp_bwd")
 
 
 def fourtune_act_fwd(act, h, n, out, stream=None):

@@ -326,6 +326,39 @@ ft_status fourtune_mlp_fwd(const ft_linear* fc1, const ft_linear* fc2, const uin
                            uint8_t* aq_codes, uint8_t* aq_scales, void* workspace,
                            size_t ws_bytes, void* stream);
 
+/* The backward of the same MLP block, mirrored: FC2's input-gradient GEMM
+ * (on FC2's tiles read transposed, section 3.2) holds dX2 = dL/d gelu(h) in
+ * its registers; its epilogue reads the matching rows of H, forms FC1's
+ * incoming gradient dY1 = bf16(dX2 * gelu'(H)) and writes it (dX2 itself is
+ * not written), and from the same values writes FC1's quantized gradient
+ * Qrow(dY1) and the fp32 sums of FC1's down-projection dY1 V1^T over each
+ * 256 columns, so FC1's backward quantize kernel, a read of dX2 and H, does
+ * not run.  Then: those sums added in order into P1 (and FC1's padded rank
+ * operands), FC2's adapter gradients, FC1's input-gradient GEMM and FC1's
+ * adapter gradients (dB1 = U1[:, r_stab:]^T dY1 from dY1).
+ *   dY: bf16 [M, N2], the gradient of Y; X: FC1's input [M, K1]; H: FC1's
+ *   output h [M, N1] from fourtune_mlp_fwd (or fourtune_linear_fwd);
+ *   U1_save, U2_save: the forward's U of each layer.
+ *   dX: bf16 [M, K1], FC1's input gradient; dA1, dB1, dA2, dB2: the adapter
+ *   gradients, rank-major as in fourtune_linear_bwd, in grad_dtype.
+ * Requirements: fc1->act_out and fc2->act_in FT_ACT_GELU_TANH, the layers
+ * chain as for fourtune_mlp_fwd, and those of fourtune_linear_bwd for each
+ * layer (dX required).  The mirror applies when both layers are FT_W4A4G4,
+ * fc2's w_block is TILE32 (the method), N2 % 128 == 0, M > 16, FC2's
+ * input-gradient GEMM runs in one pass, and R1 <= 64; otherwise the two
+ * backwards run one after the other through dX2 (the same results up to
+ * the order of dB1's fp32 sums, which the mirror forms from dY1 in
+ * 512-token chunks).
+ * workspace: at least fourtune_mlp_bwd_workspace_bytes(fc1, fc2) bytes.
+ * Errors: those of fourtune_linear_bwd for each layer; FT_ESHAPE if the
+ * layers do not chain; FT_EINVAL for the activations or a missing dX. */
+size_t fourtune_mlp_bwd_workspace_bytes(const ft_linear* fc1, const ft_linear* fc2);
+ft_status fourtune_mlp_bwd(const ft_linear* fc1, const ft_linear* fc2, const uint16_t* dY,
+                           const uint16_t* X, const uint16_t* H, const uint16_t* U1_save,
+                           const uint16_t* U2_save, uint16_t* dX, void* dA1, void* dB1, void* dA2,
+                           void* dB2, ft_dtype grad_dtype, void* workspace, size_t ws_bytes,
+                           void* stream);
+
 /* The activation on its own, with the same device functions the fused
  * kernels apply to their inputs (so that a caller, or a test, can see the
  * exact bf16 values the layers consume).  n elements, contiguous.

@@ -254,6 +254,36 @@ def test_mlp_forward_argument_errors():
     assert _mlp(f1, f2) == ops.FT_EUNSUPPORTED          # only the missing GPU stops it
 
 
+def _mlpb(f1, f2, dY=A16, X=A16, H=A16, U1=A16, U2=A16, dX=A16, dA1=A16, dB1=A16, dA2=A16, dB2=A16,
+          gdt=0, ws=A16, wsb=1 << 40):
+    return ops.lib().fourtune_mlp_bwd(ctypes.byref(f1), ctypes.byref(f2), dY, X, H, U1, U2, dX, dA1,
+                                      dB1, dA2, dB2, gdt, ws, wsb, None)
+
+
+def test_mlp_backward_argument_errors():
+    """The mirrored MLP backward checks both layers, that they chain and carry
+    the GELU between them, its pointers and its workspace before touching any
+    device."""
+    G = ops.FT_ACT_GELU_TANH
+    f1 = _layer(M=300, K=256, N=544, act_out=G)
+    f2 = _layer(M=300, K=544, N=256, act_in=G)
+    need = ops.fourtune_mlp_bwd_workspace_bytes(f1, f2)
+    assert need > ops.fourtune_workspace_bytes(f1, True) + ops.fourtune_workspace_bytes(f2, True)
+    assert need >= ops.fourtune_workspace_bytes(f1, True) + ops.fourtune_workspace_bytes(f2, True) + 300 * 544 * 2
+    assert ops.fourtune_mlp_bwd_workspace_bytes(f1, _layer(K=40)) == 0
+    assert _mlpb(f1, _layer(M=300, K=512, N=256, act_in=G)) == ops.FT_ESHAPE
+    assert _mlpb(_layer(M=300, K=256, N=544), f2) == ops.FT_EINVAL        # no GELU after FC1
+    assert _mlpb(f1, _layer(M=300, K=544, N=256)) == ops.FT_EINVAL        # no GELU before FC2
+    assert _mlpb(f1, f2, dX=None) == ops.FT_EINVAL
+    assert _mlpb(f1, f2, H=None) == ops.FT_EINVAL
+    assert _mlpb(f1, f2, dB2=None) == ops.FT_EINVAL
+    assert _mlpb(f1, f2, gdt=5) == ops.FT_EINVAL
+    assert _mlpb(f1, f2, dA1=A16 + 4) == ops.FT_EALIGN
+    assert _mlpb(f1, f2, wsb=need - 1) == ops.FT_EWORKSPACE
+    assert _mlpb(f1, f2, ws=None, wsb=need) == ops.FT_EINVAL
+    assert _mlpb(f1, f2) == ops.FT_EUNSUPPORTED          # only the missing GPU stops it
+
+
 def _fwd_noalloc(L, X=A16, Y=A16, U=A16, qc=None, qs=None):
     return ops.lib().fourtune_linear_fwd_noalloc(ctypes.byref(L), X, Y, U, qc, qs, None)
 

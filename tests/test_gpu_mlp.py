@@ -22,7 +22,7 @@ import pytest
 import torch
 
 from bit_quantized_amd import ops, synth
-from bit_quantized_amd.layer import QuantizedLinear, bits_of, mlp_forward
+from bit_quantized_amd.layer import QuantizedLinear, bits_of, mlp_backward, mlp_forward
 from oracle import linear as OL
 from oracle import mxfp4 as OQ
 
@@ -373,3 +373,88 @@ def test_mlp_fused_forward_full_size():
     D = OL.stack_down(mp.c2.L1, mp.c2.A)
     A = OQ.bf16_bits_to_f64(a_rows)
     check_rounding_flips(got["U2"][rows], A @ D, "U2 rows", np.abs(A) @ np.abs(D), F)
+
+
+# ------------------------------------------------------------------ the mirrored MLP backward
+# FC2's input-gradient GEMM forms FC1's incoming gradient dY1 = dX2 gelu'(h)
+# in its epilogue and quantizes and projects it for FC1 (fourtune_mlp_bwd).
+def _run_bwd_both(mp, full_size=False):
+    c1, c2 = mp.c1, mp.c2
+    X1, dY2 = up(c1.X), up(c2.dY)
+    h, U1, _, U2 = mlp_forward(mp.fc1, mp.fc2, X1)
+    torch.cuda.synchronize()
+    # unfused: the two backwards through dX2
+    dX2, dA2u, dB2u, _ = mp.fc2.backward(dY2, h, U2)
+    dX1u, dA1u, dB1u, _ = mp.fc1.backward(dX2, X1, U1, H=h)
+    torch.cuda.synchronize()
+    ops.fourtune_timing_reset()
+    ops.fourtune_timing_enable(True)
+    try:
+        dX1, dA1, dB1, dA2, dB2 = mlp_backward(mp.fc1, mp.fc2, dY2, X1, h, U1, U2)
+        torch.cuda.synchronize()
+    finally:
+        ops.fourtune_timing_enable(False)
+    names = _fused_kernels()
+    ops.fourtune_timing_reset()
+    T = lambda t: None if t is None else np.ascontiguousarray(bits_of(t).T)
+    Bb = lambda t: None if t is None else bits_of(t)
+    got = dict(dX1=bits_of(dX1), dA1=T(dA1), dB1=Bb(dB1), dA2=T(dA2), dB2=Bb(dB2))
+    ref = dict(dX1=bits_of(dX1u), dA1=T(dA1u), dB1=Bb(dB1u), dA2=T(dA2u), dB2=Bb(dB2u))
+    return got, ref, names, bits_of(h), bits_of(dX2), bits_of(U1)
+
+
+def _check_db1(mp, got, h_bits, dx2_bits, u1_bits):
+    """dB1 = U1[:, r_s:]^T dY1 with dY1 = gelu'(h) dX2 as the GPU forms it:
+    a correct rounding of the exact sum but for the fp32 accumulation order."""
+    c1 = mp.c1
+    if not c1.r_l:
+        return
+    dy1 = _gelu_grad_gpu(h_bits, dx2_bits)
+    Ul = OQ.bf16_bits_to_f64(u1_bits[:, c1.r_s:c1.R])
+    G = OQ.bf16_bits_to_f64(dy1)
+    check_rounding_flips(got["dB1"], Ul.T @ G, "dB1", np.abs(Ul).T @ np.abs(G), c1.M)
+
+
+@pytest.mark.parametrize("shape", [
+    (300, 256, 544, 16, 8),     # ragged rows, F = 544: last column tile of 32
+    (520, 384, 1280, 32, 32),   # R1 = 64: four rank groups
+    (600, 128, 2304, 32, 16),   # R1 = 48: three rank groups
+    (130, 256, 768, 0, 8),      # adapter only
+    (272, 128, 288, 0, 0),      # no ranks: dY1's codes only
+])
+def test_mlp_mirrored_backward_full(shape):
+    M, K, F, rs, rl = shape
+    say("case mirrored mlp backward", shape)
+    mp = MlpPair(M, K, F, rs, rl, seed=5 * M + F)
+    got, ref, names, h, dx2, u1 = _run_bwd_both(mp)
+    say("kernels", names)
+    # FC2's quantizer, its mirrored dgrad, FC1's dgrad: FC1's quantizer does not run
+    assert names.get("bwd_gemm_dgrad_mlp") == 1 and names.get("bwd_gemm_dgrad") == 1, names
+    assert names.get("bwd_quant_down") == 1, names
+    assert names.get("bwd_rank_reduce", 0) == (1 if mp.c1.R else 0), names
+    # FC2's adapter gradients come out of the same kernels
+    for k in ("dA2", "dB2"):
+        _same_bits(got[k], ref[k], k)
+    # dX1 and dA1 read P1, whose fp32 sums may round the other way where
+    # the unfused quantizer takes 128-column splits: compared to the unfused
+    # result within the accumulation bound of the exact sums
+    res = {k: OL.rel_frobenius(got[k], ref[k]) for k in ("dX1", "dA1") if got[k] is not None}
+    say("rel vs unfused", res)
+    for k, v in res.items():
+        assert v <= 1e-4, (k, v)
+    _check_db1(mp, got, h, dx2, u1)
+
+
+def test_mlp_mirrored_backward_full_size():
+    """FLUX MLP backward at full size (4608 tokens, 3072 -> 12288 -> 3072,
+    ranks 32/32): the mirrored backward gives the unfused backwards' dX1,
+    dA1, dA2 and dB2 bit for bit (FC1's quantizer sums 256-column splits at
+    this size) and dB1 within its accumulation bound."""
+    M, K, F = 4608, 3072, 12288
+    say("case mirrored mlp backward full size")
+    mp = MlpPair(M, K, F, 32, 32, seed=2)
+    got, ref, names, h, dx2, u1 = _run_bwd_both(mp)
+    assert names.get("bwd_gemm_dgrad_mlp") == 1 and names.get("bwd_rank_reduce") == 1, names
+    for k in ("dX1", "dA1", "dA2", "dB2"):
+        _same_bits(got[k], ref[k], k)
+    _check_db1(mp, got, h, dx2, u1)
