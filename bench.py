@@ -86,11 +86,11 @@ def parse():
 def layer_work(M, K, N, rs, rl):
     """Algorithmic FLOP and HBM bytes of each kernel of one fwd+bwd step.
 
-    For adapter ranks up to 32 the dB product runs inside the backward
+    For adapter ranks up to 64 the dB product runs inside the backward
     quantize kernel (which reads dY anyway), so it is counted there and the
     adapter-gradient kernel reads only X for dA."""
     R = rs + rl
-    db_fused = 0 < rl <= 32
+    db_fused = 0 < rl <= 64
     w = {
         "fwd_quant_down": {"flop": 2 * M * K * R,
                            "bytes": 2 * M * K + M * K // 2 + M * K // 32 + 2 * M * R + 2 * K * R,
@@ -225,8 +225,12 @@ def _step_kernel(kname, state):
     if "k_gemm" in kname:
         return ("fwd_gemm" if state.get("fwd") else "bwd_gemm_dgrad"), True
     if "k_lora_reduce" in kname:
-        return "bwd_lora_grads", False
+        # (alone when dA was made beside the dgrad: then it is the launch)
+        opens = not state.get("lora_open", False)
+        state["lora_open"] = False
+        return "bwd_lora_grads", opens
     if "k_lora" in kname:
+        state["lora_open"] = True
         return "bwd_lora_grads", True
     return None, False
 
@@ -472,6 +476,14 @@ def main():
                 kernels[name] = {"avg_us": round(us, 2), "launches": cnt, "bound": "hbm",
                                  "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                  "frac": round(ach / PEAK_HBM_GBS, 4)}
+        if "bwd_lora_reduce" in tm and tm["bwd_lora_reduce"][1] and "bwd_lora_grads" not in kernels:
+            # dA's partials were made by the dgrad's launch on the CUs its
+            # tiles leave free; the adapter-gradient launch is the reduction
+            tot, cnt = tm["bwd_lora_reduce"]
+            kernels["bwd_lora_grads"] = {"avg_us": round(tot / cnt * 1e3, 2), "launches": cnt,
+                                         "bound": "hbm", "beside_dgrad": True,
+                                         "note": "dA made inside bwd_gemm_dgrad's launch on the CUs "
+                                                 "its tiles leave free; this is its reduction only"}
         dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
         dk = kernels[dom]
         traffic = load_traffic(dom, sha)

@@ -131,6 +131,10 @@ struct Timed {
   }
 };
 
+// The backward's dgrad computes dA on the CUs its tiles leave free when at
+// least this many are free.
+constexpr int kSideMinFreeCUs = 16;
+
 // Checks shared by forward and backward.
 ft_status check_linear(const ft_linear* L) {
   if (!L) return FT_EINVAL;
@@ -373,6 +377,29 @@ ft_status bwd_run(const ft_linear* L, const uint16_t* dY, const uint16_t* X,
     e = tm.done(ft::launch_quant_row32(dY, h2, act, L->M, L->N, L->N, qc, qs, st));
   }
   if (e != hipSuccess) return FT_EDEVICE;
+  // the adapter gradients: dA = P[:, r_s:]^T X and dB = U[:, r_s:]^T dY
+  ft::LoraGradArgs la{}, lb{};
+  if (rl > 0) {
+    const int f32 = grad_dtype == FT_F32 ? 1 : 0;
+    la.M = L->M; la.I = L->K; la.big = X; la.small = P; la.ld_small = R; la.r0 = L->r_stab; la.rl = rl;
+    la.big2 = nullptr; la.act = L->act_in == FT_ACT_GELU_TANH ? 1 : 0;
+    la.out = dA; la.out_f32 = f32;
+    la.part = reinterpret_cast<float*>(ws + lay.dA_part);
+    lb = la;
+    lb.I = L->N; lb.big = dY; lb.small = U_save;
+    lb.big2 = L->act_out == FT_ACT_GELU_TANH ? H : nullptr;
+    lb.act = L->act_out == FT_ACT_GELU_TANH ? 2 : 0;
+    lb.out = dB;
+    lb.part = reinterpret_cast<float*>(ws + lay.dB_part);
+    if (!k1) {
+      // dY1 = dY * gelu'(H) is already formed
+      lb.big = hook->db_big; lb.big2 = nullptr; lb.act = 0;
+      lb.part = hook->db_part;
+    }
+    lb.nchunk = db_fused ? ft::quant_down_db_chunks(L->M, L->N, R, rl) : 0;
+  }
+  // dA computed by the dgrad's launch on the CUs its tiles leave free
+  bool da_side = false;
   if (dX) {
     ft::GemmArgs g{};
     g.M = L->M; g.RED = L->N; g.NOUT = L->K;
@@ -417,30 +444,34 @@ ft_status bwd_run(const ft_linear* L, const uint16_t* dY, const uint16_t* X,
       g.e_codes = ep->codes; g.e_scales = ep->scales; g.e_part = ep->part;
       g.e_pr = ep->pr; g.e_R = ep->R; g.e_nrg = ep->nrg; g.e_h = hook->h;
     }
+    // the transposed-weight dgrad whose tiles leave CUs free takes dA on
+    // them (dB done by the quantizer, ranks in one pass, X without an
+    // activation): the adapter-gradient launch is then only its reduction
+    if (rl > 0 && rl <= 64 && db_fused && la.act == 0 && g.b_transposed && !bf &&
+        !(hook && hook->epi) && (L->N & 127) == 0) {
+      const int cus = ft::cu_count();
+      const uint32_t wgs = ft::gemm_workgroups(g);
+      const uint32_t items = ft::lora_chunks(L->M) * ft::lora_col_blocks(L->K);
+      if (wgs > 0 && static_cast<int64_t>(wgs) + kSideMinFreeCUs <= cus) {
+        la.nchunk = static_cast<int>(ft::lora_chunks(L->M));
+        g.lora_a = la;
+        g.gemm_wgs = wgs;
+        g.side_wgs = std::min(static_cast<uint32_t>(cus) - wgs, items);
+        da_side = true;
+      }
+    }
     Timed tm(hook && hook->epi ? "bwd_gemm_dgrad_mlp" : "bwd_gemm_dgrad", st);
     if (tm.done(ft::launch_gemm(g, st)) != hipSuccess) return FT_EDEVICE;
   }
   if (rl > 0) {
-    const int f32 = grad_dtype == FT_F32 ? 1 : 0;
-    ft::LoraGradArgs a{};
-    a.M = L->M; a.I = L->K; a.big = X; a.small = P; a.ld_small = R; a.r0 = L->r_stab; a.rl = rl;
-    a.big2 = nullptr; a.act = L->act_in == FT_ACT_GELU_TANH ? 1 : 0;
-    a.out = dA; a.out_f32 = f32;
-    a.part = reinterpret_cast<float*>(ws + lay.dA_part);
-    ft::LoraGradArgs b = a;
-    b.I = L->N; b.big = dY; b.small = U_save;
-    b.big2 = L->act_out == FT_ACT_GELU_TANH ? H : nullptr;
-    b.act = L->act_out == FT_ACT_GELU_TANH ? 2 : 0;
-    b.out = dB;
-    b.part = reinterpret_cast<float*>(ws + lay.dB_part);
-    if (!k1) {
-      // dY1 = dY * gelu'(H) is already formed
-      b.big = hook->db_big; b.big2 = nullptr; b.act = 0;
-      b.part = hook->db_part;
+    if (da_side) {
+      // dA's partials came from the dgrad's side workgroups
+      Timed tm("bwd_lora_reduce", st);
+      if (tm.done(ft::launch_lora_reduce(la, lb, st)) != hipSuccess) return FT_EDEVICE;
+    } else {
+      Timed tm("bwd_lora_grads", st);
+      if (tm.done(ft::launch_lora_grads(la, lb, db_fused, st)) != hipSuccess) return FT_EDEVICE;
     }
-    b.nchunk = db_fused ? ft::quant_down_db_chunks(L->M, L->N, R, rl) : 0;
-    Timed tm("bwd_lora_grads", st);
-    if (tm.done(ft::launch_lora_grads(a, b, db_fused, st)) != hipSuccess) return FT_EDEVICE;
   }
   return FT_OK;
 }

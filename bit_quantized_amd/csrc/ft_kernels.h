@@ -82,6 +82,21 @@ hipError_t launch_dequant_tile32(const uint8_t* codes, const uint8_t* scales, in
 hipError_t launch_dequant_tile32_t(const uint8_t* codes, const uint8_t* scales, int64_t rows,
                                    int64_t cols, uint16_t* out, hipStream_t st);
 
+// lora.hip: out[r][i] = sum_m act(big)[m][i] * small[m][r0 + r], r < rl,
+// act as for the row quantizers (big2 is the second input of act 2).
+struct LoraGradArgs {
+  int64_t M, I;                   // rows, columns of big
+  const uint16_t* big;            // bf16 [M, I]
+  const uint16_t* big2;           // bf16 [M, I], act 2 only
+  int act;
+  const uint16_t* small;          // bf16 [M, ld_small], columns r0 .. r0+rl used
+  int ld_small, r0, rl;
+  void* out;                      // [rl, I]
+  int out_f32;                    // 0 bf16, 1 fp32
+  float* part;                    // workspace: fp32 partials per 512-token chunk
+  int nchunk;                     // partials to add (set by launch_lora_grads unless precomputed)
+};
+
 // gemm.hip: out[m][j] = sum_red deq(a)[m][red] deq(b)[j][red] + sum_r lm[m][r] lo[j][r]
 // forward: a = Qrow(X) [M, K], b = Qtile(W) [N, K], lm = U, lo = [L2^T | B^T]
 // dgrad  : a = Qrow(dY) [M, N], b = Qtile(W) [N, K] read transposed
@@ -135,8 +150,19 @@ struct GemmArgs {
   RankRows e_pr;
   int e_R, e_nrg;
   const uint16_t* e_h;
+  // The adapter gradient dA beside a transposed-weight product (b_transposed,
+  // no MLP epilogue) whose tiles leave CUs free: the launch has gemm_wgs
+  // workgroups for the product and side_wgs more, which compute lora_a's
+  // fp32 partials per 512-token chunk as the adapter-gradient kernel does
+  // (side_wgs = 0: none); k_lora_reduce, later on the stream, adds them.
+  LoraGradArgs lora_a;
+  uint32_t gemm_wgs, side_wgs;
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
+// Workgroups of the product kernel launch_gemm starts for g, side
+// workgroups not counted (0 when no device is current): a persistent grid
+// of at most one per CU for the pipelined kernel.
+uint32_t gemm_workgroups(const GemmArgs& g);
 // The fused-epilogue instantiations (g.e_codes set), gemm_mlp.hip;
 // launch_gemm hands such calls over.
 hipError_t launch_gemm_mlp(const GemmArgs& g, hipStream_t st);
@@ -168,20 +194,6 @@ inline size_t gemm_split_bytes(int64_t M, int64_t RED, int64_t NOUT) {
   return p.splits > 1 ? static_cast<size_t>(p.splits) * M * NOUT * sizeof(float) : 0;
 }
 
-// lora.hip: out[r][i] = sum_m act(big)[m][i] * small[m][r0 + r], r < rl,
-// act as for the row quantizers (big2 is the second input of act 2).
-struct LoraGradArgs {
-  int64_t M, I;                   // rows, columns of big
-  const uint16_t* big;            // bf16 [M, I]
-  const uint16_t* big2;           // bf16 [M, I], act 2 only
-  int act;
-  const uint16_t* small;          // bf16 [M, ld_small], columns r0 .. r0+rl used
-  int ld_small, r0, rl;
-  void* out;                      // [rl, I]
-  int out_f32;                    // 0 bf16, 1 fp32
-  float* part;                    // workspace: fp32 partials per 512-token chunk
-  int nchunk;                     // partials to add (set by launch_lora_grads unless precomputed)
-};
 // dA and dB of one backward: one launch computes the partials of both
 // problems, a second adds them in chunk order.  dB_done: dB's partials
 // [dB.nchunk][16 ceil(rl/16)][I] are already in dB.part (made by the
@@ -189,6 +201,14 @@ struct LoraGradArgs {
 hipError_t launch_lora_grads(const LoraGradArgs& dA, const LoraGradArgs& dB, bool dB_done,
                              hipStream_t st);
 size_t lora_grad_part_bytes(int64_t M, int64_t I, int rl);
+// dA's partials made beside a product (GemmArgs::lora_a, dA.nchunk set to
+// lora_chunks): only the reduction of dA and of the quantizer's dB
+// partials runs here (dA.rl <= 64, dB done).
+hipError_t launch_lora_reduce(const LoraGradArgs& dA, const LoraGradArgs& dB, hipStream_t st);
+// 512-token chunks and 64-column blocks of one adapter-gradient problem:
+// the work items of its partials.
+uint32_t lora_chunks(int64_t M);
+uint32_t lora_col_blocks(int64_t I);
 
 // scratch.hip: the workspace of the forward that allocates nothing, a
 // device array of kNoAllocScratchBytes (FT_NOALLOC_SCRATCH_BYTES of the C

@@ -504,9 +504,28 @@ __global__ __launch_bounds__(256) void k_split_reduce(const GemmArgs g) {
 }
 }  // namespace
 
+uint32_t gemm_workgroups(const GemmArgs& g) {
+  const uint32_t n = static_cast<uint32_t>(((g.NOUT + BN - 1) / BN) * ((g.M + BM - 1) / BM));
+  const bool bf = g.a16 != nullptr;
+  if (!g.e_codes && gemm_rows_ok(g.M, g.RED, bf, g.b_transposed != 0))
+    return static_cast<uint32_t>((g.NOUT + 31) / 32);
+  const bool pipe = (g.RED & 127) == 0 || (bf && (g.RED & 31) == 0);
+  if (!pipe) return n;
+  const int cus = cu_count();
+  if (cus <= 0) return 0;
+  const uint32_t units = !g.e_codes && g.splits > 1 ? n * static_cast<uint32_t>(g.splits) : n;
+  return std::min(units, static_cast<uint32_t>(cus));
+}
+
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   const uint32_t n = static_cast<uint32_t>(((g.NOUT + BN - 1) / BN) * ((g.M + BM - 1) / BM));
   const bool bf = g.a16 != nullptr;
+  // dA beside the product: the pipelined transposed-weight kernel only, its
+  // grid as gemm_workgroups gives it, ranks in one pass
+  if (g.side_wgs > 0 && (g.e_codes || !g.b_transposed || bf || g.b_row_scales ||
+                         (g.RED & 127) != 0 || g.gemm_wgs != gemm_workgroups(g) ||
+                         g.lora_a.rl < 1 || g.lora_a.rl > 64 || g.lora_a.act != 0))
+    return hipErrorInvalidValue;
   // MLP fusion: the fused epilogues' instantiations live in gemm_mlp.hip
   if (g.e_codes) return launch_gemm_mlp(g, st);
   if (gemm_rows_ok(g.M, g.RED, bf, g.b_transposed != 0)) {
@@ -525,7 +544,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
     const int cus = cu_count();
     if (cus <= 0) return hipErrorInvalidDevice;
     const uint32_t units = n * static_cast<uint32_t>(g.splits);
-    const uint32_t grid = units < static_cast<uint32_t>(cus) ? units : static_cast<uint32_t>(cus);
+    const uint32_t grid = (units < static_cast<uint32_t>(cus) ? units : static_cast<uint32_t>(cus)) + g.side_wgs;
     if (g.b_row_scales) hipLaunchKernelGGL((k_gemm_pipe<0, 1>), dim3(grid), dim3(256), 0, st, g);
     else if (g.b_transposed) hipLaunchKernelGGL((k_gemm_pipe<0, 3>), dim3(grid), dim3(256), 0, st, g);
     else hipLaunchKernelGGL((k_gemm_pipe<0, 0>), dim3(grid), dim3(256), 0, st, g);
@@ -547,7 +566,7 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   if ((g.RED & 127) == 0 || (bf && (g.RED & 31) == 0)) {
     const int cus = cu_count();
     if (cus <= 0) return hipErrorInvalidDevice;
-    const uint32_t grid = n < static_cast<uint32_t>(cus) ? n : static_cast<uint32_t>(cus);
+    const uint32_t grid = (n < static_cast<uint32_t>(cus) ? n : static_cast<uint32_t>(cus)) + g.side_wgs;
 #define FT_GP(NL, MODE) hipLaunchKernelGGL((k_gemm_pipe<NL, MODE>), dim3(grid), dim3(256), 0, st, g)
 #define FT_GPN(MODE) do { if (g.nlr == 4) FT_GP(4, MODE); else if (g.nlr > 0) FT_GP(2, MODE); else FT_GP(0, MODE); } while (0)
     if (g.nlr != 0 && g.nlr != 2 && g.nlr != 4) return hipErrorInvalidValue;

@@ -6,6 +6,7 @@
 
 #include "ft_device.hpp"
 #include "ft_kernels.h"
+#include "lora_block.hpp"
 
 #include <algorithm>
 
@@ -137,6 +138,38 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
+// dA beside a transposed-weight product (GemmArgs::lora_a): workgroup j of
+// the side_wgs after the product's takes the adapter-gradient work items
+// j, j + side_wgs, ... (64 columns x 512 tokens each, column block fastest)
+// in the LDS the product's stages would use.  RG rank groups of 16; ACT
+// the activation of X as loaded (0 here).
+template <int RG, int ACT>
+__device__ __forceinline__ void side_lora_rg(const GemmArgs& g, uint8_t* lds) {
+  using namespace lora_dev;
+  static_assert(2 * MS * PB * 2 + MC * small_pitch<RG>() * 2 <= NST * ST_BYTES,
+                "the adapter-gradient work item fits in the stages");
+  auto* bigL = reinterpret_cast<uint16_t (*)[MS * PB]>(lds);
+  uint16_t* smL = reinterpret_cast<uint16_t*>(lds + 2 * MS * PB * 2);
+  const uint32_t nib = static_cast<uint32_t>((g.lora_a.I + IB - 1) / IB);
+  const uint32_t items = nib * static_cast<uint32_t>((g.lora_a.M + MC - 1) / MC);
+  for (uint32_t it = blockIdx.x - g.gemm_wgs; it < items; it += g.side_wgs) {
+    // the previous item's LDS reads are done before this one's stores
+    __syncthreads();
+    lora_block<RG, ACT>(g.lora_a, it % nib, it / nib, bigL, smL);
+  }
+}
+// (X as is: with GELU recomputed on X the product's own registers spilled;
+// a layer with a GELU input runs its adapter gradients as their own launch)
+template <int ACT>
+__device__ __forceinline__ void side_lora_act(const GemmArgs& g, uint8_t* lds) {
+  switch ((g.lora_a.rl + 15) / 16) {
+    case 1: side_lora_rg<1, ACT>(g, lds); break;
+    case 2: side_lora_rg<2, ACT>(g, lds); break;
+    case 3: side_lora_rg<3, ACT>(g, lds); break;
+    default: side_lora_rg<4, ACT>(g, lds); break;
+  }
+}
+
 // EPI > 0: the MLP-fused epilogue (GemmArgs::e_codes): EPI 1..5 the
 // forward (EPI - 1 rank groups of 16 in the second linear's
 // down-projection), 6..10 the backward mirror (EPI - 6 groups in the first
@@ -148,6 +181,16 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   __shared__ __attribute__((aligned(16))) uint8_t lds[NST * ST_BYTES];
   // the output strips: a separate LDS object (the stages are DMA targets)
   __shared__ __attribute__((aligned(16))) uint8_t lds_out[4 * OUT_WAVE];
+
+  // the workgroups past the product's compute dA (transposed-weight
+  // products only; the host sets side_wgs)
+  constexpr bool SIDE = BT && EPI == 0;
+  if constexpr (SIDE) {
+    if (g.side_wgs > 0 && blockIdx.x >= g.gemm_wgs) {
+      side_lora_act<0>(g, lds);
+      return;
+    }
+  }
 
   const int t = threadIdx.x, lane = t & 63;
   const int wave = __builtin_amdgcn_readfirstlane(t >> 6);
@@ -163,7 +206,8 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   // (only without rank steps: a split launch leaves the rank part to the
   // kernel that adds the splits)
   const uint32_t S = (!LR && EPI == 0 && g.splits > 1) ? static_cast<uint32_t>(g.splits) : 1u;
-  const uint32_t ntiles = mt_n * nt_n * S, G = gridDim.x, bid = blockIdx.x;
+  const uint32_t G = SIDE && g.side_wgs > 0 ? g.gemm_wgs : gridDim.x;
+  const uint32_t ntiles = mt_n * nt_n * S, bid = blockIdx.x;
   const uint32_t full = ntiles / G, nlast = ntiles % G;
   const uint32_t my_tiles = full + (bid < nlast ? 1u : 0u);
   constexpr int NLR = NLR_;                              // rank steps: 0, 2 or 4

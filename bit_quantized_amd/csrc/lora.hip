@@ -31,126 +31,26 @@
 // dB recomputes from dY and h the same way.
 #include "ft_device.hpp"
 #include "ft_kernels.h"
+#include "lora_block.hpp"
 
 namespace ft {
 
 namespace {
 
-constexpr int IB = 64;      // columns of big per workgroup
-constexpr int MS = 64;      // tokens per step
-constexpr int NSTEP = 8;    // steps per workgroup
-constexpr int MC = MS * NSTEP;
-constexpr int PB = 80;      // LDS pitch (bf16) of a big row: 40 dwords
-// LDS pitch (bf16) of a small row: 8 (2 RG - 1) dwords, an odd multiple of 8
-template <int RG> constexpr int small_pitch() { return 16 * (2 * RG - 1); }
-
-// One workgroup: 64 columns of big (column block cb) x 512 tokens.  ACT is
-// the activation applied to big as it is loaded (rounded to bf16).
-template <int RG, int ACT>
-__device__ __forceinline__ void lora_block(const LoraGradArgs& a, uint32_t cb,
-                                           uint16_t (*bigL)[MS * PB], uint16_t* smL) {
-  constexpr int RP = RG * 16;
-  constexpr int PS = small_pitch<RG>();
-  const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
-  const int g = lane >> 4, q = lane & 15;
-  const int64_t M = a.M, I = a.I;
-  const int64_t i0 = static_cast<int64_t>(cb) * IB;
-  const int64_t mbeg = static_cast<int64_t>(blockIdx.y) * MC;
-  const int64_t mend = M < mbeg + MC ? M : mbeg + MC;
-
-  // ---- big loads of every step: thread t covers rows t/8 and 32 + t/8 of
-  // the step, columns 8 (t % 8) .. +8 (each row's 128 bytes in 8 lanes)
-  const auto rbig = make_rsrc(a.big, static_cast<uint64_t>(M) * I * 2);
-  const auto rbig2 = make_rsrc(a.big2, ACT == 2 ? static_cast<uint64_t>(M) * I * 2 : 0);
-  const int lr = t >> 3, cc = (t & 7) * 8;
-  const bool col_ok = i0 + cc < I;
-  u32x4 va[NSTEP], vb[NSTEP], ha[NSTEP], hb[NSTEP];
-#pragma unroll
-  for (int s = 0; s < NSTEP; ++s) {
-    const int64_t ma = mbeg + s * MS + lr, mb = ma + 32;
-    const uint32_t oa = col_ok && ma < mend ? static_cast<uint32_t>((ma * I + i0 + cc) * 2) : BUF_OOB;
-    const uint32_t ob = col_ok && mb < mend ? static_cast<uint32_t>((mb * I + i0 + cc) * 2) : BUF_OOB;
-    va[s] = buf_load128(rbig, oa);
-    vb[s] = buf_load128(rbig, ob);
-    if constexpr (ACT == 2) {
-      ha[s] = buf_load128(rbig2, oa);
-      hb[s] = buf_load128(rbig2, ob);
-    }
-  }
-
-  // ---- small[m][r0 + r] of the chunk, row-major: smL[m][r], ranks >= rl zero
-  const int rl = a.rl;
-  if ((a.r0 & 7) == 0 && (a.ld_small & 7) == 0 && (rl & 7) == 0) {
-    const auto rs = make_rsrc(a.small, static_cast<uint64_t>(M) * a.ld_small * 2);
-    constexpr int CPR = RP / 8;                      // 16-byte chunks per token
-    constexpr int PER = MC * CPR / 256;
-    u32x4 w[PER];
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int c = t + 256 * e;
-      const int m = c / CPR, rc = c % CPR;
-      const int64_t gm = mbeg + m;
-      w[e] = buf_load128(rs, (8 * rc < rl && gm < mend)
-                                 ? static_cast<uint32_t>((gm * a.ld_small + a.r0 + 8 * rc) * 2) : BUF_OOB);
-    }
-#pragma unroll
-    for (int e = 0; e < PER; ++e) {
-      const int c = t + 256 * e;
-      *reinterpret_cast<u32x4*>(&smL[(c / CPR) * PS + (c % CPR) * 8]) = w[e];
-    }
-  } else {
-    for (int idx = t; idx < MC * RP; idx += 256) {
-      const int m = idx / RP, r = idx % RP;
-      const int64_t gm = mbeg + m;
-      smL[m * PS + r] = (gm < mend && r < rl) ? a.small[gm * a.ld_small + a.r0 + r] : uint16_t(0);
-    }
-  }
-
-  f32x4 acc[RG];
-#pragma unroll
-  for (int c = 0; c < RG; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-#pragma unroll
-  for (int s = 0; s < NSTEP; ++s) {
-    uint16_t* bl = bigL[s & 1];
-    *reinterpret_cast<u32x4*>(&bl[lr * PB + cc]) = act_bf16x8<ACT>(va[s], ACT == 2 ? ha[s] : va[s]);
-    *reinterpret_cast<u32x4*>(&bl[(32 + lr) * PB + cc]) = act_bf16x8<ACT>(vb[s], ACT == 2 ? hb[s] : vb[s]);
-    __syncthreads();
-    // wave w: columns 16w .. 16w+15 of the block; lane q of group g addresses
-    // row 4g + q/4 (+16) of the half step, columns c0 + 4 (q % 4)
-#pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
-      const uint16_t* bp = bl + (kk * 32 + 4 * g + (q >> 2)) * PB + 16 * wave + 4 * (q & 3);
-      const u32x2 b0 = lds_read_tr16(bp), b1 = lds_read_tr16(bp + 16 * PB);
-      const u32x4 bf = {b0[0], b0[1], b1[0], b1[1]};
-#pragma unroll
-      for (int c = 0; c < RG; ++c) {
-        const uint16_t* sp = smL + (s * MS + kk * 32 + 4 * g + (q >> 2)) * PS + 16 * c + 4 * (q & 3);
-        const u32x2 a0 = lds_read_tr16(sp), a1 = lds_read_tr16(sp + 16 * PS);
-        acc[c] = mfma_bf16_16x16x32(u32x4{a0[0], a0[1], a1[0], a1[1]}, bf, acc[c]);
-      }
-    }
-  }
-
-  // acc[c][j]: rank r = 16c + 4g + j, column i = i0 + 16 wave + q;
-  // partials part[chunk][r][I], rank-major
-  const int64_t i = i0 + 16 * wave + q;
-  if (i < I) {
-    float* mypart = a.part + static_cast<int64_t>(blockIdx.y) * RP * I;
-#pragma unroll
-    for (int c = 0; c < RG; ++c)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) mypart[(16 * c + 4 * g + j) * I + i] = acc[c][j];
-  }
-}
+using lora_dev::IB;
+using lora_dev::MC;
+using lora_dev::MS;
+using lora_dev::PB;
+using lora_dev::lora_block;
+using lora_dev::small_pitch;
 
 template <int RG, int ACTA, int ACTB>
 __global__ __launch_bounds__(256) void k_lora_grads(const LoraGradArgs pa, const LoraGradArgs pb,
                                                     uint32_t nib_a) {
   __shared__ __attribute__((aligned(16))) uint16_t bigL[2][MS * PB];
   __shared__ __attribute__((aligned(16))) uint16_t smL[MC * small_pitch<RG>()];
-  if (blockIdx.x < nib_a) lora_block<RG, ACTA>(pa, blockIdx.x, bigL, smL);
-  else lora_block<RG, ACTB>(pb, blockIdx.x - nib_a, bigL, smL);
+  if (blockIdx.x < nib_a) lora_block<RG, ACTA>(pa, blockIdx.x, blockIdx.y, bigL, smL);
+  else lora_block<RG, ACTB>(pb, blockIdx.x - nib_a, blockIdx.y, bigL, smL);
 }
 
 // out[r][i .. i+3] = sum over chunks y < nchunk (in order) of part[y][r][i .. i+3];
@@ -201,6 +101,32 @@ size_t lora_grad_part_bytes(int64_t M, int64_t I, int rl) {
   return static_cast<size_t>(nmc) * I * RP * sizeof(float);
 }
 
+uint32_t lora_chunks(int64_t M) { return static_cast<uint32_t>((M + MC - 1) / MC); }
+uint32_t lora_col_blocks(int64_t I) { return static_cast<uint32_t>((I + IB - 1) / IB); }
+
+// The sums of a pass: dA's partials (dA.nchunk chunks), then dB's.
+static hipError_t reduce_pass(const LoraGradArgs& dA, const LoraGradArgs& dB, int rg,
+                              hipStream_t st) {
+  // rl * I / 4 threads per problem
+  const uint32_t nblk_a = static_cast<uint32_t>((dA.rl * (dA.I / 4) + 255) / 256);
+  const uint32_t nblk_b = static_cast<uint32_t>((dB.rl * (dB.I / 4) + 255) / 256);
+#define FT_LR(RG) \
+  hipLaunchKernelGGL(k_lora_reduce<RG>, dim3(nblk_a + nblk_b), dim3(256), 0, st, dA, dB, nblk_a)
+  switch (rg) {
+    case 1: FT_LR(1); break;
+    case 2: FT_LR(2); break;
+    case 3: FT_LR(3); break;
+    default: FT_LR(4); break;
+  }
+#undef FT_LR
+  return hipGetLastError();
+}
+
+hipError_t launch_lora_reduce(const LoraGradArgs& dA, const LoraGradArgs& dB, hipStream_t st) {
+  if (dA.rl < 1 || dA.rl > 64 || dA.nchunk < 1) return hipErrorInvalidValue;
+  return reduce_pass(dA, dB, (dA.rl + 15) / 16, st);
+}
+
 // One pass over at most 64 ranks (4 groups of 16: the rank operand of a
 // 512-token chunk fills most of the LDS at 64).
 static hipError_t lora_grads_pass(const LoraGradArgs& dA_in, const LoraGradArgs& dB_in, bool dB_done,
@@ -213,17 +139,11 @@ static hipError_t lora_grads_pass(const LoraGradArgs& dA_in, const LoraGradArgs&
   if (!dB_done) dB.nchunk = static_cast<int>(nmc);
   dim3 grid(nib_a + nib_b, nmc);
   const int rg = (dA.rl + 15) / 16;
-  // reduction: rl * I / 4 threads per problem
-  const uint32_t nblk_a = static_cast<uint32_t>((dA.rl * (dA.I / 4) + 255) / 256);
-  const uint32_t nblk_b = static_cast<uint32_t>((dB.rl * (dB.I / 4) + 255) / 256);
 #define FT_LA(RG, A, B) hipLaunchKernelGGL((k_lora_grads<RG, A, B>), grid, dim3(256), 0, st, dA, dB, nib_a)
 #define FT_L(RG)                                                                              \
   do {                                                                                        \
     if (dA.act == 1) { if (dB.act == 2) FT_LA(RG, 1, 2); else FT_LA(RG, 1, 0); }              \
     else { if (dB.act == 2) FT_LA(RG, 0, 2); else FT_LA(RG, 0, 0); }                          \
-    if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;                        \
-    hipLaunchKernelGGL(k_lora_reduce<RG>, dim3(nblk_a + nblk_b), dim3(256), 0, st, dA, dB,    \
-                       nblk_a);                                                               \
   } while (0)
   switch (rg) {
     case 1: FT_L(1); break;
@@ -233,7 +153,8 @@ static hipError_t lora_grads_pass(const LoraGradArgs& dA_in, const LoraGradArgs&
   }
 #undef FT_L
 #undef FT_LA
-  return hipGetLastError();
+  if (hipGetLastError() != hipSuccess) return hipErrorLaunchFailure;
+  return reduce_pass(dA, dB, rg, st);
 }
 
 hipError_t launch_lora_grads(const LoraGradArgs& dA, const LoraGradArgs& dB, bool dB_done,
