@@ -204,6 +204,61 @@ def test_deterministic():
         np.testing.assert_array_equal(a[k], b[k], err_msg=k)
 
 
+@pytest.mark.parametrize("shape", [
+    (520, 1024, 768, 32, 16),    # 12 dgrad tiles: nearly every CU free
+    (4608, 3072, 9216, 32, 16),  # the QKV layer: 216 dgrad tiles, 40 CUs free
+    (300, 288, 512, 16, 64),     # 64 adapter ranks (4 rank groups), ragged rows
+])
+def test_adapter_gradient_beside_dgrad(shape):
+    """dA made by the dgrad's launch on the CUs its tiles leave free (the
+    adapter-gradient launch is then its reduction only) against dA from the
+    adapter-gradient kernel itself (the same backward without dX): bit for
+    bit, and dB and P unchanged.  The library's kernel timing names which
+    path ran."""
+    M, K, N, rs, rl = shape
+    c = synth.flux_linear_case(f"beside_{M}x{K}x{N}_r{rs}_{rl}", M, K, N, rs, rl, seed=M + N)
+    say("case", c.name)
+    g = GpuCase(c)
+    _, U = g.layer.forward(g.X)
+    torch.cuda.synchronize()
+
+    def bwd(need_dx):
+        ops.fourtune_timing_reset()
+        ops.fourtune_timing_enable(True)
+        out = g.layer.backward(g.dY, g.X, U, need_dx=need_dx)
+        torch.cuda.synchronize()
+        ops.fourtune_timing_enable(False)
+        names = {k for k, (_, n) in ops.fourtune_timing_read().items() if n}
+        return out, names
+
+    (dX, dA1, dB1, P1), n1 = bwd(True)
+    (_, dA0, dB0, P0), n0 = bwd(False)
+    assert "bwd_lora_reduce" in n1 and "bwd_lora_grads" not in n1, n1
+    assert "bwd_lora_grads" in n0 and "bwd_gemm_dgrad" not in n0, n0
+    np.testing.assert_array_equal(bits_of(dA1), bits_of(dA0))
+    np.testing.assert_array_equal(bits_of(dB1), bits_of(dB0))
+    np.testing.assert_array_equal(bits_of(P1), bits_of(P0))
+    assert dX is not None
+
+
+def test_adapter_gradient_own_launch_with_gelu_input():
+    """A layer whose input is gelu(h) keeps its adapter gradients in their
+    own launch (GELU on X is not recomputed beside the dgrad)."""
+    c = synth.flux_linear_case("gelu_in_lora", 256, 512, 384, 16, 8, seed=10)
+    say("case", c.name)
+    g = GpuCase(c)
+    layer = QuantizedLinear.from_factors(up(c.W_res), up(c.L1), up(c.L2), up(c.A), up(c.B),
+                                         act_in=ops.FT_ACT_GELU_TANH)
+    _, U = layer.forward(g.X)
+    ops.fourtune_timing_reset()
+    ops.fourtune_timing_enable(True)
+    layer.backward(g.dY, g.X, U)
+    torch.cuda.synchronize()
+    ops.fourtune_timing_enable(False)
+    names = {k for k, (_, n) in ops.fourtune_timing_read().items() if n}
+    assert "bwd_lora_grads" in names and "bwd_lora_reduce" not in names, names
+
+
 def test_autograd_function_act_in():
     """A layer whose input is gelu(h) used through the autograd Function:
     h's gradient is the layer's input gradient times gelu'(h).  Checked
