@@ -225,12 +225,8 @@ def _step_kernel(kname, state):
     if "k_gemm" in kname:
         return ("fwd_gemm" if state.get("fwd") else "bwd_gemm_dgrad"), True
     if "k_lora_reduce" in kname:
-        # (alone when dA was made beside the dgrad: then it is the launch)
-        opens = not state.get("lora_open", False)
-        state["lora_open"] = False
-        return "bwd_lora_grads", opens
+        return "bwd_lora_grads", False
     if "k_lora" in kname:
-        state["lora_open"] = True
         return "bwd_lora_grads", True
     return None, False
 
@@ -476,14 +472,13 @@ def main():
                 kernels[name] = {"avg_us": round(us, 2), "launches": cnt, "bound": "hbm",
                                  "achieved": round(ach, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                                  "frac": round(ach / PEAK_HBM_GBS, 4)}
-        if "bwd_lora_reduce" in tm and tm["bwd_lora_reduce"][1] and "bwd_lora_grads" not in kernels:
-            # dA's partials were made by the dgrad's launch on the CUs its
-            # tiles leave free; the adapter-gradient launch is the reduction
-            tot, cnt = tm["bwd_lora_reduce"]
-            kernels["bwd_lora_grads"] = {"avg_us": round(tot / cnt * 1e3, 2), "launches": cnt,
-                                         "bound": "hbm", "beside_dgrad": True,
-                                         "note": "dA made inside bwd_gemm_dgrad's launch on the CUs "
-                                                 "its tiles leave free; this is its reduction only"}
+        if "bwd_lora_grads" not in kernels and "bwd_gemm_dgrad" in kernels:
+            # the adapter gradients were made by the dgrad's launch on the
+            # CUs its tiles leave free: no launch of their own
+            kernels["bwd_lora_grads"] = {"avg_us": 0.0, "launches": 0, "bound": "hbm",
+                                         "beside_dgrad": True,
+                                         "note": "dA and dB made inside bwd_gemm_dgrad's launch on "
+                                                 "the CUs its tiles leave free"}
         dom = max(kernels, key=lambda k: kernels[k]["avg_us"])
         dk = kernels[dom]
         traffic = load_traffic(dom, sha)

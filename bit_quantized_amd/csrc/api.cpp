@@ -398,7 +398,8 @@ ft_status bwd_run(const ft_linear* L, const uint16_t* dY, const uint16_t* X,
     }
     lb.nchunk = db_fused ? ft::quant_down_db_chunks(L->M, L->N, R, rl) : 0;
   }
-  // dA computed by the dgrad's launch on the CUs its tiles leave free
+  // the adapter gradients made by the dgrad's launch on the CUs its tiles
+  // leave free
   bool da_side = false;
   if (dX) {
     ft::GemmArgs g{};
@@ -444,34 +445,39 @@ ft_status bwd_run(const ft_linear* L, const uint16_t* dY, const uint16_t* X,
       g.e_codes = ep->codes; g.e_scales = ep->scales; g.e_part = ep->part;
       g.e_pr = ep->pr; g.e_R = ep->R; g.e_nrg = ep->nrg; g.e_h = hook->h;
     }
-    // the transposed-weight dgrad whose tiles leave CUs free takes dA on
-    // them (dB done by the quantizer, ranks in one pass, X without an
-    // activation): the adapter-gradient launch is then only its reduction
+    // the transposed-weight dgrad whose tiles leave CUs free computes the
+    // adapter gradients there (dB's partials made by the quantizer, ranks
+    // in one pass, X without an activation), when their estimated time
+    // (about 2.5 us per 512-token chunk of a 64-column block of dA on one
+    // CU) stays well inside the product's (about 1 us per 128-deep step of
+    // a tile): then the adapter-gradient launch does not run
     if (rl > 0 && rl <= 64 && db_fused && la.act == 0 && g.b_transposed && !bf &&
         !(hook && hook->epi) && (L->N & 127) == 0) {
       const int cus = ft::cu_count();
       const uint32_t wgs = ft::gemm_workgroups(g);
-      const uint32_t items = ft::lora_chunks(L->M) * ft::lora_col_blocks(L->K);
       if (wgs > 0 && static_cast<int64_t>(wgs) + kSideMinFreeCUs <= cus) {
-        la.nchunk = static_cast<int>(ft::lora_chunks(L->M));
-        g.lora_a = la;
-        g.gemm_wgs = wgs;
-        g.side_wgs = std::min(static_cast<uint32_t>(cus) - wgs, items);
-        da_side = true;
+        const uint32_t side = static_cast<uint32_t>(cus) - wgs;
+        const int64_t tiles = ((L->M + 255) / 256) * ((L->K + 255) / 256);
+        const int64_t units = tiles * std::max(g.splits, 1);
+        const int64_t steps = g.splits > 1 ? 2 * g.split_pairs
+                                           : (L->N / 128 + (L->N / 128) % 2) + ft::rank_pad(R) / 32;
+        const double gemm_us = static_cast<double>((units + wgs - 1) / wgs) * steps;
+        const double side_us = 2.5 * ((ft::lora_col_blocks(L->K) + side - 1) / side) * ft::lora_chunks(L->M);
+        if (side_us <= 0.8 * gemm_us) {
+          g.lora_a = la;
+          g.lora_b = lb;
+          g.gemm_wgs = wgs;
+          g.side_wgs = side;
+          da_side = true;
+        }
       }
     }
     Timed tm(hook && hook->epi ? "bwd_gemm_dgrad_mlp" : "bwd_gemm_dgrad", st);
     if (tm.done(ft::launch_gemm(g, st)) != hipSuccess) return FT_EDEVICE;
   }
-  if (rl > 0) {
-    if (da_side) {
-      // dA's partials came from the dgrad's side workgroups
-      Timed tm("bwd_lora_reduce", st);
-      if (tm.done(ft::launch_lora_reduce(la, lb, st)) != hipSuccess) return FT_EDEVICE;
-    } else {
-      Timed tm("bwd_lora_grads", st);
-      if (tm.done(ft::launch_lora_grads(la, lb, db_fused, st)) != hipSuccess) return FT_EDEVICE;
-    }
+  if (rl > 0 && !da_side) {
+    Timed tm("bwd_lora_grads", st);
+    if (tm.done(ft::launch_lora_grads(la, lb, db_fused, st)) != hipSuccess) return FT_EDEVICE;
   }
   return FT_OK;
 }

@@ -150,12 +150,13 @@ struct GemmArgs {
   RankRows e_pr;
   int e_R, e_nrg;
   const uint16_t* e_h;
-  // The adapter gradient dA beside a transposed-weight product (b_transposed,
+  // The adapter gradients beside a transposed-weight product (b_transposed,
   // no MLP epilogue) whose tiles leave CUs free: the launch has gemm_wgs
-  // workgroups for the product and side_wgs more, which compute lora_a's
-  // fp32 partials per 512-token chunk as the adapter-gradient kernel does
-  // (side_wgs = 0: none); k_lora_reduce, later on the stream, adds them.
-  LoraGradArgs lora_a;
+  // workgroups for the product and side_wgs more, which compute lora_a
+  // (dA, X without an activation, rl <= 64) whole and add lora_b's
+  // partials (dB from the backward quantizer, lora_b.nchunk > 0; none when
+  // 0), with the bits the adapter-gradient kernels give (side_wgs = 0: none).
+  LoraGradArgs lora_a, lora_b;
   uint32_t gemm_wgs, side_wgs;
 };
 hipError_t launch_gemm(const GemmArgs& g, hipStream_t st);
@@ -201,12 +202,7 @@ inline size_t gemm_split_bytes(int64_t M, int64_t RED, int64_t NOUT) {
 hipError_t launch_lora_grads(const LoraGradArgs& dA, const LoraGradArgs& dB, bool dB_done,
                              hipStream_t st);
 size_t lora_grad_part_bytes(int64_t M, int64_t I, int rl);
-// dA's partials made beside a product (GemmArgs::lora_a, dA.nchunk set to
-// lora_chunks): only the reduction of dA and of the quantizer's dB
-// partials runs here (dA.rl <= 64, dB done).
-hipError_t launch_lora_reduce(const LoraGradArgs& dA, const LoraGradArgs& dB, hipStream_t st);
-// 512-token chunks and 64-column blocks of one adapter-gradient problem:
-// the work items of its partials.
+// 512-token chunks and 64-column blocks of one adapter-gradient problem.
 uint32_t lora_chunks(int64_t M);
 uint32_t lora_col_blocks(int64_t I);
 

@@ -524,7 +524,8 @@ hipError_t launch_gemm(const GemmArgs& g, hipStream_t st) {
   // grid as gemm_workgroups gives it, ranks in one pass
   if (g.side_wgs > 0 && (g.e_codes || !g.b_transposed || bf || g.b_row_scales ||
                          (g.RED & 127) != 0 || g.gemm_wgs != gemm_workgroups(g) ||
-                         g.lora_a.rl < 1 || g.lora_a.rl > 64 || g.lora_a.act != 0))
+                         g.lora_a.rl < 1 || g.lora_a.rl > 64 || g.lora_a.act != 0 ||
+                         (g.lora_b.nchunk > 0 && g.lora_b.rl != g.lora_a.rl)))
     return hipErrorInvalidValue;
   // MLP fusion: the fused epilogues' instantiations live in gemm_mlp.hip
   if (g.e_codes) return launch_gemm_mlp(g, st);

@@ -138,35 +138,41 @@ __device__ __forceinline__ void lds_barrier() {
   __builtin_amdgcn_sched_barrier(0);
 }
 
-// dA beside a transposed-weight product (GemmArgs::lora_a): workgroup j of
-// the side_wgs after the product's takes the adapter-gradient work items
-// j, j + side_wgs, ... (64 columns x 512 tokens each, column block fastest)
-// in the LDS the product's stages would use.  RG rank groups of 16; ACT
-// the activation of X as loaded (0 here).
-template <int RG, int ACT>
+// The adapter gradients beside a transposed-weight product (GemmArgs::
+// lora_a, lora_b): workgroup j of the side_wgs after the product's takes
+// dA's 64-column blocks j, j + side_wgs, ... over every 512-token chunk (no
+// partials: each block's chunks are added in chunk order and rounded once,
+// the bits the adapter-gradient kernels give), in the LDS the product's
+// stages would use; then every side thread adds its share of the column
+// quads of dB from the quantizer's partials (lora_b.nchunk of them), in
+// chunk order.  RG rank groups of 16; X as is (ACT 0: with GELU recomputed
+// on X the product's own registers spilled, so a layer with a GELU input
+// runs its adapter gradients as their own launch).
+template <int RG>
 __device__ __forceinline__ void side_lora_rg(const GemmArgs& g, uint8_t* lds) {
   using namespace lora_dev;
   static_assert(2 * MS * PB * 2 + MC * small_pitch<RG>() * 2 <= NST * ST_BYTES,
                 "the adapter-gradient work item fits in the stages");
   auto* bigL = reinterpret_cast<uint16_t (*)[MS * PB]>(lds);
   uint16_t* smL = reinterpret_cast<uint16_t*>(lds + 2 * MS * PB * 2);
+  const uint32_t j = blockIdx.x - g.gemm_wgs;
   const uint32_t nib = static_cast<uint32_t>((g.lora_a.I + IB - 1) / IB);
-  const uint32_t items = nib * static_cast<uint32_t>((g.lora_a.M + MC - 1) / MC);
-  for (uint32_t it = blockIdx.x - g.gemm_wgs; it < items; it += g.side_wgs) {
-    // the previous item's LDS reads are done before this one's stores
-    __syncthreads();
-    lora_block<RG, ACT>(g.lora_a, it % nib, it / nib, bigL, smL);
-  }
+  for (uint32_t cb = j; cb < nib; cb += g.side_wgs) lora_column_block<RG, 0>(g.lora_a, cb, bigL, smL);
 }
-// (X as is: with GELU recomputed on X the product's own registers spilled;
-// a layer with a GELU input runs its adapter gradients as their own launch)
-template <int ACT>
-__device__ __forceinline__ void side_lora_act(const GemmArgs& g, uint8_t* lds) {
-  switch ((g.lora_a.rl + 15) / 16) {
-    case 1: side_lora_rg<1, ACT>(g, lds); break;
-    case 2: side_lora_rg<2, ACT>(g, lds); break;
-    case 3: side_lora_rg<3, ACT>(g, lds); break;
-    default: side_lora_rg<4, ACT>(g, lds); break;
+__device__ __forceinline__ void side_lora(const GemmArgs& g, uint8_t* lds) {
+  const int rg = (g.lora_a.rl + 15) / 16;
+  switch (rg) {
+    case 1: side_lora_rg<1>(g, lds); break;
+    case 2: side_lora_rg<2>(g, lds); break;
+    case 3: side_lora_rg<3>(g, lds); break;
+    default: side_lora_rg<4>(g, lds); break;
+  }
+  if (g.lora_b.nchunk > 0) {
+    const uint32_t j = blockIdx.x - g.gemm_wgs;
+    const uint64_t nq = static_cast<uint64_t>(g.lora_b.rl) * (g.lora_b.I / 4);
+    for (uint64_t idx = static_cast<uint64_t>(j) * 256 + threadIdx.x; idx < nq;
+         idx += static_cast<uint64_t>(g.side_wgs) * 256)
+      lora_dev::lora_reduce_quad(g.lora_b, rg * 16, idx);
   }
 }
 
@@ -182,12 +188,12 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
   // the output strips: a separate LDS object (the stages are DMA targets)
   __shared__ __attribute__((aligned(16))) uint8_t lds_out[4 * OUT_WAVE];
 
-  // the workgroups past the product's compute dA (transposed-weight
-  // products only; the host sets side_wgs)
+  // the workgroups past the product's compute the adapter gradients
+  // (transposed-weight products only; the host sets side_wgs)
   constexpr bool SIDE = BT && EPI == 0;
   if constexpr (SIDE) {
     if (g.side_wgs > 0 && blockIdx.x >= g.gemm_wgs) {
-      side_lora_act<0>(g, lds);
+      side_lora(g, lds);
       return;
     }
   }

@@ -42,6 +42,7 @@ using lora_dev::MC;
 using lora_dev::MS;
 using lora_dev::PB;
 using lora_dev::lora_block;
+using lora_dev::lora_reduce_quad;
 using lora_dev::small_pitch;
 
 template <int RG, int ACTA, int ACTB>
@@ -59,38 +60,11 @@ __global__ __launch_bounds__(256) void k_lora_grads(const LoraGradArgs pa, const
 template <int RG>
 __global__ __launch_bounds__(256) void k_lora_reduce(const LoraGradArgs pa, const LoraGradArgs pb,
                                                      uint32_t nblk_a) {
-  constexpr int RP = RG * 16;
   const bool is_a = blockIdx.x < nblk_a;
   const LoraGradArgs& a = is_a ? pa : pb;
   const uint64_t idx = static_cast<uint64_t>(is_a ? blockIdx.x : blockIdx.x - nblk_a) * 256 + threadIdx.x;
-  const int64_t I = a.I, I4 = I / 4;
-  if (idx >= static_cast<uint64_t>(a.rl) * I4) return;
-  const int64_t r = static_cast<int64_t>(idx / I4);
-  const int64_t i = 4 * static_cast<int64_t>(idx % I4);
-  const uint64_t stride = static_cast<uint64_t>(RP) * I;
-  const uint32_t nmc = static_cast<uint32_t>(a.nchunk);
-  // 16 chunks' loads at once, as buffer loads (past the last chunk: zero),
-  // so that a batch costs one memory latency; added in chunk order
-  const auto rpart = make_rsrc(a.part, stride * nmc * 4);
-  const uint32_t base = static_cast<uint32_t>((r * I + i) * 4);
-  f32x4 s = {0.f, 0.f, 0.f, 0.f};
-  for (uint32_t y0 = 0; y0 < nmc; y0 += 16) {
-    f32x4 v[16];
-#pragma unroll
-    for (int k = 0; k < 16; ++k) {
-      const uint32_t off = y0 + k < nmc ? base + static_cast<uint32_t>((y0 + k) * stride * 4) : BUF_OOB;
-      v[k] = __builtin_bit_cast(f32x4, buf_load128(rpart, off));
-    }
-#pragma unroll
-    for (int k = 0; k < 16; ++k) s += v[k];
-  }
-  const int64_t o = r * I + i;
-  if (a.out_f32) {
-    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = s;
-  } else {
-    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) =
-        u32x2{cvt_pk_bf16(s[0], s[1]), cvt_pk_bf16(s[2], s[3])};
-  }
+  if (idx >= static_cast<uint64_t>(a.rl) * (a.I / 4)) return;
+  lora_reduce_quad(a, RG * 16, idx);
 }
 
 }  // namespace
@@ -120,11 +94,6 @@ static hipError_t reduce_pass(const LoraGradArgs& dA, const LoraGradArgs& dB, in
   }
 #undef FT_LR
   return hipGetLastError();
-}
-
-hipError_t launch_lora_reduce(const LoraGradArgs& dA, const LoraGradArgs& dB, hipStream_t st) {
-  if (dA.rl < 1 || dA.rl > 64 || dA.nchunk < 1) return hipErrorInvalidValue;
-  return reduce_pass(dA, dB, (dA.rl + 15) / 16, st);
 }
 
 // One pass over at most 64 ranks (4 groups of 16: the rank operand of a

@@ -18,12 +18,15 @@ constexpr int PB = 80;      // LDS pitch (bf16) of a big row: 40 dwords
 // LDS pitch (bf16) of a small row: 8 (2 RG - 1) dwords, an odd multiple of 8
 template <int RG> constexpr int small_pitch() { return 16 * (2 * RG - 1); }
 
-// One work item: 64 columns of big (column block cb) x 512 tokens (chunk).
-// ACT is the activation applied to big as it is loaded (rounded to bf16).
-// The caller's 256 threads all take part (barriers inside).
+// One work item: 64 columns of big (column block cb) x 512 tokens (chunk),
+// its MFMA sums set into acc (rank r = 16 c + 4 g + j at acc[c][j], column
+// i0 + 16 wave + q).  ACT is the activation applied to big as it is loaded
+// (rounded to bf16).  The caller's 256 threads all take part (barriers
+// inside; the caller orders the LDS between items).
 template <int RG, int ACT>
-__device__ __forceinline__ void lora_block(const LoraGradArgs& a, uint32_t cb, uint32_t chunk,
-                                           uint16_t (*bigL)[MS * PB], uint16_t* smL) {
+__device__ __forceinline__ void lora_item_sums(const LoraGradArgs& a, uint32_t cb, uint32_t chunk,
+                                               uint16_t (*bigL)[MS * PB], uint16_t* smL,
+                                               f32x4 (&acc)[RG]) {
   constexpr int RP = RG * 16;
   constexpr int PS = small_pitch<RG>();
   const int t = threadIdx.x, lane = t & 63, wave = t >> 6;
@@ -81,7 +84,6 @@ __device__ __forceinline__ void lora_block(const LoraGradArgs& a, uint32_t cb, u
     }
   }
 
-  f32x4 acc[RG];
 #pragma unroll
   for (int c = 0; c < RG; ++c) acc[c] = f32x4{0.f, 0.f, 0.f, 0.f};
 
@@ -107,15 +109,97 @@ __device__ __forceinline__ void lora_block(const LoraGradArgs& a, uint32_t cb, u
     }
   }
 
-  // acc[c][j]: rank r = 16c + 4g + j, column i = i0 + 16 wave + q;
-  // partials part[chunk][r][I], rank-major
-  const int64_t i = i0 + 16 * wave + q;
+}
+
+// One work item's fp32 partials: part[chunk][r][I], rank-major.
+template <int RG, int ACT>
+__device__ __forceinline__ void lora_block(const LoraGradArgs& a, uint32_t cb, uint32_t chunk,
+                                           uint16_t (*bigL)[MS * PB], uint16_t* smL) {
+  constexpr int RP = RG * 16;
+  f32x4 acc[RG];
+  lora_item_sums<RG, ACT>(a, cb, chunk, bigL, smL, acc);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, q = lane & 15;
+  const int64_t I = a.I;
+  const int64_t i = static_cast<int64_t>(cb) * IB + 16 * wave + q;
   if (i < I) {
     float* mypart = a.part + static_cast<int64_t>(chunk) * RP * I;
 #pragma unroll
     for (int c = 0; c < RG; ++c)
 #pragma unroll
       for (int j = 0; j < 4; ++j) mypart[(16 * c + 4 * g + j) * I + i] = acc[c][j];
+  }
+}
+
+// out[r][i] (r < rl) written from an fp32 sum: bf16 (round to nearest even)
+// or fp32, as the reduction kernel writes it.
+__device__ __forceinline__ void lora_out1(const LoraGradArgs& a, int64_t o, float v) {
+  if (a.out_f32) static_cast<float*>(a.out)[o] = v;
+  else static_cast<uint16_t*>(a.out)[o] = static_cast<uint16_t>(cvt_pk_bf16(v, v) & 0xFFFFu);
+}
+
+// A whole column block of out over every 512-token chunk, without
+// partials: each chunk's sums start from zero and are added to the total
+// in chunk order, the order in which the reduction kernel adds the
+// partials, so the result is the same bits; rounded once into out.
+template <int RG, int ACT>
+__device__ __forceinline__ void lora_column_block(const LoraGradArgs& a, uint32_t cb,
+                                                  uint16_t (*bigL)[MS * PB], uint16_t* smL) {
+  f32x4 tot[RG];
+#pragma unroll
+  for (int c = 0; c < RG; ++c) tot[c] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const uint32_t nmc = static_cast<uint32_t>((a.M + MC - 1) / MC);
+  for (uint32_t ch = 0; ch < nmc; ++ch) {
+    // the previous chunk's LDS reads are done before this one's stores
+    __syncthreads();
+    f32x4 acc[RG];
+    lora_item_sums<RG, ACT>(a, cb, ch, bigL, smL, acc);
+#pragma unroll
+    for (int c = 0; c < RG; ++c) tot[c] += acc[c];
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, q = lane & 15;
+  const int64_t I = a.I;
+  const int64_t i = static_cast<int64_t>(cb) * IB + 16 * wave + q;
+  if (i < I) {
+#pragma unroll
+    for (int c = 0; c < RG; ++c)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = 16 * c + 4 * g + j;
+        if (r < a.rl) lora_out1(a, static_cast<int64_t>(r) * I + i, tot[c][j]);
+      }
+  }
+}
+
+// Quad idx (rank idx / (I/4), columns 4 (idx % (I/4)) .. +3) of out as the
+// sum over a.nchunk partials [chunk][RP][I] in chunk order, 16 chunks' loads
+// at a time (past the last chunk: zero), rounded once.  idx < rl * I / 4.
+__device__ __forceinline__ void lora_reduce_quad(const LoraGradArgs& a, int RP, uint64_t idx) {
+  const int64_t I = a.I, I4 = I / 4;
+  const int64_t r = static_cast<int64_t>(idx / I4);
+  const int64_t i = 4 * static_cast<int64_t>(idx % I4);
+  const uint64_t stride = static_cast<uint64_t>(RP) * I;
+  const uint32_t nmc = static_cast<uint32_t>(a.nchunk);
+  const auto rpart = make_rsrc(a.part, stride * nmc * 4);
+  const uint32_t base = static_cast<uint32_t>((r * I + i) * 4);
+  f32x4 s = {0.f, 0.f, 0.f, 0.f};
+  for (uint32_t y0 = 0; y0 < nmc; y0 += 16) {
+    f32x4 v[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const uint32_t off = y0 + k < nmc ? base + static_cast<uint32_t>((y0 + k) * stride * 4) : BUF_OOB;
+      v[k] = __builtin_bit_cast(f32x4, buf_load128(rpart, off));
+    }
+#pragma unroll
+    for (int k = 0; k < 16; ++k) s += v[k];
+  }
+  const int64_t o = r * I + i;
+  if (a.out_f32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(a.out) + o) = s;
+  } else {
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(a.out) + o) =
+        u32x2{cvt_pk_bf16(s[0], s[1]), cvt_pk_bf16(s[2], s[3])};
   }
 }
 

@@ -210,11 +210,10 @@ def test_deterministic():
     (300, 288, 512, 16, 64),     # 64 adapter ranks (4 rank groups), ragged rows
 ])
 def test_adapter_gradient_beside_dgrad(shape):
-    """dA made by the dgrad's launch on the CUs its tiles leave free (the
-    adapter-gradient launch is then its reduction only) against dA from the
-    adapter-gradient kernel itself (the same backward without dX): bit for
-    bit, and dB and P unchanged.  The library's kernel timing names which
-    path ran."""
+    """dA and dB made by the dgrad's launch on the CUs its tiles leave free
+    (no adapter-gradient launch) against those of the adapter-gradient
+    kernels themselves (the same backward without dX): bit for bit, and P
+    unchanged.  The library's kernel timing names which path ran."""
     M, K, N, rs, rl = shape
     c = synth.flux_linear_case(f"beside_{M}x{K}x{N}_r{rs}_{rl}", M, K, N, rs, rl, seed=M + N)
     say("case", c.name)
@@ -233,7 +232,7 @@ def test_adapter_gradient_beside_dgrad(shape):
 
     (dX, dA1, dB1, P1), n1 = bwd(True)
     (_, dA0, dB0, P0), n0 = bwd(False)
-    assert "bwd_lora_reduce" in n1 and "bwd_lora_grads" not in n1, n1
+    assert "bwd_gemm_dgrad" in n1 and "bwd_lora_grads" not in n1, n1
     assert "bwd_lora_grads" in n0 and "bwd_gemm_dgrad" not in n0, n0
     np.testing.assert_array_equal(bits_of(dA1), bits_of(dA0))
     np.testing.assert_array_equal(bits_of(dB1), bits_of(dB0))
@@ -256,7 +255,7 @@ def test_adapter_gradient_own_launch_with_gelu_input():
     torch.cuda.synchronize()
     ops.fourtune_timing_enable(False)
     names = {k for k, (_, n) in ops.fourtune_timing_read().items() if n}
-    assert "bwd_lora_grads" in names and "bwd_lora_reduce" not in names, names
+    assert "bwd_lora_grads" in names, names
 
 
 def test_autograd_function_act_in():
