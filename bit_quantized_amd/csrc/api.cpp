@@ -131,8 +131,8 @@ struct Timed {
   }
 };
 
-// The backward's dgrad computes dA on the CUs its tiles leave free when at
-// least this many are free.
+// The backward's dgrad computes the adapter gradients on the CUs its tiles
+// leave free when at least this many are free.
 constexpr int kSideMinFreeCUs = 16;
 
 // Checks shared by forward and backward.
@@ -447,27 +447,37 @@ ft_status bwd_run(const ft_linear* L, const uint16_t* dY, const uint16_t* X,
     }
     // the transposed-weight dgrad whose tiles leave CUs free computes the
     // adapter gradients there (dB's partials made by the quantizer, ranks
-    // in one pass, X without an activation), when their estimated time
-    // (about 2.5 us per 512-token chunk of a 64-column block of dA on one
-    // CU) stays well inside the product's (about 1 us per 128-deep step of
-    // a tile): then the adapter-gradient launch does not run
+    // in one pass, X without an activation): its launch gets one workgroup
+    // more per CU that is free from the start (fewer tiles than CUs) or
+    // that finishes a round early (a partial last round: the extra
+    // workgroups are dispatched as those CUs free up), when the side
+    // work's estimate (about 2.5 us per 512-token chunk of a 64-column
+    // block of dA on one CU) stays within 0.8 of the time those CUs are
+    // free (about 1 us per 128-deep step of a tile).  The adapter-gradient
+    // launch then does not run.
     if (rl > 0 && rl <= 64 && db_fused && la.act == 0 && g.b_transposed && !bf &&
         !(hook && hook->epi) && (L->N & 127) == 0) {
-      const int cus = ft::cu_count();
-      const uint32_t wgs = ft::gemm_workgroups(g);
-      if (wgs > 0 && static_cast<int64_t>(wgs) + kSideMinFreeCUs <= cus) {
-        const uint32_t side = static_cast<uint32_t>(cus) - wgs;
-        const int64_t tiles = ((L->M + 255) / 256) * ((L->K + 255) / 256);
-        const int64_t units = tiles * std::max(g.splits, 1);
-        const int64_t steps = g.splits > 1 ? 2 * g.split_pairs
-                                           : (L->N / 128 + (L->N / 128) % 2) + ft::rank_pad(R) / 32;
-        const double gemm_us = static_cast<double>((units + wgs - 1) / wgs) * steps;
+      const int64_t cus = ft::cu_count();
+      const int64_t wgs = ft::gemm_workgroups(g);
+      const int64_t tiles = ((L->M + 255) / 256) * ((L->K + 255) / 256);
+      const int64_t units = tiles * std::max(g.splits, 1);
+      const int64_t steps = g.splits > 1 ? 2 * g.split_pairs
+                                         : (L->N / 128 + (L->N / 128) % 2) + ft::rank_pad(R) / 32;
+      int64_t side = 0, free_rounds = 0;
+      if (wgs > 0 && wgs + kSideMinFreeCUs <= cus) {
+        side = cus - wgs;                                  // free from the start
+        free_rounds = (units + wgs - 1) / wgs;
+      } else if (wgs == cus && units % cus != 0 && cus - units % cus >= kSideMinFreeCUs) {
+        side = cus - units % cus;                          // free for the last round
+        free_rounds = 1;
+      }
+      if (side > 0) {
         const double side_us = 2.5 * ((ft::lora_col_blocks(L->K) + side - 1) / side) * ft::lora_chunks(L->M);
-        if (side_us <= 0.8 * gemm_us) {
+        if (side_us <= 0.8 * static_cast<double>(free_rounds * steps)) {
           g.lora_a = la;
           g.lora_b = lb;
-          g.gemm_wgs = wgs;
-          g.side_wgs = side;
+          g.gemm_wgs = static_cast<uint32_t>(wgs);
+          g.side_wgs = static_cast<uint32_t>(side);
           da_side = true;
         }
       }

@@ -208,6 +208,8 @@ def test_deterministic():
     (520, 1024, 768, 32, 16),    # 12 dgrad tiles: nearly every CU free
     (4608, 3072, 9216, 32, 16),  # the QKV layer: 216 dgrad tiles, 40 CUs free
     (300, 288, 512, 16, 64),     # 64 adapter ranks (4 rank groups), ragged rows
+    (8192, 3072, 9216, 32, 16),  # 384 dgrad tiles: the extra workgroups take the
+                                 # 128 CUs that finish a round early
 ])
 def test_adapter_gradient_beside_dgrad(shape):
     """dA and dB made by the dgrad's launch on the CUs its tiles leave free
