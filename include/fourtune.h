@@ -255,7 +255,7 @@ ft_status fourtune_linear_fwd_noalloc(const ft_linear* L, const uint16_t* X, uin
 /* Backward, Eq. (3) and the adapter gradients of section 3.2:
  *   kernel 1 reads dY once and writes Qrow(dY) (1x32 blocks along N, the
  *   reduction dimension of the input gradient) and P = bf16(dY V^T); for
- *   r_lora <= 32 it also makes per-workgroup partial sums of dB from the dY
+ *   r_lora <= 64 it also makes per-workgroup partial sums of dB from the dY
  *   it holds, so dY is read once for the whole backward;
  *   kernel 2 computes deq(Qrow(dY)) deq(Qtile(W_res)) + P D^T, reading the
  *   forward's 32x32-tile codes and scales (w_codes, w_scales) transposed,
@@ -263,7 +263,11 @@ ft_status fourtune_linear_fwd_noalloc(const ft_linear* L, const uint16_t* X, uin
  *   kernel 3 writes the adapter gradients, rank-major like At and B:
  *   dA^T = P[:, r_stab:]^T X ([r_lora, K]) and dB = U[:, r_stab:]^T dY
  *   ([r_lora, N]), in grad_dtype (FT_BF16 or FT_F32); every partial sum is
- *   added in a fixed order, so the gradients are deterministic.
+ *   added in a fixed order, so the gradients are deterministic.  When
+ *   kernel 2's tiles leave CUs free (from the start or for its last round)
+ *   and dB's partials come from kernel 1, act_in is none and r_lora <= 64,
+ *   kernel 2's launch has extra workgroups on those CUs that compute kernel
+ *   3's results, with the same bits, and kernel 3 does not run.
  * X and U_save are the forward's input and saved U.  H: bf16 [M, N], this
  * layer's forward output Y; required when act_out != FT_ACT_NONE (then the
  * incoming gradient is dY * act_out'(H), recomputed wherever it is read),
