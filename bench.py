@@ -437,7 +437,7 @@ def main():
         log(f"bench: {ms * 1e3:.1f} us/step, {step_flop / (ms * 1e-3) / 1e12:.1f} TFLOP/s")
 
         # Optionally, the same steps replayed from HIP graphs, one per input set
-        # (the library records no memset, so a step is eight kernel nodes).
+        # (the library records no memset, so a step is six kernel nodes).
         # Measured no faster than launching them one by one on this stack, so
         # the headline stays with the direct launches.
         ms_graph = None
