@@ -669,13 +669,30 @@ __global__ __launch_bounds__(256, 1) void k_gemm_pipe(const GemmArgs g) {
           for (int gi = 0; gi < EGW; ++gi) pacc[gi] = f32x4{0.f, 0.f, 0.f, 0.f};
           const int ar = ln & 15;
           const int asw = (ar & 1) | (((ar >> 2) & 1) << 1);
+          auto frag = [&](int ks) {
+            return lds_read_b128(lds_out + (wm * 2 + (ks >> 2)) * OUT_WAVE + ar * 256 +
+                                 ((((ks & 3) ^ asw) << 6) | (16 * (ln >> 4))));
+          };
+          if constexpr (EACT == 1) {
+            // the strip's eight fragments are read before the first MFMA, so
+            // their LDS latencies overlap instead of each stalling its MFMAs
+            // (the backward mirror holds h as well: there the eight
+            // fragments would not fit beside it without spilling)
+            u32x4 afs[8];
 #pragma unroll
-          for (int ks = 0; ks < 8; ++ks) {
-            const uint8_t* src = lds_out + (wm * 2 + (ks >> 2)) * OUT_WAVE + ar * 256 +
-                                 ((((ks & 3) ^ asw) << 6) | (16 * (ln >> 4)));
-            const u32x4 af = lds_read_b128(src);
+            for (int ks = 0; ks < 8; ++ks) afs[ks] = frag(ks);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int gi = 0; gi < EGW; ++gi) pacc[gi] = mfma_bf16_16x16x32(af, bfr[gi][ks], pacc[gi]);
+            for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+              for (int gi = 0; gi < EGW; ++gi) pacc[gi] = mfma_bf16_16x16x32(afs[ks], bfr[gi][ks], pacc[gi]);
+          } else {
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+              const u32x4 af = frag(ks);
+#pragma unroll
+              for (int gi = 0; gi < EGW; ++gi) pacc[gi] = mfma_bf16_16x16x32(af, bfr[gi][ks], pacc[gi]);
+            }
           }
           lds_barrier();
           const uint32_t rb = srow >> 6, sl = (srow >> 4) & 3;
