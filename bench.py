@@ -80,6 +80,9 @@ def parse():
     ap.add_argument("--summarize-pmc", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print per-launch HBM traffic (JSON) from two rocprofv3 --pmc runs of "
                          "this script with --copy-probe (FETCH_SIZE, then WRITE_SIZE) and exit")
+    ap.add_argument("--summarize-pmc-kernels", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="as --summarize-pmc, but per kernel name (any section, e.g. --only "
+                         "stress), printed as a markdown table, and exit")
     return ap.parse_args()
 
 
@@ -310,6 +313,42 @@ def summarize_pmc(fetch_dir, write_dir):
     return out
 
 
+def _pmc_per_kernel(d, counter):
+    """Mean counter value per dispatch of each kernel name, and of the reference copy."""
+    acc, n, copy = {}, {}, []
+    for r in _csv_rows(d, "counter_collection.csv"):
+        if r["Counter_Name"] != counter:
+            continue
+        k, v = r["Kernel_Name"], float(r["Counter_Value"])
+        if "neg_kernel" in k:
+            copy.append(v)
+            continue
+        acc[k] = acc.get(k, 0.0) + v
+        n[k] = n.get(k, 0) + 1
+    return {k: acc[k] / n[k] for k in acc}, (sum(copy) / len(copy) if copy else None)
+
+
+def summarize_pmc_kernels(fetch_dir, write_dir):
+    """HBM bytes per dispatch of every library kernel (ft::), FETCH_SIZE and
+    WRITE_SIZE scaled by the plain copy's reading, as a markdown table."""
+    fr, fc = _pmc_per_kernel(fetch_dir, "FETCH_SIZE")
+    wr, wc = _pmc_per_kernel(write_dir, "WRITE_SIZE")
+    if fc is None or wc is None:
+        raise SystemExit("no reference copy in the counter runs (run them with --copy-probe)")
+    nbytes = 2 * COPY_PROBE_ELEMS
+    f_fac, w_fac = fc * 1024 / nbytes, wc * 1024 / nbytes
+    lines = [f"copy probe: {nbytes} bytes each way; fetch factor {f_fac:.4f}, write factor {w_fac:.4f}; "
+             f"kernel sources `source_sha` {source_sha()}", "",
+             "| kernel | fetch MB | write MB | total MB |", "|---|---|---|---|"]
+    for k in sorted(fr, key=lambda x: -fr[x]):
+        name = k.replace("(anonymous namespace)::", "").split("(")[0].removeprefix("void ")
+        if not name.startswith("ft::"):
+            continue
+        fb, wb = fr[k] * 1024 / f_fac / 1e6, wr.get(k, 0.0) * 1024 / w_fac / 1e6
+        lines.append(f"| `{name}` | {fb:.1f} | {wb:.1f} | {fb + wb:.1f} |")
+    return "\n".join(lines)
+
+
 def copy_probe(dev, stream):
     import torch
     src = torch.ones(COPY_PROBE_ELEMS, dtype=torch.bfloat16, device=dev)
@@ -362,6 +401,9 @@ def main():
         return
     if a.summarize_pmc:
         print(json.dumps(summarize_pmc(*a.summarize_pmc), indent=1))
+        return
+    if a.summarize_pmc_kernels:
+        print(summarize_pmc_kernels(*a.summarize_pmc_kernels))
         return
     if a.summarize_counters:
         print(json.dumps(summarize_counters(a.summarize_counters), indent=1))
